@@ -1,0 +1,142 @@
+"""Seeded synthetic inputs for the splat rasterizer: 2D splats, depths, upstream image gradients, Adam state.
+
+This module only draws inputs. It holds none of the rasterizer's arithmetic, so the HIP path and the CPU oracle can
+both be fed from it without sharing any of the method's code.
+
+A splat record is 9 float32 values {x, y, a, b, c, r, g, b, o}: the mean in pixels, the conic [[a, b], [b, c]] (the
+inverse of the 2D covariance), the colour and the opacity color_a. The covariance is R diag(s1^2, s2^2) R^T with a
+rotation angle theta, built in float64 and inverted before rounding to float32.
+
+Draw order for every scene (numpy default_rng(seed)): x, y, (size class), s1, s2, theta, opacity, rgb, depth, then
+the upstream image gradient. The workloads below stand in for the trained 410k-splat Lego checkpoint at 800x800 that
+the pages measure on, which is not available; they keep its image size and splat count.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+@dataclass
+class SceneSpec:
+    name: str
+    width: int
+    height: int
+    n: int
+    seed: int
+    # (fraction, s_min, s_max) size classes, each log-uniform in [s_min, s_max] pixels
+    size_classes: tuple = ((1.0, 0.5, 8.0),)
+    opacity_mu: float = 0.0      # color_a = sigmoid(N(opacity_mu, opacity_sd))
+    opacity_sd: float = 1.0
+    depth_lo: float = 0.1
+    depth_hi: float = 10.0
+    vout_sd: float = 1.0         # upstream dL/dpixel ~ N(0, vout_sd) per channel
+    depth_levels: int = 0        # > 0: depths quantised to this many levels (forces ties)
+    margin: float = 0.0          # means drawn over [-margin, W + margin) x [-margin, H + margin)
+
+
+# The five workloads: a tiny scene, two 800x800 raster scenes, a binning stress case and the full iteration shape.
+SPECS = {
+    "tiny": SceneSpec("tiny", 64, 64, 256, seed=1, size_classes=((1.0, 0.5, 8.0),), vout_sd=1.0),
+    "raster84k": SceneSpec("raster84k", 800, 800, 84_000, seed=2, size_classes=((1.0, 0.3, 20.0),),
+                           vout_sd=0.01),
+    "raster410k": SceneSpec("raster410k", 800, 800, 410_000, seed=3,
+                            size_classes=((0.7, 0.3, 4.0), (0.3, 4.0, 40.0)),
+                            opacity_mu=-2.0, opacity_sd=1.5, vout_sd=0.01),
+    "bin1m": SceneSpec("bin1m", 800, 800, 1_000_000, seed=4, size_classes=((1.0, 0.5, 40.0),)),
+    "iter410k": SceneSpec("iter410k", 800, 800, 410_000, seed=5,
+                          size_classes=((0.7, 0.3, 4.0), (0.3, 4.0, 40.0)),
+                          opacity_mu=-2.0, opacity_sd=1.5, vout_sd=0.01),
+}
+
+# Adam parameter groups per splat: means 3, log_scales 3, rot_quats 4, raw_opacities 1, SH coefficients 16 x 3.
+ADAM_GROUP_WIDTHS = (("means", 3), ("log_scales", 3), ("rot_quats", 4), ("raw_opacities", 1), ("sh_coeffs", 48))
+
+
+@dataclass
+class Scene:
+    spec: SceneSpec
+    splats: np.ndarray   # float32 [N, 9]
+    depths: np.ndarray   # float32 [N]
+    v_out: np.ndarray    # float32 [H, W, 4] (.w is drawn but ignored by the method)
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def width(self):
+        return self.spec.width
+
+    @property
+    def height(self):
+        return self.spec.height
+
+
+def _sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def make_scene(spec: SceneSpec | str, **overrides) -> Scene:
+    if isinstance(spec, str):
+        spec = SPECS[spec]
+    if overrides:
+        spec = SceneSpec(**{**spec.__dict__, **overrides})
+    rng = np.random.default_rng(spec.seed)
+    n, W, H = spec.n, spec.width, spec.height
+    m = spec.margin
+    x = rng.uniform(-m, W + m, n)
+    y = rng.uniform(-m, H + m, n)
+    # size class per splat: exact class counts, assigned by a random permutation
+    fracs = np.array([c[0] for c in spec.size_classes], np.float64)
+    counts = np.floor(fracs / fracs.sum() * n).astype(np.int64)
+    counts[0] += n - counts.sum()
+    cls = np.repeat(np.arange(len(counts)), counts)[rng.permutation(n)]
+    lo = np.log(np.array([c[1] for c in spec.size_classes]))[cls]
+    hi = np.log(np.array([c[2] for c in spec.size_classes]))[cls]
+    s1 = np.exp(rng.uniform(lo, hi))
+    s2 = np.exp(rng.uniform(lo, hi))
+    theta = rng.uniform(0.0, np.pi, n)
+    opac = _sigmoid(rng.normal(spec.opacity_mu, spec.opacity_sd, n))
+    rgb = rng.uniform(0.0, 1.0, (n, 3))
+    depth = rng.uniform(spec.depth_lo, spec.depth_hi, n)
+    if spec.depth_levels > 0:
+        depth = spec.depth_lo + np.floor((depth - spec.depth_lo) / (spec.depth_hi - spec.depth_lo)
+                                         * spec.depth_levels) / spec.depth_levels * (spec.depth_hi - spec.depth_lo)
+        depth = np.maximum(depth, spec.depth_lo)
+    # covariance R diag(s1^2, s2^2) R^T and its inverse, in float64
+    c, s = np.cos(theta), np.sin(theta)
+    v1, v2 = s1 * s1, s2 * s2
+    sxx = c * c * v1 + s * s * v2
+    syy = s * s * v1 + c * c * v2
+    sxy = c * s * (v1 - v2)
+    det = sxx * syy - sxy * sxy
+    splats = np.stack([x, y, syy / det, -sxy / det, sxx / det, rgb[:, 0], rgb[:, 1], rgb[:, 2], opac], axis=1)
+    v_out = rng.normal(0.0, spec.vout_sd, (H, W, 4))
+    return Scene(spec, splats.astype(np.float32), depth.astype(np.float32), v_out.astype(np.float32),
+                 extra={"s1": s1, "s2": s2, "theta": theta})
+
+
+def make_adam_groups(n: int, seed: int = 5):
+    """Per group (name, param, grad, m, v) float32 arrays of n * width elements.
+
+    params ~ N(0, 1), grads ~ N(0, 1e-3), m ~ N(0, 1e-3), v = N(0, 1e-3)^2 (so that v >= 0).
+    """
+    rng = np.random.default_rng(seed + 1000)
+    groups = []
+    for name, w in ADAM_GROUP_WIDTHS:
+        k = n * w
+        p = rng.normal(0.0, 1.0, k).astype(np.float32)
+        g = rng.normal(0.0, 1e-3, k).astype(np.float32)
+        mm = rng.normal(0.0, 1e-3, k).astype(np.float32)
+        vv = (rng.normal(0.0, 1e-3, k) ** 2).astype(np.float32)
+        groups.append((name, p, g, mm, vv))
+    return groups
+
+
+# Adam hyper-parameters of the full-iteration workload; step t = 1000.
+ADAM_HPARAMS = {"lr": 1.6e-4, "beta1": 0.9, "beta2": 0.999, "eps": 1e-15, "step": 1000}
+
+
+def adam_bias_corrections(beta1: float, beta2: float, step: int) -> tuple[float, float]:
+    """bc1 = 1 - beta1^t and bc2 = 1 - beta2^t in float64, rounded to float32 (host-side scalars of the step)."""
+    return float(np.float32(1.0 - np.float64(np.float32(beta1)) ** step)), \
+        float(np.float32(1.0 - np.float64(np.float32(beta2)) ** step))

@@ -1,0 +1,185 @@
+"""Pins of the oracle's binning (emit, stable sort, per-tile ranges) against hand cases, brute force and the pages.
+
+The binning rule follows the C0 resident arena + C1 pass skip page (section 2): one key (tile_id << 32) | depth bits
+and one value (splat index) per overlapped 16x16 tile, sorted by key, then per-tile ranges.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from differentiable_gaussian_splatting_amd import scenes
+
+
+def splat_from_cov(x, y, s1, s2, theta, rgb=(1.0, 0.5, 0.25), o=0.5):
+    c, s = math.cos(theta), math.sin(theta)
+    sxx = c * c * s1 * s1 + s * s * s2 * s2
+    syy = s * s * s1 * s1 + c * c * s2 * s2
+    sxy = c * s * (s1 * s1 - s2 * s2)
+    det = sxx * syy - sxy * sxy
+    return np.array([x, y, syy / det, -sxy / det, sxx / det, *rgb, o], np.float32)
+
+
+# ----------------------------------------------------------------------------------------------- hand cases
+def test_unit_splat_at_tile_centre_gives_one_pair(orc):
+    sp = splat_from_cov(8.0, 8.0, 1.0, 1.0, 0.0)
+    b = orc.bin(sp[None], np.array([1.0], np.float32), 64, 64)
+    assert b.num_pairs == 1
+    assert int(b.keys[0] >> np.uint64(32)) == 0 and b.vals.tolist() == [0]
+
+
+def test_unit_splat_at_tile_corner_gives_four_pairs(orc):
+    sp = splat_from_cov(16.0, 16.0, 1.0, 1.0, 0.0)
+    b = orc.bin(sp[None], np.array([1.0], np.float32), 64, 64)
+    tiles = sorted(int(k >> np.uint64(32)) for k in b.keys)
+    assert tiles == [0, 1, 4, 5]  # tiles_x = 4 at 64 px
+
+
+def test_extent_touching_a_tile_edge_includes_that_tile(orc):
+    # s1 = 8 along x: conic a = 1/64, c = 1, b = 0 exactly, so rx = 3 * 8 = 24 exactly; 40 +- 24 spans [16, 64],
+    # and floor(64 / 16) = 4 includes tile 4.
+    sp = np.array([40.0, 8.0, 1.0 / 64.0, 0.0, 1.0, 1, 1, 1, 0.5], np.float32)
+    assert orc.tile_rect(sp, 1.0, 128, 64) == (1, 4, 0, 0)
+    b = orc.bin(sp[None], np.array([1.0], np.float32), 128, 64)
+    assert [int(k >> np.uint64(32)) for k in b.keys] == [1, 2, 3, 4]
+
+
+@pytest.mark.parametrize("field,value", [(0, np.nan), (2, -1.0), (4, np.inf), (8, 1.5), (8, -0.1)])
+def test_invalid_splats_are_culled(orc, field, value):
+    sp = splat_from_cov(20.0, 20.0, 2.0, 2.0, 0.0)
+    sp[field] = value
+    assert orc.bin(sp[None], np.array([1.0], np.float32), 64, 64).num_pairs == 0
+
+
+def test_singular_conic_and_bad_depth_are_culled(orc):
+    sp = np.array([20, 20, 1.0, 1.0, 1.0, 1, 1, 1, 0.5], np.float32)  # det = 0
+    assert orc.bin(sp[None], np.array([1.0], np.float32), 64, 64).num_pairs == 0
+    good = splat_from_cov(20.0, 20.0, 2.0, 2.0, 0.0)
+    for d in (0.0, -1.0, np.nan):
+        assert orc.bin(good[None], np.array([d], np.float32), 64, 64).num_pairs == 0
+
+
+def test_offscreen_splat_emits_nothing(orc):
+    sp = splat_from_cov(-100.0, 30.0, 2.0, 2.0, 0.3)
+    assert orc.bin(sp[None], np.array([1.0], np.float32), 64, 64).num_pairs == 0
+    sp = splat_from_cov(30.0, 64.0 + 40.0, 2.0, 2.0, 0.3)
+    assert orc.bin(sp[None], np.array([1.0], np.float32), 64, 64).num_pairs == 0
+
+
+def test_depth_ties_keep_index_order_and_depth_orders_within_tile(orc):
+    sps = np.stack([splat_from_cov(8.0, 8.0, 1.0, 1.0, 0.0)] * 4)
+    depths = np.array([2.0, 1.0, 2.0, 1.0], np.float32)
+    b = orc.bin(sps, depths, 16, 16)
+    assert b.vals.tolist() == [1, 3, 0, 2]
+    assert b.ranges.tolist() == [[0, 4]]
+
+
+def test_empty_tiles_get_canonical_lower_bound_ranges(orc):
+    # one splat in tile 5 of a 4x4 grid: tiles 0..4 are [0,0), tile 5 is [0,1), tiles 6..15 are [1,1)
+    sp = splat_from_cov(24.0, 24.0, 1.0, 1.0, 0.0)
+    b = orc.bin(sp[None], np.array([1.0], np.float32), 64, 64)
+    exp = [[0, 0]] * 5 + [[0, 1]] + [[1, 1]] * 10
+    assert b.ranges.tolist() == exp
+
+
+def test_ragged_image_partial_tiles(orc):
+    # 24 x 40 px: tiles_x = 2, tiles_y = 3; a splat near the right/bottom edge lands in the partial edge tiles
+    sp = splat_from_cov(22.0, 37.0, 1.0, 1.0, 0.0)
+    b = orc.bin(sp[None], np.array([1.0], np.float32), 24, 40)
+    assert b.ranges.shape == (6, 2)
+    assert [int(k >> np.uint64(32)) for k in b.keys] == [5]
+
+
+def test_empty_input(orc):
+    b = orc.bin(np.zeros((0, 9), np.float32), np.zeros(0, np.float32), 800, 800)
+    assert b.num_pairs == 0 and b.ranges.shape == (2500, 2) and not b.ranges.any()
+
+
+# ----------------------------------------------------------------------------------------------- brute force
+def _brute_force_bins(s1, s2, theta, x, y, depths, width, height, guard=1e-3):
+    """Tile sets from the covariance in float64 (not from the stored conic), a naive stable insertion sort by
+    (tile, depth) and ranges by scanning. Splats whose 3-sigma box edge lies within `guard` px of a tile edge are
+    reported so the caller can leave them out of the comparison."""
+    tx_n, ty_n = (width + 15) // 16, (height + 15) // 16
+    pairs, ambiguous = [], set()
+    for i in range(len(x)):
+        c, s = math.cos(theta[i]), math.sin(theta[i])
+        sxx = c * c * s1[i] ** 2 + s * s * s2[i] ** 2
+        syy = s * s * s1[i] ** 2 + c * c * s2[i] ** 2
+        rx, ry = 3 * math.sqrt(sxx), 3 * math.sqrt(syy)
+        edges = [(x[i] - rx) / 16, (x[i] + rx) / 16, (y[i] - ry) / 16, (y[i] + ry) / 16]
+        if any(abs(e - round(e)) * 16 < guard for e in edges):
+            ambiguous.add(i)
+        for ty in range(ty_n):
+            for tx in range(tx_n):
+                # tile [16 tx, 16 tx + 16) overlaps the closed box [x - rx, x + rx] as floor indices do
+                if math.floor(edges[0]) <= tx <= math.floor(edges[1]) and \
+                        math.floor(edges[2]) <= ty <= math.floor(edges[3]):
+                    pairs.append((ty * tx_n + tx, depths[i], i))
+    out = []
+    for p in pairs:  # naive stable insertion sort by (tile, depth)
+        j = len(out)
+        while j > 0 and (out[j - 1][0], out[j - 1][1]) > (p[0], p[1]):
+            j -= 1
+        out.insert(j, p)
+    ranges = []
+    for t in range(tx_n * ty_n):
+        lo = sum(1 for p in out if p[0] < t)
+        hi = sum(1 for p in out if p[0] <= t)
+        ranges.append([lo, hi])
+    return out, ranges, ambiguous
+
+
+@pytest.mark.parametrize("seed", [11, 12, 13])
+def test_binning_matches_brute_force_on_tiny_scenes(orc, seed):
+    sc = scenes.make_scene(scenes.SceneSpec("bf", 48, 40, 60, seed=seed, size_classes=((1.0, 0.5, 12.0),),
+                                            margin=20.0, depth_levels=8))
+    e = sc.extra
+    x, y = sc.splats[:, 0].astype(np.float64), sc.splats[:, 1].astype(np.float64)
+    pairs, ranges, amb = _brute_force_bins(e["s1"], e["s2"], e["theta"], x, y, sc.depths.astype(np.float64),
+                                           48, 40)
+    keep = np.array([i not in amb for i in range(sc.spec.n)])
+    b = orc.bin(sc.splats[keep], sc.depths[keep], 48, 40)
+    remap = np.flatnonzero(keep)
+    got = [(int(k >> np.uint64(32)), float(np.uint32(k & np.uint64(0xFFFFFFFF)).view(np.float32)), int(remap[v]))
+           for k, v in zip(b.keys, b.vals)]
+    want = [(t, float(np.float32(d)), i) for (t, d, i) in pairs if i not in amb]
+    assert got == want
+    # ranges from the brute force over the kept splats
+    tx_n, ty_n = 3, 3
+    exp_ranges = [[sum(1 for p in want if p[0] < t), sum(1 for p in want if p[0] <= t)] for t in range(tx_n * ty_n)]
+    assert b.ranges.tolist() == exp_ranges
+    # the sorted keys carry the float bits of each splat's depth
+    assert all(np.uint32(k & np.uint64(0xFFFFFFFF)) == sc.depths[keep][v].view(np.uint32)
+               for k, v in zip(b.keys, b.vals))
+
+
+def test_pair_count_on_tiny_scene_is_plausible(orc):
+    sc = scenes.make_scene("tiny")
+    b = orc.bin(sc.splats, sc.depths, 64, 64)
+    # 256 splats with s in [0.5, 8] px on a 4x4 tile grid: a few tiles per splat
+    assert 2.0 < b.num_pairs / 256 < 5.0
+    assert np.all(np.diff(b.keys.astype(np.uint64)) >= 0)
+
+
+# ----------------------------------------------------------------------------------------------- sort alone
+@pytest.mark.parametrize("n", [0, 1, 255, 256, 257, 1234, 100000])
+def test_sort_pairs_is_stable_sort(orc, n):
+    # sizes from the radix-scan parity list of the rasterize forward + adam kernel audit page (related finding
+    # "M4/A5 radix_scatter simd_ballot")
+    rng = np.random.default_rng(n)
+    keys = (rng.integers(0, 2500, n).astype(np.uint64) << np.uint64(32)) | \
+        rng.integers(0x3DCCCCCD, 0x41200000, n).astype(np.uint64)
+    vals = np.arange(n, dtype=np.uint32)
+    ko, vo = orc.sort_pairs(keys, vals)
+    order = np.argsort(keys, kind="stable")
+    assert np.array_equal(ko, keys[order]) and np.array_equal(vo, vals[order])
+
+
+def test_sort_pairs_ties_heavy(orc):
+    rng = np.random.default_rng(5000)
+    keys = rng.integers(0, 7, 5000).astype(np.uint64) << np.uint64(32)
+    vals = rng.permutation(5000).astype(np.uint32)
+    ko, vo = orc.sort_pairs(keys, vals)
+    order = np.argsort(keys, kind="stable")
+    assert np.array_equal(vo, vals[order])
