@@ -1,0 +1,122 @@
+// Fused Adam: every parameter group in one launch, four elements per thread with 16-byte loads and stores where the
+// group's arrays allow it. 28 bytes move per element (read grad, m, v, param; write m, v, param), so the kernel is
+// bound by HBM bandwidth. [rasterize forward + adam kernel audit page, section 2 "(f)": 5 groups, 59 elements per
+// splat, 28 B per element, 1,652 B per splat]
+//
+// Every operation is one IEEE fp32 operation in the order written (the file is compiled without contraction; HIP's
+// default division and square root are correctly rounded), so the step equals a plain fp32 evaluation.
+#include "gsr_internal.hpp"
+
+namespace gsr {
+namespace {
+
+constexpr uint32_t kThreads = 256;
+constexpr uint32_t kPerThread = 4;
+constexpr uint32_t kPerBlock = kThreads * kPerThread;
+
+struct AdamArgs {
+  float* param[GSR_ADAM_MAX_GROUPS];
+  const float* grad[GSR_ADAM_MAX_GROUPS];
+  float* m[GSR_ADAM_MAX_GROUPS];
+  float* v[GSR_ADAM_MAX_GROUPS];
+  uint64_t count[GSR_ADAM_MAX_GROUPS];
+  float lr[GSR_ADAM_MAX_GROUPS];
+  uint32_t vec4[GSR_ADAM_MAX_GROUPS];               // all four arrays 16-byte aligned
+  uint32_t block_start[GSR_ADAM_MAX_GROUPS + 1];    // first workgroup of each group
+  uint32_t n_groups;
+  float beta1, beta2, eps, bc1, bc2;
+};
+
+struct Hyper {
+  float b1, b2, omb1, omb2, eps, bc1, bc2, lr;
+};
+
+__device__ __forceinline__ void adam_one(float& p, float g, float& m, float& v, const Hyper& h) {
+  const float m_new = h.b1 * m + h.omb1 * g;
+  const float v_new = h.b2 * v + h.omb2 * (g * g);
+  const float m_hat = m_new / h.bc1;
+  const float v_hat = v_new / h.bc2;
+  const float denom = sqrtf(v_hat) + h.eps;
+  p = p - (h.lr * m_hat) / denom;
+  m = m_new;
+  v = v_new;
+}
+
+__global__ __launch_bounds__(kThreads) void k_adam(AdamArgs a) {
+  uint32_t q = 0;
+  while (q + 1 < a.n_groups && a.block_start[q + 1] <= blockIdx.x) ++q;
+  const uint64_t count = a.count[q];
+  const uint64_t i0 = uint64_t(blockIdx.x - a.block_start[q]) * kPerBlock + uint64_t(threadIdx.x) * kPerThread;
+  if (i0 >= count) return;
+  const Hyper h{a.beta1, a.beta2, 1.0f - a.beta1, 1.0f - a.beta2, a.eps, a.bc1, a.bc2, a.lr[q]};
+  float* __restrict__ P = a.param[q];
+  const float* __restrict__ G = a.grad[q];
+  float* __restrict__ M = a.m[q];
+  float* __restrict__ V = a.v[q];
+  if (a.vec4[q] && i0 + kPerThread <= count) {
+    float4 p = *reinterpret_cast<const float4*>(P + i0);
+    const float4 g = *reinterpret_cast<const float4*>(G + i0);
+    float4 m = *reinterpret_cast<const float4*>(M + i0);
+    float4 v = *reinterpret_cast<const float4*>(V + i0);
+    adam_one(p.x, g.x, m.x, v.x, h);
+    adam_one(p.y, g.y, m.y, v.y, h);
+    adam_one(p.z, g.z, m.z, v.z, h);
+    adam_one(p.w, g.w, m.w, v.w, h);
+    *reinterpret_cast<float4*>(P + i0) = p;
+    *reinterpret_cast<float4*>(M + i0) = m;
+    *reinterpret_cast<float4*>(V + i0) = v;
+  } else {
+    for (uint64_t i = i0; i < count && i < i0 + kPerThread; ++i) {
+      float p = P[i], m = M[i], v = V[i];
+      adam_one(p, G[i], m, v, h);
+      P[i] = p;
+      M[i] = m;
+      V[i] = v;
+    }
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+}  // namespace gsr
+
+using namespace gsr;
+
+extern "C" gsr_status gsr_adam_step(gsr_ctx* ctx, void* stream, const gsr_adam_group* groups, uint32_t n_groups,
+                                    float beta1, float beta2, float eps, float bc1, float bc2) {
+  if (!ctx) return GSR_EINVAL;
+  if (n_groups > GSR_ADAM_MAX_GROUPS)
+    return fail(ctx, GSR_EINVAL, "gsr_adam_step: %u groups, at most %d", n_groups, GSR_ADAM_MAX_GROUPS);
+  if (n_groups && !groups) return fail(ctx, GSR_EINVAL, "gsr_adam_step: null groups");
+  if (!(bc1 > 0.0f) || !(bc2 > 0.0f)) return fail(ctx, GSR_EINVAL, "gsr_adam_step: bias corrections must be > 0");
+  AdamArgs a{};
+  uint64_t blocks = 0;
+  a.n_groups = n_groups;
+  for (uint32_t q = 0; q < n_groups; ++q) {
+    const gsr_adam_group& g = groups[q];
+    if (g.count && (!g.param || !g.grad || !g.m || !g.v))
+      return fail(ctx, GSR_EINVAL, "gsr_adam_step: group %u has a null array", q);
+    a.param[q] = g.param;
+    a.grad[q] = g.grad;
+    a.m[q] = g.m;
+    a.v[q] = g.v;
+    a.count[q] = g.count;
+    a.lr[q] = g.lr;
+    a.vec4[q] = aligned16(g.param) && aligned16(g.grad) && aligned16(g.m) && aligned16(g.v);
+    a.block_start[q] = uint32_t(blocks);
+    blocks += (g.count + kPerBlock - 1) / kPerBlock;
+    if (blocks >= (uint64_t(1) << 31)) return fail(ctx, GSR_EOVERFLOW, "gsr_adam_step: too many elements");
+  }
+  a.block_start[n_groups] = uint32_t(blocks);
+  a.beta1 = beta1;
+  a.beta2 = beta2;
+  a.eps = eps;
+  a.bc1 = bc1;
+  a.bc2 = bc2;
+  if (blocks == 0) return GSR_OK;
+  gsr_status st = enter(ctx);
+  if (st) return st;
+  hipLaunchKernelGGL(k_adam, dim3(uint32_t(blocks)), dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
+  return check_launch(ctx, "gsr_adam_step");
+}

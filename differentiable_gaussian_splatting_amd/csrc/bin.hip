@@ -1,0 +1,304 @@
+// Binning: one (tile | depth) key per splat-tile overlap, a stable radix sort, per-tile ranges.
+// [C0 resident arena + C1 pass skip page, section 2 table, rows "C0" and "C1"]
+//
+// Two orderings with bit-identical results:
+//   GSR_BIN_KEY64   emit pairs splat by splat with key = (tile << 32) | depth bits, then sort the 64-bit keys
+//                   (32 depth bits + the tile id's significant bits).
+//   GSR_BIN_PRESORT sort the splats by depth bits first (n keys, not P), emit pairs in that order with the tile
+//                   id as key, then sort by the tile id's significant bits only. A stable sort of the splats by
+//                   (depth bits, index) followed by a stable sort of their pairs by tile gives each tile its pairs
+//                   in (depth bits, splat index) order, which is exactly the stable order of the 64-bit keys.
+// All extent arithmetic is one IEEE fp32 operation at a time (this file is compiled without contraction), with
+// correctly rounded division and square root, so the rectangles equal a plain fp32 evaluation.
+#include "gsr_internal.hpp"
+#include "scan_common.hpp"
+
+namespace gsr {
+namespace {
+
+constexpr uint32_t kThreads = 256;
+constexpr uint32_t kScanItems = 16;
+constexpr uint32_t kScanBlock = kThreads * kScanItems;
+
+struct Rect {
+  uint32_t tx0, ty0, w, h;  // w * h tiles; 0 when culled
+};
+
+// Validity test and the 3-sigma axis-aligned tile rectangle of one splat.
+__device__ __forceinline__ Rect tile_rect(const float* __restrict__ sp, float depth, uint32_t tiles_x,
+                                          uint32_t tiles_y) {
+  const Rect none{0, 0, 0, 0};
+  float v[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) v[k] = sp[k];
+  bool finite = __builtin_isfinite(depth);
+#pragma unroll
+  for (int k = 0; k < 9; ++k) finite = finite && __builtin_isfinite(v[k]);
+  if (!finite || !(depth > 0.0f)) return none;
+  const float x = v[0], y = v[1], a = v[2], b = v[3], c = v[4], o = v[8];
+  if (!(o >= 0.0f && o <= 1.0f) || !(a > 0.0f)) return none;
+  const float ac = a * c;
+  const float bb = b * b;
+  const float det = ac - bb;
+  if (!(det > 0.0f)) return none;
+  const float rx = 3.0f * sqrtf(c / det);
+  const float ry = 3.0f * sqrtf(a / det);
+  const float fx0 = floorf((x - rx) / 16.0f);
+  const float fx1 = floorf((x + rx) / 16.0f);
+  const float fy0 = floorf((y - ry) / 16.0f);
+  const float fy1 = floorf((y + ry) / 16.0f);
+  const float cx0 = (0.0f < fx0) ? fx0 : 0.0f;
+  const float mx = float(tiles_x - 1), my = float(tiles_y - 1);
+  const float cx1 = (fx1 < mx) ? fx1 : mx;
+  const float cy0 = (0.0f < fy0) ? fy0 : 0.0f;
+  const float cy1 = (fy1 < my) ? fy1 : my;
+  if (cx0 > cx1 || cy0 > cy1) return none;
+  const uint32_t tx0 = uint32_t(cx0), ty0 = uint32_t(cy0);
+  return Rect{tx0, ty0, uint32_t(cx1) - tx0 + 1, uint32_t(cy1) - ty0 + 1};
+}
+
+__global__ __launch_bounds__(kThreads) void k_depth_keys(const float* __restrict__ depths, uint32_t n,
+                                                         uint64_t* __restrict__ keys, uint32_t* __restrict__ idx) {
+  const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  keys[i] = __float_as_uint(depths[i]);
+  idx[i] = i;
+}
+
+// counts[j] = tiles overlapped by splat order[j] (order = identity when null).
+__global__ __launch_bounds__(kThreads) void k_count(const float* __restrict__ splats, const float* __restrict__ depths,
+                                                    uint32_t n, const uint32_t* __restrict__ order,
+                                                    uint32_t tiles_x, uint32_t tiles_y,
+                                                    uint32_t* __restrict__ counts) {
+  const uint32_t j = blockIdx.x * kThreads + threadIdx.x;
+  if (j >= n) return;
+  const uint32_t i = order ? order[j] : j;
+  if (i >= n) {  // not reachable with a permutation in `order`; guards the reads below
+    counts[j] = 0;
+    return;
+  }
+  const Rect r = tile_rect(splats + size_t(i) * 9, depths[i], tiles_x, tiles_y);
+  counts[j] = r.w * r.h;
+}
+
+// Three-launch exclusive scan of uint32 counts into uint64 offsets; offsets[n] = total.
+__global__ __launch_bounds__(kThreads) void k_scan_reduce(const uint32_t* __restrict__ counts, uint32_t n,
+                                                          uint64_t* __restrict__ part) {
+  __shared__ uint64_t smem[kThreads / kWave];
+  const uint64_t base = uint64_t(blockIdx.x) * kScanBlock;
+  uint64_t sum = 0;
+  for (uint32_t i = 0; i < kScanItems; ++i) {
+    const uint64_t j = base + uint64_t(i) * kThreads + threadIdx.x;
+    if (j < n) sum += counts[j];
+  }
+  uint64_t total;
+  block_exclusive_scan<uint64_t, kThreads>(sum, &total, smem);
+  if (threadIdx.x == 0) part[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(kThreads) void k_scan_top(uint64_t* __restrict__ part, uint32_t nb,
+                                                       uint64_t* __restrict__ offsets, uint32_t n) {
+  __shared__ uint64_t smem[kThreads / kWave];
+  uint64_t carry = 0;
+  for (uint32_t c = 0; c < nb; c += kThreads) {
+    const uint32_t j = c + threadIdx.x;
+    const uint64_t v = j < nb ? part[j] : 0;
+    uint64_t total;
+    const uint64_t ex = block_exclusive_scan<uint64_t, kThreads>(v, &total, smem);
+    if (j < nb) part[j] = carry + ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) {
+    part[nb] = carry;
+    offsets[n] = carry;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_scan_down(const uint32_t* __restrict__ counts, uint32_t n,
+                                                        const uint64_t* __restrict__ part,
+                                                        uint64_t* __restrict__ offsets) {
+  __shared__ uint64_t smem[kThreads / kWave];
+  const uint64_t base = uint64_t(blockIdx.x) * kScanBlock + uint64_t(threadIdx.x) * kScanItems;
+  uint32_t c[kScanItems];
+  uint64_t sum = 0;
+#pragma unroll
+  for (uint32_t i = 0; i < kScanItems; ++i) {
+    c[i] = (base + i < n) ? counts[base + i] : 0u;
+    sum += c[i];
+  }
+  uint64_t run = part[blockIdx.x] + block_exclusive_scan<uint64_t, kThreads>(sum, nullptr, smem);
+#pragma unroll
+  for (uint32_t i = 0; i < kScanItems; ++i) {
+    if (base + i < n) offsets[base + i] = run;
+    run += c[i];
+  }
+}
+
+// Emission. Workgroup b owns emission positions [256 b, 256 b + 256) and the contiguous output range of their
+// pairs; its threads walk that range in order (coalesced stores) and find each pair's splat by binary search.
+// Inside a splat the tiles go row by row. key_mode 0: (tile << 32) | depth bits; 1: tile id only.
+__global__ __launch_bounds__(kThreads) void k_emit(const float* __restrict__ splats, const float* __restrict__ depths,
+                                                   uint32_t n, const uint32_t* __restrict__ order, uint32_t tiles_x,
+                                                   uint32_t tiles_y, const uint64_t* __restrict__ offsets,
+                                                   int key_mode, uint64_t num_pairs, uint64_t* __restrict__ keys,
+                                                   uint32_t* __restrict__ vals) {
+  __shared__ uint64_t s_off[kThreads + 1];
+  __shared__ uint32_t s_tx0[kThreads], s_ty0[kThreads], s_w[kThreads], s_idx[kThreads], s_dbits[kThreads];
+  const uint32_t j = blockIdx.x * kThreads + threadIdx.x;
+  const uint32_t jl = min(j, n);
+  s_off[threadIdx.x] = offsets[jl];
+  if (threadIdx.x == 0) s_off[kThreads] = offsets[min(blockIdx.x * kThreads + kThreads, n)];
+  if (j < n) {
+    uint32_t i = order ? order[j] : j;
+    if (i >= n) i = 0;  // not reachable with a permutation in `order`; its count is 0 then (see k_count)
+    const Rect r = tile_rect(splats + size_t(i) * 9, depths[i], tiles_x, tiles_y);
+    s_tx0[threadIdx.x] = r.tx0;
+    s_ty0[threadIdx.x] = r.ty0;
+    s_w[threadIdx.x] = r.w ? r.w : 1u;
+    s_idx[threadIdx.x] = i;
+    s_dbits[threadIdx.x] = __float_as_uint(depths[i]);
+  }
+  __syncthreads();
+  const uint64_t begin = s_off[0], end = min(s_off[kThreads], num_pairs);
+  for (uint64_t p = begin + threadIdx.x; p < end; p += kThreads) {
+    // largest q with s_off[q] <= p
+    uint32_t lo = 0, hi = kThreads;  // invariant: s_off[lo] <= p < s_off[hi]
+    while (hi - lo > 1) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (s_off[mid] <= p)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const uint32_t k = uint32_t(p - s_off[lo]);
+    const uint32_t w = s_w[lo];
+    const uint32_t ty = s_ty0[lo] + k / w, tx = s_tx0[lo] + k % w;
+    const uint64_t tile = uint64_t(ty) * tiles_x + tx;
+    keys[p] = key_mode == 0 ? ((tile << 32) | s_dbits[lo]) : tile;
+    vals[p] = s_idx[lo];
+  }
+}
+
+// Per-tile ranges from the sorted keys; thread i in [0, P] looks at the boundary between pairs i-1 and i.
+// For the presort scheme it also writes the final 64-bit keys (tile << 32 | depth bits) to keys_final.
+__global__ __launch_bounds__(kThreads) void k_ranges(const uint64_t* __restrict__ keys,
+                                                     const uint32_t* __restrict__ vals, uint32_t P,
+                                                     uint32_t num_tiles, int tile_in_low_bits,
+                                                     const float* __restrict__ depths, uint32_t n,
+                                                     uint64_t* __restrict__ keys_final,
+                                                     uint32_t* __restrict__ ranges) {
+  const uint64_t i = uint64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (i > P) return;
+  auto tile_of = [&](uint64_t k) -> int64_t { return tile_in_low_bits ? int64_t(k) : int64_t(k >> 32); };
+  const int64_t prev = i == 0 ? -1 : tile_of(keys[i - 1]);
+  const int64_t cur = i == P ? int64_t(num_tiles) : tile_of(keys[i]);
+  if (cur != prev) {
+    for (int64_t t = prev + 1; t <= cur && t < int64_t(num_tiles); ++t) ranges[2 * t] = uint32_t(i);
+    for (int64_t t = prev < 0 ? 0 : prev; t < cur && t < int64_t(num_tiles); ++t) ranges[2 * t + 1] = uint32_t(i);
+  }
+  if (keys_final && i < P) {
+    const uint32_t v = vals[i];
+    keys_final[i] = (uint64_t(cur) << 32) | (v < n ? __float_as_uint(depths[v]) : 0u);
+  }
+}
+
+uint32_t bits_of(uint64_t v) {
+  uint32_t b = 0;
+  for (; v; v >>= 1) ++b;
+  return b;
+}
+
+uint32_t grid_for(uint64_t items, uint32_t per_block) { return uint32_t((items + per_block - 1) / per_block); }
+
+}  // namespace
+}  // namespace gsr
+
+using namespace gsr;
+
+extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, const float* depths, uint32_t n,
+                              uint32_t width, uint32_t height, gsr_bins* out) {
+  if (!ctx || !out) return GSR_EINVAL;
+  if (width == 0 || height == 0) return fail(ctx, GSR_EINVAL, "gsr_bin: empty image %ux%u", width, height);
+  if (n && (!splats || !depths)) return fail(ctx, GSR_EINVAL, "gsr_bin: null splats or depths");
+  const uint32_t tiles_x = (width + kTile - 1) / kTile, tiles_y = (height + kTile - 1) / kTile;
+  const uint64_t num_tiles = uint64_t(tiles_x) * tiles_y;
+  if (num_tiles >= (uint64_t(1) << 32)) return fail(ctx, GSR_EINVAL, "gsr_bin: too many tiles");
+  gsr_status st = enter(ctx);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Arena& a = ctx->arena;
+  const bool presort = ctx->bin_scheme == GSR_BIN_PRESORT;
+
+  if ((st = grow(ctx, a.ranges, size_t(num_tiles) * 8))) return st;
+  if ((st = grow(ctx, a.counts, size_t(n + 1) * 4)) || (st = grow(ctx, a.offsets, size_t(n + 1) * 8))) return st;
+  const uint32_t nb_scan = grid_for(n, kScanBlock);
+  if ((st = grow(ctx, a.scan_part, size_t(nb_scan + 1) * 8))) return st;
+
+  const uint32_t* order = nullptr;
+  if (presort && n) {
+    if ((st = grow(ctx, a.order, size_t(n) * 8)) || (st = grow(ctx, a.order_alt, size_t(n) * 8)) ||
+        (st = grow(ctx, a.order_vals, size_t(n) * 4)) || (st = grow(ctx, a.order_vals_alt, size_t(n) * 4)))
+      return st;
+    uint64_t* ok = static_cast<uint64_t*>(a.order.ptr);
+    uint32_t* ov = static_cast<uint32_t*>(a.order_vals.ptr);
+    hipLaunchKernelGGL(k_depth_keys, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, depths, n, ok, ov);
+    // 4 passes (even): the sorted result lands back in (order, order_vals)
+    st = radix_sort_launch(ctx, s, ok, ov, n, 32, ok, ov, static_cast<uint64_t*>(a.order_alt.ptr),
+                           static_cast<uint32_t*>(a.order_vals_alt.ptr));
+    if (st) return st;
+    order = ov;
+  }
+
+  uint32_t* counts = static_cast<uint32_t*>(a.counts.ptr);
+  uint64_t* offsets = static_cast<uint64_t*>(a.offsets.ptr);
+  uint64_t* part = static_cast<uint64_t*>(a.scan_part.ptr);
+  if (n) {
+    hipLaunchKernelGGL(k_count, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats, depths, n, order, tiles_x,
+                       tiles_y, counts);
+    hipLaunchKernelGGL(k_scan_reduce, dim3(nb_scan), dim3(kThreads), 0, s, counts, n, part);
+  }
+  hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(kThreads), 0, s, part, nb_scan, offsets, n);
+  if (n) hipLaunchKernelGGL(k_scan_down, dim3(nb_scan), dim3(kThreads), 0, s, counts, n, part, offsets);
+  if ((st = check_launch(ctx, "gsr_bin count/scan"))) return st;
+
+  // The one wait of the call: the pair count sizes the arena.
+  hipError_t e = hipMemcpyAsync(a.host_total, offsets + n, sizeof(uint64_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "gsr_bin pair count readback");
+  const uint64_t P = *a.host_total;
+  if (P >= (uint64_t(1) << 32)) return fail(ctx, GSR_EOVERFLOW, "gsr_bin: %llu pairs exceed 2^32 - 1",
+                                            (unsigned long long)P);
+
+  for (int q = 0; q < 2; ++q)
+    if ((st = grow(ctx, a.keys[q], size_t(P) * 8)) || (st = grow(ctx, a.vals[q], size_t(P) * 4))) return st;
+  uint64_t* k0 = static_cast<uint64_t*>(a.keys[0].ptr);
+  uint32_t* v0 = static_cast<uint32_t*>(a.vals[0].ptr);
+  if (n)
+    hipLaunchKernelGGL(k_emit, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats, depths, n, order, tiles_x,
+                       tiles_y, offsets, presort ? 1 : 0, P, k0, v0);
+
+  const uint32_t key_bits = presort ? bits_of(num_tiles - 1) : 32 + bits_of(num_tiles - 1);
+  int res = 0;
+  if (key_bits > 0 && P > 0) {
+    res = (sort_passes(key_bits) & 1u) ? 1 : 0;  // odd pass count: result in buffer 1
+    st = radix_sort_launch(ctx, s, k0, v0, P, key_bits, static_cast<uint64_t*>(a.keys[res].ptr),
+                           static_cast<uint32_t*>(a.vals[res].ptr), static_cast<uint64_t*>(a.keys[1 - res].ptr),
+                           static_cast<uint32_t*>(a.vals[1 - res].ptr));
+    if (st) return st;
+  }
+  uint64_t* sorted_k = static_cast<uint64_t*>(a.keys[res].ptr);
+  uint32_t* sorted_v = static_cast<uint32_t*>(a.vals[res].ptr);
+  uint64_t* final_k = presort ? (ctx->bin_keys ? static_cast<uint64_t*>(a.keys[1 - res].ptr) : nullptr) : sorted_k;
+  uint32_t* ranges = static_cast<uint32_t*>(a.ranges.ptr);
+  hipLaunchKernelGGL(k_ranges, dim3(grid_for(P + 1, kThreads)), dim3(kThreads), 0, s, sorted_k, sorted_v,
+                     uint32_t(P), uint32_t(num_tiles), presort ? 1 : 0, depths, n, presort ? final_k : nullptr,
+                     ranges);
+  if ((st = check_launch(ctx, "gsr_bin emit/sort/ranges"))) return st;
+  out->keys = final_k;
+  out->vals = sorted_v;
+  out->ranges = ranges;
+  out->num_pairs = uint32_t(P);
+  out->tiles_x = tiles_x;
+  out->tiles_y = tiles_y;
+  return GSR_OK;
+}

@@ -1,0 +1,191 @@
+// Context, arena and error plumbing of libgsr.
+#include <algorithm>
+#include <cstring>
+
+#include "gsr_internal.hpp"
+
+namespace gsr {
+
+gsr_status fail(gsr_ctx* ctx, gsr_status st, const char* fmt, ...) {
+  if (ctx) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    ctx->error = buf;
+  }
+  return st;
+}
+
+gsr_status hip_fail(gsr_ctx* ctx, hipError_t e, const char* what) {
+  return fail(ctx, GSR_EHIP, "%s: HIP error %d (%s)", what, int(e), hipGetErrorName(e));
+}
+
+gsr_status enter(gsr_ctx* ctx) {
+  hipError_t e = hipSetDevice(ctx->device);
+  if (e != hipSuccess) return hip_fail(ctx, e, "hipSetDevice");
+  return GSR_OK;
+}
+
+gsr_status grow(gsr_ctx* ctx, DevBuf& b, size_t bytes) {
+  if (bytes <= b.bytes) return GSR_OK;
+  size_t want = std::max<size_t>({bytes, b.bytes + b.bytes / 2, size_t(1) << 16});
+  void* p = nullptr;
+  hipError_t e = hipMalloc(&p, want);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky allocation error; the old buffer stays valid
+    if (want > bytes) {       // retry at the exact size before giving up
+      want = bytes;
+      e = hipMalloc(&p, want);
+      if (e != hipSuccess) (void)hipGetLastError();
+    }
+    if (e != hipSuccess)
+      return fail(ctx, GSR_ENOMEM, "device arena: could not grow a buffer to %zu bytes (%s)", bytes,
+                  hipGetErrorName(e));
+  }
+  if (b.ptr) {
+    // The old buffer may still be read by queued work on some stream: wait for the device before freeing it.
+    hipError_t se = hipDeviceSynchronize();
+    if (se != hipSuccess) {
+      (void)hipFree(p);
+      return hip_fail(ctx, se, "device arena: synchronize before growing");
+    }
+    (void)hipFree(b.ptr);
+  }
+  b.ptr = p;
+  b.bytes = want;
+  return GSR_OK;
+}
+
+gsr_status check_launch(gsr_ctx* ctx, const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(ctx, e, what);
+  return GSR_OK;
+}
+
+static void release(DevBuf& b) {
+  if (b.ptr) (void)hipFree(b.ptr);
+  b.ptr = nullptr;
+  b.bytes = 0;
+}
+
+}  // namespace gsr
+
+using namespace gsr;
+
+extern "C" {
+
+gsr_status gsr_create(gsr_ctx** out, int hip_device) {
+  if (!out) return GSR_EINVAL;
+  *out = nullptr;
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess) return GSR_EHIP;
+  if (hip_device < 0 || hip_device >= count) return GSR_EINVAL;
+  gsr_ctx* ctx = new (std::nothrow) gsr_ctx();
+  if (!ctx) return GSR_ENOMEM;
+  ctx->device = hip_device;
+  if (enter(ctx) != GSR_OK) {
+    delete ctx;
+    return GSR_EHIP;
+  }
+  e = hipHostMalloc(reinterpret_cast<void**>(&ctx->arena.host_total), sizeof(uint64_t), hipHostMallocDefault);
+  if (e != hipSuccess) {
+    delete ctx;
+    return GSR_ENOMEM;
+  }
+  *ctx->arena.host_total = 0;
+  *out = ctx;
+  return GSR_OK;
+}
+
+void gsr_destroy(gsr_ctx* ctx) {
+  if (!ctx) return;
+  (void)hipSetDevice(ctx->device);
+  Arena& a = ctx->arena;
+  for (DevBuf* b : {&a.keys[0], &a.keys[1], &a.vals[0], &a.vals[1], &a.counts, &a.offsets, &a.order, &a.order_alt,
+                    &a.order_vals, &a.order_vals_alt, &a.scan_part, &a.hist, &a.digit_tot, &a.ranges})
+    release(*b);
+  if (a.host_total) (void)hipHostFree(a.host_total);
+  delete ctx;
+}
+
+const char* gsr_last_error(const gsr_ctx* ctx) { return ctx ? ctx->error.c_str() : "null context"; }
+
+gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value) {
+  if (!ctx) return GSR_EINVAL;
+  switch (option) {
+    case GSR_OPT_BIN_SCHEME:
+      if (value != GSR_BIN_PRESORT && value != GSR_BIN_KEY64)
+        return fail(ctx, GSR_EINVAL, "gsr_set_option: unknown bin scheme %lld", (long long)value);
+      ctx->bin_scheme = int32_t(value);
+      return GSR_OK;
+    case GSR_OPT_BIN_KEYS:
+      if (value != 0 && value != 1) return fail(ctx, GSR_EINVAL, "gsr_set_option: bin keys must be 0 or 1");
+      ctx->bin_keys = value != 0;
+      return GSR_OK;
+    default:
+      return fail(ctx, GSR_EINVAL, "gsr_set_option: unknown option %d", int(option));
+  }
+}
+
+gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats) {
+  if (!ctx) return GSR_EINVAL;
+  if (max_pairs >= (uint64_t(1) << 32)) return fail(ctx, GSR_EOVERFLOW, "gsr_reserve: max_pairs >= 2^32");
+  gsr_status st = enter(ctx);
+  if (st) return st;
+  Arena& a = ctx->arena;
+  const uint64_t ns = uint64_t(max_splats) + 1;
+  const uint64_t nb = std::max<uint64_t>(sort_blocks(std::max<uint64_t>(max_pairs, ns)), 1);
+  struct {
+    DevBuf* b;
+    size_t bytes;
+  } plan[] = {
+      {&a.keys[0], size_t(max_pairs) * 8}, {&a.keys[1], size_t(max_pairs) * 8},
+      {&a.vals[0], size_t(max_pairs) * 4}, {&a.vals[1], size_t(max_pairs) * 4},
+      {&a.counts, size_t(ns) * 4},         {&a.offsets, size_t(ns + 1) * 8},
+      {&a.order, size_t(ns) * 8},          {&a.order_alt, size_t(ns) * 8},
+      {&a.order_vals, size_t(ns) * 4},     {&a.order_vals_alt, size_t(ns) * 4},
+      {&a.scan_part, size_t(nb + 1) * 8},  {&a.hist, size_t(nb) * 256 * 4},
+      {&a.digit_tot, 256 * 4},
+  };
+  for (auto& p : plan)
+    if ((st = grow(ctx, *p.b, p.bytes))) return st;
+  return GSR_OK;
+}
+
+gsr_status gsr_bins_copy(gsr_ctx* ctx, void* stream, const gsr_bins* bins, uint64_t* keys, uint32_t* vals,
+                         uint32_t* ranges) {
+  if (!ctx || !bins) return GSR_EINVAL;
+  gsr_status st = enter(ctx);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t P = bins->num_pairs;
+  const size_t T = size_t(bins->tiles_x) * bins->tiles_y;
+  if (keys && P) {
+    if (!bins->keys) return fail(ctx, GSR_EINVAL, "gsr_bins_copy: the bins carry no keys");
+    hipError_t e = hipMemcpyAsync(keys, bins->keys, P * 8, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "gsr_bins_copy keys");
+  }
+  if (vals && P) {
+    hipError_t e = hipMemcpyAsync(vals, bins->vals, P * 4, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "gsr_bins_copy vals");
+  }
+  if (ranges && T) {
+    hipError_t e = hipMemcpyAsync(ranges, bins->ranges, T * 8, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "gsr_bins_copy ranges");
+  }
+  return GSR_OK;
+}
+
+uint32_t gsr_radix_pass_count(uint64_t num_tiles, uint32_t digit_bits) {
+  if (digit_bits != 4 && digit_bits != 8) return 0;
+  uint32_t tile_bits = 0;
+  for (uint64_t v = num_tiles ? num_tiles - 1 : 0; v; v >>= 1) ++tile_bits;
+  const uint32_t all = 64 / digit_bits, depth = 32 / digit_bits;
+  const uint32_t p = depth + (tile_bits + digit_bits - 1) / digit_bits;
+  return p < all ? p : all;
+}
+
+}  // extern "C"

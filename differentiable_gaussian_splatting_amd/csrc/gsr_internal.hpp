@@ -1,0 +1,80 @@
+// Internal declarations shared by the libgsr translation units: the context, its grow-only device arena, error
+// reporting, and the launch helpers one file provides to another.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "gsr.h"
+
+namespace gsr {
+
+constexpr uint32_t kTile = 16;          // 16x16 pixel tiles
+constexpr uint32_t kTilePixels = 256;   // one workgroup of 4 wave64 per tile in the raster kernels
+constexpr uint32_t kWave = 64;
+
+// One device allocation that only ever grows. Contents are not preserved across growth.
+struct DevBuf {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+
+// Everything gsr_bin and gsr_radix_sort keep between calls. Sized by the largest call seen so far (C0 resident
+// arena: capacity only grows, so steady-state iterations allocate nothing).
+struct Arena {
+  DevBuf keys[2];     // uint64 [pair capacity], ping-pong
+  DevBuf vals[2];     // uint32 [pair capacity], ping-pong
+  DevBuf counts;      // uint32 [splat capacity] pairs per splat (in emission order)
+  DevBuf offsets;     // uint64 [splat capacity + 1] exclusive scan of counts
+  DevBuf order;       // uint64 [splat capacity] depth keys / splat order for the presort scheme (x2 for ping-pong)
+  DevBuf order_alt;   // uint64 [splat capacity]
+  DevBuf order_vals;  // uint32 [splat capacity]
+  DevBuf order_vals_alt;
+  DevBuf scan_part;   // uint64 [scan blocks] partial sums of the count scan
+  DevBuf hist;        // uint32 [256 * sort blocks] per-block digit counts, then their per-digit scan
+  DevBuf digit_tot;   // uint32 [256] per-digit totals of the current pass
+  DevBuf ranges;      // uint32 [2 * tiles]
+  uint64_t* host_total = nullptr;  // pinned host word for the one pair-count readback
+};
+
+}  // namespace gsr
+
+struct gsr_ctx {
+  int device = 0;
+  std::string error;
+  gsr::Arena arena;
+  int32_t bin_scheme = GSR_BIN_PRESORT;
+  bool bin_keys = true;
+};
+
+namespace gsr {
+
+// Records a message on ctx and returns `st`.
+gsr_status fail(gsr_ctx* ctx, gsr_status st, const char* fmt, ...);
+
+// Maps a HIP error (this call's or an earlier asynchronous one) to GSR_EHIP with its name.
+gsr_status hip_fail(gsr_ctx* ctx, hipError_t e, const char* what);
+
+// Makes ctx's device current for this thread.
+gsr_status enter(gsr_ctx* ctx);
+
+// Grows `b` to at least `bytes` (grow-only; factor 1.5 over the previous size, floor 64 KiB).
+gsr_status grow(gsr_ctx* ctx, DevBuf& b, size_t bytes);
+
+// Checks for launch errors after queuing kernels.
+gsr_status check_launch(gsr_ctx* ctx, const char* what);
+
+// Radix sort (sort.hip). Sorts n (key, value) pairs stably by the low key_bits bits, 8 bits per pass.
+// The result lands in (keys_out, vals_out); (tmp_keys, tmp_vals) are scratch of n elements. keys_in may equal
+// keys_out only if the pass count is even... callers pass distinct buffers. hist must hold 256 * sort_blocks(n).
+uint32_t sort_blocks(uint64_t n);
+uint32_t sort_passes(uint32_t key_bits);
+gsr_status radix_sort_launch(gsr_ctx* ctx, hipStream_t s, const uint64_t* keys_in, const uint32_t* vals_in,
+                             uint64_t n, uint32_t key_bits, uint64_t* keys_out, uint32_t* vals_out,
+                             uint64_t* tmp_keys, uint32_t* tmp_vals);
+
+}  // namespace gsr

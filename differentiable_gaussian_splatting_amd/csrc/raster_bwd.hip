@@ -1,0 +1,180 @@
+// Backward rasterization: one 256-thread workgroup per 16x16 tile, one pixel per thread, same LDS staging as the
+// forward. Each lane replays its forward decisions (the shared evaluate()) up to its last contributor and forms
+// the 9 gradient terms of each splat it composited. Per splat and wave:
+//   - if no lane of the wave composited it, nothing is reduced or added (W1 warp sparse skip + exp-skip page,
+//     section 1 row "W1a": an all-invalid wave would only add +0.0);
+//   - otherwise the 9 terms are summed inside each 16-lane row with DPP (xor 1, xor 2, half-mirror, mirror) and the
+//     four row sums are added into the workgroup's LDS accumulator of that splat;
+// after each batch one thread per splat adds the accumulated 9 values to splats_grad with global float atomics.
+// The per-pixel terms follow the forward-order form after = C_final - acc - mine of the M3 per-splat backward page
+// (section 1, rows "brush's actual structure" and "differences").
+#include "gsr_internal.hpp"
+#include "raster_common.hpp"
+
+namespace gsr {
+namespace {
+
+constexpr uint32_t kGrads = 9;
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false);
+  return v + __int_as_float(moved);
+}
+
+// Sum over the 16 lanes of each DPP row, left in every lane of the row.
+__device__ __forceinline__ float row_sum(float v) {
+  v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  v = dpp_add<0x141>(v);  // row_half_mirror: lane i <-> 7 - i inside each half row
+  v = dpp_add<0x140>(v);  // row_mirror: lane i <-> 15 - i
+  return v;
+}
+
+__global__ __launch_bounds__(kTilePixels) void k_zero(float* __restrict__ p, uint64_t count) {
+  const uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = 0.0f;
+}
+
+__global__ __launch_bounds__(kTilePixels) void k_backward(
+    const float* __restrict__ splats, uint32_t n, const uint32_t* __restrict__ vals,
+    const uint32_t* __restrict__ ranges, uint32_t num_pairs, uint32_t tiles_x, uint32_t width, uint32_t height,
+    const float4* __restrict__ out_rgba, const uint32_t* __restrict__ last_contrib, const float4* __restrict__ v_out,
+    float* __restrict__ splats_grad) {
+  __shared__ StagedSplat s_sp[kTilePixels];
+  __shared__ float s_acc[kTilePixels][kGrads];
+  __shared__ uint32_t s_max_last;
+  const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1);
+  const uint32_t tile = blockIdx.x;
+  const uint32_t px = (tile % tiles_x) * kTile + (tid & (kTile - 1));
+  const uint32_t py = (tile / tiles_x) * kTile + (tid / kTile);
+  const bool inside = px < width && py < height;
+  const uint32_t start = min(ranges[2 * tile], num_pairs);
+  const uint32_t end = max(start, min(ranges[2 * tile + 1], num_pairs));
+  const float cx = float(px) + 0.5f, cy = float(py) + 0.5f;
+
+  uint32_t last = 0;
+  float Cr = 0.0f, Cg = 0.0f, Cb = 0.0f, gr = 0.0f, gg = 0.0f, gb = 0.0f;
+  if (inside) {
+    const size_t p = size_t(py) * width + px;
+    last = min(last_contrib[p], end - start);
+    const float4 c = out_rgba[p];
+    const float4 g = v_out[p];
+    Cr = c.x;
+    Cg = c.y;
+    Cb = c.z;
+    gr = g.x;
+    gg = g.y;
+    gb = g.z;
+  }
+  if (tid == 0) s_max_last = 0;
+#pragma unroll
+  for (uint32_t q = 0; q < kGrads; ++q) s_acc[tid][q] = 0.0f;
+  // the wave's loop bound: the largest last contributor among its lanes
+  uint32_t wave_last = last;
+  for (uint32_t off = 32; off > 0; off >>= 1) wave_last = max(wave_last, uint32_t(__shfl_xor(int(wave_last), off)));
+  __syncthreads();
+  if (lane == 0) atomicMax(&s_max_last, wave_last);
+  __syncthreads();
+  const uint32_t stop = start + s_max_last;
+
+  float T = 1.0f, ar = 0.0f, ag = 0.0f, ab = 0.0f;
+  for (uint32_t b0 = start; b0 < stop; b0 += kTilePixels) {
+    const uint32_t k = b0 + tid;
+    if (k < stop) s_sp[tid] = stage_splat(splats, vals[k], n);
+    __syncthreads();
+    const uint32_t cnt = min(kTilePixels, stop - b0);
+    const uint32_t rel0 = b0 - start;
+    const uint32_t wcnt = wave_last > rel0 ? min(cnt, wave_last - rel0) : 0u;
+    for (uint32_t j = 0; j < wcnt; ++j) {
+      const StagedSplat& s = s_sp[j];
+      float d[kGrads];
+#pragma unroll
+      for (uint32_t q = 0; q < kGrads; ++q) d[q] = 0.0f;
+      bool contrib = false;
+      Eval e;
+      if (rel0 + j < last && evaluate(s, cx, cy, e)) {
+        contrib = true;
+        const float w = e.alpha * T;
+        d[5] = w * gr;
+        d[6] = w * gg;
+        d[7] = w * gb;
+        const float one_m = 1.0f - e.alpha;
+        const float mr = s.r * w, mg = s.g * w, mb = s.bl * w;
+        const float after_r = (Cr - ar) - mr;
+        const float after_g = (Cg - ag) - mg;
+        const float after_b = (Cb - ab) - mb;
+        const float dl_da = (gr * (s.r * T - after_r / one_m) + gg * (s.g * T - after_g / one_m)) +
+                            gb * (s.bl * T - after_b / one_m);
+        if (e.oG < kAlphaMax) {
+          d[8] = dl_da * e.G;
+          const float dl_ds = -(dl_da * e.oG);
+          d[2] = dl_ds * (0.5f * e.dx * e.dx);
+          d[3] = dl_ds * (e.dx * e.dy);
+          d[4] = dl_ds * (0.5f * e.dy * e.dy);
+          d[0] = dl_ds * -(s.a * e.dx + s.b * e.dy);
+          d[1] = dl_ds * -(s.b * e.dx + s.c * e.dy);
+        }
+        ar = ar + mr;
+        ag = ag + mg;
+        ab = ab + mb;
+        T = T * one_m;
+      }
+      if (__ballot(contrib) == 0) continue;  // the whole wave skipped this splat
+#pragma unroll
+      for (uint32_t q = 0; q < kGrads; ++q) {
+        const float row = row_sum(d[q]);
+        if ((lane & (kTile - 1)) == 0) atomicAdd(&s_acc[j][q], row);
+      }
+    }
+    __syncthreads();
+    if (tid < cnt) {
+      const uint32_t idx = s_sp[tid].idx;
+#pragma unroll
+      for (uint32_t q = 0; q < kGrads; ++q) {
+        const float v = s_acc[tid][q];
+        if (v != 0.0f && idx != 0xFFFFFFFFu) atomicAdd(splats_grad + size_t(idx) * kGrads + q, v);
+        s_acc[tid][q] = 0.0f;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+}  // namespace gsr
+
+using namespace gsr;
+
+extern "C" gsr_status gsr_render_backward(gsr_ctx* ctx, void* stream, const float* splats, uint32_t n,
+                                          const gsr_bins* bins, uint32_t width, uint32_t height,
+                                          const float* out_rgba, const float* final_T,
+                                          const uint32_t* last_contrib, const float* v_out, float* splats_grad) {
+  if (!ctx || !bins) return GSR_EINVAL;
+  if (width == 0 || height == 0) return fail(ctx, GSR_EINVAL, "gsr_render_backward: empty image");
+  const uint32_t tiles_x = (width + kTile - 1) / kTile, tiles_y = (height + kTile - 1) / kTile;
+  if (bins->tiles_x != tiles_x || bins->tiles_y != tiles_y)
+    return fail(ctx, GSR_EINVAL, "gsr_render_backward: bins are for %ux%u tiles, image needs %ux%u", bins->tiles_x,
+                bins->tiles_y, tiles_x, tiles_y);
+  if (uint64_t(n) * kGrads >= (uint64_t(1) << 32))
+    return fail(ctx, GSR_EOVERFLOW, "gsr_render_backward: n * 9 >= 2^32");
+  if (!bins->ranges || (bins->num_pairs && !bins->vals) || (n && (!splats || !splats_grad)) || !out_rgba ||
+      !final_T || !last_contrib || !v_out)
+    return fail(ctx, GSR_EINVAL, "gsr_render_backward: null pointer");
+  if (reinterpret_cast<uintptr_t>(out_rgba) % 16 || reinterpret_cast<uintptr_t>(v_out) % 16)
+    return fail(ctx, GSR_EINVAL, "gsr_render_backward: out_rgba and v_out must be 16-byte aligned");
+  const uint64_t num_tiles = uint64_t(tiles_x) * tiles_y;
+  if (num_tiles >= (uint64_t(1) << 31)) return fail(ctx, GSR_EINVAL, "gsr_render_backward: too many tiles");
+  gsr_status st = enter(ctx);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint64_t count = uint64_t(n) * kGrads;
+  if (count)
+    hipLaunchKernelGGL(k_zero, dim3(uint32_t((count + kTilePixels - 1) / kTilePixels)), dim3(kTilePixels), 0, s,
+                       splats_grad, count);
+  hipLaunchKernelGGL(k_backward, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, s, splats, n, bins->vals,
+                     bins->ranges, bins->num_pairs, tiles_x, width, height,
+                     reinterpret_cast<const float4*>(out_rgba), last_contrib, reinterpret_cast<const float4*>(v_out),
+                     splats_grad);
+  return check_launch(ctx, "gsr_render_backward");
+}

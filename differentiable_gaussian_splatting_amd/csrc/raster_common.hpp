@@ -1,0 +1,106 @@
+// Device helpers shared by the forward and backward raster kernels. Both kernels must take exactly the same
+// decisions for every (pixel, splat), so the evaluation below is the only place sigma, exp(-sigma) and alpha are
+// computed. The file is compiled without floating-point contraction: every float expression rounds once per
+// operation, in the order written, which makes each decision equal to a plain fp32 evaluation of the definition.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace gsr {
+
+// Method constants (fp32). [A.9 f16 forward page, listing: alpha clamp 0.999; W1 warp sparse skip + exp-skip page,
+// summary: alpha < 1/255 reject and the sigma >= 5.55 skip]
+constexpr float kAlphaMax = 0.999f;
+constexpr float kAlphaMin = 1.0f / 255.0f;
+constexpr float kTStop = 1e-4f;
+constexpr float kSigmaSkip = 5.55f;
+// A certain alpha reject: o * exp(-sigma) evaluated with the hardware exp2 (relative error below 1e-6 here) under
+// 1/255 by a relative margin of 2^-12 cannot reach 1/255 when evaluated exactly.
+constexpr float kAlphaMinCertain = kAlphaMin * (1.0f - 1.0f / 4096.0f);
+
+// e^x rounded to fp32, for |x| below 80. Cody-Waite reduction x = k ln2 + r with |r| <= ln2 / 2 (ln2 split into a
+// 32-bit head, exact in k * head for |k| < 2^20, and a tail), the Taylor series of e^r to degree 11 in fp64
+// (truncation below 7e-15 relative), then scaling by 2^k and one rounding to fp32. The fp64 value is within about
+// 2^-46 of e^x, so the fp32 result is the correctly rounded one except when e^x lies within 2^-46 (relative) of the
+// midpoint between two floats, i.e. about one argument in 2^22.
+__host__ __device__ __forceinline__ float exp_rn(float x) {
+  const double xd = double(x);
+  const double k = rint(xd * 1.4426950408889634074);
+  double r = fma(-k, 6.93147180369123816490e-01, xd);
+  r = fma(-k, 1.90821492927058770002e-10, r);
+  double p = 1.0 / 39916800.0;         // 1/11!
+  p = fma(p, r, 1.0 / 3628800.0);      // 1/10!
+  p = fma(p, r, 1.0 / 362880.0);       // 1/9!
+  p = fma(p, r, 1.0 / 40320.0);        // 1/8!
+  p = fma(p, r, 1.0 / 5040.0);         // 1/7!
+  p = fma(p, r, 1.0 / 720.0);          // 1/6!
+  p = fma(p, r, 1.0 / 120.0);          // 1/5!
+  p = fma(p, r, 1.0 / 24.0);           // 1/4!
+  p = fma(p, r, 1.0 / 6.0);            // 1/3!
+  p = fma(p, r, 0.5);                  // 1/2!
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  return float(ldexp(p, int(k)));
+}
+
+// One splat as staged in LDS for a batch: 48 bytes, read by every lane of a wavefront at the same address.
+struct alignas(16) StagedSplat {
+  float x, y, ha, b;  // mean, a / 2, b
+  float hc, o, r, g;  // c / 2, opacity, red, green
+  float bl, a, c;     // blue, a, c (the backward's mean gradient needs the full conic)
+  uint32_t idx;       // splat index, or 0xFFFFFFFF for a slot that must not contribute
+};
+
+__device__ __forceinline__ StagedSplat stage_splat(const float* __restrict__ splats, uint32_t idx, uint32_t n) {
+  StagedSplat s;
+  if (idx < n) {
+    const float* p = splats + size_t(idx) * 9;
+    s.x = p[0];
+    s.y = p[1];
+    s.a = p[2];
+    s.b = p[3];
+    s.c = p[4];
+    s.r = p[5];
+    s.g = p[6];
+    s.bl = p[7];
+    s.o = p[8];
+    s.ha = 0.5f * s.a;  // exact: scaling by a power of two
+    s.hc = 0.5f * s.c;
+    s.idx = idx;
+  } else {
+    // o = 0 makes every evaluation a reject
+    s.x = s.y = s.a = s.b = s.c = s.r = s.g = s.bl = s.o = s.ha = s.hc = 0.0f;
+    s.idx = 0xFFFFFFFFu;
+  }
+  return s;
+}
+
+struct Eval {
+  float dx, dy, G, oG, alpha;
+};
+
+// Evaluates splat s at pixel centre (cx, cy). Returns true when the splat passes every reject (sigma >= 0,
+// alpha >= 1/255); then e holds dx, dy, G = exp(-sigma), o G and alpha = min(0.999, o G).
+// sigma = 0.5 (a dx dx + c dy dy) + b dx dy is formed as (ha dx) dx + (hc dy) dy + (b dx) dy, which rounds to the
+// same fp32 value because halving is exact. Splats with sigma >= 5.55 are rejected before any exponential (their
+// alpha is at most e^-5.55 < 1/255 since o <= 1), and most other rejects are settled by the hardware exp2 before
+// the fp64 evaluation.
+__device__ __forceinline__ bool evaluate(const StagedSplat& s, float cx, float cy, Eval& e) {
+  e.dx = cx - s.x;
+  e.dy = cy - s.y;
+  const float t_a = (s.ha * e.dx) * e.dx;
+  const float t_c = (s.hc * e.dy) * e.dy;
+  const float t_b = (s.b * e.dx) * e.dy;
+  const float sigma = (t_a + t_c) + t_b;
+  if (!(sigma >= 0.0f && sigma < kSigmaSkip)) return false;
+  const float g_fast = __builtin_amdgcn_exp2f(sigma * -1.44269504088896341f);
+  if (s.o * g_fast < kAlphaMinCertain) return false;
+  e.G = exp_rn(-sigma);
+  e.oG = s.o * e.G;
+  e.alpha = (e.oG < kAlphaMax) ? e.oG : kAlphaMax;
+  return !(e.alpha < kAlphaMin);
+}
+
+}  // namespace gsr

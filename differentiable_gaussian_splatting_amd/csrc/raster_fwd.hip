@@ -1,0 +1,90 @@
+// Forward rasterization: one 256-thread workgroup (four wave64) per 16x16 tile, one pixel per thread.
+//
+// The tile's depth-sorted splats are staged through LDS in batches of 256 (one record per thread), read back by
+// every lane of a wave at the same address (LDS broadcast). Each lane composites front to back in registers and
+// leaves its loop when its pixel stops; a wave leaves when all 64 lanes have; the workgroup stops staging batches
+// once all 256 pixels are done (a counted barrier). [rasterize forward + adam kernel audit page, section 1 rows (a)
+// and (b): batches of 256 staged records, a done counter for the tile, the per-lane !done loop exit]
+#include "gsr_internal.hpp"
+#include "raster_common.hpp"
+
+namespace gsr {
+namespace {
+
+__global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict__ splats, uint32_t n,
+                                                         const uint32_t* __restrict__ vals,
+                                                         const uint32_t* __restrict__ ranges, uint32_t num_pairs,
+                                                         uint32_t tiles_x, uint32_t width, uint32_t height,
+                                                         float4* __restrict__ out_rgba, float* __restrict__ final_T,
+                                                         uint32_t* __restrict__ last_contrib) {
+  __shared__ StagedSplat s_sp[kTilePixels];
+  const uint32_t tid = threadIdx.x;
+  const uint32_t tile = blockIdx.x;
+  const uint32_t px = (tile % tiles_x) * kTile + (tid & (kTile - 1));
+  const uint32_t py = (tile / tiles_x) * kTile + (tid / kTile);
+  const bool inside = px < width && py < height;
+  const uint32_t start = min(ranges[2 * tile], num_pairs);
+  const uint32_t end = max(start, min(ranges[2 * tile + 1], num_pairs));
+  const float cx = float(px) + 0.5f, cy = float(py) + 0.5f;
+
+  float T = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f;
+  uint32_t last = 0;
+  bool done = !inside;
+  for (uint32_t b0 = start; b0 < end; b0 += kTilePixels) {
+    if (__syncthreads_count(done) == int(kTilePixels)) break;  // also orders the previous batch's reads
+    const uint32_t k = b0 + tid;
+    if (k < end) s_sp[tid] = stage_splat(splats, vals[k], n);
+    __syncthreads();
+    const uint32_t cnt = min(kTilePixels, end - b0);
+    for (uint32_t j = 0; j < cnt && !done; ++j) {
+      const StagedSplat& s = s_sp[j];
+      Eval e;
+      if (!evaluate(s, cx, cy, e)) continue;
+      const float next_T = T * (1.0f - e.alpha);
+      if (next_T < kTStop) {
+        done = true;
+        break;
+      }
+      const float w = e.alpha * T;
+      cr = cr + s.r * w;
+      cg = cg + s.g * w;
+      cb = cb + s.bl * w;
+      T = next_T;
+      last = b0 - start + j + 1;
+    }
+  }
+  if (inside) {
+    const size_t p = size_t(py) * width + px;
+    out_rgba[p] = make_float4(cr, cg, cb, 1.0f - T);
+    final_T[p] = T;
+    last_contrib[p] = last;
+  }
+}
+
+}  // namespace
+}  // namespace gsr
+
+using namespace gsr;
+
+extern "C" gsr_status gsr_render_forward(gsr_ctx* ctx, void* stream, const float* splats, uint32_t n,
+                                         const gsr_bins* bins, uint32_t width, uint32_t height, float* out_rgba,
+                                         float* final_T, uint32_t* last_contrib) {
+  if (!ctx || !bins) return GSR_EINVAL;
+  if (width == 0 || height == 0) return fail(ctx, GSR_EINVAL, "gsr_render_forward: empty image");
+  const uint32_t tiles_x = (width + kTile - 1) / kTile, tiles_y = (height + kTile - 1) / kTile;
+  if (bins->tiles_x != tiles_x || bins->tiles_y != tiles_y)
+    return fail(ctx, GSR_EINVAL, "gsr_render_forward: bins are for %ux%u tiles, image needs %ux%u", bins->tiles_x,
+                bins->tiles_y, tiles_x, tiles_y);
+  if (!bins->ranges || (bins->num_pairs && !bins->vals) || (n && !splats) || !out_rgba || !final_T || !last_contrib)
+    return fail(ctx, GSR_EINVAL, "gsr_render_forward: null pointer");
+  if (reinterpret_cast<uintptr_t>(out_rgba) % 16)
+    return fail(ctx, GSR_EINVAL, "gsr_render_forward: out_rgba must be 16-byte aligned");
+  const uint64_t num_tiles = uint64_t(tiles_x) * tiles_y;
+  if (num_tiles >= (uint64_t(1) << 31)) return fail(ctx, GSR_EINVAL, "gsr_render_forward: too many tiles");
+  gsr_status st = enter(ctx);
+  if (st) return st;
+  hipLaunchKernelGGL(k_forward, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, static_cast<hipStream_t>(stream),
+                     splats, n, bins->vals, bins->ranges, bins->num_pairs, tiles_x, width, height,
+                     reinterpret_cast<float4*>(out_rgba), final_T, last_contrib);
+  return check_launch(ctx, "gsr_render_forward");
+}

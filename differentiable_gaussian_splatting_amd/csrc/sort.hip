@@ -1,0 +1,211 @@
+// Stable LSD radix sort of (uint64 key, uint32 value) pairs, 8-bit digits, for gfx950.
+//
+// One pass per non-constant digit, three launches per pass (reduce-then-scan, no inter-block waiting):
+//   upsweep  each 4096-key block counts its digits (wave-aggregated with ballots, then LDS);
+//   scan     one workgroup per digit turns the per-block counts into global start positions;
+//   scatter  each block ranks its keys stably with a 64-lane ballot match (the wave64 form of the simd-ballot
+//            ranking of the pages' radix scatter), reorders them by digit in LDS, and writes each digit's run
+//            contiguously.
+// Digits above key_bits are identity passes of a stable sort and are never run (the constant-digit pass skip of
+// the C0 resident arena + C1 pass skip page, section 2 table, row "C1").
+#include "gsr_internal.hpp"
+#include "scan_common.hpp"
+
+namespace gsr {
+namespace {
+
+constexpr uint32_t kThreads = 256;
+constexpr uint32_t kItems = 16;
+constexpr uint32_t kBlockKeys = kThreads * kItems;  // 4096
+constexpr uint32_t kWaveKeys = kWave * kItems;      // 1024 consecutive keys per wave
+constexpr uint32_t kRadix = 256;
+
+__device__ __forceinline__ uint32_t digit_of(uint64_t k, uint32_t shift) { return uint32_t(k >> shift) & 0xFFu; }
+
+// Lanes of this wave whose (valid) digit equals mine: eight ballots, one per digit bit.
+__device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
+  uint64_t peers = __ballot(valid);
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    const bool set = (d >> bit) & 1u;
+    const uint64_t b = __ballot(set);
+    peers &= set ? b : ~b;
+  }
+  return peers;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(uint32_t lane) { return (uint64_t(1) << lane) - 1; }
+
+__global__ __launch_bounds__(kThreads) void k_upsweep(const uint64_t* __restrict__ keys, uint64_t n, uint32_t shift,
+                                                      uint32_t nb, uint32_t* __restrict__ hist) {
+  __shared__ uint32_t h[kRadix];
+  const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  h[tid] = 0;
+  __syncthreads();
+  const uint64_t base = uint64_t(blockIdx.x) * kBlockKeys + uint64_t(w) * kWaveKeys;
+  for (uint32_t i = 0; i < kItems; ++i) {
+    const uint64_t idx = base + uint64_t(i) * kWave + lane;
+    const bool valid = idx < n;
+    const uint32_t d = valid ? digit_of(keys[idx], shift) : 0u;
+    const uint64_t peers = match_digit(d, valid);
+    if (valid && (peers & lanemask_lt(lane)) == 0) atomicAdd(&h[d], uint32_t(__popcll(peers)));
+  }
+  __syncthreads();
+  hist[uint64_t(tid) * nb + blockIdx.x] = h[tid];
+}
+
+// Block d scans row d of hist (the counts of digit d in blocks 0..nb-1) in place; digit_tot[d] = row total.
+__global__ __launch_bounds__(kThreads) void k_scan_rows(uint32_t* __restrict__ hist, uint32_t nb,
+                                                        uint32_t* __restrict__ digit_tot) {
+  __shared__ uint32_t smem[kThreads / kWave];
+  uint32_t* row = hist + uint64_t(blockIdx.x) * nb;
+  const uint32_t per = (nb + kThreads - 1) / kThreads;
+  const uint32_t b0 = min(nb, threadIdx.x * per), b1 = min(nb, b0 + per);
+  uint32_t sum = 0;
+  for (uint32_t i = b0; i < b1; ++i) sum += row[i];
+  uint32_t total;
+  uint32_t run = block_exclusive_scan<uint32_t, kThreads>(sum, &total, smem);
+  for (uint32_t i = b0; i < b1; ++i) {
+    const uint32_t v = row[i];
+    row[i] = run;
+    run += v;
+  }
+  if (threadIdx.x == 0) digit_tot[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(kThreads) void k_scatter(const uint64_t* __restrict__ keys_in,
+                                                      const uint32_t* __restrict__ vals_in, uint64_t n,
+                                                      uint32_t shift, uint32_t nb, const uint32_t* __restrict__ hist,
+                                                      const uint32_t* __restrict__ digit_tot,
+                                                      uint64_t* __restrict__ keys_out,
+                                                      uint32_t* __restrict__ vals_out) {
+  __shared__ uint64_t s_keys[kBlockKeys];
+  __shared__ uint32_t s_vals[kBlockKeys];
+  __shared__ uint32_t s_wave[kThreads / kWave][kRadix];  // per-wave running digit counts, then wave prefixes
+  __shared__ uint32_t s_dstart[kRadix];                  // first LDS slot of each digit in this block
+  __shared__ uint32_t s_gbase[kRadix];                   // global position of this block's first key of each digit
+  __shared__ uint32_t smem[kThreads / kWave];
+  const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+
+  for (uint32_t i = tid; i < (kThreads / kWave) * kRadix; i += kThreads) (&s_wave[0][0])[i] = 0;
+  {
+    const uint32_t dbase = block_exclusive_scan<uint32_t, kThreads>(digit_tot[tid], nullptr, smem);
+    s_gbase[tid] = dbase + hist[uint64_t(tid) * nb + blockIdx.x];
+  }
+  __syncthreads();
+
+  uint64_t k[kItems];
+  uint32_t v[kItems], r[kItems];
+  const uint64_t base = uint64_t(blockIdx.x) * kBlockKeys + uint64_t(w) * kWaveKeys;
+#pragma unroll
+  for (uint32_t i = 0; i < kItems; ++i) {
+    const uint64_t idx = base + uint64_t(i) * kWave + lane;
+    const bool valid = idx < n;
+    k[i] = valid ? keys_in[idx] : 0;
+    v[i] = valid ? vals_in[idx] : 0;
+    const uint32_t d = digit_of(k[i], shift);
+    const uint64_t peers = match_digit(d, valid);
+    r[i] = 0;
+    if (valid) {
+      const uint64_t before = peers & lanemask_lt(lane);
+      const uint32_t old = s_wave[w][d];
+      r[i] = old + uint32_t(__popcll(before));
+      if (before == 0) s_wave[w][d] = old + uint32_t(__popcll(peers));
+    }
+  }
+  __syncthreads();
+  {
+    // thread tid owns digit tid: wave prefixes in place, and the digit's first slot in the block
+    uint32_t run = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < kThreads / kWave; ++q) {
+      const uint32_t c = s_wave[q][tid];
+      s_wave[q][tid] = run;
+      run += c;
+    }
+    s_dstart[tid] = block_exclusive_scan<uint32_t, kThreads>(run, nullptr, smem);
+  }
+  __syncthreads();
+#pragma unroll
+  for (uint32_t i = 0; i < kItems; ++i) {
+    const uint64_t idx = base + uint64_t(i) * kWave + lane;
+    if (idx < n) {
+      const uint32_t d = digit_of(k[i], shift);
+      const uint32_t pos = s_dstart[d] + s_wave[w][d] + r[i];
+      s_keys[pos] = k[i];
+      s_vals[pos] = v[i];
+    }
+  }
+  __syncthreads();
+  const uint64_t block0 = uint64_t(blockIdx.x) * kBlockKeys;
+  const uint32_t count = uint32_t(min<uint64_t>(kBlockKeys, n - block0));
+  for (uint32_t j = tid; j < count; j += kThreads) {
+    const uint64_t kk = s_keys[j];
+    const uint32_t d = digit_of(kk, shift);
+    const uint64_t g = uint64_t(s_gbase[d]) + (j - s_dstart[d]);
+    if (g < n) {  // always true for consistent counts; keeps a miscount from writing out of bounds
+      keys_out[g] = kk;
+      vals_out[g] = s_vals[j];
+    }
+  }
+}
+
+}  // namespace
+
+uint32_t sort_blocks(uint64_t n) { return uint32_t((n + kBlockKeys - 1) / kBlockKeys); }
+
+uint32_t sort_passes(uint32_t key_bits) { return (key_bits + 7) / 8; }
+
+// Pass p writes to keys_out when (passes - p) is odd and to tmp otherwise, so the last pass lands in keys_out.
+// The first destination must differ from keys_in: with an even pass count keys_in may be keys_out, with an odd
+// one keys_in may be tmp.
+gsr_status radix_sort_launch(gsr_ctx* ctx, hipStream_t s, const uint64_t* keys_in, const uint32_t* vals_in,
+                             uint64_t n, uint32_t key_bits, uint64_t* keys_out, uint32_t* vals_out,
+                             uint64_t* tmp_keys, uint32_t* tmp_vals) {
+  if (n == 0) return GSR_OK;
+  const uint32_t passes = sort_passes(key_bits);
+  const uint32_t nb = sort_blocks(n);
+  gsr_status st = grow(ctx, ctx->arena.hist, size_t(nb) * kRadix * 4);
+  if (st) return st;
+  if ((st = grow(ctx, ctx->arena.digit_tot, kRadix * 4))) return st;
+  uint32_t* hist = static_cast<uint32_t*>(ctx->arena.hist.ptr);
+  uint32_t* tot = static_cast<uint32_t*>(ctx->arena.digit_tot.ptr);
+  const uint64_t* src_k = keys_in;
+  const uint32_t* src_v = vals_in;
+  for (uint32_t p = 0; p < passes; ++p) {
+    const bool to_out = ((passes - p) & 1u) == 1u;
+    uint64_t* dk = to_out ? keys_out : tmp_keys;
+    uint32_t* dv = to_out ? vals_out : tmp_vals;
+    if (p == 0 && dk == keys_in) return fail(ctx, GSR_EINVAL, "radix sort: first pass would overwrite its input");
+    const uint32_t shift = 8 * p;
+    hipLaunchKernelGGL(k_upsweep, dim3(nb), dim3(kThreads), 0, s, src_k, n, shift, nb, hist);
+    hipLaunchKernelGGL(k_scan_rows, dim3(kRadix), dim3(kThreads), 0, s, hist, nb, tot);
+    hipLaunchKernelGGL(k_scatter, dim3(nb), dim3(kThreads), 0, s, src_k, src_v, n, shift, nb, hist, tot, dk, dv);
+    src_k = dk;
+    src_v = dv;
+  }
+  return check_launch(ctx, "radix sort");
+}
+
+}  // namespace gsr
+
+using namespace gsr;
+
+extern "C" gsr_status gsr_radix_sort(gsr_ctx* ctx, void* stream, const uint64_t* keys_in, const uint32_t* vals_in,
+                                     uint64_t n, uint32_t key_bits, uint64_t* keys_out, uint32_t* vals_out) {
+  if (!ctx) return GSR_EINVAL;
+  if (key_bits == 0 || key_bits > 64) return fail(ctx, GSR_EINVAL, "gsr_radix_sort: key_bits must be in 1..64");
+  if (n >= (uint64_t(1) << 32)) return fail(ctx, GSR_EOVERFLOW, "gsr_radix_sort: n >= 2^32");
+  if (n == 0) return GSR_OK;
+  if (!keys_in || !vals_in || !keys_out || !vals_out)
+    return fail(ctx, GSR_EINVAL, "gsr_radix_sort: null pointer");
+  const uint64_t lo_in = reinterpret_cast<uintptr_t>(keys_in), lo_out = reinterpret_cast<uintptr_t>(keys_out);
+  if (lo_in < lo_out + n * 8 && lo_out < lo_in + n * 8)
+    return fail(ctx, GSR_EINVAL, "gsr_radix_sort: keys_in and keys_out overlap");
+  gsr_status st = enter(ctx);
+  if (st) return st;
+  Arena& a = ctx->arena;
+  if ((st = grow(ctx, a.keys[0], size_t(n) * 8)) || (st = grow(ctx, a.vals[0], size_t(n) * 4))) return st;
+  return radix_sort_launch(ctx, static_cast<hipStream_t>(stream), keys_in, vals_in, n, key_bits, keys_out, vals_out,
+                           static_cast<uint64_t*>(a.keys[0].ptr), static_cast<uint32_t*>(a.vals[0].ptr));
+}

@@ -1,0 +1,181 @@
+/* gsr.h - C ABI of libgsr, a tile-based differentiable 2D-splat rasterizer for AMD MI355X (gfx950).
+ *
+ * The library runs the hot path of a Gaussian-splatting training step on one GPU:
+ *   gsr_bin             (tile | depth) keys per splat-tile overlap, a stable LSD radix sort, per-tile ranges
+ *   gsr_render_forward  per-pixel front-to-back alpha compositing over each 16x16 tile's depth-sorted splats
+ *   gsr_render_backward the 9 per-splat 2D gradients of that compositing
+ *   gsr_adam_step       one fused Adam step over every parameter group
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named as device pointers must point to memory allocated on the context's device (hipMalloc or a
+ *     caching allocator on top of it, such as PyTorch's). The caller owns them and keeps them alive until the work
+ *     queued on `stream` has finished.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the device's null stream. Every call queues its work on
+ *     that stream and returns without waiting, except gsr_bin, which waits once for a 4-byte count (see there).
+ *   - Arguments are checked before any work is queued; a rejected call queues nothing. An error raised by the HIP
+ *     runtime (including a fault of earlier asynchronous work found by this call) is reported as GSR_EHIP.
+ *     gsr_last_error() then holds a message for the last failing call on that context.
+ *   - One context serves one host thread and one stream at a time; it is not thread-safe.
+ *   - Splat records are 9 float32 values {x, y, a, b, c, r, g, b, o}, row-major [n][9]: the mean in pixels, the
+ *     conic [[a, b], [b, c]] (inverse 2D covariance), the colour, and the opacity color_a in [0, 1]. Pixel (px, py)
+ *     has its centre at (px + 0.5, py + 0.5). Tiles are 16x16 pixels; tiles_x = ceil(width / 16),
+ *     tiles_y = ceil(height / 16), tile id = ty * tiles_x + tx. Images are row-major.
+ */
+#ifndef GSR_H
+#define GSR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t gsr_status;
+#define GSR_OK 0
+#define GSR_EINVAL (-1)    /* bad pointer, size or option; nothing was queued                                   */
+#define GSR_ENOMEM (-2)    /* growing the device arena failed; the arena keeps its previous size and stays usable */
+#define GSR_EHIP (-3)      /* the HIP runtime reported an error; gsr_last_error() has its name                   */
+#define GSR_EOVERFLOW (-4) /* a count does not fit its 32-bit field (pairs >= 2^32, n * 9 >= 2^32)               */
+
+typedef struct gsr_ctx gsr_ctx;
+
+/* Creates a context on HIP device `hip_device`. The context owns a grow-only device arena for the binning
+ * (keys, values, per-splat counts and offsets, radix histograms, tile ranges), reused across calls: only a call
+ * that needs more room reallocates it. [C0 resident arena + C1 pass skip page, section 2 table, row "C0 resident
+ * arena"] Returns GSR_EINVAL for a null `out` or a device index out of range, GSR_EHIP or GSR_ENOMEM otherwise. */
+gsr_status gsr_create(gsr_ctx** out, int hip_device);
+
+/* Frees the arena and the context. Waits for nothing: the caller must have finished using every gsr_bins view. */
+void gsr_destroy(gsr_ctx* ctx);
+
+/* Message for the last failing call on `ctx` ("" if none). The pointer stays valid until the next call on ctx. */
+const char* gsr_last_error(const gsr_ctx* ctx);
+
+/* Grows the arena so that later gsr_bin calls with up to `max_pairs` pairs and `max_splats` splats allocate
+ * nothing (first-touch and allocation stay out of timed loops). [C0 resident arena + C1 pass skip page, section 1,
+ * "Day 0 attribution": fresh allocation 26.50 ms vs reused buffers 0.61 ms] */
+gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats);
+
+/* Context options (gsr_set_option). */
+#define GSR_OPT_BIN_SCHEME 1 /* how gsr_bin orders the pairs; both schemes give bit-identical results:           */
+#define GSR_BIN_PRESORT 0    /*   default: radix-sort splats by depth, emit pairs in that order, then a stable     */
+                             /*   radix sort of the pairs by tile id only                                         */
+#define GSR_BIN_KEY64 1      /*   emit pairs splat by splat and radix-sort the full 64-bit keys                   */
+#define GSR_OPT_BIN_KEYS 2   /* 1 (default): gsr_bin materialises the sorted 64-bit keys; 0: keys = NULL          */
+gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value);
+
+/* Views into the context's arena, valid until the next gsr_bin or gsr_reserve on the same context. A caller may
+ * also fill one with its own device buffers of the same layout (for example bins computed elsewhere). */
+typedef struct gsr_bins {
+  const uint64_t* keys;   /* [num_pairs] (tile id << 32) | float bits of the splat's depth, ascending            */
+  const uint32_t* vals;   /* [num_pairs] splat index of each key                                                */
+  const uint32_t* ranges; /* [2 * tiles_x * tiles_y] (start, end) of each tile's run in keys / vals            */
+  uint32_t num_pairs;
+  uint32_t tiles_x;
+  uint32_t tiles_y;
+} gsr_bins;
+
+/* Binning. For every splat that passes the validity test, one pair per 16x16 tile that its 3-sigma axis-aligned
+ * box overlaps: key = (tile id << 32) | float bits of depths[i], value = i. The pairs are sorted stably by key
+ * (ties in depth keep splat order) and each tile gets the [start, end) range of its pairs; tiles without pairs get
+ * start = end = the position where their pairs would be. [C0 resident arena + C1 pass skip page, section 2 table,
+ * rows "C0" and "C1"; tile size and range count from the M3 per-splat backward page, section 3 table]
+ *   splats  device [n][9] float32;  depths  device [n] float32
+ *   A splat emits nothing if any of its values or its depth is not finite, depth <= 0, a <= 0, a*c - b*b <= 0, or
+ *   o is outside [0, 1]. The box is x +- 3 sqrt(c / det), y +- 3 sqrt(a / det), det = a*c - b*b, in fp32.
+ *   out     host struct filled with views into the arena.
+ * Synchronisation: waits on `stream` once, to read the pair count before sizing the arena; the rest is queued.
+ * Errors: GSR_EINVAL (null pointers with n > 0, width or height 0, tiles_x * tiles_y >= 2^32),
+ * GSR_EOVERFLOW (2^32 or more pairs), GSR_ENOMEM, GSR_EHIP. */
+gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, const float* depths, uint32_t n,
+                   uint32_t width, uint32_t height, gsr_bins* out);
+
+/* Copies the contents of `bins` into caller buffers (device pointers; any of keys / vals / ranges may be NULL to
+ * skip it): keys [num_pairs] uint64, vals [num_pairs] uint32, ranges [2 * tiles] uint32. Queued on stream. */
+gsr_status gsr_bins_copy(gsr_ctx* ctx, void* stream, const gsr_bins* bins, uint64_t* keys, uint32_t* vals,
+                         uint32_t* ranges);
+
+/* The sort gsr_bin uses, on its own: a stable LSD radix sort by the low `key_bits` bits of 64-bit keys carrying
+ * 32-bit values, 8 bits per pass; digits above key_bits are not looked at (a key with bits set above key_bits
+ * sorts as if they were zero). The pass count is ceil(key_bits / 8): digits that the key range makes constant are
+ * skipped, the same identity-pass argument as [C0 resident arena + C1 pass skip page, section 2 table, row "C1
+ * radix pass skip"]. keys_in / vals_in / keys_out / vals_out: device [n]; in and out must not overlap.
+ * Uses the context arena as scratch. Errors: GSR_EINVAL (null pointers with n > 0, key_bits 0 or > 64),
+ * GSR_EOVERFLOW (n >= 2^32), GSR_ENOMEM, GSR_EHIP. */
+gsr_status gsr_radix_sort(gsr_ctx* ctx, void* stream, const uint64_t* keys_in, const uint32_t* vals_in, uint64_t n,
+                          uint32_t key_bits, uint64_t* keys_out, uint32_t* vals_out);
+
+/* Number of 4-bit LSD passes that are not identity passes for keys (tile id << 32) | depth bits with tile ids
+ * below num_tiles: min(16, 8 + ceil(bits(num_tiles - 1) / 4)). With digit_bits = 8 the same rule at 8-bit
+ * digits: min(8, 4 + ceil(bits(num_tiles - 1) / 8)). [C0 resident arena + C1 pass skip page, section 2 table, row
+ * "C1 radix pass skip"] Host only; returns 0 for digit_bits other than 4 or 8. */
+uint32_t gsr_radix_pass_count(uint64_t num_tiles, uint32_t digit_bits);
+
+/* Forward rasterization. For each pixel, walks its tile's pairs front to back with T = 1, C = 0:
+ *   sigma = 0.5 (a dx^2 + c dy^2) + b dx dy, (dx, dy) = pixel centre - mean; skip if sigma < 0;
+ *   alpha = min(0.999, o exp(-sigma)); skip if alpha < 1/255;
+ *   T' = T (1 - alpha); if T' < 1e-4 the pixel stops here without compositing this splat;
+ *   C += rgb (alpha T); T = T'; last = list position + 1.
+ * exp(-sigma) is the fp32 value of e^-sigma, correctly rounded except in about one case in 4 million, and every
+ * other operation is one IEEE fp32 operation in the order written (no fused multiply-add), so results match a
+ * plain fp32 evaluation of the definition. Splats with sigma >= 5.55 are skipped before the exponential, which
+ * cannot change a result because o <= 1 makes their alpha at most e^-5.55 < 1/255. [A.9 f16 forward page,
+ * implementation listing; W1 warp sparse skip + exp-skip page, summary and section 1 row "W1b"; rasterize
+ * forward + adam kernel audit page, section 1 rows (a) and (b)]
+ *   splats        device [n][9] float32 (the records the bins were built from)
+ *   bins          host struct of device views, tiles_x / tiles_y matching width / height; pairs whose value is
+ *                 >= n are ignored, and ranges are clamped to [0, num_pairs]
+ *   out_rgba      device [height][width][4] float32: (C.r, C.g, C.b, 1 - T_final)
+ *   final_T       device [height][width] float32;  last_contrib  device [height][width] uint32 (0: none)
+ * Errors: GSR_EINVAL (null pointers, size mismatch), GSR_EHIP. */
+gsr_status gsr_render_forward(gsr_ctx* ctx, void* stream, const float* splats, uint32_t n, const gsr_bins* bins,
+                              uint32_t width, uint32_t height, float* out_rgba, float* final_T,
+                              uint32_t* last_contrib);
+
+/* Backward rasterization: dL/d(splat record) for the loss whose gradient with respect to out_rgba.rgb is v_out.rgb
+ * (v_out.w is ignored). Each pixel replays its forward decisions up to last_contrib and, for each splat it
+ * composited, with w = alpha T, mine = rgb w, after = C_final - acc - mine (acc = colour composited in front):
+ *   d rgb += w g;  dL/dalpha = sum_ch g_ch (rgb_ch T - after_ch / (1 - alpha));
+ *   only if o exp(-sigma) < 0.999 (alpha not clamped): d o += dL/dalpha exp(-sigma),
+ *   dL/dsigma = -dL/dalpha o exp(-sigma), d(a, b, c) += dL/dsigma (dx^2 / 2, dx dy, dy^2 / 2),
+ *   d(x, y) -= dL/dsigma (a dx + b dy, b dx + c dy).
+ * Splats no pixel of a wavefront composites are skipped before any reduction; the per-pixel terms are summed
+ * across the wavefront and the tile on chip and added to splats_grad with one atomic per (splat, tile, value).
+ * [M3 per-splat backward page, section 1 rows "brush's actual structure" and "differences"; W1 warp sparse skip +
+ * exp-skip page, section 1 row "W1a"]
+ *   splats, bins, out_rgba, final_T, last_contrib: as produced by gsr_render_forward for the same inputs
+ *   v_out         device [height][width][4] float32
+ *   splats_grad   device [n][9] float32, overwritten (record order {x, y, a, b, c, r, g, b, o}); the summation
+ *                 order across tiles is not fixed, so results may differ in the last bits between runs
+ * Errors: GSR_EINVAL, GSR_EOVERFLOW (n * 9 >= 2^32), GSR_EHIP. */
+gsr_status gsr_render_backward(gsr_ctx* ctx, void* stream, const float* splats, uint32_t n, const gsr_bins* bins,
+                               uint32_t width, uint32_t height, const float* out_rgba, const float* final_T,
+                               const uint32_t* last_contrib, const float* v_out, float* splats_grad);
+
+/* One Adam parameter group: `count` float32 elements at device pointers param, grad, m, v, with its step size. */
+typedef struct gsr_adam_group {
+  float* param;
+  const float* grad;
+  float* m;
+  float* v;
+  uint64_t count;
+  float lr;
+} gsr_adam_group;
+
+#define GSR_ADAM_MAX_GROUPS 8
+
+/* One Adam step over up to GSR_ADAM_MAX_GROUPS groups in a single launch, element by element:
+ *   m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) g^2;  param -= lr (m / bc1) / (sqrt(v / bc2) + eps)
+ * with the bias corrections bc1 = 1 - beta1^t and bc2 = 1 - beta2^t supplied by the caller. Each operation is one
+ * IEEE fp32 operation in the order written (correctly rounded division and square root, no fused multiply-add).
+ * [rasterize forward + adam kernel audit page, section 2 "(f)": 5 groups, 59 elements per splat, 28 B per element]
+ *   groups     host array [n_groups]; groups with count 0 are allowed; arrays of different groups must not overlap
+ * Errors: GSR_EINVAL (null pointers with count > 0, n_groups > GSR_ADAM_MAX_GROUPS, bc1 or bc2 not > 0), GSR_EHIP. */
+gsr_status gsr_adam_step(gsr_ctx* ctx, void* stream, const gsr_adam_group* groups, uint32_t n_groups, float beta1,
+                         float beta2, float eps, float bc1, float bc2);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSR_H */

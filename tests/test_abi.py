@@ -1,0 +1,70 @@
+"""The C-ABI library loads on a host without a GPU and exports every entry point include/gsr.h declares; the host-only
+pass-count helper reproduces the worked cases the pages print. No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from golden.load import load
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gsr.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gsr_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from differentiable_gaussian_splatting_amd import gsr
+    return gsr.load()
+
+
+def test_header_declares_the_four_steps():
+    names = declared_functions()
+    for step in ("gsr_bin", "gsr_render_forward", "gsr_render_backward", "gsr_adam_step"):
+        assert step in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_covers_every_declared_symbol():
+    from differentiable_gaussian_splatting_amd import gsr
+    assert sorted(gsr.SIGNATURES) == declared_functions()
+
+
+def test_library_exports_nothing_undeclared():
+    from differentiable_gaussian_splatting_amd import gsr
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", gsr.LIB_PATH], capture_output=True, text=True).stdout
+    exported = sorted({ln.split()[-1] for ln in out.splitlines() if " T gsr_" in ln})
+    assert exported == declared_functions()
+
+
+def test_radix_pass_count_matches_the_pages(lib):
+    cases = load("radix_passes.txt")
+    for tiles, passes in cases.items():
+        assert lib.gsr_radix_pass_count(int(tiles), 4) == passes, tiles
+
+
+def test_radix_pass_count_at_8_bit_digits(lib):
+    # 4 depth bytes plus the tile id's bytes: 2,500 tiles (12 bits) -> 6 passes, 16 tiles -> 5, 1 tile -> 4
+    assert lib.gsr_radix_pass_count(2500, 8) == 6
+    assert lib.gsr_radix_pass_count(16, 8) == 5
+    assert lib.gsr_radix_pass_count(1, 8) == 4
+    assert lib.gsr_radix_pass_count(2**32 - 1, 8) == 8
+    assert lib.gsr_radix_pass_count(2500, 5) == 0
+
+
+def test_null_context_is_rejected_without_a_device(lib):
+    from differentiable_gaussian_splatting_amd import gsr
+    assert lib.gsr_set_option(None, 1, 0) == gsr.GSR_EINVAL
+    assert lib.gsr_reserve(None, 0, 0) == gsr.GSR_EINVAL
+    assert lib.gsr_create(None, 0) == gsr.GSR_EINVAL

@@ -1,0 +1,161 @@
+"""GPU binning and radix sort against the oracle: bit-exact keys, values and tile ranges."""
+import numpy as np
+import pytest
+
+from gpuhelp import banner, custom_scene, dev, host, oracle_bins, scene
+
+pytestmark = pytest.mark.gpu
+
+SCHEMES = {"presort": 0, "key64": 1}
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    from differentiable_gaussian_splatting_amd import gsr
+    c = gsr.Context(0)
+    yield c
+    c.close()
+
+
+def gpu_bin(ctx, splats, depths, w, h, scheme):
+    from differentiable_gaussian_splatting_amd import gsr
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SCHEME, SCHEMES[scheme])
+    b = gsr.gsr_bin(ctx, dev(splats), dev(depths), w, h)
+    keys, vals, ranges = gsr.gsr_bins_copy(ctx, b)
+    return b, host(keys, np.uint64), host(vals, np.uint32), host(ranges, np.uint32)
+
+
+def assert_bins_equal(ctx, splats, depths, w, h, scheme, ref=None):
+    import oracle
+    if ref is None:
+        ref = oracle.bin(splats, depths, w, h)
+    b, k, v, r = gpu_bin(ctx, splats, depths, w, h, scheme)
+    assert b.num_pairs == ref.num_pairs
+    assert np.array_equal(k, ref.keys), "sorted keys differ"
+    assert np.array_equal(v, ref.vals), "sorted values differ"
+    assert np.array_equal(r, ref.ranges), "tile ranges differ"
+    return b
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+@pytest.mark.parametrize("name", ["tiny", "raster84k", "raster410k", "bin1m"])
+def test_bin_matches_oracle(ctx, name, scheme):
+    banner(f"bin {name} scheme={scheme}")
+    sc = scene(name)
+    b = assert_bins_equal(ctx, sc.splats, sc.depths, sc.width, sc.height, scheme, oracle_bins(name))
+    assert b.num_pairs > sc.spec.n  # several tiles per splat on every workload
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+@pytest.mark.parametrize("w,h", [(24, 24), (100, 37), (17, 1), (16, 16), (1, 300), (1023, 769)])
+def test_bin_ragged_images(ctx, w, h, scheme):
+    banner(f"bin ragged {w}x{h} scheme={scheme}")
+    sc = custom_scene(name="ragged", width=w, height=h, n=3000, seed=w * 7 + h, size_classes=((1.0, 0.3, 30.0),),
+                      margin=40.0)
+    assert_bins_equal(ctx, sc.splats, sc.depths, w, h, scheme)
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+def test_bin_depth_ties_and_invalid_splats(ctx, scheme):
+    banner(f"bin ties+invalid scheme={scheme}")
+    sc = custom_scene(name="ties", width=160, height=120, n=20000, seed=9, size_classes=((1.0, 0.5, 12.0),),
+                      depth_levels=5, margin=30.0)
+    sp, d = sc.splats.copy(), sc.depths.copy()
+    rng = np.random.default_rng(3)
+    bad = rng.choice(len(d), 600, replace=False)
+    sp[bad[:100], 0] = np.nan
+    sp[bad[100:200], 8] = 1.5
+    sp[bad[200:300], 2] = -1.0
+    d[bad[300:400]] = 0.0
+    d[bad[400:500]] = np.inf
+    sp[bad[500:600], 3] = 100.0  # det < 0
+    assert_bins_equal(ctx, sp, d, 160, 120, scheme)
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+def test_bin_empty_and_all_culled(ctx, scheme):
+    banner(f"bin empty scheme={scheme}")
+    assert_bins_equal(ctx, np.zeros((0, 9), np.float32), np.zeros(0, np.float32), 800, 800, scheme)
+    sc = custom_scene(name="off", width=64, height=64, n=500, seed=2, margin=0.0)
+    sp = sc.splats.copy()
+    sp[:, 0] += 10000.0  # everything off screen
+    b = assert_bins_equal(ctx, sp, sc.depths, 64, 64, scheme)
+    assert b.num_pairs == 0
+
+
+def test_bin_arena_growth_and_reuse(ctx):
+    """A fresh context grows its arena call by call; results stay bit-exact, and a smaller call after a larger
+    one reuses the arena."""
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("bin arena growth")
+    fresh = gsr.Context(0)
+    try:
+        for name in ("tiny", "raster84k", "tiny"):
+            sc = scene(name)
+            assert_bins_equal(fresh, sc.splats, sc.depths, sc.width, sc.height, "presort", oracle_bins(name))
+    finally:
+        fresh.close()
+
+
+def test_bin_is_deterministic(ctx):
+    banner("bin determinism raster84k")
+    sc = scene("raster84k")
+    runs = [gpu_bin(ctx, sc.splats, sc.depths, 800, 800, "presort")[1:] for _ in range(3)]
+    for r in runs[1:]:
+        assert all(np.array_equal(a, b) for a, b in zip(r, runs[0]))
+
+
+def test_bin_without_keys(ctx):
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("bin keys off")
+    sc = scene("tiny")
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SCHEME, 0)
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_KEYS, 0)
+    try:
+        b = gsr.gsr_bin(ctx, dev(sc.splats), dev(sc.depths), 64, 64)
+        assert b.raw.keys is None
+        _, v, r = gsr.gsr_bins_copy(ctx, b)
+        ref = oracle_bins("tiny")
+        assert np.array_equal(host(v, np.uint32), ref.vals) and np.array_equal(host(r, np.uint32), ref.ranges)
+    finally:
+        gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_KEYS, 1)
+
+
+# ------------------------------------------------------------------------------------------------ the sort alone
+@pytest.mark.parametrize("n", [0, 1, 255, 256, 257, 1234, 4095, 4096, 4097, 100000, 1000003])
+@pytest.mark.parametrize("key_bits", [64, 44, 13])
+def test_radix_sort_matches_stable_sort(ctx, n, key_bits):
+    import oracle
+    from differentiable_gaussian_splatting_amd import gsr
+    banner(f"radix sort n={n} key_bits={key_bits}")
+    rng = np.random.default_rng(n + key_bits)
+    keys = rng.integers(0, np.iinfo(np.uint64).max, n, dtype=np.uint64, endpoint=True)
+    if key_bits < 64:
+        keys &= np.uint64((1 << key_bits) - 1)
+    vals = rng.permutation(n).astype(np.uint32) if n else np.zeros(0, np.uint32)
+    ko, vo = gsr.gsr_radix_sort(ctx, dev(keys), dev(vals), key_bits)
+    rk, rv = oracle.sort_pairs(keys, vals)
+    assert np.array_equal(host(ko, np.uint64), rk) and np.array_equal(host(vo, np.uint32), rv)
+
+
+def test_radix_sort_ties_heavy(ctx):
+    import oracle
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("radix sort ties n=5000")
+    rng = np.random.default_rng(5000)
+    keys = rng.integers(0, 7, 5000).astype(np.uint64) << np.uint64(32)
+    vals = rng.permutation(5000).astype(np.uint32)
+    ko, vo = gsr.gsr_radix_sort(ctx, dev(keys), dev(vals), 64)
+    rk, rv = oracle.sort_pairs(keys, vals)
+    assert np.array_equal(host(vo, np.uint32), rv) and np.array_equal(host(ko, np.uint64), rk)
+
+
+def test_radix_sort_rejects_bad_arguments(ctx):
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("radix sort argument errors")
+    k = dev(np.zeros(10, np.uint64))
+    v = dev(np.zeros(10, np.uint32))
+    with pytest.raises(gsr.GsrError):
+        gsr.gsr_radix_sort(ctx, k, v, 0)
+    with pytest.raises(gsr.GsrError):
+        gsr.gsr_radix_sort(ctx, k, v, 65)

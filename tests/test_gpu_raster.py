@@ -1,0 +1,182 @@
+"""GPU forward and backward rasterization against the oracle.
+
+Bars: the image within 1e-5 absolute per channel (in practice bit-identical: both sides evaluate the same fp32
+operations and a correctly rounded exp), final_T likewise, last_contrib exactly; the 9 splat gradients within
+|gpu - oracle| <= 1e-4 + 1e-4 |oracle| element by element. Every output element is compared, at full size.
+"""
+import numpy as np
+import pytest
+
+from gpuhelp import (banner, custom_scene, dev, grads_close, host, oracle_backward, oracle_bins, oracle_forward,
+                     scene)
+
+pytestmark = pytest.mark.gpu
+
+IMG_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    from differentiable_gaussian_splatting_amd import gsr
+    c = gsr.Context(0)
+    yield c
+    c.close()
+
+
+def oracle_bins_on_device(ob, w, h):
+    from differentiable_gaussian_splatting_amd import gsr
+    return gsr.bins_from_tensors(dev(ob.keys), dev(ob.vals), dev(ob.ranges), w, h)
+
+
+def run_forward(ctx, splats_d, bins, w, h):
+    from differentiable_gaussian_splatting_amd import gsr
+    out, ft, lc = gsr.gsr_render_forward(ctx, splats_d, bins, w, h)
+    return out, ft, lc
+
+
+def compare_forward(gpu, ref):
+    out, ft, lc = (host(gpu[0]), host(gpu[1]), host(gpu[2], np.uint32))
+    r_out, r_ft, r_lc = ref[:3]
+    assert np.array_equal(lc, r_lc), f"last_contrib differs at {np.argwhere(lc != r_lc)[:5].tolist()}"
+    d_img = np.abs(out - r_out).max() if out.size else 0.0
+    d_T = np.abs(ft - r_ft).max() if ft.size else 0.0
+    assert d_img <= IMG_TOL and d_T <= IMG_TOL, (d_img, d_T)
+    return float((out != r_out).any(axis=-1).mean()) if out.size else 0.0
+
+
+@pytest.mark.parametrize("bins_from", ["oracle", "gpu"])
+@pytest.mark.parametrize("name", ["tiny", "raster84k", "raster410k"])
+def test_forward_matches_oracle(ctx, name, bins_from):
+    from differentiable_gaussian_splatting_amd import gsr
+    banner(f"forward {name} bins={bins_from}")
+    sc = scene(name)
+    sp = dev(sc.splats)
+    if bins_from == "oracle":
+        bins = oracle_bins_on_device(oracle_bins(name), sc.width, sc.height)
+    else:
+        bins = gsr.gsr_bin(ctx, sp, dev(sc.depths), sc.width, sc.height)
+    frac = compare_forward(run_forward(ctx, sp, bins, sc.width, sc.height), oracle_forward(name))
+    print(f"  pixels not bit-identical: {frac:.2e}")
+
+
+@pytest.mark.parametrize("w,h", [(24, 24), (100, 37), (17, 1), (1, 40), (200, 145)])
+def test_forward_ragged_images(ctx, w, h):
+    import oracle
+    from differentiable_gaussian_splatting_amd import gsr
+    banner(f"forward ragged {w}x{h}")
+    sc = custom_scene(name="rag", width=w, height=h, n=1500, seed=w + 31 * h,
+                      size_classes=((0.7, 0.3, 4.0), (0.3, 4.0, 30.0)), opacity_mu=0.5, margin=30.0)
+    ob = oracle.bin(sc.splats, sc.depths, w, h)
+    ref = oracle.render_forward(sc.splats, ob, w, h)
+    sp = dev(sc.splats)
+    bins = gsr.gsr_bin(ctx, sp, dev(sc.depths), w, h)
+    compare_forward(run_forward(ctx, sp, bins, w, h), ref)
+
+
+def test_forward_empty_scene(ctx):
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("forward empty")
+    sp = dev(np.zeros((0, 9), np.float32))
+    bins = gsr.gsr_bin(ctx, sp, dev(np.zeros(0, np.float32)), 48, 40)
+    out, ft, lc = run_forward(ctx, sp, bins, 48, 40)
+    assert np.all(host(out)[..., :3] == 0) and np.all(host(ft) == 1) and np.all(host(lc) == 0)
+
+
+def test_forward_closed_form_stop_rule(ctx):
+    """14 centred o = 0.5 splats: T = 2^-13 after 13 composites, the 14th stops (bit-exact on the GPU too)."""
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("forward stop rule")
+    sp = np.tile(np.array([8.5, 8.5, 0.25, 0.0, 0.25, 1.0, 0.5, 0.25, 0.5], np.float32), (14, 1))
+    d = np.arange(1, 15, dtype=np.float32)
+    bins = gsr.gsr_bin(ctx, dev(sp), dev(d), 16, 16)
+    out, ft, lc = run_forward(ctx, dev(sp), bins, 16, 16)
+    assert host(ft)[8, 8] == 2.0 ** -13 and host(lc)[8, 8] == 13
+    assert host(out)[8, 8, :3].tolist() == [c * (1 - 2.0 ** -13) for c in (1.0, 0.5, 0.25)]
+
+
+def test_forward_ignores_out_of_range_values(ctx):
+    """Bins whose values point past n contribute nothing (no out-of-bounds read)."""
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("forward bad values")
+    sp = np.array([[8.5, 8.5, 0.25, 0.0, 0.25, 1.0, 1.0, 1.0, 0.5]], np.float32)
+    vals = np.array([0, 7, 1 << 30], np.uint32)
+    ranges = np.array([[0, 3]], np.uint32)
+    bins = gsr.bins_from_tensors(None, dev(vals), dev(ranges), 16, 16)
+    out, ft, lc = run_forward(ctx, dev(sp), bins, 16, 16)
+    assert host(out)[8, 8, 0] == 0.5 and host(lc)[8, 8] == 1
+
+
+# ------------------------------------------------------------------------------------------------ backward
+def run_backward(ctx, sc, bins, out, ft, lc, v_out=None):
+    from differentiable_gaussian_splatting_amd import gsr
+    return gsr.gsr_render_backward(ctx, dev(sc.splats), bins, sc.width, sc.height, out, ft, lc,
+                                   dev(sc.v_out if v_out is None else v_out))
+
+
+@pytest.mark.parametrize("name", ["tiny", "raster84k", "raster410k"])
+def test_backward_matches_oracle(ctx, name):
+    from differentiable_gaussian_splatting_amd import gsr
+    banner(f"backward {name}")
+    sc = scene(name)
+    sp = dev(sc.splats)
+    bins = gsr.gsr_bin(ctx, sp, dev(sc.depths), sc.width, sc.height)
+    out, ft, lc = run_forward(ctx, sp, bins, sc.width, sc.height)
+    g = host(run_backward(ctx, sc, bins, out, ft, lc))
+    ref = oracle_backward(name)
+    ok, worst, at = grads_close(g, ref)
+    print(f"  worst |gpu-ref| / (1e-4 + 1e-4 |ref|) = {worst:.3g} at {at}")
+    assert ok, (worst, at, g[at], ref[at])
+
+
+@pytest.mark.parametrize("w,h", [(24, 24), (100, 37), (200, 145)])
+def test_backward_ragged_images(ctx, w, h):
+    import oracle
+    from differentiable_gaussian_splatting_amd import gsr
+    banner(f"backward ragged {w}x{h}")
+    sc = custom_scene(name="rag", width=w, height=h, n=1500, seed=w + 31 * h,
+                      size_classes=((0.7, 0.3, 4.0), (0.3, 4.0, 30.0)), opacity_mu=0.5, vout_sd=0.1, margin=30.0)
+    ob = oracle.bin(sc.splats, sc.depths, w, h)
+    r_out, r_ft, r_lc, _ = oracle.render_forward(sc.splats, ob, w, h)
+    ref = oracle.render_backward(sc.splats, ob, w, h, r_out, r_ft, r_lc, sc.v_out)
+    sp = dev(sc.splats)
+    bins = gsr.gsr_bin(ctx, sp, dev(sc.depths), w, h)
+    out, ft, lc = run_forward(ctx, sp, bins, w, h)
+    ok, worst, at = grads_close(host(run_backward(ctx, sc, bins, out, ft, lc)), ref)
+    assert ok, (worst, at)
+
+
+def test_backward_single_pixel_is_byte_identical(ctx):
+    """With one non-zero upstream pixel each gradient is a single per-pixel term, so the summation order no longer
+    matters and the GPU must equal the oracle bit for bit (the single-pixel byte-equality fixture of the W1 warp
+    sparse skip + exp-skip page, section 1, parity item (2))."""
+    import oracle
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("backward single pixel")
+    sc = scene("tiny")
+    ob = oracle_bins("tiny")
+    r_out, r_ft, r_lc, _ = oracle_forward("tiny")
+    sp = dev(sc.splats)
+    bins = gsr.gsr_bin(ctx, sp, dev(sc.depths), 64, 64)
+    out, ft, lc = run_forward(ctx, sp, bins, 64, 64)
+    rng = np.random.default_rng(7)
+    for _ in range(6):
+        py, px = (int(v) for v in rng.integers(0, 64, 2))
+        v = np.zeros((64, 64, 4), np.float32)
+        v[py, px, :3] = rng.normal(size=3)
+        ref = oracle.render_backward(sc.splats, ob, 64, 64, r_out, r_ft, r_lc, v)
+        g = host(run_backward(ctx, sc, bins, out, ft, lc, v))
+        assert np.array_equal(g, ref), (px, py, np.argwhere(g != ref)[:5].tolist())
+
+
+def test_backward_self_noise_is_within_tolerance(ctx):
+    """Run-to-run differences come only from the order of float atomics across tiles."""
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("backward self-noise raster84k")
+    sc = scene("raster84k")
+    sp = dev(sc.splats)
+    bins = gsr.gsr_bin(ctx, sp, dev(sc.depths), 800, 800)
+    out, ft, lc = run_forward(ctx, sp, bins, 800, 800)
+    runs = [host(run_backward(ctx, sc, bins, out, ft, lc)) for _ in range(3)]
+    for r in runs[1:]:
+        ok, worst, _ = grads_close(r, runs[0].astype(np.float64))
+        assert ok and worst < 0.5, worst
