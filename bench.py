@@ -1,0 +1,253 @@
+"""Benchmark of the splat rasterizer hot path on one MI355X.
+
+A step is one pass of the whole path over the 800x800, 410k-splat workload: bin (emit, radix sort, tile ranges),
+render_forward, render_backward, then the fused Adam step over 59 float32 parameters per splat (5 groups). Inputs
+are seeded synthetic data resident in device memory before the timed region; the arena is pre-grown.
+
+Prints one JSON line: the metric is splat-pixel evaluations per second over whole steps, where the evaluations of a
+step are E_fwd (list entries the forward examines, up to and including each pixel's stopping splat) plus E_bwd
+(entries the backward replays, the sum of last_contrib), both counted exactly by the CPU oracle on the same input.
+
+    python bench.py [--steps K] [--warmup W] [--workload iter410k] [--no-cpu-baseline]
+    python bench.py --calib-copy      # a plain 256 MiB device copy, to scale HBM byte counters
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd raster ms/iter @800×800, 410k splats; splat-pixel evals/s"
+UNIT = "splat-pixel evals/s"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+# fp32 vector rate without packed dual-fp32 instructions: 256 CUs x 64 lanes x 2 flops (FMA) x 2.4 GHz
+ALU_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
+ALU_PUBLISHED_TFLOPS = 157.3  # the published fp32 vector figure, which counts packed dual-fp32 FMA
+
+# Algorithmic operation counts per evaluation (each add, sub, mul, min, exp counts 1; comparisons and negations 0):
+#   sigma       dx, dy, (a dx) dx, (c dy) dy, (b dx) dy, two sums, x0.5                        = 11
+#   alpha       exp, o G, min                                                                  = 3
+#   stop test   1 - alpha, T (1 - alpha)                                                       = 2
+#   composite   alpha T, rgb w (3), C += (3)                                                   = 7
+#   backward, per composited entry (73): the replay 11 + 3 + 1; w = alpha T; w g (3); mine (3);
+#               after = (C - acc) - mine (6); rgb T, after / (1 - alpha), their difference, times g (12) and the
+#               sum (2); dL/dalpha G, dL/dsigma (2); dx^2/2, dx dy, dy^2/2 (5); conic terms (3); a dx + b dy,
+#               b dx + c dy (6) and their products (2); acc += mine (3); T update (1); 9 accumulations
+FWD_OPS = {"sigma_skip": 11, "alpha_reject": 14, "stop": 16, "contrib": 23}
+BWD_OPS = {"sigma_skip": 11, "alpha_reject": 14, "contrib": 73}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="iter410k")
+    ap.add_argument("--bin-scheme", choices=["presort", "key64"], default="presort")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true")
+    return ap.parse_args()
+
+
+def calib_copy():
+    """Copies 256 MiB device to device ten times: rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE on this run give the
+    counters' reading for a known traffic of 256 MiB read + 256 MiB written per copy."""
+    import torch
+    n = 64 * 1024 * 1024
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": 4 * n, "calib_copy_bytes_written": 4 * n, "copies": 10}))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def run_oracle(sc, adam_groups, hp, bc):
+    """CPU baseline leg: the plain single-threaded oracle over one whole step of the same workload; also the exact
+    evaluation counts used by the GPU figure and the flop model."""
+    import numpy as np
+
+    import oracle
+    t = {}
+    t0 = time.perf_counter()
+    ob = oracle.bin(sc.splats, sc.depths, sc.width, sc.height)
+    t["bin"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    out, ft, lc, fst = oracle.render_forward(sc.splats, ob, sc.width, sc.height)
+    t["forward"] = time.perf_counter() - t0
+    bst = {}
+    t0 = time.perf_counter()
+    oracle.render_backward(sc.splats, ob, sc.width, sc.height, out, ft, lc, sc.v_out, stats=bst)
+    t["backward"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for _, p, g, m, v in adam_groups:
+        oracle.adam_step(p, g, m, v, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], *bc)
+    t["adam"] = time.perf_counter() - t0
+    return {"times": t, "fwd_stats": fst, "bwd_stats": bst, "num_pairs": ob.num_pairs, "out": out, "lc": lc,
+            "ranges": ob.ranges}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the tile-sharded multi-GPU "
+              "path is design-only)", file=sys.stderr)
+        sys.exit(2)
+    if args.calib_copy:
+        calib_copy()
+        return
+
+    import numpy as np
+    import torch
+
+    from differentiable_gaussian_splatting_amd import gsr, scenes
+
+    print(f"[bench] workload {args.workload}: generating inputs", file=sys.stderr, flush=True)
+    sc = scenes.make_scene(args.workload)
+    W, H, N = sc.width, sc.height, sc.spec.n
+    hp = scenes.ADAM_HPARAMS
+    bc = scenes.adam_bias_corrections(hp["beta1"], hp["beta2"], hp["step"])
+    adam_host = scenes.make_adam_groups(N, seed=sc.spec.seed)
+
+    ctx = gsr.Context(0)
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SCHEME, gsr.GSR_BIN_PRESORT if args.bin_scheme == "presort"
+                       else gsr.GSR_BIN_KEY64)
+    splats = torch.from_numpy(sc.splats).cuda()
+    depths = torch.from_numpy(sc.depths).cuda()
+    v_out = torch.from_numpy(sc.v_out).cuda()
+    out_rgba = torch.empty((H, W, 4), dtype=torch.float32, device="cuda")
+    final_T = torch.empty((H, W), dtype=torch.float32, device="cuda")
+    last_contrib = torch.empty((H, W), dtype=torch.int32, device="cuda")
+    grad = torch.empty((N, 9), dtype=torch.float32, device="cuda")
+    groups = [tuple(torch.from_numpy(a).cuda() for a in g[1:]) + (hp["lr"],) for g in adam_host]
+    adam_elems = sum(g[0].numel() for g in groups)
+
+    # pre-grow the arena (first-touch and allocation stay out of the timed region)
+    bins = gsr.gsr_bin(ctx, splats, depths, W, H)
+    gsr.gsr_reserve(ctx, int(bins.num_pairs * 1.05) + 1024, N)
+
+    stream = torch.cuda.current_stream()
+    names = ["bin", "forward", "backward", "adam"]
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        b = gsr.gsr_bin(ctx, splats, depths, W, H)
+        if ev:
+            ev[1].record(stream)
+        gsr.gsr_render_forward(ctx, splats, b, W, H, out_rgba, final_T, last_contrib)
+        if ev:
+            ev[2].record(stream)
+        gsr.gsr_render_backward(ctx, splats, b, W, H, out_rgba, final_T, last_contrib, v_out, grad)
+        if ev:
+            ev[3].record(stream)
+        gsr.gsr_adam_step(ctx, groups, hp["beta1"], hp["beta2"], hp["eps"], *bc)
+        if ev:
+            ev[4].record(stream)
+        return b
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronized on both sides; per-stage HIP events on the same stream
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        b = step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    stage_ms = {nm: float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
+                for i, nm in enumerate(names)}
+    stage_ms_median = {nm: float(np.median([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
+                       for i, nm in enumerate(names)}
+    P = b.num_pairs
+    e_bwd_gpu = int(last_contrib.to(torch.int64).sum().item())
+
+    # CPU baseline leg (rank 0, N = 1): the oracle on one whole step of the same input; its exact counts
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline: oracle over one step", file=sys.stderr, flush=True)
+        cpu = run_oracle(sc, adam_host, hp, bc)
+        assert cpu["num_pairs"] == P, "pair count differs from the oracle"
+        assert int(cpu["lc"].astype(np.int64).sum()) == e_bwd_gpu, "last_contrib sum differs from the oracle"
+
+    result = {"metric": METRIC, "unit": UNIT, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": "f32", "data": "synthetic",
+              "config": {"workload": f"{args.workload}: {W}x{H} image, {N} splats "
+                                     "(70% s in 0.3-4 px, 30% s in 4-40 px, color_a = sigmoid(N(-2, 1.5))), "
+                                     "bin + forward + backward + fused Adam over 59 fp32 params per splat",
+                         "image": [W, H], "splats": N, "pairs": P, "adam_elements": adam_elems,
+                         "bin_scheme": args.bin_scheme}}
+    result["stage_ms"] = stage_ms
+    result["stage_ms_median"] = stage_ms_median
+    result["fwd_bwd_ms"] = stage_ms["forward"] + stage_ms["backward"]
+    if cpu is not None:
+        fs, bs = cpu["fwd_stats"], cpu["bwd_stats"]
+        e_fwd, e_bwd = fs["visited"], bs["visited"]
+        evals = e_fwd + e_bwd
+        result["value"] = evals * args.steps / wall
+        result["evals_per_step"] = {"E_fwd": e_fwd, "E_bwd": e_bwd,
+                                    "E_nom": int((cpu["ranges"][:, 1].astype(np.int64) -
+                                                  cpu["ranges"][:, 0]).sum() * 256)}
+        result["fwd_bwd_evals_per_s"] = evals / (result["fwd_bwd_ms"] * 1e-3)
+        # algorithmic operations per launch
+        fwd_ops = (FWD_OPS["sigma_skip"] * (fs["sigma_neg"] + fs["sigma_ge_skip"]) +
+                   FWD_OPS["alpha_reject"] * (fs["alpha_reject"] - fs["sigma_ge_skip"]) +
+                   FWD_OPS["stop"] * fs["stopped"] + FWD_OPS["contrib"] * fs["contrib"])
+        bwd_ops = (BWD_OPS["sigma_skip"] * (bs["sigma_neg"] + bs["sigma_ge_skip"]) +
+                   BWD_OPS["alpha_reject"] * (bs["alpha_reject"] - bs["sigma_ge_skip"]) +
+                   BWD_OPS["contrib"] * bs["contrib"])
+        adam_bytes = 28 * adam_elems
+        roofs = {
+            "forward": {"bound": "alu", "achieved": fwd_ops / (stage_ms["forward"] * 1e-3) / 1e12,
+                        "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s", "work_per_launch": fwd_ops},
+            "backward": {"bound": "alu", "achieved": bwd_ops / (stage_ms["backward"] * 1e-3) / 1e12,
+                         "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s", "work_per_launch": bwd_ops},
+            "adam": {"bound": "hbm", "achieved": adam_bytes / (stage_ms["adam"] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "work_per_launch": adam_bytes},
+        }
+        for r in roofs.values():
+            r["frac"] = r["achieved"] / r["peak"]
+            r["traffic"] = None
+        for k in ("forward", "backward"):
+            roofs[k]["frac_of_published_157_3"] = roofs[k]["achieved"] / ALU_PUBLISHED_TFLOPS
+        dominant = max(("forward", "backward", "adam"), key=lambda k: stage_ms[k])
+        result["roofline"] = {"kernel": dominant, **roofs[dominant]}
+        result["rooflines"] = roofs
+        ct = cpu["times"]
+        cpu_step = sum(ct.values())
+        result["cpu_baseline"] = {"value": evals / cpu_step, "unit": UNIT, "cores": 1, "kind": "oracle",
+                                  "sample": "one whole step of the same workload (bin + forward + backward + Adam "
+                                            "over all 410k splats), single-threaded",
+                                  "stage_s": ct, "host_cpus": os.cpu_count(), "host_cpu_model": cpu_model()}
+    else:
+        result["value"] = None
+    print(json.dumps(result), flush=True)
+    ctx.close()
+
+
+if __name__ == "__main__":
+    main()

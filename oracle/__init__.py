@@ -53,7 +53,7 @@ def _load():
     lib.oracle_sort_pairs.argtypes = [P, P, u64, P, P]
     lib.oracle_render_forward_f32.argtypes = [P, P, P, u32, u32, P, P, P, P]
     lib.oracle_render_forward_f64.argtypes = [P, P, P, u32, u32, P, P, P, P]
-    lib.oracle_render_backward_f32.argtypes = [P, u32, P, P, u32, u32, P, P, P, P, P]
+    lib.oracle_render_backward_f32.argtypes = [P, u32, P, P, u32, u32, P, P, P, P, P, P]
     lib.oracle_render_backward_f64.argtypes = [P, u32, P, P, u32, u32, P, P, P, P, P]
     lib.oracle_adam_step.argtypes = [P, P, P, P, u64, f32, f32, f32, f32, f32, f32]
     lib.oracle_trace_pixel_f32.argtypes = [P, P, P, u32, u32, u32, u32, u32, P, P, P, P, P]
@@ -153,18 +153,28 @@ def render_forward(splats, bins: Bins, width: int, height: int, precision: str =
     return out, ft, lc, {k: int(v) for k, v in zip(STAT_NAMES, st)}
 
 
+BWD_STAT_NAMES = ("visited", "sigma_neg", "sigma_ge_skip", "alpha_reject", "contrib", "clamped")
+
+
 def render_backward(splats, bins: Bins, width: int, height: int, out_rgba, final_T, last_contrib, v_out,
-                    precision: str = "f32"):
-    """Returns splats_grad [N, 9] (float32, or float64 for precision='f64')."""
+                    precision: str = "f32", stats: dict | None = None):
+    """Returns splats_grad [N, 9] (float32, or float64 for precision='f64'). For precision='f32', a dict passed
+    as `stats` receives the replay counters (BWD_STAT_NAMES)."""
     lib = _load()
     dt = np.float32 if precision == "f32" else np.float64
     s = _c(splats, dt).reshape(-1, 9)
     n = s.shape[0]
     grad = np.zeros((n, 9), dt)
-    fn = lib.oracle_render_backward_f32 if precision == "f32" else lib.oracle_render_backward_f64
-    _check(fn(_ptr(s), n, _ptr(_c(bins.vals, np.uint32)), _ptr(_c(bins.ranges, np.uint32)), width, height,
-              _ptr(_c(out_rgba, dt)), _ptr(_c(final_T, dt)), _ptr(_c(last_contrib, np.uint32)),
-              _ptr(_c(v_out, dt)), _ptr(grad)), "render_backward")
+    args = [_ptr(s), n, _ptr(_c(bins.vals, np.uint32)), _ptr(_c(bins.ranges, np.uint32)), width, height,
+            _ptr(_c(out_rgba, dt)), _ptr(_c(final_T, dt)), _ptr(_c(last_contrib, np.uint32)), _ptr(_c(v_out, dt)),
+            _ptr(grad)]
+    if precision == "f32":
+        st = np.zeros(6, np.uint64)
+        _check(lib.oracle_render_backward_f32(*args, _ptr(st)), "render_backward")
+        if stats is not None:
+            stats.update({k: int(v) for k, v in zip(BWD_STAT_NAMES, st)})
+    else:
+        _check(lib.oracle_render_backward_f64(*args), "render_backward")
     return grad
 
 

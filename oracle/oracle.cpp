@@ -267,10 +267,20 @@ void render_forward(const R* splats, const uint32_t* vals, const uint32_t* range
 // Backward, per pixel (B1..B9); per-splat sums in double, in a fixed order (pixels row-major, then list order).
 // ---------------------------------------------------------------------------------------------------------------
 
+// Counters of the backward's replay (entries before each pixel's last contributor).
+struct BwdStats {
+  uint64_t visited;        // sum over pixels of last_contrib
+  uint64_t sigma_neg;      // rejected because sigma < 0
+  uint64_t sigma_ge_skip;  // rejected with sigma >= 5.55 (a subset of alpha_reject)
+  uint64_t alpha_reject;   // rejected because alpha < 1/255
+  uint64_t contrib;        // composited, gradient terms formed
+  uint64_t clamped;        // composited with o*G >= 0.999 (no opacity / geometry terms)
+};
+
 template <typename R>
 void render_backward(const R* splats, uint32_t n, const uint32_t* vals, const uint32_t* ranges, uint32_t width,
                      uint32_t height, const R* out_rgba, const R* final_T, const uint32_t* last_contrib,
-                     const R* v_out, double* acc_grad /* [n][9] */) {
+                     const R* v_out, double* acc_grad /* [n][9] */, BwdStats* st) {
   using C = Consts<R>;
   (void)final_T;  // the forward-order form needs C_final and the replayed T, not the final T
   std::fill(acc_grad, acc_grad + size_t(n) * 9, 0.0);
@@ -291,7 +301,15 @@ void render_backward(const R* splats, uint32_t n, const uint32_t* vals, const ui
         const uint32_t idx = vals[k];
         const Splat<R> s = load_splat(splats, idx);
         const Eval<R> e = evaluate(s, cx, cy);
+        st->visited++;
+        if (e.d == kSigmaNeg) st->sigma_neg++;
+        if (e.d == kAlphaReject) {
+          st->alpha_reject++;
+          if (e.sigma >= R(5.55f)) st->sigma_ge_skip++;
+        }
         if (e.d != kComposite) continue;
+        st->contrib++;
+        if (!(e.oG < C::alpha_max)) st->clamped++;
         double* gr = acc_grad + size_t(idx) * 9;
         const R rgb[3] = {s.r, s.g, s.bl};
         // B1: weight of this splat in the pixel, and the colour gradient.
@@ -417,14 +435,18 @@ int oracle_render_forward_f64(const double* splats, const uint32_t* vals, const 
 }
 
 // splats_grad [n][9] in the record order {x, y, a, b, c, r, g, b, o}; sums kept in double, rounded once.
+// stats[6] (optional) = {visited, sigma_neg, sigma_ge_skip, alpha_reject, contrib, clamped} of the replay.
 int oracle_render_backward_f32(const float* splats, uint32_t n, const uint32_t* vals, const uint32_t* ranges,
                                uint32_t width, uint32_t height, const float* out_rgba, const float* final_T,
-                               const uint32_t* last_contrib, const float* v_out, float* splats_grad) {
+                               const uint32_t* last_contrib, const float* v_out, float* splats_grad,
+                               uint64_t* stats) {
   if (!ranges || !out_rgba || !last_contrib || !v_out || (n && !splats_grad) || width == 0 || height == 0)
     return -1;
   std::vector<double> acc(size_t(n) * 9);
+  BwdStats st{};
   render_backward<float>(splats, n, vals, ranges, width, height, out_rgba, final_T, last_contrib, v_out,
-                         acc.data());
+                         acc.data(), &st);
+  if (stats) std::memcpy(stats, &st, sizeof st);
   for (size_t k = 0; k < acc.size(); ++k) splats_grad[k] = float(acc[k]);
   return 0;
 }
@@ -434,8 +456,9 @@ int oracle_render_backward_f64(const double* splats, uint32_t n, const uint32_t*
                                const uint32_t* last_contrib, const double* v_out, double* splats_grad) {
   if (!ranges || !out_rgba || !last_contrib || !v_out || (n && !splats_grad) || width == 0 || height == 0)
     return -1;
+  BwdStats st{};
   render_backward<double>(splats, n, vals, ranges, width, height, out_rgba, final_T, last_contrib, v_out,
-                          splats_grad);
+                          splats_grad, &st);
   return 0;
 }
 
