@@ -125,6 +125,10 @@ gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value) {
       if (value != 0 && value != 1) return fail(ctx, GSR_EINVAL, "gsr_set_option: bin keys must be 0 or 1");
       ctx->bin_keys = value != 0;
       return GSR_OK;
+    case GSR_OPT_RASTER_SKIP:
+      if (value != 0 && value != 1) return fail(ctx, GSR_EINVAL, "gsr_set_option: raster skip must be 0 or 1");
+      ctx->raster_skip = value != 0;
+      return GSR_OK;
     default:
       return fail(ctx, GSR_EINVAL, "gsr_set_option: unknown option %d", int(option));
   }

@@ -49,6 +49,7 @@ struct gsr_ctx {
   gsr::Arena arena;
   int32_t bin_scheme = GSR_BIN_PRESORT;
   bool bin_keys = true;
+  bool raster_skip = true;  // per-wave cull and the backward's all-lanes-rejected skip
 };
 
 namespace gsr {

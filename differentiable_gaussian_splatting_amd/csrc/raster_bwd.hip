@@ -1,6 +1,7 @@
-// Backward rasterization: one 256-thread workgroup per 16x16 tile, one pixel per thread, same LDS staging as the
-// forward. Each lane replays its forward decisions (the shared evaluate()) up to its last contributor and forms
-// the 9 gradient terms of each splat it composited. Per splat and wave:
+// Backward rasterization: one 256-thread workgroup per 16x16 tile (four wave64, one 8x8 block each), one pixel per
+// thread, same LDS staging and per-wave cull as the forward. Each lane replays its forward decisions (the shared
+// evaluate()) up to its last contributor and forms the 9 gradient terms of each splat it composited; a wave stops
+// at the largest last contributor among its lanes. Per splat and wave:
 //   - if no lane of the wave composited it, nothing is reduced or added (W1 warp sparse skip + exp-skip page,
 //     section 1 row "W1a": an all-invalid wave would only add +0.0);
 //   - otherwise the 9 terms are summed inside each 16-lane row with DPP (xor 1, xor 2, half-mirror, mirror) and the
@@ -36,18 +37,23 @@ __global__ __launch_bounds__(kTilePixels) void k_zero(float* __restrict__ p, uin
   if (i < count) p[i] = 0.0f;
 }
 
+// kSkip: each wave walks only the staged splats that can reach alpha >= 1/255 in its 8x8 block, and skips the
+// reduction of a splat no lane composited. Both skip only additions of +0.0 and certain rejects.
+template <bool kSkip>
 __global__ __launch_bounds__(kTilePixels) void k_backward(
     const float* __restrict__ splats, uint32_t n, const uint32_t* __restrict__ vals,
     const uint32_t* __restrict__ ranges, uint32_t num_pairs, uint32_t tiles_x, uint32_t width, uint32_t height,
     const float4* __restrict__ out_rgba, const uint32_t* __restrict__ last_contrib, const float4* __restrict__ v_out,
     float* __restrict__ splats_grad) {
+  constexpr uint32_t kWaves = kTilePixels / kWave;
   __shared__ StagedSplat s_sp[kTilePixels];
   __shared__ float s_acc[kTilePixels][kGrads];
+  __shared__ uint64_t s_mask[kWaves][kWaves];  // [reading wave][staging wave]
   __shared__ uint32_t s_max_last;
-  const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1);
+  const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const uint32_t tile = blockIdx.x;
-  const uint32_t px = (tile % tiles_x) * kTile + (tid & (kTile - 1));
-  const uint32_t py = (tile / tiles_x) * kTile + (tid / kTile);
+  const uint32_t tx0 = (tile % tiles_x) * kTile, ty0 = (tile / tiles_x) * kTile;
+  const uint32_t px = tx0 + lane_px(w, lane), py = ty0 + lane_py(w, lane);
   const bool inside = px < width && py < height;
   const uint32_t start = min(ranges[2 * tile], num_pairs);
   const uint32_t end = max(start, min(ranges[2 * tile + 1], num_pairs));
@@ -70,9 +76,10 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
   if (tid == 0) s_max_last = 0;
 #pragma unroll
   for (uint32_t q = 0; q < kGrads; ++q) s_acc[tid][q] = 0.0f;
-  // the wave's loop bound: the largest last contributor among its lanes
+  // the wave's bound: the largest last contributor among its lanes
   uint32_t wave_last = last;
   for (uint32_t off = 32; off > 0; off >>= 1) wave_last = max(wave_last, uint32_t(__shfl_xor(int(wave_last), off)));
+  wave_last = __builtin_amdgcn_readfirstlane(wave_last);
   __syncthreads();
   if (lane == 0) atomicMax(&s_max_last, wave_last);
   __syncthreads();
@@ -81,59 +88,77 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
   float T = 1.0f, ar = 0.0f, ag = 0.0f, ab = 0.0f;
   for (uint32_t b0 = start; b0 < stop; b0 += kTilePixels) {
     const uint32_t k = b0 + tid;
-    if (k < stop) s_sp[tid] = stage_splat(splats, vals[k], n);
+    uint32_t reach = 0;
+    if (k < stop) {
+      const StagedSplat st = stage_splat(splats, vals[k], n);
+      s_sp[tid] = st;
+      reach = kSkip ? reach_mask(st, float(tx0) + 0.5f, float(ty0) + 0.5f) : 0xFu;
+    }
+#pragma unroll
+    for (uint32_t q = 0; q < kWaves; ++q) {
+      const uint64_t bits = __ballot((reach >> q) & 1u);
+      if (lane == 0) s_mask[q][w] = bits;
+    }
     __syncthreads();
-    const uint32_t cnt = min(kTilePixels, stop - b0);
     const uint32_t rel0 = b0 - start;
-    const uint32_t wcnt = wave_last > rel0 ? min(cnt, wave_last - rel0) : 0u;
-    for (uint32_t j = 0; j < wcnt; ++j) {
-      const StagedSplat& s = s_sp[j];
-      float d[kGrads];
-#pragma unroll
-      for (uint32_t q = 0; q < kGrads; ++q) d[q] = 0.0f;
-      bool contrib = false;
-      Eval e;
-      if (rel0 + j < last && evaluate(s, cx, cy, e)) {
-        contrib = true;
-        const float w = e.alpha * T;
-        d[5] = w * gr;
-        d[6] = w * gg;
-        d[7] = w * gb;
-        const float one_m = 1.0f - e.alpha;
-        const float mr = s.r * w, mg = s.g * w, mb = s.bl * w;
-        const float after_r = (Cr - ar) - mr;
-        const float after_g = (Cg - ag) - mg;
-        const float after_b = (Cb - ab) - mb;
-        const float dl_da = (gr * (s.r * T - after_r / one_m) + gg * (s.g * T - after_g / one_m)) +
-                            gb * (s.bl * T - after_b / one_m);
-        if (e.oG < kAlphaMax) {
-          d[8] = dl_da * e.G;
-          const float dl_ds = -(dl_da * e.oG);
-          d[2] = dl_ds * (0.5f * e.dx * e.dx);
-          d[3] = dl_ds * (e.dx * e.dy);
-          d[4] = dl_ds * (0.5f * e.dy * e.dy);
-          d[0] = dl_ds * -(s.a * e.dx + s.b * e.dy);
-          d[1] = dl_ds * -(s.b * e.dx + s.c * e.dy);
+    for (uint32_t sw = 0; sw < kWaves; ++sw) {
+      uint64_t m = uniform64(s_mask[w][sw]);
+      while (m) {
+        const uint32_t j = sw * kWave + uint32_t(__builtin_ctzll(m));
+        m &= m - 1;
+        if (rel0 + j >= wave_last) {
+          m = 0;
+          sw = kWaves;  // past every lane's last contributor: done with this batch and the tile
+          break;
         }
-        ar = ar + mr;
-        ag = ag + mg;
-        ab = ab + mb;
-        T = T * one_m;
-      }
-      if (__ballot(contrib) == 0) continue;  // the whole wave skipped this splat
+        const StagedSplat& s = s_sp[j];
+        float d[kGrads];
 #pragma unroll
-      for (uint32_t q = 0; q < kGrads; ++q) {
-        const float row = row_sum(d[q]);
-        if ((lane & (kTile - 1)) == 0) atomicAdd(&s_acc[j][q], row);
+        for (uint32_t q = 0; q < kGrads; ++q) d[q] = 0.0f;
+        bool contrib = false;
+        Eval e;
+        if (rel0 + j < last && evaluate(s, cx, cy, e)) {
+          contrib = true;
+          const float one_m = 1.0f - e.alpha;
+          const float wgt = e.alpha * T;
+          d[5] = wgt * gr;
+          d[6] = wgt * gg;
+          d[7] = wgt * gb;
+          const float mr = s.r * wgt, mg = s.g * wgt, mb = s.bl * wgt;
+          // dL/dalpha = T (g . rgb) - (g . after) / (1 - alpha), after = C_final - acc - mine
+          const float g_rgb = __fmaf_rn(gb, s.bl, __fmaf_rn(gg, s.g, gr * s.r));
+          const float g_after = __fmaf_rn(gb, (Cb - ab) - mb, __fmaf_rn(gg, (Cg - ag) - mg, gr * ((Cr - ar) - mr)));
+          const float dl_da = __fmaf_rn(T, g_rgb, -g_after * __builtin_amdgcn_rcpf(one_m));
+          if (e.oG < kAlphaMax) {
+            d[8] = dl_da * e.G;
+            const float dl_ds = -(dl_da * e.oG);
+            const float hx = 0.5f * dl_ds * e.dx, hy = 0.5f * dl_ds * e.dy;
+            d[2] = hx * e.dx;
+            d[3] = dl_ds * e.dx * e.dy;
+            d[4] = hy * e.dy;
+            d[0] = -dl_ds * __fmaf_rn(s.a, e.dx, s.b * e.dy);
+            d[1] = -dl_ds * __fmaf_rn(s.b, e.dx, s.c * e.dy);
+          }
+          ar = ar + mr;
+          ag = ag + mg;
+          ab = ab + mb;
+          T = T * one_m;
+        }
+        if (kSkip && __ballot(contrib) == 0) continue;  // no lane composited this splat
+#pragma unroll
+        for (uint32_t q = 0; q < kGrads; ++q) {
+          const float row = row_sum(d[q]);
+          if ((lane & (kTile - 1)) == 0) atomicAdd(&s_acc[j][q], row);
+        }
       }
     }
     __syncthreads();
-    if (tid < cnt) {
+    if (k < stop) {
       const uint32_t idx = s_sp[tid].idx;
 #pragma unroll
       for (uint32_t q = 0; q < kGrads; ++q) {
         const float v = s_acc[tid][q];
-        if (v != 0.0f && idx != 0xFFFFFFFFu) atomicAdd(splats_grad + size_t(idx) * kGrads + q, v);
+        if ((!kSkip || v != 0.0f) && idx != 0xFFFFFFFFu) atomicAdd(splats_grad + size_t(idx) * kGrads + q, v);
         s_acc[tid][q] = 0.0f;
       }
     }
@@ -172,7 +197,8 @@ extern "C" gsr_status gsr_render_backward(gsr_ctx* ctx, void* stream, const floa
   if (count)
     hipLaunchKernelGGL(k_zero, dim3(uint32_t((count + kTilePixels - 1) / kTilePixels)), dim3(kTilePixels), 0, s,
                        splats_grad, count);
-  hipLaunchKernelGGL(k_backward, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, s, splats, n, bins->vals,
+  auto kernel = ctx->raster_skip ? k_backward<true> : k_backward<false>;
+  hipLaunchKernelGGL(kernel, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, s, splats, n, bins->vals,
                      bins->ranges, bins->num_pairs, tiles_x, width, height,
                      reinterpret_cast<const float4*>(out_rgba), last_contrib, reinterpret_cast<const float4*>(v_out),
                      splats_grad);

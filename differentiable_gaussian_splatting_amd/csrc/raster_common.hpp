@@ -77,6 +77,47 @@ __device__ __forceinline__ StagedSplat stage_splat(const float* __restrict__ spl
   return s;
 }
 
+// Pixel of lane `lane` of wave `w` in a 16x16 tile: each wave covers one 8x8 quarter (waves 0..3 = top-left,
+// top-right, bottom-left, bottom-right), lanes row-major inside it.
+__device__ __forceinline__ uint32_t lane_px(uint32_t w, uint32_t lane) { return 8u * (w & 1u) + (lane & 7u); }
+__device__ __forceinline__ uint32_t lane_py(uint32_t w, uint32_t lane) { return 8u * (w >> 1) + (lane >> 3); }
+
+// Which of the tile's four 8x8 wave blocks splat s can reach with alpha >= 1/255: bit q set unless the splat is
+// provably a reject at every pixel centre of block q. (x0, y0) is the first pixel centre of the tile.
+// alpha <= o exp(-sigma) reaches 1/255 only where sigma <= L = ln(255 o), an ellipse whose bounding box has
+// half-widths sqrt(2 L c / det) and sqrt(2 L a / det). The box is widened for the rounding of the fp32 sigma
+// (relative error up to about 8 eps kappa, kappa <= (a + c)^2 / det the conic's condition number) and of alpha,
+// and evaluated in fp64. A splat that is not finite or not positive definite is never culled: the per-lane
+// evaluation then decides, exactly as without the cull. Skipping a certain reject changes no result.
+__device__ __forceinline__ uint32_t reach_mask(const StagedSplat& s, float x0, float y0) {
+  if (s.o < 0.99f / 255.0f) return 0u;  // alpha <= o < 1/255 everywhere (a NaN o falls through)
+  const double a = s.a, b = s.b, c = s.c;
+  const double det = a * c - b * b;
+  if (!(det > 0.0 && a > 0.0)) return 0xFu;
+  const double L = log(255.0 * double(s.o));
+  const double kappa = (a + c) * (a + c) / det;
+  const double Lm = fmax(L, 0.0) * (1.0 + 1e-6 * kappa) + 1e-3;
+  const double rx = sqrt(2.0 * Lm * c / det) * 1.001 + 1e-3;
+  const double ry = sqrt(2.0 * Lm * a / det) * 1.001 + 1e-3;
+  const double x = s.x, y = s.y;
+  uint32_t m = 0;
+#pragma unroll
+  for (uint32_t q = 0; q < 4; ++q) {
+    const double xl = double(x0) + 8.0 * (q & 1u), xh = xl + 7.0;
+    const double yl = double(y0) + 8.0 * (q >> 1), yh = yl + 7.0;
+    const bool disjoint = (x - rx > xh) || (x + rx < xl) || (y - ry > yh) || (y + ry < yl);
+    if (!disjoint) m |= 1u << q;
+  }
+  return m;
+}
+
+// Wave-uniform 64-bit value held in scalar registers.
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return (uint64_t(hi) << 32) | lo;
+}
+
 struct Eval {
   float dx, dy, G, oG, alpha;
 };

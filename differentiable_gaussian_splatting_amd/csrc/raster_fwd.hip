@@ -1,9 +1,11 @@
-// Forward rasterization: one 256-thread workgroup (four wave64) per 16x16 tile, one pixel per thread.
+// Forward rasterization: one 256-thread workgroup (four wave64, one 8x8 pixel block each) per 16x16 tile, one
+// pixel per thread.
 //
 // The tile's depth-sorted splats are staged through LDS in batches of 256 (one record per thread), read back by
-// every lane of a wave at the same address (LDS broadcast). Each lane composites front to back in registers and
-// leaves its loop when its pixel stops; a wave leaves when all 64 lanes have; the workgroup stops staging batches
-// once all 256 pixels are done (a counted barrier). [rasterize forward + adam kernel audit page, section 1 rows (a)
+// every lane of a wave at the same address (LDS broadcast). While staging, each thread also marks which wave blocks
+// its splat can reach; each wave then walks only those slots, in order, with a scalar loop over ballot bits. Each
+// lane composites front to back in registers and stops when its pixel does; a wave leaves when all 64 lanes have;
+// the workgroup stops staging batches once all 256 pixels are done (a counted barrier). [rasterize forward + adam kernel audit page, section 1 rows (a)
 // and (b): batches of 256 staged records, a done counter for the tile, the per-lane !done loop exit]
 #include "gsr_internal.hpp"
 #include "raster_common.hpp"
@@ -11,17 +13,22 @@
 namespace gsr {
 namespace {
 
+// kCull: each wave walks only the staged splats that can reach alpha >= 1/255 in its 8x8 block (reach_mask); the
+// others are certain rejects for every lane of the wave, so skipping them changes no result.
+template <bool kCull>
 __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict__ splats, uint32_t n,
                                                          const uint32_t* __restrict__ vals,
                                                          const uint32_t* __restrict__ ranges, uint32_t num_pairs,
                                                          uint32_t tiles_x, uint32_t width, uint32_t height,
                                                          float4* __restrict__ out_rgba, float* __restrict__ final_T,
                                                          uint32_t* __restrict__ last_contrib) {
+  constexpr uint32_t kWaves = kTilePixels / kWave;
   __shared__ StagedSplat s_sp[kTilePixels];
-  const uint32_t tid = threadIdx.x;
+  __shared__ uint64_t s_mask[kWaves][kWaves];  // [reading wave][staging wave]: slots that can reach the reader
+  const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const uint32_t tile = blockIdx.x;
-  const uint32_t px = (tile % tiles_x) * kTile + (tid & (kTile - 1));
-  const uint32_t py = (tile / tiles_x) * kTile + (tid / kTile);
+  const uint32_t tx0 = (tile % tiles_x) * kTile, ty0 = (tile / tiles_x) * kTile;
+  const uint32_t px = tx0 + lane_px(w, lane), py = ty0 + lane_py(w, lane);
   const bool inside = px < width && py < height;
   const uint32_t start = min(ranges[2 * tile], num_pairs);
   const uint32_t end = max(start, min(ranges[2 * tile + 1], num_pairs));
@@ -33,24 +40,44 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
   for (uint32_t b0 = start; b0 < end; b0 += kTilePixels) {
     if (__syncthreads_count(done) == int(kTilePixels)) break;  // also orders the previous batch's reads
     const uint32_t k = b0 + tid;
-    if (k < end) s_sp[tid] = stage_splat(splats, vals[k], n);
+    uint32_t reach = 0;
+    if (k < end) {
+      const StagedSplat st = stage_splat(splats, vals[k], n);
+      s_sp[tid] = st;
+      reach = kCull ? reach_mask(st, float(tx0) + 0.5f, float(ty0) + 0.5f) : 0xFu;
+    }
+#pragma unroll
+    for (uint32_t q = 0; q < kWaves; ++q) {
+      const uint64_t bits = __ballot((reach >> q) & 1u);
+      if (lane == 0) s_mask[q][w] = bits;
+    }
     __syncthreads();
-    const uint32_t cnt = min(kTilePixels, end - b0);
-    for (uint32_t j = 0; j < cnt && !done; ++j) {
-      const StagedSplat& s = s_sp[j];
-      Eval e;
-      if (!evaluate(s, cx, cy, e)) continue;
-      const float next_T = T * (1.0f - e.alpha);
-      if (next_T < kTStop) {
-        done = true;
-        break;
+    if (__ballot(!done) == 0) continue;  // this wave is finished; keep joining the barriers
+    for (uint32_t sw = 0; sw < kWaves; ++sw) {
+      uint64_t m = uniform64(s_mask[w][sw]);
+      while (m) {
+        const uint32_t j = sw * kWave + uint32_t(__builtin_ctzll(m));
+        m &= m - 1;
+        if (!done) {
+          const StagedSplat& s = s_sp[j];
+          Eval e;
+          if (evaluate(s, cx, cy, e)) {
+            const float next_T = T * (1.0f - e.alpha);
+            if (next_T < kTStop) {
+              done = true;
+            } else {
+              const float wgt = e.alpha * T;
+              cr = cr + s.r * wgt;
+              cg = cg + s.g * wgt;
+              cb = cb + s.bl * wgt;
+              T = next_T;
+              last = b0 - start + j + 1;
+            }
+          }
+        }
+        if (__ballot(!done) == 0) break;
       }
-      const float w = e.alpha * T;
-      cr = cr + s.r * w;
-      cg = cg + s.g * w;
-      cb = cb + s.bl * w;
-      T = next_T;
-      last = b0 - start + j + 1;
+      if (__ballot(!done) == 0) break;
     }
   }
   if (inside) {
@@ -83,7 +110,8 @@ extern "C" gsr_status gsr_render_forward(gsr_ctx* ctx, void* stream, const float
   if (num_tiles >= (uint64_t(1) << 31)) return fail(ctx, GSR_EINVAL, "gsr_render_forward: too many tiles");
   gsr_status st = enter(ctx);
   if (st) return st;
-  hipLaunchKernelGGL(k_forward, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, static_cast<hipStream_t>(stream),
+  auto kernel = ctx->raster_skip ? k_forward<true> : k_forward<false>;
+  hipLaunchKernelGGL(kernel, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, static_cast<hipStream_t>(stream),
                      splats, n, bins->vals, bins->ranges, bins->num_pairs, tiles_x, width, height,
                      reinterpret_cast<float4*>(out_rgba), final_T, last_contrib);
   return check_launch(ctx, "gsr_render_forward");

@@ -62,6 +62,11 @@ gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats);
                              /*   radix sort of the pairs by tile id only                                         */
 #define GSR_BIN_KEY64 1      /*   emit pairs splat by splat and radix-sort the full 64-bit keys                   */
 #define GSR_OPT_BIN_KEYS 2   /* 1 (default): gsr_bin materialises the sorted 64-bit keys; 0: keys = NULL          */
+#define GSR_OPT_RASTER_SKIP 3 /* 1 (default): the raster kernels skip work that provably changes nothing - splats   */
+                              /*   that cannot reach alpha >= 1/255 in a wavefront's 8x8 block, and, in the        */
+                              /*   backward, splats no lane of a wavefront composited; 0: every lane evaluates    */
+                              /*   every splat up to its bound. Results are identical either way (the A/B switch  */
+                              /*   of the W1 warp sparse skip + exp-skip page, section 1, "raster_backward_sparse")*/
 gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value);
 
 /* Views into the context's arena, valid until the next gsr_bin or gsr_reserve on the same context. A caller may
