@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="iter410k")
     ap.add_argument("--bin-scheme", choices=["presort", "key64"], default="presort")
+    ap.add_argument("--raster-skip", type=int, choices=[0, 1], default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
     return ap.parse_args()
@@ -129,6 +130,7 @@ def main():
     ctx = gsr.Context(0)
     gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SCHEME, gsr.GSR_BIN_PRESORT if args.bin_scheme == "presort"
                        else gsr.GSR_BIN_KEY64)
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_RASTER_SKIP, args.raster_skip)
     splats = torch.from_numpy(sc.splats).cuda()
     depths = torch.from_numpy(sc.depths).cuda()
     v_out = torch.from_numpy(sc.v_out).cuda()
@@ -200,7 +202,7 @@ def main():
                                      "(70% s in 0.3-4 px, 30% s in 4-40 px, color_a = sigmoid(N(-2, 1.5))), "
                                      "bin + forward + backward + fused Adam over 59 fp32 params per splat",
                          "image": [W, H], "splats": N, "pairs": P, "adam_elements": adam_elems,
-                         "bin_scheme": args.bin_scheme}}
+                         "bin_scheme": args.bin_scheme, "raster_skip": args.raster_skip}}
     result["stage_ms"] = stage_ms
     result["stage_ms_median"] = stage_ms_median
     result["fwd_bwd_ms"] = stage_ms["forward"] + stage_ms["backward"]

@@ -22,26 +22,26 @@ constexpr float kAlphaMinCertain = kAlphaMin * (1.0f - 1.0f / 4096.0f);
 
 // e^x rounded to fp32, for |x| below 80. Cody-Waite reduction x = k ln2 + r with |r| <= ln2 / 2 (ln2 split into a
 // 32-bit head, exact in k * head for |k| < 2^20, and a tail), the Taylor series of e^r to degree 11 in fp64
-// (truncation below 7e-15 relative), then scaling by 2^k and one rounding to fp32. The fp64 value is within about
-// 2^-46 of e^x, so the fp32 result is the correctly rounded one except when e^x lies within 2^-46 (relative) of the
-// midpoint between two floats, i.e. about one argument in 2^22.
+// (truncation below 7e-15 relative) evaluated by Estrin's scheme (pairs, then powers r^2, r^4, r^8: every fma adds
+// a temporary, so no coefficient register is overwritten), then scaling by 2^k and one rounding to fp32. The fp64
+// value is within about 2^-46 of e^x, so the fp32 result is the correctly rounded one except when e^x lies within
+// 2^-46 (relative) of the midpoint between two floats, i.e. about one argument in 2^22.
 __host__ __device__ __forceinline__ float exp_rn(float x) {
   const double xd = double(x);
   const double k = rint(xd * 1.4426950408889634074);
   double r = fma(-k, 6.93147180369123816490e-01, xd);
   r = fma(-k, 1.90821492927058770002e-10, r);
-  double p = 1.0 / 39916800.0;         // 1/11!
-  p = fma(p, r, 1.0 / 3628800.0);      // 1/10!
-  p = fma(p, r, 1.0 / 362880.0);       // 1/9!
-  p = fma(p, r, 1.0 / 40320.0);        // 1/8!
-  p = fma(p, r, 1.0 / 5040.0);         // 1/7!
-  p = fma(p, r, 1.0 / 720.0);          // 1/6!
-  p = fma(p, r, 1.0 / 120.0);          // 1/5!
-  p = fma(p, r, 1.0 / 24.0);           // 1/4!
-  p = fma(p, r, 1.0 / 6.0);            // 1/3!
-  p = fma(p, r, 0.5);                  // 1/2!
-  p = fma(p, r, 1.0);
-  p = fma(p, r, 1.0);
+  const double r2 = r * r, r4 = r2 * r2, r8 = r4 * r4;
+  const double q0 = r + 1.0;                                  // 1 + r
+  const double q1 = fma(1.0 / 6.0, r, 0.5);                   // 1/2! + r/3!
+  const double q2 = fma(1.0 / 120.0, r, 1.0 / 24.0);          // 1/4! + r/5!
+  const double q3 = fma(1.0 / 5040.0, r, 1.0 / 720.0);        // 1/6! + r/7!
+  const double q4 = fma(1.0 / 362880.0, r, 1.0 / 40320.0);    // 1/8! + r/9!
+  const double q5 = fma(1.0 / 39916800.0, r, 1.0 / 3628800.0);  // 1/10! + r/11!
+  const double s0 = fma(q1, r2, q0);
+  const double s1 = fma(q3, r2, q2);
+  const double s2 = fma(q5, r2, q4);
+  const double p = fma(s2, r8, fma(s1, r4, s0));
   return float(ldexp(p, int(k)));
 }
 

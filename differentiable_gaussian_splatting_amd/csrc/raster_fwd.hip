@@ -36,9 +36,12 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
 
   float T = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f;
   uint32_t last = 0;
-  bool done = !inside;
+  // A lane whose pixel has stopped (or lies outside the image) moves its centre to +inf: sigma is then inf or NaN
+  // for every later splat, which evaluate() rejects, so finished lanes need no test of their own.
+  const float kFar = __builtin_huge_valf();
+  float cxe = inside ? cx : kFar;
   for (uint32_t b0 = start; b0 < end; b0 += kTilePixels) {
-    if (__syncthreads_count(done) == int(kTilePixels)) break;  // also orders the previous batch's reads
+    if (__syncthreads_count(cxe == kFar) == int(kTilePixels)) break;  // also orders the previous batch's reads
     const uint32_t k = b0 + tid;
     uint32_t reach = 0;
     if (k < end) {
@@ -52,32 +55,32 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
       if (lane == 0) s_mask[q][w] = bits;
     }
     __syncthreads();
-    if (__ballot(!done) == 0) continue;  // this wave is finished; keep joining the barriers
+    if (__ballot(cxe != kFar) == 0) continue;  // this wave is finished; keep joining the barriers
     for (uint32_t sw = 0; sw < kWaves; ++sw) {
       uint64_t m = uniform64(s_mask[w][sw]);
       while (m) {
         const uint32_t j = sw * kWave + uint32_t(__builtin_ctzll(m));
         m &= m - 1;
-        if (!done) {
-          const StagedSplat& s = s_sp[j];
-          Eval e;
-          if (evaluate(s, cx, cy, e)) {
-            const float next_T = T * (1.0f - e.alpha);
-            if (next_T < kTStop) {
-              done = true;
-            } else {
-              const float wgt = e.alpha * T;
-              cr = cr + s.r * wgt;
-              cg = cg + s.g * wgt;
-              cb = cb + s.bl * wgt;
-              T = next_T;
-              last = b0 - start + j + 1;
-            }
+        const StagedSplat& s = s_sp[j];
+        Eval e;
+        if (evaluate(s, cxe, cy, e)) {
+          const float next_T = T * (1.0f - e.alpha);
+          if (next_T < kTStop) {
+            cxe = kFar;  // the pixel stops here; this splat is not composited
+          } else {
+            const float wgt = e.alpha * T;
+            cr = cr + s.r * wgt;
+            cg = cg + s.g * wgt;
+            cb = cb + s.bl * wgt;
+            T = next_T;
+            last = b0 - start + j + 1;
           }
         }
-        if (__ballot(!done) == 0) break;
+        if (__ballot(cxe != kFar) == 0) {
+          sw = kWaves;
+          break;
+        }
       }
-      if (__ballot(!done) == 0) break;
     }
   }
   if (inside) {
