@@ -4,8 +4,9 @@
 // at the largest last contributor among its lanes. Per splat and wave:
 //   - if no lane of the wave composited it, nothing is reduced or added (W1 warp sparse skip + exp-skip page,
 //     section 1 row "W1a": an all-invalid wave would only add +0.0);
-//   - otherwise the 9 terms are summed inside each 16-lane row with DPP (xor 1, xor 2, half-mirror, mirror) and the
-//     four row sums are added into the workgroup's LDS accumulator of that splat;
+//   - otherwise the 9 terms are summed across the wave with DPP (inside each 16-lane row: xor 1, xor 2, half-mirror,
+//     mirror; across rows: row_bcast 15 and 31) and lane 63 adds the 9 sums into the workgroup's LDS accumulator of
+//     that splat;
 // after each batch one thread per splat adds the accumulated 9 values to splats_grad with global float atomics.
 // The per-pixel terms follow the forward-order form after = C_final - acc - mine of the M3 per-splat backward page
 // (section 1, rows "brush's actual structure" and "differences").
@@ -17,9 +18,12 @@ namespace {
 
 constexpr uint32_t kGrads = 9;
 
+// v + (v of the lane selected by kCtrl). Every control used here selects a lane of the same 16-lane row and all 64
+// lanes are active, so bound_ctrl (read 0 from an invalid lane) never applies; setting it lets the compiler fold the
+// move into a single v_add_f32_dpp.
 template <int kCtrl>
 __device__ __forceinline__ float dpp_add(float v) {
-  const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false);
+  const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, true);
   return v + __int_as_float(moved);
 }
 
@@ -29,6 +33,15 @@ __device__ __forceinline__ float row_sum(float v) {
   v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
   v = dpp_add<0x141>(v);  // row_half_mirror: lane i <-> 7 - i inside each half row
   v = dpp_add<0x140>(v);  // row_mirror: lane i <-> 15 - i
+  return v;
+}
+
+// Sum over all 64 lanes, left in lane 63: row sums, then row_bcast:15 (rows 1 and 3 add the last lane of the row
+// before them) and row_bcast:31 (rows 2 and 3 add lane 31). Rows a control does not enable add 0.
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+  v = row_sum(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
   return v;
 }
 
@@ -115,10 +128,9 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
         float d[kGrads];
 #pragma unroll
         for (uint32_t q = 0; q < kGrads; ++q) d[q] = 0.0f;
-        bool contrib = false;
         Eval e;
-        if (rel0 + j < last && evaluate(s, cx, cy, e)) {
-          contrib = true;
+        const bool contrib = rel0 + j < last && evaluate<false>(s, cx, cy, e);
+        if (contrib) {
           const float one_m = 1.0f - e.alpha;
           const float wgt = e.alpha * T;
           d[5] = wgt * gr;
@@ -129,26 +141,29 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
           const float g_rgb = __fmaf_rn(gb, s.bl, __fmaf_rn(gg, s.g, gr * s.r));
           const float g_after = __fmaf_rn(gb, (Cb - ab) - mb, __fmaf_rn(gg, (Cg - ag) - mg, gr * ((Cr - ar) - mr)));
           const float dl_da = __fmaf_rn(T, g_rgb, -g_after * __builtin_amdgcn_rcpf(one_m));
-          if (e.oG < kAlphaMax) {
-            d[8] = dl_da * e.G;
-            const float dl_ds = -(dl_da * e.oG);
-            const float hx = 0.5f * dl_ds * e.dx, hy = 0.5f * dl_ds * e.dy;
-            d[2] = hx * e.dx;
-            d[3] = dl_ds * e.dx * e.dy;
-            d[4] = hy * e.dy;
-            d[0] = -dl_ds * __fmaf_rn(s.a, e.dx, s.b * e.dy);
-            d[1] = -dl_ds * __fmaf_rn(s.b, e.dx, s.c * e.dy);
-          }
+          // alpha depends on o and sigma only below the clamp: the opacity and geometry terms get a 0 / 1 factor
+          const float dl_da_u = (e.oG < kAlphaMax) ? dl_da : 0.0f;
+          d[8] = dl_da_u * e.G;
+          const float dl_ds = -(dl_da_u * e.oG);
+          const float hx = 0.5f * dl_ds * e.dx, hy = 0.5f * dl_ds * e.dy;
+          d[2] = hx * e.dx;
+          d[3] = dl_ds * e.dx * e.dy;
+          d[4] = hy * e.dy;
+          d[0] = -dl_ds * __fmaf_rn(s.a, e.dx, s.b * e.dy);
+          d[1] = -dl_ds * __fmaf_rn(s.b, e.dx, s.c * e.dy);
           ar = ar + mr;
           ag = ag + mg;
           ab = ab + mb;
           T = T * one_m;
         }
         if (kSkip && __ballot(contrib) == 0) continue;  // no lane composited this splat
+        float rs[kGrads];
 #pragma unroll
-        for (uint32_t q = 0; q < kGrads; ++q) {
-          const float row = row_sum(d[q]);
-          if ((lane & (kTile - 1)) == 0) atomicAdd(&s_acc[j][q], row);
+        for (uint32_t q = 0; q < kGrads; ++q) rs[q] = wave_sum_to_lane63(d[q]);
+        if (lane == kWave - 1) {  // one LDS atomic per value and wave; the 4 waves rarely meet on one address
+          float* acc = &s_acc[j][0];
+#pragma unroll
+          for (uint32_t q = 0; q < kGrads; ++q) atomicAdd(acc + q, rs[q]);
         }
       }
     }

@@ -85,27 +85,31 @@ __device__ __forceinline__ uint32_t lane_py(uint32_t w, uint32_t lane) { return 
 // Which of the tile's four 8x8 wave blocks splat s can reach with alpha >= 1/255: bit q set unless the splat is
 // provably a reject at every pixel centre of block q. (x0, y0) is the first pixel centre of the tile.
 // alpha <= o exp(-sigma) reaches 1/255 only where sigma <= L = ln(255 o), an ellipse whose bounding box has
-// half-widths sqrt(2 L c / det) and sqrt(2 L a / det). The box is widened for the rounding of the fp32 sigma
-// (relative error up to about 8 eps kappa, kappa <= (a + c)^2 / det the conic's condition number) and of alpha,
-// and evaluated in fp64. A splat that is not finite or not positive definite is never culled: the per-lane
-// evaluation then decides, exactly as without the cull. Skipping a certain reject changes no result.
+// half-widths sqrt(2 L c / det) and sqrt(2 L a / det). Evaluated in fp32 and widened for every rounding involved:
+// the fp32 sigma of the per-lane test (relative error below 4.5 eps kappa, where kappa = (a + c)^2 / det bounds the
+// conic's condition number), the fp32 det here (relative error below 2 eps kappa), the fast log (absolute error
+// below 1e-5), sqrt and the products (a few ulp): L gets +1e-3 and the factor 1 + 1e-6 kappa, the half-widths
+// x1.001 + 0.01 px. A splat that is not finite, not positive definite or worse conditioned than kappa = 1e5 is never
+// culled: the per-lane evaluation then decides, exactly as without the cull. Skipping a certain reject changes no
+// result.
 __device__ __forceinline__ uint32_t reach_mask(const StagedSplat& s, float x0, float y0) {
   if (s.o < 0.99f / 255.0f) return 0u;  // alpha <= o < 1/255 everywhere (a NaN o falls through)
-  const double a = s.a, b = s.b, c = s.c;
-  const double det = a * c - b * b;
-  if (!(det > 0.0 && a > 0.0)) return 0xFu;
-  const double L = log(255.0 * double(s.o));
-  const double kappa = (a + c) * (a + c) / det;
-  const double Lm = fmax(L, 0.0) * (1.0 + 1e-6 * kappa) + 1e-3;
-  const double rx = sqrt(2.0 * Lm * c / det) * 1.001 + 1e-3;
-  const double ry = sqrt(2.0 * Lm * a / det) * 1.001 + 1e-3;
-  const double x = s.x, y = s.y;
+  const float det = s.a * s.c - s.b * s.b;
+  if (!(det > 0.0f && s.a > 0.0f)) return 0xFu;
+  const float apc = s.a + s.c;
+  const float kappa = apc * apc / det;
+  if (!(kappa <= 1e5f)) return 0xFu;
+  const float L = __logf(255.0f * s.o);
+  const float Lm = (fmaxf(L, 0.0f) + 1e-3f) * (1.0f + 1e-6f * kappa);
+  const float two_l_det = 2.0f * Lm / det;
+  const float rx = __builtin_sqrtf(two_l_det * s.c) * 1.001f + 0.01f;
+  const float ry = __builtin_sqrtf(two_l_det * s.a) * 1.001f + 0.01f;
   uint32_t m = 0;
 #pragma unroll
   for (uint32_t q = 0; q < 4; ++q) {
-    const double xl = double(x0) + 8.0 * (q & 1u), xh = xl + 7.0;
-    const double yl = double(y0) + 8.0 * (q >> 1), yh = yl + 7.0;
-    const bool disjoint = (x - rx > xh) || (x + rx < xl) || (y - ry > yh) || (y + ry < yl);
+    const float xl = x0 + 8.0f * float(q & 1u), xh = xl + 7.0f;
+    const float yl = y0 + 8.0f * float(q >> 1), yh = yl + 7.0f;
+    const bool disjoint = (s.x - rx > xh) || (s.x + rx < xl) || (s.y - ry > yh) || (s.y + ry < yl);
     if (!disjoint) m |= 1u << q;
   }
   return m;
@@ -128,6 +132,18 @@ struct Eval {
 // same fp32 value because halving is exact. Splats with sigma >= 5.55 are rejected before any exponential (their
 // alpha is at most e^-5.55 < 1/255 since o <= 1), and most other rejects are settled by the hardware exp2 before
 // the fp64 evaluation.
+//
+// kExactValues = true (forward): every splat that passes is evaluated with the correctly rounded G, so alpha and the
+// transmittance chain are exactly those of a plain fp32 evaluation - the stop test T' < 1e-4 depends on them.
+// kExactValues = false (backward): the decisions must still be exact (reject or composite, clamped or not), but the
+// values only feed gradient terms. G comes from the hardware exp2 (relative error below 3e-7 for sigma < 5.55) and
+// the fp64 value is computed only when o G lies within 2^-18 (relative) of 1/255 or of 0.999, where the fast value
+// could fall on the other side of a threshold.
+constexpr float kBand = 1.0f / 262144.0f;
+constexpr float kAlphaMinLo = kAlphaMin * (1.0f - kBand), kAlphaMinHi = kAlphaMin * (1.0f + kBand);
+constexpr float kAlphaMaxLo = kAlphaMax * (1.0f - kBand), kAlphaMaxHi = kAlphaMax * (1.0f + kBand);
+
+template <bool kExactValues>
 __device__ __forceinline__ bool evaluate(const StagedSplat& s, float cx, float cy, Eval& e) {
   e.dx = cx - s.x;
   e.dy = cy - s.y;
@@ -137,8 +153,15 @@ __device__ __forceinline__ bool evaluate(const StagedSplat& s, float cx, float c
   const float sigma = (t_a + t_c) + t_b;
   if (!(sigma >= 0.0f && sigma < kSigmaSkip)) return false;
   const float g_fast = __builtin_amdgcn_exp2f(sigma * -1.44269504088896341f);
-  if (s.o * g_fast < kAlphaMinCertain) return false;
-  e.G = exp_rn(-sigma);
+  const float og_fast = s.o * g_fast;
+  if (kExactValues) {
+    if (og_fast < kAlphaMinCertain) return false;
+    e.G = exp_rn(-sigma);
+  } else {
+    if (og_fast < kAlphaMinLo) return false;
+    const bool near = og_fast < kAlphaMinHi || (og_fast > kAlphaMaxLo && og_fast < kAlphaMaxHi);
+    e.G = near ? exp_rn(-sigma) : g_fast;
+  }
   e.oG = s.o * e.G;
   e.alpha = (e.oG < kAlphaMax) ? e.oG : kAlphaMax;
   return !(e.alpha < kAlphaMin);

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
         m &= m - 1;
         const StagedSplat& s = s_sp[j];
         Eval e;
-        if (evaluate(s, cxe, cy, e)) {
+        if (evaluate<true>(s, cxe, cy, e)) {
           const float next_T = T * (1.0f - e.alpha);
           if (next_T < kTStop) {
             cxe = kFar;  // the pixel stops here; this splat is not composited
