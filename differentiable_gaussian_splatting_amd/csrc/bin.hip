@@ -58,7 +58,7 @@ __device__ __forceinline__ Rect tile_rect(const float* __restrict__ sp, float de
 }
 
 __global__ __launch_bounds__(kThreads) void k_depth_keys(const float* __restrict__ depths, uint32_t n,
-                                                         uint64_t* __restrict__ keys, uint32_t* __restrict__ idx) {
+                                                         uint32_t* __restrict__ keys, uint32_t* __restrict__ idx) {
   const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
   if (i >= n) return;
   keys[i] = __float_as_uint(depths[i]);
@@ -136,11 +136,12 @@ __global__ __launch_bounds__(kThreads) void k_scan_down(const uint32_t* __restri
 
 // Emission. Workgroup b owns emission positions [256 b, 256 b + 256) and the contiguous output range of their
 // pairs; its threads walk that range in order (coalesced stores) and find each pair's splat by binary search.
-// Inside a splat the tiles go row by row. key_mode 0: (tile << 32) | depth bits; 1: tile id only.
+// Inside a splat the tiles go row by row. 64-bit keys: (tile << 32) | depth bits; 32-bit keys: the tile id only.
+template <typename K>
 __global__ __launch_bounds__(kThreads) void k_emit(const float* __restrict__ splats, const float* __restrict__ depths,
                                                    uint32_t n, const uint32_t* __restrict__ order, uint32_t tiles_x,
                                                    uint32_t tiles_y, const uint64_t* __restrict__ offsets,
-                                                   int key_mode, uint64_t num_pairs, uint64_t* __restrict__ keys,
+                                                   uint64_t num_pairs, K* __restrict__ keys,
                                                    uint32_t* __restrict__ vals) {
   __shared__ uint64_t s_off[kThreads + 1];
   __shared__ uint32_t s_tx0[kThreads], s_ty0[kThreads], s_w[kThreads], s_idx[kThreads], s_dbits[kThreads];
@@ -174,22 +175,25 @@ __global__ __launch_bounds__(kThreads) void k_emit(const float* __restrict__ spl
     const uint32_t w = s_w[lo];
     const uint32_t ty = s_ty0[lo] + k / w, tx = s_tx0[lo] + k % w;
     const uint64_t tile = uint64_t(ty) * tiles_x + tx;
-    keys[p] = key_mode == 0 ? ((tile << 32) | s_dbits[lo]) : tile;
+    if constexpr (sizeof(K) == 8)
+      keys[p] = (tile << 32) | s_dbits[lo];
+    else
+      keys[p] = K(tile);
     vals[p] = s_idx[lo];
   }
 }
 
 // Per-tile ranges from the sorted keys; thread i in [0, P] looks at the boundary between pairs i-1 and i.
 // For the presort scheme it also writes the final 64-bit keys (tile << 32 | depth bits) to keys_final.
-__global__ __launch_bounds__(kThreads) void k_ranges(const uint64_t* __restrict__ keys,
-                                                     const uint32_t* __restrict__ vals, uint32_t P,
-                                                     uint32_t num_tiles, int tile_in_low_bits,
+template <typename K>
+__global__ __launch_bounds__(kThreads) void k_ranges(const K* __restrict__ keys, const uint32_t* __restrict__ vals,
+                                                     uint32_t P, uint32_t num_tiles,
                                                      const float* __restrict__ depths, uint32_t n,
                                                      uint64_t* __restrict__ keys_final,
                                                      uint32_t* __restrict__ ranges) {
   const uint64_t i = uint64_t(blockIdx.x) * kThreads + threadIdx.x;
   if (i > P) return;
-  auto tile_of = [&](uint64_t k) -> int64_t { return tile_in_low_bits ? int64_t(k) : int64_t(k >> 32); };
+  auto tile_of = [](K k) -> int64_t { return sizeof(K) == 8 ? int64_t(uint64_t(k) >> 32) : int64_t(k); };
   const int64_t prev = i == 0 ? -1 : tile_of(keys[i - 1]);
   const int64_t cur = i == P ? int64_t(num_tiles) : tile_of(keys[i]);
   if (cur != prev) {
@@ -239,12 +243,12 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     if ((st = grow(ctx, a.order, size_t(n) * 8)) || (st = grow(ctx, a.order_alt, size_t(n) * 8)) ||
         (st = grow(ctx, a.order_vals, size_t(n) * 4)) || (st = grow(ctx, a.order_vals_alt, size_t(n) * 4)))
       return st;
-    uint64_t* ok = static_cast<uint64_t*>(a.order.ptr);
+    uint32_t* ok = static_cast<uint32_t*>(a.order.ptr);
     uint32_t* ov = static_cast<uint32_t*>(a.order_vals.ptr);
     hipLaunchKernelGGL(k_depth_keys, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, depths, n, ok, ov);
     // 4 passes (even): the sorted result lands back in (order, order_vals)
-    st = radix_sort_launch(ctx, s, ok, ov, n, 32, ok, ov, static_cast<uint64_t*>(a.order_alt.ptr),
-                           static_cast<uint32_t*>(a.order_vals_alt.ptr));
+    st = radix_sort_launch<uint32_t>(ctx, s, ok, ov, n, 32, ok, ov, static_cast<uint32_t*>(a.order_alt.ptr),
+                                     static_cast<uint32_t*>(a.order_vals_alt.ptr));
     if (st) return st;
     order = ov;
   }
@@ -271,28 +275,48 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
 
   for (int q = 0; q < 2; ++q)
     if ((st = grow(ctx, a.keys[q], size_t(P) * 8)) || (st = grow(ctx, a.vals[q], size_t(P) * 4))) return st;
-  uint64_t* k0 = static_cast<uint64_t*>(a.keys[0].ptr);
   uint32_t* v0 = static_cast<uint32_t*>(a.vals[0].ptr);
-  if (n)
-    hipLaunchKernelGGL(k_emit, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats, depths, n, order, tiles_x,
-                       tiles_y, offsets, presort ? 1 : 0, P, k0, v0);
-
-  const uint32_t key_bits = presort ? bits_of(num_tiles - 1) : 32 + bits_of(num_tiles - 1);
-  int res = 0;
-  if (key_bits > 0 && P > 0) {
-    res = (sort_passes(key_bits) & 1u) ? 1 : 0;  // odd pass count: result in buffer 1
-    st = radix_sort_launch(ctx, s, k0, v0, P, key_bits, static_cast<uint64_t*>(a.keys[res].ptr),
-                           static_cast<uint32_t*>(a.vals[res].ptr), static_cast<uint64_t*>(a.keys[1 - res].ptr),
-                           static_cast<uint32_t*>(a.vals[1 - res].ptr));
-    if (st) return st;
-  }
-  uint64_t* sorted_k = static_cast<uint64_t*>(a.keys[res].ptr);
-  uint32_t* sorted_v = static_cast<uint32_t*>(a.vals[res].ptr);
-  uint64_t* final_k = presort ? (ctx->bin_keys ? static_cast<uint64_t*>(a.keys[1 - res].ptr) : nullptr) : sorted_k;
   uint32_t* ranges = static_cast<uint32_t*>(a.ranges.ptr);
-  hipLaunchKernelGGL(k_ranges, dim3(grid_for(P + 1, kThreads)), dim3(kThreads), 0, s, sorted_k, sorted_v,
-                     uint32_t(P), uint32_t(num_tiles), presort ? 1 : 0, depths, n, presort ? final_k : nullptr,
-                     ranges);
+  const uint32_t tile_bits = bits_of(num_tiles - 1);
+  int res = 0;
+  uint64_t* final_k = nullptr;
+  if (presort) {
+    // tile ids as 32-bit keys, sorted by their tile_bits low bits
+    uint32_t* kb[2] = {static_cast<uint32_t*>(a.keys[0].ptr), static_cast<uint32_t*>(a.keys[1].ptr)};
+    if (n)
+      hipLaunchKernelGGL(k_emit<uint32_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats, depths, n,
+                         order, tiles_x, tiles_y, offsets, P, kb[0], v0);
+    if (tile_bits > 0 && P > 0) {
+      res = (sort_passes(tile_bits) & 1u) ? 1 : 0;  // odd pass count: result in buffer 1
+      st = radix_sort_launch<uint32_t>(ctx, s, kb[0], v0, P, tile_bits, kb[res],
+                                       static_cast<uint32_t*>(a.vals[res].ptr), kb[1 - res],
+                                       static_cast<uint32_t*>(a.vals[1 - res].ptr));
+      if (st) return st;
+    }
+    // the other key buffer is free now: it receives the 64-bit keys
+    final_k = ctx->bin_keys ? static_cast<uint64_t*>(a.keys[1 - res].ptr) : nullptr;
+    hipLaunchKernelGGL(k_ranges<uint32_t>, dim3(grid_for(P + 1, kThreads)), dim3(kThreads), 0, s, kb[res],
+                       static_cast<const uint32_t*>(a.vals[res].ptr), uint32_t(P), uint32_t(num_tiles), depths, n,
+                       final_k, ranges);
+  } else {
+    uint64_t* kb[2] = {static_cast<uint64_t*>(a.keys[0].ptr), static_cast<uint64_t*>(a.keys[1].ptr)};
+    if (n)
+      hipLaunchKernelGGL(k_emit<uint64_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats, depths, n,
+                         order, tiles_x, tiles_y, offsets, P, kb[0], v0);
+    if (P > 0) {
+      const uint32_t key_bits = 32 + tile_bits;
+      res = (sort_passes(key_bits) & 1u) ? 1 : 0;
+      st = radix_sort_launch<uint64_t>(ctx, s, kb[0], v0, P, key_bits, kb[res],
+                                       static_cast<uint32_t*>(a.vals[res].ptr), kb[1 - res],
+                                       static_cast<uint32_t*>(a.vals[1 - res].ptr));
+      if (st) return st;
+    }
+    final_k = kb[res];
+    hipLaunchKernelGGL(k_ranges<uint64_t>, dim3(grid_for(P + 1, kThreads)), dim3(kThreads), 0, s, kb[res],
+                       static_cast<const uint32_t*>(a.vals[res].ptr), uint32_t(P), uint32_t(num_tiles), depths, n,
+                       static_cast<uint64_t*>(nullptr), ranges);
+  }
+  uint32_t* sorted_v = static_cast<uint32_t*>(a.vals[res].ptr);
   if ((st = check_launch(ctx, "gsr_bin emit/sort/ranges"))) return st;
   out->keys = final_k;
   out->vals = sorted_v;

@@ -141,7 +141,7 @@ gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats) {
   if (st) return st;
   Arena& a = ctx->arena;
   const uint64_t ns = uint64_t(max_splats) + 1;
-  const uint64_t nb = std::max<uint64_t>(sort_blocks(std::max<uint64_t>(max_pairs, ns)), 1);
+  const uint64_t nb = std::max<uint64_t>({sort_blocks(max_pairs), sort_blocks(ns), 1});
   struct {
     DevBuf* b;
     size_t bytes;

@@ -69,13 +69,14 @@ gsr_status grow(gsr_ctx* ctx, DevBuf& b, size_t bytes);
 // Checks for launch errors after queuing kernels.
 gsr_status check_launch(gsr_ctx* ctx, const char* what);
 
-// Radix sort (sort.hip). Sorts n (key, value) pairs stably by the low key_bits bits, 8 bits per pass.
-// The result lands in (keys_out, vals_out); (tmp_keys, tmp_vals) are scratch of n elements. keys_in may equal
-// keys_out only if the pass count is even... callers pass distinct buffers. hist must hold 256 * sort_blocks(n).
+// Radix sort (sort.hip). Sorts n (key, value) pairs stably by the low key_bits bits, 8 bits per pass. The result
+// lands in (keys_out, vals_out); (tmp_keys, tmp_vals) are scratch of n elements. The first pass must not write
+// over keys_in: keys_in may equal keys_out when the pass count is even and tmp_keys when it is odd. Uses the
+// arena's histogram buffers (grown as needed).
 uint32_t sort_blocks(uint64_t n);
 uint32_t sort_passes(uint32_t key_bits);
-gsr_status radix_sort_launch(gsr_ctx* ctx, hipStream_t s, const uint64_t* keys_in, const uint32_t* vals_in,
-                             uint64_t n, uint32_t key_bits, uint64_t* keys_out, uint32_t* vals_out,
-                             uint64_t* tmp_keys, uint32_t* tmp_vals);
+template <typename K>
+gsr_status radix_sort_launch(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint32_t* vals_in, uint64_t n,
+                             uint32_t key_bits, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals);
 
 }  // namespace gsr

@@ -1,13 +1,14 @@
-// Stable LSD radix sort of (uint64 key, uint32 value) pairs, 8-bit digits, for gfx950.
+// Stable LSD radix sort of (key, uint32 value) pairs with 32- or 64-bit keys, 8-bit digits, for gfx950.
 //
 // One pass per non-constant digit, three launches per pass (reduce-then-scan, no inter-block waiting):
-//   upsweep  each 4096-key block counts its digits (wave-aggregated with ballots, then LDS);
+//   upsweep  each block of 256 x kItems keys counts its digits (wave-aggregated with ballots, then LDS);
 //   scan     one workgroup per digit turns the per-block counts into global start positions;
 //   scatter  each block ranks its keys stably with a 64-lane ballot match (the wave64 form of the simd-ballot
 //            ranking of the pages' radix scatter), reorders them by digit in LDS, and writes each digit's run
 //            contiguously.
 // Digits above key_bits are identity passes of a stable sort and are never run (the constant-digit pass skip of
-// the C0 resident arena + C1 pass skip page, section 2 table, row "C1").
+// the C0 resident arena + C1 pass skip page, section 2 table, row "C1"). Small sorts use 1024-key blocks so the
+// grid still covers the 256 compute units; large ones 2048-key blocks.
 #include "gsr_internal.hpp"
 #include "scan_common.hpp"
 
@@ -15,12 +16,13 @@ namespace gsr {
 namespace {
 
 constexpr uint32_t kThreads = 256;
-constexpr uint32_t kItems = 16;
-constexpr uint32_t kBlockKeys = kThreads * kItems;  // 4096
-constexpr uint32_t kWaveKeys = kWave * kItems;      // 1024 consecutive keys per wave
 constexpr uint32_t kRadix = 256;
+constexpr uint64_t kSmallSort = uint64_t(1) << 21;  // below this many keys: 4 keys per thread, else 8
 
-__device__ __forceinline__ uint32_t digit_of(uint64_t k, uint32_t shift) { return uint32_t(k >> shift) & 0xFFu; }
+template <typename K>
+__device__ __forceinline__ uint32_t digit_of(K k, uint32_t shift) {
+  return uint32_t(k >> shift) & 0xFFu;
+}
 
 // Lanes of this wave whose (valid) digit equals mine: eight ballots, one per digit bit.
 __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
@@ -36,13 +38,16 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
 
 __device__ __forceinline__ uint64_t lanemask_lt(uint32_t lane) { return (uint64_t(1) << lane) - 1; }
 
-__global__ __launch_bounds__(kThreads) void k_upsweep(const uint64_t* __restrict__ keys, uint64_t n, uint32_t shift,
+template <typename K, uint32_t kItems>
+__global__ __launch_bounds__(kThreads) void k_upsweep(const K* __restrict__ keys, uint64_t n, uint32_t shift,
                                                       uint32_t nb, uint32_t* __restrict__ hist) {
+  constexpr uint32_t kBlockKeys = kThreads * kItems, kWaveKeys = kWave * kItems;
   __shared__ uint32_t h[kRadix];
   const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   h[tid] = 0;
   __syncthreads();
   const uint64_t base = uint64_t(blockIdx.x) * kBlockKeys + uint64_t(w) * kWaveKeys;
+#pragma unroll
   for (uint32_t i = 0; i < kItems; ++i) {
     const uint64_t idx = base + uint64_t(i) * kWave + lane;
     const bool valid = idx < n;
@@ -73,13 +78,14 @@ __global__ __launch_bounds__(kThreads) void k_scan_rows(uint32_t* __restrict__ h
   if (threadIdx.x == 0) digit_tot[blockIdx.x] = total;
 }
 
-__global__ __launch_bounds__(kThreads) void k_scatter(const uint64_t* __restrict__ keys_in,
-                                                      const uint32_t* __restrict__ vals_in, uint64_t n,
-                                                      uint32_t shift, uint32_t nb, const uint32_t* __restrict__ hist,
-                                                      const uint32_t* __restrict__ digit_tot,
-                                                      uint64_t* __restrict__ keys_out,
+template <typename K, uint32_t kItems>
+__global__ __launch_bounds__(kThreads) void k_scatter(const K* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
+                                                      uint64_t n, uint32_t shift, uint32_t nb,
+                                                      const uint32_t* __restrict__ hist,
+                                                      const uint32_t* __restrict__ digit_tot, K* __restrict__ keys_out,
                                                       uint32_t* __restrict__ vals_out) {
-  __shared__ uint64_t s_keys[kBlockKeys];
+  constexpr uint32_t kBlockKeys = kThreads * kItems, kWaveKeys = kWave * kItems;
+  __shared__ K s_keys[kBlockKeys];
   __shared__ uint32_t s_vals[kBlockKeys];
   __shared__ uint32_t s_wave[kThreads / kWave][kRadix];  // per-wave running digit counts, then wave prefixes
   __shared__ uint32_t s_dstart[kRadix];                  // first LDS slot of each digit in this block
@@ -94,15 +100,15 @@ __global__ __launch_bounds__(kThreads) void k_scatter(const uint64_t* __restrict
   }
   __syncthreads();
 
-  uint64_t k[kItems];
+  K k[kItems];
   uint32_t v[kItems], r[kItems];
   const uint64_t base = uint64_t(blockIdx.x) * kBlockKeys + uint64_t(w) * kWaveKeys;
 #pragma unroll
   for (uint32_t i = 0; i < kItems; ++i) {
     const uint64_t idx = base + uint64_t(i) * kWave + lane;
     const bool valid = idx < n;
-    k[i] = valid ? keys_in[idx] : 0;
-    v[i] = valid ? vals_in[idx] : 0;
+    k[i] = valid ? keys_in[idx] : K(0);
+    v[i] = valid ? vals_in[idx] : 0u;
     const uint32_t d = digit_of(k[i], shift);
     const uint64_t peers = match_digit(d, valid);
     r[i] = 0;
@@ -140,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void k_scatter(const uint64_t* __restrict
   const uint64_t block0 = uint64_t(blockIdx.x) * kBlockKeys;
   const uint32_t count = uint32_t(min<uint64_t>(kBlockKeys, n - block0));
   for (uint32_t j = tid; j < count; j += kThreads) {
-    const uint64_t kk = s_keys[j];
+    const K kk = s_keys[j];
     const uint32_t d = digit_of(kk, shift);
     const uint64_t g = uint64_t(s_gbase[d]) + (j - s_dstart[d]);
     if (g < n) {  // always true for consistent counts; keeps a miscount from writing out of bounds
@@ -150,42 +156,59 @@ __global__ __launch_bounds__(kThreads) void k_scatter(const uint64_t* __restrict
   }
 }
 
+template <typename K, uint32_t kItems>
+gsr_status run_passes(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint32_t* vals_in, uint64_t n,
+                      uint32_t passes, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals) {
+  const uint32_t nb = uint32_t((n + kThreads * kItems - 1) / (kThreads * kItems));
+  gsr_status st = grow(ctx, ctx->arena.hist, size_t(nb) * kRadix * 4);
+  if (st) return st;
+  if ((st = grow(ctx, ctx->arena.digit_tot, kRadix * 4))) return st;
+  uint32_t* hist = static_cast<uint32_t*>(ctx->arena.hist.ptr);
+  uint32_t* tot = static_cast<uint32_t*>(ctx->arena.digit_tot.ptr);
+  const K* src_k = keys_in;
+  const uint32_t* src_v = vals_in;
+  for (uint32_t p = 0; p < passes; ++p) {
+    const bool to_out = ((passes - p) & 1u) == 1u;
+    K* dk = to_out ? keys_out : tmp_keys;
+    uint32_t* dv = to_out ? vals_out : tmp_vals;
+    if (p == 0 && dk == keys_in) return fail(ctx, GSR_EINVAL, "radix sort: first pass would overwrite its input");
+    const uint32_t shift = 8 * p;
+    hipLaunchKernelGGL((k_upsweep<K, kItems>), dim3(nb), dim3(kThreads), 0, s, src_k, n, shift, nb, hist);
+    hipLaunchKernelGGL(k_scan_rows, dim3(kRadix), dim3(kThreads), 0, s, hist, nb, tot);
+    hipLaunchKernelGGL((k_scatter<K, kItems>), dim3(nb), dim3(kThreads), 0, s, src_k, src_v, n, shift, nb, hist, tot,
+                       dk, dv);
+    src_k = dk;
+    src_v = dv;
+  }
+  return check_launch(ctx, "radix sort");
+}
+
 }  // namespace
 
-uint32_t sort_blocks(uint64_t n) { return uint32_t((n + kBlockKeys - 1) / kBlockKeys); }
+uint32_t sort_blocks(uint64_t n) {
+  const uint64_t per = kThreads * (n < kSmallSort ? 4u : 8u);
+  return uint32_t((n + per - 1) / per);
+}
 
 uint32_t sort_passes(uint32_t key_bits) { return (key_bits + 7) / 8; }
 
 // Pass p writes to keys_out when (passes - p) is odd and to tmp otherwise, so the last pass lands in keys_out.
 // The first destination must differ from keys_in: with an even pass count keys_in may be keys_out, with an odd
 // one keys_in may be tmp.
-gsr_status radix_sort_launch(gsr_ctx* ctx, hipStream_t s, const uint64_t* keys_in, const uint32_t* vals_in,
-                             uint64_t n, uint32_t key_bits, uint64_t* keys_out, uint32_t* vals_out,
-                             uint64_t* tmp_keys, uint32_t* tmp_vals) {
+template <typename K>
+gsr_status radix_sort_launch(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint32_t* vals_in, uint64_t n,
+                             uint32_t key_bits, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals) {
   if (n == 0) return GSR_OK;
   const uint32_t passes = sort_passes(key_bits);
-  const uint32_t nb = sort_blocks(n);
-  gsr_status st = grow(ctx, ctx->arena.hist, size_t(nb) * kRadix * 4);
-  if (st) return st;
-  if ((st = grow(ctx, ctx->arena.digit_tot, kRadix * 4))) return st;
-  uint32_t* hist = static_cast<uint32_t*>(ctx->arena.hist.ptr);
-  uint32_t* tot = static_cast<uint32_t*>(ctx->arena.digit_tot.ptr);
-  const uint64_t* src_k = keys_in;
-  const uint32_t* src_v = vals_in;
-  for (uint32_t p = 0; p < passes; ++p) {
-    const bool to_out = ((passes - p) & 1u) == 1u;
-    uint64_t* dk = to_out ? keys_out : tmp_keys;
-    uint32_t* dv = to_out ? vals_out : tmp_vals;
-    if (p == 0 && dk == keys_in) return fail(ctx, GSR_EINVAL, "radix sort: first pass would overwrite its input");
-    const uint32_t shift = 8 * p;
-    hipLaunchKernelGGL(k_upsweep, dim3(nb), dim3(kThreads), 0, s, src_k, n, shift, nb, hist);
-    hipLaunchKernelGGL(k_scan_rows, dim3(kRadix), dim3(kThreads), 0, s, hist, nb, tot);
-    hipLaunchKernelGGL(k_scatter, dim3(nb), dim3(kThreads), 0, s, src_k, src_v, n, shift, nb, hist, tot, dk, dv);
-    src_k = dk;
-    src_v = dv;
-  }
-  return check_launch(ctx, "radix sort");
+  if (n < kSmallSort)
+    return run_passes<K, 4>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals);
+  return run_passes<K, 8>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals);
 }
+
+template gsr_status radix_sort_launch<uint32_t>(gsr_ctx*, hipStream_t, const uint32_t*, const uint32_t*, uint64_t,
+                                                uint32_t, uint32_t*, uint32_t*, uint32_t*, uint32_t*);
+template gsr_status radix_sort_launch<uint64_t>(gsr_ctx*, hipStream_t, const uint64_t*, const uint32_t*, uint64_t,
+                                                uint32_t, uint64_t*, uint32_t*, uint64_t*, uint32_t*);
 
 }  // namespace gsr
 
@@ -206,6 +229,7 @@ extern "C" gsr_status gsr_radix_sort(gsr_ctx* ctx, void* stream, const uint64_t*
   if (st) return st;
   Arena& a = ctx->arena;
   if ((st = grow(ctx, a.keys[0], size_t(n) * 8)) || (st = grow(ctx, a.vals[0], size_t(n) * 4))) return st;
-  return radix_sort_launch(ctx, static_cast<hipStream_t>(stream), keys_in, vals_in, n, key_bits, keys_out, vals_out,
-                           static_cast<uint64_t*>(a.keys[0].ptr), static_cast<uint32_t*>(a.vals[0].ptr));
+  return radix_sort_launch<uint64_t>(ctx, static_cast<hipStream_t>(stream), keys_in, vals_in, n, key_bits, keys_out,
+                                     vals_out, static_cast<uint64_t*>(a.keys[0].ptr),
+                                     static_cast<uint32_t*>(a.vals[0].ptr));
 }
