@@ -4,9 +4,9 @@
 // at the largest last contributor among its lanes. Per splat and wave:
 //   - if no lane of the wave composited it, nothing is reduced or added (W1 warp sparse skip + exp-skip page,
 //     section 1 row "W1a": an all-invalid wave would only add +0.0);
-//   - otherwise the 9 terms are summed across the wave with DPP (inside each 16-lane row: xor 1, xor 2, half-mirror,
-//     mirror; across rows: row_bcast 15 and 31) and lane 63 adds the 9 sums into the workgroup's LDS accumulator of
-//     that splat;
+//   - otherwise the 9 terms are summed inside each 16-lane row with DPP (xor 1, xor 2, half-mirror, mirror), lane t
+//     of each row keeps the row sum of term t, one permlane16/32 swap pair sums that across the rows, and lanes 0..8
+//     add the 9 totals into the workgroup's LDS accumulator of that splat;
 // after each batch one thread per splat adds the accumulated 9 values to splats_grad with global float atomics.
 // The per-pixel terms follow the forward-order form after = C_final - acc - mine of the M3 per-splat backward page
 // (section 1, rows "brush's actual structure" and "differences").
@@ -36,13 +36,14 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
-// Sum over all 64 lanes, left in lane 63: row sums, then row_bcast:15 (rows 1 and 3 add the last lane of the row
-// before them) and row_bcast:31 (rows 2 and 3 add lane 31). Rows a control does not enable add 0.
-__device__ __forceinline__ float wave_sum_to_lane63(float v) {
-  v = row_sum(v);
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
-  return v;
+// Sum of x over the four 16-lane rows, in every lane: v_permlane16_swap exchanges the odd rows of one copy with the
+// even rows of the other (adding the two copies gives row pairs (0+1), (2+3)), then v_permlane32_swap exchanges the
+// halves (adding gives all four rows). Both are gfx950 cross-lane moves that take no LDS.
+__device__ __forceinline__ float sum_rows(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 __global__ __launch_bounds__(kTilePixels) void k_zero(float* __restrict__ p, uint64_t count) {
@@ -64,6 +65,7 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
   __shared__ uint64_t s_mask[kWaves][kWaves];  // [reading wave][staging wave]
   __shared__ uint32_t s_max_last;
   const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const uint32_t lane_in_row = lane & 15u;
   const uint32_t tile = blockIdx.x;
   const uint32_t tx0 = (tile % tiles_x) * kTile, ty0 = (tile / tiles_x) * kTile;
   const uint32_t px = tx0 + lane_px(w, lane), py = ty0 + lane_py(w, lane);
@@ -157,14 +159,16 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
           T = T * one_m;
         }
         if (kSkip && __ballot(contrib) == 0) continue;  // no lane composited this splat
-        float rs[kGrads];
+        // Row sums of all 9 terms, then transpose: lane t of each row keeps term t, so a single cross-row sum
+        // finishes all 9 and lanes 0..8 add them to the LDS accumulator (distinct addresses, one instruction).
+        float x = 0.0f;
 #pragma unroll
-        for (uint32_t q = 0; q < kGrads; ++q) rs[q] = wave_sum_to_lane63(d[q]);
-        if (lane == kWave - 1) {  // one LDS atomic per value and wave; the 4 waves rarely meet on one address
-          float* acc = &s_acc[j][0];
-#pragma unroll
-          for (uint32_t q = 0; q < kGrads; ++q) atomicAdd(acc + q, rs[q]);
+        for (uint32_t q = 0; q < kGrads; ++q) {
+          const float rq = row_sum(d[q]);
+          x = (lane_in_row == q) ? rq : x;
         }
+        x = sum_rows(x);
+        if (lane < kGrads) atomicAdd(&s_acc[j][lane], x);
       }
     }
     __syncthreads();
