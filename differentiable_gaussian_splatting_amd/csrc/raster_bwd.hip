@@ -146,13 +146,15 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
           // alpha depends on o and sigma only below the clamp: the opacity and geometry terms get a 0 / 1 factor
           const float dl_da_u = (e.oG < kAlphaMax) ? dl_da : 0.0f;
           d[8] = dl_da_u * e.G;
-          const float dl_ds = -(dl_da_u * e.oG);
-          const float hx = 0.5f * dl_ds * e.dx, hy = 0.5f * dl_ds * e.dy;
-          d[2] = hx * e.dx;
-          d[3] = dl_ds * e.dx * e.dy;
-          d[4] = hy * e.dy;
-          d[0] = -dl_ds * __fmaf_rn(s.a, e.dx, s.b * e.dy);
-          d[1] = -dl_ds * __fmaf_rn(s.b, e.dx, s.c * e.dy);
+          // u = -dL/dsigma: d mean = u (a dx + b dy, b dx + c dy); the conic slots hold u dx dx, u dx dy, u dy dy,
+          // whose factors -1/2, -1, -1/2 are applied once per splat when the tile's sums are flushed.
+          const float u = dl_da_u * e.oG;
+          const float ux = u * e.dx, uy = u * e.dy;
+          d[0] = __fmaf_rn(s.a, ux, s.b * uy);
+          d[1] = __fmaf_rn(s.b, ux, s.c * uy);
+          d[2] = ux * e.dx;
+          d[3] = ux * e.dy;
+          d[4] = uy * e.dy;
           ar = ar + mr;
           ag = ag + mg;
           ab = ab + mb;
@@ -174,11 +176,20 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
     __syncthreads();
     if (k < stop) {
       const uint32_t idx = s_sp[tid].idx;
+      float v[kGrads];
 #pragma unroll
       for (uint32_t q = 0; q < kGrads; ++q) {
-        const float v = s_acc[tid][q];
-        if ((!kSkip || v != 0.0f) && idx != 0xFFFFFFFFu) atomicAdd(splats_grad + size_t(idx) * kGrads + q, v);
+        v[q] = s_acc[tid][q];
         s_acc[tid][q] = 0.0f;
+      }
+      // conic slots: the tile's sums of u dx dx, u dx dy, u dy dy scale to dL/da, dL/db, dL/dc
+      v[2] = -0.5f * v[2];
+      v[3] = -v[3];
+      v[4] = -0.5f * v[4];
+      if (idx != 0xFFFFFFFFu) {
+#pragma unroll
+        for (uint32_t q = 0; q < kGrads; ++q)
+          if (!kSkip || v[q] != 0.0f) atomicAdd(splats_grad + size_t(idx) * kGrads + q, v[q]);
       }
     }
     __syncthreads();
