@@ -4,9 +4,9 @@
 // at the largest last contributor among its lanes. Per splat and wave:
 //   - if no lane of the wave composited it, nothing is reduced or added (W1 warp sparse skip + exp-skip page,
 //     section 1 row "W1a": an all-invalid wave would only add +0.0);
-//   - otherwise the 9 terms are summed inside each 16-lane row with DPP (xor 1, xor 2, half-mirror, mirror), lane t
-//     of each row keeps the row sum of term t, one permlane16/32 swap pair sums that across the rows, and lanes 0..8
-//     add the 9 totals into the workgroup's LDS accumulator of that splat;
+//   - otherwise the 9 terms are summed over the wave by a transposing butterfly (permlane32/16 swaps, then DPP) that
+//     leaves each total in one lane, and those nine lanes add them into the workgroup's LDS accumulator of that
+//     splat;
 // after each batch one thread per splat adds the accumulated 9 values to splats_grad with global float atomics.
 // The per-pixel terms follow the forward-order form after = C_final - acc - mine of the M3 per-splat backward page
 // (section 1, rows "brush's actual structure" and "differences").
@@ -27,23 +27,77 @@ __device__ __forceinline__ float dpp_add(float v) {
   return v + __int_as_float(moved);
 }
 
-// Sum over the 16 lanes of each DPP row, left in every lane of the row.
-__device__ __forceinline__ float row_sum(float v) {
-  v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
-  v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
-  v = dpp_add<0x141>(v);  // row_half_mirror: lane i <-> 7 - i inside each half row
-  v = dpp_add<0x140>(v);  // row_mirror: lane i <-> 15 - i
-  return v;
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(p[0]);
+  b = __uint_as_float(p[1]);
 }
 
-// Sum of x over the four 16-lane rows, in every lane: v_permlane16_swap exchanges the odd rows of one copy with the
-// even rows of the other (adding the two copies gives row pairs (0+1), (2+3)), then v_permlane32_swap exchanges the
-// halves (adding gives all four rows). Both are gfx950 cross-lane moves that take no LDS.
-__device__ __forceinline__ float sum_rows(float x) {
-  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(p[0]);
+  b = __uint_as_float(p[1]);
+}
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_get(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, true));
+}
+
+// Sums each of the 9 values in d over the 64 lanes of the wave with a transposing butterfly: at every halving step
+// a lane keeps one value of each pair and adds its partner's copy of it, so the number of values per lane halves
+// while the lane set summed doubles. Steps: the two 32-lane halves (v_permlane32_swap: one swap exchanges a half of
+// each of two registers, and adding the pair gives each half the sum of one of them), the row pairs of each half
+// (v_permlane16_swap, likewise), lanes i and i^8 of a row (DPP row_ror:8 with selects), lanes i and 7-i of a half
+// row (DPP row_half_mirror with selects), then lanes i^2 and i^1 (DPP quad permutes, plain sums). Every lane ends
+// with the 64-lane total of one value; which one depends only on the lane's position (see transpose_index).
+// 29 VALU instructions instead of 36 DPP adds for row sums plus a cross-row step for all 9 values.
+__device__ __forceinline__ float transpose_reduce(const float (&d)[9], uint32_t lane) {
+  float r[5];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    float a = d[2 * m], b = d[2 * m + 1];
+    swap32(a, b);
+    r[m] = a + b;
+  }
+  {
+    float a = d[8], b = 0.0f;
+    swap32(a, b);
+    r[4] = a + b;
+  }
+  float s[3];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    float a = r[2 * n], b = r[2 * n + 1];
+    swap16(a, b);
+    s[n] = a + b;
+  }
+  {
+    float a = r[4], b = 0.0f;
+    swap16(a, b);
+    s[2] = a + b;
+  }
+  const bool lo8 = (lane & 8u) == 0;
+  const float t0 = (lo8 ? s[0] : s[1]) + dpp_get<0x128>(lo8 ? s[1] : s[0]);  // row_ror:8 pairs i with i ^ 8
+  const float t1 = (lo8 ? s[2] : 0.0f) + dpp_get<0x128>(lo8 ? 0.0f : s[2]);
+  const bool lo4 = (lane & 4u) == 0;
+  float u = (lo4 ? t0 : t1) + dpp_get<0x141>(lo4 ? t1 : t0);  // row_half_mirror pairs i with 7 - i
+  u = dpp_add<0x4E>(u);                                        // quad_perm [2,3,0,1]
+  u = dpp_add<0xB1>(u);                                        // quad_perm [1,0,3,2]
+  return u;
+}
+
+// Which of the 9 values transpose_reduce leaves in this lane (-1: a padding slot), found by running the same
+// network on the indices 1..9, identical in every lane: the total is 64 (index + 1). Must be called with all 64
+// lanes active (the network reads other lanes). The inputs carry a lane-dependent +0 so that the compiler keeps
+// the lane exchanges instead of folding them as uniform constants.
+__device__ __forceinline__ int transpose_index(uint32_t lane) {
+  const float zero = 0.0f * float(lane);
+  float idx[9];
+#pragma unroll
+  for (int q = 0; q < 9; ++q) idx[q] = float(q + 1) + zero;
+  const float t = transpose_reduce(idx, lane);
+  return int(t * (1.0f / 64.0f) + 0.5f) - 1;
 }
 
 __global__ __launch_bounds__(kTilePixels) void k_zero(float* __restrict__ p, uint64_t count) {
@@ -65,7 +119,8 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
   __shared__ uint64_t s_mask[kWaves][kWaves];  // [reading wave][staging wave]
   __shared__ uint32_t s_max_last;
   const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  const uint32_t lane_in_row = lane & 15u;
+  const int slot_any = transpose_index(lane);               // all lanes take part in the exchanges
+  const int my_slot = (lane & 3u) == 0 ? slot_any : -1;      // the term this lane totals (4 copies; one adds)
   const uint32_t tile = blockIdx.x;
   const uint32_t tx0 = (tile % tiles_x) * kTile, ty0 = (tile / tiles_x) * kTile;
   const uint32_t px = tx0 + lane_px(w, lane), py = ty0 + lane_py(w, lane);
@@ -161,16 +216,9 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
           T = T * one_m;
         }
         if (kSkip && __ballot(contrib) == 0) continue;  // no lane composited this splat
-        // Row sums of all 9 terms, then transpose: lane t of each row keeps term t, so a single cross-row sum
-        // finishes all 9 and lanes 0..8 add them to the LDS accumulator (distinct addresses, one instruction).
-        float x = 0.0f;
-#pragma unroll
-        for (uint32_t q = 0; q < kGrads; ++q) {
-          const float rq = row_sum(d[q]);
-          x = (lane_in_row == q) ? rq : x;
-        }
-        x = sum_rows(x);
-        if (lane < kGrads) atomicAdd(&s_acc[j][lane], x);
+        // Wave totals of the 9 terms; nine lanes add them to the LDS accumulator (distinct addresses).
+        const float x = transpose_reduce(d, lane);
+        if (my_slot >= 0) atomicAdd(&s_acc[j][my_slot], x);
       }
     }
     __syncthreads();
