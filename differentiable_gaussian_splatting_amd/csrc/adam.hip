@@ -1,7 +1,7 @@
-// Fused Adam: every parameter group in one launch, four elements per thread with 16-byte loads and stores where the
-// group's arrays allow it. 28 bytes move per element (read grad, m, v, param; write m, v, param), so the kernel is
-// bound by HBM bandwidth. [rasterize forward + adam kernel audit page, section 2 "(f)": 5 groups, 59 elements per
-// splat, 28 B per element, 1,652 B per splat]
+// Fused Adam: every parameter group in one launch, eight elements per thread (two 16-byte non-temporal loads per
+// array, all issued before any arithmetic) where the group's arrays allow it. 28 bytes move per element (read grad,
+// m, v, param; write m, v, param), so the kernel is bound by HBM bandwidth. [rasterize forward + adam kernel audit
+// page, section 2 "(f)": 5 groups, 59 elements per splat, 28 B per element, 1,652 B per splat]
 //
 // Every operation is one IEEE fp32 operation in the order written (the file is compiled without contraction; HIP's
 // default division and square root are correctly rounded), so the step equals a plain fp32 evaluation.
@@ -11,7 +11,8 @@ namespace gsr {
 namespace {
 
 constexpr uint32_t kThreads = 256;
-constexpr uint32_t kPerThread = 4;
+constexpr uint32_t kVec = 2;                     // float4 loads per array and thread
+constexpr uint32_t kPerThread = 4 * kVec;        // elements per thread
 constexpr uint32_t kPerBlock = kThreads * kPerThread;
 
 struct AdamArgs {
@@ -42,31 +43,51 @@ __device__ __forceinline__ void adam_one(float& p, float g, float& m, float& v, 
   v = v_new;
 }
 
+// Streaming loads and stores (no reuse): non-temporal, so they do not displace anything in the caches.
+using f4 = float __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f4 ld_stream(const float* p) { return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p)); }
+__device__ __forceinline__ void st_stream(float* p, f4 v) { __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p)); }
+
 __global__ __launch_bounds__(kThreads) void k_adam(AdamArgs a) {
   uint32_t q = 0;
   while (q + 1 < a.n_groups && a.block_start[q + 1] <= blockIdx.x) ++q;
   const uint64_t count = a.count[q];
-  const uint64_t i0 = uint64_t(blockIdx.x - a.block_start[q]) * kPerBlock + uint64_t(threadIdx.x) * kPerThread;
-  if (i0 >= count) return;
+  // a block covers kPerBlock consecutive elements; thread t takes float4 number t and t + kThreads (coalesced)
+  const uint64_t blk0 = uint64_t(blockIdx.x - a.block_start[q]) * kPerBlock;
+  if (blk0 >= count) return;
   const Hyper h{a.beta1, a.beta2, 1.0f - a.beta1, 1.0f - a.beta2, a.eps, a.bc1, a.bc2, a.lr[q]};
   float* __restrict__ P = a.param[q];
   const float* __restrict__ G = a.grad[q];
   float* __restrict__ M = a.m[q];
   float* __restrict__ V = a.v[q];
-  if (a.vec4[q] && i0 + kPerThread <= count) {
-    float4 p = *reinterpret_cast<const float4*>(P + i0);
-    const float4 g = *reinterpret_cast<const float4*>(G + i0);
-    float4 m = *reinterpret_cast<const float4*>(M + i0);
-    float4 v = *reinterpret_cast<const float4*>(V + i0);
-    adam_one(p.x, g.x, m.x, v.x, h);
-    adam_one(p.y, g.y, m.y, v.y, h);
-    adam_one(p.z, g.z, m.z, v.z, h);
-    adam_one(p.w, g.w, m.w, v.w, h);
-    *reinterpret_cast<float4*>(P + i0) = p;
-    *reinterpret_cast<float4*>(M + i0) = m;
-    *reinterpret_cast<float4*>(V + i0) = v;
+  if (a.vec4[q] && blk0 + kPerBlock <= count) {
+    f4 p[kVec], g[kVec], m[kVec], v[kVec];
+#pragma unroll
+    for (uint32_t c = 0; c < kVec; ++c) {
+      const uint64_t i = blk0 + 4 * (uint64_t(c) * kThreads + threadIdx.x);
+      p[c] = ld_stream(P + i);
+      g[c] = ld_stream(G + i);
+      m[c] = ld_stream(M + i);
+      v[c] = ld_stream(V + i);
+    }
+#pragma unroll
+    for (uint32_t c = 0; c < kVec; ++c) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float pe = p[c][e], me = m[c][e], ve = v[c][e];
+        adam_one(pe, g[c][e], me, ve, h);
+        p[c][e] = pe;
+        m[c][e] = me;
+        v[c][e] = ve;
+      }
+      const uint64_t i = blk0 + 4 * (uint64_t(c) * kThreads + threadIdx.x);
+      st_stream(P + i, p[c]);
+      st_stream(M + i, m[c]);
+      st_stream(V + i, v[c]);
+    }
   } else {
-    for (uint64_t i = i0; i < count && i < i0 + kPerThread; ++i) {
+    // tail block or unaligned arrays: element by element
+    for (uint64_t i = blk0 + threadIdx.x; i < count && i < blk0 + kPerBlock; i += kThreads) {
       float p = P[i], m = M[i], v = V[i];
       adam_one(p, G[i], m, v, h);
       P[i] = p;
