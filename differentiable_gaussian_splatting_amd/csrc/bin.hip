@@ -183,26 +183,61 @@ __global__ __launch_bounds__(kThreads) void k_emit(const float* __restrict__ spl
   }
 }
 
-// Per-tile ranges from the sorted keys; thread i in [0, P] looks at the boundary between pairs i-1 and i.
-// For the presort scheme it also writes the final 64-bit keys (tile << 32 | depth bits) to keys_final.
+// Per-tile ranges from the sorted keys: the boundary between pairs i-1 and i (i in [0, P]) opens the ranges of
+// the tiles after the previous pair's and closes those before the current pair's. Each thread takes kRangeItems
+// consecutive boundaries (16-byte loads of 32-bit keys and values). For the presort scheme it also writes the final
+// 64-bit keys (tile << 32 | depth bits) to keys_final.
+constexpr uint32_t kRangeItems = 4;
+
 template <typename K>
 __global__ __launch_bounds__(kThreads) void k_ranges(const K* __restrict__ keys, const uint32_t* __restrict__ vals,
                                                      uint32_t P, uint32_t num_tiles,
                                                      const float* __restrict__ depths, uint32_t n,
                                                      uint64_t* __restrict__ keys_final,
                                                      uint32_t* __restrict__ ranges) {
-  const uint64_t i = uint64_t(blockIdx.x) * kThreads + threadIdx.x;
-  if (i > P) return;
+  const uint64_t i0 = (uint64_t(blockIdx.x) * kThreads + threadIdx.x) * kRangeItems;
+  if (i0 > P) return;
   auto tile_of = [](K k) -> int64_t { return sizeof(K) == 8 ? int64_t(uint64_t(k) >> 32) : int64_t(k); };
-  const int64_t prev = i == 0 ? -1 : tile_of(keys[i - 1]);
-  const int64_t cur = i == P ? int64_t(num_tiles) : tile_of(keys[i]);
-  if (cur != prev) {
-    for (int64_t t = prev + 1; t <= cur && t < int64_t(num_tiles); ++t) ranges[2 * t] = uint32_t(i);
-    for (int64_t t = prev < 0 ? 0 : prev; t < cur && t < int64_t(num_tiles); ++t) ranges[2 * t + 1] = uint32_t(i);
+  // tiles of pairs i0 - 1 .. i0 + kRangeItems - 1 (-1 before the first pair, num_tiles from pair P on)
+  int64_t t[kRangeItems + 1];
+  uint32_t v[kRangeItems];
+  t[0] = i0 == 0 ? -1 : tile_of(keys[i0 - 1]);
+  if (sizeof(K) == 4 && i0 + kRangeItems <= P) {
+    const uint4 kk = *reinterpret_cast<const uint4*>(keys + i0);
+    const uint4 vv = *reinterpret_cast<const uint4*>(vals + i0);
+    t[1] = kk.x, t[2] = kk.y, t[3] = kk.z, t[4] = kk.w;
+    v[0] = vv.x, v[1] = vv.y, v[2] = vv.z, v[3] = vv.w;
+  } else {
+#pragma unroll
+    for (uint32_t q = 0; q < kRangeItems; ++q) {
+      const uint64_t i = i0 + q;
+      t[q + 1] = i < P ? tile_of(keys[i]) : int64_t(num_tiles);
+      v[q] = i < P ? vals[i] : 0u;
+    }
   }
-  if (keys_final && i < P) {
-    const uint32_t v = vals[i];
-    keys_final[i] = (uint64_t(cur) << 32) | (v < n ? __float_as_uint(depths[v]) : 0u);
+#pragma unroll
+  for (uint32_t q = 0; q < kRangeItems; ++q) {
+    const uint64_t i = i0 + q;
+    const int64_t prev = t[q], cur = t[q + 1];
+    if (i <= P && cur != prev) {
+      for (int64_t u = prev + 1; u <= cur && u < int64_t(num_tiles); ++u) ranges[2 * u] = uint32_t(i);
+      for (int64_t u = prev < 0 ? 0 : prev; u < cur && u < int64_t(num_tiles); ++u) ranges[2 * u + 1] = uint32_t(i);
+    }
+  }
+  if (keys_final) {
+    uint64_t f[kRangeItems];
+#pragma unroll
+    for (uint32_t q = 0; q < kRangeItems; ++q)
+      f[q] = (uint64_t(t[q + 1]) << 32) | (v[q] < n ? __float_as_uint(depths[v[q]]) : 0u);
+    if (i0 + kRangeItems <= P) {
+      ulonglong2* dst = reinterpret_cast<ulonglong2*>(keys_final + i0);
+      dst[0] = make_ulonglong2(f[0], f[1]);
+      dst[1] = make_ulonglong2(f[2], f[3]);
+    } else {
+#pragma unroll
+      for (uint32_t q = 0; q < kRangeItems; ++q)
+        if (i0 + q < P) keys_final[i0 + q] = f[q];
+    }
   }
 }
 
@@ -295,7 +330,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     }
     // the other key buffer is free now: it receives the 64-bit keys
     final_k = ctx->bin_keys ? static_cast<uint64_t*>(a.keys[1 - res].ptr) : nullptr;
-    hipLaunchKernelGGL(k_ranges<uint32_t>, dim3(grid_for(P + 1, kThreads)), dim3(kThreads), 0, s, kb[res],
+    hipLaunchKernelGGL(k_ranges<uint32_t>, dim3(grid_for(P + 1, kThreads * kRangeItems)), dim3(kThreads), 0, s, kb[res],
                        static_cast<const uint32_t*>(a.vals[res].ptr), uint32_t(P), uint32_t(num_tiles), depths, n,
                        final_k, ranges);
   } else {
@@ -312,7 +347,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
       if (st) return st;
     }
     final_k = kb[res];
-    hipLaunchKernelGGL(k_ranges<uint64_t>, dim3(grid_for(P + 1, kThreads)), dim3(kThreads), 0, s, kb[res],
+    hipLaunchKernelGGL(k_ranges<uint64_t>, dim3(grid_for(P + 1, kThreads * kRangeItems)), dim3(kThreads), 0, s, kb[res],
                        static_cast<const uint32_t*>(a.vals[res].ptr), uint32_t(P), uint32_t(num_tiles), depths, n,
                        static_cast<uint64_t*>(nullptr), ranges);
   }

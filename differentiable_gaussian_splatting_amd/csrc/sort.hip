@@ -1,7 +1,7 @@
-// Stable LSD radix sort of (key, uint32 value) pairs with 32- or 64-bit keys, 8-bit digits, for gfx950.
+// Stable LSD radix sort of (key, uint32 value) pairs with 32- or 64-bit keys, 6- or 8-bit digits, for gfx950.
 //
 // One pass per non-constant digit, three launches per pass (reduce-then-scan, no inter-block waiting):
-//   upsweep  each block of 256 x kItems keys counts its digits (wave-aggregated with ballots, then LDS);
+//   upsweep  each block of 256 x kItems keys counts its digits (per-wave LDS histograms);
 //   scan     one workgroup per digit turns the per-block counts into global start positions;
 //   scatter  each block ranks its keys stably with a 64-lane ballot match (the wave64 form of the simd-ballot
 //            ranking of the pages' radix scatter), reorders them by digit in LDS, and writes each digit's run
@@ -16,19 +16,19 @@ namespace gsr {
 namespace {
 
 constexpr uint32_t kThreads = 256;
-constexpr uint32_t kRadix = 256;
 constexpr uint64_t kSmallSort = uint64_t(1) << 21;  // below this many keys: 4 keys per thread, else 8
 
-template <typename K>
+template <uint32_t kBits, typename K>
 __device__ __forceinline__ uint32_t digit_of(K k, uint32_t shift) {
-  return uint32_t(k >> shift) & 0xFFu;
+  return uint32_t(k >> shift) & ((1u << kBits) - 1u);
 }
 
-// Lanes of this wave whose (valid) digit equals mine: eight ballots, one per digit bit.
+// Lanes of this wave whose (valid) digit equals mine: one ballot per digit bit.
+template <uint32_t kBits>
 __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
   uint64_t peers = __ballot(valid);
 #pragma unroll
-  for (int bit = 0; bit < 8; ++bit) {
+  for (uint32_t bit = 0; bit < kBits; ++bit) {
     const bool set = (d >> bit) & 1u;
     const uint64_t b = __ballot(set);
     peers &= set ? b : ~b;
@@ -38,25 +38,33 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
 
 __device__ __forceinline__ uint64_t lanemask_lt(uint32_t lane) { return (uint64_t(1) << lane) - 1; }
 
-template <typename K, uint32_t kItems>
+// Digit counts of one block of keys. The order of the keys does not matter here, so each wave adds its keys to a
+// histogram of its own with LDS atomics (a wave's atomics on one address serialise, different waves never share
+// one), and the four are summed at the end.
+template <typename K, uint32_t kItems, uint32_t kBits>
 __global__ __launch_bounds__(kThreads) void k_upsweep(const K* __restrict__ keys, uint64_t n, uint32_t shift,
                                                       uint32_t nb, uint32_t* __restrict__ hist) {
+  constexpr uint32_t kRadix = 1u << kBits, kWaves = kThreads / kWave;
   constexpr uint32_t kBlockKeys = kThreads * kItems, kWaveKeys = kWave * kItems;
-  __shared__ uint32_t h[kRadix];
+  __shared__ uint32_t h[kWaves][kRadix];
   const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  h[tid] = 0;
-  __syncthreads();
+  for (uint32_t i = tid; i < kWaves * kRadix; i += kThreads) (&h[0][0])[i] = 0;
   const uint64_t base = uint64_t(blockIdx.x) * kBlockKeys + uint64_t(w) * kWaveKeys;
+  // every load is issued before the first count (clamped indexes: no masked loads, no wait per key)
+  K k[kItems];
 #pragma unroll
-  for (uint32_t i = 0; i < kItems; ++i) {
-    const uint64_t idx = base + uint64_t(i) * kWave + lane;
-    const bool valid = idx < n;
-    const uint32_t d = valid ? digit_of(keys[idx], shift) : 0u;
-    const uint64_t peers = match_digit(d, valid);
-    if (valid && (peers & lanemask_lt(lane)) == 0) atomicAdd(&h[d], uint32_t(__popcll(peers)));
-  }
+  for (uint32_t i = 0; i < kItems; ++i) k[i] = keys[min(base + uint64_t(i) * kWave + lane, n - 1)];
   __syncthreads();
-  hist[uint64_t(tid) * nb + blockIdx.x] = h[tid];
+#pragma unroll
+  for (uint32_t i = 0; i < kItems; ++i)
+    if (base + uint64_t(i) * kWave + lane < n) atomicAdd(&h[w][digit_of<kBits>(k[i], shift)], 1u);
+  __syncthreads();
+  if (tid < kRadix) {
+    uint32_t c = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < kWaves; ++q) c += h[q][tid];
+    hist[uint64_t(tid) * nb + blockIdx.x] = c;
+  }
 }
 
 // Block d scans row d of hist (the counts of digit d in blocks 0..nb-1) in place; digit_tot[d] = row total.
@@ -78,39 +86,46 @@ __global__ __launch_bounds__(kThreads) void k_scan_rows(uint32_t* __restrict__ h
   if (threadIdx.x == 0) digit_tot[blockIdx.x] = total;
 }
 
-template <typename K, uint32_t kItems>
+template <typename K, uint32_t kItems, uint32_t kBits>
 __global__ __launch_bounds__(kThreads) void k_scatter(const K* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
                                                       uint64_t n, uint32_t shift, uint32_t nb,
                                                       const uint32_t* __restrict__ hist,
                                                       const uint32_t* __restrict__ digit_tot, K* __restrict__ keys_out,
                                                       uint32_t* __restrict__ vals_out) {
+  constexpr uint32_t kRadix = 1u << kBits, kWaves = kThreads / kWave;
   constexpr uint32_t kBlockKeys = kThreads * kItems, kWaveKeys = kWave * kItems;
   __shared__ K s_keys[kBlockKeys];
   __shared__ uint32_t s_vals[kBlockKeys];
-  __shared__ uint32_t s_wave[kThreads / kWave][kRadix];  // per-wave running digit counts, then wave prefixes
-  __shared__ uint32_t s_dstart[kRadix];                  // first LDS slot of each digit in this block
-  __shared__ uint32_t s_gbase[kRadix];                   // global position of this block's first key of each digit
-  __shared__ uint32_t smem[kThreads / kWave];
+  __shared__ uint32_t s_wave[kWaves][kRadix];  // per-wave running digit counts, then wave prefixes
+  __shared__ uint32_t s_dstart[kRadix];        // first LDS slot of each digit in this block
+  __shared__ uint32_t s_gbase[kRadix];         // global position of this block's first key of each digit
+  __shared__ uint32_t smem[kWaves];
   const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
 
-  for (uint32_t i = tid; i < (kThreads / kWave) * kRadix; i += kThreads) (&s_wave[0][0])[i] = 0;
-  {
-    const uint32_t dbase = block_exclusive_scan<uint32_t, kThreads>(digit_tot[tid], nullptr, smem);
-    s_gbase[tid] = dbase + hist[uint64_t(tid) * nb + blockIdx.x];
-  }
-  __syncthreads();
-
+  // all key and value loads are issued first (clamped indexes, no masked loads), so their latency overlaps the
+  // block's scan of the digit bases below
   K k[kItems];
   uint32_t v[kItems], r[kItems];
   const uint64_t base = uint64_t(blockIdx.x) * kBlockKeys + uint64_t(w) * kWaveKeys;
 #pragma unroll
   for (uint32_t i = 0; i < kItems; ++i) {
-    const uint64_t idx = base + uint64_t(i) * kWave + lane;
-    const bool valid = idx < n;
-    k[i] = valid ? keys_in[idx] : K(0);
-    v[i] = valid ? vals_in[idx] : 0u;
-    const uint32_t d = digit_of(k[i], shift);
-    const uint64_t peers = match_digit(d, valid);
+    const uint64_t idx = min(base + uint64_t(i) * kWave + lane, n - 1);
+    k[i] = keys_in[idx];
+    v[i] = vals_in[idx];
+  }
+  for (uint32_t i = tid; i < kWaves * kRadix; i += kThreads) (&s_wave[0][0])[i] = 0;
+  {
+    const uint32_t dbase = block_exclusive_scan<uint32_t, kThreads>(tid < kRadix ? digit_tot[tid] : 0u, nullptr,
+                                                                     smem);
+    if (tid < kRadix) s_gbase[tid] = dbase + hist[uint64_t(tid) * nb + blockIdx.x];
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (uint32_t i = 0; i < kItems; ++i) {
+    const bool valid = base + uint64_t(i) * kWave + lane < n;
+    const uint32_t d = digit_of<kBits>(k[i], shift);
+    const uint64_t peers = match_digit<kBits>(d, valid);
     r[i] = 0;
     if (valid) {
       const uint64_t before = peers & lanemask_lt(lane);
@@ -121,22 +136,25 @@ __global__ __launch_bounds__(kThreads) void k_scatter(const K* __restrict__ keys
   }
   __syncthreads();
   {
-    // thread tid owns digit tid: wave prefixes in place, and the digit's first slot in the block
+    // thread tid < kRadix owns digit tid: wave prefixes in place, and the digit's first slot in the block
     uint32_t run = 0;
+    if (tid < kRadix) {
 #pragma unroll
-    for (uint32_t q = 0; q < kThreads / kWave; ++q) {
-      const uint32_t c = s_wave[q][tid];
-      s_wave[q][tid] = run;
-      run += c;
+      for (uint32_t q = 0; q < kWaves; ++q) {
+        const uint32_t c = s_wave[q][tid];
+        s_wave[q][tid] = run;
+        run += c;
+      }
     }
-    s_dstart[tid] = block_exclusive_scan<uint32_t, kThreads>(run, nullptr, smem);
+    const uint32_t ds = block_exclusive_scan<uint32_t, kThreads>(run, nullptr, smem);
+    if (tid < kRadix) s_dstart[tid] = ds;
   }
   __syncthreads();
 #pragma unroll
   for (uint32_t i = 0; i < kItems; ++i) {
     const uint64_t idx = base + uint64_t(i) * kWave + lane;
     if (idx < n) {
-      const uint32_t d = digit_of(k[i], shift);
+      const uint32_t d = digit_of<kBits>(k[i], shift);
       const uint32_t pos = s_dstart[d] + s_wave[w][d] + r[i];
       s_keys[pos] = k[i];
       s_vals[pos] = v[i];
@@ -147,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void k_scatter(const K* __restrict__ keys
   const uint32_t count = uint32_t(min<uint64_t>(kBlockKeys, n - block0));
   for (uint32_t j = tid; j < count; j += kThreads) {
     const K kk = s_keys[j];
-    const uint32_t d = digit_of(kk, shift);
+    const uint32_t d = digit_of<kBits>(kk, shift);
     const uint64_t g = uint64_t(s_gbase[d]) + (j - s_dstart[d]);
     if (g < n) {  // always true for consistent counts; keeps a miscount from writing out of bounds
       keys_out[g] = kk;
@@ -156,9 +174,10 @@ __global__ __launch_bounds__(kThreads) void k_scatter(const K* __restrict__ keys
   }
 }
 
-template <typename K, uint32_t kItems>
+template <typename K, uint32_t kItems, uint32_t kBits>
 gsr_status run_passes(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint32_t* vals_in, uint64_t n,
                       uint32_t passes, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals) {
+  constexpr uint32_t kRadix = 1u << kBits;
   const uint32_t nb = uint32_t((n + kThreads * kItems - 1) / (kThreads * kItems));
   gsr_status st = grow(ctx, ctx->arena.hist, size_t(nb) * kRadix * 4);
   if (st) return st;
@@ -172,16 +191,20 @@ gsr_status run_passes(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint3
     K* dk = to_out ? keys_out : tmp_keys;
     uint32_t* dv = to_out ? vals_out : tmp_vals;
     if (p == 0 && dk == keys_in) return fail(ctx, GSR_EINVAL, "radix sort: first pass would overwrite its input");
-    const uint32_t shift = 8 * p;
-    hipLaunchKernelGGL((k_upsweep<K, kItems>), dim3(nb), dim3(kThreads), 0, s, src_k, n, shift, nb, hist);
+    const uint32_t shift = kBits * p;
+    hipLaunchKernelGGL((k_upsweep<K, kItems, kBits>), dim3(nb), dim3(kThreads), 0, s, src_k, n, shift, nb, hist);
     hipLaunchKernelGGL(k_scan_rows, dim3(kRadix), dim3(kThreads), 0, s, hist, nb, tot);
-    hipLaunchKernelGGL((k_scatter<K, kItems>), dim3(nb), dim3(kThreads), 0, s, src_k, src_v, n, shift, nb, hist, tot,
-                       dk, dv);
+    hipLaunchKernelGGL((k_scatter<K, kItems, kBits>), dim3(nb), dim3(kThreads), 0, s, src_k, src_v, n, shift, nb,
+                       hist, tot, dk, dv);
     src_k = dk;
     src_v = dv;
   }
   return check_launch(ctx, "radix sort");
 }
+
+// Keys of up to 12 significant bits take 6-bit digits (64 buckets: longer runs per block in the scatter and
+// fewer ballots per key), longer keys 8-bit digits.
+constexpr uint32_t kNarrowKeyBits = 12;
 
 }  // namespace
 
@@ -190,7 +213,9 @@ uint32_t sort_blocks(uint64_t n) {
   return uint32_t((n + per - 1) / per);
 }
 
-uint32_t sort_passes(uint32_t key_bits) { return (key_bits + 7) / 8; }
+uint32_t sort_passes(uint32_t key_bits) {
+  return key_bits <= kNarrowKeyBits ? (key_bits + 5) / 6 : (key_bits + 7) / 8;
+}
 
 // Pass p writes to keys_out when (passes - p) is odd and to tmp otherwise, so the last pass lands in keys_out.
 // The first destination must differ from keys_in: with an even pass count keys_in may be keys_out, with an odd
@@ -200,9 +225,14 @@ gsr_status radix_sort_launch(gsr_ctx* ctx, hipStream_t s, const K* keys_in, cons
                              uint32_t key_bits, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals) {
   if (n == 0) return GSR_OK;
   const uint32_t passes = sort_passes(key_bits);
+  if (key_bits <= kNarrowKeyBits) {
+    if (n < kSmallSort)
+      return run_passes<K, 4, 6>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals);
+    return run_passes<K, 8, 6>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals);
+  }
   if (n < kSmallSort)
-    return run_passes<K, 4>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals);
-  return run_passes<K, 8>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals);
+    return run_passes<K, 4, 8>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals);
+  return run_passes<K, 8, 8>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals);
 }
 
 template gsr_status radix_sort_launch<uint32_t>(gsr_ctx*, hipStream_t, const uint32_t*, const uint32_t*, uint64_t,
