@@ -10,6 +10,8 @@
 //                   in (depth bits, splat index) order, which is exactly the stable order of the 64-bit keys.
 // All extent arithmetic is one IEEE fp32 operation at a time (this file is compiled without contraction), with
 // correctly rounded division and square root, so the rectangles equal a plain fp32 evaluation.
+#include <algorithm>
+
 #include "gsr_internal.hpp"
 #include "scan_common.hpp"
 
@@ -57,39 +59,61 @@ __device__ __forceinline__ Rect tile_rect(const float* __restrict__ sp, float de
   return Rect{tx0, ty0, uint32_t(cx1) - tx0 + 1, uint32_t(cy1) - ty0 + 1};
 }
 
-__global__ __launch_bounds__(kThreads) void k_depth_keys(const float* __restrict__ depths, uint32_t n,
-                                                         uint32_t* __restrict__ keys, uint32_t* __restrict__ idx) {
+// Per splat, in index order (coalesced reads of the records): the tile rectangle and its tile count, the depth
+// sort key and index for the presort scheme, and the block's count total in part[block].
+__global__ __launch_bounds__(kThreads) void k_prep(const float* __restrict__ splats, const float* __restrict__ depths,
+                                                   uint32_t n, uint32_t tiles_x, uint32_t tiles_y,
+                                                   uint4* __restrict__ rects, uint32_t* __restrict__ counts,
+                                                   uint32_t* __restrict__ dkeys, uint32_t* __restrict__ didx,
+                                                   uint64_t* __restrict__ part) {
+  __shared__ uint64_t smem[kThreads / kWave];
   const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
-  if (i >= n) return;
-  keys[i] = __float_as_uint(depths[i]);
-  idx[i] = i;
-}
-
-// counts[j] = tiles overlapped by splat order[j] (order = identity when null).
-__global__ __launch_bounds__(kThreads) void k_count(const float* __restrict__ splats, const float* __restrict__ depths,
-                                                    uint32_t n, const uint32_t* __restrict__ order,
-                                                    uint32_t tiles_x, uint32_t tiles_y,
-                                                    uint32_t* __restrict__ counts) {
-  const uint32_t j = blockIdx.x * kThreads + threadIdx.x;
-  if (j >= n) return;
-  const uint32_t i = order ? order[j] : j;
-  if (i >= n) {  // not reachable with a permutation in `order`; guards the reads below
-    counts[j] = 0;
-    return;
+  uint64_t c = 0;
+  if (i < n) {
+    const float depth = depths[i];
+    const Rect r = tile_rect(splats + size_t(i) * 9, depth, tiles_x, tiles_y);
+    rects[i] = make_uint4(r.tx0, r.ty0, r.w, r.h);
+    c = uint64_t(r.w) * r.h;
+    counts[i] = uint32_t(c);
+    if (dkeys) {
+      dkeys[i] = __float_as_uint(depth);
+      didx[i] = i;
+    }
   }
-  const Rect r = tile_rect(splats + size_t(i) * 9, depths[i], tiles_x, tiles_y);
-  counts[j] = r.w * r.h;
+  uint64_t total;
+  block_exclusive_scan<uint64_t, kThreads>(c, &total, smem);
+  if (threadIdx.x == 0) part[blockIdx.x] = total;
 }
 
-// Three-launch exclusive scan of uint32 counts into uint64 offsets; offsets[n] = total.
-__global__ __launch_bounds__(kThreads) void k_scan_reduce(const uint32_t* __restrict__ counts, uint32_t n,
+// *total = sum of part[0..nb), by one workgroup.
+__global__ __launch_bounds__(kThreads) void k_total(const uint64_t* __restrict__ part, uint32_t nb,
+                                                    uint64_t* __restrict__ total) {
+  __shared__ uint64_t smem[kThreads / kWave];
+  uint64_t sum = 0;
+  for (uint32_t j = threadIdx.x; j < nb; j += kThreads) sum += part[j];
+  uint64_t all;
+  block_exclusive_scan<uint64_t, kThreads>(sum, &all, smem);
+  if (threadIdx.x == 0) *total = all;
+}
+
+// Three-launch exclusive scan of uint32 counts into uint64 offsets; offsets[n] = total. With `order`, position j
+// takes counts[order[j]] (order must be a permutation of 0..n-1; other entries count 0).
+__device__ __forceinline__ uint32_t count_at(const uint32_t* __restrict__ counts, const uint32_t* __restrict__ order,
+                                             uint32_t n, uint64_t j) {
+  if (!order) return counts[j];
+  const uint32_t i = order[j];
+  return i < n ? counts[i] : 0u;
+}
+
+__global__ __launch_bounds__(kThreads) void k_scan_reduce(const uint32_t* __restrict__ counts,
+                                                          const uint32_t* __restrict__ order, uint32_t n,
                                                           uint64_t* __restrict__ part) {
   __shared__ uint64_t smem[kThreads / kWave];
   const uint64_t base = uint64_t(blockIdx.x) * kScanBlock;
   uint64_t sum = 0;
   for (uint32_t i = 0; i < kScanItems; ++i) {
     const uint64_t j = base + uint64_t(i) * kThreads + threadIdx.x;
-    if (j < n) sum += counts[j];
+    if (j < n) sum += count_at(counts, order, n, j);
   }
   uint64_t total;
   block_exclusive_scan<uint64_t, kThreads>(sum, &total, smem);
@@ -114,7 +138,8 @@ __global__ __launch_bounds__(kThreads) void k_scan_top(uint64_t* __restrict__ pa
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_scan_down(const uint32_t* __restrict__ counts, uint32_t n,
+__global__ __launch_bounds__(kThreads) void k_scan_down(const uint32_t* __restrict__ counts,
+                                                        const uint32_t* __restrict__ order, uint32_t n,
                                                         const uint64_t* __restrict__ part,
                                                         uint64_t* __restrict__ offsets) {
   __shared__ uint64_t smem[kThreads / kWave];
@@ -123,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void k_scan_down(const uint32_t* __restri
   uint64_t sum = 0;
 #pragma unroll
   for (uint32_t i = 0; i < kScanItems; ++i) {
-    c[i] = (base + i < n) ? counts[base + i] : 0u;
+    c[i] = (base + i < n) ? count_at(counts, order, n, base + i) : 0u;
     sum += c[i];
   }
   uint64_t run = part[blockIdx.x] + block_exclusive_scan<uint64_t, kThreads>(sum, nullptr, smem);
@@ -138,11 +163,10 @@ __global__ __launch_bounds__(kThreads) void k_scan_down(const uint32_t* __restri
 // pairs; its threads walk that range in order (coalesced stores) and find each pair's splat by binary search.
 // Inside a splat the tiles go row by row. 64-bit keys: (tile << 32) | depth bits; 32-bit keys: the tile id only.
 template <typename K>
-__global__ __launch_bounds__(kThreads) void k_emit(const float* __restrict__ splats, const float* __restrict__ depths,
+__global__ __launch_bounds__(kThreads) void k_emit(const uint4* __restrict__ rects, const float* __restrict__ depths,
                                                    uint32_t n, const uint32_t* __restrict__ order, uint32_t tiles_x,
-                                                   uint32_t tiles_y, const uint64_t* __restrict__ offsets,
-                                                   uint64_t num_pairs, K* __restrict__ keys,
-                                                   uint32_t* __restrict__ vals) {
+                                                   const uint64_t* __restrict__ offsets, uint64_t num_pairs,
+                                                   K* __restrict__ keys, uint32_t* __restrict__ vals) {
   __shared__ uint64_t s_off[kThreads + 1];
   __shared__ uint32_t s_tx0[kThreads], s_ty0[kThreads], s_w[kThreads], s_idx[kThreads], s_dbits[kThreads];
   const uint32_t j = blockIdx.x * kThreads + threadIdx.x;
@@ -151,13 +175,13 @@ __global__ __launch_bounds__(kThreads) void k_emit(const float* __restrict__ spl
   if (threadIdx.x == 0) s_off[kThreads] = offsets[min(blockIdx.x * kThreads + kThreads, n)];
   if (j < n) {
     uint32_t i = order ? order[j] : j;
-    if (i >= n) i = 0;  // not reachable with a permutation in `order`; its count is 0 then (see k_count)
-    const Rect r = tile_rect(splats + size_t(i) * 9, depths[i], tiles_x, tiles_y);
-    s_tx0[threadIdx.x] = r.tx0;
-    s_ty0[threadIdx.x] = r.ty0;
-    s_w[threadIdx.x] = r.w ? r.w : 1u;
+    if (i >= n) i = 0;  // not reachable with a permutation in `order`; its count is 0 then (see count_at)
+    const uint4 r = rects[i];
+    s_tx0[threadIdx.x] = r.x;
+    s_ty0[threadIdx.x] = r.y;
+    s_w[threadIdx.x] = r.z ? r.z : 1u;
     s_idx[threadIdx.x] = i;
-    s_dbits[threadIdx.x] = __float_as_uint(depths[i]);
+    if constexpr (sizeof(K) == 8) s_dbits[threadIdx.x] = __float_as_uint(depths[i]);
   }
   __syncthreads();
   const uint64_t begin = s_off[0], end = min(s_off[kThreads], num_pairs);
@@ -185,8 +209,8 @@ __global__ __launch_bounds__(kThreads) void k_emit(const float* __restrict__ spl
 
 // Per-tile ranges from the sorted keys: the boundary between pairs i-1 and i (i in [0, P]) opens the ranges of
 // the tiles after the previous pair's and closes those before the current pair's. Each thread takes kRangeItems
-// consecutive boundaries (16-byte loads of 32-bit keys and values). For the presort scheme it also writes the final
-// 64-bit keys (tile << 32 | depth bits) to keys_final.
+// consecutive boundaries (16-byte loads of 32-bit keys). With keys_final (the presort scheme when no sort pass
+// ran) it also writes the final 64-bit keys (tile << 32 | depth bits).
 constexpr uint32_t kRangeItems = 4;
 
 template <typename K>
@@ -204,15 +228,18 @@ __global__ __launch_bounds__(kThreads) void k_ranges(const K* __restrict__ keys,
   t[0] = i0 == 0 ? -1 : tile_of(keys[i0 - 1]);
   if (sizeof(K) == 4 && i0 + kRangeItems <= P) {
     const uint4 kk = *reinterpret_cast<const uint4*>(keys + i0);
-    const uint4 vv = *reinterpret_cast<const uint4*>(vals + i0);
     t[1] = kk.x, t[2] = kk.y, t[3] = kk.z, t[4] = kk.w;
-    v[0] = vv.x, v[1] = vv.y, v[2] = vv.z, v[3] = vv.w;
   } else {
 #pragma unroll
-    for (uint32_t q = 0; q < kRangeItems; ++q) {
-      const uint64_t i = i0 + q;
-      t[q + 1] = i < P ? tile_of(keys[i]) : int64_t(num_tiles);
-      v[q] = i < P ? vals[i] : 0u;
+    for (uint32_t q = 0; q < kRangeItems; ++q) t[q + 1] = i0 + q < P ? tile_of(keys[i0 + q]) : int64_t(num_tiles);
+  }
+  if (keys_final) {
+    if (i0 + kRangeItems <= P) {
+      const uint4 vv = *reinterpret_cast<const uint4*>(vals + i0);
+      v[0] = vv.x, v[1] = vv.y, v[2] = vv.z, v[3] = vv.w;
+    } else {
+#pragma unroll
+      for (uint32_t q = 0; q < kRangeItems; ++q) v[q] = i0 + q < P ? vals[i0 + q] : 0u;
     }
   }
 #pragma unroll
@@ -269,40 +296,55 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   const bool presort = ctx->bin_scheme == GSR_BIN_PRESORT;
 
   if ((st = grow(ctx, a.ranges, size_t(num_tiles) * 8))) return st;
-  if ((st = grow(ctx, a.counts, size_t(n + 1) * 4)) || (st = grow(ctx, a.offsets, size_t(n + 1) * 8))) return st;
-  const uint32_t nb_scan = grid_for(n, kScanBlock);
-  if ((st = grow(ctx, a.scan_part, size_t(nb_scan + 1) * 8))) return st;
-
-  const uint32_t* order = nullptr;
+  if ((st = grow(ctx, a.counts, size_t(n + 1) * 4)) || (st = grow(ctx, a.offsets, size_t(n + 1) * 8)) ||
+      (st = grow(ctx, a.rects, size_t(n + 1) * 16)))
+    return st;
+  const uint32_t nb_prep = grid_for(n, kThreads), nb_scan = grid_for(n, kScanBlock);
+  if ((st = grow(ctx, a.scan_part, size_t(std::max(nb_prep, nb_scan) + 1) * 8))) return st;
   if (presort && n) {
     if ((st = grow(ctx, a.order, size_t(n) * 8)) || (st = grow(ctx, a.order_alt, size_t(n) * 8)) ||
         (st = grow(ctx, a.order_vals, size_t(n) * 4)) || (st = grow(ctx, a.order_vals_alt, size_t(n) * 4)))
       return st;
-    uint32_t* ok = static_cast<uint32_t*>(a.order.ptr);
-    uint32_t* ov = static_cast<uint32_t*>(a.order_vals.ptr);
-    hipLaunchKernelGGL(k_depth_keys, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, depths, n, ok, ov);
+  }
+  uint4* rects = static_cast<uint4*>(a.rects.ptr);
+  uint32_t* counts = static_cast<uint32_t*>(a.counts.ptr);
+  uint64_t* offsets = static_cast<uint64_t*>(a.offsets.ptr);
+  uint64_t* part = static_cast<uint64_t*>(a.scan_part.ptr);
+  uint32_t* ok = static_cast<uint32_t*>(a.order.ptr);
+  uint32_t* ov = static_cast<uint32_t*>(a.order_vals.ptr);
+
+  // Rectangles, counts and the pair total first; the total goes to the host while the depth sort runs.
+  if (n) {
+    hipLaunchKernelGGL(k_prep, dim3(nb_prep), dim3(kThreads), 0, s, splats, depths, n, tiles_x, tiles_y, rects, counts,
+                       presort ? ok : static_cast<uint32_t*>(nullptr), presort ? ov : static_cast<uint32_t*>(nullptr),
+                       part);
+    hipLaunchKernelGGL(k_total, dim3(1), dim3(kThreads), 0, s, part, nb_prep, offsets + n);
+  } else {
+    hipLaunchKernelGGL(k_total, dim3(1), dim3(kThreads), 0, s, part, 0u, offsets);
+  }
+  if ((st = check_launch(ctx, "gsr_bin rectangles"))) return st;
+  hipError_t e = hipMemcpyAsync(a.host_total, offsets + n, sizeof(uint64_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipEventRecord(a.total_ready, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "gsr_bin pair count readback");
+
+  const uint32_t* order = nullptr;
+  if (presort && n) {
     // 4 passes (even): the sorted result lands back in (order, order_vals)
     st = radix_sort_launch<uint32_t>(ctx, s, ok, ov, n, 32, ok, ov, static_cast<uint32_t*>(a.order_alt.ptr),
                                      static_cast<uint32_t*>(a.order_vals_alt.ptr));
     if (st) return st;
     order = ov;
   }
-
-  uint32_t* counts = static_cast<uint32_t*>(a.counts.ptr);
-  uint64_t* offsets = static_cast<uint64_t*>(a.offsets.ptr);
-  uint64_t* part = static_cast<uint64_t*>(a.scan_part.ptr);
+  // offsets in emission order (depth order for the presort scheme); the scan rewrites offsets[n] with the same total
   if (n) {
-    hipLaunchKernelGGL(k_count, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats, depths, n, order, tiles_x,
-                       tiles_y, counts);
-    hipLaunchKernelGGL(k_scan_reduce, dim3(nb_scan), dim3(kThreads), 0, s, counts, n, part);
+    hipLaunchKernelGGL(k_scan_reduce, dim3(nb_scan), dim3(kThreads), 0, s, counts, order, n, part);
+    hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(kThreads), 0, s, part, nb_scan, offsets, n);
+    hipLaunchKernelGGL(k_scan_down, dim3(nb_scan), dim3(kThreads), 0, s, counts, order, n, part, offsets);
   }
-  hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(kThreads), 0, s, part, nb_scan, offsets, n);
-  if (n) hipLaunchKernelGGL(k_scan_down, dim3(nb_scan), dim3(kThreads), 0, s, counts, n, part, offsets);
-  if ((st = check_launch(ctx, "gsr_bin count/scan"))) return st;
+  if ((st = check_launch(ctx, "gsr_bin depth sort/scan"))) return st;
 
-  // The one wait of the call: the pair count sizes the arena.
-  hipError_t e = hipMemcpyAsync(a.host_total, offsets + n, sizeof(uint64_t), hipMemcpyDeviceToHost, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  // The one wait of the call: the pair count sizes the arena and the launches below.
+  e = hipEventSynchronize(a.total_ready);
   if (e != hipSuccess) return hip_fail(ctx, e, "gsr_bin pair count readback");
   const uint64_t P = *a.host_total;
   if (P >= (uint64_t(1) << 32)) return fail(ctx, GSR_EOVERFLOW, "gsr_bin: %llu pairs exceed 2^32 - 1",
@@ -319,25 +361,36 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     // tile ids as 32-bit keys, sorted by their tile_bits low bits
     uint32_t* kb[2] = {static_cast<uint32_t*>(a.keys[0].ptr), static_cast<uint32_t*>(a.keys[1].ptr)};
     if (n)
-      hipLaunchKernelGGL(k_emit<uint32_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats, depths, n,
-                         order, tiles_x, tiles_y, offsets, P, kb[0], v0);
+      hipLaunchKernelGGL(k_emit<uint32_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, rects, depths, n, order,
+                         tiles_x, offsets, P, kb[0], v0);
+    // The 64-bit keys go to the key buffer the sorted tile ids do not end in, written by the last sort pass (or by
+    // the range kernel when there is no pass).
+    bool keys_done = !ctx->bin_keys;
     if (tile_bits > 0 && P > 0) {
       res = (sort_passes(tile_bits) & 1u) ? 1 : 0;  // odd pass count: result in buffer 1
-      st = radix_sort_launch<uint32_t>(ctx, s, kb[0], v0, P, tile_bits, kb[res],
-                                       static_cast<uint32_t*>(a.vals[res].ptr), kb[1 - res],
-                                       static_cast<uint32_t*>(a.vals[1 - res].ptr));
+      uint32_t* vr = static_cast<uint32_t*>(a.vals[res].ptr);
+      uint32_t* vt = static_cast<uint32_t*>(a.vals[1 - res].ptr);
+      if (ctx->bin_keys) {
+        // the last pass reads buffer 1 - res and writes buffer res; the 64-bit keys need a third place
+        if ((st = grow(ctx, a.order_alt, std::max<size_t>(size_t(n) * 8, size_t(P) * 8)))) return st;
+        final_k = static_cast<uint64_t*>(a.order_alt.ptr);
+        st = radix_sort_tiles_final(ctx, s, kb[0], v0, P, tile_bits, kb[res], vr, kb[1 - res], vt, final_k, depths, n);
+        keys_done = true;
+      } else {
+        st = radix_sort_launch<uint32_t>(ctx, s, kb[0], v0, P, tile_bits, kb[res], vr, kb[1 - res], vt);
+      }
       if (st) return st;
     }
-    // the other key buffer is free now: it receives the 64-bit keys
-    final_k = ctx->bin_keys ? static_cast<uint64_t*>(a.keys[1 - res].ptr) : nullptr;
-    hipLaunchKernelGGL(k_ranges<uint32_t>, dim3(grid_for(P + 1, kThreads * kRangeItems)), dim3(kThreads), 0, s, kb[res],
-                       static_cast<const uint32_t*>(a.vals[res].ptr), uint32_t(P), uint32_t(num_tiles), depths, n,
-                       final_k, ranges);
+    uint64_t* ranges_final = nullptr;
+    if (!keys_done) final_k = ranges_final = static_cast<uint64_t*>(a.keys[1 - res].ptr);
+    hipLaunchKernelGGL(k_ranges<uint32_t>, dim3(grid_for(P + 1, kThreads * kRangeItems)), dim3(kThreads), 0, s,
+                       kb[res], static_cast<const uint32_t*>(a.vals[res].ptr), uint32_t(P), uint32_t(num_tiles),
+                       depths, n, ranges_final, ranges);
   } else {
     uint64_t* kb[2] = {static_cast<uint64_t*>(a.keys[0].ptr), static_cast<uint64_t*>(a.keys[1].ptr)};
     if (n)
-      hipLaunchKernelGGL(k_emit<uint64_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats, depths, n,
-                         order, tiles_x, tiles_y, offsets, P, kb[0], v0);
+      hipLaunchKernelGGL(k_emit<uint64_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, rects, depths, n, order,
+                         tiles_x, offsets, P, kb[0], v0);
     if (P > 0) {
       const uint32_t key_bits = 32 + tile_bits;
       res = (sort_passes(key_bits) & 1u) ? 1 : 0;
@@ -347,9 +400,9 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
       if (st) return st;
     }
     final_k = kb[res];
-    hipLaunchKernelGGL(k_ranges<uint64_t>, dim3(grid_for(P + 1, kThreads * kRangeItems)), dim3(kThreads), 0, s, kb[res],
-                       static_cast<const uint32_t*>(a.vals[res].ptr), uint32_t(P), uint32_t(num_tiles), depths, n,
-                       static_cast<uint64_t*>(nullptr), ranges);
+    hipLaunchKernelGGL(k_ranges<uint64_t>, dim3(grid_for(P + 1, kThreads * kRangeItems)), dim3(kThreads), 0, s,
+                       kb[res], static_cast<const uint32_t*>(a.vals[res].ptr), uint32_t(P), uint32_t(num_tiles),
+                       depths, n, static_cast<uint64_t*>(nullptr), ranges);
   }
   uint32_t* sorted_v = static_cast<uint32_t*>(a.vals[res].ptr);
   if ((st = check_launch(ctx, "gsr_bin emit/sort/ranges"))) return st;

@@ -96,6 +96,12 @@ gsr_status gsr_create(gsr_ctx** out, int hip_device) {
     return GSR_ENOMEM;
   }
   *ctx->arena.host_total = 0;
+  e = hipEventCreateWithFlags(&ctx->arena.total_ready, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    (void)hipHostFree(ctx->arena.host_total);
+    delete ctx;
+    return GSR_EHIP;
+  }
   *out = ctx;
   return GSR_OK;
 }
@@ -105,9 +111,10 @@ void gsr_destroy(gsr_ctx* ctx) {
   (void)hipSetDevice(ctx->device);
   Arena& a = ctx->arena;
   for (DevBuf* b : {&a.keys[0], &a.keys[1], &a.vals[0], &a.vals[1], &a.counts, &a.offsets, &a.order, &a.order_alt,
-                    &a.order_vals, &a.order_vals_alt, &a.scan_part, &a.hist, &a.digit_tot, &a.ranges})
+                    &a.order_vals, &a.order_vals_alt, &a.scan_part, &a.hist, &a.digit_tot, &a.ranges, &a.rects})
     release(*b);
   if (a.host_total) (void)hipHostFree(a.host_total);
+  if (a.total_ready) (void)hipEventDestroy(a.total_ready);
   delete ctx;
 }
 
@@ -149,10 +156,12 @@ gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats) {
       {&a.keys[0], size_t(max_pairs) * 8}, {&a.keys[1], size_t(max_pairs) * 8},
       {&a.vals[0], size_t(max_pairs) * 4}, {&a.vals[1], size_t(max_pairs) * 4},
       {&a.counts, size_t(ns) * 4},         {&a.offsets, size_t(ns + 1) * 8},
-      {&a.order, size_t(ns) * 8},          {&a.order_alt, size_t(ns) * 8},
+      {&a.order, size_t(ns) * 8},
+      {&a.order_alt, size_t(std::max<uint64_t>(ns, max_pairs)) * 8},  // also the presort scheme's 64-bit keys
       {&a.order_vals, size_t(ns) * 4},     {&a.order_vals_alt, size_t(ns) * 4},
-      {&a.scan_part, size_t(nb + 1) * 8},  {&a.hist, size_t(nb) * 256 * 4},
-      {&a.digit_tot, 256 * 4},
+      {&a.scan_part, size_t(std::max<uint64_t>(nb, ns / 256 + 1) + 1) * 8},
+      {&a.hist, size_t(nb) * 256 * 4},     {&a.digit_tot, 256 * 4},
+      {&a.rects, size_t(ns) * 16},
   };
   for (auto& p : plan)
     if ((st = grow(ctx, *p.b, p.bytes))) return st;

@@ -31,14 +31,16 @@ struct Arena {
   DevBuf counts;      // uint32 [splat capacity] pairs per splat (in emission order)
   DevBuf offsets;     // uint64 [splat capacity + 1] exclusive scan of counts
   DevBuf order;       // uint64 [splat capacity] depth keys / splat order for the presort scheme (x2 for ping-pong)
-  DevBuf order_alt;   // uint64 [splat capacity]
+  DevBuf order_alt;   // uint64 [max(splat, pair capacity)]: depth sort scratch, then the presort scheme's 64-bit keys
   DevBuf order_vals;  // uint32 [splat capacity]
   DevBuf order_vals_alt;
   DevBuf scan_part;   // uint64 [scan blocks] partial sums of the count scan
   DevBuf hist;        // uint32 [256 * sort blocks] per-block digit counts, then their per-digit scan
   DevBuf digit_tot;   // uint32 [256] per-digit totals of the current pass
   DevBuf ranges;      // uint32 [2 * tiles]
+  DevBuf rects;       // uint32x4 [splat capacity] tile rectangle (tx0, ty0, w, h) of each splat, natural order
   uint64_t* host_total = nullptr;  // pinned host word for the one pair-count readback
+  hipEvent_t total_ready = nullptr;  // recorded after the readback is queued
 };
 
 }  // namespace gsr
@@ -69,14 +71,21 @@ gsr_status grow(gsr_ctx* ctx, DevBuf& b, size_t bytes);
 // Checks for launch errors after queuing kernels.
 gsr_status check_launch(gsr_ctx* ctx, const char* what);
 
-// Radix sort (sort.hip). Sorts n (key, value) pairs stably by the low key_bits bits, 8 bits per pass. The result
-// lands in (keys_out, vals_out); (tmp_keys, tmp_vals) are scratch of n elements. The first pass must not write
-// over keys_in: keys_in may equal keys_out when the pass count is even and tmp_keys when it is odd. Uses the
-// arena's histogram buffers (grown as needed).
+// Radix sort (sort.hip). Sorts n (key, value) pairs stably by the low key_bits bits, 6 or 8 bits per pass
+// (sort_passes). The result lands in (keys_out, vals_out); (tmp_keys, tmp_vals) are scratch of n elements. The
+// first pass must not write over keys_in: keys_in may equal keys_out when the pass count is even and tmp_keys when
+// it is odd. Uses the arena's histogram buffers (grown as needed).
 uint32_t sort_blocks(uint64_t n);
 uint32_t sort_passes(uint32_t key_bits);
 template <typename K>
 gsr_status radix_sort_launch(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint32_t* vals_in, uint64_t n,
                              uint32_t key_bits, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals);
+
+// The same sort of 32-bit tile ids whose last pass also writes keys_final[g] = (key << 32) | bits(depths[val]) for
+// every output position g (values below n_depths; others get depth bits 0). Requires key_bits > 0.
+gsr_status radix_sort_tiles_final(gsr_ctx* ctx, hipStream_t s, const uint32_t* keys_in, const uint32_t* vals_in,
+                                  uint64_t n, uint32_t key_bits, uint32_t* keys_out, uint32_t* vals_out,
+                                  uint32_t* tmp_keys, uint32_t* tmp_vals, uint64_t* keys_final,
+                                  const float* depths, uint32_t n_depths);
 
 }  // namespace gsr

@@ -86,12 +86,15 @@ __global__ __launch_bounds__(kThreads) void k_scan_rows(uint32_t* __restrict__ h
   if (threadIdx.x == 0) digit_tot[blockIdx.x] = total;
 }
 
-template <typename K, uint32_t kItems, uint32_t kBits>
+// kFinal (32-bit tile ids, last pass): also writes keys_final[g] = (tile << 32) | bits(depths[value]).
+template <typename K, uint32_t kItems, uint32_t kBits, bool kFinal>
 __global__ __launch_bounds__(kThreads) void k_scatter(const K* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
                                                       uint64_t n, uint32_t shift, uint32_t nb,
                                                       const uint32_t* __restrict__ hist,
                                                       const uint32_t* __restrict__ digit_tot, K* __restrict__ keys_out,
-                                                      uint32_t* __restrict__ vals_out) {
+                                                      uint32_t* __restrict__ vals_out,
+                                                      uint64_t* __restrict__ keys_final,
+                                                      const float* __restrict__ depths, uint32_t n_depths) {
   constexpr uint32_t kRadix = 1u << kBits, kWaves = kThreads / kWave;
   constexpr uint32_t kBlockKeys = kThreads * kItems, kWaveKeys = kWave * kItems;
   __shared__ K s_keys[kBlockKeys];
@@ -168,15 +171,25 @@ __global__ __launch_bounds__(kThreads) void k_scatter(const K* __restrict__ keys
     const uint32_t d = digit_of<kBits>(kk, shift);
     const uint64_t g = uint64_t(s_gbase[d]) + (j - s_dstart[d]);
     if (g < n) {  // always true for consistent counts; keeps a miscount from writing out of bounds
+      const uint32_t val = s_vals[j];
       keys_out[g] = kk;
-      vals_out[g] = s_vals[j];
+      vals_out[g] = val;
+      if constexpr (kFinal)
+        keys_final[g] = (uint64_t(kk) << 32) | (val < n_depths ? __float_as_uint(depths[val]) : 0u);
     }
   }
 }
 
+struct FinalKeys {
+  uint64_t* keys = nullptr;
+  const float* depths = nullptr;
+  uint32_t n = 0;
+};
+
 template <typename K, uint32_t kItems, uint32_t kBits>
 gsr_status run_passes(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint32_t* vals_in, uint64_t n,
-                      uint32_t passes, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals) {
+                      uint32_t passes, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals,
+                      FinalKeys fin) {
   constexpr uint32_t kRadix = 1u << kBits;
   const uint32_t nb = uint32_t((n + kThreads * kItems - 1) / (kThreads * kItems));
   gsr_status st = grow(ctx, ctx->arena.hist, size_t(nb) * kRadix * 4);
@@ -194,8 +207,15 @@ gsr_status run_passes(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint3
     const uint32_t shift = kBits * p;
     hipLaunchKernelGGL((k_upsweep<K, kItems, kBits>), dim3(nb), dim3(kThreads), 0, s, src_k, n, shift, nb, hist);
     hipLaunchKernelGGL(k_scan_rows, dim3(kRadix), dim3(kThreads), 0, s, hist, nb, tot);
-    hipLaunchKernelGGL((k_scatter<K, kItems, kBits>), dim3(nb), dim3(kThreads), 0, s, src_k, src_v, n, shift, nb,
-                       hist, tot, dk, dv);
+    bool final_pass = false;
+    if constexpr (sizeof(K) == 4) final_pass = fin.keys && p + 1 == passes;
+    if (final_pass)
+      hipLaunchKernelGGL((k_scatter<K, kItems, kBits, true>), dim3(nb), dim3(kThreads), 0, s, src_k, src_v, n, shift,
+                         nb, hist, tot, dk, dv, fin.keys, fin.depths, fin.n);
+    else
+      hipLaunchKernelGGL((k_scatter<K, kItems, kBits, false>), dim3(nb), dim3(kThreads), 0, s, src_k, src_v, n, shift,
+                         nb, hist, tot, dk, dv, static_cast<uint64_t*>(nullptr), static_cast<const float*>(nullptr),
+                         0u);
     src_k = dk;
     src_v = dv;
   }
@@ -220,19 +240,37 @@ uint32_t sort_passes(uint32_t key_bits) {
 // Pass p writes to keys_out when (passes - p) is odd and to tmp otherwise, so the last pass lands in keys_out.
 // The first destination must differ from keys_in: with an even pass count keys_in may be keys_out, with an odd
 // one keys_in may be tmp.
+namespace {
 template <typename K>
-gsr_status radix_sort_launch(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint32_t* vals_in, uint64_t n,
-                             uint32_t key_bits, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals) {
+gsr_status sort_any(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint32_t* vals_in, uint64_t n,
+                    uint32_t key_bits, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals,
+                    FinalKeys fin) {
   if (n == 0) return GSR_OK;
   const uint32_t passes = sort_passes(key_bits);
   if (key_bits <= kNarrowKeyBits) {
     if (n < kSmallSort)
-      return run_passes<K, 4, 6>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals);
-    return run_passes<K, 8, 6>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals);
+      return run_passes<K, 4, 6>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals, fin);
+    return run_passes<K, 8, 6>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals, fin);
   }
   if (n < kSmallSort)
-    return run_passes<K, 4, 8>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals);
-  return run_passes<K, 8, 8>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals);
+    return run_passes<K, 4, 8>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals, fin);
+  return run_passes<K, 8, 8>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals, fin);
+}
+}  // namespace
+
+template <typename K>
+gsr_status radix_sort_launch(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint32_t* vals_in, uint64_t n,
+                             uint32_t key_bits, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals) {
+  return sort_any<K>(ctx, s, keys_in, vals_in, n, key_bits, keys_out, vals_out, tmp_keys, tmp_vals, FinalKeys{});
+}
+
+gsr_status radix_sort_tiles_final(gsr_ctx* ctx, hipStream_t s, const uint32_t* keys_in, const uint32_t* vals_in,
+                                  uint64_t n, uint32_t key_bits, uint32_t* keys_out, uint32_t* vals_out,
+                                  uint32_t* tmp_keys, uint32_t* tmp_vals, uint64_t* keys_final,
+                                  const float* depths, uint32_t n_depths) {
+  if (key_bits == 0) return fail(ctx, GSR_EINVAL, "radix sort: final keys need at least one pass");
+  return sort_any<uint32_t>(ctx, s, keys_in, vals_in, n, key_bits, keys_out, vals_out, tmp_keys, tmp_vals,
+                            FinalKeys{keys_final, depths, n_depths});
 }
 
 template gsr_status radix_sort_launch<uint32_t>(gsr_ctx*, hipStream_t, const uint32_t*, const uint32_t*, uint64_t,
