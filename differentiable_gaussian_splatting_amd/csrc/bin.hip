@@ -105,15 +105,25 @@ __device__ __forceinline__ uint32_t count_at(const uint32_t* __restrict__ counts
   return i < n ? counts[i] : 0u;
 }
 
+// With `ordered`, the gathered counts are also stored in emission order for the down-sweep.
 __global__ __launch_bounds__(kThreads) void k_scan_reduce(const uint32_t* __restrict__ counts,
                                                           const uint32_t* __restrict__ order, uint32_t n,
-                                                          uint64_t* __restrict__ part) {
+                                                          uint64_t* __restrict__ part,
+                                                          uint32_t* __restrict__ ordered) {
   __shared__ uint64_t smem[kThreads / kWave];
   const uint64_t base = uint64_t(blockIdx.x) * kScanBlock;
   uint64_t sum = 0;
+  uint32_t c[kScanItems];
+#pragma unroll
   for (uint32_t i = 0; i < kScanItems; ++i) {
     const uint64_t j = base + uint64_t(i) * kThreads + threadIdx.x;
-    if (j < n) sum += count_at(counts, order, n, j);
+    c[i] = j < n ? count_at(counts, order, n, j) : 0u;
+  }
+#pragma unroll
+  for (uint32_t i = 0; i < kScanItems; ++i) {
+    const uint64_t j = base + uint64_t(i) * kThreads + threadIdx.x;
+    sum += c[i];
+    if (ordered && j < n) ordered[j] = c[i];
   }
   uint64_t total;
   block_exclusive_scan<uint64_t, kThreads>(sum, &total, smem);
@@ -159,51 +169,117 @@ __global__ __launch_bounds__(kThreads) void k_scan_down(const uint32_t* __restri
   }
 }
 
+// k / w for k < 2^20 and w >= 1 by a float quotient (the fast reciprocal is within 2^-22 relative, so the
+// truncated quotient is off by at most one) and one correction; larger k take the integer division.
+__device__ __forceinline__ uint32_t div_small(uint32_t k, uint32_t w) {
+  if (k >= (1u << 20)) return k / w;
+  uint32_t q = uint32_t(float(k) * __builtin_amdgcn_rcpf(float(w)));
+  const int32_t r = int32_t(k) - int32_t(q * w);
+  if (r < 0)
+    --q;
+  else if (r >= int32_t(w))
+    ++q;
+  return q;
+}
+
+// Exclusive running maximum over a workgroup of kThreads threads (a multiple of 64), seeded with `carry`: thread t
+// gets the maximum of carry and the values of threads 0..t-1. Every thread must call it. `total` receives the
+// maximum over the workgroup and the carry.
+template <unsigned kThreads>
+__device__ __forceinline__ uint32_t block_exclusive_max(uint32_t v, uint32_t carry, uint32_t* total,
+                                                        uint32_t* smem) {
+  constexpr unsigned kWaves = kThreads / 64;
+  const unsigned lane = threadIdx.x & 63u, w = threadIdx.x / 64u;
+  uint32_t x = v;
+#pragma unroll
+  for (unsigned off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x = max(x, y);
+  }
+  uint32_t ex = __shfl_up(x, 1, 64);
+  if (lane == 0) ex = 0;
+  if (lane == 63) smem[w] = x;
+  __syncthreads();
+  uint32_t before = carry, all = carry;
+#pragma unroll
+  for (unsigned q = 0; q < kWaves; ++q) {
+    const uint32_t m = smem[q];
+    if (q < w) before = max(before, m);
+    all = max(all, m);
+  }
+  __syncthreads();
+  *total = all;
+  return max(before, ex);
+}
+
 // Emission. Workgroup b owns emission positions [256 b, 256 b + 256) and the contiguous output range of their
-// pairs; its threads walk that range in order (coalesced stores) and find each pair's splat by binary search.
-// Inside a splat the tiles go row by row. 64-bit keys: (tile << 32) | depth bits; 32-bit keys: the tile id only.
+// pairs, which it writes in chunks of 1024 pairs, four consecutive pairs per thread (coalesced stores). In each
+// chunk every splat marks the slot of its first pair with its position + 1, and a running maximum over the chunk
+// (seeded with the previous chunk's last owner) gives each pair its splat. Inside a splat the tiles go row by
+// row. 64-bit keys: (tile << 32) | depth bits; 32-bit keys: the tile id only.
 template <typename K>
 __global__ __launch_bounds__(kThreads) void k_emit(const uint4* __restrict__ rects, const float* __restrict__ depths,
                                                    uint32_t n, const uint32_t* __restrict__ order, uint32_t tiles_x,
                                                    const uint64_t* __restrict__ offsets, uint64_t num_pairs,
                                                    K* __restrict__ keys, uint32_t* __restrict__ vals) {
+  constexpr uint32_t kPer = 4, kChunk = kPer * kThreads;
   __shared__ uint64_t s_off[kThreads + 1];
   __shared__ uint32_t s_tx0[kThreads], s_ty0[kThreads], s_w[kThreads], s_idx[kThreads], s_dbits[kThreads];
-  const uint32_t j = blockIdx.x * kThreads + threadIdx.x;
-  const uint32_t jl = min(j, n);
-  s_off[threadIdx.x] = offsets[jl];
-  if (threadIdx.x == 0) s_off[kThreads] = offsets[min(blockIdx.x * kThreads + kThreads, n)];
+  __shared__ uint32_t s_mark[kChunk];
+  __shared__ uint32_t smem[kThreads / kWave];
+  const uint32_t tid = threadIdx.x;
+  const uint32_t j = blockIdx.x * kThreads + tid;
+  s_off[tid] = offsets[min(j, n)];
+  if (tid == 0) s_off[kThreads] = offsets[min(blockIdx.x * kThreads + kThreads, n)];
   if (j < n) {
     uint32_t i = order ? order[j] : j;
     if (i >= n) i = 0;  // not reachable with a permutation in `order`; its count is 0 then (see count_at)
     const uint4 r = rects[i];
-    s_tx0[threadIdx.x] = r.x;
-    s_ty0[threadIdx.x] = r.y;
-    s_w[threadIdx.x] = r.z ? r.z : 1u;
-    s_idx[threadIdx.x] = i;
-    if constexpr (sizeof(K) == 8) s_dbits[threadIdx.x] = __float_as_uint(depths[i]);
+    s_tx0[tid] = r.x;
+    s_ty0[tid] = r.y;
+    s_w[tid] = r.z ? r.z : 1u;
+    s_idx[tid] = i;
+    if constexpr (sizeof(K) == 8) s_dbits[tid] = __float_as_uint(depths[i]);
   }
   __syncthreads();
   const uint64_t begin = s_off[0], end = min(s_off[kThreads], num_pairs);
-  for (uint64_t p = begin + threadIdx.x; p < end; p += kThreads) {
-    // largest q with s_off[q] <= p
-    uint32_t lo = 0, hi = kThreads;  // invariant: s_off[lo] <= p < s_off[hi]
-    while (hi - lo > 1) {
-      const uint32_t mid = (lo + hi) >> 1;
-      if (s_off[mid] <= p)
-        lo = mid;
-      else
-        hi = mid;
+  const uint64_t my_start = s_off[tid];
+  const bool has_pairs = s_off[tid + 1] > my_start;
+  uint32_t carry = 0;
+  for (uint64_t c0 = begin; c0 < end; c0 += kChunk) {
+#pragma unroll
+    for (uint32_t e = 0; e < kPer; ++e) s_mark[e * kThreads + tid] = 0;
+    __syncthreads();
+    // splats with pairs have distinct first positions
+    if (has_pairs && my_start >= c0 && my_start < c0 + kChunk) s_mark[my_start - c0] = tid + 1;
+    __syncthreads();
+    uint32_t m[kPer];
+    uint32_t run = 0;
+#pragma unroll
+    for (uint32_t e = 0; e < kPer; ++e) {
+      run = max(run, s_mark[kPer * tid + e]);
+      m[e] = run;
     }
-    const uint32_t k = uint32_t(p - s_off[lo]);
-    const uint32_t w = s_w[lo];
-    const uint32_t ty = s_ty0[lo] + k / w, tx = s_tx0[lo] + k % w;
-    const uint64_t tile = uint64_t(ty) * tiles_x + tx;
-    if constexpr (sizeof(K) == 8)
-      keys[p] = (tile << 32) | s_dbits[lo];
-    else
-      keys[p] = K(tile);
-    vals[p] = s_idx[lo];
+    uint32_t chunk_max;
+    const uint32_t before = block_exclusive_max<kThreads>(run, carry, &chunk_max, smem);
+#pragma unroll
+    for (uint32_t e = 0; e < kPer; ++e) {
+      const uint64_t p = c0 + kPer * tid + e;
+      const uint32_t owner = max(before, m[e]);  // >= 1 for every pair below end
+      if (p < end && owner > 0) {
+        const uint32_t q = owner - 1;
+        const uint32_t k = uint32_t(p - s_off[q]);
+        const uint32_t w = s_w[q];
+        const uint32_t row = div_small(k, w);
+        const uint64_t tile = uint64_t(s_ty0[q] + row) * tiles_x + (s_tx0[q] + (k - row * w));
+        if constexpr (sizeof(K) == 8)
+          keys[p] = (tile << 32) | s_dbits[q];
+        else
+          keys[p] = K(tile);
+        vals[p] = s_idx[q];
+      }
+    }
+    carry = chunk_max;
   }
 }
 
@@ -337,9 +413,12 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   }
   // offsets in emission order (depth order for the presort scheme); the scan rewrites offsets[n] with the same total
   if (n) {
-    hipLaunchKernelGGL(k_scan_reduce, dim3(nb_scan), dim3(kThreads), 0, s, counts, order, n, part);
+    // the presort scheme gathers its counts once, into the depth sort's (now free) value scratch
+    uint32_t* ordered = order ? static_cast<uint32_t*>(a.order_vals_alt.ptr) : nullptr;
+    hipLaunchKernelGGL(k_scan_reduce, dim3(nb_scan), dim3(kThreads), 0, s, counts, order, n, part, ordered);
     hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(kThreads), 0, s, part, nb_scan, offsets, n);
-    hipLaunchKernelGGL(k_scan_down, dim3(nb_scan), dim3(kThreads), 0, s, counts, order, n, part, offsets);
+    hipLaunchKernelGGL(k_scan_down, dim3(nb_scan), dim3(kThreads), 0, s, order ? ordered : counts,
+                       static_cast<const uint32_t*>(nullptr), n, part, offsets);
   }
   if ((st = check_launch(ctx, "gsr_bin depth sort/scan"))) return st;
 
