@@ -231,9 +231,13 @@ def main():
             "adam": {"bound": "hbm", "achieved": adam_bytes / (stage_ms["adam"] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "work_per_launch": adam_bytes},
         }
-        for r in roofs.values():
+        # HBM bytes per launch from the committed counter summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated);
+        # null when the kernel's sources changed since the counters were taken
+        from differentiable_gaussian_splatting_amd import profiling
+        traffic_md = os.path.join(ROOT, "profiles", f"hbm_counters_{args.workload}.md")
+        for k, r in roofs.items():
             r["frac"] = r["achieved"] / r["peak"]
-            r["traffic"] = None
+            r["traffic"] = profiling.traffic_for(profiling.STAGE_KERNEL[k], traffic_md)
         for k in ("forward", "backward"):
             roofs[k]["frac_of_published_157_3"] = roofs[k]["achieved"] / ALU_PUBLISHED_TFLOPS
         dominant = max(("forward", "backward", "adam"), key=lambda k: stage_ms[k])
