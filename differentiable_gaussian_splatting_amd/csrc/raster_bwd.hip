@@ -7,7 +7,8 @@
 //   - otherwise the 9 terms are summed over the wave by a transposing butterfly (permlane32/16 swaps, then DPP) that
 //     leaves each total in one lane, and those nine lanes add them into the workgroup's LDS accumulator of that
 //     splat;
-// after each batch one thread per splat adds the accumulated 9 values to splats_grad with global float atomics.
+// after each batch one thread per splat adds the accumulated 9 values to splats_grad with global float atomics,
+// which complete while the next batch is processed (the loop's barriers order LDS only).
 // The per-pixel terms follow the forward-order form after = C_final - acc - mine of the M3 per-splat backward page
 // (section 1, rows "brush's actual structure" and "differences").
 #include "gsr_internal.hpp"
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
       const uint64_t bits = __ballot((reach >> q) & 1u);
       if (lane == 0) s_mask[q][w] = bits;
     }
-    __syncthreads();
+    lds_barrier();
     const uint32_t rel0 = b0 - start;
     for (uint32_t sw = 0; sw < kWaves; ++sw) {
       uint64_t m = uniform64(s_mask[w][sw]);
@@ -221,26 +222,20 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
         if (my_slot >= 0) atomicAdd(&s_acc[j][my_slot], x);
       }
     }
-    __syncthreads();
-    if (k < stop) {
-      const uint32_t idx = s_sp[tid].idx;
-      float v[kGrads];
-#pragma unroll
-      for (uint32_t q = 0; q < kGrads; ++q) {
-        v[q] = s_acc[tid][q];
-        s_acc[tid][q] = 0.0f;
-      }
-      // conic slots: the tile's sums of u dx dx, u dx dy, u dy dy scale to dL/da, dL/db, dL/dc
-      v[2] = -0.5f * v[2];
-      v[3] = -v[3];
-      v[4] = -0.5f * v[4];
-      if (idx != 0xFFFFFFFFu) {
-#pragma unroll
-        for (uint32_t q = 0; q < kGrads; ++q)
-          if (!kSkip || v[q] != 0.0f) atomicAdd(splats_grad + size_t(idx) * kGrads + q, v[q]);
-      }
+    lds_barrier();
+    // Flush: the batch's accumulator is read in its [slot][value] order, so the 64 lanes of an atomic instruction
+    // add to the consecutive values of about seven splats (a few cache lines) rather than to 64 scattered records.
+    // The conic slots' sums of u dx dx, u dx dy, u dy dy scale to dL/da, dL/db, dL/dc.
+    const uint32_t staged = min(kTilePixels, stop - b0);
+    for (uint32_t f = tid; f < staged * kGrads; f += kTilePixels) {
+      const uint32_t slot = f / kGrads, q = f - slot * kGrads;
+      float v = (&s_acc[0][0])[f];
+      (&s_acc[0][0])[f] = 0.0f;
+      v = q == 2 || q == 4 ? -0.5f * v : q == 3 ? -v : v;
+      const uint32_t idx = s_sp[slot].idx;
+      if (idx != 0xFFFFFFFFu && (!kSkip || v != 0.0f)) atomicAdd(splats_grad + size_t(idx) * kGrads + q, v);
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 

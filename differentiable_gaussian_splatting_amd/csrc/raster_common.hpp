@@ -115,6 +115,16 @@ __device__ __forceinline__ uint32_t reach_mask(const StagedSplat& s, float x0, f
   return m;
 }
 
+// Workgroup barrier that orders LDS accesses only: it waits for the wave's own LDS operations, not for its
+// outstanding global memory operations (unlike __syncthreads, whose fence also drains every pending global store and
+// atomic). For loops whose barriers protect LDS buffers while global atomics, which nothing in the workgroup reads
+// back, may complete later.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Wave-uniform 64-bit value held in scalar registers.
 __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
