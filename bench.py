@@ -51,6 +51,7 @@ def parse():
     ap.add_argument("--workload", default="iter410k")
     ap.add_argument("--bin-scheme", choices=["presort", "key64"], default="presort")
     ap.add_argument("--raster-skip", type=int, choices=[0, 1], default=1)
+    ap.add_argument("--bin-rule", choices=["box", "ellipse"], default="box")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
     return ap.parse_args()
@@ -80,7 +81,7 @@ def cpu_model():
     return platform.processor()
 
 
-def run_oracle(sc, adam_groups, hp, bc):
+def run_oracle(sc, adam_groups, hp, bc, bin_rule="box"):
     """CPU baseline leg: the plain single-threaded oracle over one whole step of the same workload; also the exact
     evaluation counts used by the GPU figure and the flop model."""
     import numpy as np
@@ -88,7 +89,7 @@ def run_oracle(sc, adam_groups, hp, bc):
     import oracle
     t = {}
     t0 = time.perf_counter()
-    ob = oracle.bin(sc.splats, sc.depths, sc.width, sc.height)
+    ob = oracle.bin(sc.splats, sc.depths, sc.width, sc.height, rule=bin_rule)
     t["bin"] = time.perf_counter() - t0
     t0 = time.perf_counter()
     out, ft, lc, fst = oracle.render_forward(sc.splats, ob, sc.width, sc.height)
@@ -131,6 +132,7 @@ def main():
     gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SCHEME, gsr.GSR_BIN_PRESORT if args.bin_scheme == "presort"
                        else gsr.GSR_BIN_KEY64)
     gsr.gsr_set_option(ctx, gsr.GSR_OPT_RASTER_SKIP, args.raster_skip)
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_RULE, gsr.GSR_BIN_ELLIPSE if args.bin_rule == "ellipse" else gsr.GSR_BIN_BOX)
     splats = torch.from_numpy(sc.splats).cuda()
     depths = torch.from_numpy(sc.depths).cuda()
     v_out = torch.from_numpy(sc.v_out).cuda()
@@ -191,7 +193,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline: oracle over one step", file=sys.stderr, flush=True)
-        cpu = run_oracle(sc, adam_host, hp, bc)
+        cpu = run_oracle(sc, adam_host, hp, bc, args.bin_rule)
         assert cpu["num_pairs"] == P, "pair count differs from the oracle"
         assert int(cpu["lc"].astype(np.int64).sum()) == e_bwd_gpu, "last_contrib sum differs from the oracle"
 
@@ -202,7 +204,8 @@ def main():
                                      "(70% s in 0.3-4 px, 30% s in 4-40 px, color_a = sigmoid(N(-2, 1.5))), "
                                      "bin + forward + backward + fused Adam over 59 fp32 params per splat",
                          "image": [W, H], "splats": N, "pairs": P, "adam_elements": adam_elems,
-                         "bin_scheme": args.bin_scheme, "raster_skip": args.raster_skip}}
+                         "bin_scheme": args.bin_scheme, "bin_rule": args.bin_rule,
+                         "raster_skip": args.raster_skip}}
     result["stage_ms"] = stage_ms
     result["stage_ms_median"] = stage_ms_median
     result["fwd_bwd_ms"] = stage_ms["forward"] + stage_ms["backward"]

@@ -61,8 +61,47 @@ __device__ __forceinline__ Rect tile_rect(const float* __restrict__ sp, float de
 
 // Per splat, in index order (coalesced reads of the records): the tile rectangle and its tile count, the depth
 // sort key and index for the presort scheme, and the block's count total in part[block].
+// The exact-ellipse overlap rule (GSR_BIN_ELLIPSE): tile (tx, ty) of the box is kept when the 3-sigma ellipse
+// (p - mean)^T [[a b][b c]] (p - mean) <= 9 meets the tile's closed square [16 tx, 16 tx + 16] x [16 ty, 16 ty + 16].
+// The minimum of the quadratic over the square is 0 when the mean lies in it, else the least of the four edge
+// minima (the vertex of the one-dimensional quadratic clamped to the edge). One IEEE fp32 operation at a time in
+// this order, so the decision equals a plain fp32 evaluation of the same definition.
+__device__ __forceinline__ float conic_q(float a, float b, float c, float dx, float dy) {
+  return ((a * dx) * dx + ((b + b) * dx) * dy) + (c * dy) * dy;
+}
+
+__device__ __forceinline__ float clamp_f(float v, float lo, float hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+__device__ __forceinline__ bool ellipse_meets_tile(float x, float y, float a, float b, float c, uint32_t tx,
+                                                   uint32_t ty) {
+  const float x0 = 16.0f * float(tx), x1 = x0 + 16.0f;
+  const float y0 = 16.0f * float(ty), y1 = y0 + 16.0f;
+  const float dx0 = x0 - x, dx1 = x1 - x;
+  const float dy0 = y0 - y, dy1 = y1 - y;
+  if (dx0 <= 0.0f && dx1 >= 0.0f && dy0 <= 0.0f && dy1 >= 0.0f) return true;
+  float best = __builtin_huge_valf();
+  float q = conic_q(a, b, c, dx0, clamp_f(-(b * dx0) / c, dy0, dy1));
+  best = q < best ? q : best;
+  q = conic_q(a, b, c, dx1, clamp_f(-(b * dx1) / c, dy0, dy1));
+  best = q < best ? q : best;
+  q = conic_q(a, b, c, clamp_f(-(b * dy0) / a, dx0, dx1), dy0);
+  best = q < best ? q : best;
+  q = conic_q(a, b, c, clamp_f(-(b * dy1) / a, dx0, dx1), dy1);
+  best = q < best ? q : best;
+  return best <= 9.0f;
+}
+
+// Number of the box's tiles the ellipse rule keeps.
+__device__ uint32_t ellipse_count(const float* __restrict__ sp, const Rect& r) {
+  const float x = sp[0], y = sp[1], a = sp[2], b = sp[3], c = sp[4];
+  uint32_t cnt = 0;
+  for (uint32_t dy = 0; dy < r.h; ++dy)
+    for (uint32_t dx = 0; dx < r.w; ++dx) cnt += ellipse_meets_tile(x, y, a, b, c, r.tx0 + dx, r.ty0 + dy);
+  return cnt;
+}
+
 __global__ __launch_bounds__(kThreads) void k_prep(const float* __restrict__ splats, const float* __restrict__ depths,
-                                                   uint32_t n, uint32_t tiles_x, uint32_t tiles_y,
+                                                   uint32_t n, uint32_t tiles_x, uint32_t tiles_y, bool ellipse,
                                                    uint4* __restrict__ rects, uint32_t* __restrict__ counts,
                                                    uint32_t* __restrict__ dkeys, uint32_t* __restrict__ didx,
                                                    uint64_t* __restrict__ part) {
@@ -73,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const float* __restrict__ spl
     const float depth = depths[i];
     const Rect r = tile_rect(splats + size_t(i) * 9, depth, tiles_x, tiles_y);
     rects[i] = make_uint4(r.tx0, r.ty0, r.w, r.h);
-    c = uint64_t(r.w) * r.h;
+    c = ellipse ? ellipse_count(splats + size_t(i) * 9, r) : uint64_t(r.w) * r.h;
     counts[i] = uint32_t(c);
     if (dkeys) {
       dkeys[i] = __float_as_uint(depth);
@@ -283,6 +322,40 @@ __global__ __launch_bounds__(kThreads) void k_emit(const uint4* __restrict__ rec
   }
 }
 
+// Emission under the ellipse rule: thread j walks its splat's box row by row and writes the kept tiles at
+// offsets[j] onwards (each splat's pairs are contiguous; the stores are not coalesced across threads).
+template <typename K>
+__global__ __launch_bounds__(kThreads) void k_emit_ellipse(const float* __restrict__ splats,
+                                                           const uint4* __restrict__ rects,
+                                                           const float* __restrict__ depths, uint32_t n,
+                                                           const uint32_t* __restrict__ order, uint32_t tiles_x,
+                                                           const uint64_t* __restrict__ offsets,
+                                                           uint64_t num_pairs, K* __restrict__ keys,
+                                                           uint32_t* __restrict__ vals) {
+  const uint32_t j = blockIdx.x * kThreads + threadIdx.x;
+  if (j >= n) return;
+  const uint32_t i = order ? order[j] : j;
+  if (i >= n) return;  // not reachable with a permutation in `order`
+  const uint4 r = rects[i];
+  const float* sp = splats + size_t(i) * 9;
+  const float x = sp[0], y = sp[1], a = sp[2], b = sp[3], c = sp[4];
+  const uint32_t dbits = __float_as_uint(depths[i]);
+  uint64_t p = offsets[j];
+  const uint64_t p_end = min(offsets[j + 1], num_pairs);
+  // rect = (tx0, ty0, w, h)
+  for (uint32_t ty = r.y; ty < r.y + r.w && p < p_end; ++ty)
+    for (uint32_t tx = r.x; tx < r.x + r.z && p < p_end; ++tx) {
+      if (!ellipse_meets_tile(x, y, a, b, c, tx, ty)) continue;
+      const uint64_t tile = uint64_t(ty) * tiles_x + tx;
+      if constexpr (sizeof(K) == 8)
+        keys[p] = (tile << 32) | dbits;
+      else
+        keys[p] = K(tile);
+      vals[p] = i;
+      ++p;
+    }
+}
+
 // Per-tile ranges from the sorted keys: the boundary between pairs i-1 and i (i in [0, P]) opens the ranges of
 // the tiles after the previous pair's and closes those before the current pair's. Each thread takes kRangeItems
 // consecutive boundaries (16-byte loads of 32-bit keys). With keys_final (the presort scheme when no sort pass
@@ -370,6 +443,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   Arena& a = ctx->arena;
   const bool presort = ctx->bin_scheme == GSR_BIN_PRESORT;
+  const bool ellipse = ctx->bin_rule == GSR_BIN_ELLIPSE;
 
   if ((st = grow(ctx, a.ranges, size_t(num_tiles) * 8))) return st;
   if ((st = grow(ctx, a.counts, size_t(n + 1) * 4)) || (st = grow(ctx, a.offsets, size_t(n + 1) * 8)) ||
@@ -391,7 +465,8 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
 
   // Rectangles, counts and the pair total first; the total goes to the host while the depth sort runs.
   if (n) {
-    hipLaunchKernelGGL(k_prep, dim3(nb_prep), dim3(kThreads), 0, s, splats, depths, n, tiles_x, tiles_y, rects, counts,
+    hipLaunchKernelGGL(k_prep, dim3(nb_prep), dim3(kThreads), 0, s, splats, depths, n, tiles_x, tiles_y, ellipse,
+                       rects, counts,
                        presort ? ok : static_cast<uint32_t*>(nullptr), presort ? ov : static_cast<uint32_t*>(nullptr),
                        part);
     hipLaunchKernelGGL(k_total, dim3(1), dim3(kThreads), 0, s, part, nb_prep, offsets + n);
@@ -440,8 +515,14 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     // tile ids as 32-bit keys, sorted by their tile_bits low bits
     uint32_t* kb[2] = {static_cast<uint32_t*>(a.keys[0].ptr), static_cast<uint32_t*>(a.keys[1].ptr)};
     if (n)
-      hipLaunchKernelGGL(k_emit<uint32_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, rects, depths, n, order,
-                         tiles_x, offsets, P, kb[0], v0);
+    {
+      if (ellipse)
+        hipLaunchKernelGGL(k_emit_ellipse<uint32_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats, rects,
+                           depths, n, order, tiles_x, offsets, P, kb[0], v0);
+      else
+        hipLaunchKernelGGL(k_emit<uint32_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, rects, depths, n, order,
+                           tiles_x, offsets, P, kb[0], v0);
+    }
     // The 64-bit keys go to the key buffer the sorted tile ids do not end in, written by the last sort pass (or by
     // the range kernel when there is no pass).
     bool keys_done = !ctx->bin_keys;
@@ -468,8 +549,14 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   } else {
     uint64_t* kb[2] = {static_cast<uint64_t*>(a.keys[0].ptr), static_cast<uint64_t*>(a.keys[1].ptr)};
     if (n)
-      hipLaunchKernelGGL(k_emit<uint64_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, rects, depths, n, order,
-                         tiles_x, offsets, P, kb[0], v0);
+    {
+      if (ellipse)
+        hipLaunchKernelGGL(k_emit_ellipse<uint64_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats, rects,
+                           depths, n, order, tiles_x, offsets, P, kb[0], v0);
+      else
+        hipLaunchKernelGGL(k_emit<uint64_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, rects, depths, n, order,
+                           tiles_x, offsets, P, kb[0], v0);
+    }
     if (P > 0) {
       const uint32_t key_bits = 32 + tile_bits;
       res = (sort_passes(key_bits) & 1u) ? 1 : 0;

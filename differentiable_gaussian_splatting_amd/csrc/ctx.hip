@@ -128,6 +128,11 @@ gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value) {
         return fail(ctx, GSR_EINVAL, "gsr_set_option: unknown bin scheme %lld", (long long)value);
       ctx->bin_scheme = int32_t(value);
       return GSR_OK;
+    case GSR_OPT_BIN_RULE:
+      if (value != GSR_BIN_BOX && value != GSR_BIN_ELLIPSE)
+        return fail(ctx, GSR_EINVAL, "gsr_set_option: unknown overlap rule %lld", (long long)value);
+      ctx->bin_rule = int32_t(value);
+      return GSR_OK;
     case GSR_OPT_BIN_KEYS:
       if (value != 0 && value != 1) return fail(ctx, GSR_EINVAL, "gsr_set_option: bin keys must be 0 or 1");
       ctx->bin_keys = value != 0;

@@ -67,6 +67,13 @@ gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats);
                               /*   backward, splats no lane of a wavefront composited; 0: every lane evaluates    */
                               /*   every splat up to its bound. Results are identical either way (the A/B switch  */
                               /*   of the W1 warp sparse skip + exp-skip page, section 1, "raster_backward_sparse")*/
+#define GSR_OPT_BIN_RULE 4    /* which tiles a splat is binned to (the pages never state the rule; the 1M-splat    */
+                             /*   stress count of about 16M keys fits the ellipse rule):                          */
+#define GSR_BIN_BOX 0        /*   default: every tile of the axis-aligned box of the 3-sigma ellipse              */
+#define GSR_BIN_ELLIPSE 1    /*   the box's tiles whose closed 16x16 square the 3-sigma ellipse                   */
+                             /*   (p - mean)^T [[a b][b c]] (p - mean) <= 9 meets, decided in fp32 from the       */
+                             /*   minimum of the quadratic over the square (0 if the mean is inside, else the     */
+                             /*   least edge minimum at the clamped vertex)                                       */
 gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value);
 
 /* Views into the context's arena, valid until the next gsr_bin or gsr_reserve on the same context. A caller may

@@ -50,6 +50,9 @@ def _load():
     lib.oracle_bin_count.argtypes = [P, P, u32, u32, u32, P]
     lib.oracle_tile_rect.argtypes = [P, f32, u32, u32, P]
     lib.oracle_bin.argtypes = [P, P, u32, u32, u32, P, P, P, u64]
+    lib.oracle_bin_rule.argtypes = [P, P, u32, u32, u32, ctypes.c_int, P, P, P, u64]
+    lib.oracle_bin_count_rule.argtypes = [P, P, u32, u32, u32, ctypes.c_int, P]
+    lib.oracle_ellipse_meets_tile.argtypes = [P, u32, u32]
     lib.oracle_sort_pairs.argtypes = [P, P, u64, P, P]
     lib.oracle_render_forward_f32.argtypes = [P, P, P, u32, u32, P, P, P, P]
     lib.oracle_render_forward_f64.argtypes = [P, P, P, u32, u32, P, P, P, P]
@@ -104,21 +107,42 @@ def tile_rect(splat, depth: float, width: int, height: int):
     return None if empty else tuple(int(v) for v in rect)
 
 
-def bin(splats, depths, width: int, height: int) -> Bins:
-    """Emit, stable-sort and range-extract the (tile | depth) keys."""
+RULES = {"box": 0, "ellipse": 1}
+
+
+def ellipse_meets_tile(splat, tx: int, ty: int) -> bool:
+    """The exact-ellipse rule's test of one splat against one tile."""
+    s = _c(splat, np.float32).reshape(9)
+    return bool(_load().oracle_ellipse_meets_tile(_ptr(s), tx, ty))
+
+
+def bin_count(splats, depths, width: int, height: int, rule: str = "box") -> int:
+    """Number of (splat, tile) pairs the binning emits under the rule."""
+    s = _c(splats, np.float32).reshape(-1, 9)
+    d = _c(depths, np.float32).reshape(-1)
+    p = ctypes.c_uint64(0)
+    _check(_load().oracle_bin_count_rule(_ptr(s), _ptr(d), s.shape[0], width, height, RULES[rule],
+                                         ctypes.byref(p)), "bin_count")
+    return int(p.value)
+
+
+def bin(splats, depths, width: int, height: int, rule: str = "box") -> Bins:
+    """Emit, stable-sort and range-extract the (tile | depth) keys; rule 'box' (the 3-sigma box) or 'ellipse'
+    (the box's tiles that the 3-sigma ellipse meets)."""
     lib = _load()
     s = _c(splats, np.float32).reshape(-1, 9)
     d = _c(depths, np.float32).reshape(-1)
     n = s.shape[0]
     assert d.shape[0] == n
+    r = RULES[rule]
     p = ctypes.c_uint64(0)
-    _check(lib.oracle_bin_count(_ptr(s), _ptr(d), n, width, height, ctypes.byref(p)), "bin_count")
+    _check(lib.oracle_bin_count_rule(_ptr(s), _ptr(d), n, width, height, r, ctypes.byref(p)), "bin_count")
     tx, ty = tiles_of(width, height)
     keys = np.zeros(p.value, np.uint64)
     vals = np.zeros(p.value, np.uint32)
     ranges = np.zeros((tx * ty, 2), np.uint32)
-    _check(lib.oracle_bin(_ptr(s), _ptr(d), n, width, height, _ptr(keys), _ptr(vals), _ptr(ranges), p.value),
-           "bin")
+    _check(lib.oracle_bin_rule(_ptr(s), _ptr(d), n, width, height, r, _ptr(keys), _ptr(vals), _ptr(ranges),
+                               p.value), "bin")
     return Bins(keys, vals, ranges, tx, ty)
 
 

@@ -28,7 +28,8 @@
 //                 gradient from that pixel (the page's "raw_alpha < 0.999" branch).
 //   culling       a splat is not binned if any field or its depth is non-finite, depth <= 0, a <= 0,
 //                 a*c - b*b <= 0, or o lies outside [0, 1].
-//   overlap rule  the axis-aligned box of the 3-sigma ellipse: rx = 3 sqrt(c/det), ry = 3 sqrt(a/det).
+//   overlap rule  the axis-aligned box of the 3-sigma ellipse: rx = 3 sqrt(c/det), ry = 3 sqrt(a/det); or, as an
+//                 option, the tiles of that box which the 3-sigma ellipse itself meets (ellipse_meets_tile).
 //
 // Built with g++ -O2 -ffp-contract=off and no fast-math, so every float expression below rounds after each
 // operation, in the order written.
@@ -113,6 +114,43 @@ TileRect tile_rect(const float* sp, float depth, uint32_t tiles_x, uint32_t tile
   return TileRect{false, uint32_t(cx0), uint32_t(cx1), uint32_t(cy0), uint32_t(cy1)};
 }
 
+// The exact-ellipse rule: tile (tx, ty) of the box is kept when the 3-sigma ellipse
+// q(p) = (p - mean)^T [[a b][b c]] (p - mean) <= 9 meets the tile's closed square [16 tx, 16 tx + 16] x
+// [16 ty, 16 ty + 16], i.e. when the minimum of q over the square is at most 9. That minimum is 0 if the mean lies
+// in the square; otherwise it is on the boundary, the least of the four edge minima, each at the vertex of the
+// one-dimensional quadratic clamped to the edge. fp32, one rounding per operation, in the order written.
+float conic_q(float a, float b, float c, float dx, float dy) {
+  return ((a * dx) * dx + ((b + b) * dx) * dy) + (c * dy) * dy;
+}
+
+float clamp_f(float v, float lo, float hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+bool ellipse_meets_tile(float x, float y, float a, float b, float c, uint32_t tx, uint32_t ty) {
+  const float x0 = 16.0f * float(tx), x1 = x0 + 16.0f;
+  const float y0 = 16.0f * float(ty), y1 = y0 + 16.0f;
+  const float dx0 = x0 - x, dx1 = x1 - x;
+  const float dy0 = y0 - y, dy1 = y1 - y;
+  if (dx0 <= 0.0f && dx1 >= 0.0f && dy0 <= 0.0f && dy1 >= 0.0f) return true;
+  const float ex[2] = {dx0, dx1}, ey[2] = {dy0, dy1};
+  float best = INFINITY;
+  for (int e = 0; e < 2; ++e) {  // the edges x = x0 and x = x1: q(dx, .) is least at dy = -b dx / c
+    const float dx = ex[e];
+    const float dy = clamp_f(-(b * dx) / c, dy0, dy1);
+    best = std::min(best, conic_q(a, b, c, dx, dy));
+  }
+  for (int e = 0; e < 2; ++e) {  // the edges y = y0 and y = y1: q(., dy) is least at dx = -b dy / a
+    const float dy = ey[e];
+    const float dx = clamp_f(-(b * dy) / a, dx0, dx1);
+    best = std::min(best, conic_q(a, b, c, dx, dy));
+  }
+  return best <= 9.0f;
+}
+
+// Whether rule `ellipse` keeps tile (tx, ty) of splat sp's box (every box tile under the box rule).
+bool keep_tile(const float* sp, bool ellipse, uint32_t tx, uint32_t ty) {
+  return !ellipse || ellipse_meets_tile(sp[0], sp[1], sp[2], sp[3], sp[4], tx, ty);
+}
+
 uint32_t float_bits(float f) {
   uint32_t u;
   std::memcpy(&u, &f, 4);
@@ -124,15 +162,16 @@ struct Pair {
   uint32_t val;
 };
 
-// Emission in splat order, tiles row-major inside each splat's rectangle.
+// Emission in splat order, tiles row-major inside each splat's rectangle (those the rule keeps).
 std::vector<Pair> emit_pairs(const float* splats, const float* depths, uint32_t n, uint32_t tiles_x,
-                             uint32_t tiles_y) {
+                             uint32_t tiles_y, bool ellipse) {
   std::vector<Pair> pairs;
   for (uint32_t i = 0; i < n; ++i) {
     TileRect r = tile_rect(splats + size_t(i) * 9, depths[i], tiles_x, tiles_y);
     if (r.empty) continue;
     for (uint32_t ty = r.ty0; ty <= r.ty1; ++ty)
       for (uint32_t tx = r.tx0; tx <= r.tx1; ++tx) {
+        if (!keep_tile(splats + size_t(i) * 9, ellipse, tx, ty)) continue;
         const uint64_t tile = uint64_t(ty) * tiles_x + tx;
         pairs.push_back(Pair{(tile << 32) | uint64_t(float_bits(depths[i])), i});
       }
@@ -349,18 +388,30 @@ void render_backward(const R* splats, uint32_t n, const uint32_t* vals, const ui
 
 extern "C" {
 
-// Number of (splat, tile) pairs the binning emits.
-int oracle_bin_count(const float* splats, const float* depths, uint32_t n, uint32_t width, uint32_t height,
-                     uint64_t* num_pairs) {
-  if (!num_pairs || (n && (!splats || !depths)) || width == 0 || height == 0) return -1;
+// Number of (splat, tile) pairs the binning emits (rule 0: box, 1: exact ellipse).
+int oracle_bin_count_rule(const float* splats, const float* depths, uint32_t n, uint32_t width, uint32_t height,
+                          int rule, uint64_t* num_pairs) {
+  if (!num_pairs || (n && (!splats || !depths)) || width == 0 || height == 0 || (rule != 0 && rule != 1)) return -1;
   const uint32_t tiles_x = (width + kTile - 1) / kTile, tiles_y = (height + kTile - 1) / kTile;
   uint64_t total = 0;
   for (uint32_t i = 0; i < n; ++i) {
     TileRect r = tile_rect(splats + size_t(i) * 9, depths[i], tiles_x, tiles_y);
-    if (!r.empty) total += uint64_t(r.tx1 - r.tx0 + 1) * (r.ty1 - r.ty0 + 1);
+    if (r.empty) continue;
+    for (uint32_t ty = r.ty0; ty <= r.ty1; ++ty)
+      for (uint32_t tx = r.tx0; tx <= r.tx1; ++tx) total += keep_tile(splats + size_t(i) * 9, rule == 1, tx, ty);
   }
   *num_pairs = total;
   return 0;
+}
+
+int oracle_bin_count(const float* splats, const float* depths, uint32_t n, uint32_t width, uint32_t height,
+                     uint64_t* num_pairs) {
+  return oracle_bin_count_rule(splats, depths, n, width, height, 0, num_pairs);
+}
+
+// The exact-ellipse test of one splat {x, y, a, b, c} against tile (tx, ty): 1 kept, 0 not.
+int oracle_ellipse_meets_tile(const float* splat, uint32_t tx, uint32_t ty) {
+  return ellipse_meets_tile(splat[0], splat[1], splat[2], splat[3], splat[4], tx, ty) ? 1 : 0;
 }
 
 // Tile rectangle of one splat: rect = {tx0, tx1, ty0, ty1}; returns 1 if the splat is culled or off the grid.
@@ -374,12 +425,13 @@ int oracle_tile_rect(const float* splat, float depth, uint32_t width, uint32_t h
   return r.empty ? 1 : 0;
 }
 
-// Sorted keys [capacity], values [capacity] and per-tile ranges [2 * tiles] (start, end) for the pair list.
-int oracle_bin(const float* splats, const float* depths, uint32_t n, uint32_t width, uint32_t height,
-               uint64_t* keys, uint32_t* vals, uint32_t* ranges, uint64_t capacity) {
-  if ((n && (!splats || !depths)) || width == 0 || height == 0 || !ranges) return -1;
+// Sorted keys [capacity], values [capacity] and per-tile ranges [2 * tiles] (start, end) for the pair list
+// (rule 0: box, 1: exact ellipse).
+int oracle_bin_rule(const float* splats, const float* depths, uint32_t n, uint32_t width, uint32_t height, int rule,
+                    uint64_t* keys, uint32_t* vals, uint32_t* ranges, uint64_t capacity) {
+  if ((n && (!splats || !depths)) || width == 0 || height == 0 || !ranges || (rule != 0 && rule != 1)) return -1;
   const uint32_t tiles_x = (width + kTile - 1) / kTile, tiles_y = (height + kTile - 1) / kTile;
-  std::vector<Pair> pairs = emit_pairs(splats, depths, n, tiles_x, tiles_y);
+  std::vector<Pair> pairs = emit_pairs(splats, depths, n, tiles_x, tiles_y, rule == 1);
   if (pairs.size() > capacity || (!pairs.empty() && (!keys || !vals))) return -1;
   std::stable_sort(pairs.begin(), pairs.end(), [](const Pair& l, const Pair& r) { return l.key < r.key; });
   for (size_t k = 0; k < pairs.size(); ++k) {
@@ -397,6 +449,11 @@ int oracle_bin(const float* splats, const float* depths, uint32_t n, uint32_t wi
     ranges[2 * t + 1] = uint32_t(hi - pairs.begin());
   }
   return 0;
+}
+
+int oracle_bin(const float* splats, const float* depths, uint32_t n, uint32_t width, uint32_t height,
+               uint64_t* keys, uint32_t* vals, uint32_t* ranges, uint64_t capacity) {
+  return oracle_bin_rule(splats, depths, n, width, height, 0, keys, vals, ranges, capacity);
 }
 
 // Stable sort of (key, value) pairs by key; the reference for the radix sort alone.

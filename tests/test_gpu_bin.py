@@ -159,3 +159,38 @@ def test_radix_sort_rejects_bad_arguments(ctx):
         gsr.gsr_radix_sort(ctx, k, v, 0)
     with pytest.raises(gsr.GsrError):
         gsr.gsr_radix_sort(ctx, k, v, 65)
+
+
+# ------------------------------------------------------------------------------------- exact-ellipse overlap rule
+def set_rule(ctx, rule):
+    from differentiable_gaussian_splatting_amd import gsr
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_RULE, gsr.GSR_BIN_ELLIPSE if rule == "ellipse" else gsr.GSR_BIN_BOX)
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+@pytest.mark.parametrize("name", ["tiny", "raster84k", "bin1m"])
+def test_bin_ellipse_rule_matches_oracle(ctx, name, scheme):
+    import oracle
+    banner(f"bin ellipse {name} scheme={scheme}")
+    sc = scene(name)
+    ref = oracle.bin(sc.splats, sc.depths, sc.width, sc.height, rule="ellipse")
+    set_rule(ctx, "ellipse")
+    try:
+        assert_bins_equal(ctx, sc.splats, sc.depths, sc.width, sc.height, scheme, ref)
+    finally:
+        set_rule(ctx, "box")
+    print(f"  {ref.num_pairs} pairs")
+
+
+@pytest.mark.parametrize("w,h", [(24, 24), (100, 37), (1023, 769)])
+def test_bin_ellipse_rule_ragged_images(ctx, w, h):
+    import oracle
+    banner(f"bin ellipse ragged {w}x{h}")
+    sc = custom_scene(name="r", width=w, height=h, n=3000, seed=w + h, size_classes=((1.0, 0.5, 30.0),), margin=20.0)
+    set_rule(ctx, "ellipse")
+    try:
+        for scheme in SCHEMES:
+            assert_bins_equal(ctx, sc.splats, sc.depths, w, h, scheme,
+                              oracle.bin(sc.splats, sc.depths, w, h, rule="ellipse"))
+    finally:
+        set_rule(ctx, "box")

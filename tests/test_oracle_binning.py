@@ -183,3 +183,92 @@ def test_sort_pairs_ties_heavy(orc):
     ko, vo = orc.sort_pairs(keys, vals)
     order = np.argsort(keys, kind="stable")
     assert np.array_equal(vo, vals[order])
+
+
+# ------------------------------------------------------------------------------------- exact-ellipse overlap rule
+def _sq_min_by_optimizer(splat, tx, ty):
+    """Minimum of q(p) = (p - mean)^T C (p - mean) over the closed tile square, by a bounded quasi-Newton solver
+    (scipy L-BFGS-B from the square's centre and corners) in float64: a method independent of the rule's formula."""
+    from scipy.optimize import minimize
+    x, y, a, b, c = (float(v) for v in splat[:5])
+    C = np.array([[a, b], [b, c]])
+    mu = np.array([x, y])
+
+    def f(p):
+        d = p - mu
+        return float(d @ C @ d), 2.0 * (C @ d)
+
+    lo, hi = np.array([16.0 * tx, 16.0 * ty]), np.array([16.0 * tx + 16, 16.0 * ty + 16])
+    best = np.inf
+    for start in ((lo + hi) / 2, lo, hi, np.array([lo[0], hi[1]]), np.array([hi[0], lo[1]])):
+        r = minimize(f, start, jac=True, method="L-BFGS-B", bounds=list(zip(lo, hi)),
+                     options={"ftol": 1e-15, "gtol": 1e-12, "maxiter": 500})
+        best = min(best, r.fun)
+    return best
+
+
+@pytest.mark.parametrize("seed", [21, 22])
+def test_ellipse_rule_matches_geometry(orc, seed):
+    """Every box tile the ellipse rule keeps (drops) has its minimum of q over the square below (above) 9, found by a
+    general bounded minimiser; only minima within 1e-4 relative of 9 (fp32 rounding can go either way) are
+    skipped."""
+    sc = scenes.make_scene(scenes.SceneSpec(name="ell", width=96, height=96, n=120,
+                                            size_classes=((1.0, 0.7, 12.0),), seed=seed))
+    checked = skipped = 0
+    for i in range(sc.splats.shape[0]):
+        rect = orc.tile_rect(sc.splats[i], float(sc.depths[i]), 96, 96)
+        if rect is None:
+            continue
+        tx0, tx1, ty0, ty1 = rect
+        for ty in range(ty0, ty1 + 1):
+            for tx in range(tx0, tx1 + 1):
+                m = _sq_min_by_optimizer(sc.splats[i], tx, ty)
+                if abs(m - 9.0) < 9e-4:
+                    skipped += 1
+                    continue
+                assert orc.ellipse_meets_tile(sc.splats[i], tx, ty) == (m < 9.0), (i, tx, ty, m)
+                checked += 1
+    assert checked > 500 and skipped < 0.01 * checked, (checked, skipped)
+
+
+def test_ellipse_rule_hand_cases(orc):
+    """A thin 45-degree splat through tile (1, 1) (3-sigma half-length 24 px, half-width 1.5 px): its box is 3x3
+    tiles, the ellipse misses the off-diagonal corners (2, 0) and (0, 2) and, near the shared corners (16, 16) and
+    (32, 32), meets the four tiles around each. A round splat inside one tile keeps one tile; one centred on a tile
+    corner keeps all four."""
+    s1, s2, th = 8.0, 0.5, np.pi / 4
+    R = np.array([[np.cos(th), -np.sin(th)], [np.sin(th), np.cos(th)]])
+    cov = R @ np.diag([s1 * s1, s2 * s2]) @ R.T
+    inv = np.linalg.inv(cov)
+    diag = np.array([[24.0, 24.0, inv[0, 0], inv[0, 1], inv[1, 1], 1, 1, 1, 0.5]], np.float32)
+    b = orc.bin(diag, np.ones(1, np.float32), 48, 48, rule="ellipse")
+    tiles = sorted(int(k >> np.uint64(32)) for k in b.keys)
+    assert tiles == sorted(ty * 3 + tx for tx, ty in [(0, 0), (1, 0), (0, 1), (1, 1), (2, 1), (1, 2), (2, 2)])
+    assert orc.bin(diag, np.ones(1, np.float32), 48, 48).num_pairs == 9
+    inside = np.array([[24.0, 24.0, 1.0, 0.0, 1.0, 1, 1, 1, 0.5]], np.float32)
+    corner = np.array([[16.0, 16.0, 1.0, 0.0, 1.0, 1, 1, 1, 0.5]], np.float32)
+    assert orc.bin(inside, np.ones(1, np.float32), 48, 48, rule="ellipse").num_pairs == 1
+    assert orc.bin(corner, np.ones(1, np.float32), 48, 48, rule="ellipse").num_pairs == 4
+
+
+def test_ellipse_rule_is_a_filter_of_the_box_rule(orc):
+    """Same culling, same order: the ellipse bins are the box bins with the dropped tiles removed."""
+    sc = scenes.make_scene(scenes.SceneSpec(name="f", width=160, height=128, n=3000,
+                                            size_classes=((1.0, 0.5, 20.0),), seed=31))
+    box = orc.bin(sc.splats, sc.depths, 160, 128)
+    ell = orc.bin(sc.splats, sc.depths, 160, 128, rule="ellipse")
+    keep = np.array([orc.ellipse_meets_tile(sc.splats[v], int(k >> np.uint64(32)) % box.tiles_x,
+                                            int(k >> np.uint64(32)) // box.tiles_x)
+                     for k, v in zip(box.keys, box.vals)], bool)
+    assert 0 < ell.num_pairs < box.num_pairs
+    assert np.array_equal(ell.keys, box.keys[keep]) and np.array_equal(ell.vals, box.vals[keep])
+
+
+def test_ellipse_rule_gives_the_pages_stress_key_count(orc):
+    """The binning-stress workload (1M splats, sizes 0.5-40 px, 800x800) is stated to give about 16M keys; the box
+    rule gives about 26M, the ellipse rule 16.3M."""
+    sc = scenes.make_scene("bin1m")
+    n_box = orc.bin_count(sc.splats, sc.depths, 800, 800)
+    n_ell = orc.bin_count(sc.splats, sc.depths, 800, 800, rule="ellipse")
+    assert 25.0e6 < n_box < 27.0e6
+    assert 15.5e6 < n_ell < 16.8e6
