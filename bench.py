@@ -102,8 +102,18 @@ def run_oracle(sc, adam_groups, hp, bc, bin_rule="box"):
     for _, p, g, m, v in adam_groups:
         oracle.adam_step(p, g, m, v, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], *bc)
     t["adam"] = time.perf_counter() - t0
-    return {"times": t, "fwd_stats": fst, "bwd_stats": bst, "num_pairs": ob.num_pairs, "out": out, "lc": lc,
-            "ranges": ob.ranges}
+    # the same step with the forward and backward spread over the host's cores by bands of tile rows (binning's
+    # stable sort and Adam stay single-threaded)
+    threads = max(1, min(16, os.cpu_count() or 1))
+    tm = {"bin": t["bin"], "adam": t["adam"]}
+    t0 = time.perf_counter()
+    oracle.render_forward_mt(sc.splats, ob, sc.width, sc.height, threads)
+    tm["forward"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.render_backward_mt(sc.splats, ob, sc.width, sc.height, out, ft, lc, sc.v_out, threads)
+    tm["backward"] = time.perf_counter() - t0
+    return {"times": t, "times_mt": tm, "threads": threads, "fwd_stats": fst, "bwd_stats": bst,
+            "num_pairs": ob.num_pairs, "out": out, "lc": lc, "ranges": ob.ranges}
 
 
 def main():
@@ -252,6 +262,13 @@ def main():
                                   "sample": "one whole step of the same workload (bin + forward + backward + Adam "
                                             "over all 410k splats), single-threaded",
                                   "stage_s": ct, "host_cpus": os.cpu_count(), "host_cpu_model": cpu_model()}
+        cm = cpu["times_mt"]
+        result["cpu_baseline_all_cores"] = {"value": evals / sum(cm.values()), "unit": UNIT, "cores": cpu["threads"],
+                                            "kind": "oracle",
+                                            "sample": "the same step with the oracle's forward and backward run by "
+                                                      f"{cpu['threads']} threads over bands of tile rows (binning "
+                                                      "and Adam single-threaded)",
+                                            "stage_s": cm}
     else:
         result["value"] = None
     print(json.dumps(result), flush=True)

@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.cpp")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 # Plain IEEE arithmetic: no fused multiply-add contraction, no fast-math.
-_CXXFLAGS = ["-O2", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math"]
+_CXXFLAGS = ["-O2", "-std=c++17", "-fPIC", "-shared", "-pthread", "-ffp-contract=off", "-fno-fast-math"]
 
 _lib = None
 
@@ -59,6 +59,8 @@ def _load():
     lib.oracle_render_backward_f32.argtypes = [P, u32, P, P, u32, u32, P, P, P, P, P, P]
     lib.oracle_render_backward_f64.argtypes = [P, u32, P, P, u32, u32, P, P, P, P, P]
     lib.oracle_adam_step.argtypes = [P, P, P, P, u64, f32, f32, f32, f32, f32, f32]
+    lib.oracle_render_forward_f32_mt.argtypes = [P, P, P, u32, u32, P, P, P, u32]
+    lib.oracle_render_backward_f32_mt.argtypes = [P, u32, P, P, u32, u32, P, P, P, P, P, u32]
     lib.oracle_trace_pixel_f32.argtypes = [P, P, P, u32, u32, u32, u32, u32, P, P, P, P, P]
     for name in ("oracle_bin_count", "oracle_tile_rect", "oracle_bin", "oracle_sort_pairs",
                  "oracle_render_forward_f32", "oracle_render_forward_f64", "oracle_render_backward_f32",
@@ -199,6 +201,34 @@ def render_backward(splats, bins: Bins, width: int, height: int, out_rgba, final
             stats.update({k: int(v) for k, v in zip(BWD_STAT_NAMES, st)})
     else:
         _check(lib.oracle_render_backward_f64(*args), "render_backward")
+    return grad
+
+
+def render_forward_mt(splats, bins: Bins, width: int, height: int, threads: int):
+    """render_forward (f32) spread over host threads by bands of tile rows (for timing on all cores); the same
+    outputs as the single-threaded call."""
+    lib = _load()
+    s = _c(splats, np.float32).reshape(-1, 9)
+    out = np.zeros((height, width, 4), np.float32)
+    ft = np.zeros((height, width), np.float32)
+    lc = np.zeros((height, width), np.uint32)
+    _check(lib.oracle_render_forward_f32_mt(_ptr(s), _ptr(_c(bins.vals, np.uint32)), _ptr(_c(bins.ranges, np.uint32)),
+                                            width, height, _ptr(out), _ptr(ft), _ptr(lc), threads), "forward_mt")
+    return out, ft, lc
+
+
+def render_backward_mt(splats, bins: Bins, width: int, height: int, out_rgba, final_T, last_contrib, v_out,
+                       threads: int):
+    """render_backward (f32) spread over host threads; per-thread sums in double added in thread order."""
+    lib = _load()
+    s = _c(splats, np.float32).reshape(-1, 9)
+    n = s.shape[0]
+    grad = np.zeros((n, 9), np.float32)
+    _check(lib.oracle_render_backward_f32_mt(_ptr(s), n, _ptr(_c(bins.vals, np.uint32)),
+                                             _ptr(_c(bins.ranges, np.uint32)), width, height,
+                                             _ptr(_c(out_rgba, np.float32)), _ptr(_c(final_T, np.float32)),
+                                             _ptr(_c(last_contrib, np.uint32)), _ptr(_c(v_out, np.float32)),
+                                             _ptr(grad), threads), "backward_mt")
     return grad
 
 

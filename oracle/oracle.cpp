@@ -41,6 +41,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <thread>
 #include <vector>
 
 namespace {
@@ -286,9 +287,10 @@ PixelOut<R> forward_pixel(const R* splats, const uint32_t* vals, uint32_t start,
 
 template <typename R>
 void render_forward(const R* splats, const uint32_t* vals, const uint32_t* ranges, uint32_t width,
-                    uint32_t height, R* out_rgba, R* final_T, uint32_t* last_contrib, FwdStats* st) {
+                    uint32_t row_begin, uint32_t row_end, R* out_rgba, R* final_T, uint32_t* last_contrib,
+                    FwdStats* st) {
   const uint32_t tiles_x = (width + kTile - 1) / kTile;
-  for (uint32_t py = 0; py < height; ++py)
+  for (uint32_t py = row_begin; py < row_end; ++py)
     for (uint32_t px = 0; px < width; ++px) {
       const uint32_t t = (py / kTile) * tiles_x + (px / kTile);
       const PixelOut<R> o = forward_pixel(splats, vals, ranges[2 * t], ranges[2 * t + 1], px, py, st);
@@ -318,13 +320,14 @@ struct BwdStats {
 
 template <typename R>
 void render_backward(const R* splats, uint32_t n, const uint32_t* vals, const uint32_t* ranges, uint32_t width,
-                     uint32_t height, const R* out_rgba, const R* final_T, const uint32_t* last_contrib,
-                     const R* v_out, double* acc_grad /* [n][9] */, BwdStats* st) {
+                     uint32_t row_begin, uint32_t row_end, const R* out_rgba, const R* final_T,
+                     const uint32_t* last_contrib, const R* v_out, double* acc_grad /* [n][9], accumulated */,
+                     BwdStats* st) {
   using C = Consts<R>;
   (void)final_T;  // the forward-order form needs C_final and the replayed T, not the final T
-  std::fill(acc_grad, acc_grad + size_t(n) * 9, 0.0);
+  (void)n;
   const uint32_t tiles_x = (width + kTile - 1) / kTile;
-  for (uint32_t py = 0; py < height; ++py)
+  for (uint32_t py = row_begin; py < row_end; ++py)
     for (uint32_t px = 0; px < width; ++px) {
       const size_t p = size_t(py) * width + px;
       const uint32_t t = (py / kTile) * tiles_x + (px / kTile);
@@ -377,6 +380,18 @@ void render_backward(const R* splats, uint32_t n, const uint32_t* vals, const ui
         T = T * one_m;
       }
     }
+}
+
+// Runs fn(thread, row_begin, row_end) over bands of 16 pixel rows dealt round-robin to `threads` threads.
+template <typename Fn>
+void run_bands(uint32_t height, uint32_t threads, Fn fn) {
+  const uint32_t bands = (height + kTile - 1) / kTile;
+  std::vector<std::thread> pool;
+  for (uint32_t t = 0; t < threads; ++t)
+    pool.emplace_back([=] {
+      for (uint32_t b = t; b < bands; b += threads) fn(t, b * kTile, std::min(height, (b + 1) * kTile));
+    });
+  for (auto& th : pool) th.join();
 }
 
 }  // namespace
@@ -476,7 +491,7 @@ int oracle_render_forward_f32(const float* splats, const uint32_t* vals, const u
                               uint64_t* stats) {
   if (!ranges || !out_rgba || !final_T || !last_contrib || width == 0 || height == 0) return -1;
   FwdStats st{};
-  render_forward<float>(splats, vals, ranges, width, height, out_rgba, final_T, last_contrib, &st);
+  render_forward<float>(splats, vals, ranges, width, 0, height, out_rgba, final_T, last_contrib, &st);
   if (stats) std::memcpy(stats, &st, sizeof st);
   return 0;
 }
@@ -486,7 +501,7 @@ int oracle_render_forward_f64(const double* splats, const uint32_t* vals, const 
                               uint64_t* stats) {
   if (!ranges || !out_rgba || !final_T || !last_contrib || width == 0 || height == 0) return -1;
   FwdStats st{};
-  render_forward<double>(splats, vals, ranges, width, height, out_rgba, final_T, last_contrib, &st);
+  render_forward<double>(splats, vals, ranges, width, 0, height, out_rgba, final_T, last_contrib, &st);
   if (stats) std::memcpy(stats, &st, sizeof st);
   return 0;
 }
@@ -499,9 +514,9 @@ int oracle_render_backward_f32(const float* splats, uint32_t n, const uint32_t* 
                                uint64_t* stats) {
   if (!ranges || !out_rgba || !last_contrib || !v_out || (n && !splats_grad) || width == 0 || height == 0)
     return -1;
-  std::vector<double> acc(size_t(n) * 9);
+  std::vector<double> acc(size_t(n) * 9, 0.0);
   BwdStats st{};
-  render_backward<float>(splats, n, vals, ranges, width, height, out_rgba, final_T, last_contrib, v_out,
+  render_backward<float>(splats, n, vals, ranges, width, 0, height, out_rgba, final_T, last_contrib, v_out,
                          acc.data(), &st);
   if (stats) std::memcpy(stats, &st, sizeof st);
   for (size_t k = 0; k < acc.size(); ++k) splats_grad[k] = float(acc[k]);
@@ -514,8 +529,46 @@ int oracle_render_backward_f64(const double* splats, uint32_t n, const uint32_t*
   if (!ranges || !out_rgba || !last_contrib || !v_out || (n && !splats_grad) || width == 0 || height == 0)
     return -1;
   BwdStats st{};
-  render_backward<double>(splats, n, vals, ranges, width, height, out_rgba, final_T, last_contrib, v_out,
+  std::fill(splats_grad, splats_grad + size_t(n) * 9, 0.0);
+  render_backward<double>(splats, n, vals, ranges, width, 0, height, out_rgba, final_T, last_contrib, v_out,
                           splats_grad, &st);
+  return 0;
+}
+
+// The same forward and backward spread over `threads` host threads for timing on all cores: bands of 16 pixel
+// rows (one tile row) are dealt round-robin to the threads, which run the per-pixel functions above unchanged.
+// The forward's outputs are identical to the single-threaded call; the backward's per-splat sums are kept per
+// thread in double and added in thread order, so they may differ from the single-threaded sums in the last bits
+// of the double before the one rounding to fp32.
+int oracle_render_forward_f32_mt(const float* splats, const uint32_t* vals, const uint32_t* ranges, uint32_t width,
+                                 uint32_t height, float* out_rgba, float* final_T, uint32_t* last_contrib,
+                                 uint32_t threads) {
+  if (!ranges || !out_rgba || !final_T || !last_contrib || width == 0 || height == 0 || threads == 0) return -1;
+  std::vector<FwdStats> st(threads);
+  run_bands(height, threads, [&](uint32_t t, uint32_t y0, uint32_t y1) {
+    render_forward<float>(splats, vals, ranges, width, y0, y1, out_rgba, final_T, last_contrib, &st[t]);
+  });
+  return 0;
+}
+
+int oracle_render_backward_f32_mt(const float* splats, uint32_t n, const uint32_t* vals, const uint32_t* ranges,
+                                  uint32_t width, uint32_t height, const float* out_rgba, const float* final_T,
+                                  const uint32_t* last_contrib, const float* v_out, float* splats_grad,
+                                  uint32_t threads) {
+  if (!ranges || !out_rgba || !last_contrib || !v_out || (n && !splats_grad) || width == 0 || height == 0 ||
+      threads == 0)
+    return -1;
+  std::vector<std::vector<double>> acc(threads, std::vector<double>(size_t(n) * 9, 0.0));
+  std::vector<BwdStats> st(threads);
+  run_bands(height, threads, [&](uint32_t t, uint32_t y0, uint32_t y1) {
+    render_backward<float>(splats, n, vals, ranges, width, y0, y1, out_rgba, final_T, last_contrib, v_out,
+                           acc[t].data(), &st[t]);
+  });
+  for (size_t k = 0; k < size_t(n) * 9; ++k) {
+    double sum = 0.0;
+    for (uint32_t t = 0; t < threads; ++t) sum += acc[t][k];
+    splats_grad[k] = float(sum);
+  }
   return 0;
 }
 

@@ -164,3 +164,19 @@ def test_f32_backward_matches_f64_tiny_scene(orc):
     g32 = analytic(orc, sc.splats, bins, 64, 64, sc.v_out, "f32")
     g64 = analytic(orc, sc.splats.astype(np.float64), bins, 64, 64, sc.v_out.astype(np.float64))
     assert np.allclose(g32, g64, rtol=1e-4, atol=1e-4)
+
+
+def test_threaded_oracle_matches_single_threaded(orc):
+    """The all-cores timing wrapper runs the same per-pixel code by bands of tile rows: identical forward outputs,
+    backward sums equal up to the order of double additions."""
+    from differentiable_gaussian_splatting_amd import scenes
+    sc = scenes.make_scene(scenes.SceneSpec(name="mt", width=120, height=88, n=2000, seed=41,
+                                            size_classes=((1.0, 0.5, 12.0),)))
+    b = orc.bin(sc.splats, sc.depths, 120, 88)
+    out, ft, lc, _ = orc.render_forward(sc.splats, b, 120, 88)
+    g = orc.render_backward(sc.splats, b, 120, 88, out, ft, lc, sc.v_out)
+    for threads in (1, 3, 8):
+        o2, f2, l2 = orc.render_forward_mt(sc.splats, b, 120, 88, threads)
+        assert np.array_equal(o2, out) and np.array_equal(f2, ft) and np.array_equal(l2, lc)
+        g2 = orc.render_backward_mt(sc.splats, b, 120, 88, out, ft, lc, sc.v_out, threads)
+        assert np.allclose(g2, g, rtol=1e-6, atol=1e-9)
