@@ -417,6 +417,46 @@ __global__ __launch_bounds__(kThreads) void k_ranges(const K* __restrict__ keys,
   }
 }
 
+// Longest lists first, so that the raster kernels start the slowest tiles at once and the short ones fill the
+// workgroup slots that free up (the tile loads differ several-fold, and the grid exceeds the resident slots).
+constexpr uint32_t kOrderThreads = 1024, kOrderClasses = 64;
+
+__global__ __launch_bounds__(kOrderThreads) void k_tile_order(const uint32_t* __restrict__ ranges,
+                                                              const uint32_t* __restrict__ cost, uint32_t num_tiles,
+                                                              uint32_t num_pairs, uint32_t* __restrict__ order) {
+  __shared__ uint32_t s_count[kOrderClasses], s_base[kOrderClasses];
+  __shared__ uint32_t s_max;
+  const uint32_t tid = threadIdx.x;
+  if (tid < kOrderClasses) s_count[tid] = 0;
+  if (tid == 0) s_max = 0;
+  __syncthreads();
+  auto len_of = [&](uint32_t t) {
+    if (cost) return cost[4 * t] + cost[4 * t + 1] + cost[4 * t + 2] + cost[4 * t + 3];
+    const uint32_t start = min(ranges[2 * t], num_pairs);
+    const uint32_t end = max(start, min(ranges[2 * t + 1], num_pairs));
+    return end - start;
+  };
+  uint32_t lmax = 0;
+  for (uint32_t t = tid; t < num_tiles; t += kOrderThreads) lmax = max(lmax, len_of(t));
+  atomicMax(&s_max, lmax);
+  __syncthreads();
+  const uint64_t span = uint64_t(s_max) + 1;
+  auto class_of = [&](uint32_t t) {  // 0 = longest
+    return kOrderClasses - 1 - uint32_t(uint64_t(len_of(t)) * kOrderClasses / span);
+  };
+  for (uint32_t t = tid; t < num_tiles; t += kOrderThreads) atomicAdd(&s_count[class_of(t)], 1u);
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t run = 0;
+    for (uint32_t c = 0; c < kOrderClasses; ++c) {
+      s_base[c] = run;
+      run += s_count[c];
+    }
+  }
+  __syncthreads();
+  for (uint32_t t = tid; t < num_tiles; t += kOrderThreads) order[atomicAdd(&s_base[class_of(t)], 1u)] = t;
+}
+
 uint32_t bits_of(uint64_t v) {
   uint32_t b = 0;
   for (; v; v >>= 1) ++b;
@@ -426,6 +466,27 @@ uint32_t bits_of(uint64_t v) {
 uint32_t grid_for(uint64_t items, uint32_t per_block) { return uint32_t((items + per_block - 1) / per_block); }
 
 }  // namespace
+}  // namespace gsr
+
+namespace gsr {
+
+void launch_tile_order(hipStream_t s, const uint32_t* ranges, const uint32_t* cost, uint32_t num_tiles,
+                       uint32_t num_pairs, uint32_t* order) {
+  if (num_tiles)
+    hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(kOrderThreads), 0, s, ranges, cost, num_tiles, num_pairs, order);
+}
+
+const uint32_t* raster_tile_order(gsr_ctx* ctx, hipStream_t s, const gsr_bins* bins, gsr_status* st) {
+  Arena& a = ctx->arena;
+  const uint64_t num_tiles = uint64_t(bins->tiles_x) * bins->tiles_y;
+  *st = GSR_OK;
+  if ((*st = grow(ctx, a.tile_order_ext, size_t(num_tiles) * 4))) return nullptr;
+  uint32_t* order = static_cast<uint32_t*>(a.tile_order_ext.ptr);
+  const uint32_t* cost = ctx->cost_tiles == num_tiles ? static_cast<const uint32_t*>(a.tile_cost.ptr) : nullptr;
+  launch_tile_order(s, bins->ranges, cost, uint32_t(num_tiles), bins->num_pairs, order);
+  return order;
+}
+
 }  // namespace gsr
 
 using namespace gsr;

@@ -111,7 +111,8 @@ void gsr_destroy(gsr_ctx* ctx) {
   (void)hipSetDevice(ctx->device);
   Arena& a = ctx->arena;
   for (DevBuf* b : {&a.keys[0], &a.keys[1], &a.vals[0], &a.vals[1], &a.counts, &a.offsets, &a.order, &a.order_alt,
-                    &a.order_vals, &a.order_vals_alt, &a.scan_part, &a.hist, &a.digit_tot, &a.ranges, &a.rects})
+                    &a.order_vals, &a.order_vals_alt, &a.scan_part, &a.hist, &a.digit_tot, &a.ranges, &a.rects,
+                    &a.tile_order_ext, &a.tile_cost})
     release(*b);
   if (a.host_total) (void)hipHostFree(a.host_total);
   if (a.total_ready) (void)hipEventDestroy(a.total_ready);

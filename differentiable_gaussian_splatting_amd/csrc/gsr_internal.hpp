@@ -39,6 +39,8 @@ struct Arena {
   DevBuf digit_tot;   // uint32 [256] per-digit totals of the current pass
   DevBuf ranges;      // uint32 [2 * tiles]
   DevBuf rects;       // uint32x4 [splat capacity] tile rectangle (tx0, ty0, w, h) of each splat, natural order
+  DevBuf tile_order_ext;  // uint32 [tiles] raster launch order: the slowest expected tiles first
+  DevBuf tile_cost;   // uint32 [4 tiles] splats each wavefront of the last forward walked (launch-order hint)
   uint64_t* host_total = nullptr;  // pinned host word for the one pair-count readback
   hipEvent_t total_ready = nullptr;  // recorded after the readback is queued
 };
@@ -53,6 +55,7 @@ struct gsr_ctx {
   int32_t bin_rule = GSR_BIN_BOX;
   bool bin_keys = true;
   bool raster_skip = true;  // per-wave cull and the backward's all-lanes-rejected skip
+  uint64_t cost_tiles = 0;  // tile count of the grid tile_cost describes (0: none yet)
 };
 
 namespace gsr {
@@ -71,6 +74,17 @@ gsr_status grow(gsr_ctx* ctx, DevBuf& b, size_t bytes);
 
 // Checks for launch errors after queuing kernels.
 gsr_status check_launch(gsr_ctx* ctx, const char* what);
+
+// Raster launch order (bin.hip): writes into `order` the tiles 0..num_tiles-1 with the longest pair lists first
+// (64 length classes; any order inside a class), on stream s. One workgroup.
+// With `cost` ([4 tiles], per-wavefront walk lengths of an earlier forward on the same grid), tiles are ranked by
+// their summed cost instead of their list length.
+void launch_tile_order(hipStream_t s, const uint32_t* ranges, const uint32_t* cost, uint32_t num_tiles,
+                       uint32_t num_pairs, uint32_t* order);
+// The launch order of the raster kernels for `bins`, computed now into the arena: by the last forward's measured
+// per-tile cost when it ran on the same tile grid, else by list length. Results never depend on the order; it only
+// lets the slowest tiles start first. Null on failure (the error is recorded on ctx).
+const uint32_t* raster_tile_order(gsr_ctx* ctx, hipStream_t s, const gsr_bins* bins, gsr_status* st);
 
 // Radix sort (sort.hip). Sorts n (key, value) pairs stably by the low key_bits bits, 6 or 8 bits per pass
 // (sort_passes). The result lands in (keys_out, vals_out); (tmp_keys, tmp_vals) are scratch of n elements. The

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
     const float* __restrict__ splats, uint32_t n, const uint32_t* __restrict__ vals,
     const uint32_t* __restrict__ ranges, uint32_t num_pairs, uint32_t tiles_x, uint32_t width, uint32_t height,
     const float4* __restrict__ out_rgba, const uint32_t* __restrict__ last_contrib, const float4* __restrict__ v_out,
-    float* __restrict__ splats_grad) {
+    float* __restrict__ splats_grad, const uint32_t* __restrict__ tile_order, uint32_t num_tiles) {
   constexpr uint32_t kWaves = kTilePixels / kWave;
   __shared__ StagedSplat s_sp[kTilePixels];
   __shared__ float s_acc[kTilePixels][kGrads];
@@ -122,7 +122,8 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
   const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int slot_any = transpose_index(lane);               // all lanes take part in the exchanges
   const int my_slot = (lane & 3u) == 0 ? slot_any : -1;      // the term this lane totals (4 copies; one adds)
-  const uint32_t tile = blockIdx.x;
+  const uint32_t tile = tile_order[blockIdx.x];  // slowest expected first (a permutation of the tiles)
+  if (tile >= num_tiles) return;                 // not reachable with a permutation; keeps reads in bounds
   const uint32_t tx0 = (tile % tiles_x) * kTile, ty0 = (tile / tiles_x) * kTile;
   const uint32_t px = tx0 + lane_px(w, lane), py = ty0 + lane_py(w, lane);
   const bool inside = px < width && py < height;
@@ -270,10 +271,12 @@ extern "C" gsr_status gsr_render_backward(gsr_ctx* ctx, void* stream, const floa
   if (count)
     hipLaunchKernelGGL(k_zero, dim3(uint32_t((count + kTilePixels - 1) / kTilePixels)), dim3(kTilePixels), 0, s,
                        splats_grad, count);
+  const uint32_t* order = raster_tile_order(ctx, s, bins, &st);
+  if (!order) return st;
   auto kernel = ctx->raster_skip ? k_backward<true> : k_backward<false>;
   hipLaunchKernelGGL(kernel, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, s, splats, n, bins->vals,
                      bins->ranges, bins->num_pairs, tiles_x, width, height,
                      reinterpret_cast<const float4*>(out_rgba), last_contrib, reinterpret_cast<const float4*>(v_out),
-                     splats_grad);
+                     splats_grad, order, uint32_t(num_tiles));
   return check_launch(ctx, "gsr_render_backward");
 }

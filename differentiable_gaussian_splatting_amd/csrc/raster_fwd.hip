@@ -21,12 +21,15 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
                                                          const uint32_t* __restrict__ ranges, uint32_t num_pairs,
                                                          uint32_t tiles_x, uint32_t width, uint32_t height,
                                                          float4* __restrict__ out_rgba, float* __restrict__ final_T,
-                                                         uint32_t* __restrict__ last_contrib) {
+                                                         uint32_t* __restrict__ last_contrib,
+                                                         const uint32_t* __restrict__ tile_order, uint32_t num_tiles,
+                                                         uint32_t* __restrict__ tile_cost) {
   constexpr uint32_t kWaves = kTilePixels / kWave;
   __shared__ StagedSplat s_sp[kTilePixels];
   __shared__ uint64_t s_mask[kWaves][kWaves];  // [reading wave][staging wave]: slots that can reach the reader
   const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  const uint32_t tile = blockIdx.x;
+  const uint32_t tile = tile_order[blockIdx.x];  // slowest expected first (a permutation of the tiles)
+  if (tile >= num_tiles) return;                 // not reachable with a permutation; keeps reads in bounds
   const uint32_t tx0 = (tile % tiles_x) * kTile, ty0 = (tile / tiles_x) * kTile;
   const uint32_t px = tx0 + lane_px(w, lane), py = ty0 + lane_py(w, lane);
   const bool inside = px < width && py < height;
@@ -36,6 +39,7 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
 
   float T = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f;
   uint32_t last = 0;
+  uint32_t walked = 0;  // splats this wave evaluated (wave-uniform): the tile's cost for the launch order
   // A lane whose pixel has stopped (or lies outside the image) moves its centre to +inf: sigma is then inf or NaN
   // for every later splat, which evaluate() rejects, so finished lanes need no test of their own.
   const float kFar = __builtin_huge_valf();
@@ -62,6 +66,7 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
         const uint32_t j = sw * kWave + uint32_t(__builtin_ctzll(m));
         m &= m - 1;
         const StagedSplat& s = s_sp[j];
+        ++walked;
         Eval e;
         if (evaluate<true>(s, cxe, cy, e)) {
           const float next_T = T * (1.0f - e.alpha);
@@ -89,6 +94,7 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
     final_T[p] = T;
     last_contrib[p] = last;
   }
+  if (lane == 0) tile_cost[4 * size_t(tile) + w] = walked;
 }
 
 }  // namespace
@@ -113,9 +119,16 @@ extern "C" gsr_status gsr_render_forward(gsr_ctx* ctx, void* stream, const float
   if (num_tiles >= (uint64_t(1) << 31)) return fail(ctx, GSR_EINVAL, "gsr_render_forward: too many tiles");
   gsr_status st = enter(ctx);
   if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint32_t* order = raster_tile_order(ctx, s, bins, &st);
+  if (!order) return st;
+  // the walk lengths of this forward rank the tiles of the next raster launch on this grid
+  if ((st = grow(ctx, ctx->arena.tile_cost, size_t(num_tiles) * 16))) return st;
   auto kernel = ctx->raster_skip ? k_forward<true> : k_forward<false>;
-  hipLaunchKernelGGL(kernel, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, static_cast<hipStream_t>(stream),
-                     splats, n, bins->vals, bins->ranges, bins->num_pairs, tiles_x, width, height,
-                     reinterpret_cast<float4*>(out_rgba), final_T, last_contrib);
-  return check_launch(ctx, "gsr_render_forward");
+  hipLaunchKernelGGL(kernel, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, s, splats, n, bins->vals,
+                     bins->ranges, bins->num_pairs, tiles_x, width, height, reinterpret_cast<float4*>(out_rgba),
+                     final_T, last_contrib, order, uint32_t(num_tiles), static_cast<uint32_t*>(ctx->arena.tile_cost.ptr));
+  if ((st = check_launch(ctx, "gsr_render_forward"))) return st;
+  ctx->cost_tiles = num_tiles;
+  return GSR_OK;
 }
