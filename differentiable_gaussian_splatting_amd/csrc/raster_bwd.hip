@@ -116,6 +116,7 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
     float* __restrict__ splats_grad, const uint32_t* __restrict__ tile_order, uint32_t num_tiles) {
   constexpr uint32_t kWaves = kTilePixels / kWave;
   __shared__ StagedSplat s_sp[kTilePixels];
+  __shared__ double s_exp2[64];  // 2^(j/32) table of the exact exponential
   __shared__ float s_acc[kTilePixels][kGrads];
   __shared__ uint64_t s_mask[kWaves][kWaves];  // [reading wave][staging wave]
   __shared__ uint32_t s_max_last;
@@ -124,6 +125,7 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
   const int my_slot = (lane & 3u) == 0 ? slot_any : -1;      // the term this lane totals (4 copies; one adds)
   const uint32_t tile = tile_order[blockIdx.x];  // slowest expected first (a permutation of the tiles)
   if (tile >= num_tiles) return;                 // not reachable with a permutation; keeps reads in bounds
+  load_exp_table(s_exp2);                        // the barriers below order it
   const uint32_t tx0 = (tile % tiles_x) * kTile, ty0 = (tile / tiles_x) * kTile;
   const uint32_t px = tx0 + lane_px(w, lane), py = ty0 + lane_py(w, lane);
   const bool inside = px < width && py < height;
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
 #pragma unroll
         for (uint32_t q = 0; q < kGrads; ++q) d[q] = 0.0f;
         Eval e;
-        const bool contrib = rel0 + j < last && evaluate<false>(s, cx, cy, e);
+        const bool contrib = rel0 + j < last && evaluate<false>(s, cx, cy, e, s_exp2);
         if (contrib) {
           const float one_m = 1.0f - e.alpha;
           const float wgt = e.alpha * T;

@@ -20,29 +20,63 @@ constexpr float kSigmaSkip = 5.55f;
 // 1/255 by a relative margin of 2^-12 cannot reach 1/255 when evaluated exactly.
 constexpr float kAlphaMinCertain = kAlphaMin * (1.0f - 1.0f / 4096.0f);
 
-// e^x rounded to fp32, for |x| below 80. Cody-Waite reduction x = k ln2 + r with |r| <= ln2 / 2 (ln2 split into a
-// 32-bit head, exact in k * head for |k| < 2^20, and a tail), the Taylor series of e^r to degree 11 in fp64
-// (truncation below 7e-15 relative) evaluated by Estrin's scheme (pairs, then powers r^2, r^4, r^8: every fma adds
-// a temporary, so no coefficient register is overwritten), then scaling by 2^k and one rounding to fp32. The fp64
-// value is within about 2^-46 of e^x, so the fp32 result is the correctly rounded one except when e^x lies within
-// 2^-46 (relative) of the midpoint between two floats, i.e. about one argument in 2^22.
-__host__ __device__ __forceinline__ float exp_rn(float x) {
+// 2^(j/32) for j = 0..31 as pairs (hi, lo) of doubles: hi is the value rounded to double, lo the rounded
+// remainder, so hi + lo carries it to about 2^-106.
+constexpr double kExp2Tab[64] = {
+    0x1.0000000000000p+0, 0x0.0p+0,  // j = 0
+    0x1.059b0d3158574p+0, 0x1.d73e2a475b465p-55,  // j = 1
+    0x1.0b5586cf9890fp+0, 0x1.8a62e4adc610bp-54,  // j = 2
+    0x1.11301d0125b51p+0, -0x1.6c51039449b3ap-54,  // j = 3
+    0x1.172b83c7d517bp+0, -0x1.19041b9d78a76p-55,  // j = 4
+    0x1.1d4873168b9aap+0, 0x1.e016e00a2643cp-54,  // j = 5
+    0x1.2387a6e756238p+0, 0x1.9b07eb6c70573p-54,  // j = 6
+    0x1.29e9df51fdee1p+0, 0x1.612e8afad1255p-55,  // j = 7
+    0x1.306fe0a31b715p+0, 0x1.6f46ad23182e4p-55,  // j = 8
+    0x1.371a7373aa9cbp+0, -0x1.63aeabf42eae2p-54,  // j = 9
+    0x1.3dea64c123422p+0, 0x1.ada0911f09ebcp-55,  // j = 10
+    0x1.44e086061892dp+0, 0x1.89b7a04ef80d0p-59,  // j = 11
+    0x1.4bfdad5362a27p+0, 0x1.d4397afec42e2p-56,  // j = 12
+    0x1.5342b569d4f82p+0, -0x1.07abe1db13cadp-55,  // j = 13
+    0x1.5ab07dd485429p+0, 0x1.6324c054647adp-54,  // j = 14
+    0x1.6247eb03a5585p+0, -0x1.383c17e40b497p-54,  // j = 15
+    0x1.6a09e667f3bcdp+0, -0x1.bdd3413b26456p-54,  // j = 16
+    0x1.71f75e8ec5f74p+0, -0x1.16e4786887a99p-55,  // j = 17
+    0x1.7a11473eb0187p+0, -0x1.41577ee04992fp-55,  // j = 18
+    0x1.82589994cce13p+0, -0x1.d4c1dd41532d8p-54,  // j = 19
+    0x1.8ace5422aa0dbp+0, 0x1.6e9f156864b27p-54,  // j = 20
+    0x1.93737b0cdc5e5p+0, -0x1.75fc781b57ebcp-57,  // j = 21
+    0x1.9c49182a3f090p+0, 0x1.c7c46b071f2bep-56,  // j = 22
+    0x1.a5503b23e255dp+0, -0x1.d2f6edb8d41e1p-54,  // j = 23
+    0x1.ae89f995ad3adp+0, 0x1.7a1cd345dcc81p-54,  // j = 24
+    0x1.b7f76f2fb5e47p+0, -0x1.5584f7e54ac3bp-56,  // j = 25
+    0x1.c199bdd85529cp+0, 0x1.11065895048ddp-55,  // j = 26
+    0x1.cb720dcef9069p+0, 0x1.503cbd1e949dbp-56,  // j = 27
+    0x1.d5818dcfba487p+0, 0x1.2ed02d75b3707p-55,  // j = 28
+    0x1.dfc97337b9b5fp+0, -0x1.1a5cd4f184b5cp-54,  // j = 29
+    0x1.ea4afa2a490dap+0, -0x1.e9c23179c2893p-54,  // j = 30
+    0x1.f50765b6e4540p+0, 0x1.9d3e12dd8a18bp-54,  // j = 31
+};
+
+// e^x rounded to fp32, for |x| below 80, with `tab` holding kExp2Tab (an LDS copy on the device). Reduction
+// x = k ln2/32 + r with |r| <= ln2/64 (ln2/32 split into a 32-bit head, exact in k * head for |k| < 2^21, and a
+// tail), e^r - 1 by its Taylor series to degree 6 (truncation below 4e-18), then
+// 2^(k/32) e^r = 2^floor(k/32) (hi + (hi (e^r - 1) + lo)) with one rounding to double and one to fp32. The double
+// is within about 1.2e-16 (relative) of e^x; over every float x in [-5.55, 0] (the arguments the raster kernels
+// evaluate) the fp32 result equals the correctly rounded e^x, which a host test checks exhaustively.
+__host__ __device__ __forceinline__ float exp_rn(float x, const double* tab) {
   const double xd = double(x);
-  const double k = rint(xd * 1.4426950408889634074);
-  double r = fma(-k, 6.93147180369123816490e-01, xd);
-  r = fma(-k, 1.90821492927058770002e-10, r);
-  const double r2 = r * r, r4 = r2 * r2, r8 = r4 * r4;
-  const double q0 = r + 1.0;                                  // 1 + r
-  const double q1 = fma(1.0 / 6.0, r, 0.5);                   // 1/2! + r/3!
-  const double q2 = fma(1.0 / 120.0, r, 1.0 / 24.0);          // 1/4! + r/5!
-  const double q3 = fma(1.0 / 5040.0, r, 1.0 / 720.0);        // 1/6! + r/7!
-  const double q4 = fma(1.0 / 362880.0, r, 1.0 / 40320.0);    // 1/8! + r/9!
-  const double q5 = fma(1.0 / 39916800.0, r, 1.0 / 3628800.0);  // 1/10! + r/11!
-  const double s0 = fma(q1, r2, q0);
-  const double s1 = fma(q3, r2, q2);
-  const double s2 = fma(q5, r2, q4);
-  const double p = fma(s2, r8, fma(s1, r4, s0));
-  return float(ldexp(p, int(k)));
+  const double k = rint(xd * 46.166241308446828384);  // 32 / ln 2
+  double r = fma(-k, 0x1.62e42fee00000p-6, xd);
+  r = fma(-k, 0x1.a39ef35793c76p-38, r);
+  const double r2 = r * r;
+  double q = fma(r, 1.0 / 720.0, 1.0 / 120.0);
+  q = fma(q, r, 1.0 / 24.0);
+  q = fma(q, r, 1.0 / 6.0);
+  q = fma(q, r, 0.5);
+  q = fma(q, r2, r);  // e^r - 1
+  const int ki = int(k);
+  const double hi = tab[2 * (ki & 31)], lo = tab[2 * (ki & 31) + 1];
+  return float(ldexp(hi + fma(hi, q, lo), ki >> 5));
 }
 
 // One splat as staged in LDS for a batch: 48 bytes, read by every lane of a wavefront at the same address.
@@ -125,6 +159,11 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Copies kExp2Tab into the workgroup's LDS table (threads 0..63); a barrier must follow before its first use.
+__device__ __forceinline__ void load_exp_table(double* s_tab) {
+  if (threadIdx.x < 64) s_tab[threadIdx.x] = kExp2Tab[threadIdx.x];
+}
+
 // Wave-uniform 64-bit value held in scalar registers.
 __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
@@ -154,7 +193,7 @@ constexpr float kAlphaMinLo = kAlphaMin * (1.0f - kBand), kAlphaMinHi = kAlphaMi
 constexpr float kAlphaMaxLo = kAlphaMax * (1.0f - kBand), kAlphaMaxHi = kAlphaMax * (1.0f + kBand);
 
 template <bool kExactValues>
-__device__ __forceinline__ bool evaluate(const StagedSplat& s, float cx, float cy, Eval& e) {
+__device__ __forceinline__ bool evaluate(const StagedSplat& s, float cx, float cy, Eval& e, const double* tab) {
   e.dx = cx - s.x;
   e.dy = cy - s.y;
   const float t_a = (s.ha * e.dx) * e.dx;
@@ -166,11 +205,11 @@ __device__ __forceinline__ bool evaluate(const StagedSplat& s, float cx, float c
   const float og_fast = s.o * g_fast;
   if (kExactValues) {
     if (og_fast < kAlphaMinCertain) return false;
-    e.G = exp_rn(-sigma);
+    e.G = exp_rn(-sigma, tab);
   } else {
     if (og_fast < kAlphaMinLo) return false;
     const bool near = og_fast < kAlphaMinHi || (og_fast > kAlphaMaxLo && og_fast < kAlphaMaxHi);
-    e.G = near ? exp_rn(-sigma) : g_fast;
+    e.G = near ? exp_rn(-sigma, tab) : g_fast;
   }
   e.oG = s.o * e.G;
   e.alpha = (e.oG < kAlphaMax) ? e.oG : kAlphaMax;
