@@ -128,9 +128,9 @@ uint32_t gsr_radix_pass_count(uint64_t num_tiles, uint32_t digit_bits);
  *   alpha = min(0.999, o exp(-sigma)); skip if alpha < 1/255;
  *   T' = T (1 - alpha); if T' < 1e-4 the pixel stops here without compositing this splat;
  *   C += rgb (alpha T); T = T'; last = list position + 1.
- * exp(-sigma) is the fp32 value of e^-sigma, correctly rounded except in about one case in 4 million, and every
- * other operation is one IEEE fp32 operation in the order written (no fused multiply-add), so results match a
- * plain fp32 evaluation of the definition. Splats with sigma >= 5.55 are skipped before the exponential, which
+ * exp(-sigma) is the correctly rounded fp32 value of e^-sigma (on every float sigma in [0, 5.55] it equals the
+ * double-precision exp rounded to fp32), and every other operation is one IEEE fp32 operation in the order written
+ * (no fused multiply-add), so results match a plain fp32 evaluation of the definition. Splats with sigma >= 5.55 are skipped before the exponential, which
  * cannot change a result because o <= 1 makes their alpha at most e^-5.55 < 1/255. [A.9 f16 forward page,
  * implementation listing; W1 warp sparse skip + exp-skip page, summary and section 1 row "W1b"; rasterize
  * forward + adam kernel audit page, section 1 rows (a) and (b)]
