@@ -476,14 +476,19 @@ void launch_tile_order(hipStream_t s, const uint32_t* ranges, const uint32_t* co
     hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(kOrderThreads), 0, s, ranges, cost, num_tiles, num_pairs, order);
 }
 
-const uint32_t* raster_tile_order(gsr_ctx* ctx, hipStream_t s, const gsr_bins* bins, gsr_status* st) {
+const uint32_t* raster_tile_order(gsr_ctx* ctx, hipStream_t s, const gsr_bins* bins, bool backward,
+                                  gsr_status* st) {
   Arena& a = ctx->arena;
   const uint64_t num_tiles = uint64_t(bins->tiles_x) * bins->tiles_y;
   *st = GSR_OK;
+  if (backward && ctx->order_ranges == bins->ranges && ctx->order_tiles == num_tiles && a.tile_order_ext.ptr)
+    return static_cast<const uint32_t*>(a.tile_order_ext.ptr);
   if ((*st = grow(ctx, a.tile_order_ext, size_t(num_tiles) * 4))) return nullptr;
   uint32_t* order = static_cast<uint32_t*>(a.tile_order_ext.ptr);
   const uint32_t* cost = ctx->cost_tiles == num_tiles ? static_cast<const uint32_t*>(a.tile_cost.ptr) : nullptr;
   launch_tile_order(s, bins->ranges, cost, uint32_t(num_tiles), bins->num_pairs, order);
+  ctx->order_ranges = backward ? nullptr : bins->ranges;
+  ctx->order_tiles = num_tiles;
   return order;
 }
 
@@ -501,6 +506,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   if (num_tiles >= (uint64_t(1) << 32)) return fail(ctx, GSR_EINVAL, "gsr_bin: too many tiles");
   gsr_status st = enter(ctx);
   if (st) return st;
+  ctx->order_ranges = nullptr;  // the ranges are rewritten: rank again before the next raster launch
   hipStream_t s = static_cast<hipStream_t>(stream);
   Arena& a = ctx->arena;
   const bool presort = ctx->bin_scheme == GSR_BIN_PRESORT;

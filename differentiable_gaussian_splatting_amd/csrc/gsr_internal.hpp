@@ -56,6 +56,8 @@ struct gsr_ctx {
   bool bin_keys = true;
   bool raster_skip = true;  // per-wave cull and the backward's all-lanes-rejected skip
   uint64_t cost_tiles = 0;  // tile count of the grid tile_cost describes (0: none yet)
+  const uint32_t* order_ranges = nullptr;  // the ranges tile_order_ext was last ranked for (by a forward)
+  uint64_t order_tiles = 0;
 };
 
 namespace gsr {
@@ -84,7 +86,9 @@ void launch_tile_order(hipStream_t s, const uint32_t* ranges, const uint32_t* co
 // The launch order of the raster kernels for `bins`, computed now into the arena: by the last forward's measured
 // per-tile cost when it ran on the same tile grid, else by list length. Results never depend on the order; it only
 // lets the slowest tiles start first. Null on failure (the error is recorded on ctx).
-const uint32_t* raster_tile_order(gsr_ctx* ctx, hipStream_t s, const gsr_bins* bins, gsr_status* st);
+// The backward reuses the order the forward ranked for the same ranges pointer and grid (gsr_bin clears it).
+const uint32_t* raster_tile_order(gsr_ctx* ctx, hipStream_t s, const gsr_bins* bins, bool backward,
+                                  gsr_status* st);
 
 // Radix sort (sort.hip). Sorts n (key, value) pairs stably by the low key_bits bits, 6 or 8 bits per pass
 // (sort_passes). The result lands in (keys_out, vals_out); (tmp_keys, tmp_vals) are scratch of n elements. The

@@ -273,7 +273,7 @@ extern "C" gsr_status gsr_render_backward(gsr_ctx* ctx, void* stream, const floa
   if (count)
     hipLaunchKernelGGL(k_zero, dim3(uint32_t((count + kTilePixels - 1) / kTilePixels)), dim3(kTilePixels), 0, s,
                        splats_grad, count);
-  const uint32_t* order = raster_tile_order(ctx, s, bins, &st);
+  const uint32_t* order = raster_tile_order(ctx, s, bins, true, &st);
   if (!order) return st;
   auto kernel = ctx->raster_skip ? k_backward<true> : k_backward<false>;
   hipLaunchKernelGGL(kernel, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, s, splats, n, bins->vals,

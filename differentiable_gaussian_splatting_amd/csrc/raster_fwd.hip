@@ -122,7 +122,7 @@ extern "C" gsr_status gsr_render_forward(gsr_ctx* ctx, void* stream, const float
   gsr_status st = enter(ctx);
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const uint32_t* order = raster_tile_order(ctx, s, bins, &st);
+  const uint32_t* order = raster_tile_order(ctx, s, bins, false, &st);
   if (!order) return st;
   // the walk lengths of this forward rank the tiles of the next raster launch on this grid
   if ((st = grow(ctx, ctx->arena.tile_cost, size_t(num_tiles) * 16))) return st;
