@@ -205,12 +205,13 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
           // alpha depends on o and sigma only below the clamp: the opacity and geometry terms get a 0 / 1 factor
           const float dl_da_u = (e.oG < kAlphaMax) ? dl_da : 0.0f;
           d[8] = dl_da_u * e.G;
-          // u = -dL/dsigma: d mean = u (a dx + b dy, b dx + c dy); the conic slots hold u dx dx, u dx dy, u dy dy,
-          // whose factors -1/2, -1, -1/2 are applied once per splat when the tile's sums are flushed.
+          // u = -dL/dsigma: d mean = u (a dx + b dy, b dx + c dy), held halved (formed from a / 2, b / 2, c / 2:
+          // exactly half); the conic slots hold u dx dx, u dx dy, u dy dy. The factors 2 and -1/2, -1, -1/2 are
+          // applied once per splat when the tile's sums are flushed.
           const float u = dl_da_u * e.oG;
           const float ux = u * e.dx, uy = u * e.dy;
-          d[0] = __fmaf_rn(s.a, ux, s.b * uy);
-          d[1] = __fmaf_rn(s.b, ux, s.c * uy);
+          d[0] = __fmaf_rn(s.ha, ux, s.hb * uy);
+          d[1] = __fmaf_rn(s.hb, ux, s.hc * uy);
           d[2] = ux * e.dx;
           d[3] = ux * e.dy;
           d[4] = uy * e.dy;
@@ -228,13 +229,14 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
     lds_barrier();
     // Flush: the batch's accumulator is read in its [slot][value] order, so the 64 lanes of an atomic instruction
     // add to the consecutive values of about seven splats (a few cache lines) rather than to 64 scattered records.
-    // The conic slots' sums of u dx dx, u dx dy, u dy dy scale to dL/da, dL/db, dL/dc.
+    // The mean slots' sums double to dL/dmean; the conic slots' sums of u dx dx, u dx dy, u dy dy scale to dL/da,
+    // dL/db, dL/dc.
     const uint32_t staged = min(kTilePixels, stop - b0);
     for (uint32_t f = tid; f < staged * kGrads; f += kTilePixels) {
       const uint32_t slot = f / kGrads, q = f - slot * kGrads;
       float v = (&s_acc[0][0])[f];
       (&s_acc[0][0])[f] = 0.0f;
-      v = q == 2 || q == 4 ? -0.5f * v : q == 3 ? -v : v;
+      v = q < 2 ? v + v : q == 2 || q == 4 ? -0.5f * v : q == 3 ? -v : v;
       const uint32_t idx = s_sp[slot].idx;
       if (idx != 0xFFFFFFFFu && (!kSkip || v != 0.0f)) atomicAdd(splats_grad + size_t(idx) * kGrads + q, v);
     }

@@ -11,14 +11,10 @@
 namespace gsr {
 
 // Method constants (fp32). [A.9 f16 forward page, listing: alpha clamp 0.999; W1 warp sparse skip + exp-skip page,
-// summary: alpha < 1/255 reject and the sigma >= 5.55 skip]
+// summary: alpha < 1/255 reject and the sigma >= 5.55 skip, which the per-splat bound lr below contains]
 constexpr float kAlphaMax = 0.999f;
 constexpr float kAlphaMin = 1.0f / 255.0f;
 constexpr float kTStop = 1e-4f;
-constexpr float kSigmaSkip = 5.55f;
-// A certain alpha reject: o * exp(-sigma) evaluated with the hardware exp2 (relative error below 1e-6 here) under
-// 1/255 by a relative margin of 2^-12 cannot reach 1/255 when evaluated exactly.
-constexpr float kAlphaMinCertain = kAlphaMin * (1.0f - 1.0f / 4096.0f);
 
 // 2^(j/32) for j = 0..31 as pairs (hi, lo) of doubles: hi is the value rounded to double, lo the rounded
 // remainder, so hi + lo carries it to about 2^-106.
@@ -79,11 +75,16 @@ __host__ __device__ __forceinline__ float exp_rn(float x, const double* tab) {
   return float(ldexp(hi + fma(hi, q, lo), ki >> 5));
 }
 
-// One splat as staged in LDS for a batch: 48 bytes, read by every lane of a wavefront at the same address.
+// One splat as staged in LDS for a batch: 48 bytes, read by every lane of a wavefront at the same address. The
+// conic is kept as a / 2 and c / 2 (what sigma uses) beside b and b / 2; a and c are ha + ha and hc + hc, exactly.
+// lr bounds sigma: alpha <= o e^-sigma < 1/255 wherever sigma > lr, so those evaluations are certain rejects.
+// lr is ln(255 o) from the fast log, raised by 2^-16 relative and 2^-16 absolute (far more than the log's and the
+// product's rounding), and +inf when that log is NaN (o < 0 or NaN: the exact evaluation then decides). For
+// o <= 1, lr < 5.55: the bound contains the sigma >= 5.55 skip.
 struct alignas(16) StagedSplat {
   float x, y, ha, b;  // mean, a / 2, b
   float hc, o, r, g;  // c / 2, opacity, red, green
-  float bl, a, c;     // blue, a, c (the backward's mean gradient needs the full conic)
+  float bl, lr, hb;   // blue, the sigma bound, b / 2
   uint32_t idx;       // splat index, or 0xFFFFFFFF for a slot that must not contribute
 };
 
@@ -93,19 +94,21 @@ __device__ __forceinline__ StagedSplat stage_splat(const float* __restrict__ spl
     const float* p = splats + size_t(idx) * 9;
     s.x = p[0];
     s.y = p[1];
-    s.a = p[2];
+    s.ha = 0.5f * p[2];  // exact: scaling by a power of two
     s.b = p[3];
-    s.c = p[4];
+    s.hb = 0.5f * s.b;
+    s.hc = 0.5f * p[4];
     s.r = p[5];
     s.g = p[6];
     s.bl = p[7];
     s.o = p[8];
-    s.ha = 0.5f * s.a;  // exact: scaling by a power of two
-    s.hc = 0.5f * s.c;
+    const float L = __logf(255.0f * s.o);
+    s.lr = L == L ? (L + __builtin_fabsf(L) * (1.0f / 65536.0f)) + (1.0f / 65536.0f) : __builtin_huge_valf();
     s.idx = idx;
   } else {
     // o = 0 makes every evaluation a reject
-    s.x = s.y = s.a = s.b = s.c = s.r = s.g = s.bl = s.o = s.ha = s.hc = 0.0f;
+    s.x = s.y = s.ha = s.b = s.hb = s.hc = s.r = s.g = s.bl = s.o = 0.0f;
+    s.lr = -__builtin_huge_valf();
     s.idx = 0xFFFFFFFFu;
   }
   return s;
@@ -128,16 +131,17 @@ __device__ __forceinline__ uint32_t lane_py(uint32_t w, uint32_t lane) { return 
 // result.
 __device__ __forceinline__ uint32_t reach_mask(const StagedSplat& s, float x0, float y0) {
   if (s.o < 0.99f / 255.0f) return 0u;  // alpha <= o < 1/255 everywhere (a NaN o falls through)
-  const float det = s.a * s.c - s.b * s.b;
-  if (!(det > 0.0f && s.a > 0.0f)) return 0xFu;
-  const float apc = s.a + s.c;
+  const float a = s.ha + s.ha, c = s.hc + s.hc;
+  const float det = a * c - s.b * s.b;
+  if (!(det > 0.0f && a > 0.0f)) return 0xFu;
+  const float apc = a + c;
   const float kappa = apc * apc / det;
   if (!(kappa <= 1e5f)) return 0xFu;
-  const float L = __logf(255.0f * s.o);
+  const float L = s.lr;  // at least ln(255 o)
   const float Lm = (fmaxf(L, 0.0f) + 1e-3f) * (1.0f + 1e-6f * kappa);
   const float two_l_det = 2.0f * Lm / det;
-  const float rx = __builtin_sqrtf(two_l_det * s.c) * 1.001f + 0.01f;
-  const float ry = __builtin_sqrtf(two_l_det * s.a) * 1.001f + 0.01f;
+  const float rx = __builtin_sqrtf(two_l_det * c) * 1.001f + 0.01f;
+  const float ry = __builtin_sqrtf(two_l_det * a) * 1.001f + 0.01f;
   uint32_t m = 0;
 #pragma unroll
   for (uint32_t q = 0; q < 4; ++q) {
@@ -178,14 +182,14 @@ struct Eval {
 // Evaluates splat s at pixel centre (cx, cy). Returns true when the splat passes every reject (sigma >= 0,
 // alpha >= 1/255); then e holds dx, dy, G = exp(-sigma), o G and alpha = min(0.999, o G).
 // sigma = 0.5 (a dx dx + c dy dy) + b dx dy is formed as (ha dx) dx + (hc dy) dy + (b dx) dy, which rounds to the
-// same fp32 value because halving is exact. Splats with sigma >= 5.55 are rejected before any exponential (their
-// alpha is at most e^-5.55 < 1/255 since o <= 1), and most other rejects are settled by the hardware exp2 before
-// the fp64 evaluation.
+// same fp32 value because halving is exact. Evaluations with sigma > lr (the splat's bound, at least ln(255 o)) are
+// rejected before any exponential: their alpha is below 1/255 by a margin no rounding can close. This contains the
+// pages' sigma >= 5.55 skip (lr < 5.55 for o <= 1) and is exact for any o.
 //
 // kExactValues = true (forward): every splat that passes is evaluated with the correctly rounded G, so alpha and the
 // transmittance chain are exactly those of a plain fp32 evaluation - the stop test T' < 1e-4 depends on them.
 // kExactValues = false (backward): the decisions must still be exact (reject or composite, clamped or not), but the
-// values only feed gradient terms. G comes from the hardware exp2 (relative error below 3e-7 for sigma < 5.55) and
+// values only feed gradient terms. G comes from the hardware exp2 (relative error below 5.2e-7 for sigma < 5.55) and
 // the fp64 value is computed only when o G lies within 2^-18 (relative) of 1/255 or of 0.999, where the fast value
 // could fall on the other side of a threshold.
 constexpr float kBand = 1.0f / 262144.0f;
@@ -200,13 +204,12 @@ __device__ __forceinline__ bool evaluate(const StagedSplat& s, float cx, float c
   const float t_c = (s.hc * e.dy) * e.dy;
   const float t_b = (s.b * e.dx) * e.dy;
   const float sigma = (t_a + t_c) + t_b;
-  if (!(sigma >= 0.0f && sigma < kSigmaSkip)) return false;
-  const float g_fast = __builtin_amdgcn_exp2f(sigma * -1.44269504088896341f);
-  const float og_fast = s.o * g_fast;
+  if (!(sigma >= 0.0f && sigma <= s.lr)) return false;  // sigma < 0, or a certain alpha reject (see lr)
   if (kExactValues) {
-    if (og_fast < kAlphaMinCertain) return false;
     e.G = exp_rn(-sigma, tab);
   } else {
+    const float g_fast = __builtin_amdgcn_exp2f(sigma * -1.44269504088896341f);
+    const float og_fast = s.o * g_fast;
     if (og_fast < kAlphaMinLo) return false;
     const bool near = og_fast < kAlphaMinHi || (og_fast > kAlphaMaxLo && og_fast < kAlphaMaxHi);
     e.G = near ? exp_rn(-sigma, tab) : g_fast;
