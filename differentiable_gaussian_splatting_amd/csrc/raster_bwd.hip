@@ -186,11 +186,12 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
           break;
         }
         const StagedSplat& s = s_sp[j];
+        Eval e;
+        const bool contrib = rel0 + j < last && evaluate<false>(s, cx, cy, e, s_exp2);
+        if (kSkip && __ballot(contrib) == 0) continue;  // no lane composited this splat
         float d[kGrads];
 #pragma unroll
         for (uint32_t q = 0; q < kGrads; ++q) d[q] = 0.0f;
-        Eval e;
-        const bool contrib = rel0 + j < last && evaluate<false>(s, cx, cy, e, s_exp2);
         if (contrib) {
           const float one_m = 1.0f - e.alpha;
           const float wgt = e.alpha * T;
@@ -198,47 +199,62 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
           d[6] = wgt * gg;
           d[7] = wgt * gb;
           const float mr = s.r * wgt, mg = s.g * wgt, mb = s.bl * wgt;
-          // dL/dalpha = T (g . rgb) - (g . after) / (1 - alpha), after = C_final - acc - mine
+          // dL/dalpha = T (g . rgb) - (g . after) / (1 - alpha), after = C_final - acc - mine, per channel as
+          // (C_final - acc) - mine: after is a difference of nearly equal values that 1 / (1 - alpha) amplifies, so
+          // its rounding follows that of the plain per-channel evaluation
           const float g_rgb = __fmaf_rn(gb, s.bl, __fmaf_rn(gg, s.g, gr * s.r));
           const float g_after = __fmaf_rn(gb, (Cb - ab) - mb, __fmaf_rn(gg, (Cg - ag) - mg, gr * ((Cr - ar) - mr)));
           const float dl_da = __fmaf_rn(T, g_rgb, -g_after * __builtin_amdgcn_rcpf(one_m));
-          // alpha depends on o and sigma only below the clamp: the opacity and geometry terms get a 0 / 1 factor
-          const float dl_da_u = (e.oG < kAlphaMax) ? dl_da : 0.0f;
-          d[8] = dl_da_u * e.G;
-          // u = -dL/dsigma: d mean = u (a dx + b dy, b dx + c dy), held halved (formed from a / 2, b / 2, c / 2:
-          // exactly half); the conic slots hold u dx dx, u dx dy, u dy dy. The factors 2 and -1/2, -1, -1/2 are
-          // applied once per splat when the tile's sums are flushed.
-          const float u = dl_da_u * e.oG;
-          const float ux = u * e.dx, uy = u * e.dy;
-          d[0] = __fmaf_rn(s.ha, ux, s.hb * uy);
-          d[1] = __fmaf_rn(s.hb, ux, s.hc * uy);
-          d[2] = ux * e.dx;
-          d[3] = ux * e.dy;
-          d[4] = uy * e.dy;
+          // alpha depends on o and sigma only below the clamp: the opacity and geometry terms get a 0 / 1 factor.
+          // v = dL/do = dL/dalpha G. With u = -dL/dsigma = o v, the mean gradient is u (a dx + b dy, b dx + c dy)
+          // and the conic's is -u (dx dx / 2, dx dy, dy dy / 2); o, a, b, c are the splat's, so the sums taken are
+          // those of v dx, v dy, v dx dx, v dx dy, v dy dy, and the splat's factors are applied once per splat when
+          // the tile's sums are flushed.
+          const float v = (e.oG < kAlphaMax) ? dl_da * e.G : 0.0f;
+          const float vx = v * e.dx, vy = v * e.dy;
+          d[0] = vx;
+          d[1] = vy;
+          d[2] = vx * e.dx;
+          d[3] = vx * e.dy;
+          d[4] = vy * e.dy;
+          d[8] = v;
           ar = ar + mr;
           ag = ag + mg;
           ab = ab + mb;
           T = T * one_m;
         }
-        if (kSkip && __ballot(contrib) == 0) continue;  // no lane composited this splat
         // Wave totals of the 9 terms; nine lanes add them to the LDS accumulator (distinct addresses).
         const float x = transpose_reduce(d, lane);
         if (my_slot >= 0) atomicAdd(&s_acc[j][my_slot], x);
       }
     }
     lds_barrier();
+    // Per staged splat, its geometry sums S0..S4 (of v dx, v dy, v dx dx, v dx dy, v dy dy) become
+    // dL/dmean = o (a S0 + b S1, b S0 + c S1), formed as 2 o (ha S0 + hb S1, hb S0 + hc S1), and
+    // dL/d(a, b, c) = -o (S2 / 2, S3, S4 / 2). A splat no pixel composited keeps its zeros whatever its values.
+    const uint32_t staged = min(kTilePixels, stop - b0);
+    if (tid < staged) {
+      float* acc = s_acc[tid];
+      const float s0 = acc[0], s1 = acc[1], s2 = acc[2], s3 = acc[3], s4 = acc[4];
+      if (s0 != 0.0f || s1 != 0.0f || s2 != 0.0f || s3 != 0.0f || s4 != 0.0f) {
+        const StagedSplat& sp = s_sp[tid];
+        const float o2 = sp.o + sp.o;
+        acc[0] = o2 * __fmaf_rn(sp.ha, s0, sp.hb * s1);
+        acc[1] = o2 * __fmaf_rn(sp.hb, s0, sp.hc * s1);
+        acc[2] = (-0.5f * sp.o) * s2;
+        acc[3] = -sp.o * s3;
+        acc[4] = (-0.5f * sp.o) * s4;
+      }
+    }
+    lds_barrier();
     // Flush: the batch's accumulator is read in its [slot][value] order, so the 64 lanes of an atomic instruction
     // add to the consecutive values of about seven splats (a few cache lines) rather than to 64 scattered records.
-    // The mean slots' sums double to dL/dmean; the conic slots' sums of u dx dx, u dx dy, u dy dy scale to dL/da,
-    // dL/db, dL/dc.
-    const uint32_t staged = min(kTilePixels, stop - b0);
     for (uint32_t f = tid; f < staged * kGrads; f += kTilePixels) {
       const uint32_t slot = f / kGrads, q = f - slot * kGrads;
-      float v = (&s_acc[0][0])[f];
+      const float g = (&s_acc[0][0])[f];
       (&s_acc[0][0])[f] = 0.0f;
-      v = q < 2 ? v + v : q == 2 || q == 4 ? -0.5f * v : q == 3 ? -v : v;
       const uint32_t idx = s_sp[slot].idx;
-      if (idx != 0xFFFFFFFFu && (!kSkip || v != 0.0f)) atomicAdd(splats_grad + size_t(idx) * kGrads + q, v);
+      if (idx != 0xFFFFFFFFu && (!kSkip || g != 0.0f)) atomicAdd(splats_grad + size_t(idx) * kGrads + q, g);
     }
     lds_barrier();
   }
