@@ -186,43 +186,42 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
           break;
         }
         const StagedSplat& s = s_sp[j];
-        Eval e;
-        const bool contrib = rel0 + j < last && evaluate<false>(s, cx, cy, e, s_exp2);
+        Eval e;  // dx and dy are set in every lane; G, oG and alpha only where the evaluation passed
+        const bool contrib = evaluate<false>(s, cx, cy, e, s_exp2) && rel0 + j < last;
         if (kSkip && __ballot(contrib) == 0) continue;  // no lane composited this splat
+        // Every lane forms the terms; in a lane that did not composite the splat, alpha = 0 and v = 0 make them
+        // +-0 and leave T and acc as they are (the splat is binned, so its values are finite).
         float d[kGrads];
-#pragma unroll
-        for (uint32_t q = 0; q < kGrads; ++q) d[q] = 0.0f;
-        if (contrib) {
-          const float one_m = 1.0f - e.alpha;
-          const float wgt = e.alpha * T;
-          d[5] = wgt * gr;
-          d[6] = wgt * gg;
-          d[7] = wgt * gb;
-          const float mr = s.r * wgt, mg = s.g * wgt, mb = s.bl * wgt;
-          // dL/dalpha = T (g . rgb) - (g . after) / (1 - alpha), after = C_final - acc - mine, per channel as
-          // (C_final - acc) - mine: after is a difference of nearly equal values that 1 / (1 - alpha) amplifies, so
-          // its rounding follows that of the plain per-channel evaluation
-          const float g_rgb = __fmaf_rn(gb, s.bl, __fmaf_rn(gg, s.g, gr * s.r));
-          const float g_after = __fmaf_rn(gb, (Cb - ab) - mb, __fmaf_rn(gg, (Cg - ag) - mg, gr * ((Cr - ar) - mr)));
-          const float dl_da = __fmaf_rn(T, g_rgb, -g_after * __builtin_amdgcn_rcpf(one_m));
-          // alpha depends on o and sigma only below the clamp: the opacity and geometry terms get a 0 / 1 factor.
-          // v = dL/do = dL/dalpha G. With u = -dL/dsigma = o v, the mean gradient is u (a dx + b dy, b dx + c dy)
-          // and the conic's is -u (dx dx / 2, dx dy, dy dy / 2); o, a, b, c are the splat's, so the sums taken are
-          // those of v dx, v dy, v dx dx, v dx dy, v dy dy, and the splat's factors are applied once per splat when
-          // the tile's sums are flushed.
-          const float v = (e.oG < kAlphaMax) ? dl_da * e.G : 0.0f;
-          const float vx = v * e.dx, vy = v * e.dy;
-          d[0] = vx;
-          d[1] = vy;
-          d[2] = vx * e.dx;
-          d[3] = vx * e.dy;
-          d[4] = vy * e.dy;
-          d[8] = v;
-          ar = ar + mr;
-          ag = ag + mg;
-          ab = ab + mb;
-          T = T * one_m;
-        }
+        const float alpha = contrib ? e.alpha : 0.0f;
+        const float one_m = 1.0f - alpha;
+        const float wgt = alpha * T;
+        d[5] = contrib ? wgt * gr : 0.0f;  // exact zeros also where the upstream gradient is not finite
+        d[6] = contrib ? wgt * gg : 0.0f;
+        d[7] = contrib ? wgt * gb : 0.0f;
+        const float mr = s.r * wgt, mg = s.g * wgt, mb = s.bl * wgt;
+        // dL/dalpha = T (g . rgb) - (g . after) / (1 - alpha), after = C_final - acc - mine, per channel as
+        // (C_final - acc) - mine: after is a difference of nearly equal values that 1 / (1 - alpha) amplifies, so
+        // its rounding follows that of the plain per-channel evaluation
+        const float g_rgb = __fmaf_rn(gb, s.bl, __fmaf_rn(gg, s.g, gr * s.r));
+        const float g_after = __fmaf_rn(gb, (Cb - ab) - mb, __fmaf_rn(gg, (Cg - ag) - mg, gr * ((Cr - ar) - mr)));
+        const float dl_da = __fmaf_rn(T, g_rgb, -g_after * __builtin_amdgcn_rcpf(one_m));
+        // alpha depends on o and sigma only below the clamp: the opacity and geometry terms get a 0 / 1 factor.
+        // v = dL/do = dL/dalpha G. With u = -dL/dsigma = o v, the mean gradient is u (a dx + b dy, b dx + c dy)
+        // and the conic's is -u (dx dx / 2, dx dy, dy dy / 2); o, a, b, c are the splat's, so the sums taken are
+        // those of v dx, v dy, v dx dx, v dx dy, v dy dy, and the splat's factors are applied once per splat when
+        // the tile's sums are flushed.
+        const float v = (contrib && e.oG < kAlphaMax) ? dl_da * e.G : 0.0f;
+        const float vx = v * e.dx, vy = v * e.dy;
+        d[0] = vx;
+        d[1] = vy;
+        d[2] = vx * e.dx;
+        d[3] = vx * e.dy;
+        d[4] = vy * e.dy;
+        d[8] = v;
+        ar = ar + mr;
+        ag = ag + mg;
+        ab = ab + mb;
+        T = T * one_m;
         // Wave totals of the 9 terms; nine lanes add them to the LDS accumulator (distinct addresses).
         const float x = transpose_reduce(d, lane);
         if (my_slot >= 0) atomicAdd(&s_acc[j][my_slot], x);
