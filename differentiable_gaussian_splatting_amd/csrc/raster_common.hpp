@@ -75,6 +75,49 @@ __host__ __device__ __forceinline__ float exp_rn(float x, const double* tab) {
   return float(ldexp(hi + fma(hi, q, lo), ki >> 5));
 }
 
+// The forward's form of exp_rn: e^-s for s in [0, 5.70] with `tab` holding kExpTabN pairs (hi, lo), entry k being
+// 2^(-k/32): kExp2Tab's pair for the residue of -k scaled by 2^floor(-k/32), which is exact. With k = round(32 s /
+// ln 2) the table entry already carries the power of two, so no ldexp or index masking follows the series. Every
+// step equals exp_rn's for x = -s (the same reduction, series and roundings, the scaling moved into the table),
+// so the result is bit-identical to exp_rn(-s) - the host test checks both exhaustively. Beyond s = 5.70 the
+// last entry is used (a wrong value, never a read out of range); the kernels evaluate it for s <= ln(255 o)
+// plus a margin, below 5.55 for o <= 1.
+constexpr uint32_t kExpTabN = 264;
+
+__host__ __device__ __forceinline__ void exp_neg_entry(uint32_t kp, double* hi_lo) {
+  const int k = -int(kp);
+  hi_lo[0] = ldexp(kExp2Tab[2 * (k & 31)], k >> 5);
+  hi_lo[1] = ldexp(kExp2Tab[2 * (k & 31) + 1], k >> 5);
+}
+
+// fma(a, b, c) for a wave-uniform constant c, taken from scalar registers: the compiler's own choice, the tied
+// v_fmac form, would copy the constant into the destination register before every use.
+__host__ __device__ __forceinline__ double fma_uniform_c(double a, double b, double c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  double d;
+  asm("v_fma_f64 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "s"(c));
+  return d;
+#else
+  return fma(a, b, c);
+#endif
+}
+
+__host__ __device__ __forceinline__ float exp_neg_rn(float s, const double* tab) {
+  const double sd = double(s);
+  const double k = rint(sd * 46.166241308446828384);  // 32 / ln 2
+  double r = fma(k, 0x1.62e42fee00000p-6, -sd);
+  r = fma(k, 0x1.a39ef35793c76p-38, r);
+  const double r2 = r * r;
+  double q = fma_uniform_c(r, 1.0 / 720.0, 1.0 / 120.0);
+  q = fma_uniform_c(q, r, 1.0 / 24.0);
+  q = fma_uniform_c(q, r, 1.0 / 6.0);
+  q = fma(q, r, 0.5);
+  q = fma(q, r2, r);  // e^r - 1
+  const uint32_t ki = uint32_t(fmin(k, double(kExpTabN - 1)));
+  const double hi = tab[2 * ki], lo = tab[2 * ki + 1];
+  return float(hi + fma(hi, q, lo));
+}
+
 // One splat as staged in LDS for a batch: 48 bytes, read by every lane of a wavefront at the same address. The
 // conic is kept as a / 2 and c / 2 (what sigma uses) beside b and b / 2; a and c are ha + ha and hc + hc, exactly.
 // lr bounds sigma: alpha <= o e^-sigma < 1/255 wherever sigma > lr, so those evaluations are certain rejects.
@@ -168,6 +211,11 @@ __device__ __forceinline__ void load_exp_table(double* s_tab) {
   if (threadIdx.x < 64) s_tab[threadIdx.x] = kExp2Tab[threadIdx.x];
 }
 
+// Fills the workgroup's LDS table of exp_neg_rn (kExpTabN pairs); a barrier must follow before its first use.
+__device__ __forceinline__ void load_exp_neg_table(double* s_tab) {
+  for (uint32_t k = threadIdx.x; k < kExpTabN; k += blockDim.x) exp_neg_entry(k, s_tab + 2 * k);
+}
+
 // Wave-uniform 64-bit value held in scalar registers.
 __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
@@ -186,9 +234,10 @@ struct Eval {
 // rejected before any exponential: their alpha is below 1/255 by a margin no rounding can close. This contains the
 // pages' sigma >= 5.55 skip (lr < 5.55 for o <= 1) and is exact for any o.
 //
-// kExactValues = true (forward): every splat that passes is evaluated with the correctly rounded G, so alpha and the
-// transmittance chain are exactly those of a plain fp32 evaluation - the stop test T' < 1e-4 depends on them.
-// kExactValues = false (backward): the decisions must still be exact (reject or composite, clamped or not), but the
+// kExactValues = true (forward, `tab` = the exp_neg_rn table): every splat that passes is evaluated with the correctly
+// rounded G, so alpha and the transmittance chain are exactly those of a plain fp32 evaluation - the stop test
+// T' < 1e-4 depends on them.
+// kExactValues = false (backward, `tab` = kExp2Tab): the decisions must still be exact (reject or composite, clamped or not), but the
 // values only feed gradient terms. G comes from the hardware exp2 (relative error below 5.2e-7 for sigma < 5.55) and
 // the fp64 value is computed only when o G lies within 2^-18 (relative) of 1/255 or of 0.999, where the fast value
 // could fall on the other side of a threshold.
@@ -206,7 +255,7 @@ __device__ __forceinline__ bool evaluate(const StagedSplat& s, float cx, float c
   const float sigma = (t_a + t_c) + t_b;
   if (!(sigma >= 0.0f && sigma <= s.lr)) return false;  // sigma < 0, or a certain alpha reject (see lr)
   if (kExactValues) {
-    e.G = exp_rn(-sigma, tab);
+    e.G = exp_neg_rn(sigma, tab);
   } else {
     const float g_fast = __builtin_amdgcn_exp2f(sigma * -1.44269504088896341f);
     const float og_fast = s.o * g_fast;

@@ -26,12 +26,12 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
                                                          uint32_t* __restrict__ tile_cost) {
   constexpr uint32_t kWaves = kTilePixels / kWave;
   __shared__ StagedSplat s_sp[kTilePixels];
-  __shared__ double s_exp2[64];  // 2^(j/32) table of the exact exponential
+  __shared__ double s_exp2[2 * kExpTabN];  // 2^(-k/32) table of the exact exponential
   __shared__ uint64_t s_mask[kWaves][kWaves];  // [reading wave][staging wave]: slots that can reach the reader
   const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const uint32_t tile = tile_order[blockIdx.x];  // slowest expected first (a permutation of the tiles)
   if (tile >= num_tiles) return;                 // not reachable with a permutation; keeps reads in bounds
-  load_exp_table(s_exp2);                        // the first batch barrier orders it
+  load_exp_neg_table(s_exp2);                    // the first batch barrier orders it
   const uint32_t tx0 = (tile % tiles_x) * kTile, ty0 = (tile / tiles_x) * kTile;
   const uint32_t px = tx0 + lane_px(w, lane), py = ty0 + lane_py(w, lane);
   const bool inside = px < width && py < height;

@@ -1,4 +1,4 @@
-"""The raster kernels' exact exponential, built for the host from the kernels' own header, against the oracle's
+"""The raster kernels' exact exponentials (exp_rn, and the forward's exp_neg_rn of the negated argument), built for the host from the kernels' own header, against the oracle's
 definition of the fp32 e^x, float(exp(double(x))), over every float argument the kernels evaluate (x in [-5.55, 0],
 about 1.09e9 floats): every decision that depends on exp(-sigma) is then the same on both sides.
 
@@ -44,6 +44,7 @@ def test_exact_exponential_is_correctly_rounded_on_every_argument(tmp_path):
                     "-o", str(exe)], check=True, capture_output=True)
     threads = str(min(16, os.cpu_count() or 1))
     out = subprocess.run([str(exe), threads], check=True, capture_output=True, text=True).stdout.split()
-    total, bad = int(out[0]), int(out[1])
+    total, bad, bad_neg = int(out[0]), int(out[1]), int(out[2])
     assert total == 1_085_381_019
     assert bad == 0
+    assert bad_neg == 0
