@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void k_total(const uint64_t* __restrict__
   if (threadIdx.x == 0) *total = all;
 }
 
-// Three-launch exclusive scan of uint32 counts into uint64 offsets; offsets[n] = total. With `order`, position j
+// Two-launch exclusive scan of uint32 counts into uint64 offsets; offsets[n] = total. With `order`, position j
 // takes counts[order[j]] (order must be a permutation of 0..n-1; other entries count 0).
 __device__ __forceinline__ uint32_t count_at(const uint32_t* __restrict__ counts, const uint32_t* __restrict__ order,
                                              uint32_t n, uint64_t j) {
@@ -144,12 +144,35 @@ __device__ __forceinline__ uint32_t count_at(const uint32_t* __restrict__ counts
   return i < n ? counts[i] : 0u;
 }
 
-// With `ordered`, the gathered counts are also stored in emission order for the down-sweep.
+// Exclusive scan of part[0..nb) in place by one workgroup (reading the entries with atomics: see
+// count_done_after); part[nb] and offsets[n] receive the total.
+__device__ __forceinline__ void scan_parts(uint64_t* __restrict__ part, uint32_t nb, uint64_t* __restrict__ offsets,
+                                           uint32_t n, uint64_t* smem) {
+  uint64_t carry = 0;
+  for (uint32_t c = 0; c < nb; c += kThreads) {
+    const uint32_t j = c + threadIdx.x;
+    const uint64_t v = j < nb ? atomicAdd(reinterpret_cast<unsigned long long*>(part + j), 0ull) : 0;
+    uint64_t total;
+    const uint64_t ex = block_exclusive_scan<uint64_t, kThreads>(v, &total, smem);
+    if (j < nb) part[j] = carry + ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) {
+    part[nb] = carry;
+    offsets[n] = carry;
+  }
+}
+
+// With `ordered`, the gathered counts are also stored in emission order for the down-sweep. Block sums are
+// published with atomic exchanges; the block that finishes last reads them back with atomics, turns part[0..nb)
+// into its exclusive scan and writes the total to part[nb] and offsets[n].
 __global__ __launch_bounds__(kThreads) void k_scan_reduce(const uint32_t* __restrict__ counts,
                                                           const uint32_t* __restrict__ order, uint32_t n,
                                                           uint64_t* __restrict__ part,
-                                                          uint32_t* __restrict__ ordered) {
+                                                          uint32_t* __restrict__ ordered, uint32_t* done,
+                                                          uint32_t* done_alias, uint64_t* __restrict__ offsets) {
   __shared__ uint64_t smem[kThreads / kWave];
+  __shared__ uint32_t s_last;
   const uint64_t base = uint64_t(blockIdx.x) * kScanBlock;
   uint64_t sum = 0;
   uint32_t c[kScanItems];
@@ -166,25 +189,13 @@ __global__ __launch_bounds__(kThreads) void k_scan_reduce(const uint32_t* __rest
   }
   uint64_t total;
   block_exclusive_scan<uint64_t, kThreads>(sum, &total, smem);
-  if (threadIdx.x == 0) part[blockIdx.x] = total;
-}
-
-__global__ __launch_bounds__(kThreads) void k_scan_top(uint64_t* __restrict__ part, uint32_t nb,
-                                                       uint64_t* __restrict__ offsets, uint32_t n) {
-  __shared__ uint64_t smem[kThreads / kWave];
-  uint64_t carry = 0;
-  for (uint32_t c = 0; c < nb; c += kThreads) {
-    const uint32_t j = c + threadIdx.x;
-    const uint64_t v = j < nb ? part[j] : 0;
-    uint64_t total;
-    const uint64_t ex = block_exclusive_scan<uint64_t, kThreads>(v, &total, smem);
-    if (j < nb) part[j] = carry + ex;
-    carry += total;
-  }
   if (threadIdx.x == 0) {
-    part[nb] = carry;
-    offsets[n] = carry;
+    const uint64_t before = atomicExch(reinterpret_cast<unsigned long long*>(part + blockIdx.x), total);
+    s_last = count_done_after(before, done, done_alias, gridDim.x) ? 1u : 0u;
   }
+  __syncthreads();
+  if (!s_last) return;
+  scan_parts(part, gridDim.x, offsets, n, smem);
 }
 
 __global__ __launch_bounds__(kThreads) void k_scan_down(const uint32_t* __restrict__ counts,
@@ -261,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void k_emit(const uint4* __restrict__ rec
                                                    uint32_t n, const uint32_t* __restrict__ order, uint32_t tiles_x,
                                                    const uint64_t* __restrict__ offsets, uint64_t num_pairs,
                                                    K* __restrict__ keys, uint32_t* __restrict__ vals) {
-  constexpr uint32_t kPer = 4, kChunk = kPer * kThreads;
+  constexpr uint32_t kPer = 4, kChunk = kPer * kThreads;  // kPer = 4: one 16-byte vector of values per thread
   __shared__ uint64_t s_off[kThreads + 1];
   __shared__ uint32_t s_tx0[kThreads], s_ty0[kThreads], s_w[kThreads], s_idx[kThreads], s_dbits[kThreads];
   __shared__ uint32_t s_mark[kChunk];
@@ -301,22 +312,43 @@ __global__ __launch_bounds__(kThreads) void k_emit(const uint4* __restrict__ rec
     }
     uint32_t chunk_max;
     const uint32_t before = block_exclusive_max<kThreads>(run, carry, &chunk_max, smem);
+    // the thread's kPer consecutive pairs; written as 16-byte vectors when all of them exist (p0 is a multiple of
+    // kPer, so the vectors are aligned), element by element at the ends of the range
+    const uint64_t p0 = c0 + kPer * tid;
+    K kk[kPer];
+    uint32_t vv[kPer];
+    bool ok[kPer];
 #pragma unroll
     for (uint32_t e = 0; e < kPer; ++e) {
-      const uint64_t p = c0 + kPer * tid + e;
+      const uint64_t p = p0 + e;
       const uint32_t owner = max(before, m[e]);  // >= 1 for every pair below end
-      if (p < end && owner > 0) {
-        const uint32_t q = owner - 1;
-        const uint32_t k = uint32_t(p - s_off[q]);
-        const uint32_t w = s_w[q];
-        const uint32_t row = div_small(k, w);
-        const uint64_t tile = uint64_t(s_ty0[q] + row) * tiles_x + (s_tx0[q] + (k - row * w));
-        if constexpr (sizeof(K) == 8)
-          keys[p] = (tile << 32) | s_dbits[q];
-        else
-          keys[p] = K(tile);
-        vals[p] = s_idx[q];
+      ok[e] = p < end && owner > 0;
+      const uint32_t q = owner > 0 ? owner - 1 : 0;
+      const uint32_t k = uint32_t(p - s_off[q]);
+      const uint32_t w = s_w[q];
+      const uint32_t row = div_small(k, w);
+      const uint64_t tile = uint64_t(s_ty0[q] + row) * tiles_x + (s_tx0[q] + (k - row * w));
+      if constexpr (sizeof(K) == 8)
+        kk[e] = (tile << 32) | s_dbits[q];
+      else
+        kk[e] = K(tile);
+      vv[e] = s_idx[q];
+    }
+    if (ok[0] && ok[1] && ok[2] && ok[3]) {
+      if constexpr (sizeof(K) == 8) {
+        reinterpret_cast<ulonglong2*>(keys + p0)[0] = make_ulonglong2(kk[0], kk[1]);
+        reinterpret_cast<ulonglong2*>(keys + p0)[1] = make_ulonglong2(kk[2], kk[3]);
+      } else {
+        *reinterpret_cast<uint4*>(keys + p0) = make_uint4(kk[0], kk[1], kk[2], kk[3]);
       }
+      *reinterpret_cast<uint4*>(vals + p0) = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+    } else {
+#pragma unroll
+      for (uint32_t e = 0; e < kPer; ++e)
+        if (ok[e]) {
+          keys[p0 + e] = kk[e];
+          vals[p0 + e] = vv[e];
+        }
     }
     carry = chunk_max;
   }
@@ -557,8 +589,8 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   if (n) {
     // the presort scheme gathers its counts once, into the depth sort's (now free) value scratch
     uint32_t* ordered = order ? static_cast<uint32_t*>(a.order_vals_alt.ptr) : nullptr;
-    hipLaunchKernelGGL(k_scan_reduce, dim3(nb_scan), dim3(kThreads), 0, s, counts, order, n, part, ordered);
-    hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(kThreads), 0, s, part, nb_scan, offsets, n);
+    hipLaunchKernelGGL(k_scan_reduce, dim3(nb_scan), dim3(kThreads), 0, s, counts, order, n, part, ordered,
+                       a.done, a.done, offsets);
     hipLaunchKernelGGL(k_scan_down, dim3(nb_scan), dim3(kThreads), 0, s, order ? ordered : counts,
                        static_cast<const uint32_t*>(nullptr), n, part, offsets);
   }

@@ -90,15 +90,20 @@ gsr_status gsr_create(gsr_ctx** out, int hip_device) {
     delete ctx;
     return GSR_EHIP;
   }
-  e = hipHostMalloc(reinterpret_cast<void**>(&ctx->arena.host_total), sizeof(uint64_t), hipHostMallocDefault);
+  Arena& a = ctx->arena;
+  e = hipHostMalloc(reinterpret_cast<void**>(&a.host_total), sizeof(uint64_t), hipHostMallocDefault);
   if (e != hipSuccess) {
     delete ctx;
     return GSR_ENOMEM;
   }
-  *ctx->arena.host_total = 0;
-  e = hipEventCreateWithFlags(&ctx->arena.total_ready, hipEventDisableTiming);
+  *a.host_total = 0;
+  // the count scan's last-block-done counter, zero between launches
+  e = hipMalloc(reinterpret_cast<void**>(&a.done), sizeof(uint32_t));
+  if (e == hipSuccess) e = hipMemset(a.done, 0, sizeof(uint32_t));
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&a.total_ready, hipEventDisableTiming);
   if (e != hipSuccess) {
-    (void)hipHostFree(ctx->arena.host_total);
+    if (a.done) (void)hipFree(a.done);
+    (void)hipHostFree(a.host_total);
     delete ctx;
     return GSR_EHIP;
   }
@@ -115,6 +120,7 @@ void gsr_destroy(gsr_ctx* ctx) {
                     &a.tile_order_ext, &a.tile_cost})
     release(*b);
   if (a.host_total) (void)hipHostFree(a.host_total);
+  if (a.done) (void)hipFree(a.done);
   if (a.total_ready) (void)hipEventDestroy(a.total_ready);
   delete ctx;
 }

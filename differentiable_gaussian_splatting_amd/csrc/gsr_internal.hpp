@@ -42,6 +42,7 @@ struct Arena {
   DevBuf tile_order_ext;  // uint32 [tiles] raster launch order: the slowest expected tiles first
   DevBuf tile_cost;   // uint32 [4 tiles] splats each wavefront of the last forward walked (launch-order hint)
   uint64_t* host_total = nullptr;  // pinned host word for the one pair-count readback
+  uint32_t* done = nullptr;        // last-block-done counter of the count scan (0 between launches)
   hipEvent_t total_ready = nullptr;  // recorded after the readback is queued
 };
 

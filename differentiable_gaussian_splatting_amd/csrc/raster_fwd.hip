@@ -67,7 +67,14 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
       while (m) {
         const uint32_t j = sw * kWave + uint32_t(__builtin_ctzll(m));
         m &= m - 1;
-        const StagedSplat& s = s_sp[j];
+        // the whole record in three 16-byte reads from one address register (the loop reads every field of it
+        // in some branch; read lazily each branch would need its own address)
+        const float4* rec = reinterpret_cast<const float4*>(&s_sp[j]);
+        const float4 q0 = rec[0], q1 = rec[1], q2 = rec[2];
+        StagedSplat s;
+        s.x = q0.x, s.y = q0.y, s.ha = q0.z, s.b = q0.w;
+        s.hc = q1.x, s.o = q1.y, s.r = q1.z, s.g = q1.w;
+        s.bl = q2.x, s.lr = q2.y, s.hb = q2.z, s.idx = __float_as_uint(q2.w);
         ++walked;
         Eval e;
         if (evaluate<true>(s, cxe, cy, e, s_exp2)) {

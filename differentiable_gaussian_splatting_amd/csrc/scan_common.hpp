@@ -31,4 +31,20 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T* total, T* smem) {
   return before + x - v;
 }
 
+// Last-block-done without fences. Thread 0 of each of the nb blocks of a grid publishes its block's result with a
+// device-scope atomic (an add or an exchange) and passes that atomic's return value here as `dep`. The count of
+// finished blocks is then incremented at an address computed from `dep` (always `done`: `done_alias` is the same
+// counter passed as a second argument, so the compiler cannot drop the choice), so the increment is issued only once
+// the publishing atomic has returned, that is, has been performed where every block's atomics meet. Returns true
+// for the block that counts last; it must read the published values with atomics (read-modify-write of 0), which
+// then see every block's, and it returns the counter to 0 for the next launch. Device-scope fences would order the
+// same accesses but write back the whole L2 of the issuing die in every block. No block waits for another.
+__device__ __forceinline__ bool count_done_after(uint64_t dep, uint32_t* done, uint32_t* done_alias, uint32_t nb) {
+  uint32_t* d = dep == ~uint64_t(0) ? done_alias : done;
+  const uint32_t prev = atomicAdd(d, 1u);
+  const bool last = prev == nb - 1;
+  if (last) atomicExch(done, 0u);
+  return last;
+}
+
 }  // namespace gsr
