@@ -11,6 +11,8 @@
 // which complete while the next batch is processed (the loop's barriers order LDS only).
 // The per-pixel terms follow the forward-order form after = C_final - acc - mine of the M3 per-splat backward page
 // (section 1, rows "brush's actual structure" and "differences").
+#include <type_traits>
+
 #include "gsr_internal.hpp"
 #include "raster_common.hpp"
 
@@ -147,6 +149,10 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
     gg = g.y;
     gb = g.z;
   }
+  // A lane that does not composite a splat has wgt = 0, so its colour terms wgt g are exact zeros unless its
+  // upstream gradient g is not finite; waves holding such a pixel select the zeros explicitly.
+  const bool g_finite = __builtin_isfinite(gr) && __builtin_isfinite(gg) && __builtin_isfinite(gb);
+  const bool wave_g_finite = __builtin_amdgcn_readfirstlane(uint32_t(__ballot(!g_finite) == 0)) != 0;
   if (tid == 0) s_max_last = 0;
 #pragma unroll
   for (uint32_t q = 0; q < kGrads; ++q) s_acc[tid][q] = 0.0f;
@@ -159,6 +165,10 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
   __syncthreads();
   const uint32_t stop = start + s_max_last;
 
+  // The batch loop, instantiated twice: kGuard selects the colour terms' explicit zeros (waves with a non-finite
+  // upstream gradient). Waves of one workgroup may run different instantiations; both pass the same barriers.
+  auto batches = [&](auto guard) {
+  constexpr bool kGuard = decltype(guard)::value;
   float T = 1.0f, ar = 0.0f, ag = 0.0f, ab = 0.0f;
   for (uint32_t b0 = start; b0 < stop; b0 += kTilePixels) {
     const uint32_t k = b0 + tid;
@@ -185,7 +195,13 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
           sw = kWaves;  // past every lane's last contributor: done with this batch and the tile
           break;
         }
-        const StagedSplat& s = s_sp[j];
+        // the whole record in three 16-byte reads from one address register
+        const float4* rec = reinterpret_cast<const float4*>(&s_sp[j]);
+        const float4 q0 = rec[0], q1 = rec[1], q2 = rec[2];
+        StagedSplat s;
+        s.x = q0.x, s.y = q0.y, s.ha = q0.z, s.b = q0.w;
+        s.hc = q1.x, s.o = q1.y, s.r = q1.z, s.g = q1.w;
+        s.bl = q2.x, s.lr = q2.y, s.hb = q2.z, s.idx = __float_as_uint(q2.w);
         Eval e;  // dx and dy are set in every lane; G, oG and alpha only where the evaluation passed
         const bool contrib = evaluate<false>(s, cx, cy, e, s_exp2) && rel0 + j < last;
         if (kSkip && __ballot(contrib) == 0) continue;  // no lane composited this splat
@@ -195,9 +211,14 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
         const float alpha = contrib ? e.alpha : 0.0f;
         const float one_m = 1.0f - alpha;
         const float wgt = alpha * T;
-        d[5] = contrib ? wgt * gr : 0.0f;  // exact zeros also where the upstream gradient is not finite
-        d[6] = contrib ? wgt * gg : 0.0f;
-        d[7] = contrib ? wgt * gb : 0.0f;
+        d[5] = wgt * gr;
+        d[6] = wgt * gg;
+        d[7] = wgt * gb;
+        if constexpr (kGuard) {
+          d[5] = contrib ? d[5] : 0.0f;
+          d[6] = contrib ? d[6] : 0.0f;
+          d[7] = contrib ? d[7] : 0.0f;
+        }
         const float mr = s.r * wgt, mg = s.g * wgt, mb = s.bl * wgt;
         // dL/dalpha = T (g . rgb) - (g . after) / (1 - alpha), after = C_final - acc - mine, per channel as
         // (C_final - acc) - mine: after is a difference of nearly equal values that 1 / (1 - alpha) amplifies, so
@@ -257,6 +278,11 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
     }
     lds_barrier();
   }
+  };
+  if (wave_g_finite)
+    batches(std::false_type{});
+  else
+    batches(std::true_type{});
 }
 
 }  // namespace

@@ -145,6 +145,36 @@ def test_backward_ragged_images(ctx, w, h):
     assert ok, (worst, at)
 
 
+def test_backward_nan_upstream_gradient_stays_with_its_pixel(ctx):
+    """Pixels with a NaN upstream gradient give NaN terms to the splats they composite and nothing to the others:
+    the positions of NaN gradients equal the oracle's and every other gradient is within tolerance. (A wave that
+    holds such a pixel takes the kernel's guarded form of the colour terms.)"""
+    import oracle
+    from differentiable_gaussian_splatting_amd import gsr
+    w, h = 64, 48
+    banner(f"backward NaN upstream gradient {w}x{h}")
+    sc = custom_scene(name="nanv", width=w, height=h, n=600, seed=77,
+                      size_classes=((0.7, 0.3, 4.0), (0.3, 4.0, 20.0)), opacity_mu=0.5, vout_sd=0.1, margin=10.0)
+    v_out = sc.v_out.copy()
+    rng = np.random.default_rng(5)
+    for p in rng.choice(w * h, 6, replace=False):
+        v_out.reshape(-1, 4)[p, rng.integers(0, 3)] = np.nan
+    ob = oracle.bin(sc.splats, sc.depths, w, h)
+    r_out, r_ft, r_lc, _ = oracle.render_forward(sc.splats, ob, w, h)
+    ref = oracle.render_backward(sc.splats, ob, w, h, r_out, r_ft, r_lc, v_out)
+    sp = dev(sc.splats)
+    bins = gsr.gsr_bin(ctx, sp, dev(sc.depths), w, h)
+    out, ft, lc = run_forward(ctx, sp, bins, w, h)
+    g = host(run_backward(ctx, sc, bins, out, ft, lc, v_out))
+    nan_ref, nan_gpu = np.isnan(ref), np.isnan(g)
+    assert nan_ref.any(), "the case must put NaN into some gradients"
+    assert np.array_equal(nan_gpu, nan_ref), np.argwhere(nan_gpu != nan_ref)[:5].tolist()
+    assert not np.isinf(g).any() and not np.isinf(ref).any()
+    keep = ~nan_ref
+    ok, worst, at = grads_close(np.where(keep, g, 0), np.where(keep, ref, 0))
+    assert ok, (worst, at)
+
+
 def set_skip(ctx, on: bool):
     from differentiable_gaussian_splatting_amd import gsr
     gsr.gsr_set_option(ctx, gsr.GSR_OPT_RASTER_SKIP, 1 if on else 0)
