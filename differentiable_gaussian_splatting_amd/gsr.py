@@ -40,6 +40,19 @@ class gsr_adam_group(ctypes.Structure):
                 ("v", ctypes.c_void_p), ("count", ctypes.c_uint64), ("lr", ctypes.c_float)]
 
 
+class gsr_camera(ctypes.Structure):
+    _fields_ = [("R", ctypes.c_float * 9), ("tv", ctypes.c_float * 3), ("fx", ctypes.c_float),
+                ("fy", ctypes.c_float), ("cx", ctypes.c_float), ("cy", ctypes.c_float), ("near", ctypes.c_float)]
+
+
+def camera(R, tv, fx: float, fy: float, cx: float, cy: float, near: float = 0.01) -> gsr_camera:
+    """A gsr_camera from a 3x3 world-to-camera rotation R (any nested sequence or array), a translation tv and the
+    pinhole intrinsics."""
+    flat = [float(v) for row in R for v in row]
+    return gsr_camera((ctypes.c_float * 9)(*flat), (ctypes.c_float * 3)(*[float(v) for v in tv]), fx, fy, cx, cy,
+                      near)
+
+
 # Every symbol include/gsr.h declares, with its ctypes signature.
 _P, _U32, _U64, _I32, _I64, _F = (ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int32,
                                   ctypes.c_int64, ctypes.c_float)
@@ -56,6 +69,9 @@ SIGNATURES = {
     "gsr_render_forward": (_I32, [_P, _P, _P, _U32, ctypes.POINTER(gsr_bins), _U32, _U32, _P, _P, _P]),
     "gsr_render_backward": (_I32, [_P, _P, _P, _U32, ctypes.POINTER(gsr_bins), _U32, _U32, _P, _P, _P, _P, _P]),
     "gsr_adam_step": (_I32, [_P, _P, ctypes.POINTER(gsr_adam_group), _U32, _F, _F, _F, _F, _F]),
+    "gsr_project_forward": (_I32, [_P, _P, ctypes.POINTER(gsr_camera), _U32, _P, _P, _P, _P, _P, _P, _P]),
+    "gsr_project_backward": (_I32, [_P, _P, ctypes.POINTER(gsr_camera), _U32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    _P, _P]),
 }
 
 _lib = None
@@ -263,3 +279,48 @@ def gsr_adam_step(ctx: Context, groups, beta1: float, beta2: float, eps: float, 
         arr[q] = gsr_adam_group(_ptr(p), _ptr(g), _ptr(m), _ptr(v), k, lr)
     ctx.check(load().gsr_adam_step(ctx.handle, _stream(stream), arr, len(groups), beta1, beta2, eps, bc1, bc2),
               "gsr_adam_step")
+
+
+_PARAM_WIDTHS = (("means", 3), ("log_scales", 3), ("quats", 4), ("raw_opacities", 1), ("sh", 48))
+
+
+def _need_params(ctx: Context, params):
+    n = params[0].numel() // 3
+    for t, (name, k) in zip(params, _PARAM_WIDTHS):
+        _need(t, name, (torch.float32,), n * k, ctx.device)
+    return n
+
+
+def gsr_project_forward(ctx: Context, cam: gsr_camera, means, log_scales, quats, raw_opacities, sh,
+                        splats: torch.Tensor | None = None, depths: torch.Tensor | None = None, stream=None):
+    """Returns (splats float32 [N, 9], depths float32 [N]) of the Gaussians (float32 device tensors: means [N, 3],
+    log_scales [N, 3], quats [N, 4], raw_opacities [N], sh [N, 16, 3])."""
+    params = (means, log_scales, quats, raw_opacities, sh)
+    n = _need_params(ctx, params)
+    dev = ctx.device
+    if splats is None:
+        splats = torch.empty((n, 9), dtype=torch.float32, device=dev)
+    if depths is None:
+        depths = torch.empty(n, dtype=torch.float32, device=dev)
+    _need(splats, "splats", (torch.float32,), n * 9, dev)
+    _need(depths, "depths", (torch.float32,), n, dev)
+    ctx.check(load().gsr_project_forward(ctx.handle, _stream(stream), ctypes.byref(cam), n,
+                                         *[_ptr(t) for t in params], _ptr(splats), _ptr(depths)),
+              "gsr_project_forward")
+    return splats, depths
+
+
+def gsr_project_backward(ctx: Context, cam: gsr_camera, means, log_scales, quats, raw_opacities, sh,
+                         splats_grad: torch.Tensor, grads=None, stream=None):
+    """Returns the gradients (means, log_scales, quats, raw_opacities, sh), each shaped like its parameter."""
+    params = (means, log_scales, quats, raw_opacities, sh)
+    n = _need_params(ctx, params)
+    _need(splats_grad, "splats_grad", (torch.float32,), n * 9, ctx.device)
+    if grads is None:
+        grads = tuple(torch.empty_like(t) for t in params)
+    for t, g, (name, k) in zip(params, grads, _PARAM_WIDTHS):
+        _need(g, name + "_grad", (torch.float32,), n * k, ctx.device)
+    ctx.check(load().gsr_project_backward(ctx.handle, _stream(stream), ctypes.byref(cam), n,
+                                          *[_ptr(t) for t in params], _ptr(splats_grad), *[_ptr(g) for g in grads]),
+              "gsr_project_backward")
+    return grads

@@ -140,3 +140,108 @@ def adam_bias_corrections(beta1: float, beta2: float, step: int) -> tuple[float,
     """bc1 = 1 - beta1^t and bc2 = 1 - beta2^t in float64, rounded to float32 (host-side scalars of the step)."""
     return float(np.float32(1.0 - np.float64(np.float32(beta1)) ** step)), \
         float(np.float32(1.0 - np.float64(np.float32(beta2)) ** step))
+
+
+# ---------------------------------------------------------------------------------------------- 3D Gaussians
+@dataclass
+class GaussianSpec:
+    """3D Gaussians in front of a pinhole camera, drawn so that their projected sizes follow `size_classes`
+    (log-uniform, pixels) like the 2D workloads. Draw order (default_rng(seed)): depth z, pixel position, size class,
+    per-axis log-scale jitter, quaternion, raw opacity, SH coefficients, then the upstream record gradient."""
+    name: str
+    width: int
+    height: int
+    n: int
+    seed: int
+    size_classes: tuple = ((1.0, 0.5, 8.0),)
+    aniso_sd: float = 0.3        # log-scale jitter per axis around the class size
+    opacity_mu: float = 0.0      # raw opacity ~ N(opacity_mu, opacity_sd)
+    opacity_sd: float = 1.0
+    depth_lo: float = 2.0
+    depth_hi: float = 10.0
+    margin: float = 0.0          # pixel positions drawn over [-margin, W + margin) x [-margin, H + margin)
+    focal: float = 800.0
+    cam_axis: tuple = (0.0, 0.0, 1.0)
+    cam_angle: float = 0.0       # camera rotation about cam_axis, radians
+    cam_t: tuple = (0.0, 0.0, 0.0)
+    dc_sd: float = 1.0           # SH degree-0 coefficients ~ N(0, dc_sd)
+    sh_sd: float = 0.1           # higher SH coefficients ~ N(0, sh_sd)
+    grad_sd: float = 1e-2        # upstream dL/d(record) ~ N(0, grad_sd)
+    near_frac: float = 0.0       # fraction placed behind the near plane (culled)
+
+
+GAUSS_SPECS = {
+    "gauss_tiny": GaussianSpec("gauss_tiny", 64, 48, 300, seed=11, size_classes=((1.0, 0.5, 8.0),), margin=8.0,
+                               cam_axis=(0.3, -0.5, 0.8), cam_angle=0.4, cam_t=(0.2, -0.1, 0.5), near_frac=0.05),
+    "gauss_ragged": GaussianSpec("gauss_ragged", 100, 37, 1_000, seed=12, size_classes=((0.7, 0.3, 4.0),
+                                                                                         (0.3, 4.0, 40.0)),
+                                 margin=20.0, cam_axis=(1.0, 0.2, 0.0), cam_angle=-0.3, near_frac=0.02),
+    "gauss410k": GaussianSpec("gauss410k", 800, 800, 410_000, seed=13,
+                              size_classes=((0.7, 0.3, 4.0), (0.3, 4.0, 40.0)), opacity_mu=-2.0, opacity_sd=1.5),
+}
+
+
+@dataclass
+class GaussianScene:
+    spec: GaussianSpec
+    camera: dict            # R [3, 3], tv [3], fx, fy, cx, cy, near (float64 / float)
+    means: np.ndarray       # float32 [N, 3]
+    log_scales: np.ndarray  # float32 [N, 3]
+    quats: np.ndarray       # float32 [N, 4] (w, x, y, z), not normalised
+    raw_opacities: np.ndarray  # float32 [N]
+    sh: np.ndarray          # float32 [N, 16, 3]
+    splats_grad: np.ndarray  # float32 [N, 9] upstream gradient of the records
+
+    @property
+    def width(self):
+        return self.spec.width
+
+    @property
+    def height(self):
+        return self.spec.height
+
+
+def _axis_angle(axis, angle):
+    k = np.asarray(axis, np.float64)
+    k = k / np.linalg.norm(k)
+    K = np.array([[0, -k[2], k[1]], [k[2], 0, -k[0]], [-k[1], k[0], 0]])
+    return np.eye(3) + np.sin(angle) * K + (1 - np.cos(angle)) * (K @ K)
+
+
+def make_gaussians(spec: GaussianSpec | str, **overrides) -> GaussianScene:
+    if isinstance(spec, str):
+        spec = GAUSS_SPECS[spec]
+    if overrides:
+        spec = GaussianSpec(**{**spec.__dict__, **overrides})
+    rng = np.random.default_rng(spec.seed)
+    n, W, H, f = spec.n, spec.width, spec.height, spec.focal
+    R = _axis_angle(spec.cam_axis, spec.cam_angle).astype(np.float32).astype(np.float64)
+    tv = np.asarray(spec.cam_t, np.float32).astype(np.float64)
+    cam = {"R": R, "tv": tv, "fx": f, "fy": f, "cx": W / 2.0, "cy": H / 2.0, "near": 0.01}
+    z = rng.uniform(spec.depth_lo, spec.depth_hi, n)
+    m = spec.margin
+    px = rng.uniform(-m, W + m, n)
+    py = rng.uniform(-m, H + m, n)
+    fracs = np.array([c[0] for c in spec.size_classes], np.float64)
+    counts = np.floor(fracs / fracs.sum() * n).astype(np.int64)
+    counts[0] += n - counts.sum()
+    cls = np.repeat(np.arange(len(counts)), counts)[rng.permutation(n)]
+    lo = np.log(np.array([c[1] for c in spec.size_classes]))[cls]
+    hi = np.log(np.array([c[2] for c in spec.size_classes]))[cls]
+    s_px = np.exp(rng.uniform(lo, hi))
+    log_scales = np.log(s_px * z / f)[:, None] + rng.normal(0.0, spec.aniso_sd, (n, 3))
+    quats = rng.normal(size=(n, 4))
+    raw_op = rng.normal(spec.opacity_mu, spec.opacity_sd, n)
+    sh = rng.normal(0.0, spec.sh_sd, (n, 16, 3))
+    sh[:, 0, :] = rng.normal(0.0, spec.dc_sd, (n, 3))
+    grad = rng.normal(0.0, spec.grad_sd, (n, 9))
+    # camera coordinates from the pixel position and depth, then world coordinates p = R^T (t - tv)
+    t = np.stack([(px - cam["cx"]) * z / f, (py - cam["cy"]) * z / f, z], axis=1)
+    k_near = int(round(spec.near_frac * n))
+    if k_near:
+        behind = rng.choice(n, k_near, replace=False)
+        t[behind, 2] = rng.uniform(-1.0, cam["near"], k_near)
+    means = (t - tv) @ R
+    return GaussianScene(spec, cam, means.astype(np.float32), log_scales.astype(np.float32),
+                         quats.astype(np.float32), raw_op.astype(np.float32), sh.astype(np.float32),
+                         grad.astype(np.float32))

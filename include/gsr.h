@@ -5,6 +5,8 @@
  *   gsr_render_forward  per-pixel front-to-back alpha compositing over each 16x16 tile's depth-sorted splats
  *   gsr_render_backward the 9 per-splat 2D gradients of that compositing
  *   gsr_adam_step       one fused Adam step over every parameter group
+ * and, on either side of it, the projection of 3D Gaussians to those splats and the projection's backward pass
+ * (gsr_project_forward / gsr_project_backward).
  *
  * Conventions shared by every entry point
  *   - Pointers named as device pointers must point to memory allocated on the context's device (hipMalloc or a
@@ -185,6 +187,50 @@ typedef struct gsr_adam_group {
  * Errors: GSR_EINVAL (null pointers with count > 0, n_groups > GSR_ADAM_MAX_GROUPS, bc1 or bc2 not > 0), GSR_EHIP. */
 gsr_status gsr_adam_step(gsr_ctx* ctx, void* stream, const gsr_adam_group* groups, uint32_t n_groups, float beta1,
                          float beta2, float eps, float bc1, float bc2);
+
+/* Pinhole camera of the projection. World point p has camera coordinates t = R p + tv; pixel coordinates are
+ * (fx tx / tz + cx, fy ty / tz + cy) in the frame where pixel (px, py) has its centre at (px + 0.5, py + 0.5). */
+typedef struct gsr_camera {
+  float R[9];  /* world-to-camera rotation, row-major */
+  float tv[3];
+  float fx, fy, cx, cy;
+  float near;  /* Gaussians with tz <= near (or a NaN tz) are culled */
+} gsr_camera;
+
+/* Projection of n 3D Gaussians to splat records and depths. The parameter groups are those of the pages' trainer
+ * (means 3, log_scales 3, rot_quats 4, raw_opacities 1, sh_coeffs 16 x 3: SH degree 3, 59 floats per Gaussian;
+ * M3 per-splat backward page, full-scale parity table; rasterize forward + adam kernel audit page, section 2 "(f)"),
+ * and the record's opacity is the sigmoid of the raw opacity (W1 warp sparse skip + exp-skip page, section 1). The
+ * pages print no projection formula; this is the pinhole EWA projection:
+ *   t = R p + tv;  Sigma = Rq diag(exp(log_s))^2 Rq^T with Rq the rotation of the normalised quaternion (w, x, y, z);
+ *   J = d(pixel mean)/dt = [[fx / tz, 0, -fx tx / tz^2], [0, fy / tz, -fy ty / tz^2]];
+ *   Sigma' = J R Sigma R^T J^T + 0.3 I (a 0.3 px^2 low-pass); [[a, b], [b, c]] = Sigma'^-1;
+ *   (x, y) = (fx tx / tz + cx, fy ty / tz + cy);  o = 1 / (1 + exp(-raw));  depth = tz;
+ *   rgb = max(sum_k sh[k] Y_k(d) + 0.5, 0), d = (p - camera centre) / |p - camera centre|, Y_0..Y_15 the real
+ *   spherical harmonics of degrees 0..3 (orthonormal, Condon-Shortley signs, ordered by degree, then m = -l..l).
+ * A culled Gaussian gets the record 0 and depth 0, which gsr_bin skips. fp32 throughout; results agree with an
+ * exact evaluation to about 1e-6 relative (the 2x2 determinant is a sum of squares, see project.hip).
+ *   cam            host pointer
+ *   means, log_scales  device [n][3];  quats device [n][4] (16-byte aligned);  raw_opacities device [n]
+ *   sh             device [n][16][3] (coefficient-major, channel fastest; 16-byte aligned)
+ *   splats         device [n][9] float32, written;  depths device [n] float32, written
+ * Errors: GSR_EINVAL (null pointers, misalignment), GSR_EOVERFLOW (n * 48 >= 2^32), GSR_EHIP. */
+gsr_status gsr_project_forward(gsr_ctx* ctx, void* stream, const gsr_camera* cam, uint32_t n, const float* means,
+                               const float* log_scales, const float* quats, const float* raw_opacities,
+                               const float* sh, float* splats, float* depths);
+
+/* Backward pass of gsr_project_forward: given dL/d(record) for each Gaussian, the gradients of its five parameter
+ * groups, by the chain rule through the same formulas (recomputed, nothing is cached between the two calls);
+ * the clamp of a colour channel at 0 passes no gradient, and a culled Gaussian gets zero gradients.
+ *   cam, n, means .. sh  as given to gsr_project_forward
+ *   splats_grad    device [n][9] float32 (as written by gsr_render_backward)
+ *   *_grad         device arrays shaped like their parameters (quats_grad and sh_grad 16-byte aligned), overwritten
+ * Errors: GSR_EINVAL, GSR_EOVERFLOW, GSR_EHIP. */
+gsr_status gsr_project_backward(gsr_ctx* ctx, void* stream, const gsr_camera* cam, uint32_t n, const float* means,
+                                const float* log_scales, const float* quats, const float* raw_opacities,
+                                const float* sh, const float* splats_grad, float* means_grad,
+                                float* log_scales_grad, float* quats_grad, float* raw_opacities_grad,
+                                float* sh_grad);
 
 #ifdef __cplusplus
 }

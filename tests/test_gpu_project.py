@@ -1,0 +1,176 @@
+"""GPU projection of 3D Gaussians (gsr_project_forward / gsr_project_backward) against the fp64 oracle.
+
+Bars. Forward, element by element, bounds derived from fp32 rounding of the same formulas (u = 2^-24):
+  mean:   |dx| <= 16 u (fx / tz (|R p| + |tv| + |tx / tz| (|R p|_z + |tv_z|)) + |x|)   the camera transform's rounding
+          carried through the pinhole division, plus the division and the final fma
+  conic:  |d(a, b, c)| <= 256 u (|a| + |c|)   (the determinant is a sum of squares, so the conic keeps relative
+          accuracy to within a few dozen roundings of its norm)
+  colour: |d rgb| <= 64 u (1 + sum_k |sh_k|)  (16 fma of |Y_k| <= 3 terms, and the direction's rounding)
+  opacity |do| <= 8 u o;  depth |dz| <= 8 u (|R p|_z + |tv_z|)
+Backward: |gpu - oracle| <= 1e-4 + 1e-4 |oracle| for every element of the five gradients (the tolerance of the
+pages' parity table for exactly these tensors). A colour channel whose unclamped value lies within its forward bound
+of 0 is an ambiguous clamp decision (either side may take it); the SH and mean gradients of such Gaussians, the
+only ones the decision reaches, are excluded from the comparison and the Gaussians counted (the count must stay
+below 1e-4 of them).
+"""
+import numpy as np
+import pytest
+
+from gpuhelp import banner, dev, host
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    from differentiable_gaussian_splatting_amd import gsr
+    c = gsr.Context(0)
+    yield c
+    c.close()
+
+
+def gpu_camera(cam):
+    from differentiable_gaussian_splatting_amd import gsr
+    return gsr.camera(cam["R"], cam["tv"], cam["fx"], cam["fy"], cam["cx"], cam["cy"], cam["near"])
+
+
+def oracle_camera(cam):
+    from oracle import project as op
+    return op.Camera(R=cam["R"], tv=cam["tv"], fx=cam["fx"], fy=cam["fy"], cx=cam["cx"], cy=cam["cy"],
+                     near=cam["near"])
+
+
+def params_of(g):
+    return g.means, g.log_scales, g.quats, g.raw_opacities, g.sh
+
+
+def forward_bounds(g, rec):
+    cam = g.camera
+    R, tv = cam["R"], cam["tv"]
+    p = g.means.astype(np.float64)
+    aRp = np.abs(p) @ np.abs(R).T + np.abs(tv)  # |R p| + |tv| per camera axis
+    t = p @ R.T + tv
+    tz = np.where(t[:, 2] > 0, t[:, 2], 1.0)
+    bx = 16 * U * (cam["fx"] / tz * (aRp[:, 0] + np.abs(t[:, 0] / tz) * aRp[:, 2]) + np.abs(rec[:, 0]))
+    by = 16 * U * (cam["fy"] / tz * (aRp[:, 1] + np.abs(t[:, 1] / tz) * aRp[:, 2]) + np.abs(rec[:, 1]))
+    bcon = 256 * U * (np.abs(rec[:, 2]) + np.abs(rec[:, 4]))
+    bcol = 64 * U * (1.0 + np.abs(g.sh.astype(np.float64)).sum(axis=1))  # [N, 3]
+    bo = 8 * U * np.abs(rec[:, 8])
+    bz = 8 * U * aRp[:, 2]
+    return np.column_stack([bx, by, bcon, bcon, bcon, bcol, bo]), bz
+
+
+def run_forward(ctx, g):
+    from differentiable_gaussian_splatting_amd import gsr
+    sp, d = gsr.gsr_project_forward(ctx, gpu_camera(g.camera), *[dev(a) for a in params_of(g)])
+    return host(sp), host(d)
+
+
+def check_forward(g, rec_gpu, depth_gpu):
+    from oracle import project as op
+    rec, depth = op.project_forward(oracle_camera(g.camera), *params_of(g))
+    bound, bz = forward_bounds(g, rec)
+    err = np.abs(rec_gpu.astype(np.float64) - rec)
+    ratio = err / np.maximum(bound, 1e-30)
+    ratio[bound == 0] = np.where(err[bound == 0] == 0, 0.0, np.inf)
+    culled = depth == 0
+    assert np.array_equal(depth_gpu == 0, culled), "culling decisions differ"
+    assert (rec_gpu[culled] == 0).all()
+    zr = np.abs(depth_gpu - depth) / np.maximum(bz, 1e-30)
+    worst = np.unravel_index(np.argmax(ratio), ratio.shape)
+    print(f"  forward: worst error / bound {ratio.max():.3g} at {worst}, depth {zr.max():.3g}, culled {culled.sum()}")
+    assert ratio.max() <= 1.0, (worst, rec_gpu[worst[0]], rec[worst[0]])
+    assert zr.max() <= 1.0
+    return rec, bound
+
+
+def check_backward(ctx, g, rec, bound):
+    from differentiable_gaussian_splatting_amd import gsr
+    from oracle import project as op
+    ps = [dev(a) for a in params_of(g)]
+    grads = gsr.gsr_project_backward(ctx, gpu_camera(g.camera), *ps, dev(g.splats_grad))
+    ref = op.project_backward(oracle_camera(g.camera), *params_of(g), g.splats_grad)
+    # unclamped colours of the oracle: rgb where lit; a channel near 0 may be decided either way
+    from oracle.project import _params64  # the oracle's own unclamped value
+    import torch
+    with torch.no_grad():
+        ts = _params64(*params_of(g))
+        c = torch.as_tensor(op.Camera.centre(oracle_camera(g.camera)))
+        v = ts[0] - c
+        d = v / torch.linalg.norm(v, dim=1, keepdim=True)
+        raw = (torch.einsum("nk,nkc->nc", op.sh_basis(d), ts[4].reshape(-1, 16, 3)) + 0.5).numpy()
+    ambiguous = (np.abs(raw) <= bound[:, 5:8]).any(axis=1) & (rec[:, 8] > 0)
+    print(f"  backward: {ambiguous.sum()} Gaussians with an ambiguous colour clamp")
+    # expected about n x 3 channels x 2 x (bound ~ 3e-5) x (density of the colour at 0 ~ 0.3): well below 1e-4 n
+    assert ambiguous.sum() <= max(2, g.spec.n // 10_000)
+    for name, gg, rr in zip(("means", "log_scales", "quats", "raw_opacities", "sh"), grads, ref):
+        # the clamp decision reaches the SH and mean gradients only; the other groups are compared everywhere
+        keep = ~ambiguous if name in ("means", "sh") else np.ones(g.spec.n, bool)
+        a = host(gg).reshape(g.spec.n, -1)[keep].astype(np.float64)
+        b = rr.reshape(g.spec.n, -1)[keep]
+        ratio = np.abs(a - b) / (1e-4 + 1e-4 * np.abs(b))
+        w = np.unravel_index(np.argmax(ratio), ratio.shape) if ratio.size else None
+        print(f"  {name}: worst |gpu - ref| / (1e-4 + 1e-4 |ref|) = {ratio.max() if ratio.size else 0:.3g}")
+        assert ratio.size == 0 or ratio.max() <= 1.0, (name, w, a[w], b[w])
+        culled = rec[:, 8] == 0
+        assert (host(gg).reshape(g.spec.n, -1)[culled] == 0).all()
+
+
+@pytest.mark.parametrize("name", ["gauss_tiny", "gauss_ragged", "gauss410k"])
+def test_project_matches_oracle(ctx, name):
+    from differentiable_gaussian_splatting_amd import scenes
+    banner(f"project {name}")
+    g = scenes.make_gaussians(name)
+    rec_gpu, depth_gpu = run_forward(ctx, g)
+    rec, bound = check_forward(g, rec_gpu, depth_gpu)
+    check_backward(ctx, g, rec, bound)
+
+
+def test_project_counts_not_multiple_of_the_block(ctx):
+    from differentiable_gaussian_splatting_amd import scenes
+    for n in (1, 255, 257, 1000):
+        banner(f"project n={n}")
+        g = scenes.make_gaussians("gauss_tiny", n=n, seed=100 + n)
+        rec_gpu, depth_gpu = run_forward(ctx, g)
+        rec, bound = check_forward(g, rec_gpu, depth_gpu)
+        check_backward(ctx, g, rec, bound)
+
+
+def test_project_empty_and_bad_arguments(ctx):
+    import torch
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("project empty / bad arguments")
+    cam = gsr.camera(np.eye(3), [0, 0, 0], 100.0, 100.0, 8.0, 8.0)
+    z3 = torch.empty((0, 3), device="cuda")
+    sp, d = gsr.gsr_project_forward(ctx, cam, z3, z3, torch.empty((0, 4), device="cuda"),
+                                    torch.empty(0, device="cuda"), torch.empty((0, 16, 3), device="cuda"))
+    assert sp.numel() == 0 and d.numel() == 0
+    lib = gsr.load()
+    st = lib.gsr_project_forward(ctx.handle, None, None, 4, None, None, None, None, None, None, None)
+    assert st == gsr.GSR_EINVAL
+
+
+def test_project_chain_with_the_rasterizer(ctx):
+    """Projection, binning, forward, backward and the projection's backward chained on the GPU: the projection's
+    gradients match the oracle's for the rasterizer gradients the GPU produced (each stage's own parity is tested on
+    its own)."""
+    from differentiable_gaussian_splatting_amd import gsr, scenes
+    from oracle import project as op
+    banner("project -> raster -> project backward, gauss_tiny")
+    g = scenes.make_gaussians("gauss_tiny")
+    ps = [dev(a) for a in params_of(g)]
+    cam = gpu_camera(g.camera)
+    sp, depth = gsr.gsr_project_forward(ctx, cam, *ps)
+    W, H = g.width, g.height
+    bins = gsr.gsr_bin(ctx, sp, depth, W, H)
+    out, ft, lc = gsr.gsr_render_forward(ctx, sp, bins, W, H)
+    v_out = dev(np.random.default_rng(9).normal(0, 0.1, (H, W, 4)).astype(np.float32))
+    sg = gsr.gsr_render_backward(ctx, sp, bins, W, H, out, ft, lc, v_out)
+    grads = gsr.gsr_project_backward(ctx, cam, *ps, sg)
+    assert np.abs(host(sg)).sum() > 0
+    ref = op.project_backward(oracle_camera(g.camera), *params_of(g), host(sg))
+    for gg, rr in zip(grads, ref):
+        a = host(gg).reshape(rr.shape).astype(np.float64)
+        assert (np.abs(a - rr) <= 1e-4 + 1e-4 * np.abs(rr)).all()
