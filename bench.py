@@ -7,6 +7,8 @@ are seeded synthetic data resident in device memory before the timed region; the
 Prints one JSON line: the metric is splat-pixel evaluations per second over whole steps, where the evaluations of a
 step are E_fwd (list entries the forward examines, up to and including each pixel's stopping splat) plus E_bwd
 (entries the backward replays, the sum of last_contrib), both counted exactly by the CPU oracle on the same input.
+A "projection" block beside it times the steps on either side of the path on their own: the projection of 410k 3D
+Gaussians and its backward pass, and a whole iteration chaining them with the path and Adam.
 
     python bench.py [--steps K] [--warmup W] [--workload iter410k] [--no-cpu-baseline]
     python bench.py --calib-copy      # a plain 256 MiB device copy, to scale HBM byte counters
@@ -271,8 +273,101 @@ def main():
                                             "stage_s": cm}
     else:
         result["value"] = None
+    result["projection"] = bench_projection(args, ctx, gsr, scenes, sc, hp=hp, bc=bc)
     print(json.dumps(result), flush=True)
     ctx.close()
+
+
+def bench_projection(args, ctx, gsr, scenes, sc, hp, bc):
+    """The steps on either side of the path, timed on their own (not part of `value`): the projection of 410k 3D
+    Gaussians to splats and its backward pass, and a whole training iteration that chains them with the path
+    (project, bin, forward, backward, project backward, Adam on the five parameter groups with those gradients)."""
+    import numpy as np
+    import torch
+    from differentiable_gaussian_splatting_amd import profiling
+
+    g3 = scenes.make_gaussians("gauss410k")
+    n = g3.spec.n
+    cam = gsr.camera(g3.camera["R"], g3.camera["tv"], g3.camera["fx"], g3.camera["fy"], g3.camera["cx"],
+                     g3.camera["cy"], g3.camera["near"])
+    ps = [torch.from_numpy(a).cuda() for a in (g3.means, g3.log_scales, g3.quats, g3.raw_opacities, g3.sh)]
+    sg = torch.from_numpy(g3.splats_grad).cuda()
+    sp, dp = gsr.gsr_project_forward(ctx, cam, *ps)
+    grads = gsr.gsr_project_backward(ctx, cam, *ps, sg)
+    stream = torch.cuda.current_stream()
+    reps = max(5, args.steps)
+    for _ in range(3):
+        gsr.gsr_project_forward(ctx, cam, *ps, splats=sp, depths=dp)
+        gsr.gsr_project_backward(ctx, cam, *ps, sg, grads=grads)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for k in range(reps):
+        ev[k][0].record(stream)
+        gsr.gsr_project_forward(ctx, cam, *ps, splats=sp, depths=dp)
+        ev[k][1].record(stream)
+        gsr.gsr_project_backward(ctx, cam, *ps, sg, grads=grads)
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    f_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    b_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    # algorithmic bytes: forward reads 59 parameters and writes the 9-value record and the depth; the backward reads
+    # the parameters and the record gradient and writes 59 gradients
+    f_bytes, b_bytes = n * (59 + 10) * 4, n * (59 + 9 + 59) * 4
+    traffic_md = os.path.join(ROOT, "profiles", f"hbm_counters_{args.workload}.md")
+    roofs = {}
+    for k, ms, by in (("project_forward", f_ms, f_bytes), ("project_backward", b_ms, b_bytes)):
+        ach = by / (ms * 1e-3) / 1e9
+        roofs[k] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                    "work_per_launch": by, "traffic": profiling.traffic_for(profiling.STAGE_KERNEL[k], traffic_md)}
+
+    # a whole iteration on the projected splats
+    W, H = sc.width, sc.height
+    v_out = torch.from_numpy(sc.v_out).cuda()
+    out = torch.empty((H, W, 4), dtype=torch.float32, device="cuda")
+    ft = torch.empty((H, W), dtype=torch.float32, device="cuda")
+    lc = torch.empty((H, W), dtype=torch.int32, device="cuda")
+    rec_grad = torch.empty((n, 9), dtype=torch.float32, device="cuda")
+    ms_ = [torch.zeros_like(p) for p in ps]
+    vs_ = [torch.zeros_like(p) for p in ps]
+    adam = [(p, g, m, v, hp["lr"]) for p, g, m, v in zip(ps, grads, ms_, vs_)]
+
+    def iteration():
+        gsr.gsr_project_forward(ctx, cam, *ps, splats=sp, depths=dp)
+        b = gsr.gsr_bin(ctx, sp, dp, W, H)
+        gsr.gsr_render_forward(ctx, sp, b, W, H, out, ft, lc)
+        gsr.gsr_render_backward(ctx, sp, b, W, H, out, ft, lc, v_out, rec_grad)
+        gsr.gsr_project_backward(ctx, cam, *ps, rec_grad, grads=grads)
+        gsr.gsr_adam_step(ctx, adam, hp["beta1"], hp["beta2"], hp["eps"], *bc)
+        return b
+
+    for _ in range(3):
+        iteration()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        b = iteration()
+    torch.cuda.synchronize()
+    it_ms = (time.perf_counter() - t0) * 1e3 / reps
+    out_d = {"workload": f"gauss410k: {n} 3D Gaussians (means, log_scales, quats, raw_opacities, SH degree 3) seen "
+                         f"by an {W}x{H} pinhole camera, projected sizes as the path's workload",
+             "forward_ms": f_ms, "backward_ms": b_ms, "rooflines": roofs,
+             "iteration_ms": it_ms, "iteration_pairs": b.num_pairs,
+             "iteration": "project + bin + forward + backward + project backward + Adam on the 5 groups"}
+    if not args.no_cpu_baseline:
+        from oracle import project as op
+        ocam = op.Camera(R=g3.camera["R"], tv=g3.camera["tv"], fx=g3.camera["fx"], fy=g3.camera["fy"],
+                         cx=g3.camera["cx"], cy=g3.camera["cy"], near=g3.camera["near"])
+        par = (g3.means, g3.log_scales, g3.quats, g3.raw_opacities, g3.sh)
+        t0 = time.perf_counter()
+        op.project_forward(ocam, *par)
+        t1 = time.perf_counter()
+        op.project_backward(ocam, *par, g3.splats_grad)
+        t2 = time.perf_counter()
+        out_d["cpu_baseline"] = {"forward_s": t1 - t0, "backward_s": t2 - t1, "kind": "oracle",
+                                 "cores": torch.get_num_threads(),
+                                 "sample": "the oracle's fp64 projection and its automatic backward over all "
+                                           f"{n} Gaussians"}
+    return out_d
 
 
 if __name__ == "__main__":
