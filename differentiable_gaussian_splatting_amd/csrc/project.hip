@@ -155,11 +155,52 @@ __device__ __forceinline__ void load3(const float* __restrict__ a, uint32_t i, f
   v[2] = a[3 * size_t(i) + 2];
 }
 
+// The SH blocks of a workgroup's 256 Gaussians are contiguous (256 x 192 B). The backward moves them between HBM and
+// LDS with 16-byte accesses of consecutive threads to consecutive addresses, and each thread reads or writes its own
+// 48 values in LDS (a thread storing its own 192 bytes makes every wave-wide store touch 64 lines); the forward
+// loads them directly, which measured faster there (no 48 KB of LDS per workgroup, twice the resident waves).
+constexpr uint32_t kShVec = 12;  // float4 per Gaussian
+
+__device__ __forceinline__ void stage_sh_in(const float* __restrict__ sh, uint32_t n, float4* s_sh) {
+  const uint32_t g0 = blockIdx.x * kThreads;
+  const uint32_t count = min(kThreads, n - g0) * kShVec;
+  const float4* src = reinterpret_cast<const float4*>(sh) + size_t(g0) * kShVec;
+#pragma unroll
+  for (uint32_t j = 0; j < kShVec; ++j) {
+    const uint32_t e = threadIdx.x + j * kThreads;
+    if (e < count) s_sh[e] = src[e];
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void stage_sh_out(float* __restrict__ out, uint32_t n, const float4* s_sh) {
+  __syncthreads();
+  const uint32_t g0 = blockIdx.x * kThreads;
+  const uint32_t count = min(kThreads, n - g0) * kShVec;
+  float4* dst = reinterpret_cast<float4*>(out) + size_t(g0) * kShVec;
+#pragma unroll
+  for (uint32_t j = 0; j < kShVec; ++j) {
+    const uint32_t e = threadIdx.x + j * kThreads;
+    if (e < count) dst[e] = s_sh[e];
+  }
+}
+
 __device__ __forceinline__ void load_sh(const float* __restrict__ sh, uint32_t i, float (&c)[48]) {
   const float4* s4 = reinterpret_cast<const float4*>(sh + 48 * size_t(i));
 #pragma unroll
-  for (int k = 0; k < 12; ++k) {
+  for (uint32_t k = 0; k < kShVec; ++k) {
     const float4 v = s4[k];
+    c[4 * k] = v.x;
+    c[4 * k + 1] = v.y;
+    c[4 * k + 2] = v.z;
+    c[4 * k + 3] = v.w;
+  }
+}
+
+__device__ __forceinline__ void read_sh(const float4* s_sh, float (&c)[48]) {
+#pragma unroll
+  for (uint32_t k = 0; k < kShVec; ++k) {
+    const float4 v = s_sh[threadIdx.x * kShVec + k];
     c[4 * k] = v.x;
     c[4 * k + 1] = v.y;
     c[4 * k + 2] = v.z;
@@ -191,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void k_project_forward(Cam cam, uint32_t 
   Proj P;
   project_one(cam, p, ls, q, P);
   float c[48];
-  load_sh(sh, i, c);
+  load_sh(sh, i, c);  // direct 16-byte loads: staging through LDS (as the backward does) measured slower here
   float Y[16];
   sh_basis(P.dir[0], P.dir[1], P.dir[2], Y);
   float rgb[3];
@@ -215,20 +256,19 @@ __global__ __launch_bounds__(kThreads) void k_project_forward(Cam cam, uint32_t 
   depths[i] = P.t[2];
 }
 
-__global__ __launch_bounds__(kThreads) void k_project_backward(
-    Cam cam, uint32_t n, const float* __restrict__ means, const float* __restrict__ log_scales,
-    const float* __restrict__ quats, const float* __restrict__ raw_op, const float* __restrict__ sh,
-    const float* __restrict__ splats_grad, float* __restrict__ g_means, float* __restrict__ g_log_scales,
-    float* __restrict__ g_quats, float* __restrict__ g_raw_op, float* __restrict__ g_sh) {
-  const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
-  if (i >= n) return;
+__device__ __forceinline__ void backward_one(const Cam& cam, uint32_t i, const float* __restrict__ means,
+                                             const float* __restrict__ log_scales, const float* __restrict__ quats,
+                                             const float* __restrict__ raw_op, const float* __restrict__ splats_grad,
+                                             float* __restrict__ g_means, float* __restrict__ g_log_scales,
+                                             float* __restrict__ g_quats, float* __restrict__ g_raw_op,
+                                             float4* s_sh) {
   float p[3], ls[3], q[4];
   load3(means, i, p);
   load3(log_scales, i, ls);
   const float4 q4 = reinterpret_cast<const float4*>(quats)[i];
   q[0] = q4.x, q[1] = q4.y, q[2] = q4.z, q[3] = q4.w;
   const float tz0 = fmaf(cam.R[8], p[2], fmaf(cam.R[7], p[1], fmaf(cam.R[6], p[0], cam.tv[2])));
-  float4* gsh4 = reinterpret_cast<float4*>(g_sh + 48 * size_t(i));
+  float4* gsh4 = s_sh + threadIdx.x * kShVec;  // the thread's coefficients, overwritten by their gradients
   if (!(tz0 > cam.near)) {
 #pragma unroll
     for (int k = 0; k < 3; ++k) g_means[3 * size_t(i) + k] = g_log_scales[3 * size_t(i) + k] = 0.0f;
@@ -250,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void k_project_backward(
 
   // colour: d sh, and d dir through the basis
   float c[48];
-  load_sh(sh, i, c);
+  read_sh(s_sh, c);
   float Y[16];
   sh_basis(P.dir[0], P.dir[1], P.dir[2], Y);
   float gc[3];
@@ -343,6 +383,20 @@ __global__ __launch_bounds__(kThreads) void k_project_backward(
 #pragma unroll
   for (int k = 0; k < 3; ++k)
     g_means[3 * size_t(i) + k] = gp[k] + fmaf(R[6 + k], dtz, fmaf(R[3 + k], dty, R[k] * dtx));
+}
+
+__global__ __launch_bounds__(kThreads) void k_project_backward(
+    Cam cam, uint32_t n, const float* __restrict__ means, const float* __restrict__ log_scales,
+    const float* __restrict__ quats, const float* __restrict__ raw_op, const float* __restrict__ sh,
+    const float* __restrict__ splats_grad, float* __restrict__ g_means, float* __restrict__ g_log_scales,
+    float* __restrict__ g_quats, float* __restrict__ g_raw_op, float* __restrict__ g_sh) {
+  __shared__ float4 s_sh[kThreads * kShVec];  // the coefficients in, then their gradients out
+  stage_sh_in(sh, n, s_sh);
+  const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+  // every thread of the workgroup reaches the barrier of stage_sh_out, so the work below runs under a condition
+  if (i < n) backward_one(cam, i, means, log_scales, quats, raw_op, splats_grad, g_means, g_log_scales, g_quats,
+                          g_raw_op, s_sh);
+  stage_sh_out(g_sh, n, s_sh);
 }
 
 Cam make_cam(const gsr_camera& c) {
