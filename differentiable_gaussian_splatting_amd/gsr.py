@@ -72,6 +72,7 @@ SIGNATURES = {
     "gsr_project_forward": (_I32, [_P, _P, ctypes.POINTER(gsr_camera), _U32, _P, _P, _P, _P, _P, _P, _P]),
     "gsr_project_backward": (_I32, [_P, _P, ctypes.POINTER(gsr_camera), _U32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _P]),
+    "gsr_loss_l1_ssim": (_I32, [_P, _P, _U32, _U32, _P, _P, _P, _P]),
 }
 
 _lib = None
@@ -324,3 +325,22 @@ def gsr_project_backward(ctx: Context, cam: gsr_camera, means, log_scales, quats
                                           *[_ptr(t) for t in params], _ptr(splats_grad), *[_ptr(g) for g in grads]),
               "gsr_project_backward")
     return grads
+
+
+def gsr_loss_l1_ssim(ctx: Context, out_rgba: torch.Tensor, target: torch.Tensor, v_out: torch.Tensor | None = None,
+                     loss: torch.Tensor | None = None, stream=None):
+    """L1 + SSIM of out_rgba [H, W, 4] (its rgb) against target [H, W, 3]. Returns (v_out float32 [H, W, 4],
+    loss float32 [3] = (L, mean|x - y|, mean SSIM)), both on the device."""
+    dev = ctx.device
+    H, W = out_rgba.shape[0], out_rgba.shape[1]
+    _need(out_rgba, "out_rgba", (torch.float32,), H * W * 4, dev)
+    _need(target, "target", (torch.float32,), H * W * 3, dev)
+    if v_out is None:
+        v_out = torch.empty((H, W, 4), dtype=torch.float32, device=dev)
+    if loss is None:
+        loss = torch.empty(3, dtype=torch.float32, device=dev)
+    _need(v_out, "v_out", (torch.float32,), H * W * 4, dev)
+    _need(loss, "loss", (torch.float32,), 3, dev)
+    ctx.check(load().gsr_loss_l1_ssim(ctx.handle, _stream(stream), W, H, _ptr(out_rgba), _ptr(target), _ptr(v_out),
+                                      _ptr(loss)), "gsr_loss_l1_ssim")
+    return v_out, loss

@@ -6,7 +6,8 @@
  *   gsr_render_backward the 9 per-splat 2D gradients of that compositing
  *   gsr_adam_step       one fused Adam step over every parameter group
  * and, on either side of it, the projection of 3D Gaussians to those splats and the projection's backward pass
- * (gsr_project_forward / gsr_project_backward).
+ * (gsr_project_forward / gsr_project_backward), and the L1 + SSIM loss that gives the backward its v_out
+ * (gsr_loss_l1_ssim).
  *
  * Conventions shared by every entry point
  *   - Pointers named as device pointers must point to memory allocated on the context's device (hipMalloc or a
@@ -231,6 +232,22 @@ gsr_status gsr_project_backward(gsr_ctx* ctx, void* stream, const gsr_camera* ca
                                 const float* sh, const float* splats_grad, float* means_grad,
                                 float* log_scales_grad, float* quats_grad, float* raw_opacities_grad,
                                 float* sh_grad);
+
+/* The training loss on the rendered image and its gradient, which is the v_out of gsr_render_backward:
+ *   L = (1 - 0.2) mean|x - y| + 0.2 (1 - mean S),
+ *   S = ((2 mx my + C1)(2 sxy + C2)) / ((mx^2 + my^2 + C1)(sx + sy + C2)),  C1 = 0.01^2,  C2 = 0.03^2,
+ * per channel with mx = G * x, sx = G * x^2 - mx^2, sxy = G * (x y) - mx my, G * the correlation with the normalised
+ * 11-tap Gaussian window (sigma 1.5) in each direction over the zero-padded image; means over the 3 W H values.
+ * The pages name a fused L1 + SSIM loss and its backward (M3 per-splat backward page, the brush change it ports) and
+ * the SSIM window sizes 7 and 11 (SSIM float4 finding); the constants and the weight 0.2 are the usual ones.
+ * fp32 arithmetic; the loss adds per-tile fp64 partial sums in a fixed order (the same value on every run).
+ *   out_rgba   device [height][width][4] float32 (x = its first three channels; 16-byte aligned)
+ *   target     device [height][width][3] float32 (y)
+ *   v_out      device [height][width][4] float32, written: dL/dx in .xyz, 0 in .w (16-byte aligned)
+ *   loss       device [3] float32, written: L, mean|x - y|, mean S
+ * Errors: GSR_EINVAL (null pointers, empty image, misalignment), GSR_ENOMEM, GSR_EHIP. */
+gsr_status gsr_loss_l1_ssim(gsr_ctx* ctx, void* stream, uint32_t width, uint32_t height, const float* out_rgba,
+                            const float* target, float* v_out, float* loss);
 
 #ifdef __cplusplus
 }
