@@ -8,7 +8,8 @@ Prints one JSON line: the metric is splat-pixel evaluations per second over whol
 step are E_fwd (list entries the forward examines, up to and including each pixel's stopping splat) plus E_bwd
 (entries the backward replays, the sum of last_contrib), both counted exactly by the CPU oracle on the same input.
 A "projection" block beside it times the steps on either side of the path on their own: the projection of 410k 3D
-Gaussians and its backward pass, and a whole iteration chaining them with the path and Adam.
+Gaussians and its backward pass, the L1 + SSIM loss, and a whole training iteration chaining them with the path and
+Adam.
 
     python bench.py [--steps K] [--warmup W] [--workload iter410k] [--no-cpu-baseline]
     python bench.py --calib-copy      # a plain 256 MiB device copy, to scale HBM byte counters
@@ -43,6 +44,10 @@ ALU_PUBLISHED_TFLOPS = 157.3  # the published fp32 vector figure, which counts p
 #               b dx + c dy (6) and their products (2); acc += mine (3); T update (1); 9 accumulations
 FWD_OPS = {"sigma_skip": 11, "alpha_reject": 14, "stop": 16, "contrib": 23}
 BWD_OPS = {"sigma_skip": 11, "alpha_reject": 14, "contrib": 73}
+# L1 + SSIM per pixel and channel: the products x^2, y^2, x y (3); 5 quantities x 11 taps x 2 passes as FMA (220);
+# variances, covariance and S with its three derivatives (25); 3 derivative maps x 11 taps x 2 passes (132); the
+# gradient's combination with the L1 sign (6)
+LOSS_OPS = 3 + 220 + 25 + 132 + 6
 
 
 def parse():
@@ -320,9 +325,11 @@ def bench_projection(args, ctx, gsr, scenes, sc, hp, bc):
         roofs[k] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                     "work_per_launch": by, "traffic": profiling.traffic_for(profiling.STAGE_KERNEL[k], traffic_md)}
 
-    # a whole iteration on the projected splats
+    # a whole training iteration on the projected splats, with the loss giving the backward its v_out
     W, H = sc.width, sc.height
-    v_out = torch.from_numpy(sc.v_out).cuda()
+    target = torch.from_numpy(scenes.make_target(W, H)).cuda()
+    v_out = torch.empty((H, W, 4), dtype=torch.float32, device="cuda")
+    loss_val = torch.empty(3, dtype=torch.float32, device="cuda")
     out = torch.empty((H, W, 4), dtype=torch.float32, device="cuda")
     ft = torch.empty((H, W), dtype=torch.float32, device="cuda")
     lc = torch.empty((H, W), dtype=torch.int32, device="cuda")
@@ -335,6 +342,7 @@ def bench_projection(args, ctx, gsr, scenes, sc, hp, bc):
         gsr.gsr_project_forward(ctx, cam, *ps, splats=sp, depths=dp)
         b = gsr.gsr_bin(ctx, sp, dp, W, H)
         gsr.gsr_render_forward(ctx, sp, b, W, H, out, ft, lc)
+        gsr.gsr_loss_l1_ssim(ctx, out, target, v_out, loss_val)
         gsr.gsr_render_backward(ctx, sp, b, W, H, out, ft, lc, v_out, rec_grad)
         gsr.gsr_project_backward(ctx, cam, *ps, rec_grad, grads=grads)
         gsr.gsr_adam_step(ctx, adam, hp["beta1"], hp["beta2"], hp["eps"], *bc)
@@ -348,11 +356,26 @@ def bench_projection(args, ctx, gsr, scenes, sc, hp, bc):
         b = iteration()
     torch.cuda.synchronize()
     it_ms = (time.perf_counter() - t0) * 1e3 / reps
+    loss_after = loss_val.tolist()
+    # the loss alone, on the last rendered image
+    lev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for k in range(reps):
+        lev[k][0].record(stream)
+        gsr.gsr_loss_l1_ssim(ctx, out, target, v_out, loss_val)
+        lev[k][1].record(stream)
+    torch.cuda.synchronize()
+    l_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in lev]))
+    loss_ops = 3 * W * H * LOSS_OPS
+    roofs["loss_l1_ssim"] = {"bound": "alu", "achieved": loss_ops / (l_ms * 1e-3) / 1e12, "peak": ALU_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "work_per_launch": loss_ops,
+                             "traffic": profiling.traffic_for(profiling.STAGE_KERNEL["loss_l1_ssim"], traffic_md)}
+    roofs["loss_l1_ssim"]["frac"] = roofs["loss_l1_ssim"]["achieved"] / ALU_PEAK_TFLOPS
     out_d = {"workload": f"gauss410k: {n} 3D Gaussians (means, log_scales, quats, raw_opacities, SH degree 3) seen "
                          f"by an {W}x{H} pinhole camera, projected sizes as the path's workload",
-             "forward_ms": f_ms, "backward_ms": b_ms, "rooflines": roofs,
-             "iteration_ms": it_ms, "iteration_pairs": b.num_pairs,
-             "iteration": "project + bin + forward + backward + project backward + Adam on the 5 groups"}
+             "forward_ms": f_ms, "backward_ms": b_ms, "loss_ms": l_ms, "rooflines": roofs,
+             "iteration_ms": it_ms, "iteration_pairs": b.num_pairs, "iteration_loss": loss_after,
+             "iteration": "project + bin + forward + L1/SSIM loss + backward + project backward + Adam on the 5 "
+                          "groups"}
     if not args.no_cpu_baseline:
         from oracle import project as op
         ocam = op.Camera(R=g3.camera["R"], tv=g3.camera["tv"], fx=g3.camera["fx"], fy=g3.camera["fy"],

@@ -117,7 +117,7 @@ void gsr_destroy(gsr_ctx* ctx) {
   Arena& a = ctx->arena;
   for (DevBuf* b : {&a.keys[0], &a.keys[1], &a.vals[0], &a.vals[1], &a.counts, &a.offsets, &a.order, &a.order_alt,
                     &a.order_vals, &a.order_vals_alt, &a.scan_part, &a.hist, &a.digit_tot, &a.ranges, &a.rects,
-                    &a.tile_order_ext, &a.tile_cost, &a.loss_part})
+                    &a.tile_order_ext, &a.tile_cost, &a.loss_part, &a.loss_maps})
     release(*b);
   if (a.host_total) (void)hipHostFree(a.host_total);
   if (a.done) (void)hipFree(a.done);

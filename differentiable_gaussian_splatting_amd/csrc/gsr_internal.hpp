@@ -42,6 +42,7 @@ struct Arena {
   DevBuf tile_order_ext;  // uint32 [tiles] raster launch order: the slowest expected tiles first
   DevBuf tile_cost;   // uint32 [4 tiles] splats each wavefront of the last forward walked (launch-order hint)
   DevBuf loss_part;   // double [2 tiles] per-tile sums of the SSIM map and |x - y| (the loss)
+  DevBuf loss_maps;   // float [9][H][W] the SSIM map's three derivatives per channel, between the loss's passes
   uint64_t* host_total = nullptr;  // pinned host word for the one pair-count readback
   uint32_t* done = nullptr;        // last-block-done counter of the count scan (0 between launches)
   hipEvent_t total_ready = nullptr;  // recorded after the readback is queued

@@ -12,12 +12,9 @@
 //   dL/dx(q) = (1 - lam) sign(x - y) / (3 H W) - lam / (3 H W) [G * df/dmx + 2 x G * df/d(G*x^2) + y G * df/d(G*xy)](q)
 // (G is symmetric, so its transpose is the same correlation).
 //
-// One workgroup per 16x16 tile and per image, all in LDS: the tile's pixels need the derivative maps on the tile
-// grown by 5 (26 x 26), which need the images on the tile grown by 10 (36 x 36). Per channel: load x and y (zeros
-// outside the image), a horizontal then a vertical 11-tap pass of the five products, the map values and their three
-// derivatives (zero outside the image), a horizontal and a vertical pass of those, and the gradient. Each tile writes
-// its sums of S and |x - y| (fp64) to its own slot; one workgroup adds the slots in order, so the loss is the same on
-// every run.
+// Two passes over 16x16 tiles (see k_ssim_maps and k_ssim_grad), with every window sum in LDS. Each tile of the first
+// pass writes its sums of S and |x - y| (fp64) to its own slot; the second pass's first workgroup adds the slots in
+// order, so the loss is the same on every run.
 #include <cmath>
 
 #include "gsr_internal.hpp"
@@ -28,8 +25,8 @@ namespace {
 constexpr uint32_t kThreads = 256;
 constexpr int kT = 16;              // output tile
 constexpr int kR = 5;               // window radius
-constexpr int kP = kT + 2 * kR;     // 26: derivative maps
-constexpr int kI = kT + 4 * kR;     // 36: images
+constexpr int kP = kT + 2 * kR;     // 26: the tile grown by the window radius
+constexpr int kLoads = (kP * kP + 255) / 256;  // positions of the 26 x 26 region per thread (256 threads)
 constexpr float kC1 = 0.01f * 0.01f;
 constexpr float kC2 = 0.03f * 0.03f;
 
@@ -49,127 +46,116 @@ __device__ __forceinline__ double block_sum(double v, double* s_red) {
   return t;
 }
 
-__global__ __launch_bounds__(kThreads) void k_l1_ssim(Taps taps, uint32_t width, uint32_t height, uint32_t tiles_x,
-                                                      float lam, float inv_n, const float4* __restrict__ out_rgba,
-                                                      const float* __restrict__ target, float4* __restrict__ v_out,
-                                                      double* __restrict__ part) {
-  __shared__ float s_x[kI][kI], s_y[kI][kI];
-  __shared__ float s_h[5][kI][kP];   // horizontal sums of x, y, xx, yy, xy
-  __shared__ float s_d[3][kP][kP];   // df/dmx, df/dSxx, df/dSxy (0 outside the image)
-  __shared__ float s_h2[3][kP][kT];  // their horizontal sums
+// Pass 1 (k_ssim_maps), per 16x16 tile: both images on the tile grown by 5 (26 x 26, all channels, zeros outside),
+// a horizontal 11-tap pass of the five products on 26 rows x the tile's 16 columns, a vertical pass at the tile's
+// pixels, then S and its three derivatives there, written to nine planes [map][channel][H][W]; the tile's sums of S
+// and |x - y| go to its slot. Pass 2 (k_ssim_grad), per tile: the nine planes on the tile grown by 5, a horizontal
+// and a vertical pass, and the gradient at the tile's pixels. Splitting at the derivative maps costs their 9 x 4 B
+// per pixel of traffic but halves the recomputed halo (a fused pass needs the images on the tile grown by 10).
+__global__ __launch_bounds__(kThreads) void k_ssim_maps(Taps taps, uint32_t width, uint32_t height, uint32_t tiles_x,
+                                                        const float4* __restrict__ out_rgba,
+                                                        const float* __restrict__ target, float* __restrict__ maps,
+                                                        double* __restrict__ part) {
+  __shared__ float s_x[3][kP][kP], s_y[3][kP][kP];
+  __shared__ float s_h[5][kP][kT];
   __shared__ double s_red[kThreads / 64];
-  const uint32_t tid = threadIdx.x;
+  const int tid = int(threadIdx.x);
   const int tx0 = int(blockIdx.x % tiles_x) * kT, ty0 = int(blockIdx.x / tiles_x) * kT;
   const int W = int(width), H = int(height);
-  const int ox = tid % kT, oy = tid / kT;  // this thread's output pixel in the tile
-  const int px = tx0 + ox, py = ty0 + oy;
-  const bool inside = px < W && py < H;
-  const size_t pix = inside ? size_t(py) * W + px : 0;
-  float g_out[3];
-  double ssim_sum = 0.0, l1_sum = 0.0;
-
-  for (int c = 0; c < 3; ++c) {
-    // images on the tile grown by 10, zero outside
-    for (int e = tid; e < kI * kI; e += kThreads) {
-      const int r = e / kI, q = e % kI;
-      const int gx = tx0 - 2 * kR + q, gy = ty0 - 2 * kR + r;
-      float xv = 0.0f, yv = 0.0f;
-      if (gx >= 0 && gy >= 0 && gx < W && gy < H) {
-        const size_t p = size_t(gy) * W + gx;
-        xv = reinterpret_cast<const float*>(out_rgba)[4 * p + c];
-        yv = target[3 * p + c];
-      }
-      s_x[r][q] = xv;
-      s_y[r][q] = yv;
-    }
-    __syncthreads();
-    // horizontal pass: rows 0..35, columns of the 26-wide region
-    for (int e = tid; e < kI * kP; e += kThreads) {
-      const int r = e / kP, q = e % kP;
-      float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f, a4 = 0.0f;
+  const size_t plane = size_t(W) * H;
+  {
+    // every load of the thread's (at most kLoads) positions is issued before the first store to LDS
+    float4 xv[kLoads];
+    float yv[kLoads][3];
 #pragma unroll
-      for (int t = 0; t < 2 * kR + 1; ++t) {
-        const float xv = s_x[r][q + t], yv = s_y[r][q + t], g = taps.g[t];
-        a0 = fmaf(g, xv, a0);
-        a1 = fmaf(g, yv, a1);
-        a2 = fmaf(g, xv * xv, a2);
-        a3 = fmaf(g, yv * yv, a3);
-        a4 = fmaf(g, xv * yv, a4);
-      }
-      s_h[0][r][q] = a0;
-      s_h[1][r][q] = a1;
-      s_h[2][r][q] = a2;
-      s_h[3][r][q] = a3;
-      s_h[4][r][q] = a4;
-    }
-    __syncthreads();
-    // vertical pass on the 26 x 26 region: the map and its three derivatives
-    for (int e = tid; e < kP * kP; e += kThreads) {
+    for (int it = 0; it < kLoads; ++it) {
+      const int e = tid + it * int(kThreads);
       const int r = e / kP, q = e % kP;
       const int gx = tx0 - kR + q, gy = ty0 - kR + r;
-      float d0 = 0.0f, d1 = 0.0f, d2 = 0.0f, S = 0.0f;
-      if (gx >= 0 && gy >= 0 && gx < W && gy < H) {
-        float mx = 0.0f, my = 0.0f, xx = 0.0f, yy = 0.0f, xy = 0.0f;
-#pragma unroll
-        for (int t = 0; t < 2 * kR + 1; ++t) {
-          const float g = taps.g[t];
-          mx = fmaf(g, s_h[0][r + t][q], mx);
-          my = fmaf(g, s_h[1][r + t][q], my);
-          xx = fmaf(g, s_h[2][r + t][q], xx);
-          yy = fmaf(g, s_h[3][r + t][q], yy);
-          xy = fmaf(g, s_h[4][r + t][q], xy);
-        }
-        const float sx = xx - mx * mx, sy = yy - my * my, sxy = xy - mx * my;
-        const float A = 2.0f * mx * my + kC1, B = 2.0f * sxy + kC2;
-        const float C = mx * mx + my * my + kC1, D = sx + sy + kC2;
-        const float iM = 1.0f / (C * D);
-        S = (A * B) * iM;
-        d0 = (2.0f * my * (B - A) - S * (2.0f * mx) * (D - C)) * iM;
-        d1 = -S / D;
-        d2 = 2.0f * A * iM;
+      xv[it] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      yv[it][0] = yv[it][1] = yv[it][2] = 0.0f;
+      if (e < kP * kP && gx >= 0 && gy >= 0 && gx < W && gy < H) {
+        const size_t p = size_t(gy) * W + gx;
+        xv[it] = out_rgba[p];
+        yv[it][0] = target[3 * p];
+        yv[it][1] = target[3 * p + 1];
+        yv[it][2] = target[3 * p + 2];
       }
-      s_d[0][r][q] = d0;
-      s_d[1][r][q] = d1;
-      s_d[2][r][q] = d2;
-      if (r >= kR && r < kR + kT && q >= kR && q < kR + kT) ssim_sum += double(S);  // the tile's own pixels
     }
-    __syncthreads();
-    // horizontal pass of the derivative maps: rows 0..25, the tile's 16 columns
-    for (int e = tid; e < kP * kT; e += kThreads) {
-      const int r = e / kT, q = e % kT;
-      float b0 = 0.0f, b1 = 0.0f, b2 = 0.0f;
 #pragma unroll
-      for (int t = 0; t < 2 * kR + 1; ++t) {
-        const float g = taps.g[t];
-        b0 = fmaf(g, s_d[0][r][q + t], b0);
-        b1 = fmaf(g, s_d[1][r][q + t], b1);
-        b2 = fmaf(g, s_d[2][r][q + t], b2);
-      }
-      s_h2[0][r][q] = b0;
-      s_h2[1][r][q] = b1;
-      s_h2[2][r][q] = b2;
+    for (int it = 0; it < kLoads; ++it) {
+      const int e = tid + it * int(kThreads);
+      if (e >= kP * kP) break;
+      const int r = e / kP, q = e % kP;
+      s_x[0][r][q] = xv[it].x;
+      s_x[1][r][q] = xv[it].y;
+      s_x[2][r][q] = xv[it].z;
+      s_y[0][r][q] = yv[it][0];
+      s_y[1][r][q] = yv[it][1];
+      s_y[2][r][q] = yv[it][2];
     }
-    __syncthreads();
-    // vertical pass at this thread's pixel, and the gradient
-    {
-      float b0 = 0.0f, b1 = 0.0f, b2 = 0.0f;
-#pragma unroll
-      for (int t = 0; t < 2 * kR + 1; ++t) {
-        const float g = taps.g[t];
-        b0 = fmaf(g, s_h2[0][oy + t][ox], b0);
-        b1 = fmaf(g, s_h2[1][oy + t][ox], b1);
-        b2 = fmaf(g, s_h2[2][oy + t][ox], b2);
-      }
-      const float xv = s_x[oy + 2 * kR][ox + 2 * kR], yv = s_y[oy + 2 * kR][ox + 2 * kR];
-      const float dssim = fmaf(yv, b2, fmaf(2.0f * xv, b1, b0));
-      const float diff = xv - yv;
-      const float sgn = diff > 0.0f ? 1.0f : (diff < 0.0f ? -1.0f : 0.0f);
-      g_out[c] = ((1.0f - lam) * sgn - lam * dssim) * inv_n;
-      if (inside) l1_sum += double(fabsf(diff));
-    }
-    __syncthreads();  // the next channel overwrites the LDS images
   }
-  if (inside) v_out[pix] = make_float4(g_out[0], g_out[1], g_out[2], 0.0f);
+  __syncthreads();
+  const int ox = tid % kT, oy = tid / kT;
+  const int px = tx0 + ox, py = ty0 + oy;
+  const bool inside = px < W && py < H;
+  double ssim_sum = 0.0, l1_sum = 0.0;
+  for (int c = 0; c < 3; ++c) {
+    // horizontal: rows 0..25, the tile's 16 columns; a thread takes two neighbouring columns and slides the window
+    // over the 12 values they share (208 threads, one pass)
+    if (tid < kP * (kT / 2)) {
+      const int r = tid % kP, q0 = 2 * (tid / kP);
+      float a[5][2];
+#pragma unroll
+      for (int o = 0; o < 2; ++o) a[0][o] = a[1][o] = a[2][o] = a[3][o] = a[4][o] = 0.0f;
+#pragma unroll
+      for (int j = 0; j <= 2 * kR + 1; ++j) {
+        const float xv = s_x[c][r][q0 + j], yv = s_y[c][r][q0 + j];
+        const float xx = xv * xv, yy = yv * yv, xy = xv * yv;
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+          const int t = j - o;
+          if (t >= 0 && t <= 2 * kR) {
+            const float g = taps.g[t];
+            a[0][o] = fmaf(g, xv, a[0][o]);
+            a[1][o] = fmaf(g, yv, a[1][o]);
+            a[2][o] = fmaf(g, xx, a[2][o]);
+            a[3][o] = fmaf(g, yy, a[3][o]);
+            a[4][o] = fmaf(g, xy, a[4][o]);
+          }
+        }
+      }
+#pragma unroll
+      for (int o = 0; o < 2; ++o)
+#pragma unroll
+        for (int k = 0; k < 5; ++k) s_h[k][r][q0 + o] = a[k][o];
+    }
+    __syncthreads();
+    float mx = 0.0f, my = 0.0f, xx = 0.0f, yy = 0.0f, xy = 0.0f;
+#pragma unroll
+    for (int t = 0; t <= 2 * kR; ++t) {
+      const float g = taps.g[t];
+      mx = fmaf(g, s_h[0][oy + t][ox], mx);
+      my = fmaf(g, s_h[1][oy + t][ox], my);
+      xx = fmaf(g, s_h[2][oy + t][ox], xx);
+      yy = fmaf(g, s_h[3][oy + t][ox], yy);
+      xy = fmaf(g, s_h[4][oy + t][ox], xy);
+    }
+    __syncthreads();  // the next channel overwrites s_h
+    if (inside) {
+      const float sx = xx - mx * mx, sy = yy - my * my, sxy = xy - mx * my;
+      const float A = 2.0f * mx * my + kC1, B = 2.0f * sxy + kC2;
+      const float C = mx * mx + my * my + kC1, D = sx + sy + kC2;
+      const float iM = 1.0f / (C * D);
+      const float S = (A * B) * iM;
+      const size_t p = size_t(py) * W + px;
+      maps[(0 * 3 + c) * plane + p] = (2.0f * my * (B - A) - S * (2.0f * mx) * (D - C)) * iM;
+      maps[(1 * 3 + c) * plane + p] = -S / D;
+      maps[(2 * 3 + c) * plane + p] = 2.0f * A * iM;
+      ssim_sum += double(S);
+      l1_sum += double(fabsf(s_x[c][oy + kR][ox + kR] - s_y[c][oy + kR][ox + kR]));
+    }
+  }
   const double s_tot = block_sum(ssim_sum, s_red);
   const double l_tot = block_sum(l1_sum, s_red);
   if (tid == 0) {
@@ -178,11 +164,10 @@ __global__ __launch_bounds__(kThreads) void k_l1_ssim(Taps taps, uint32_t width,
   }
 }
 
-// out[0] = loss, out[1] = mean |x - y|, out[2] = mean S: the tiles' sums added in tile order by one workgroup.
-__global__ __launch_bounds__(kThreads) void k_l1_ssim_total(const double* __restrict__ part, uint32_t num_tiles,
-                                                            double inv_n, float lam, float* __restrict__ out) {
-  __shared__ double s_red[kThreads / 64];
-  // fixed assignment of tiles to threads and a fixed reduction tree: the same sum on every run
+// The loss from the tiles' sums (written by k_ssim_maps, so complete when this kernel starts), added in tile order
+// with a fixed reduction tree by one workgroup: out[0] = loss, out[1] = mean |x - y|, out[2] = mean S.
+__device__ __forceinline__ void loss_total(const double* __restrict__ part, uint32_t num_tiles, double inv_n,
+                                           float lam, float* __restrict__ out, double* s_red) {
   double s = 0.0, l = 0.0;
   for (uint32_t t = threadIdx.x; t < num_tiles; t += kThreads) {
     s += part[2 * size_t(t)];
@@ -196,6 +181,96 @@ __global__ __launch_bounds__(kThreads) void k_l1_ssim_total(const double* __rest
     out[1] = float(l1m);
     out[2] = float(sm);
   }
+}
+
+__global__ __launch_bounds__(kThreads) void k_ssim_grad(Taps taps, uint32_t width, uint32_t height, uint32_t tiles_x,
+                                                        float lam, float inv_n, const float4* __restrict__ out_rgba,
+                                                        const float* __restrict__ target,
+                                                        const float* __restrict__ maps, float4* __restrict__ v_out,
+                                                        const double* __restrict__ part, double inv_nd,
+                                                        float* __restrict__ loss) {
+  __shared__ float s_d[9][kP][kP];   // the nine planes on the tile grown by 5 (0 outside the image)
+  __shared__ float s_h[9][kP][kT];   // their horizontal sums
+  __shared__ double s_red[kThreads / 64];
+  const int tid = int(threadIdx.x);
+  if (blockIdx.x == 0) loss_total(part, gridDim.x, inv_nd, lam, loss, s_red);
+  const int tx0 = int(blockIdx.x % tiles_x) * kT, ty0 = int(blockIdx.x / tiles_x) * kT;
+  const int W = int(width), H = int(height);
+  const size_t plane = size_t(W) * H;
+  {
+    float v[kLoads][9];
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it) {
+      const int e = tid + it * int(kThreads);
+      const int r = e / kP, q = e % kP;
+      const int gx = tx0 - kR + q, gy = ty0 - kR + r;
+      const bool in = e < kP * kP && gx >= 0 && gy >= 0 && gx < W && gy < H;
+      const size_t p = in ? size_t(gy) * W + gx : 0;
+#pragma unroll
+      for (int k = 0; k < 9; ++k) v[it][k] = in ? maps[k * plane + p] : 0.0f;
+    }
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it) {
+      const int e = tid + it * int(kThreads);
+      if (e >= kP * kP) break;
+      const int r = e / kP, q = e % kP;
+#pragma unroll
+      for (int k = 0; k < 9; ++k) s_d[k][r][q] = v[it][k];
+    }
+  }
+  __syncthreads();
+  if (tid < kP * (kT / 2)) {  // two neighbouring columns per thread, as in k_ssim_maps
+    const int r = tid % kP, q0 = 2 * (tid / kP);
+    float b[9][2];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) b[k][0] = b[k][1] = 0.0f;
+#pragma unroll
+    for (int j = 0; j <= 2 * kR + 1; ++j) {
+      float v[9];
+#pragma unroll
+      for (int k = 0; k < 9; ++k) v[k] = s_d[k][r][q0 + j];
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+        const int t = j - o;
+        if (t >= 0 && t <= 2 * kR) {
+          const float g = taps.g[t];
+#pragma unroll
+          for (int k = 0; k < 9; ++k) b[k][o] = fmaf(g, v[k], b[k][o]);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      s_h[k][r][q0] = b[k][0];
+      s_h[k][r][q0 + 1] = b[k][1];
+    }
+  }
+  __syncthreads();
+  const int ox = tid % kT, oy = tid / kT;
+  const int px = tx0 + ox, py = ty0 + oy;
+  if (px >= W || py >= H) return;
+  float b[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) b[k] = 0.0f;
+#pragma unroll
+  for (int t = 0; t <= 2 * kR; ++t) {
+    const float g = taps.g[t];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) b[k] = fmaf(g, s_h[k][oy + t][ox], b[k]);
+  }
+  const size_t p = size_t(py) * W + px;
+  const float4 x4 = out_rgba[p];
+  const float xs[3] = {x4.x, x4.y, x4.z};
+  float g[3];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    const float xv = xs[c], yv = target[3 * p + c];
+    const float dssim = fmaf(yv, b[6 + c], fmaf(2.0f * xv, b[3 + c], b[c]));
+    const float diff = xv - yv;
+    const float sgn = diff > 0.0f ? 1.0f : (diff < 0.0f ? -1.0f : 0.0f);
+    g[c] = ((1.0f - lam) * sgn - lam * dssim) * inv_n;
+  }
+  v_out[p] = make_float4(g[0], g[1], g[2], 0.0f);
 }
 
 Taps make_taps() {
@@ -228,12 +303,16 @@ extern "C" gsr_status gsr_loss_l1_ssim(gsr_ctx* ctx, void* stream, uint32_t widt
   gsr_status st = enter(ctx);
   if (st) return st;
   if ((st = grow(ctx, ctx->arena.loss_part, size_t(num_tiles) * 16))) return st;
+  if ((st = grow(ctx, ctx->arena.loss_maps, size_t(width) * height * 9 * sizeof(float)))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   double* part = static_cast<double*>(ctx->arena.loss_part.ptr);
+  float* maps = static_cast<float*>(ctx->arena.loss_maps.ptr);
   const double n = 3.0 * double(width) * double(height);
-  hipLaunchKernelGGL(k_l1_ssim, dim3(uint32_t(num_tiles)), dim3(kThreads), 0, s, make_taps(), width, height,
-                     uint32_t(tiles_x), 0.2f, float(1.0 / n), reinterpret_cast<const float4*>(out_rgba), target,
-                     reinterpret_cast<float4*>(v_out), part);
-  hipLaunchKernelGGL(k_l1_ssim_total, dim3(1), dim3(kThreads), 0, s, part, uint32_t(num_tiles), 1.0 / n, 0.2f, loss);
+  const Taps taps = make_taps();
+  hipLaunchKernelGGL(k_ssim_maps, dim3(uint32_t(num_tiles)), dim3(kThreads), 0, s, taps, width, height,
+                     uint32_t(tiles_x), reinterpret_cast<const float4*>(out_rgba), target, maps, part);
+  hipLaunchKernelGGL(k_ssim_grad, dim3(uint32_t(num_tiles)), dim3(kThreads), 0, s, taps, width, height,
+                     uint32_t(tiles_x), 0.2f, float(1.0 / n), reinterpret_cast<const float4*>(out_rgba), target, maps,
+                     reinterpret_cast<float4*>(v_out), part, 1.0 / n, loss);
   return check_launch(ctx, "gsr_loss_l1_ssim");
 }

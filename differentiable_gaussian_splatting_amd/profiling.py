@@ -32,10 +32,13 @@ KERNEL_SOURCES = {
     "k_adam": ["adam.hip", "gsr_internal.hpp"],
     "k_project_forward": ["project.hip", "gsr_internal.hpp"],
     "k_project_backward": ["project.hip", "gsr_internal.hpp"],
+    "k_ssim_maps": ["loss.hip", "gsr_internal.hpp"],
+    "k_ssim_grad": ["loss.hip", "gsr_internal.hpp"],
 }
 # bench.py stage -> kernel
 STAGE_KERNEL = {"forward": "k_forward", "backward": "k_backward", "adam": "k_adam",
-                "project_forward": "k_project_forward", "project_backward": "k_project_backward"}
+                "project_forward": "k_project_forward", "project_backward": "k_project_backward",
+                "loss_l1_ssim": "k_ssim_maps"}
 CALIB_BYTES = 256 * 1024 * 1024  # read and written by each copy of bench.py --calib-copy
 TRAFFIC_BEGIN, TRAFFIC_END = "<!-- traffic-json", "traffic-json -->"
 

@@ -245,3 +245,14 @@ def make_gaussians(spec: GaussianSpec | str, **overrides) -> GaussianScene:
     return GaussianScene(spec, cam, means.astype(np.float32), log_scales.astype(np.float32),
                          quats.astype(np.float32), raw_op.astype(np.float32), sh.astype(np.float32),
                          grad.astype(np.float32))
+
+
+def make_target(width: int, height: int, seed: int = 21) -> np.ndarray:
+    """A target image [H, W, 3] float32 in [0, 1] for the loss: uniform values averaged over a 5 x 5 box (structure at
+    a few pixels' scale) mixed 4:1 with fresh uniform noise."""
+    rng = np.random.default_rng(seed)
+    base = rng.uniform(0.0, 1.0, (height + 4, width + 4, 3))
+    c = np.cumsum(np.cumsum(np.pad(base, ((1, 0), (1, 0), (0, 0))), axis=0), axis=1)
+    box = (c[5:, 5:] - c[:-5, 5:] - c[5:, :-5] + c[:-5, :-5]) / 25.0
+    t = 0.8 * box + 0.2 * rng.uniform(0.0, 1.0, (height, width, 3))
+    return np.clip(t, 0.0, 1.0).astype(np.float32)
