@@ -117,7 +117,7 @@ void gsr_destroy(gsr_ctx* ctx) {
   Arena& a = ctx->arena;
   for (DevBuf* b : {&a.keys[0], &a.keys[1], &a.vals[0], &a.vals[1], &a.counts, &a.offsets, &a.order, &a.order_alt,
                     &a.order_vals, &a.order_vals_alt, &a.scan_part, &a.hist, &a.digit_tot, &a.ranges, &a.rects,
-                    &a.tile_order_ext, &a.tile_cost, &a.loss_part, &a.loss_maps})
+                    &a.tile_order_ext, &a.tile_cost, &a.loss_part, &a.loss_maps, &a.grad_fixed})
     release(*b);
   if (a.host_total) (void)hipHostFree(a.host_total);
   if (a.done) (void)hipFree(a.done);
@@ -147,6 +147,10 @@ gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value) {
     case GSR_OPT_RASTER_SKIP:
       if (value != 0 && value != 1) return fail(ctx, GSR_EINVAL, "gsr_set_option: raster skip must be 0 or 1");
       ctx->raster_skip = value != 0;
+      return GSR_OK;
+    case GSR_OPT_DETERMINISTIC:
+      if (value != 0 && value != 1) return fail(ctx, GSR_EINVAL, "gsr_set_option: deterministic must be 0 or 1");
+      ctx->deterministic = value != 0;
       return GSR_OK;
     default:
       return fail(ctx, GSR_EINVAL, "gsr_set_option: unknown option %d", int(option));

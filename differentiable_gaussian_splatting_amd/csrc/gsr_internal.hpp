@@ -43,6 +43,7 @@ struct Arena {
   DevBuf tile_cost;   // uint32 [4 tiles] splats each wavefront of the last forward walked (launch-order hint)
   DevBuf loss_part;   // double [2 tiles] per-tile sums of the SSIM map and |x - y| (the loss)
   DevBuf loss_maps;   // float [9][H][W] the SSIM map's three derivatives per channel, between the loss's passes
+  DevBuf grad_fixed;  // the deterministic backward's sums: uint64 [n][9][2] fixed point, then uint32 [n] flags
   uint64_t* host_total = nullptr;  // pinned host word for the one pair-count readback
   uint32_t* done = nullptr;        // last-block-done counter of the count scan (0 between launches)
   hipEvent_t total_ready = nullptr;  // recorded after the readback is queued
@@ -58,6 +59,7 @@ struct gsr_ctx {
   int32_t bin_rule = GSR_BIN_BOX;
   bool bin_keys = true;
   bool raster_skip = true;  // per-wave cull and the backward's all-lanes-rejected skip
+  bool deterministic = false;  // backward sums independent of scheduling (fixed-point atomics)
   uint64_t cost_tiles = 0;  // tile count of the grid tile_cost describes (0: none yet)
   const uint32_t* order_ranges = nullptr;  // the ranges tile_order_ext was last ranked for (by a forward)
   uint64_t order_tiles = 0;

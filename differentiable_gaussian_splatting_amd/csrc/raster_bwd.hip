@@ -110,16 +110,87 @@ __global__ __launch_bounds__(kTilePixels) void k_zero(float* __restrict__ p, uin
 
 // kSkip: each wave walks only the staged splats that can reach alpha >= 1/255 in its 8x8 block, and skips the
 // reduction of a splat no lane composited. Both skip only additions of +0.0 and certain rejects.
-template <bool kSkip>
+// kDet: sums that do not depend on scheduling. Waves 0-1 and waves 2-3 each add into an accumulator of their own:
+// float addition is commutative, so two additions to a zeroed cell give the same bits in either order (three would
+// not); the two accumulators are added at the flush. Each tile's totals are added into 128-bit fixed-point sums
+// (value x 2^48, rounded to nearest) with two 64-bit integer atomics: integer addition is exact, so any order of the
+// tiles gives the same bits. The low word starts at 2^63 (a bias taken off at the end), so the high word is touched
+// only when a running sum passes +-32768. Tile totals that are not finite, or of magnitude 2^79 and up, set bits in
+// a per-splat flag word instead (NaN; +inf; -inf), from which the conversion rebuilds what a float sum would give.
+constexpr double kFixedScale = 0x1p48;
+constexpr unsigned long long kFixedBias = 0x8000000000000000ull;
+
+struct FixedSums {
+  unsigned long long* words;  // [n * 9][2]: low word (biased), high word
+  uint32_t* flags;            // [n]: bit q NaN, bit 9 + q +inf, bit 18 + q -inf, for value q
+};
+
+__device__ __forceinline__ void add_fixed(FixedSums acc, uint32_t idx, uint32_t q, float g) {
+  const double t = double(g) * kFixedScale;  // exact
+  if (!(fabs(t) < 0x1p127)) {
+    const uint32_t bit = g != g ? q : (g > 0.0f ? kGrads + q : 2 * kGrads + q);
+    atomicOr(acc.flags + idx, 1u << bit);
+    return;
+  }
+  __int128 v;
+  if (fabs(t) < 0x1p62) {
+    v = __double2ll_rn(t);
+  } else {  // an integer m 2^(e - 53) with |m| < 2^53 and e - 53 in [10, 74]
+    int e;
+    const double f = frexp(t, &e);
+    v = static_cast<__int128>(static_cast<long long>(f * 0x1p53)) << (e - 53);
+  }
+  const unsigned long long lo = static_cast<unsigned long long>(v);
+  const long long hi = static_cast<long long>(v >> 64);
+  unsigned long long* word = acc.words + 2 * (size_t(idx) * kGrads + q);
+  const unsigned long long old = atomicAdd(word, lo);
+  const long long carry_hi = hi + (old + lo < old ? 1 : 0);  // the low word wrapped: carry into the high word
+  if (carry_hi != 0) atomicAdd(word + 1, static_cast<unsigned long long>(carry_hi));
+}
+
+__global__ __launch_bounds__(kTilePixels) void k_fixed_clear(FixedSums acc, uint64_t count, uint32_t n) {
+  const uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < count) {
+    acc.words[2 * i] = kFixedBias;
+    acc.words[2 * i + 1] = 0;
+  }
+  if (i < n) acc.flags[i] = 0;
+}
+
+__global__ __launch_bounds__(kTilePixels) void k_fixed_to_float(FixedSums acc, float* __restrict__ out,
+                                                                uint64_t count) {
+  const uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  const uint32_t idx = uint32_t(i / kGrads), q = uint32_t(i - uint64_t(idx) * kGrads);
+  const uint32_t fl = acc.flags[idx];
+  const bool nan = (fl >> q) & 1u, pinf = (fl >> (kGrads + q)) & 1u, ninf = (fl >> (2 * kGrads + q)) & 1u;
+  float r;
+  if (nan || (pinf && ninf)) {
+    r = __builtin_nanf("");
+  } else if (pinf || ninf) {
+    r = pinf ? __builtin_inff() : -__builtin_inff();
+  } else {
+    const long long lo = static_cast<long long>(acc.words[2 * i] ^ kFixedBias);  // the sum is hi 2^64 + lo
+    const long long hi = static_cast<long long>(acc.words[2 * i + 1]);
+    if (hi == 0)
+      r = static_cast<float>(lo) * float(1.0 / kFixedScale);  // one rounding; the scaling is exact
+    else
+      r = float((double(hi) * 0x1p64 + double(lo)) * (1.0 / kFixedScale));
+  }
+  out[i] = r;
+}
+
+template <bool kSkip, bool kDet>
 __global__ __launch_bounds__(kTilePixels) void k_backward(
     const float* __restrict__ splats, uint32_t n, const uint32_t* __restrict__ vals,
     const uint32_t* __restrict__ ranges, uint32_t num_pairs, uint32_t tiles_x, uint32_t width, uint32_t height,
     const float4* __restrict__ out_rgba, const uint32_t* __restrict__ last_contrib, const float4* __restrict__ v_out,
-    float* __restrict__ splats_grad, const uint32_t* __restrict__ tile_order, uint32_t num_tiles) {
+    float* __restrict__ splats_grad, FixedSums fixed, const uint32_t* __restrict__ tile_order, uint32_t num_tiles) {
   constexpr uint32_t kWaves = kTilePixels / kWave;
   __shared__ StagedSplat s_sp[kTilePixels];
   __shared__ double s_exp2[64];  // 2^(j/32) table of the exact exponential
-  __shared__ float s_acc[kTilePixels][kGrads];
+  constexpr uint32_t kAcc = kDet ? 2 : 1;  // accumulators: one per pair of waves, or one for all four
+  __shared__ float s_acc[kAcc][kTilePixels][kGrads];
   __shared__ uint64_t s_mask[kWaves][kWaves];  // [reading wave][staging wave]
   __shared__ uint32_t s_max_last;
   const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
@@ -155,7 +226,9 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
   const bool wave_g_finite = __builtin_amdgcn_readfirstlane(uint32_t(__ballot(!g_finite) == 0)) != 0;
   if (tid == 0) s_max_last = 0;
 #pragma unroll
-  for (uint32_t q = 0; q < kGrads; ++q) s_acc[tid][q] = 0.0f;
+  for (uint32_t a = 0; a < kAcc; ++a)
+#pragma unroll
+    for (uint32_t q = 0; q < kGrads; ++q) s_acc[a][tid][q] = 0.0f;
   // the wave's bound: the largest last contributor among its lanes
   uint32_t wave_last = last;
   for (uint32_t off = 32; off > 0; off >>= 1) wave_last = max(wave_last, uint32_t(__shfl_xor(int(wave_last), off)));
@@ -245,7 +318,7 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
         T = T * one_m;
         // Wave totals of the 9 terms; nine lanes add them to the LDS accumulator (distinct addresses).
         const float x = transpose_reduce(d, lane);
-        if (my_slot >= 0) atomicAdd(&s_acc[j][my_slot], x);
+        if (my_slot >= 0) atomicAdd(&s_acc[kDet ? w >> 1 : 0][j][my_slot], x);
       }
     }
     lds_barrier();
@@ -254,7 +327,11 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
     // dL/d(a, b, c) = -o (S2 / 2, S3, S4 / 2). A splat no pixel composited keeps its zeros whatever its values.
     const uint32_t staged = min(kTilePixels, stop - b0);
     if (tid < staged) {
-      float* acc = s_acc[tid];
+      float* acc = s_acc[0][tid];
+      if constexpr (kDet) {
+#pragma unroll
+        for (uint32_t q = 0; q < kGrads; ++q) acc[q] += s_acc[1][tid][q];
+      }
       const float s0 = acc[0], s1 = acc[1], s2 = acc[2], s3 = acc[3], s4 = acc[4];
       if (s0 != 0.0f || s1 != 0.0f || s2 != 0.0f || s3 != 0.0f || s4 != 0.0f) {
         const StagedSplat& sp = s_sp[tid];
@@ -271,10 +348,16 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
     // add to the consecutive values of about seven splats (a few cache lines) rather than to 64 scattered records.
     for (uint32_t f = tid; f < staged * kGrads; f += kTilePixels) {
       const uint32_t slot = f / kGrads, q = f - slot * kGrads;
-      const float g = (&s_acc[0][0])[f];
-      (&s_acc[0][0])[f] = 0.0f;
+      const float g = (&s_acc[0][0][0])[f];
+#pragma unroll
+      for (uint32_t a = 0; a < kAcc; ++a) (&s_acc[a][0][0])[f] = 0.0f;
       const uint32_t idx = s_sp[slot].idx;
-      if (idx != 0xFFFFFFFFu && (!kSkip || g != 0.0f)) atomicAdd(splats_grad + size_t(idx) * kGrads + q, g);
+      if (idx != 0xFFFFFFFFu && (!kSkip || g != 0.0f)) {
+        if constexpr (kDet)
+          add_fixed(fixed, idx, q, g);
+        else
+          atomicAdd(splats_grad + size_t(idx) * kGrads + q, g);
+      }
     }
     lds_barrier();
   }
@@ -313,15 +396,25 @@ extern "C" gsr_status gsr_render_backward(gsr_ctx* ctx, void* stream, const floa
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint64_t count = uint64_t(n) * kGrads;
-  if (count)
-    hipLaunchKernelGGL(k_zero, dim3(uint32_t((count + kTilePixels - 1) / kTilePixels)), dim3(kTilePixels), 0, s,
-                       splats_grad, count);
+  const bool det = ctx->deterministic && count;
+  FixedSums fixed{nullptr, nullptr};
+  const dim3 value_grid(uint32_t((count + kTilePixels - 1) / kTilePixels));
+  if (det) {
+    if ((st = grow(ctx, ctx->arena.grad_fixed, size_t(count) * 16 + size_t(n) * 4))) return st;
+    fixed.words = static_cast<unsigned long long*>(ctx->arena.grad_fixed.ptr);
+    fixed.flags = reinterpret_cast<uint32_t*>(fixed.words + 2 * count);
+    hipLaunchKernelGGL(k_fixed_clear, value_grid, dim3(kTilePixels), 0, s, fixed, count, n);
+  } else if (count) {
+    hipLaunchKernelGGL(k_zero, value_grid, dim3(kTilePixels), 0, s, splats_grad, count);
+  }
   const uint32_t* order = raster_tile_order(ctx, s, bins, true, &st);
   if (!order) return st;
-  auto kernel = ctx->raster_skip ? k_backward<true> : k_backward<false>;
+  auto kernel = ctx->raster_skip ? (det ? k_backward<true, true> : k_backward<true, false>)
+                                 : (det ? k_backward<false, true> : k_backward<false, false>);
   hipLaunchKernelGGL(kernel, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, s, splats, n, bins->vals,
                      bins->ranges, bins->num_pairs, tiles_x, width, height,
                      reinterpret_cast<const float4*>(out_rgba), last_contrib, reinterpret_cast<const float4*>(v_out),
-                     splats_grad, order, uint32_t(num_tiles));
+                     splats_grad, fixed, order, uint32_t(num_tiles));
+  if (det) hipLaunchKernelGGL(k_fixed_to_float, value_grid, dim3(kTilePixels), 0, s, fixed, splats_grad, count);
   return check_launch(ctx, "gsr_render_backward");
 }

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libgsr.so")
 GSR_OK, GSR_EINVAL, GSR_ENOMEM, GSR_EHIP, GSR_EOVERFLOW = 0, -1, -2, -3, -4
 GSR_OPT_BIN_SCHEME, GSR_BIN_PRESORT, GSR_BIN_KEY64, GSR_OPT_BIN_KEYS, GSR_OPT_RASTER_SKIP = 1, 0, 1, 2, 3
 GSR_OPT_BIN_RULE, GSR_BIN_BOX, GSR_BIN_ELLIPSE = 4, 0, 1
+GSR_OPT_DETERMINISTIC = 5
 GSR_ADAM_MAX_GROUPS = 8
 _STATUS = {GSR_EINVAL: "GSR_EINVAL", GSR_ENOMEM: "GSR_ENOMEM", GSR_EHIP: "GSR_EHIP", GSR_EOVERFLOW: "GSR_EOVERFLOW"}
 

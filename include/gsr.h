@@ -77,6 +77,15 @@ gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats);
                              /*   (p - mean)^T [[a b][b c]] (p - mean) <= 9 meets, decided in fp32 from the       */
                              /*   minimum of the quadratic over the square (0 if the mean is inside, else the     */
                              /*   least edge minimum at the clamped vertex)                                       */
+#define GSR_OPT_DETERMINISTIC 5 /* 0 (default): the backward adds its per-tile sums with float atomics, so the     */
+                              /*   last bits of splats_grad depend on scheduling; 1: the same bits on every run.   */
+                              /*   Each wavefront keeps its own per-batch sums (added in wavefront order), and the */
+                              /*   tiles' totals are summed exactly as 128-bit fixed-point integers (each rounded  */
+                              /*   to a multiple of 2^-48) and rounded to float once. A non-finite tile total, or  */
+                              /*   one of magnitude 2^79 or more, gives NaN or +-inf as a float sum would. Costs an */
+                              /*   arena buffer of 148 bytes per splat and some of the backward's speed. (The     */
+                              /*   per-splat backward page shrinks, but does not remove, the run-to-run noise by  */
+                              /*   changing the loop order; its determinism note.)                                */
 gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value);
 
 /* Views into the context's arena, valid until the next gsr_bin or gsr_reserve on the same context. A caller may

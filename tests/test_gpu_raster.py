@@ -145,14 +145,21 @@ def test_backward_ragged_images(ctx, w, h):
     assert ok, (worst, at)
 
 
-def test_backward_nan_upstream_gradient_stays_with_its_pixel(ctx):
+def set_det(ctx, on: bool):
+    from differentiable_gaussian_splatting_amd import gsr
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_DETERMINISTIC, 1 if on else 0)
+
+
+@pytest.mark.parametrize("det", [False, True])
+def test_backward_nan_upstream_gradient_stays_with_its_pixel(ctx, det):
     """Pixels with a NaN upstream gradient give NaN terms to the splats they composite and nothing to the others:
     the positions of NaN gradients equal the oracle's and every other gradient is within tolerance. (A wave that
-    holds such a pixel takes the kernel's guarded form of the colour terms.)"""
+    holds such a pixel takes the kernel's guarded form of the colour terms; the deterministic sums carry NaN in
+    their flag words.)"""
     import oracle
     from differentiable_gaussian_splatting_amd import gsr
     w, h = 64, 48
-    banner(f"backward NaN upstream gradient {w}x{h}")
+    banner(f"backward NaN upstream gradient {w}x{h} deterministic={det}")
     sc = custom_scene(name="nanv", width=w, height=h, n=600, seed=77,
                       size_classes=((0.7, 0.3, 4.0), (0.3, 4.0, 20.0)), opacity_mu=0.5, vout_sd=0.1, margin=10.0)
     v_out = sc.v_out.copy()
@@ -165,7 +172,11 @@ def test_backward_nan_upstream_gradient_stays_with_its_pixel(ctx):
     sp = dev(sc.splats)
     bins = gsr.gsr_bin(ctx, sp, dev(sc.depths), w, h)
     out, ft, lc = run_forward(ctx, sp, bins, w, h)
-    g = host(run_backward(ctx, sc, bins, out, ft, lc, v_out))
+    set_det(ctx, det)
+    try:
+        g = host(run_backward(ctx, sc, bins, out, ft, lc, v_out))
+    finally:
+        set_det(ctx, False)
     nan_ref, nan_gpu = np.isnan(ref), np.isnan(g)
     assert nan_ref.any(), "the case must put NaN into some gradients"
     assert np.array_equal(nan_gpu, nan_ref), np.argwhere(nan_gpu != nan_ref)[:5].tolist()
@@ -265,6 +276,58 @@ def test_backward_self_noise_is_within_tolerance(ctx):
     for r in runs[1:]:
         ok, worst, _ = grads_close(r, runs[0].astype(np.float64))
         assert ok and worst < 0.5, worst
+
+
+@pytest.mark.parametrize("name", ["tiny", "raster84k", "raster410k"])
+def test_deterministic_backward_matches_oracle_and_repeats(ctx, name):
+    """With the deterministic option the gradients meet the oracle bar and are the same bits on every run, and with
+    the skips on or off (the skips drop only +-0.0 terms, which leave an exact sum unchanged)."""
+    from differentiable_gaussian_splatting_amd import gsr
+    banner(f"deterministic backward {name}")
+    sc = scene(name)
+    sp = dev(sc.splats)
+    bins = gsr.gsr_bin(ctx, sp, dev(sc.depths), sc.width, sc.height)
+    out, ft, lc = run_forward(ctx, sp, bins, sc.width, sc.height)
+    set_det(ctx, True)
+    try:
+        runs = [host(run_backward(ctx, sc, bins, out, ft, lc)) for _ in range(3)]
+        set_skip(ctx, False)
+        runs.append(host(run_backward(ctx, sc, bins, out, ft, lc)))
+    finally:
+        set_skip(ctx, True)
+        set_det(ctx, False)
+    for r in runs[1:]:
+        assert r.tobytes() == runs[0].tobytes(), np.argwhere(r != runs[0])[:5].tolist()
+    ok, worst, at = grads_close(runs[0], oracle_backward(name))
+    print(f"  worst |gpu-ref| / (1e-4 + 1e-4 |ref|) = {worst:.3g} at {at}")
+    assert ok, (worst, at)
+
+
+@pytest.mark.parametrize("scale", [1e-7, 1e5])
+def test_deterministic_backward_at_small_and_large_gradient_scales(ctx, scale):
+    """Upstream gradients scaled by 1e-7 (the size of a mean loss's per-pixel gradient over a large image) and by 1e5
+    (sums far past +-32768, so the high words carry): the relative bar of the oracle comparison still holds, with
+    the absolute part scaled alike, so the fixed-point resolution costs no relative accuracy at either end."""
+    import oracle
+    from differentiable_gaussian_splatting_amd import gsr
+    banner(f"deterministic backward, upstream scale {scale:g}")
+    sc = scene("tiny")
+    v = (sc.v_out.astype(np.float64) * scale).astype(np.float32)
+    r_out, r_ft, r_lc, _ = oracle_forward("tiny")
+    ref = oracle.render_backward(sc.splats, oracle_bins("tiny"), 64, 64, r_out, r_ft, r_lc, v)
+    sp = dev(sc.splats)
+    bins = gsr.gsr_bin(ctx, sp, dev(sc.depths), 64, 64)
+    out, ft, lc = run_forward(ctx, sp, bins, 64, 64)
+    set_det(ctx, True)
+    try:
+        g = host(run_backward(ctx, sc, bins, out, ft, lc, v)).astype(np.float64)
+    finally:
+        set_det(ctx, False)
+    if scale > 1:
+        assert np.abs(ref).max() > 32768
+    err = np.abs(g - ref) / (1e-4 * scale + 1e-4 * np.abs(ref))
+    print(f"  worst error / bound {err.max():.3g}")
+    assert err.max() <= 1.0, np.unravel_index(np.argmax(err), err.shape)
 
 
 def test_raster_on_ellipse_bins_matches_oracle(ctx):
