@@ -205,6 +205,8 @@ def main():
                        for i, nm in enumerate(names)}
     P = b.num_pairs
     e_bwd_gpu = int(last_contrib.to(torch.int64).sum().item())
+    det = bench_deterministic_backward(args, ctx, gsr, torch, np, stream, splats, b, W, H, out_rgba, final_T,
+                                       last_contrib, v_out, grad)
 
     # CPU baseline leg (rank 0, N = 1): the oracle on one whole step of the same input; its exact counts
     cpu = None
@@ -226,6 +228,8 @@ def main():
     result["stage_ms"] = stage_ms
     result["stage_ms_median"] = stage_ms_median
     result["fwd_bwd_ms"] = stage_ms["forward"] + stage_ms["backward"]
+    det["ratio_to_default"] = det["ms"] / stage_ms["backward"]
+    result["deterministic_backward"] = det
     if cpu is not None:
         fs, bs = cpu["fwd_stats"], cpu["bwd_stats"]
         e_fwd, e_bwd = fs["visited"], bs["visited"]
@@ -281,6 +285,32 @@ def main():
     result["projection"] = bench_projection(args, ctx, gsr, scenes, sc, hp=hp, bc=bc)
     print(json.dumps(result), flush=True)
     ctx.close()
+
+
+def bench_deterministic_backward(args, ctx, gsr, torch, np, stream, splats, b, W, H, out_rgba, final_T, last_contrib,
+                                 v_out, grad):
+    """The backward with GSR_OPT_DETERMINISTIC on the last step's bins and image, timed like the step's stages
+    (outside the step's timed region); a second run checks that the gradients repeat bit for bit, and the largest
+    difference from the default mode's gradients is reported."""
+    ref = grad.clone()
+    g = [torch.empty_like(grad), torch.empty_like(grad)]
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_DETERMINISTIC, 1)
+    try:
+        gsr.gsr_render_backward(ctx, splats, b, W, H, out_rgba, final_T, last_contrib, v_out, g[0])
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            ev[k][0].record(stream)
+            gsr.gsr_render_backward(ctx, splats, b, W, H, out_rgba, final_T, last_contrib, v_out, g[1])
+            ev[k][1].record(stream)
+        torch.cuda.synchronize()
+    finally:
+        gsr.gsr_set_option(ctx, gsr.GSR_OPT_DETERMINISTIC, 0)
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    same = bool(torch.equal(g[0].view(torch.int32), g[1].view(torch.int32)))
+    dev = ((g[0] - ref).abs() / (1e-4 + 1e-4 * ref.abs())).max().item()
+    return {"ms": ms, "repeats_bit_identical": same,
+            "max_diff_to_default_in_units_of_1e-4_abs_plus_rel": dev}
 
 
 def bench_projection(args, ctx, gsr, scenes, sc, hp, bc):
@@ -370,10 +400,44 @@ def bench_projection(args, ctx, gsr, scenes, sc, hp, bc):
                              "unit": "TFLOP/s", "work_per_launch": loss_ops,
                              "traffic": profiling.traffic_for(profiling.STAGE_KERNEL["loss_l1_ssim"], traffic_md)}
     roofs["loss_l1_ssim"]["frac"] = roofs["loss_l1_ssim"]["achieved"] / ALU_PEAK_TFLOPS
+
+    # Visible-only Adam against the dense step, with the visibility of this view (b, the last iteration's bins) and
+    # of the same camera panned by half the image width (its principal point moved by W / 2), which sees part of
+    # the Gaussians; algorithmic bytes = 28 per element of a visible splat + 4 per splat for its pair count
+    def time_adam(visible):
+        ae = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for k in range(reps):
+            ae[k][0].record(stream)
+            if visible is None:
+                gsr.gsr_adam_step(ctx, adam, hp["beta1"], hp["beta2"], hp["eps"], *bc)
+            else:
+                gsr.gsr_adam_step_visible(ctx, adam, hp["beta1"], hp["beta2"], hp["eps"], *bc, visible, n)
+            ae[k][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in ae]))
+
+    dense_ms = time_adam(None)
+    sparse = {"dense_ms": dense_ms, "dense_bytes": 28 * 59 * n}
+    pan = gsr.camera(g3.camera["R"], g3.camera["tv"], g3.camera["fx"], g3.camera["fy"], g3.camera["cx"] + W / 2,
+                     g3.camera["cy"], g3.camera["near"])
+    for view, c in (("this_view", None), ("panned_half_width", pan)):
+        if c is None:
+            vb = b
+        else:
+            sp2, dp2 = gsr.gsr_project_forward(ctx, c, *ps)
+            vb = gsr.gsr_bin(ctx, sp2, dp2, W, H)
+        nvis = int((gsr.gsr_bins_splat_pairs(ctx, vb) != 0).sum().item())
+        ms = time_adam(vb)
+        by = 28 * 59 * nvis + 4 * n
+        ach = by / (ms * 1e-3) / 1e9
+        sparse[view] = {"visible_fraction": nvis / n, "ms": ms, "speedup_vs_dense": dense_ms / ms,
+                        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": ach / HBM_PEAK_GBS, "work_per_launch": by}}
     out_d = {"workload": f"gauss410k: {n} 3D Gaussians (means, log_scales, quats, raw_opacities, SH degree 3) seen "
                          f"by an {W}x{H} pinhole camera, projected sizes as the path's workload",
              "forward_ms": f_ms, "backward_ms": b_ms, "loss_ms": l_ms, "rooflines": roofs,
              "iteration_ms": it_ms, "iteration_pairs": b.num_pairs, "iteration_loss": loss_after,
+             "adam_visible_only": sparse,
              "iteration": "project + bin + forward + L1/SSIM loss + backward + project backward + Adam on the 5 "
                           "groups"}
     if not args.no_cpu_baseline:

@@ -677,5 +677,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   out->num_pairs = uint32_t(P);
   out->tiles_x = tiles_x;
   out->tiles_y = tiles_y;
+  out->splat_pairs = n ? counts : nullptr;
+  out->num_splats = n;
   return GSR_OK;
 }

@@ -185,7 +185,7 @@ gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats) {
 }
 
 gsr_status gsr_bins_copy(gsr_ctx* ctx, void* stream, const gsr_bins* bins, uint64_t* keys, uint32_t* vals,
-                         uint32_t* ranges) {
+                         uint32_t* ranges, uint32_t* splat_pairs) {
   if (!ctx || !bins) return GSR_EINVAL;
   gsr_status st = enter(ctx);
   if (st) return st;
@@ -204,6 +204,12 @@ gsr_status gsr_bins_copy(gsr_ctx* ctx, void* stream, const gsr_bins* bins, uint6
   if (ranges && T) {
     hipError_t e = hipMemcpyAsync(ranges, bins->ranges, T * 8, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "gsr_bins_copy ranges");
+  }
+  if (splat_pairs && bins->num_splats) {
+    if (!bins->splat_pairs) return fail(ctx, GSR_EINVAL, "gsr_bins_copy: the bins carry no splat_pairs");
+    hipError_t e = hipMemcpyAsync(splat_pairs, bins->splat_pairs, size_t(bins->num_splats) * 4,
+                                  hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "gsr_bins_copy splat_pairs");
   }
   return GSR_OK;
 }

@@ -180,12 +180,18 @@ __global__ __launch_bounds__(kTilePixels) void k_fixed_to_float(FixedSums acc, f
   out[i] = r;
 }
 
+#define GSR_BACKWARD_PARAMS                                                                                        \
+  const float *__restrict__ splats, uint32_t n, const uint32_t *__restrict__ vals,                                  \
+      const uint32_t *__restrict__ ranges, uint32_t num_pairs, uint32_t tiles_x, uint32_t width, uint32_t height,   \
+      const float4 *__restrict__ out_rgba, const uint32_t *__restrict__ last_contrib,                               \
+      const float4 *__restrict__ v_out, float *__restrict__ splats_grad, FixedSums fixed,                           \
+      const uint32_t *__restrict__ tile_order, uint32_t num_tiles
+#define GSR_BACKWARD_ARGS \
+  splats, n, vals, ranges, num_pairs, tiles_x, width, height, out_rgba, last_contrib, v_out, splats_grad, fixed, \
+      tile_order, num_tiles
+
 template <bool kSkip, bool kDet>
-__global__ __launch_bounds__(kTilePixels) void k_backward(
-    const float* __restrict__ splats, uint32_t n, const uint32_t* __restrict__ vals,
-    const uint32_t* __restrict__ ranges, uint32_t num_pairs, uint32_t tiles_x, uint32_t width, uint32_t height,
-    const float4* __restrict__ out_rgba, const uint32_t* __restrict__ last_contrib, const float4* __restrict__ v_out,
-    float* __restrict__ splats_grad, FixedSums fixed, const uint32_t* __restrict__ tile_order, uint32_t num_tiles) {
+__device__ __forceinline__ void backward_tile(GSR_BACKWARD_PARAMS) {
   constexpr uint32_t kWaves = kTilePixels / kWave;
   __shared__ StagedSplat s_sp[kTilePixels];
   __shared__ double s_exp2[64];  // 2^(j/32) table of the exact exponential
@@ -368,6 +374,17 @@ __global__ __launch_bounds__(kTilePixels) void k_backward(
     batches(std::true_type{});
 }
 
+// One block per 16x16 tile; the deterministic form under a name of its own, so that profiles keep the two apart.
+template <bool kSkip>
+__global__ __launch_bounds__(kTilePixels) void k_backward(GSR_BACKWARD_PARAMS) {
+  backward_tile<kSkip, false>(GSR_BACKWARD_ARGS);
+}
+
+template <bool kSkip>
+__global__ __launch_bounds__(kTilePixels) void k_backward_det(GSR_BACKWARD_PARAMS) {
+  backward_tile<kSkip, true>(GSR_BACKWARD_ARGS);
+}
+
 }  // namespace
 }  // namespace gsr
 
@@ -409,8 +426,8 @@ extern "C" gsr_status gsr_render_backward(gsr_ctx* ctx, void* stream, const floa
   }
   const uint32_t* order = raster_tile_order(ctx, s, bins, true, &st);
   if (!order) return st;
-  auto kernel = ctx->raster_skip ? (det ? k_backward<true, true> : k_backward<true, false>)
-                                 : (det ? k_backward<false, true> : k_backward<false, false>);
+  auto kernel = ctx->raster_skip ? (det ? k_backward_det<true> : k_backward<true>)
+                                 : (det ? k_backward_det<false> : k_backward<false>);
   hipLaunchKernelGGL(kernel, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, s, splats, n, bins->vals,
                      bins->ranges, bins->num_pairs, tiles_x, width, height,
                      reinterpret_cast<const float4*>(out_rgba), last_contrib, reinterpret_cast<const float4*>(v_out),

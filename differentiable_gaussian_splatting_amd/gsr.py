@@ -33,7 +33,8 @@ class GsrError(RuntimeError):
 
 class gsr_bins(ctypes.Structure):
     _fields_ = [("keys", ctypes.c_void_p), ("vals", ctypes.c_void_p), ("ranges", ctypes.c_void_p),
-                ("num_pairs", ctypes.c_uint32), ("tiles_x", ctypes.c_uint32), ("tiles_y", ctypes.c_uint32)]
+                ("num_pairs", ctypes.c_uint32), ("tiles_x", ctypes.c_uint32), ("tiles_y", ctypes.c_uint32),
+                ("splat_pairs", ctypes.c_void_p), ("num_splats", ctypes.c_uint32)]
 
 
 class gsr_adam_group(ctypes.Structure):
@@ -64,12 +65,13 @@ SIGNATURES = {
     "gsr_reserve": (_I32, [_P, _U64, _U32]),
     "gsr_set_option": (_I32, [_P, _I32, _I64]),
     "gsr_bin": (_I32, [_P, _P, _P, _P, _U32, _U32, _U32, ctypes.POINTER(gsr_bins)]),
-    "gsr_bins_copy": (_I32, [_P, _P, ctypes.POINTER(gsr_bins), _P, _P, _P]),
+    "gsr_bins_copy": (_I32, [_P, _P, ctypes.POINTER(gsr_bins), _P, _P, _P, _P]),
     "gsr_radix_sort": (_I32, [_P, _P, _P, _P, _U64, _U32, _P, _P]),
     "gsr_radix_pass_count": (_U32, [_U64, _U32]),
     "gsr_render_forward": (_I32, [_P, _P, _P, _U32, ctypes.POINTER(gsr_bins), _U32, _U32, _P, _P, _P]),
     "gsr_render_backward": (_I32, [_P, _P, _P, _U32, ctypes.POINTER(gsr_bins), _U32, _U32, _P, _P, _P, _P, _P]),
     "gsr_adam_step": (_I32, [_P, _P, ctypes.POINTER(gsr_adam_group), _U32, _F, _F, _F, _F, _F]),
+    "gsr_adam_step_visible": (_I32, [_P, _P, ctypes.POINTER(gsr_adam_group), _U32, _F, _F, _F, _F, _F, _P, _U32]),
     "gsr_project_forward": (_I32, [_P, _P, ctypes.POINTER(gsr_camera), _U32, _P, _P, _P, _P, _P, _P, _P]),
     "gsr_project_backward": (_I32, [_P, _P, ctypes.POINTER(gsr_camera), _U32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _P]),
@@ -198,7 +200,7 @@ def bins_from_tensors(keys: torch.Tensor | None, vals: torch.Tensor, ranges: tor
     _need(ranges, "ranges", (torch.int32,), 2 * tx * ty)
     if keys is not None:
         _need(keys, "keys", (torch.int64,), vals.numel())
-    raw = gsr_bins(_ptr(keys), _ptr(vals), _ptr(ranges), vals.numel(), tx, ty)
+    raw = gsr_bins(_ptr(keys), _ptr(vals), _ptr(ranges), vals.numel(), tx, ty, None, 0)
     return Bins(raw, (keys, vals, ranges))
 
 
@@ -211,8 +213,16 @@ def gsr_bins_copy(ctx: Context, bins: Bins, stream=None):
     vals = torch.empty(P, dtype=torch.int32, device=dev)
     ranges = torch.empty((T, 2), dtype=torch.int32, device=dev)
     ctx.check(load().gsr_bins_copy(ctx.handle, _stream(stream), ctypes.byref(bins.raw), _ptr(keys), _ptr(vals),
-                                   _ptr(ranges)), "gsr_bins_copy")
+                                   _ptr(ranges), None), "gsr_bins_copy")
     return keys, vals, ranges
+
+
+def gsr_bins_splat_pairs(ctx: Context, bins: Bins, stream=None) -> torch.Tensor:
+    """The number of pairs each splat emitted, copied into a new int32 tensor [num_splats]."""
+    out = torch.empty(int(bins.raw.num_splats), dtype=torch.int32, device=ctx.device)
+    ctx.check(load().gsr_bins_copy(ctx.handle, _stream(stream), ctypes.byref(bins.raw), None, None, None,
+                                   _ptr(out)), "gsr_bins_copy")
+    return out
 
 
 def gsr_radix_sort(ctx: Context, keys: torch.Tensor, vals: torch.Tensor, key_bits: int = 64, stream=None):
@@ -271,6 +281,31 @@ def gsr_render_backward(ctx: Context, splats: torch.Tensor, bins: Bins, width: i
 def gsr_adam_step(ctx: Context, groups, beta1: float, beta2: float, eps: float, bc1: float, bc2: float,
                   stream=None):
     """groups: sequence of (param, grad, m, v, lr) float32 device tensors of equal sizes; updated in place."""
+    arr = _adam_groups(ctx, groups)
+    ctx.check(load().gsr_adam_step(ctx.handle, _stream(stream), arr, len(groups), beta1, beta2, eps, bc1, bc2),
+              "gsr_adam_step")
+
+
+def gsr_adam_step_visible(ctx: Context, groups, beta1: float, beta2: float, eps: float, bc1: float, bc2: float,
+                          visible, n: int | None = None, stream=None):
+    """gsr_adam_step for the splats with a non-zero entry in `visible` only: a Bins (its splat_pairs, with n given)
+    or an int32 device tensor [n]. Each group holds n splats' elements, consecutive per splat."""
+    if isinstance(visible, Bins):
+        if n is None:
+            raise ValueError("n is needed with a Bins")
+        ptr = visible.raw.splat_pairs if n else None
+        if n and not ptr:
+            raise ValueError("these bins carry no splat_pairs")
+    else:
+        n = visible.numel() if n is None else n
+        _need(visible, "visible", (torch.int32,), n, ctx.device)
+        ptr = _ptr(visible)
+    arr = _adam_groups(ctx, groups)
+    ctx.check(load().gsr_adam_step_visible(ctx.handle, _stream(stream), arr, len(groups), beta1, beta2, eps, bc1,
+                                           bc2, ptr, n), "gsr_adam_step_visible")
+
+
+def _adam_groups(ctx: Context, groups):
     if len(groups) > GSR_ADAM_MAX_GROUPS:
         raise ValueError(f"at most {GSR_ADAM_MAX_GROUPS} groups")
     arr = (gsr_adam_group * max(1, len(groups)))()
@@ -279,8 +314,7 @@ def gsr_adam_step(ctx: Context, groups, beta1: float, beta2: float, eps: float, 
         for t, name in ((p, "param"), (g, "grad"), (m, "m"), (v, "v")):
             _need(t, f"group {q} {name}", (torch.float32,), k, ctx.device)
         arr[q] = gsr_adam_group(_ptr(p), _ptr(g), _ptr(m), _ptr(v), k, lr)
-    ctx.check(load().gsr_adam_step(ctx.handle, _stream(stream), arr, len(groups), beta1, beta2, eps, bc1, bc2),
-              "gsr_adam_step")
+    return arr
 
 
 _PARAM_WIDTHS = (("means", 3), ("log_scales", 3), ("quats", 4), ("raw_opacities", 1), ("sh", 48))

@@ -29,6 +29,7 @@ CSRC = os.path.join(HERE, "csrc")
 KERNEL_SOURCES = {
     "k_forward": ["raster_fwd.hip", "raster_common.hpp", "gsr_internal.hpp"],
     "k_backward": ["raster_bwd.hip", "raster_common.hpp", "gsr_internal.hpp"],
+    "k_backward_det": ["raster_bwd.hip", "raster_common.hpp", "gsr_internal.hpp"],
     "k_adam": ["adam.hip", "gsr_internal.hpp"],
     "k_project_forward": ["project.hip", "gsr_internal.hpp"],
     "k_project_backward": ["project.hip", "gsr_internal.hpp"],
@@ -36,7 +37,8 @@ KERNEL_SOURCES = {
     "k_ssim_grad": ["loss.hip", "gsr_internal.hpp"],
 }
 # bench.py stage -> kernel
-STAGE_KERNEL = {"forward": "k_forward", "backward": "k_backward", "adam": "k_adam",
+STAGE_KERNEL = {"forward": "k_forward", "backward": "k_backward", "backward_deterministic": "k_backward_det",
+                "adam": "k_adam",
                 "project_forward": "k_project_forward", "project_backward": "k_project_backward",
                 "loss_l1_ssim": "k_ssim_maps"}
 CALIB_BYTES = 256 * 1024 * 1024  # read and written by each copy of bench.py --calib-copy

@@ -4,7 +4,8 @@
  *   gsr_bin             (tile | depth) keys per splat-tile overlap, a stable LSD radix sort, per-tile ranges
  *   gsr_render_forward  per-pixel front-to-back alpha compositing over each 16x16 tile's depth-sorted splats
  *   gsr_render_backward the 9 per-splat 2D gradients of that compositing
- *   gsr_adam_step       one fused Adam step over every parameter group
+ *   gsr_adam_step       one fused Adam step over every parameter group (gsr_adam_step_visible: only the splats
+ *                       binned in the view)
  * and, on either side of it, the projection of 3D Gaussians to those splats and the projection's backward pass
  * (gsr_project_forward / gsr_project_backward), and the L1 + SSIM loss that gives the backward its v_out
  * (gsr_loss_l1_ssim).
@@ -97,6 +98,8 @@ typedef struct gsr_bins {
   uint32_t num_pairs;
   uint32_t tiles_x;
   uint32_t tiles_y;
+  const uint32_t* splat_pairs; /* [num_splats] pairs of each splat (0: not binned), or NULL; filled by gsr_bin   */
+  uint32_t num_splats;
 } gsr_bins;
 
 /* Binning. For every splat that passes the validity test, one pair per 16x16 tile that its 3-sigma axis-aligned
@@ -107,17 +110,19 @@ typedef struct gsr_bins {
  *   splats  device [n][9] float32;  depths  device [n] float32
  *   A splat emits nothing if any of its values or its depth is not finite, depth <= 0, a <= 0, a*c - b*b <= 0, or
  *   o is outside [0, 1]. The box is x +- 3 sqrt(c / det), y +- 3 sqrt(a / det), det = a*c - b*b, in fp32.
- *   out     host struct filled with views into the arena.
+ *   out     host struct filled with views into the arena (valid until the context's next gsr_bin), including
+ *           splat_pairs: the number of pairs each splat emitted (0 for a culled or off-image splat).
  * Synchronisation: waits on `stream` once, to read the pair count before sizing the arena; the rest is queued.
  * Errors: GSR_EINVAL (null pointers with n > 0, width or height 0, tiles_x * tiles_y >= 2^32),
  * GSR_EOVERFLOW (2^32 or more pairs), GSR_ENOMEM, GSR_EHIP. */
 gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, const float* depths, uint32_t n,
                    uint32_t width, uint32_t height, gsr_bins* out);
 
-/* Copies the contents of `bins` into caller buffers (device pointers; any of keys / vals / ranges may be NULL to
- * skip it): keys [num_pairs] uint64, vals [num_pairs] uint32, ranges [2 * tiles] uint32. Queued on stream. */
+/* Copies the contents of `bins` into caller buffers (device pointers; any of them may be NULL to skip it):
+ * keys [num_pairs] uint64, vals [num_pairs] uint32, ranges [2 * tiles] uint32, splat_pairs [num_splats] uint32.
+ * Queued on stream. GSR_EINVAL when keys or splat_pairs is asked for and the bins carry none. */
 gsr_status gsr_bins_copy(gsr_ctx* ctx, void* stream, const gsr_bins* bins, uint64_t* keys, uint32_t* vals,
-                         uint32_t* ranges);
+                         uint32_t* ranges, uint32_t* splat_pairs);
 
 /* The sort gsr_bin uses, on its own: a stable LSD radix sort by the low `key_bits` bits of 64-bit keys carrying
  * 32-bit values, 8 bits per pass; digits above key_bits are not looked at (a key with bits set above key_bits
@@ -197,6 +202,21 @@ typedef struct gsr_adam_group {
  * Errors: GSR_EINVAL (null pointers with count > 0, n_groups > GSR_ADAM_MAX_GROUPS, bc1 or bc2 not > 0), GSR_EHIP. */
 gsr_status gsr_adam_step(gsr_ctx* ctx, void* stream, const gsr_adam_group* groups, uint32_t n_groups, float beta1,
                          float beta2, float eps, float bc1, float bc2);
+
+/* Visible-only Adam: the step of gsr_adam_step for the splats that were binned in this view, and no change at all
+ * (param, m and v keep their bits; the gradient is not read) for the others, whose moments dense Adam would decay
+ * and whose parameters it would still move. Each group holds n splats' worth of elements, k = count / n consecutive
+ * elements per splat (3, 3, 4, 1, 48 for the Gaussians' groups). Skipping the invisible splats' bytes is the only
+ * saving left to a bandwidth-bound Adam; the result differs from dense Adam by design. [rasterize forward + adam
+ * kernel audit page, section 2 "(h)": the visible-only skip, gsplat's sparse-gradient Adam]
+ *   splat_pairs  device [n] uint32; splat i is visible when splat_pairs[i] != 0 (gsr_bins.splat_pairs of the
+ *                view's bins, or any caller mask of that type)
+ * Visible splats get exactly gsr_adam_step's bits.
+ * Errors: as gsr_adam_step; GSR_EINVAL also when a group's count is not a multiple of n (or not 0 when n = 0), or
+ * k > 1024, or splat_pairs is NULL with n > 0. */
+gsr_status gsr_adam_step_visible(gsr_ctx* ctx, void* stream, const gsr_adam_group* groups, uint32_t n_groups,
+                                 float beta1, float beta2, float eps, float bc1, float bc2,
+                                 const uint32_t* splat_pairs, uint32_t n);
 
 /* Pinhole camera of the projection. World point p has camera coordinates t = R p + tv; pixel coordinates are
  * (fx tx / tz + cx, fy ty / tz + cy) in the frame where pixel (px, py) has its centre at (px + 0.5, py + 0.5). */

@@ -244,6 +244,22 @@ def adam_step(param, grad, m, v, lr, beta1, beta2, eps, bc1, bc2):
     return p, mm, vv
 
 
+def adam_step_visible(param, grad, m, v, lr, beta1, beta2, eps, bc1, bc2, visible):
+    """Visible-only Adam (rasterize forward + adam kernel audit page, section 2 "(h)"): the rows [n, k] of splats with
+    visible[i] true take adam_step; the other rows of param, m and v are returned unchanged. Returns new copies."""
+    vis = np.asarray(visible, bool).reshape(-1)
+    n = vis.shape[0]
+    p = np.array(param, np.float32, copy=True).reshape(n, -1)
+    mm = np.array(m, np.float32, copy=True).reshape(n, -1)
+    vv = np.array(v, np.float32, copy=True).reshape(n, -1)
+    g = np.asarray(grad, np.float32).reshape(n, -1)
+    if vis.any():
+        rp, rm, rv = adam_step(p[vis], g[vis], mm[vis], vv[vis], lr, beta1, beta2, eps, bc1, bc2)
+        k = p.shape[1]
+        p[vis], mm[vis], vv[vis] = rp.reshape(-1, k), rm.reshape(-1, k), rv.reshape(-1, k)
+    return p.reshape(-1), mm.reshape(-1), vv.reshape(-1)
+
+
 TRACE_CODES = {1: "sigma_neg", 2: "alpha_reject", 3: "stop", 4: "composite", 5: "composite_clamped"}
 
 

@@ -79,3 +79,127 @@ def test_adam_rejects_too_many_groups(ctx):
         gsr.gsr_adam_step(ctx, [(t, t, t, t, 1e-3)] * 9, 0.9, 0.999, 1e-15, 0.1, 0.001)
     with pytest.raises(gsr.GsrError):
         gsr.gsr_adam_step(ctx, [(t, t, t, t, 1e-3)], 0.9, 0.999, 1e-15, 0.0, 0.001)
+
+
+# ---------------------------------------------------------------------------------------- visible-only Adam
+def check_visible(ctx, groups, lrs, step, vis, mask_dev=None):
+    """gsr_adam_step_visible against oracle.adam_step_visible, bit for bit, on every array of every group."""
+    import oracle
+    from differentiable_gaussian_splatting_amd import gsr
+    n = vis.shape[0]
+    bc1, bc2 = scenes.adam_bias_corrections(HP["beta1"], HP["beta2"], step)
+    dev_groups = [(dev(p), dev(g), dev(m), dev(v), lr) for (_, p, g, m, v), lr in zip(groups, lrs)]
+    if mask_dev is None:
+        mask_dev = dev(vis.astype(np.int32) * np.random.default_rng(n).integers(1, 5, n).astype(np.int32))
+    gsr.gsr_adam_step_visible(ctx, dev_groups, HP["beta1"], HP["beta2"], HP["eps"], bc1, bc2, mask_dev, n)
+    for (name, p, g, m, v), (dp, _, dm, dv, _), lr in zip(groups, dev_groups, lrs):
+        rp, rm, rv = oracle.adam_step_visible(p, g, m, v, lr, HP["beta1"], HP["beta2"], HP["eps"], bc1, bc2, vis)
+        assert np.array_equal(host(dp), rp), f"{name}: param differs"
+        assert np.array_equal(host(dm), rm), f"{name}: m differs"
+        assert np.array_equal(host(dv), rv), f"{name}: v differs"
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.03, 0.5, 0.97, 1.0])
+def test_adam_visible_full_iteration_shape(ctx, frac):
+    banner(f"adam visible 410k x 59, visible fraction {frac}")
+    n = 410_000
+    groups = scenes.make_adam_groups(n, seed=6)
+    vis = np.random.default_rng(1).uniform(size=n) < frac
+    check_visible(ctx, groups, [HP["lr"]] * 5, HP["step"], vis)
+
+
+@pytest.mark.parametrize("n", [1, 3, 257, 1023, 1025, 43691])
+def test_adam_visible_odd_sizes(ctx, n):
+    """Sizes whose groups end inside a block and whose splats straddle float4s and blocks (k = 3, 1, 48)."""
+    banner(f"adam visible n={n}")
+    groups = scenes.make_adam_groups(n, seed=n + 1)
+    vis = np.random.default_rng(n).uniform(size=n) < 0.6
+    check_visible(ctx, groups, [1e-3, 2e-4, 5e-5, 1e-2, 1.6e-4], step=4, vis=vis)
+
+
+def test_adam_visible_runs_of_hidden_splats(ctx):
+    """Long runs of hidden and of visible splats (whole float4s and blocks skipped) next to alternating ones."""
+    banner("adam visible runs")
+    n = 20_000
+    vis = np.zeros(n, bool)
+    vis[1000:5000] = True
+    vis[9000:9001] = True
+    vis[12000:20000:2] = True
+    check_visible(ctx, scenes.make_adam_groups(n, seed=9), [1.6e-4] * 5, step=20, vis=vis)
+
+
+def test_adam_visible_all_visible_equals_dense(ctx):
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("adam visible == dense when all are visible")
+    n = 5000
+    groups = scenes.make_adam_groups(n, seed=10)
+    bc1, bc2 = scenes.adam_bias_corrections(0.9, 0.999, 30)
+    a = [(dev(p), dev(g), dev(m), dev(v), 1e-3) for _, p, g, m, v in groups]
+    b = [(dev(p), dev(g), dev(m), dev(v), 1e-3) for _, p, g, m, v in groups]
+    gsr.gsr_adam_step(ctx, a, 0.9, 0.999, 1e-15, bc1, bc2)
+    gsr.gsr_adam_step_visible(ctx, b, 0.9, 0.999, 1e-15, bc1, bc2, dev(np.ones(n, np.int32)))
+    for x, y in zip(a, b):
+        for s, t in zip(x[:4], y[:4]):
+            assert np.array_equal(host(s), host(t))
+
+
+def test_adam_visible_from_bins(ctx):
+    """The visibility of a view: the bins' splat_pairs of a scene with splats off the image."""
+    import oracle
+    from differentiable_gaussian_splatting_amd import gsr
+    from gpuhelp import custom_scene
+    banner("adam visible from bins")
+    sc = custom_scene(name="offimg", width=128, height=96, n=6000, seed=21, margin=40.0)
+    bins = gsr.gsr_bin(ctx, dev(sc.splats), dev(sc.depths), 128, 96)
+    ob = oracle.bin(sc.splats, sc.depths, 128, 96)
+    vis = np.bincount(ob.vals, minlength=6000) > 0
+    assert 0.2 < vis.mean() < 0.9, vis.mean()
+    groups = scenes.make_adam_groups(6000, seed=21)
+    check_visible(ctx, groups, [1.6e-4] * 5, step=100, vis=vis, mask_dev=None)
+    # the same through the Bins object
+    import torch  # noqa: F401
+    bc1, bc2 = scenes.adam_bias_corrections(HP["beta1"], HP["beta2"], 100)
+    d = [(dev(p), dev(g), dev(m), dev(v), 1.6e-4) for _, p, g, m, v in groups]
+    gsr.gsr_adam_step_visible(ctx, d, HP["beta1"], HP["beta2"], HP["eps"], bc1, bc2, bins, 6000)
+    for (name, p, g, m, v), (dp, _, dm, dv, _) in zip(groups, d):
+        rp, rm, rv = oracle.adam_step_visible(p, g, m, v, 1.6e-4, HP["beta1"], HP["beta2"], HP["eps"], bc1, bc2, vis)
+        assert np.array_equal(host(dp), rp) and np.array_equal(host(dm), rm) and np.array_equal(host(dv), rv), name
+
+
+def test_adam_visible_unaligned_and_empty(ctx):
+    """Arrays one element past a 16-byte boundary take the element-by-element path; n = 0 with empty groups is a
+    no-op."""
+    import oracle
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("adam visible unaligned / empty")
+    n, k = 1700, 3
+    rng = np.random.default_rng(4)
+    base = [rng.normal(0, s, n * k + 1).astype(np.float32) for s in (1.0, 1e-3, 1e-3)]
+    base.append((rng.normal(0, 1e-3, n * k + 1) ** 2).astype(np.float32))
+    d = [dev(a) for a in base]
+    vis = rng.uniform(size=n) < 0.5
+    bc1, bc2 = scenes.adam_bias_corrections(0.9, 0.999, 10)
+    gsr.gsr_adam_step_visible(ctx, [(*[t[1:] for t in d], 1e-3)], 0.9, 0.999, 1e-15, bc1, bc2,
+                              dev(vis.astype(np.int32)))
+    rp, rm, rv = oracle.adam_step_visible(base[0][1:], base[1][1:], base[2][1:], base[3][1:], 1e-3, 0.9, 0.999, 1e-15,
+                                          bc1, bc2, vis)
+    assert np.array_equal(host(d[0])[1:], rp) and np.array_equal(host(d[2])[1:], rm)
+    assert np.array_equal(host(d[3])[1:], rv) and host(d[0])[0] == base[0][0]
+    empty = [dev(np.zeros(0, np.float32)) for _ in range(4)]
+    gsr.gsr_adam_step_visible(ctx, [(*empty, 1e-3)], 0.9, 0.999, 1e-15, bc1, bc2, dev(np.zeros(0, np.int32)))
+
+
+def test_adam_visible_rejects_bad_arguments(ctx):
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("adam visible argument errors")
+    t = dev(np.zeros(10, np.float32))
+    mask = dev(np.ones(4, np.int32))
+    with pytest.raises(gsr.GsrError):  # 10 elements are not a multiple of 4 splats
+        gsr.gsr_adam_step_visible(ctx, [(t, t, t, t, 1e-3)], 0.9, 0.999, 1e-15, 0.1, 0.001, mask)
+    with pytest.raises(gsr.GsrError):  # 10 elements with no splats
+        gsr.gsr_adam_step_visible(ctx, [(t, t, t, t, 1e-3)], 0.9, 0.999, 1e-15, 0.1, 0.001,
+                                  dev(np.zeros(0, np.int32)))
+    big = dev(np.zeros(2 * 1025, np.float32))
+    with pytest.raises(gsr.GsrError):  # 1025 elements per splat
+        gsr.gsr_adam_step_visible(ctx, [(big, big, big, big, 1e-3)], 0.9, 0.999, 1e-15, 0.1, 0.001,
+                                  dev(np.ones(2, np.int32)))

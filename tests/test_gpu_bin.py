@@ -29,11 +29,15 @@ def assert_bins_equal(ctx, splats, depths, w, h, scheme, ref=None):
     import oracle
     if ref is None:
         ref = oracle.bin(splats, depths, w, h)
+    from differentiable_gaussian_splatting_amd import gsr
     b, k, v, r = gpu_bin(ctx, splats, depths, w, h, scheme)
     assert b.num_pairs == ref.num_pairs
     assert np.array_equal(k, ref.keys), "sorted keys differ"
     assert np.array_equal(v, ref.vals), "sorted values differ"
     assert np.array_equal(r, ref.ranges), "tile ranges differ"
+    n = splats.shape[0]
+    sp = host(gsr.gsr_bins_splat_pairs(ctx, b), np.uint32)
+    assert sp.shape == (n,) and np.array_equal(sp, np.bincount(ref.vals, minlength=n)), "splat_pairs differ"
     return b
 
 

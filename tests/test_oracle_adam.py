@@ -76,3 +76,65 @@ def test_bias_corrections_at_step_1000():
     b1, b2 = bc(1000)
     # beta2 enters as the fp32 value 0.999f = 0.99900001287, so 1 - beta2^1000 sits 4.7e-6 below 1 - 0.999^1000
     assert b1 == np.float32(1.0) and abs(b2 - (1 - 0.999 ** 1000)) < 1e-5
+
+
+# ---------------------------------------------------------------------------------------- visible-only Adam
+def _groups_and_mask(n, frac, seed):
+    groups = scenes.make_adam_groups(n, seed=seed)
+    vis = np.random.default_rng(seed).uniform(size=n) < frac
+    return groups, vis
+
+
+def test_visible_only_adam_with_every_splat_visible_is_dense_adam(orc):
+    groups, _ = _groups_and_mask(300, 1.0, 1)
+    for _, p, g, m, v in groups:
+        want = orc.adam_step(p, g, m, v, LR, B1, B2, EPS, *bc(7))
+        got = orc.adam_step_visible(p, g, m, v, LR, B1, B2, EPS, *bc(7), np.ones(300, bool))
+        for a, b in zip(got, want):
+            assert np.array_equal(a, b)
+
+
+def test_visible_only_adam_with_no_splat_visible_changes_nothing(orc):
+    groups, _ = _groups_and_mask(300, 0.0, 2)
+    for _, p, g, m, v in groups:
+        got = orc.adam_step_visible(p, g, m, v, LR, B1, B2, EPS, *bc(7), np.zeros(300, bool))
+        for a, b in zip(got, (p, m, v)):
+            assert np.array_equal(a, b)
+
+
+def test_visible_only_adam_masks_whole_splats(orc):
+    """Groups are [n, k] with k consecutive elements per splat: the k elements of a visible splat equal dense Adam's
+    (Adam is element-wise), the k elements of an invisible one keep their bits, and a splat-by-element mistake (a
+    mask applied to elements, or to a [k, n] layout) fails one of the two."""
+    n = 257
+    groups, vis = _groups_and_mask(n, 0.5, 3)
+    assert 0 < vis.sum() < n
+    for name, p, g, m, v in groups:
+        k = p.size // n
+        dense = orc.adam_step(p, g, m, v, LR, B1, B2, EPS, *bc(9))
+        got = orc.adam_step_visible(p, g, m, v, LR, B1, B2, EPS, *bc(9), vis)
+        el = np.repeat(vis, k)
+        for a, d, orig in zip(got, dense, (p, m, v)):
+            assert np.array_equal(a[el], d[el]), name
+            assert np.array_equal(a[~el], orig[~el]), name
+            if k > 1:  # the dense result differs from the original on invisible elements, so the mask matters
+                assert not np.array_equal(d[~el], orig[~el])
+
+
+def test_visible_only_adam_skips_the_moment_decay_of_hidden_splats(orc):
+    """A splat hidden for one step keeps m and v (dense Adam would scale them by beta1 and beta2); when it is seen
+    again its step uses those kept moments: the result equals dense Adam over the visible steps only."""
+    p, g, m, v = (np.array([0.5], np.float32), np.array([2e-3], np.float32), np.array([1e-3], np.float32),
+                  np.array([1e-6], np.float32))
+    state = (p, m, v)
+    for t, seen in ((1, True), (2, False), (3, True)):
+        state = orc.adam_step_visible(state[0], g, state[1], state[2], LR, B1, B2, EPS, *bc(t), np.array([seen]))
+    want = orc.adam_step(p, g, m, v, LR, B1, B2, EPS, *bc(1))
+    want = orc.adam_step(want[0], g, want[1], want[2], LR, B1, B2, EPS, *bc(3))
+    for a, b in zip(state, want):
+        assert np.array_equal(a, b)
+    # and the moments are not those of dense Adam over all three steps
+    dense = (p, m, v)
+    for t in (1, 2, 3):
+        dense = orc.adam_step(dense[0], g, dense[1], dense[2], LR, B1, B2, EPS, *bc(t))
+    assert state[1][0] != dense[1][0]
