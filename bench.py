@@ -28,6 +28,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fwd+bwd raster ms/iter @800×800, 410k splats; splat-pixel evals/s"
 UNIT = "splat-pixel evals/s"
+TIMED_RANGE = "timed steps"  # ROCTx range around the timed steps
+MEASURED_RANGE = "measured steps"  # ROCTx range around the steps that carry HIP events
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 # fp32 vector rate without packed dual-fp32 instructions: 256 CUs x 64 lanes x 2 flops (FMA) x 2.4 GHz
 ALU_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
@@ -123,6 +125,19 @@ def run_oracle(sc, adam_groups, hp, bc, bin_rule="box"):
             "num_pairs": ob.num_pairs, "out": out, "lc": lc, "ranges": ob.ranges}
 
 
+def roctx():
+    """The ROCTx marker library (its ranges cost nothing unless a profiler records them), or None."""
+    import ctypes
+    for name in ("librocprofiler-sdk-roctx.so.1", "libroctx64.so.4"):
+        try:
+            lib = ctypes.CDLL(name)
+        except OSError:
+            continue
+        lib.roctxRangePushA.argtypes = [ctypes.c_char_p]
+        return lib
+    return None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -189,20 +204,48 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, synchronized on both sides; per-stage HIP events on the same stream
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # timed region: exactly K steps, synchronized on both sides, with nothing else on the stream (HIP events
+    # between the kernels cost about 50 us of launch gaps per step, so they are taken in the steps after it)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    rx = roctx()  # the timed region as a ROCTx range, so that a kernel trace can single out its dispatches
     torch.cuda.synchronize()
+    if rx:
+        rx.roctxRangePushA(TIMED_RANGE.encode())
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        b = step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if rx:
+        rx.roctxRangePop()
+    ms_per_step = wall * 1e3 / args.steps
+
+    # K more steps with HIP events on the library's stream: torch's around each stage (its launches and small
+    # kernels included), the library's around each stage's main kernel (GSR_OPT_KERNEL_TIMING); the kernels' own
+    # durations are the ones the rooflines use
+    print(f"[bench] {args.steps} steps with per-stage and per-kernel events", file=sys.stderr, flush=True)
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, args.steps)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    if rx:
+        rx.roctxRangePushA(MEASURED_RANGE.encode())
     for k in range(args.steps):
         b = step(events[k])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    if rx:
+        rx.roctxRangePop()
     stage_ms = {nm: float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
                 for i, nm in enumerate(names)}
     stage_ms_median = {nm: float(np.median([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
                        for i, nm in enumerate(names)}
+    kernel_stage = {"bin": gsr.GSR_STAGE_BIN, "forward": gsr.GSR_STAGE_FORWARD, "backward": gsr.GSR_STAGE_BACKWARD,
+                    "adam": gsr.GSR_STAGE_ADAM}
+    kernel_ms = {}
+    for nm, stg in kernel_stage.items():
+        t = gsr.gsr_kernel_times(ctx, stg)
+        assert len(t) == args.steps, f"{nm}: {len(t)} launches recorded"
+        kernel_ms[nm] = float(np.mean(t))
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, 0)
     P = b.num_pairs
     e_bwd_gpu = int(last_contrib.to(torch.int64).sum().item())
     det = bench_deterministic_backward(args, ctx, gsr, torch, np, stream, splats, b, W, H, out_rgba, final_T,
@@ -227,8 +270,13 @@ def main():
                          "raster_skip": args.raster_skip}}
     result["stage_ms"] = stage_ms
     result["stage_ms_median"] = stage_ms_median
+    result["kernel_ms"] = kernel_ms  # the main kernel(s) of each stage alone (GSR_OPT_KERNEL_TIMING)
+    result["timing"] = ("value and ms_per_step: wall clock of the K timed steps, which carry no events; stage_ms "
+                        "and kernel_ms: HIP events in K further steps (torch's around each stage, the library's "
+                        "around each stage's main kernel on its stream)")
     result["fwd_bwd_ms"] = stage_ms["forward"] + stage_ms["backward"]
     det["ratio_to_default"] = det["ms"] / stage_ms["backward"]
+    det["kernel_ratio_to_default"] = det["kernel_ms"] / kernel_ms["backward"]
     result["deterministic_backward"] = det
     if cpu is not None:
         fs, bs = cpu["fwd_stats"], cpu["bwd_stats"]
@@ -248,13 +296,15 @@ def main():
                    BWD_OPS["contrib"] * bs["contrib"])
         adam_bytes = 28 * adam_elems
         roofs = {
-            "forward": {"bound": "alu", "achieved": fwd_ops / (stage_ms["forward"] * 1e-3) / 1e12,
+            "forward": {"bound": "alu", "achieved": fwd_ops / (kernel_ms["forward"] * 1e-3) / 1e12,
                         "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s", "work_per_launch": fwd_ops},
-            "backward": {"bound": "alu", "achieved": bwd_ops / (stage_ms["backward"] * 1e-3) / 1e12,
+            "backward": {"bound": "alu", "achieved": bwd_ops / (kernel_ms["backward"] * 1e-3) / 1e12,
                          "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s", "work_per_launch": bwd_ops},
-            "adam": {"bound": "hbm", "achieved": adam_bytes / (stage_ms["adam"] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "work_per_launch": adam_bytes},
+            "adam": {"bound": "hbm", "achieved": adam_bytes / (kernel_ms["adam"] * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "work_per_launch": adam_bytes},
         }
+        for k, r in roofs.items():
+            r["kernel_ms"] = kernel_ms[k]
         # HBM bytes per launch from the committed counter summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated);
         # null when the kernel's sources changed since the counters were taken
         from differentiable_gaussian_splatting_amd import profiling
@@ -264,7 +314,7 @@ def main():
             r["traffic"] = profiling.traffic_for(profiling.STAGE_KERNEL[k], traffic_md)
         for k in ("forward", "backward"):
             roofs[k]["frac_of_published_157_3"] = roofs[k]["achieved"] / ALU_PUBLISHED_TFLOPS
-        dominant = max(("forward", "backward", "adam"), key=lambda k: stage_ms[k])
+        dominant = max(("forward", "backward", "adam"), key=lambda k: kernel_ms[k])
         result["roofline"] = {"kernel": dominant, **roofs[dominant]}
         result["rooflines"] = roofs
         ct = cpu["times"]
@@ -295,6 +345,7 @@ def bench_deterministic_backward(args, ctx, gsr, torch, np, stream, splats, b, W
     ref = grad.clone()
     g = [torch.empty_like(grad), torch.empty_like(grad)]
     gsr.gsr_set_option(ctx, gsr.GSR_OPT_DETERMINISTIC, 1)
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, args.steps)
     try:
         gsr.gsr_render_backward(ctx, splats, b, W, H, out_rgba, final_T, last_contrib, v_out, g[0])
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
@@ -304,12 +355,14 @@ def bench_deterministic_backward(args, ctx, gsr, torch, np, stream, splats, b, W
             gsr.gsr_render_backward(ctx, splats, b, W, H, out_rgba, final_T, last_contrib, v_out, g[1])
             ev[k][1].record(stream)
         torch.cuda.synchronize()
+        kms = float(np.mean(gsr.gsr_kernel_times(ctx, gsr.GSR_STAGE_BACKWARD)))
     finally:
+        gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, 0)
         gsr.gsr_set_option(ctx, gsr.GSR_OPT_DETERMINISTIC, 0)
     ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     same = bool(torch.equal(g[0].view(torch.int32), g[1].view(torch.int32)))
     dev = ((g[0] - ref).abs() / (1e-4 + 1e-4 * ref.abs())).max().item()
-    return {"ms": ms, "repeats_bit_identical": same,
+    return {"ms": ms, "kernel_ms": kms, "repeats_bit_identical": same,
             "max_diff_to_default_in_units_of_1e-4_abs_plus_rel": dev}
 
 

@@ -195,8 +195,10 @@ gsr_status adam_launch(gsr_ctx* ctx, void* stream, const gsr_adam_group* groups,
   if (blocks == 0) return GSR_OK;
   gsr_status st = enter(ctx);
   if (st) return st;
+  timing_mark(ctx, GSR_STAGE_ADAM, static_cast<hipStream_t>(stream), false);
   hipLaunchKernelGGL(sparse ? k_adam<true> : k_adam<false>, dim3(uint32_t(blocks)), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), a);
+  timing_mark(ctx, GSR_STAGE_ADAM, static_cast<hipStream_t>(stream), true);
   return check_launch(ctx, what);
 }
 

@@ -563,6 +563,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   uint32_t* ov = static_cast<uint32_t*>(a.order_vals.ptr);
 
   // Rectangles, counts and the pair total first; the total goes to the host while the depth sort runs.
+  timing_mark(ctx, GSR_STAGE_BIN, s, false);
   if (n) {
     hipLaunchKernelGGL(k_prep, dim3(nb_prep), dim3(kThreads), 0, s, splats, depths, n, tiles_x, tiles_y, ellipse,
                        rects, counts,
@@ -670,6 +671,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
                        depths, n, static_cast<uint64_t*>(nullptr), ranges);
   }
   uint32_t* sorted_v = static_cast<uint32_t*>(a.vals[res].ptr);
+  timing_mark(ctx, GSR_STAGE_BIN, s, true);
   if ((st = check_launch(ctx, "gsr_bin emit/sort/ranges"))) return st;
   out->keys = final_k;
   out->vals = sorted_v;

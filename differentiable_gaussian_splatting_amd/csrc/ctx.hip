@@ -64,6 +64,40 @@ gsr_status check_launch(gsr_ctx* ctx, const char* what) {
   return GSR_OK;
 }
 
+void timing_mark(gsr_ctx* ctx, int stage, hipStream_t s, bool end) {
+  if (!ctx->timing_cap) return;
+  const uint64_t slot = ctx->timing_count[stage] % ctx->timing_cap;
+  // a failed record shows up as an error of gsr_kernel_times, not of the call being timed
+  (void)hipEventRecord(ctx->timing_events[(size_t(stage) * ctx->timing_cap + slot) * 2 + (end ? 1 : 0)], s);
+  if (end) ++ctx->timing_count[stage];
+}
+
+static void timing_release(gsr_ctx* ctx) {
+  for (hipEvent_t e : ctx->timing_events) (void)hipEventDestroy(e);
+  ctx->timing_events.clear();
+  ctx->timing_cap = 0;
+  for (uint64_t& c : ctx->timing_count) c = 0;
+}
+
+static gsr_status timing_setup(gsr_ctx* ctx, uint32_t cap) {
+  timing_release(ctx);
+  if (!cap) return GSR_OK;
+  gsr_status st = enter(ctx);
+  if (st) return st;
+  ctx->timing_events.reserve(size_t(cap) * GSR_NUM_STAGES * 2);
+  for (size_t i = 0; i < size_t(cap) * GSR_NUM_STAGES * 2; ++i) {
+    hipEvent_t e = nullptr;
+    const hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) {
+      timing_release(ctx);
+      return hip_fail(ctx, err, "gsr_set_option: creating timing events");
+    }
+    ctx->timing_events.push_back(e);
+  }
+  ctx->timing_cap = cap;
+  return GSR_OK;
+}
+
 static void release(DevBuf& b) {
   if (b.ptr) (void)hipFree(b.ptr);
   b.ptr = nullptr;
@@ -122,6 +156,7 @@ void gsr_destroy(gsr_ctx* ctx) {
   if (a.host_total) (void)hipHostFree(a.host_total);
   if (a.done) (void)hipFree(a.done);
   if (a.total_ready) (void)hipEventDestroy(a.total_ready);
+  timing_release(ctx);
   delete ctx;
 }
 
@@ -152,9 +187,32 @@ gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value) {
       if (value != 0 && value != 1) return fail(ctx, GSR_EINVAL, "gsr_set_option: deterministic must be 0 or 1");
       ctx->deterministic = value != 0;
       return GSR_OK;
+    case GSR_OPT_KERNEL_TIMING:
+      if (value < 0 || value > 4096)
+        return fail(ctx, GSR_EINVAL, "gsr_set_option: kernel timing ring must hold 0..4096 launches");
+      return timing_setup(ctx, uint32_t(value));
     default:
       return fail(ctx, GSR_EINVAL, "gsr_set_option: unknown option %d", int(option));
   }
+}
+
+gsr_status gsr_kernel_times(gsr_ctx* ctx, int32_t stage, float* ms, uint32_t max, uint32_t* count) {
+  if (!ctx || !count || (max && !ms)) return GSR_EINVAL;
+  *count = 0;
+  if (stage < 0 || stage >= GSR_NUM_STAGES) return fail(ctx, GSR_EINVAL, "gsr_kernel_times: no stage %d", stage);
+  if (!ctx->timing_cap) return fail(ctx, GSR_EINVAL, "gsr_kernel_times: kernel timing is off");
+  gsr_status st = enter(ctx);
+  if (st) return st;
+  const uint64_t rec = ctx->timing_count[stage];
+  const uint64_t n = std::min<uint64_t>({rec, ctx->timing_cap, max});
+  for (uint64_t i = rec - n, j = 0; i < rec; ++i, ++j) {
+    const size_t at = (size_t(stage) * ctx->timing_cap + i % ctx->timing_cap) * 2;
+    hipError_t e = hipEventSynchronize(ctx->timing_events[at + 1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms[j], ctx->timing_events[at], ctx->timing_events[at + 1]);
+    if (e != hipSuccess) return hip_fail(ctx, e, "gsr_kernel_times");
+  }
+  *count = uint32_t(n);
+  return GSR_OK;
 }
 
 gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats) {

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "gsr.h"
 
@@ -63,6 +64,10 @@ struct gsr_ctx {
   uint64_t cost_tiles = 0;  // tile count of the grid tile_cost describes (0: none yet)
   const uint32_t* order_ranges = nullptr;  // the ranges tile_order_ext was last ranked for (by a forward)
   uint64_t order_tiles = 0;
+  // GSR_OPT_KERNEL_TIMING: events [stage][slot][begin, end], a ring of timing_cap launches per stage
+  std::vector<hipEvent_t> timing_events;
+  uint32_t timing_cap = 0;
+  uint64_t timing_count[GSR_NUM_STAGES] = {};
 };
 
 namespace gsr {
@@ -81,6 +86,9 @@ gsr_status grow(gsr_ctx* ctx, DevBuf& b, size_t bytes);
 
 // Checks for launch errors after queuing kernels.
 gsr_status check_launch(gsr_ctx* ctx, const char* what);
+
+// With kernel timing on, records the begin (end = false) or end event of the stage's current launch on `s`.
+void timing_mark(gsr_ctx* ctx, int stage, hipStream_t s, bool end);
 
 // Raster launch order (bin.hip): writes into `order` the tiles 0..num_tiles-1 with the longest pair lists first
 // (64 length classes; any order inside a class), on stream s. One workgroup.

@@ -309,10 +309,12 @@ extern "C" gsr_status gsr_loss_l1_ssim(gsr_ctx* ctx, void* stream, uint32_t widt
   float* maps = static_cast<float*>(ctx->arena.loss_maps.ptr);
   const double n = 3.0 * double(width) * double(height);
   const Taps taps = make_taps();
+  timing_mark(ctx, GSR_STAGE_LOSS, s, false);
   hipLaunchKernelGGL(k_ssim_maps, dim3(uint32_t(num_tiles)), dim3(kThreads), 0, s, taps, width, height,
                      uint32_t(tiles_x), reinterpret_cast<const float4*>(out_rgba), target, maps, part);
   hipLaunchKernelGGL(k_ssim_grad, dim3(uint32_t(num_tiles)), dim3(kThreads), 0, s, taps, width, height,
                      uint32_t(tiles_x), 0.2f, float(1.0 / n), reinterpret_cast<const float4*>(out_rgba), target, maps,
                      reinterpret_cast<float4*>(v_out), part, 1.0 / n, loss);
+  timing_mark(ctx, GSR_STAGE_LOSS, s, true);
   return check_launch(ctx, "gsr_loss_l1_ssim");
 }

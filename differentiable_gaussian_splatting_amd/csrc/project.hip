@@ -433,9 +433,11 @@ extern "C" gsr_status gsr_project_forward(gsr_ctx* ctx, void* stream, const gsr_
   if (uint64_t(n) * 48 >= (uint64_t(1) << 32)) return fail(ctx, GSR_EOVERFLOW, "gsr_project_forward: n * 48 >= 2^32");
   gsr_status st = enter(ctx);
   if (st) return st;
+  timing_mark(ctx, GSR_STAGE_PROJECT_FORWARD, static_cast<hipStream_t>(stream), false);
   hipLaunchKernelGGL(k_project_forward, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), make_cam(*cam), n, means, log_scales, quats, raw_opacities, sh,
                      splats, depths);
+  timing_mark(ctx, GSR_STAGE_PROJECT_FORWARD, static_cast<hipStream_t>(stream), true);
   return check_launch(ctx, "gsr_project_forward");
 }
 
@@ -456,8 +458,10 @@ extern "C" gsr_status gsr_project_backward(gsr_ctx* ctx, void* stream, const gsr
     return fail(ctx, GSR_EOVERFLOW, "gsr_project_backward: n * 48 >= 2^32");
   gsr_status st = enter(ctx);
   if (st) return st;
+  timing_mark(ctx, GSR_STAGE_PROJECT_BACKWARD, static_cast<hipStream_t>(stream), false);
   hipLaunchKernelGGL(k_project_backward, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), make_cam(*cam), n, means, log_scales, quats, raw_opacities, sh,
                      splats_grad, means_grad, log_scales_grad, quats_grad, raw_opacities_grad, sh_grad);
+  timing_mark(ctx, GSR_STAGE_PROJECT_BACKWARD, static_cast<hipStream_t>(stream), true);
   return check_launch(ctx, "gsr_project_backward");
 }

@@ -428,10 +428,12 @@ extern "C" gsr_status gsr_render_backward(gsr_ctx* ctx, void* stream, const floa
   if (!order) return st;
   auto kernel = ctx->raster_skip ? (det ? k_backward_det<true> : k_backward<true>)
                                  : (det ? k_backward_det<false> : k_backward<false>);
+  timing_mark(ctx, GSR_STAGE_BACKWARD, s, false);
   hipLaunchKernelGGL(kernel, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, s, splats, n, bins->vals,
                      bins->ranges, bins->num_pairs, tiles_x, width, height,
                      reinterpret_cast<const float4*>(out_rgba), last_contrib, reinterpret_cast<const float4*>(v_out),
                      splats_grad, fixed, order, uint32_t(num_tiles));
+  timing_mark(ctx, GSR_STAGE_BACKWARD, s, true);
   if (det) hipLaunchKernelGGL(k_fixed_to_float, value_grid, dim3(kTilePixels), 0, s, fixed, splats_grad, count);
   return check_launch(ctx, "gsr_render_backward");
 }

@@ -134,9 +134,11 @@ extern "C" gsr_status gsr_render_forward(gsr_ctx* ctx, void* stream, const float
   // the walk lengths of this forward rank the tiles of the next raster launch on this grid
   if ((st = grow(ctx, ctx->arena.tile_cost, size_t(num_tiles) * 16))) return st;
   auto kernel = ctx->raster_skip ? k_forward<true> : k_forward<false>;
+  timing_mark(ctx, GSR_STAGE_FORWARD, s, false);
   hipLaunchKernelGGL(kernel, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, s, splats, n, bins->vals,
                      bins->ranges, bins->num_pairs, tiles_x, width, height, reinterpret_cast<float4*>(out_rgba),
                      final_T, last_contrib, order, uint32_t(num_tiles), static_cast<uint32_t*>(ctx->arena.tile_cost.ptr));
+  timing_mark(ctx, GSR_STAGE_FORWARD, s, true);
   if ((st = check_launch(ctx, "gsr_render_forward"))) return st;
   ctx->cost_tiles = num_tiles;
   return GSR_OK;

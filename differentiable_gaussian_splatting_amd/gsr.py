@@ -21,6 +21,9 @@ GSR_OK, GSR_EINVAL, GSR_ENOMEM, GSR_EHIP, GSR_EOVERFLOW = 0, -1, -2, -3, -4
 GSR_OPT_BIN_SCHEME, GSR_BIN_PRESORT, GSR_BIN_KEY64, GSR_OPT_BIN_KEYS, GSR_OPT_RASTER_SKIP = 1, 0, 1, 2, 3
 GSR_OPT_BIN_RULE, GSR_BIN_BOX, GSR_BIN_ELLIPSE = 4, 0, 1
 GSR_OPT_DETERMINISTIC = 5
+GSR_OPT_KERNEL_TIMING = 6
+(GSR_STAGE_BIN, GSR_STAGE_FORWARD, GSR_STAGE_BACKWARD, GSR_STAGE_ADAM, GSR_STAGE_PROJECT_FORWARD,
+ GSR_STAGE_PROJECT_BACKWARD, GSR_STAGE_LOSS) = range(7)
 GSR_ADAM_MAX_GROUPS = 8
 _STATUS = {GSR_EINVAL: "GSR_EINVAL", GSR_ENOMEM: "GSR_ENOMEM", GSR_EHIP: "GSR_EHIP", GSR_EOVERFLOW: "GSR_EOVERFLOW"}
 
@@ -71,6 +74,7 @@ SIGNATURES = {
     "gsr_render_forward": (_I32, [_P, _P, _P, _U32, ctypes.POINTER(gsr_bins), _U32, _U32, _P, _P, _P]),
     "gsr_render_backward": (_I32, [_P, _P, _P, _U32, ctypes.POINTER(gsr_bins), _U32, _U32, _P, _P, _P, _P, _P]),
     "gsr_adam_step": (_I32, [_P, _P, ctypes.POINTER(gsr_adam_group), _U32, _F, _F, _F, _F, _F]),
+    "gsr_kernel_times": (_I32, [_P, _I32, _P, _U32, _P]),
     "gsr_adam_step_visible": (_I32, [_P, _P, ctypes.POINTER(gsr_adam_group), _U32, _F, _F, _F, _F, _F, _P, _U32]),
     "gsr_project_forward": (_I32, [_P, _P, ctypes.POINTER(gsr_camera), _U32, _P, _P, _P, _P, _P, _P, _P]),
     "gsr_project_backward": (_I32, [_P, _P, ctypes.POINTER(gsr_camera), _U32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -175,6 +179,14 @@ def gsr_reserve(ctx: Context, max_pairs: int, max_splats: int):
 
 def gsr_set_option(ctx: Context, option: int, value: int):
     ctx.check(load().gsr_set_option(ctx.handle, option, value), "gsr_set_option")
+
+
+def gsr_kernel_times(ctx: Context, stage: int, max_count: int = 4096) -> list:
+    """GPU milliseconds of the last recorded launches of `stage` (GSR_OPT_KERNEL_TIMING on), oldest first."""
+    buf = (ctypes.c_float * max(1, max_count))()
+    count = ctypes.c_uint32(0)
+    ctx.check(load().gsr_kernel_times(ctx.handle, stage, buf, max_count, ctypes.byref(count)), "gsr_kernel_times")
+    return [float(buf[i]) for i in range(count.value)]
 
 
 def gsr_radix_pass_count(num_tiles: int, digit_bits: int) -> int:

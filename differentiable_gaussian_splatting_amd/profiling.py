@@ -1,9 +1,11 @@
 """rocprofv3 output -> the short text summaries kept under profiles/, and the HBM traffic record bench.py reads.
 
-    python -m differentiable_gaussian_splatting_amd.profiling trace STATS_CSV --title T --cmd CMD > profiles/x.md
+    python -m differentiable_gaussian_splatting_amd.profiling trace STATS_CSV --title T --cmd CMD [--timed-range R]
     python -m differentiable_gaussian_splatting_amd.profiling pmc --dir D --cmd CMD --workload W > profiles/y.md
 
-`trace` turns a `rocprofv3 --kernel-trace --stats` kernel_stats.csv into a table of per-kernel calls and durations.
+`trace` turns a `rocprofv3 --kernel-trace --stats` kernel_stats.csv into a table of per-kernel calls and durations;
+with `--timed-range` (and `--marker-trace` in the rocprofv3 run) it first tabulates the dispatches inside that
+ROCTx range, which bench.py opens around its timed steps.
 `pmc` reads the counter_collection.csv files of the passes under D (subdirectories valu, flops, fetch, write,
 calib_fetch, calib_write; each made by one `rocprofv3 --pmc` run) and writes per-kernel counter averages per
 dispatch. HBM bytes per launch are FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled so that the same counters
@@ -36,18 +38,20 @@ KERNEL_SOURCES = {
     "k_ssim_maps": ["loss.hip", "gsr_internal.hpp"],
     "k_ssim_grad": ["loss.hip", "gsr_internal.hpp"],
 }
-# bench.py stage -> kernel
-STAGE_KERNEL = {"forward": "k_forward", "backward": "k_backward", "backward_deterministic": "k_backward_det",
-                "adam": "k_adam",
-                "project_forward": "k_project_forward", "project_backward": "k_project_backward",
-                "loss_l1_ssim": "k_ssim_maps"}
+# bench.py stage -> the kernel instance its default configuration launches (template arguments as rocprofv3
+# prints them: the raster kernels with the skips on, the dense Adam)
+STAGE_KERNEL = {"forward": "k_forward<true>", "backward": "k_backward<true>",
+                "backward_deterministic": "k_backward_det<true>", "adam": "k_adam<false>",
+                "adam_visible": "k_adam<true>", "project_forward": "k_project_forward",
+                "project_backward": "k_project_backward", "loss_l1_ssim": ("k_ssim_maps", "k_ssim_grad")}
 CALIB_BYTES = 256 * 1024 * 1024  # read and written by each copy of bench.py --calib-copy
 TRAFFIC_BEGIN, TRAFFIC_END = "<!-- traffic-json", "traffic-json -->"
 
 
 def source_hash(kernel: str) -> str:
+    """Hash of the sources and build flags of a kernel (any instance of it: the name before '<' is looked up)."""
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES[kernel]:
+    for name in KERNEL_SOURCES[kernel.split("<")[0]]:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     with open(os.path.join(HERE, "build.py"), "rb") as f:
@@ -67,10 +71,45 @@ def base_kernel(name: str) -> str:
     return short_name(name).split("<")[0]
 
 
-def trace_md(stats_csv: str, title: str, cmd: str) -> str:
+def _range_window(marker_csv: str, name: str):
+    """(start, end) timestamps of the ROCTx range `name` in a rocprofv3 marker trace, or None."""
+    try:
+        rows = list(csv.DictReader(open(marker_csv)))
+    except OSError:
+        return None
+    for r in rows:
+        if name in r.values():
+            return int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+    return None
+
+
+def timed_table(kernel_csv: str, window) -> list:
+    """Per-kernel calls and durations of the dispatches that ran inside `window`, longest total first."""
+    acc = collections.defaultdict(list)
+    for r in csv.DictReader(open(kernel_csv)):
+        t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        if t0 >= window[0] and t1 <= window[1]:
+            acc[short_name(r["Kernel_Name"])].append(t1 - t0)
+    total = sum(sum(v) for v in acc.values()) or 1
+    out = ["| kernel | calls | avg µs | min µs | max µs | total ms | % |", "|---|---|---|---|---|---|---|"]
+    for k, v in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| `{k[:90]}` | {len(v)} | {sum(v) / len(v) / 1e3:.2f} | {min(v) / 1e3:.2f} | "
+                   f"{max(v) / 1e3:.2f} | {sum(v) / 1e6:.3f} | {100 * sum(v) / total:.2f} |")
+    return out
+
+
+def trace_md(stats_csv: str, title: str, cmd: str, timed_range: str | None = None) -> str:
+    """The kernel summary of a trace; with `timed_range`, first a table of the dispatches inside that ROCTx range
+    (read from the kernel and marker traces written next to the stats file)."""
     rows = list(csv.DictReader(open(stats_csv)))
-    out = [f"# {title}", "", "Command (repository root on the GPU box):", "", "```", cmd, "```", "",
-           "| kernel | calls | avg µs | min µs | max µs | total ms | % |", "|---|---|---|---|---|---|---|"]
+    out = [f"# {title}", "", "Command (repository root on the GPU box):", "", "```", cmd, "```", ""]
+    if timed_range:
+        stem = stats_csv[:-len("kernel_stats.csv")]
+        window = _range_window(stem + "marker_api_trace.csv", timed_range)
+        if window:
+            out += [f"Dispatches inside the ROCTx range \"{timed_range}\" ({(window[1] - window[0]) / 1e6:.3f} ms):", ""]
+            out += timed_table(stem + "kernel_trace.csv", window) + ["", "Every dispatch of the run:", ""]
+    out += ["| kernel | calls | avg µs | min µs | max µs | total ms | % |", "|---|---|---|---|---|---|---|"]
     for r in rows:
         out.append(f"| `{short_name(r['Name'])[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
@@ -78,11 +117,18 @@ def trace_md(stats_csv: str, title: str, cmd: str) -> str:
     return "\n".join(out) + "\n"
 
 
-def _counters(path: str):
-    """{kernel short name: {counter: mean value per dispatch}}; the mean duration in ns is under '_ns'."""
+def _counters(path: str, first: int | None = None):
+    """{kernel short name: {counter: mean value per dispatch}}; the mean duration in ns is under '_ns'. With
+    `first`, only each kernel's first `first` dispatches count (bench.py runs its step before anything else)."""
     acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    seen = collections.defaultdict(list)
     for r in csv.DictReader(open(path)):
         k = short_name(r["Kernel_Name"])
+        d = r["Dispatch_Id"]
+        if d not in seen[k]:
+            seen[k].append(d)
+        if first is not None and seen[k].index(d) >= first:
+            continue
         acc[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
         acc[k]["_ns"].append(float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
     return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}, None
@@ -96,12 +142,12 @@ def _find_csv(d: str):
     return None
 
 
-def pmc_md(base: str, cmd: str, workload: str) -> str:
+def pmc_md(base: str, cmd: str, workload: str, first: int | None = None) -> str:
     passes = {}
     for p in ("valu", "flops", "fetch", "write", "calib_fetch", "calib_write"):
         path = _find_csv(os.path.join(base, p))
         if path:
-            passes[p] = _counters(path)
+            passes[p] = _counters(path, None if p.startswith("calib") else first)
     # calibration: the copy kernel's counter reading for CALIB_BYTES each way
     scale = {}
     for cnt, p in (("FETCH_SIZE", "calib_fetch"), ("WRITE_SIZE", "calib_write")):
@@ -119,7 +165,10 @@ def pmc_md(base: str, cmd: str, workload: str) -> str:
     cols = [("valu", "_ns"), ("valu", "SQ_INSTS_VALU"), ("valu", "SQ_INSTS_SALU"), ("valu", "SQ_INSTS_LDS"),
             ("flops", "SQ_INSTS_VALU_FLOPS_FP32"), ("flops", "SQ_INSTS_VALU_FLOPS_FP64"),
             ("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")]
-    lines += ["Per dispatch (mean over the profiled dispatches). `_ns` is the dispatch duration in the valu pass;",
+    lines += [("Per dispatch (mean over each kernel's first %d dispatches: the step's warmup and timed launches "
+               "come before\nthe other blocks of bench.py, which run some of the same kernels on other inputs). "
+               % first if first else "Per dispatch (mean over the profiled dispatches). ") +
+              "`_ns` is the dispatch duration in the valu pass;",
               "VALU issue = SQ_INSTS_VALU x 4 cycles (a wave64 instruction on a 16-lane SIMD) / (1024 SIMDs x",
               "duration x 2.4 GHz); the FLOPS counters count per wave instruction (an FMA counts 2), so counted",
               "TFLOP/s = 64 lanes x (FLOPS_FP32 + FLOPS_FP64) / duration, an upper bound (inactive lanes count).", "",
@@ -136,10 +185,10 @@ def pmc_md(base: str, cmd: str, workload: str) -> str:
         hbm = None
         if fetch is not None and write is not None and len(scale) == 2:
             hbm = fetch * 1024 * scale["FETCH_SIZE"] + write * 1024 * scale["WRITE_SIZE"]
-            bk = base_kernel(k)
-            if bk in KERNEL_SOURCES:
-                record[bk] = {"hbm_bytes": hbm, "fetch_kib": fetch, "write_kib": write,
-                              "sources": source_hash(bk), "instance": k}
+            if base_kernel(k) in KERNEL_SOURCES:  # one record per instance (k_adam<false> and <true> differ)
+                inst = short_name(k).replace(", ", ",").replace("unsigned int", "uint32")
+                record[inst] = {"hbm_bytes": hbm, "fetch_kib": fetch, "write_kib": write,
+                                "sources": source_hash(inst)}
         v = passes.get("valu", ({}, {}))[0].get(k, {})
         f = passes.get("flops", ({}, {}))[0].get(k, {})
         ns = v.get("_ns")
@@ -166,7 +215,11 @@ def read_traffic(md_path: str):
 
 
 def traffic_for(kernel: str, md_path: str):
-    """Recorded HBM bytes per launch of `kernel`, or None when unrecorded or its sources changed since."""
+    """Recorded HBM bytes per launch of the kernel instance `kernel` (e.g. "k_adam<false>"; a tuple of instances
+    gives their sum), or None when unrecorded or its sources changed since."""
+    if isinstance(kernel, (tuple, list)):  # a stage of several kernels: their sum
+        parts = [traffic_for(k, md_path) for k in kernel]
+        return None if any(p is None for p in parts) else sum(parts)
     rec = read_traffic(md_path)
     if not rec or kernel not in rec.get("kernels", {}):
         return None
@@ -181,15 +234,17 @@ def main(argv=None):
     t.add_argument("stats_csv")
     t.add_argument("--title", required=True)
     t.add_argument("--cmd", required=True)
+    t.add_argument("--timed-range", default=None, help="ROCTx range whose dispatches get a table of their own")
     p = sub.add_parser("pmc")
     p.add_argument("--dir", required=True)
     p.add_argument("--cmd", required=True)
     p.add_argument("--workload", required=True)
+    p.add_argument("--first", type=int, default=None, help="count only each kernel's first N dispatches")
     a = ap.parse_args(argv)
     if a.what == "trace":
-        sys.stdout.write(trace_md(a.stats_csv, a.title, a.cmd))
+        sys.stdout.write(trace_md(a.stats_csv, a.title, a.cmd, a.timed_range))
     else:
-        sys.stdout.write(pmc_md(a.dir, a.cmd, a.workload))
+        sys.stdout.write(pmc_md(a.dir, a.cmd, a.workload, a.first))
 
 
 if __name__ == "__main__":

@@ -80,14 +80,34 @@ gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats);
                              /*   least edge minimum at the clamped vertex)                                       */
 #define GSR_OPT_DETERMINISTIC 5 /* 0 (default): the backward adds its per-tile sums with float atomics, so the     */
                               /*   last bits of splats_grad depend on scheduling; 1: the same bits on every run.   */
-                              /*   Each wavefront keeps its own per-batch sums (added in wavefront order), and the */
-                              /*   tiles' totals are summed exactly as 128-bit fixed-point integers (each rounded  */
-                              /*   to a multiple of 2^-48) and rounded to float once. A non-finite tile total, or  */
-                              /*   one of magnitude 2^79 or more, gives NaN or +-inf as a float sum would. Costs an */
-                              /*   arena buffer of 148 bytes per splat and some of the backward's speed. (The     */
-                              /*   per-splat backward page shrinks, but does not remove, the run-to-run noise by  */
-                              /*   changing the loop order; its determinism note.)                                */
+                              /*   Within a tile, each pair of wavefronts adds into a per-batch sum of its own     */
+                              /*   (two additions to a zeroed cell commute exactly) and the two are added at the  */
+                              /*   end of the batch; the tiles' totals are summed as 128-bit fixed-point integers  */
+                              /*   (each rounded to a multiple of 2^-48) and rounded to float once. A tile total   */
+                              /*   that is not finite, or of magnitude 2^79 or more, gives NaN or +-inf as a      */
+                              /*   float sum would. Costs an arena buffer of 148 bytes per splat and about a fifth */
+                              /*   of the backward's speed. (The per-splat backward page shrinks, but does not    */
+                              /*   remove, the run-to-run noise by changing the loop order; its determinism note.) */
+#define GSR_OPT_KERNEL_TIMING 6 /* 0 (default): off; n in 1..4096: every entry point records a pair of HIP events   */
+                              /*   on its stream around its main kernel(s), in a ring of the last n launches per  */
+                              /*   stage (read with gsr_kernel_times); setting the option clears the rings        */
 gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value);
+
+/* Stages timed by GSR_OPT_KERNEL_TIMING, each the kernels between its pair of events. */
+#define GSR_STAGE_BIN 0              /* gsr_bin, first launch to last (its wait for the pair count included)      */
+#define GSR_STAGE_FORWARD 1          /* the forward raster kernel                                                */
+#define GSR_STAGE_BACKWARD 2         /* the backward raster kernel (not its zero fill, tile ranking or, with     */
+                                     /*   GSR_OPT_DETERMINISTIC, the clearing and conversion of the fixed sums)  */
+#define GSR_STAGE_ADAM 3             /* the Adam kernel, dense or visible-only                                   */
+#define GSR_STAGE_PROJECT_FORWARD 4  /* the projection kernel                                                    */
+#define GSR_STAGE_PROJECT_BACKWARD 5 /* the projection's backward kernel                                         */
+#define GSR_STAGE_LOSS 6             /* both passes of the L1 + SSIM loss                                        */
+#define GSR_NUM_STAGES 7
+
+/* GPU durations in milliseconds of the recorded launches of `stage`, oldest first: the last min(recorded, ring
+ * size, max) of them. Waits for the newest one to finish. *count = the number written.
+ * Errors: GSR_EINVAL (null ctx, ms with max > 0, or count; stage out of range; timing off), GSR_EHIP. */
+gsr_status gsr_kernel_times(gsr_ctx* ctx, int32_t stage, float* ms, uint32_t max, uint32_t* count);
 
 /* Views into the context's arena, valid until the next gsr_bin or gsr_reserve on the same context. A caller may
  * also fill one with its own device buffers of the same layout (for example bins computed elsewhere). */
