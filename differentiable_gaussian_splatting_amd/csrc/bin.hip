@@ -266,12 +266,14 @@ __device__ __forceinline__ uint32_t block_exclusive_max(uint32_t v, uint32_t car
 // pairs, which it writes in chunks of 1024 pairs, four consecutive pairs per thread (coalesced stores). In each
 // chunk every splat marks the slot of its first pair with its position + 1, and a running maximum over the chunk
 // (seeded with the previous chunk's last owner) gives each pair its splat. Inside a splat the tiles go row by
-// row. 64-bit keys: (tile << 32) | depth bits; 32-bit keys: the tile id only.
-template <typename K>
+// row. 64-bit keys: (tile << 32) | depth bits; 32-bit keys: the tile id only, or with kPacked
+// (tile << idx_bits) | splat and no value array.
+template <typename K, bool kPacked = false>
 __global__ __launch_bounds__(kThreads) void k_emit(const uint4* __restrict__ rects, const float* __restrict__ depths,
                                                    uint32_t n, const uint32_t* __restrict__ order, uint32_t tiles_x,
                                                    const uint64_t* __restrict__ offsets, uint64_t num_pairs,
-                                                   K* __restrict__ keys, uint32_t* __restrict__ vals) {
+                                                   K* __restrict__ keys, uint32_t* __restrict__ vals,
+                                                   uint32_t idx_bits) {
   constexpr uint32_t kPer = 4, kChunk = kPer * kThreads;  // kPer = 4: one 16-byte vector of values per thread
   __shared__ uint64_t s_off[kThreads + 1];
   __shared__ uint32_t s_tx0[kThreads], s_ty0[kThreads], s_w[kThreads], s_idx[kThreads], s_dbits[kThreads];
@@ -330,6 +332,8 @@ __global__ __launch_bounds__(kThreads) void k_emit(const uint4* __restrict__ rec
       const uint64_t tile = uint64_t(s_ty0[q] + row) * tiles_x + (s_tx0[q] + (k - row * w));
       if constexpr (sizeof(K) == 8)
         kk[e] = (tile << 32) | s_dbits[q];
+      else if constexpr (kPacked)
+        kk[e] = K((uint32_t(tile) << idx_bits) | s_idx[q]);
       else
         kk[e] = K(tile);
       vv[e] = s_idx[q];
@@ -341,13 +345,13 @@ __global__ __launch_bounds__(kThreads) void k_emit(const uint4* __restrict__ rec
       } else {
         *reinterpret_cast<uint4*>(keys + p0) = make_uint4(kk[0], kk[1], kk[2], kk[3]);
       }
-      *reinterpret_cast<uint4*>(vals + p0) = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+      if constexpr (!kPacked) *reinterpret_cast<uint4*>(vals + p0) = make_uint4(vv[0], vv[1], vv[2], vv[3]);
     } else {
 #pragma unroll
       for (uint32_t e = 0; e < kPer; ++e)
         if (ok[e]) {
           keys[p0 + e] = kk[e];
-          vals[p0 + e] = vv[e];
+          if constexpr (!kPacked) vals[p0 + e] = vv[e];
         }
     }
     carry = chunk_max;
@@ -356,14 +360,14 @@ __global__ __launch_bounds__(kThreads) void k_emit(const uint4* __restrict__ rec
 
 // Emission under the ellipse rule: thread j walks its splat's box row by row and writes the kept tiles at
 // offsets[j] onwards (each splat's pairs are contiguous; the stores are not coalesced across threads).
-template <typename K>
+template <typename K, bool kPacked = false>
 __global__ __launch_bounds__(kThreads) void k_emit_ellipse(const float* __restrict__ splats,
                                                            const uint4* __restrict__ rects,
                                                            const float* __restrict__ depths, uint32_t n,
                                                            const uint32_t* __restrict__ order, uint32_t tiles_x,
                                                            const uint64_t* __restrict__ offsets,
                                                            uint64_t num_pairs, K* __restrict__ keys,
-                                                           uint32_t* __restrict__ vals) {
+                                                           uint32_t* __restrict__ vals, uint32_t idx_bits) {
   const uint32_t j = blockIdx.x * kThreads + threadIdx.x;
   if (j >= n) return;
   const uint32_t i = order ? order[j] : j;
@@ -381,9 +385,11 @@ __global__ __launch_bounds__(kThreads) void k_emit_ellipse(const float* __restri
       const uint64_t tile = uint64_t(ty) * tiles_x + tx;
       if constexpr (sizeof(K) == 8)
         keys[p] = (tile << 32) | dbits;
+      else if constexpr (kPacked)
+        keys[p] = K((uint32_t(tile) << idx_bits) | i);
       else
         keys[p] = K(tile);
-      vals[p] = i;
+      if constexpr (!kPacked) vals[p] = i;
       ++p;
     }
 }
@@ -391,7 +397,8 @@ __global__ __launch_bounds__(kThreads) void k_emit_ellipse(const float* __restri
 // Per-tile ranges from the sorted keys: the boundary between pairs i-1 and i (i in [0, P]) opens the ranges of
 // the tiles after the previous pair's and closes those before the current pair's. Each thread takes kRangeItems
 // consecutive boundaries (16-byte loads of 32-bit keys). With keys_final (the presort scheme when no sort pass
-// ran) it also writes the final 64-bit keys (tile << 32 | depth bits).
+// ran) it also writes the final 64-bit keys (tile << 32 | depth bits). 32-bit keys hold the tile id above bit
+// tile_shift (packed keys; 0 otherwise).
 constexpr uint32_t kRangeItems = 4;
 
 template <typename K>
@@ -399,17 +406,19 @@ __global__ __launch_bounds__(kThreads) void k_ranges(const K* __restrict__ keys,
                                                      uint32_t P, uint32_t num_tiles,
                                                      const float* __restrict__ depths, uint32_t n,
                                                      uint64_t* __restrict__ keys_final,
-                                                     uint32_t* __restrict__ ranges) {
+                                                     uint32_t* __restrict__ ranges, uint32_t tile_shift) {
   const uint64_t i0 = (uint64_t(blockIdx.x) * kThreads + threadIdx.x) * kRangeItems;
   if (i0 > P) return;
-  auto tile_of = [](K k) -> int64_t { return sizeof(K) == 8 ? int64_t(uint64_t(k) >> 32) : int64_t(k); };
+  auto tile_of = [tile_shift](K k) -> int64_t {
+    return sizeof(K) == 8 ? int64_t(uint64_t(k) >> 32) : int64_t(uint32_t(k) >> tile_shift);
+  };
   // tiles of pairs i0 - 1 .. i0 + kRangeItems - 1 (-1 before the first pair, num_tiles from pair P on)
   int64_t t[kRangeItems + 1];
   uint32_t v[kRangeItems];
   t[0] = i0 == 0 ? -1 : tile_of(keys[i0 - 1]);
   if (sizeof(K) == 4 && i0 + kRangeItems <= P) {
     const uint4 kk = *reinterpret_cast<const uint4*>(keys + i0);
-    t[1] = kk.x, t[2] = kk.y, t[3] = kk.z, t[4] = kk.w;
+    t[1] = kk.x >> tile_shift, t[2] = kk.y >> tile_shift, t[3] = kk.z >> tile_shift, t[4] = kk.w >> tile_shift;
   } else {
 #pragma unroll
     for (uint32_t q = 0; q < kRangeItems; ++q) t[q + 1] = i0 + q < P ? tile_of(keys[i0 + q]) : int64_t(num_tiles);
@@ -611,17 +620,41 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   const uint32_t tile_bits = bits_of(num_tiles - 1);
   int res = 0;
   uint64_t* final_k = nullptr;
-  if (presort) {
+  uint32_t* sorted_v = nullptr;
+  // the splat index and the tile id share one 32-bit key when they fit (and there is a tile pass to unpack it)
+  const uint32_t idx_bits = bits_of(n ? n - 1 : 0);
+  const bool packed = presort && n && P > 0 && tile_bits > 0 && idx_bits + tile_bits <= 32;
+  if (packed) {
+    uint32_t* kb[2] = {static_cast<uint32_t*>(a.keys[0].ptr), static_cast<uint32_t*>(a.keys[1].ptr)};
+    if (ellipse)
+      hipLaunchKernelGGL((k_emit_ellipse<uint32_t, true>), dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats,
+                         rects, depths, n, order, tiles_x, offsets, P, kb[0], static_cast<uint32_t*>(nullptr),
+                         idx_bits);
+    else
+      hipLaunchKernelGGL((k_emit<uint32_t, true>), dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, rects, depths,
+                         n, order, tiles_x, offsets, P, kb[0], static_cast<uint32_t*>(nullptr), idx_bits);
+    res = (sort_passes(tile_bits) & 1u) ? 1 : 0;  // the first pass writes buffer 1 either way
+    if (ctx->bin_keys) {
+      if ((st = grow(ctx, a.order_alt, std::max<size_t>(size_t(n) * 8, size_t(P) * 8)))) return st;
+      final_k = static_cast<uint64_t*>(a.order_alt.ptr);
+    }
+    st = radix_sort_tiles_packed(ctx, s, kb[0], P, idx_bits, tile_bits, kb[res], kb[1 - res], v0, final_k, depths, n);
+    if (st) return st;
+    hipLaunchKernelGGL(k_ranges<uint32_t>, dim3(grid_for(P + 1, kThreads * kRangeItems)), dim3(kThreads), 0, s,
+                       kb[res], static_cast<const uint32_t*>(v0), uint32_t(P), uint32_t(num_tiles), depths, n,
+                       static_cast<uint64_t*>(nullptr), ranges, idx_bits);
+    sorted_v = v0;
+  } else if (presort) {
     // tile ids as 32-bit keys, sorted by their tile_bits low bits
     uint32_t* kb[2] = {static_cast<uint32_t*>(a.keys[0].ptr), static_cast<uint32_t*>(a.keys[1].ptr)};
     if (n)
     {
       if (ellipse)
         hipLaunchKernelGGL(k_emit_ellipse<uint32_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats, rects,
-                           depths, n, order, tiles_x, offsets, P, kb[0], v0);
+                           depths, n, order, tiles_x, offsets, P, kb[0], v0, 0u);
       else
         hipLaunchKernelGGL(k_emit<uint32_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, rects, depths, n, order,
-                           tiles_x, offsets, P, kb[0], v0);
+                           tiles_x, offsets, P, kb[0], v0, 0u);
     }
     // The 64-bit keys go to the key buffer the sorted tile ids do not end in, written by the last sort pass (or by
     // the range kernel when there is no pass).
@@ -645,17 +678,18 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     if (!keys_done) final_k = ranges_final = static_cast<uint64_t*>(a.keys[1 - res].ptr);
     hipLaunchKernelGGL(k_ranges<uint32_t>, dim3(grid_for(P + 1, kThreads * kRangeItems)), dim3(kThreads), 0, s,
                        kb[res], static_cast<const uint32_t*>(a.vals[res].ptr), uint32_t(P), uint32_t(num_tiles),
-                       depths, n, ranges_final, ranges);
+                       depths, n, ranges_final, ranges, 0u);
+    sorted_v = static_cast<uint32_t*>(a.vals[res].ptr);
   } else {
     uint64_t* kb[2] = {static_cast<uint64_t*>(a.keys[0].ptr), static_cast<uint64_t*>(a.keys[1].ptr)};
     if (n)
     {
       if (ellipse)
         hipLaunchKernelGGL(k_emit_ellipse<uint64_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats, rects,
-                           depths, n, order, tiles_x, offsets, P, kb[0], v0);
+                           depths, n, order, tiles_x, offsets, P, kb[0], v0, 0u);
       else
         hipLaunchKernelGGL(k_emit<uint64_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, rects, depths, n, order,
-                           tiles_x, offsets, P, kb[0], v0);
+                           tiles_x, offsets, P, kb[0], v0, 0u);
     }
     if (P > 0) {
       const uint32_t key_bits = 32 + tile_bits;
@@ -668,9 +702,9 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     final_k = kb[res];
     hipLaunchKernelGGL(k_ranges<uint64_t>, dim3(grid_for(P + 1, kThreads * kRangeItems)), dim3(kThreads), 0, s,
                        kb[res], static_cast<const uint32_t*>(a.vals[res].ptr), uint32_t(P), uint32_t(num_tiles),
-                       depths, n, static_cast<uint64_t*>(nullptr), ranges);
+                       depths, n, static_cast<uint64_t*>(nullptr), ranges, 0u);
+    sorted_v = static_cast<uint32_t*>(a.vals[res].ptr);
   }
-  uint32_t* sorted_v = static_cast<uint32_t*>(a.vals[res].ptr);
   timing_mark(ctx, GSR_STAGE_BIN, s, true);
   if ((st = check_launch(ctx, "gsr_bin emit/sort/ranges"))) return st;
   out->keys = final_k;

@@ -120,4 +120,11 @@ gsr_status radix_sort_tiles_final(gsr_ctx* ctx, hipStream_t s, const uint32_t* k
                                   uint32_t* tmp_keys, uint32_t* tmp_vals, uint64_t* keys_final,
                                   const float* depths, uint32_t n_depths);
 
+// The tile sort on packed keys (tile << idx_bits) | value (idx_bits + tile_bits <= 32): sorts stably by the tile
+// field, keys only; the last pass writes the sorted keys to keys_out, the values to vals_out and, when keys_final
+// is not null, keys_final[g] = (tile << 32) | bits(depths[value]). Same pass-parity rule as radix_sort_launch.
+gsr_status radix_sort_tiles_packed(gsr_ctx* ctx, hipStream_t s, const uint32_t* keys_in, uint64_t n,
+                                   uint32_t idx_bits, uint32_t tile_bits, uint32_t* keys_out, uint32_t* tmp_keys,
+                                   uint32_t* vals_out, uint64_t* keys_final, const float* depths, uint32_t n_depths);
+
 }  // namespace gsr

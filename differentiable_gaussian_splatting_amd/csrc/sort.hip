@@ -9,6 +9,11 @@
 // Digits above key_bits are identity passes of a stable sort and are never run (the constant-digit pass skip of
 // the C0 resident arena + C1 pass skip page, section 2 table, row "C1"). Small sorts use 1024-key blocks so the
 // grid still covers the 256 compute units; large ones 2048-key blocks.
+//
+// Packed form (binning's tile sort when the splat index and the tile id fit 32 bits together): each key is
+// (tile << idx_bits) | splat, there is no separate value array, and the passes sort by the tile field only; the
+// last pass unpacks the splat index into the value output (and the 64-bit keys when asked). Every pass then moves
+// 4 bytes per pair instead of 8.
 #include "gsr_internal.hpp"
 #include "scan_common.hpp"
 
@@ -86,19 +91,22 @@ __global__ __launch_bounds__(kThreads) void k_scan_rows(uint32_t* __restrict__ h
   if (threadIdx.x == 0) digit_tot[blockIdx.x] = total;
 }
 
-// kFinal (32-bit tile ids, last pass): also writes keys_final[g] = (tile << 32) | bits(depths[value]).
-template <typename K, uint32_t kItems, uint32_t kBits, bool kFinal>
+// kFinal (32-bit tile ids, last pass): also writes keys_final[g] = (tile << 32) | bits(depths[value]) (when
+// keys_final is not null). kPacked: keys are (tile << idx_bits) | value with no value array; a kFinal pass writes
+// the unpacked values to vals_out, other passes write keys only.
+template <typename K, uint32_t kItems, uint32_t kBits, bool kFinal, bool kPacked = false>
 __global__ __launch_bounds__(kThreads) void k_scatter(const K* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
                                                       uint64_t n, uint32_t shift, uint32_t nb,
                                                       const uint32_t* __restrict__ hist,
                                                       const uint32_t* __restrict__ digit_tot, K* __restrict__ keys_out,
                                                       uint32_t* __restrict__ vals_out,
                                                       uint64_t* __restrict__ keys_final,
-                                                      const float* __restrict__ depths, uint32_t n_depths) {
+                                                      const float* __restrict__ depths, uint32_t n_depths,
+                                                      uint32_t idx_bits) {
   constexpr uint32_t kRadix = 1u << kBits, kWaves = kThreads / kWave;
   constexpr uint32_t kBlockKeys = kThreads * kItems, kWaveKeys = kWave * kItems;
   __shared__ K s_keys[kBlockKeys];
-  __shared__ uint32_t s_vals[kBlockKeys];
+  __shared__ uint32_t s_vals[kPacked ? 1 : kBlockKeys];
   __shared__ uint32_t s_wave[kWaves][kRadix];  // per-wave running digit counts, then wave prefixes
   __shared__ uint32_t s_dstart[kRadix];        // first LDS slot of each digit in this block
   __shared__ uint32_t s_gbase[kRadix];         // global position of this block's first key of each digit
@@ -114,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void k_scatter(const K* __restrict__ keys
   for (uint32_t i = 0; i < kItems; ++i) {
     const uint64_t idx = min(base + uint64_t(i) * kWave + lane, n - 1);
     k[i] = keys_in[idx];
-    v[i] = vals_in[idx];
+    if constexpr (!kPacked) v[i] = vals_in[idx];
   }
   for (uint32_t i = tid; i < kWaves * kRadix; i += kThreads) (&s_wave[0][0])[i] = 0;
   {
@@ -160,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void k_scatter(const K* __restrict__ keys
       const uint32_t d = digit_of<kBits>(k[i], shift);
       const uint32_t pos = s_dstart[d] + s_wave[w][d] + r[i];
       s_keys[pos] = k[i];
-      s_vals[pos] = v[i];
+      if constexpr (!kPacked) s_vals[pos] = v[i];
     }
   }
   __syncthreads();
@@ -171,11 +179,21 @@ __global__ __launch_bounds__(kThreads) void k_scatter(const K* __restrict__ keys
     const uint32_t d = digit_of<kBits>(kk, shift);
     const uint64_t g = uint64_t(s_gbase[d]) + (j - s_dstart[d]);
     if (g < n) {  // always true for consistent counts; keeps a miscount from writing out of bounds
-      const uint32_t val = s_vals[j];
       keys_out[g] = kk;
-      vals_out[g] = val;
-      if constexpr (kFinal)
-        keys_final[g] = (uint64_t(kk) << 32) | (val < n_depths ? __float_as_uint(depths[val]) : 0u);
+      if constexpr (kPacked) {
+        if constexpr (kFinal) {
+          const uint32_t val = uint32_t(kk) & ((1u << idx_bits) - 1u);
+          vals_out[g] = val;
+          if (keys_final)
+            keys_final[g] = (uint64_t(uint32_t(kk) >> idx_bits) << 32) |
+                            (val < n_depths ? __float_as_uint(depths[val]) : 0u);
+        }
+      } else {
+        const uint32_t val = s_vals[j];
+        vals_out[g] = val;
+        if constexpr (kFinal)
+          keys_final[g] = (uint64_t(kk) << 32) | (val < n_depths ? __float_as_uint(depths[val]) : 0u);
+      }
     }
   }
 }
@@ -184,6 +202,8 @@ struct FinalKeys {
   uint64_t* keys = nullptr;
   const float* depths = nullptr;
   uint32_t n = 0;
+  bool packed = false;    // keys are (tile << idx_bits) | value; vals_in is unused
+  uint32_t idx_bits = 0;  // packed: width of the value field, which the passes skip
 };
 
 template <typename K, uint32_t kItems, uint32_t kBits>
@@ -204,18 +224,35 @@ gsr_status run_passes(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint3
     K* dk = to_out ? keys_out : tmp_keys;
     uint32_t* dv = to_out ? vals_out : tmp_vals;
     if (p == 0 && dk == keys_in) return fail(ctx, GSR_EINVAL, "radix sort: first pass would overwrite its input");
-    const uint32_t shift = kBits * p;
+    const uint32_t shift = fin.idx_bits + kBits * p;
     hipLaunchKernelGGL((k_upsweep<K, kItems, kBits>), dim3(nb), dim3(kThreads), 0, s, src_k, n, shift, nb, hist);
     hipLaunchKernelGGL(k_scan_rows, dim3(kRadix), dim3(kThreads), 0, s, hist, nb, tot);
+    const bool last = p + 1 == passes;
+    if constexpr (sizeof(K) == 4) {
+      if (fin.packed) {
+        // keys only; the last pass unpacks the values (into vals_out, which the caller sized)
+        if (last)
+          hipLaunchKernelGGL((k_scatter<K, kItems, kBits, true, true>), dim3(nb), dim3(kThreads), 0, s, src_k,
+                             static_cast<const uint32_t*>(nullptr), n, shift, nb, hist, tot, dk, vals_out, fin.keys,
+                             fin.depths, fin.n, fin.idx_bits);
+        else
+          hipLaunchKernelGGL((k_scatter<K, kItems, kBits, false, true>), dim3(nb), dim3(kThreads), 0, s, src_k,
+                             static_cast<const uint32_t*>(nullptr), n, shift, nb, hist, tot, dk,
+                             static_cast<uint32_t*>(nullptr), static_cast<uint64_t*>(nullptr),
+                             static_cast<const float*>(nullptr), 0u, fin.idx_bits);
+        src_k = dk;
+        continue;
+      }
+    }
     bool final_pass = false;
-    if constexpr (sizeof(K) == 4) final_pass = fin.keys && p + 1 == passes;
+    if constexpr (sizeof(K) == 4) final_pass = fin.keys && last;
     if (final_pass)
       hipLaunchKernelGGL((k_scatter<K, kItems, kBits, true>), dim3(nb), dim3(kThreads), 0, s, src_k, src_v, n, shift,
-                         nb, hist, tot, dk, dv, fin.keys, fin.depths, fin.n);
+                         nb, hist, tot, dk, dv, fin.keys, fin.depths, fin.n, 0u);
     else
       hipLaunchKernelGGL((k_scatter<K, kItems, kBits, false>), dim3(nb), dim3(kThreads), 0, s, src_k, src_v, n, shift,
                          nb, hist, tot, dk, dv, static_cast<uint64_t*>(nullptr), static_cast<const float*>(nullptr),
-                         0u);
+                         0u, 0u);
     src_k = dk;
     src_v = dv;
   }
@@ -271,6 +308,16 @@ gsr_status radix_sort_tiles_final(gsr_ctx* ctx, hipStream_t s, const uint32_t* k
   if (key_bits == 0) return fail(ctx, GSR_EINVAL, "radix sort: final keys need at least one pass");
   return sort_any<uint32_t>(ctx, s, keys_in, vals_in, n, key_bits, keys_out, vals_out, tmp_keys, tmp_vals,
                             FinalKeys{keys_final, depths, n_depths});
+}
+
+gsr_status radix_sort_tiles_packed(gsr_ctx* ctx, hipStream_t s, const uint32_t* keys_in, uint64_t n,
+                                   uint32_t idx_bits, uint32_t tile_bits, uint32_t* keys_out, uint32_t* tmp_keys,
+                                   uint32_t* vals_out, uint64_t* keys_final, const float* depths, uint32_t n_depths) {
+  if (tile_bits == 0 || idx_bits + tile_bits > 32)
+    return fail(ctx, GSR_EINVAL, "radix sort: packed keys need 1..32 - idx_bits tile bits");
+  if (!vals_out) return fail(ctx, GSR_EINVAL, "radix sort: packed keys need a value output");
+  FinalKeys fin{keys_final, depths, n_depths, true, idx_bits};
+  return sort_any<uint32_t>(ctx, s, keys_in, nullptr, n, tile_bits, keys_out, vals_out, tmp_keys, nullptr, fin);
 }
 
 template gsr_status radix_sort_launch<uint32_t>(gsr_ctx*, hipStream_t, const uint32_t*, const uint32_t*, uint64_t,

@@ -87,6 +87,25 @@ def test_bin_empty_and_all_culled(ctx, scheme):
     assert b.num_pairs == 0
 
 
+@pytest.mark.parametrize("w,h,n", [(16, 16, 700), (1024, 1024, 1 << 20), (65536, 32768, 3000)])
+def test_bin_packed_and_unpacked_tile_sort(ctx, w, h, n):
+    """The presort scheme packs (tile, splat) into one 32-bit key when bits(n - 1) + bits(tiles - 1) <= 32: a
+    single tile (no tile pass: not packed), 2^20 splats on 4096 tiles (exactly 32 bits: packed), and 2^23 tiles
+    with 3000 splats (36 bits: the two-array form). All bit-exact against the oracle."""
+    banner(f"bin packing {w}x{h} n={n}")
+    # round splats of s in 0.5-20 px over the image (drawn here: the scene generator's per-pixel upstream gradient
+    # would not fit the largest image)
+    rng = np.random.default_rng(n + w)
+    s = np.exp(rng.uniform(np.log(0.5), np.log(20.0), n))
+    sp = np.zeros((n, 9), np.float32)
+    sp[:, 0], sp[:, 1] = rng.uniform(0, w, n), rng.uniform(0, h, n)
+    sp[:, 2] = sp[:, 4] = 1.0 / s ** 2
+    sp[:, 5:8] = rng.uniform(0, 1, (n, 3))
+    sp[:, 8] = rng.uniform(0.05, 1.0, n)
+    depths = rng.uniform(0.1, 10.0, n).astype(np.float32)
+    assert_bins_equal(ctx, sp, depths, w, h, "presort")
+
+
 def test_bin_arena_growth_and_reuse(ctx):
     """A fresh context grows its arena call by call; results stay bit-exact, and a smaller call after a larger
     one reuses the arena."""
