@@ -312,6 +312,8 @@ def main():
         for k, r in roofs.items():
             r["frac"] = r["achieved"] / r["peak"]
             r["traffic"] = profiling.traffic_for(profiling.STAGE_KERNEL[k], traffic_md)
+            if r["bound"] == "alu":  # the share of VALU issue slots the kernel used (its counters, same record)
+                r["valu_issue_frac"] = profiling.valu_issue_for(profiling.STAGE_KERNEL[k], traffic_md)
         for k in ("forward", "backward"):
             roofs[k]["frac_of_published_157_3"] = roofs[k]["achieved"] / ALU_PUBLISHED_TFLOPS
         dominant = max(("forward", "backward", "adam"), key=lambda k: kernel_ms[k])

@@ -182,17 +182,17 @@ def pmc_md(base: str, cmd: str, workload: str, first: int | None = None) -> str:
             vals.append("" if v is None else f"{v:.4g}")
         fetch = passes.get("fetch", ({}, {}))[0].get(k, {}).get("FETCH_SIZE")
         write = passes.get("write", ({}, {}))[0].get(k, {}).get("WRITE_SIZE")
+        v = passes.get("valu", ({}, {}))[0].get(k, {})
+        f = passes.get("flops", ({}, {}))[0].get(k, {})
+        ns = v.get("_ns")
+        issue = v["SQ_INSTS_VALU"] * 4 / (1024 * ns * 2.4) if ns and "SQ_INSTS_VALU" in v else None
         hbm = None
         if fetch is not None and write is not None and len(scale) == 2:
             hbm = fetch * 1024 * scale["FETCH_SIZE"] + write * 1024 * scale["WRITE_SIZE"]
             if base_kernel(k) in KERNEL_SOURCES:  # one record per instance (k_adam<false> and <true> differ)
                 inst = short_name(k).replace(", ", ",").replace("unsigned int", "uint32")
-                record[inst] = {"hbm_bytes": hbm, "fetch_kib": fetch, "write_kib": write,
+                record[inst] = {"hbm_bytes": hbm, "fetch_kib": fetch, "write_kib": write, "valu_issue": issue,
                                 "sources": source_hash(inst)}
-        v = passes.get("valu", ({}, {}))[0].get(k, {})
-        f = passes.get("flops", ({}, {}))[0].get(k, {})
-        ns = v.get("_ns")
-        issue = v["SQ_INSTS_VALU"] * 4 / (1024 * ns * 2.4) if ns and "SQ_INSTS_VALU" in v else None
         tf = (64 * (f.get("SQ_INSTS_VALU_FLOPS_FP32", 0) + f.get("SQ_INSTS_VALU_FLOPS_FP64", 0)) / (f["_ns"] * 1e3)
               if f.get("_ns") else None)
         lines.append(f"| `{k[:60]}` | " + " | ".join(vals) + f" | {'' if issue is None else f'{issue:.3f}'} | "
@@ -225,6 +225,16 @@ def traffic_for(kernel: str, md_path: str):
         return None
     k = rec["kernels"][kernel]
     return k["hbm_bytes"] if k.get("sources") == source_hash(kernel) else None
+
+
+def valu_issue_for(kernel, md_path: str):
+    """Recorded fraction of the chip's VALU issue slots the kernel instance used (SQ_INSTS_VALU x 4 cycles over
+    1024 SIMDs x duration x 2.4 GHz), or None when unrecorded or its sources changed since."""
+    rec = read_traffic(md_path)
+    if not rec or kernel not in rec.get("kernels", {}):
+        return None
+    k = rec["kernels"][kernel]
+    return k.get("valu_issue") if k.get("sources") == source_hash(kernel) else None
 
 
 def main(argv=None):

@@ -224,6 +224,31 @@ def test_skips_change_no_result(ctx, name):
         assert np.array_equal(ga, gb)
 
 
+def test_backward_zeroes_and_fills_unaligned_gradient_buffers(ctx):
+    """splats_grad starting 4 bytes past a 16-byte boundary (the zero fill takes its element-by-element path) gets
+    the same bits as an aligned one, over buffers that held NaN before the call. One non-zero upstream pixel makes
+    each gradient a single term, so both runs are exact and comparable bit for bit."""
+    import torch
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("backward into an unaligned gradient buffer")
+    sc = scene("raster84k")
+    sp = dev(sc.splats)
+    bins = gsr.gsr_bin(ctx, sp, dev(sc.depths), sc.width, sc.height)
+    out, ft, lc = run_forward(ctx, sp, bins, sc.width, sc.height)
+    v = np.zeros((sc.height, sc.width, 4), np.float32)
+    v[400, 300, :3] = (0.5, -1.0, 2.0)
+    n = sc.splats.shape[0]
+    aligned = torch.full((n, 9), float("nan"), device="cuda")
+    raw = torch.full((n * 9 + 1,), float("nan"), device="cuda")
+    unaligned = raw[1:].view(n, 9)
+    assert unaligned.data_ptr() % 16 == 4
+    for g in (aligned, unaligned):
+        gsr.gsr_render_backward(ctx, sp, bins, sc.width, sc.height, out, ft, lc, dev(v), g)
+    a, u = host(aligned), host(unaligned)
+    assert not np.isnan(a).any() and (a != 0).any()
+    assert a.tobytes() == u.tobytes()
+
+
 def test_backward_single_pixel_matches_oracle(ctx):
     """With one non-zero upstream pixel each gradient is one per-pixel term: no summation order is involved."""
     import oracle
