@@ -68,3 +68,38 @@ def test_null_context_is_rejected_without_a_device(lib):
     assert lib.gsr_set_option(None, 1, 0) == gsr.GSR_EINVAL
     assert lib.gsr_reserve(None, 0, 0) == gsr.GSR_EINVAL
     assert lib.gsr_create(None, 0) == gsr.GSR_EINVAL
+
+
+def test_header_is_c_and_the_binding_matches_its_layouts(tmp_path):
+    """include/gsr.h compiles as C99 and C++11 with warnings as errors, and a C program built from it reports the
+    sizes and field offsets of the structs and the values of the constants the ctypes binding uses."""
+    import subprocess
+
+    from differentiable_gaussian_splatting_amd import gsr
+    structs = {"gsr_bins": gsr.gsr_bins, "gsr_adam_group": gsr.gsr_adam_group, "gsr_camera": gsr.gsr_camera}
+    lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "gsr.h"', "int main(void) {"]
+    for name, cls in structs.items():
+        lines.append(f'  printf("{name} size %zu\\n", sizeof({name}));')
+        for field, _ in cls._fields_:
+            lines.append(f'  printf("{name}.{field} %zu\\n", offsetof({name}, {field}));')
+    consts = [c for c in dir(gsr) if c.startswith("GSR_") and isinstance(getattr(gsr, c), int)]
+    for c in consts:
+        lines.append(f'  printf("{c} %d\\n", (int)({c}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    inc = os.path.join(ROOT, "include")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", inc, str(src), "-o", str(exe)], check=True)
+    cpp = tmp_path / "h.cpp"
+    cpp.write_text('#include "gsr.h"\nint main() { return 0; }\n')
+    subprocess.run(["g++", "-std=c++11", "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-I", inc, str(cpp)],
+                   check=True)
+    got = dict(line.rsplit(" ", 1) for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                                 text=True).stdout.splitlines())
+    for name, cls in structs.items():
+        assert int(got[f"{name} size"]) == ctypes.sizeof(cls), name
+        for field, _ in cls._fields_:
+            assert int(got[f"{name}.{field}"]) == getattr(cls, field).offset, f"{name}.{field}"
+    for c in consts:
+        assert int(got[c]) == getattr(gsr, c), c
