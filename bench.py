@@ -239,7 +239,8 @@ def main():
     stage_ms_median = {nm: float(np.median([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
                        for i, nm in enumerate(names)}
     kernel_stage = {"bin": gsr.GSR_STAGE_BIN, "forward": gsr.GSR_STAGE_FORWARD, "backward": gsr.GSR_STAGE_BACKWARD,
-                    "adam": gsr.GSR_STAGE_ADAM}
+                    "adam": gsr.GSR_STAGE_ADAM, "depth_sort": gsr.GSR_STAGE_DEPTH_SORT,
+                    "tile_sort": gsr.GSR_STAGE_TILE_SORT}
     kernel_ms = {}
     for nm, stg in kernel_stage.items():
         t = gsr.gsr_kernel_times(ctx, stg)
@@ -305,12 +306,16 @@ def main():
         }
         for k, r in roofs.items():
             r["kernel_ms"] = kernel_ms[k]
+        roofs["sort"] = sort_roofline(args, N, P, W, H, kernel_ms)
         # HBM bytes per launch from the committed counter summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated);
         # null when the kernel's sources changed since the counters were taken
         from differentiable_gaussian_splatting_amd import profiling
         traffic_md = os.path.join(ROOT, "profiles", f"hbm_counters_{args.workload}.md")
         for k, r in roofs.items():
             r["frac"] = r["achieved"] / r["peak"]
+            if k == "sort":
+                r["traffic"] = profiling.traffic_for(profiling.sort_kernels(r["passes"]), traffic_md)
+                continue
             r["traffic"] = profiling.traffic_for(profiling.STAGE_KERNEL[k], traffic_md)
             if r["bound"] == "alu":  # the share of VALU issue slots the kernel used (its counters, same record)
                 r["valu_issue_frac"] = profiling.valu_issue_for(profiling.STAGE_KERNEL[k], traffic_md)
@@ -337,6 +342,31 @@ def main():
     result["projection"] = bench_projection(args, ctx, gsr, scenes, sc, hp=hp, bc=bc)
     print(json.dumps(result), flush=True)
     ctx.close()
+
+
+def sort_roofline(args, N, P, W, H, kernel_ms):
+    """The binning's two radix sorts (presort scheme) against HBM: algorithmic bytes of this scheme per launch over
+    their kernels' own time. Depth sort: 4 passes of 8-bit digits over the n 32-bit depth keys with their indices,
+    each pass reading the keys for the histogram (4 B) and reading and writing key and index (16 B). Tile sort: 2
+    passes of 6-bit digits over the pairs; packed (tile and splat in one 32-bit word when they fit) a pass reads
+    the words twice and writes them once (12 B), and the last one also writes the splat index (4 B), the 64-bit key
+    (8 B) and gathers the depth (4 B); unpacked each pass moves tile id and index (20 B) and the last one adds the
+    64-bit key and the depth gather (12 B). The pages' target is stated for their 64-bit key sort, P (8 + 24 d) B at
+    d = 6 passes, at 70 % of the peak: its time is reported beside ours."""
+    tiles = ((W + 15) // 16) * ((H + 15) // 16)
+    bits = lambda v: int(v).bit_length()
+    tile_bits = bits(tiles - 1)
+    tile_passes = (tile_bits + 5) // 6
+    packed = N > 0 and tile_bits > 0 and bits(N - 1) + tile_bits <= 32
+    per_pair = (12 * tile_passes + 16) if packed else (20 * tile_passes + 12)
+    by = 4 * 20 * N + per_pair * P
+    ms = kernel_ms["depth_sort"] + kernel_ms["tile_sort"]
+    pages_bytes = P * (8 + 24 * 6)
+    return {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "work_per_launch": by, "kernel_ms": ms, "depth_sort_ms": kernel_ms["depth_sort"],
+            "tile_sort_ms": kernel_ms["tile_sort"], "packed": packed, "passes": {"depth": 4, "tile": tile_passes},
+            "pages_64bit_sort_bytes": pages_bytes,
+            "pages_target_ms_at_70pct": pages_bytes / (0.7 * HBM_PEAK_GBS * 1e9) * 1e3}
 
 
 def bench_deterministic_backward(args, ctx, gsr, torch, np, stream, splats, b, W, H, out_rgba, final_T, last_contrib,

@@ -590,9 +590,11 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   const uint32_t* order = nullptr;
   if (presort && n) {
     // 4 passes (even): the sorted result lands back in (order, order_vals)
+    timing_mark(ctx, GSR_STAGE_DEPTH_SORT, s, false);
     st = radix_sort_launch<uint32_t>(ctx, s, ok, ov, n, 32, ok, ov, static_cast<uint32_t*>(a.order_alt.ptr),
                                      static_cast<uint32_t*>(a.order_vals_alt.ptr));
     if (st) return st;
+    timing_mark(ctx, GSR_STAGE_DEPTH_SORT, s, true);
     order = ov;
   }
   // offsets in emission order (depth order for the presort scheme); the scan rewrites offsets[n] with the same total
@@ -638,8 +640,10 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
       if ((st = grow(ctx, a.order_alt, std::max<size_t>(size_t(n) * 8, size_t(P) * 8)))) return st;
       final_k = static_cast<uint64_t*>(a.order_alt.ptr);
     }
+    timing_mark(ctx, GSR_STAGE_TILE_SORT, s, false);
     st = radix_sort_tiles_packed(ctx, s, kb[0], P, idx_bits, tile_bits, kb[res], kb[1 - res], v0, final_k, depths, n);
     if (st) return st;
+    timing_mark(ctx, GSR_STAGE_TILE_SORT, s, true);
     hipLaunchKernelGGL(k_ranges<uint32_t>, dim3(grid_for(P + 1, kThreads * kRangeItems)), dim3(kThreads), 0, s,
                        kb[res], static_cast<const uint32_t*>(v0), uint32_t(P), uint32_t(num_tiles), depths, n,
                        static_cast<uint64_t*>(nullptr), ranges, idx_bits);
@@ -663,6 +667,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
       res = (sort_passes(tile_bits) & 1u) ? 1 : 0;  // odd pass count: result in buffer 1
       uint32_t* vr = static_cast<uint32_t*>(a.vals[res].ptr);
       uint32_t* vt = static_cast<uint32_t*>(a.vals[1 - res].ptr);
+      timing_mark(ctx, GSR_STAGE_TILE_SORT, s, false);
       if (ctx->bin_keys) {
         // the last pass reads buffer 1 - res and writes buffer res; the 64-bit keys need a third place
         if ((st = grow(ctx, a.order_alt, std::max<size_t>(size_t(n) * 8, size_t(P) * 8)))) return st;
@@ -673,6 +678,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
         st = radix_sort_launch<uint32_t>(ctx, s, kb[0], v0, P, tile_bits, kb[res], vr, kb[1 - res], vt);
       }
       if (st) return st;
+      timing_mark(ctx, GSR_STAGE_TILE_SORT, s, true);
     }
     uint64_t* ranges_final = nullptr;
     if (!keys_done) final_k = ranges_final = static_cast<uint64_t*>(a.keys[1 - res].ptr);
@@ -694,10 +700,12 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     if (P > 0) {
       const uint32_t key_bits = 32 + tile_bits;
       res = (sort_passes(key_bits) & 1u) ? 1 : 0;
+      timing_mark(ctx, GSR_STAGE_TILE_SORT, s, false);
       st = radix_sort_launch<uint64_t>(ctx, s, kb[0], v0, P, key_bits, kb[res],
                                        static_cast<uint32_t*>(a.vals[res].ptr), kb[1 - res],
                                        static_cast<uint32_t*>(a.vals[1 - res].ptr));
       if (st) return st;
+      timing_mark(ctx, GSR_STAGE_TILE_SORT, s, true);
     }
     final_k = kb[res];
     hipLaunchKernelGGL(k_ranges<uint64_t>, dim3(grid_for(P + 1, kThreads * kRangeItems)), dim3(kThreads), 0, s,

@@ -8,7 +8,7 @@
 //            contiguously.
 // Digits above key_bits are identity passes of a stable sort and are never run (the constant-digit pass skip of
 // the C0 resident arena + C1 pass skip page, section 2 table, row "C1"). Small sorts use 1024-key blocks so the
-// grid still covers the 256 compute units; large ones 2048-key blocks.
+// grid still covers the 256 compute units; large ones 4096-key blocks.
 //
 // Packed form (binning's tile sort when the splat index and the tile id fit 32 bits together): each key is
 // (tile << idx_bits) | splat, there is no separate value array, and the passes sort by the tile field only; the
@@ -21,7 +21,8 @@ namespace gsr {
 namespace {
 
 constexpr uint32_t kThreads = 256;
-constexpr uint64_t kSmallSort = uint64_t(1) << 21;  // below this many keys: 4 keys per thread, else 8
+constexpr uint64_t kSmallSort = uint64_t(1) << 21;  // below this many keys: 4 keys per thread, else 16
+constexpr uint32_t kLargeItems = 16;  // 4096-key blocks: digit runs twice as long in the scatter's writes
 
 template <uint32_t kBits, typename K>
 __device__ __forceinline__ uint32_t digit_of(K k, uint32_t shift) {
@@ -266,7 +267,7 @@ constexpr uint32_t kNarrowKeyBits = 12;
 }  // namespace
 
 uint32_t sort_blocks(uint64_t n) {
-  const uint64_t per = kThreads * (n < kSmallSort ? 4u : 8u);
+  const uint64_t per = kThreads * (n < kSmallSort ? 4u : kLargeItems);
   return uint32_t((n + per - 1) / per);
 }
 
@@ -287,11 +288,13 @@ gsr_status sort_any(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint32_
   if (key_bits <= kNarrowKeyBits) {
     if (n < kSmallSort)
       return run_passes<K, 4, 6>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals, fin);
-    return run_passes<K, 8, 6>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals, fin);
+    return run_passes<K, kLargeItems, 6>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals,
+                                         fin);
   }
   if (n < kSmallSort)
     return run_passes<K, 4, 8>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals, fin);
-  return run_passes<K, 8, 8>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals, fin);
+  return run_passes<K, kLargeItems, 8>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals,
+                                       fin);
 }
 }  // namespace
 

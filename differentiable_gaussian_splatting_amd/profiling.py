@@ -37,6 +37,9 @@ KERNEL_SOURCES = {
     "k_project_backward": ["project.hip", "gsr_internal.hpp"],
     "k_ssim_maps": ["loss.hip", "gsr_internal.hpp"],
     "k_ssim_grad": ["loss.hip", "gsr_internal.hpp"],
+    "k_upsweep": ["sort.hip", "scan_common.hpp", "gsr_internal.hpp"],
+    "k_scan_rows": ["sort.hip", "scan_common.hpp", "gsr_internal.hpp"],
+    "k_scatter": ["sort.hip", "scan_common.hpp", "gsr_internal.hpp"],
 }
 # bench.py stage -> the kernel instance its default configuration launches (template arguments as rocprofv3
 # prints them: the raster kernels with the skips on, the dense Adam)
@@ -44,6 +47,19 @@ STAGE_KERNEL = {"forward": "k_forward<true>", "backward": "k_backward<true>",
                 "backward_deterministic": "k_backward_det<true>", "adam": "k_adam<false>",
                 "adam_visible": "k_adam<true>", "project_forward": "k_project_forward",
                 "project_backward": "k_project_backward", "loss_l1_ssim": ("k_ssim_maps", "k_ssim_grad")}
+
+
+def sort_kernels(passes: dict) -> tuple:
+    """The kernel instances of the binning's two radix sorts in the default configuration (presort scheme: 4 passes
+    of 8-bit digits over the depth keys, then the tile passes of 6-bit digits over packed keys), one entry per
+    launch, for traffic_for."""
+    depth = ("k_upsweep<uint32,4u,8u>", "k_scan_rows", "k_scatter<uint32,4u,8u,false,false>") * passes["depth"]
+    t = passes["tile"]
+    tile = ("k_upsweep<uint32,8u,6u>", "k_scan_rows") * t + ("k_scatter<uint32,8u,6u,false,true>",) * (t - 1) + \
+        ("k_scatter<uint32,8u,6u,true,true>",)
+    return depth + tile
+
+
 CALIB_BYTES = 256 * 1024 * 1024  # read and written by each copy of bench.py --calib-copy
 TRAFFIC_BEGIN, TRAFFIC_END = "<!-- traffic-json", "traffic-json -->"
 

@@ -102,7 +102,10 @@ gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value);
 #define GSR_STAGE_PROJECT_FORWARD 4  /* the projection kernel                                                    */
 #define GSR_STAGE_PROJECT_BACKWARD 5 /* the projection's backward kernel                                         */
 #define GSR_STAGE_LOSS 6             /* both passes of the L1 + SSIM loss                                        */
-#define GSR_NUM_STAGES 7
+#define GSR_STAGE_DEPTH_SORT 7       /* inside gsr_bin: the radix sort of the splats by depth (presort scheme)   */
+#define GSR_STAGE_TILE_SORT 8        /* inside gsr_bin: the radix sort of the pairs (by tile, or by the 64-bit   */
+                                     /*   key with GSR_BIN_KEY64)                                                */
+#define GSR_NUM_STAGES 9
 
 /* GPU durations in milliseconds of the recorded launches of `stage`, oldest first: the last min(recorded, ring
  * size, max) of them. Waits for the newest one to finish. *count = the number written.

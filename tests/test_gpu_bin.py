@@ -145,7 +145,8 @@ def test_bin_without_keys(ctx):
 
 
 # ------------------------------------------------------------------------------------------------ the sort alone
-@pytest.mark.parametrize("n", [0, 1, 255, 256, 257, 1234, 4095, 4096, 4097, 100000, 1000003])
+@pytest.mark.parametrize("n", [0, 1, 255, 256, 257, 1234, 4095, 4096, 4097, 100000, 1000003, 2097151, 2097152,
+                               3000017])
 @pytest.mark.parametrize("key_bits", [64, 44, 13])
 def test_radix_sort_matches_stable_sort(ctx, n, key_bits):
     import oracle

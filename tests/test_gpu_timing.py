@@ -25,10 +25,14 @@ def test_kernel_times_record_each_stage_in_a_ring(ctx):
         b = gsr.gsr_bin(ctx, sp, dp, sc.width, sc.height)
         out, ft, lc = gsr.gsr_render_forward(ctx, sp, b, sc.width, sc.height)
         gsr.gsr_render_backward(ctx, sp, b, sc.width, sc.height, out, ft, lc, vo)
-    for stage in (gsr.GSR_STAGE_BIN, gsr.GSR_STAGE_FORWARD, gsr.GSR_STAGE_BACKWARD):
+    for stage in (gsr.GSR_STAGE_BIN, gsr.GSR_STAGE_FORWARD, gsr.GSR_STAGE_BACKWARD, gsr.GSR_STAGE_DEPTH_SORT,
+                  gsr.GSR_STAGE_TILE_SORT):
         t = gsr.gsr_kernel_times(ctx, stage)
         assert len(t) == 3 and all(0 < x < 1000 for x in t), (stage, t)  # the last 3 of 5 launches
         assert len(gsr.gsr_kernel_times(ctx, stage, max_count=2)) == 2
+    # the two sorts lie inside the bin stage
+    assert sum(gsr.gsr_kernel_times(ctx, gsr.GSR_STAGE_DEPTH_SORT)) + \
+        sum(gsr.gsr_kernel_times(ctx, gsr.GSR_STAGE_TILE_SORT)) < sum(gsr.gsr_kernel_times(ctx, gsr.GSR_STAGE_BIN))
     assert gsr.gsr_kernel_times(ctx, gsr.GSR_STAGE_ADAM) == []  # nothing recorded yet
     z = dev(np.zeros(8, np.float32))
     gsr.gsr_adam_step(ctx, [(z, z, z, z, 1e-3)], 0.9, 0.999, 1e-15, 0.1, 0.001)
@@ -49,6 +53,6 @@ def test_kernel_timing_rejects_bad_arguments(ctx):
     with pytest.raises(gsr.GsrError):
         gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, -1)
     gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, 2)
-    for bad in (-1, gsr.GSR_STAGE_LOSS + 1):
+    for bad in (-1, gsr.GSR_STAGE_TILE_SORT + 1):
         with pytest.raises(gsr.GsrError):
             gsr.gsr_kernel_times(ctx, bad)
