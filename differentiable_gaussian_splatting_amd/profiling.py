@@ -55,8 +55,8 @@ def sort_kernels(passes: dict) -> tuple:
     launch, for traffic_for."""
     depth = ("k_upsweep<uint32,4u,8u>", "k_scan_rows", "k_scatter<uint32,4u,8u,false,false>") * passes["depth"]
     t = passes["tile"]
-    tile = ("k_upsweep<uint32,8u,6u>", "k_scan_rows") * t + ("k_scatter<uint32,8u,6u,false,true>",) * (t - 1) + \
-        ("k_scatter<uint32,8u,6u,true,true>",)
+    tile = ("k_upsweep<uint32,16u,6u>", "k_scan_rows") * t + ("k_scatter<uint32,16u,6u,false,true>",) * (t - 1) + \
+        ("k_scatter<uint32,16u,6u,true,true>",)
     return depth + tile
 
 
