@@ -118,7 +118,7 @@ def trace_md(stats_csv: str, title: str, cmd: str, timed_range: str | None = Non
     """The kernel summary of a trace; with `timed_range`, first a table of the dispatches inside that ROCTx range
     (read from the kernel and marker traces written next to the stats file)."""
     rows = list(csv.DictReader(open(stats_csv)))
-    out = [f"# {title}", "", "Command (repository root on the GPU box):", "", "```", cmd, "```", ""]
+    out = [f"# {title}", "", "Command (run from the repository root):", "", "```", cmd, "```", ""]
     if timed_range:
         stem = stats_csv[:-len("kernel_stats.csv")]
         window = _range_window(stem + "marker_api_trace.csv", timed_range)
@@ -172,7 +172,7 @@ def pmc_md(base: str, cmd: str, workload: str, first: int | None = None) -> str:
             if vals:
                 scale[cnt] = CALIB_BYTES / (max(vals) * 1024.0)
     kernels = sorted({k for p in passes.values() for k in p[0]})
-    lines = [f"# Hardware counters, {workload}", "", "Commands (repository root on the GPU box; one `rocprofv3 --pmc` "
+    lines = [f"# Hardware counters, {workload}", "", "Commands (run from the repository root; one `rocprofv3 --pmc` "
              "run per pass):", "", "```", cmd, "```", ""]
     if scale:
         lines += ["Calibration (`bench.py --calib-copy`, 256 MiB read + 256 MiB written per copy): bytes = "
