@@ -251,6 +251,8 @@ def main():
     e_bwd_gpu = int(last_contrib.to(torch.int64).sum().item())
     det = bench_deterministic_backward(args, ctx, gsr, torch, np, stream, splats, b, W, H, out_rgba, final_T,
                                        last_contrib, v_out, grad)
+    per_splat = bench_per_splat_backward(args, ctx, gsr, torch, np, splats, b, W, H, out_rgba, final_T,
+                                         last_contrib, v_out, grad)
 
     # CPU baseline leg (rank 0, N = 1): the oracle on one whole step of the same input; its exact counts
     cpu = None
@@ -279,6 +281,8 @@ def main():
     det["ratio_to_default"] = det["ms"] / stage_ms["backward"]
     det["kernel_ratio_to_default"] = det["kernel_ms"] / kernel_ms["backward"]
     result["deterministic_backward"] = det
+    per_splat["kernel_ratio_to_default"] = per_splat["kernel_ms"] / kernel_ms["backward"]
+    result["per_splat_backward"] = per_splat
     if cpu is not None:
         fs, bs = cpu["fwd_stats"], cpu["bwd_stats"]
         e_fwd, e_bwd = fs["visited"], bs["visited"]
@@ -342,6 +346,26 @@ def main():
     result["projection"] = bench_projection(args, ctx, gsr, scenes, sc, hp=hp, bc=bc)
     print(json.dumps(result), flush=True)
     ctx.close()
+
+
+def bench_per_splat_backward(args, ctx, gsr, torch, np, splats, b, W, H, out_rgba, final_T, last_contrib, v_out,
+                             grad):
+    """The backward in the per-splat loop order (GSR_BACKWARD_PER_SPLAT) on the last step's bins and image: its
+    kernel's time from the library's events over K launches, and the largest difference from the default order's
+    gradients in units of the parity bar (both sum the same terms in other orders)."""
+    ref = grad.clone()
+    g = torch.empty_like(grad)
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_BACKWARD_SCHEME, gsr.GSR_BACKWARD_PER_SPLAT)
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, args.steps)
+    try:
+        for _ in range(args.steps):
+            gsr.gsr_render_backward(ctx, splats, b, W, H, out_rgba, final_T, last_contrib, v_out, g)
+        kms = float(np.mean(gsr.gsr_kernel_times(ctx, gsr.GSR_STAGE_BACKWARD)))
+    finally:
+        gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, 0)
+        gsr.gsr_set_option(ctx, gsr.GSR_OPT_BACKWARD_SCHEME, gsr.GSR_BACKWARD_PER_PIXEL)
+    dev = ((g - ref).abs() / (1e-4 + 1e-4 * ref.abs())).max().item()
+    return {"kernel_ms": kms, "max_diff_to_default_in_units_of_1e-4_abs_plus_rel": dev}
 
 
 def sort_roofline(args, N, P, W, H, kernel_ms):

@@ -187,6 +187,11 @@ gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value) {
       if (value != 0 && value != 1) return fail(ctx, GSR_EINVAL, "gsr_set_option: deterministic must be 0 or 1");
       ctx->deterministic = value != 0;
       return GSR_OK;
+    case GSR_OPT_BACKWARD_SCHEME:
+      if (value != GSR_BACKWARD_PER_PIXEL && value != GSR_BACKWARD_PER_SPLAT)
+        return fail(ctx, GSR_EINVAL, "gsr_set_option: unknown backward scheme %lld", (long long)value);
+      ctx->backward_scheme = int32_t(value);
+      return GSR_OK;
     case GSR_OPT_KERNEL_TIMING:
       if (value < 0 || value > 4096)
         return fail(ctx, GSR_EINVAL, "gsr_set_option: kernel timing ring must hold 0..4096 launches");

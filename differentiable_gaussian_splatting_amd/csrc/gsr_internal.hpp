@@ -61,6 +61,7 @@ struct gsr_ctx {
   bool bin_keys = true;
   bool raster_skip = true;  // per-wave cull and the backward's all-lanes-rejected skip
   bool deterministic = false;  // backward sums independent of scheduling (fixed-point atomics)
+  int32_t backward_scheme = GSR_BACKWARD_PER_PIXEL;
   uint64_t cost_tiles = 0;  // tile count of the grid tile_cost describes (0: none yet)
   const uint32_t* order_ranges = nullptr;  // the ranges tile_order_ext was last ranked for (by a forward)
   uint64_t order_tiles = 0;

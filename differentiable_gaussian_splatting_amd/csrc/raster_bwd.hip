@@ -381,6 +381,174 @@ __device__ __forceinline__ void backward_tile(GSR_BACKWARD_PARAMS) {
     batches(std::true_type{});
 }
 
+// Per-splat backward (the loop order of the M3 per-splat backward page: a thread owns a splat and visits the
+// tile's pixels in a diagonal schedule, so that its nine sums stay in the thread and need no cross-lane reduction).
+// Here each wave owns one 8x8 block of the tile and needs no barrier after the set-up: it takes the tile's list up
+// to the block's last contributor in chunks of 64, keeps the splats the block cull lets through (compacted in list
+// order, lane j = the chunk's j-th such splat), and sweeps: at step t lane j evaluates pixel p = t - j of the
+// block. The pixel's state before the splat (T and the accumulated colour) comes from lane j - 1, which held that
+// pixel one step earlier (a one-lane shift of the wave), or for lane 0 from LDS, where the last lane of the
+// previous chunk left it. Every (pixel, splat) term is the per-pixel kernel's; a lane adds its splat's terms in
+// pixel order, applies the splat's factors once per chunk and adds the nine results to splats_grad (float atomics,
+// or the fixed-point sums under kDet, which need no other care: each sum is formed in a fixed order).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kWaveShr1 = 0x138;  // DPP wave_shr:1, lane i takes lane i - 1
+
+template <bool kSkip, bool kDet>
+__device__ __forceinline__ void backward_splat_tile(GSR_BACKWARD_PARAMS) {
+  constexpr uint32_t kWaves = kTilePixels / kWave;
+  __shared__ double s_exp2[64];
+  __shared__ float4 s_pix[kWaves][kWave];    // C_final rgb, last contributor (bits)
+  __shared__ float4 s_grad[kWaves][kWave];   // upstream gradient rgb
+  __shared__ float4 s_state[kWaves][kWave];  // T and the accumulated rgb before the next chunk
+  __shared__ StagedSplat s_sp[kWaves][kWave];
+  __shared__ uint32_t s_rel[kWaves][kWave];
+  const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const uint32_t tile = tile_order[blockIdx.x];
+  if (tile >= num_tiles) return;  // not reachable with a permutation; keeps reads in bounds
+  load_exp_table(s_exp2);
+  const uint32_t tx0 = (tile % tiles_x) * kTile, ty0 = (tile / tiles_x) * kTile;
+  const uint32_t start = min(ranges[2 * tile], num_pairs);
+  const uint32_t end = max(start, min(ranges[2 * tile + 1], num_pairs));
+  {
+    // lane l sets up pixel l of the wave's block
+    const uint32_t px = tx0 + lane_px(w, lane), py = ty0 + lane_py(w, lane);
+    uint32_t last = 0;
+    float4 c = make_float4(0.0f, 0.0f, 0.0f, 0.0f), g = c;
+    if (px < width && py < height) {
+      const size_t p = size_t(py) * width + px;
+      last = min(last_contrib[p], end - start);
+      c = out_rgba[p];
+      g = v_out[p];
+    }
+    s_pix[w][lane] = make_float4(c.x, c.y, c.z, __uint_as_float(last));
+    s_grad[w][lane] = make_float4(g.x, g.y, g.z, 0.0f);
+    s_state[w][lane] = make_float4(1.0f, 0.0f, 0.0f, 0.0f);
+  }
+  __syncthreads();  // the exponential table; the rest is wave-private from here on
+  uint32_t wave_last = __float_as_uint(s_pix[w][lane].w);
+  const float4 gl = s_grad[w][lane];
+  const bool g_finite = __builtin_isfinite(gl.x) && __builtin_isfinite(gl.y) && __builtin_isfinite(gl.z);
+  const bool wave_g_finite = __builtin_amdgcn_readfirstlane(uint32_t(__ballot(!g_finite) == 0)) != 0;
+  for (uint32_t off = 32; off > 0; off >>= 1) wave_last = max(wave_last, uint32_t(__shfl_xor(int(wave_last), off)));
+  const uint32_t limit = min(__builtin_amdgcn_readfirstlane(wave_last), end - start);
+
+  auto chunks = [&](auto guard) {
+  constexpr bool kGuard = decltype(guard)::value;
+  for (uint32_t rel0 = 0; rel0 < limit; rel0 += kWave) {
+    // this chunk's candidates, culled against the wave's block and compacted in list order
+    const uint32_t rel = rel0 + lane;
+    StagedSplat cand;
+    bool keep = false;
+    if (rel < limit) {
+      cand = stage_splat(splats, vals[start + rel], n);
+      keep = kSkip ? ((reach_mask(cand, float(tx0) + 0.5f, float(ty0) + 0.5f) >> w) & 1u) != 0 : true;
+    }
+    const uint64_t kept = __ballot(keep);
+    const uint32_t m = uint32_t(__popcll(kept));
+    if (m == 0) continue;
+    if (keep) {
+      const uint32_t slot = uint32_t(__popcll(kept & ((uint64_t(1) << lane) - 1)));
+      s_sp[w][slot] = cand;
+      s_rel[w][slot] = rel;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    const bool mine = lane < m;
+    const StagedSplat s = s_sp[w][mine ? lane : 0];
+    const uint32_t srel = s_rel[w][mine ? lane : 0];
+    float acc[kGrads];
+#pragma unroll
+    for (uint32_t q = 0; q < kGrads; ++q) acc[q] = 0.0f;
+    float oT = 1.0f, oar = 0.0f, oag = 0.0f, oab = 0.0f;  // this lane's outgoing state of the previous step
+    for (uint32_t t = 0; t < kWave + m - 1; ++t) {
+      const int pi = int(t) - int(lane);
+      const bool act = mine && pi >= 0 && pi < int(kWave);
+      const uint32_t p = uint32_t(min(max(pi, 0), int(kWave) - 1));
+      // incoming state: the previous lane's outgoing one; lane 0 reads the pixel's state from LDS
+      float T = dpp_mov<kWaveShr1>(oT), ar = dpp_mov<kWaveShr1>(oar), ag = dpp_mov<kWaveShr1>(oag),
+            ab = dpp_mov<kWaveShr1>(oab);
+      if (lane == 0) {
+        const float4 st = s_state[w][p];
+        T = st.x, ar = st.y, ag = st.z, ab = st.w;
+      }
+      const float4 pc = s_pix[w][p];
+      const float4 pg = s_grad[w][p];
+      const float cx = float(tx0 + lane_px(w, p)) + 0.5f, cy = float(ty0 + lane_py(w, p)) + 0.5f;
+      Eval e;  // evaluated in every lane, so that dx and dy are set where the terms below multiply them by 0
+      const bool pass = evaluate<false>(s, cx, cy, e, s_exp2);
+      const bool contrib = act && pass && srel < __float_as_uint(pc.w);
+      const float alpha = contrib ? e.alpha : 0.0f;
+      const float one_m = 1.0f - alpha;
+      const float wgt = alpha * T;
+      float d5 = wgt * pg.x, d6 = wgt * pg.y, d7 = wgt * pg.z;
+      if constexpr (kGuard) {
+        d5 = contrib ? d5 : 0.0f;
+        d6 = contrib ? d6 : 0.0f;
+        d7 = contrib ? d7 : 0.0f;
+      }
+      const float mr = s.r * wgt, mg = s.g * wgt, mb = s.bl * wgt;
+      // as in the per-pixel kernel: after = (C_final - acc) - mine per channel
+      const float g_rgb = __fmaf_rn(pg.z, s.bl, __fmaf_rn(pg.y, s.g, pg.x * s.r));
+      const float g_after =
+          __fmaf_rn(pg.z, (pc.z - ab) - mb, __fmaf_rn(pg.y, (pc.y - ag) - mg, pg.x * ((pc.x - ar) - mr)));
+      const float dl_da = __fmaf_rn(T, g_rgb, -g_after * __builtin_amdgcn_rcpf(one_m));
+      const float v = (contrib && e.oG < kAlphaMax) ? dl_da * e.G : 0.0f;
+      const float vx = v * e.dx, vy = v * e.dy;
+      acc[0] += vx;
+      acc[1] += vy;
+      acc[2] += vx * e.dx;
+      acc[3] += vx * e.dy;
+      acc[4] += vy * e.dy;
+      acc[5] += d5;
+      acc[6] += d6;
+      acc[7] += d7;
+      acc[8] += v;
+      oT = T * one_m;
+      oar = ar + mr;
+      oag = ag + mg;
+      oab = ab + mb;
+      if (act && lane == m - 1) s_state[w][p] = make_float4(oT, oar, oag, oab);
+    }
+    // the splat's factors, as at the per-pixel kernel's flush, then its nine totals
+    if (mine && s.idx != 0xFFFFFFFFu) {
+      const float s0 = acc[0], s1 = acc[1], s2 = acc[2], s3 = acc[3], s4 = acc[4];
+      const float o2 = s.o + s.o;
+      acc[0] = o2 * __fmaf_rn(s.ha, s0, s.hb * s1);
+      acc[1] = o2 * __fmaf_rn(s.hb, s0, s.hc * s1);
+      acc[2] = (-0.5f * s.o) * s2;
+      acc[3] = -s.o * s3;
+      acc[4] = (-0.5f * s.o) * s4;
+#pragma unroll
+      for (uint32_t q = 0; q < kGrads; ++q) {
+        if (acc[q] == 0.0f) continue;
+        if constexpr (kDet)
+          add_fixed(fixed, s.idx, q, acc[q]);
+        else
+          atomicAdd(splats_grad + size_t(s.idx) * kGrads + q, acc[q]);
+      }
+    }
+    // the next chunk overwrites s_sp / s_rel, which this chunk's lanes read at its start only
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  }
+  };
+  if (wave_g_finite)
+    chunks(std::false_type{});
+  else
+    chunks(std::true_type{});
+}
+
+template <bool kSkip, bool kDet>
+__global__ __launch_bounds__(kTilePixels) void k_backward_splat(GSR_BACKWARD_PARAMS) {
+  backward_splat_tile<kSkip, kDet>(GSR_BACKWARD_ARGS);
+}
+
 // One block per 16x16 tile; the deterministic form under a name of its own, so that profiles keep the two apart.
 template <bool kSkip>
 __global__ __launch_bounds__(kTilePixels) void k_backward(GSR_BACKWARD_PARAMS) {
@@ -436,6 +604,9 @@ extern "C" gsr_status gsr_render_backward(gsr_ctx* ctx, void* stream, const floa
   if (!order) return st;
   auto kernel = ctx->raster_skip ? (det ? k_backward_det<true> : k_backward<true>)
                                  : (det ? k_backward_det<false> : k_backward<false>);
+  if (ctx->backward_scheme == GSR_BACKWARD_PER_SPLAT)
+    kernel = ctx->raster_skip ? (det ? k_backward_splat<true, true> : k_backward_splat<true, false>)
+                              : (det ? k_backward_splat<false, true> : k_backward_splat<false, false>);
   timing_mark(ctx, GSR_STAGE_BACKWARD, s, false);
   hipLaunchKernelGGL(kernel, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, s, splats, n, bins->vals,
                      bins->ranges, bins->num_pairs, tiles_x, width, height,

@@ -32,6 +32,7 @@ KERNEL_SOURCES = {
     "k_forward": ["raster_fwd.hip", "raster_common.hpp", "gsr_internal.hpp"],
     "k_backward": ["raster_bwd.hip", "raster_common.hpp", "gsr_internal.hpp"],
     "k_backward_det": ["raster_bwd.hip", "raster_common.hpp", "gsr_internal.hpp"],
+    "k_backward_splat": ["raster_bwd.hip", "raster_common.hpp", "gsr_internal.hpp"],
     "k_adam": ["adam.hip", "gsr_internal.hpp"],
     "k_project_forward": ["project.hip", "gsr_internal.hpp"],
     "k_project_backward": ["project.hip", "gsr_internal.hpp"],
@@ -44,7 +45,8 @@ KERNEL_SOURCES = {
 # bench.py stage -> the kernel instance its default configuration launches (template arguments as rocprofv3
 # prints them: the raster kernels with the skips on, the dense Adam)
 STAGE_KERNEL = {"forward": "k_forward<true>", "backward": "k_backward<true>",
-                "backward_deterministic": "k_backward_det<true>", "adam": "k_adam<false>",
+                "backward_deterministic": "k_backward_det<true>", "backward_per_splat": "k_backward_splat<true,false>",
+                "adam": "k_adam<false>",
                 "adam_visible": "k_adam<true>", "project_forward": "k_project_forward",
                 "project_backward": "k_project_backward", "loss_l1_ssim": ("k_ssim_maps", "k_ssim_grad")}
 

@@ -88,6 +88,12 @@ gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats);
                               /*   float sum would. Costs an arena buffer of 148 bytes per splat and about a fifth */
                               /*   of the backward's speed. (The per-splat backward page shrinks, but does not    */
                               /*   remove, the run-to-run noise by changing the loop order; its determinism note.) */
+#define GSR_OPT_BACKWARD_SCHEME 7 /* the backward's loop order; both give the same terms, summed in other orders:   */
+#define GSR_BACKWARD_PER_PIXEL 0  /*   default: a lane per pixel walks the splats; the 64 lanes' terms are reduced   */
+                                  /*   across the wave for every splat some lane composited                          */
+#define GSR_BACKWARD_PER_SPLAT 1  /*   a lane per splat sweeps the 64 pixels of its wave's 8x8 block in a diagonal  */
+                                  /*   schedule, the pixel state passed lane to lane (the M3 per-splat backward     */
+                                  /*   page's order); no cross-lane reduction, each splat's sums in pixel order     */
 #define GSR_OPT_KERNEL_TIMING 6 /* 0 (default): off; n in 1..4096: every entry point records a pair of HIP events   */
                               /*   on its stream around its main kernel(s), in a ring of the last n launches per  */
                               /*   stage (read with gsr_kernel_times); setting the option clears the rings        */
