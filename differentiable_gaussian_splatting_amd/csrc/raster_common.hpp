@@ -77,11 +77,12 @@ __host__ __device__ __forceinline__ float exp_rn(float x, const double* tab) {
 
 // The forward's form of exp_rn: e^-s for s in [0, 5.70] with `tab` holding kExpTabN pairs (hi, lo), entry k being
 // 2^(-k/32): kExp2Tab's pair for the residue of -k scaled by 2^floor(-k/32), which is exact. With k = round(32 s /
-// ln 2) the table entry already carries the power of two, so no ldexp or index masking follows the series. Every
-// step equals exp_rn's for x = -s (the same reduction, series and roundings, the scaling moved into the table),
-// so the result is bit-identical to exp_rn(-s) - the host test checks both exhaustively. Beyond s = 5.70 the
-// last entry is used (a wrong value, never a read out of range); the kernels evaluate it for s <= ln(255 o)
-// plus a margin, below 5.55 for o <= 1.
+// ln 2) the table entry already carries the power of two, so no ldexp or index masking follows the series; k is
+// found by one rounding of s 32 / ln 2 (adding 1.5 2^52 leaves it in the low word, so no conversion follows
+// either), where exp_rn rounds the product first, which can pick the neighbouring k at a tie: either residue lies
+// in the series' range. Both functions are correctly rounded on every argument, so they agree bit for bit - the
+// host test checks both exhaustively. Beyond s = 5.70 the last entry is used (a wrong value, never a read out of
+// range); the kernels evaluate it for s <= ln(255 o) plus a margin, below 5.55 for o <= 1.
 constexpr uint32_t kExpTabN = 264;
 
 __host__ __device__ __forceinline__ void exp_neg_entry(uint32_t kp, double* hi_lo) {
@@ -104,7 +105,11 @@ __host__ __device__ __forceinline__ double fma_uniform_c(double a, double b, dou
 
 __host__ __device__ __forceinline__ float exp_neg_rn(float s, const double* tab) {
   const double sd = double(s);
-  const double k = rint(sd * 46.166241308446828384);  // 32 / ln 2
+  // k = the integer nearest sd 32 / ln 2, by adding 1.5 2^52 (one rounding to an integer, left in the low word)
+  const double t = fma(sd, 46.166241308446828384, 0x1.8p52);
+  const double k = t - 0x1.8p52;
+  uint64_t tbits;
+  __builtin_memcpy(&tbits, &t, sizeof tbits);
   double r = fma(k, 0x1.62e42fee00000p-6, -sd);
   r = fma(k, 0x1.a39ef35793c76p-38, r);
   const double r2 = r * r;
@@ -113,7 +118,7 @@ __host__ __device__ __forceinline__ float exp_neg_rn(float s, const double* tab)
   q = fma_uniform_c(q, r, 1.0 / 6.0);
   q = fma(q, r, 0.5);
   q = fma(q, r2, r);  // e^r - 1
-  const uint32_t ki = uint32_t(fmin(k, double(kExpTabN - 1)));
+  const uint32_t ki = uint32_t(tbits) < kExpTabN - 1 ? uint32_t(tbits) : kExpTabN - 1;  // k for 0 <= k < 2^31
   const double hi = tab[2 * ki], lo = tab[2 * ki + 1];
   return float(hi + fma(hi, q, lo));
 }
