@@ -12,7 +12,9 @@
 //   dL/dx(q) = (1 - lam) sign(x - y) / (3 H W) - lam / (3 H W) [G * df/dmx + 2 x G * df/d(G*x^2) + y G * df/d(G*xy)](q)
 // (G is symmetric, so its transpose is the same correlation).
 //
-// Two passes over 16x16 tiles (see k_ssim_maps and k_ssim_grad), with every window sum in LDS. Each tile of the first
+// Two passes over 16x16 tiles (see k_ssim_maps and k_ssim_grad), with every window sum in LDS; each of the chip's
+// eight dies takes one band of tiles (band_tile), so that neighbouring tiles read their shared halos through the
+// same L2. Each tile of the first
 // pass writes its sums of S and |x - y| (fp64) to its own slot; the second pass's first workgroup adds the slots in
 // order, so the loss is the same on every run.
 #include <cmath>
@@ -34,6 +36,15 @@ struct Taps {
   float g[2 * kR + 1];
 };
 
+// Tile of workgroup b: workgroups go to the eight dies (XCDs) in turn, b to die b % 8, so die x takes the tiles of
+// one contiguous band [x band, (x + 1) band) of the image in raster order, and the halos that neighbouring tiles
+// share are read through that die's L2. Workgroups past the last tile return.
+constexpr uint32_t kXcds = 8;
+__device__ __forceinline__ uint32_t band_tile(uint32_t num_tiles) {
+  const uint32_t band = (num_tiles + kXcds - 1) / kXcds;
+  return (blockIdx.x % kXcds) * band + blockIdx.x / kXcds;
+}
+
 __device__ __forceinline__ double block_sum(double v, double* s_red) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
   const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
@@ -53,6 +64,7 @@ __device__ __forceinline__ double block_sum(double v, double* s_red) {
 // and a vertical pass, and the gradient at the tile's pixels. Splitting at the derivative maps costs their 9 x 4 B
 // per pixel of traffic but halves the recomputed halo (a fused pass needs the images on the tile grown by 10).
 __global__ __launch_bounds__(kThreads) void k_ssim_maps(Taps taps, uint32_t width, uint32_t height, uint32_t tiles_x,
+                                                        uint32_t num_tiles,
                                                         const float4* __restrict__ out_rgba,
                                                         const float* __restrict__ target, float* __restrict__ maps,
                                                         double* __restrict__ part) {
@@ -60,7 +72,9 @@ __global__ __launch_bounds__(kThreads) void k_ssim_maps(Taps taps, uint32_t widt
   __shared__ float s_h[5][kP][kT];
   __shared__ double s_red[kThreads / 64];
   const int tid = int(threadIdx.x);
-  const int tx0 = int(blockIdx.x % tiles_x) * kT, ty0 = int(blockIdx.x / tiles_x) * kT;
+  const uint32_t tile = band_tile(num_tiles);
+  if (tile >= num_tiles) return;
+  const int tx0 = int(tile % tiles_x) * kT, ty0 = int(tile / tiles_x) * kT;
   const int W = int(width), H = int(height);
   const size_t plane = size_t(W) * H;
   {
@@ -159,8 +173,8 @@ __global__ __launch_bounds__(kThreads) void k_ssim_maps(Taps taps, uint32_t widt
   const double s_tot = block_sum(ssim_sum, s_red);
   const double l_tot = block_sum(l1_sum, s_red);
   if (tid == 0) {
-    part[2 * size_t(blockIdx.x)] = s_tot;
-    part[2 * size_t(blockIdx.x) + 1] = l_tot;
+    part[2 * size_t(tile)] = s_tot;
+    part[2 * size_t(tile) + 1] = l_tot;
   }
 }
 
@@ -184,6 +198,7 @@ __device__ __forceinline__ void loss_total(const double* __restrict__ part, uint
 }
 
 __global__ __launch_bounds__(kThreads) void k_ssim_grad(Taps taps, uint32_t width, uint32_t height, uint32_t tiles_x,
+                                                        uint32_t num_tiles,
                                                         float lam, float inv_n, const float4* __restrict__ out_rgba,
                                                         const float* __restrict__ target,
                                                         const float* __restrict__ maps, float4* __restrict__ v_out,
@@ -193,8 +208,10 @@ __global__ __launch_bounds__(kThreads) void k_ssim_grad(Taps taps, uint32_t widt
   __shared__ float s_h[9][kP][kT];   // their horizontal sums
   __shared__ double s_red[kThreads / 64];
   const int tid = int(threadIdx.x);
-  if (blockIdx.x == 0) loss_total(part, gridDim.x, inv_nd, lam, loss, s_red);
-  const int tx0 = int(blockIdx.x % tiles_x) * kT, ty0 = int(blockIdx.x / tiles_x) * kT;
+  if (blockIdx.x == 0) loss_total(part, num_tiles, inv_nd, lam, loss, s_red);
+  const uint32_t tile = band_tile(num_tiles);
+  if (tile >= num_tiles) return;
+  const int tx0 = int(tile % tiles_x) * kT, ty0 = int(tile / tiles_x) * kT;
   const int W = int(width), H = int(height);
   const size_t plane = size_t(W) * H;
   {
@@ -310,10 +327,11 @@ extern "C" gsr_status gsr_loss_l1_ssim(gsr_ctx* ctx, void* stream, uint32_t widt
   const double n = 3.0 * double(width) * double(height);
   const Taps taps = make_taps();
   timing_mark(ctx, GSR_STAGE_LOSS, s, false);
-  hipLaunchKernelGGL(k_ssim_maps, dim3(uint32_t(num_tiles)), dim3(kThreads), 0, s, taps, width, height,
-                     uint32_t(tiles_x), reinterpret_cast<const float4*>(out_rgba), target, maps, part);
-  hipLaunchKernelGGL(k_ssim_grad, dim3(uint32_t(num_tiles)), dim3(kThreads), 0, s, taps, width, height,
-                     uint32_t(tiles_x), 0.2f, float(1.0 / n), reinterpret_cast<const float4*>(out_rgba), target, maps,
+  const uint32_t grid = uint32_t((num_tiles + kXcds - 1) / kXcds * kXcds);
+  hipLaunchKernelGGL(k_ssim_maps, dim3(grid), dim3(kThreads), 0, s, taps, width, height, uint32_t(tiles_x),
+                     uint32_t(num_tiles), reinterpret_cast<const float4*>(out_rgba), target, maps, part);
+  hipLaunchKernelGGL(k_ssim_grad, dim3(grid), dim3(kThreads), 0, s, taps, width, height, uint32_t(tiles_x),
+                     uint32_t(num_tiles), 0.2f, float(1.0 / n), reinterpret_cast<const float4*>(out_rgba), target, maps,
                      reinterpret_cast<float4*>(v_out), part, 1.0 / n, loss);
   timing_mark(ctx, GSR_STAGE_LOSS, s, true);
   return check_launch(ctx, "gsr_loss_l1_ssim");
