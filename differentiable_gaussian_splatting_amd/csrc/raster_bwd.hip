@@ -551,7 +551,7 @@ __global__ __launch_bounds__(kTilePixels) void k_backward_splat(GSR_BACKWARD_PAR
 
 // One block per 16x16 tile; the deterministic form under a name of its own, so that profiles keep the two apart.
 template <bool kSkip>
-__global__ __launch_bounds__(kTilePixels) void k_backward(GSR_BACKWARD_PARAMS) {
+__global__ __launch_bounds__(kTilePixels) __attribute__((amdgpu_waves_per_eu(7))) void k_backward(GSR_BACKWARD_PARAMS) {
   backward_tile<kSkip, false>(GSR_BACKWARD_ARGS);
 }
 

@@ -81,9 +81,10 @@ __host__ __device__ __forceinline__ float exp_rn(float x, const double* tab) {
 // found by one rounding of s 32 / ln 2 (adding 1.5 2^52 leaves it in the low word, so no conversion follows
 // either), where exp_rn rounds the product first, which can pick the neighbouring k at a tie: either residue lies
 // in the series' range. Both functions are correctly rounded on every argument, so they agree bit for bit - the
-// host test checks both exhaustively. Beyond s = 5.70 the last entry is used (a wrong value, never a read out of
-// range); the kernels evaluate it for s <= ln(255 o) plus a margin, below 5.55 for o <= 1.
+// host test checks both exhaustively. The caller keeps s <= kSigmaCap (the kernels evaluate s <= lr <= kSigmaCap,
+// see StagedSplat), which keeps k below kExpTabN: the table index needs no clamp.
 constexpr uint32_t kExpTabN = 264;
+constexpr float kSigmaCap = 5.70f;  // round(5.70 * 32 / ln 2) = 263 = kExpTabN - 1
 
 __host__ __device__ __forceinline__ void exp_neg_entry(uint32_t kp, double* hi_lo) {
   const int k = -int(kp);
@@ -118,7 +119,7 @@ __host__ __device__ __forceinline__ float exp_neg_rn(float s, const double* tab)
   q = fma_uniform_c(q, r, 1.0 / 6.0);
   q = fma(q, r, 0.5);
   q = fma(q, r2, r);  // e^r - 1
-  const uint32_t ki = uint32_t(tbits) < kExpTabN - 1 ? uint32_t(tbits) : kExpTabN - 1;  // k for 0 <= k < 2^31
+  const uint32_t ki = uint32_t(tbits);  // k, below kExpTabN for 0 <= s <= kSigmaCap
   const double hi = tab[2 * ki], lo = tab[2 * ki + 1];
   return float(hi + fma(hi, q, lo));
 }
@@ -127,8 +128,10 @@ __host__ __device__ __forceinline__ float exp_neg_rn(float s, const double* tab)
 // conic is kept as a / 2 and c / 2 (what sigma uses) beside b and b / 2; a and c are ha + ha and hc + hc, exactly.
 // lr bounds sigma: alpha <= o e^-sigma < 1/255 wherever sigma > lr, so those evaluations are certain rejects.
 // lr is ln(255 o) from the fast log, raised by 2^-16 relative and 2^-16 absolute (far more than the log's and the
-// product's rounding), and +inf when that log is NaN (o < 0 or NaN: the exact evaluation then decides). For
-// o <= 1, lr < 5.55: the bound contains the sigma >= 5.55 skip.
+// product's rounding), then clamped to [0, kSigmaCap]. For 0 <= o <= 1 (every splat the binning keeps) it lies in
+// [0, 5.55): the clamp at 0 only lets sigma = 0 through where o < 1/255, which alpha then rejects, and the one at
+// kSigmaCap never binds; the bound contains the sigma >= 5.55 skip. A NaN log (o < 0 or NaN, never binned) gives
+// kSigmaCap, and the exact evaluation decides.
 struct alignas(16) StagedSplat {
   float x, y, ha, b;  // mean, a / 2, b
   float hc, o, r, g;  // c / 2, opacity, red, green
@@ -151,12 +154,13 @@ __device__ __forceinline__ StagedSplat stage_splat(const float* __restrict__ spl
     s.bl = p[7];
     s.o = p[8];
     const float L = __logf(255.0f * s.o);
-    s.lr = L == L ? (L + __builtin_fabsf(L) * (1.0f / 65536.0f)) + (1.0f / 65536.0f) : __builtin_huge_valf();
+    const float lr = L == L ? (L + __builtin_fabsf(L) * (1.0f / 65536.0f)) + (1.0f / 65536.0f) : kSigmaCap;
+    s.lr = __builtin_fminf(__builtin_fmaxf(lr, 0.0f), kSigmaCap);
     s.idx = idx;
   } else {
     // o = 0 makes every evaluation a reject
     s.x = s.y = s.ha = s.b = s.hb = s.hc = s.r = s.g = s.bl = s.o = 0.0f;
-    s.lr = -__builtin_huge_valf();
+    s.lr = 0.0f;
     s.idx = 0xFFFFFFFFu;
   }
   return s;
@@ -169,11 +173,15 @@ __device__ __forceinline__ uint32_t lane_py(uint32_t w, uint32_t lane) { return 
 
 // Which of the tile's four 8x8 wave blocks splat s can reach with alpha >= 1/255: bit q set unless the splat is
 // provably a reject at every pixel centre of block q. (x0, y0) is the first pixel centre of the tile.
-// alpha <= o exp(-sigma) reaches 1/255 only where sigma <= L = ln(255 o), an ellipse whose bounding box has
-// half-widths sqrt(2 L c / det) and sqrt(2 L a / det). Evaluated in fp32 and widened for every rounding involved:
-// the fp32 sigma of the per-lane test (relative error below 4.5 eps kappa, where kappa = (a + c)^2 / det bounds the
-// conic's condition number), the fp32 det here (relative error below 2 eps kappa), the fast log (absolute error
-// below 1e-5), sqrt and the products (a few ulp): L gets +1e-3 and the factor 1 + 1e-6 kappa, the half-widths
+// alpha <= o exp(-sigma) reaches 1/255 only where sigma <= L = ln(255 o), an ellipse. A block is dropped when a
+// separating axis shows the ellipse misses the rectangle spanned by the block's pixel centres: the x and y axes
+// (the ellipse's bounding box, half-widths sqrt(2 L c / det) and sqrt(2 L a / det)) and the two diagonals (half-
+// ranges of x + y and x - y: sqrt(2 L (a + c -+ 2 b) / det)), an octagon around the ellipse that also drops the
+// blocks beside a thin tilted splat which its bounding box still meets. Evaluated in fp32 and widened for every
+// rounding involved: the fp32 sigma of the per-lane test (relative error below 4.5 eps kappa, where
+// kappa = (a + c)^2 / det bounds the conic's condition number), det here and a + c -+ 2 b (relative errors below
+// 2 eps kappa and eps kappa / 2 + eps, as a + c -+ 2 b >= 2 det / (a + c)), the fast log (absolute error below 1e-5),
+// the reciprocal, square roots and products (a few ulp): L gets +1e-3 and the factor 1 + 1e-6 kappa, the half-widths
 // x1.001 + 0.01 px. A splat that is not finite, not positive definite or worse conditioned than kappa = 1e5 is never
 // culled: the per-lane evaluation then decides, exactly as without the cull. Skipping a certain reject changes no
 // result.
@@ -182,21 +190,44 @@ __device__ __forceinline__ uint32_t reach_mask(const StagedSplat& s, float x0, f
   const float a = s.ha + s.ha, c = s.hc + s.hc;
   const float det = a * c - s.b * s.b;
   if (!(det > 0.0f && a > 0.0f)) return 0xFu;
-  const float apc = a + c;
-  const float kappa = apc * apc / det;
+  const float apc = a + c, b2 = s.b + s.b;
+  const float inv_det = __builtin_amdgcn_rcpf(det);
+  const float kappa = apc * apc * inv_det;
   if (!(kappa <= 1e5f)) return 0xFu;
   const float L = s.lr;  // at least ln(255 o)
   const float Lm = (fmaxf(L, 0.0f) + 1e-3f) * (1.0f + 1e-6f * kappa);
-  const float two_l_det = 2.0f * Lm / det;
-  const float rx = __builtin_sqrtf(two_l_det * c) * 1.001f + 0.01f;
-  const float ry = __builtin_sqrtf(two_l_det * a) * 1.001f + 0.01f;
-  uint32_t m = 0;
-#pragma unroll
-  for (uint32_t q = 0; q < 4; ++q) {
-    const float xl = x0 + 8.0f * float(q & 1u), xh = xl + 7.0f;
-    const float yl = y0 + 8.0f * float(q >> 1), yh = yl + 7.0f;
-    const bool disjoint = (s.x - rx > xh) || (s.x + rx < xl) || (s.y - ry > yh) || (s.y + ry < yl);
-    if (!disjoint) m |= 1u << q;
+  const float two_l_det = 2.0f * Lm * inv_det;
+  // Blocks q = 0..3: columns q & 1 and rows q >> 1 of the 2 x 2 grid; each axis test clears the blocks it separates.
+  // Over a block's pixel centres x - x0 spans [0, 7] or [8, 15] (likewise y - y0), (x + y) - (x0 + y0) spans [0, 14],
+  // [8, 22] (q = 1, 2) or [16, 30], and (x - y) - (x0 - y0) spans [-7, 7] (q = 0, 3), [1, 15] or [-15, -1].
+  uint32_t m = 0xFu;
+  {
+    const float r = __builtin_amdgcn_sqrtf(two_l_det * c) * 1.001f + 0.01f;
+    const float lo = s.x - r, hi = s.x + r;
+    if (lo > x0 + 7.0f || hi < x0) m &= ~0x5u;
+    if (lo > x0 + 15.0f || hi < x0 + 8.0f) m &= ~0xAu;
+  }
+  {
+    const float r = __builtin_amdgcn_sqrtf(two_l_det * a) * 1.001f + 0.01f;
+    const float lo = s.y - r, hi = s.y + r;
+    if (lo > y0 + 7.0f || hi < y0) m &= ~0x3u;
+    if (lo > y0 + 15.0f || hi < y0 + 8.0f) m &= ~0xCu;
+  }
+  {
+    const float r = __builtin_amdgcn_sqrtf(two_l_det * (apc - b2)) * 1.001f + 0.01f;  // x + y
+    const float v = s.x + s.y, o = x0 + y0;
+    const float lo = v - r, hi = v + r;
+    if (lo > o + 14.0f || hi < o) m &= ~0x1u;
+    if (lo > o + 22.0f || hi < o + 8.0f) m &= ~0x6u;
+    if (lo > o + 30.0f || hi < o + 16.0f) m &= ~0x8u;
+  }
+  {
+    const float r = __builtin_amdgcn_sqrtf(two_l_det * (apc + b2)) * 1.001f + 0.01f;  // x - y
+    const float v = s.x - s.y, o = x0 - y0;
+    const float lo = v - r, hi = v + r;
+    if (lo > o + 7.0f || hi < o - 7.0f) m &= ~0x9u;
+    if (lo > o + 15.0f || hi < o + 1.0f) m &= ~0x2u;
+    if (lo > o - 1.0f || hi < o - 15.0f) m &= ~0x4u;
   }
   return m;
 }
@@ -237,7 +268,10 @@ struct Eval {
 // sigma = 0.5 (a dx dx + c dy dy) + b dx dy is formed as (ha dx) dx + (hc dy) dy + (b dx) dy, which rounds to the
 // same fp32 value because halving is exact. Evaluations with sigma > lr (the splat's bound, at least ln(255 o)) are
 // rejected before any exponential: their alpha is below 1/255 by a margin no rounding can close. This contains the
-// pages' sigma >= 5.55 skip (lr < 5.55 for o <= 1) and is exact for any o.
+// pages' sigma >= 5.55 skip (lr < 5.55 for o <= 1) and is exact for 0 <= o <= 1. Both ends are tested at once on
+// the bit patterns: for a, c > 0 (binned splats) the fp32 sigma is +0 or more, never -0 (the two squares are +0 or
+// positive and +0 + -0 = +0), and lr lies in [+0, kSigmaCap], where unsigned order is float order; a negative or NaN
+// sigma has a larger pattern than any such lr.
 //
 // kExactValues = true (forward, `tab` = the exp_neg_rn table): every splat that passes is evaluated with the correctly
 // rounded G, so alpha and the transmittance chain are exactly those of a plain fp32 evaluation - the stop test
@@ -258,7 +292,7 @@ __device__ __forceinline__ bool evaluate(const StagedSplat& s, float cx, float c
   const float t_c = (s.hc * e.dy) * e.dy;
   const float t_b = (s.b * e.dx) * e.dy;
   const float sigma = (t_a + t_c) + t_b;
-  if (!(sigma >= 0.0f && sigma <= s.lr)) return false;  // sigma < 0, or a certain alpha reject (see lr)
+  if (!(__float_as_uint(sigma) <= __float_as_uint(s.lr))) return false;  // sigma < 0, NaN, or above lr
   if (kExactValues) {
     e.G = exp_neg_rn(sigma, tab);
   } else {

@@ -78,17 +78,18 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
         ++walked;
         Eval e;
         if (evaluate<true>(s, cxe, cy, e, s_exp2)) {
+          // Without branches: a pixel that stops here (this splat is not composited) adds r 0 = +-0 to its
+          // colours, which leaves them as they are (a sum that starts at +0 is never -0, and binned colours are
+          // finite), and keeps T and last.
           const float next_T = T * (1.0f - e.alpha);
-          if (next_T < kTStop) {
-            cxe = kFar;  // the pixel stops here; this splat is not composited
-          } else {
-            const float wgt = e.alpha * T;
-            cr = cr + s.r * wgt;
-            cg = cg + s.g * wgt;
-            cb = cb + s.bl * wgt;
-            T = next_T;
-            last = b0 - start + j + 1;
-          }
+          const bool stop = next_T < kTStop;
+          const float wgt = stop ? 0.0f : e.alpha * T;
+          cr = cr + s.r * wgt;
+          cg = cg + s.g * wgt;
+          cb = cb + s.bl * wgt;
+          T = stop ? T : next_T;
+          last = stop ? last : b0 - start + j + 1;
+          cxe = stop ? kFar : cxe;
         }
         if (__ballot(cxe != kFar) == 0) {
           sw = kWaves;

@@ -180,7 +180,8 @@ uint32_t gsr_radix_pass_count(uint64_t num_tiles, uint32_t digit_bits);
  * cannot change a result because o <= 1 makes their alpha at most e^-5.55 < 1/255. [A.9 f16 forward page,
  * implementation listing; W1 warp sparse skip + exp-skip page, summary and section 1 row "W1b"; rasterize
  * forward + adam kernel audit page, section 1 rows (a) and (b)]
- *   splats        device [n][9] float32 (the records the bins were built from)
+ *   splats        device [n][9] float32 (the records the bins were built from; the result is defined for the
+ *                 splats gsr_bin keeps - finite, a > 0, det > 0, 0 <= o <= 1 - whatever else the bins hold)
  *   bins          host struct of device views, tiles_x / tiles_y matching width / height; pairs whose value is
  *                 >= n are ignored, and ranges are clamped to [0, num_pairs]
  *   out_rgba      device [height][width][4] float32: (C.r, C.g, C.b, 1 - T_final)
