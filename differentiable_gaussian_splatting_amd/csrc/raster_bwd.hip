@@ -289,8 +289,8 @@ __device__ __forceinline__ void backward_tile(GSR_BACKWARD_PARAMS) {
         s.hc = q1.x, s.o = q1.y, s.r = q1.z, s.g = q1.w;
         s.bl = q2.x, s.lr = q2.y, s.hb = q2.z, s.idx = __float_as_uint(q2.w);
         Eval e;  // dx and dy are set in every lane; G, oG and alpha only where the evaluation passed
-        const bool contrib = evaluate<false>(s, cx, cy, e, s_exp2) && rel0 + j < last;
-        if (kSkip && __ballot(contrib) == 0) continue;  // no lane composited this splat
+        const bool contrib = evaluate<false>(s, cx, cy, e, s_exp2) & (rel0 + j < last);
+        if (kSkip && __builtin_amdgcn_ballot_w64(contrib) == 0) continue;  // no lane composited this splat
         // Every lane forms the terms; in a lane that did not composite the splat, alpha = 0 and v = 0 make them
         // +-0 and leave T and acc as they are (the splat is binned, so its values are finite).
         float d[kGrads];

@@ -292,19 +292,30 @@ __device__ __forceinline__ bool evaluate(const StagedSplat& s, float cx, float c
   const float t_c = (s.hc * e.dy) * e.dy;
   const float t_b = (s.b * e.dx) * e.dy;
   const float sigma = (t_a + t_c) + t_b;
-  if (!(__float_as_uint(sigma) <= __float_as_uint(s.lr))) return false;  // sigma < 0, NaN, or above lr
-  if (kExactValues) {
+  const bool in_range = __float_as_uint(sigma) <= __float_as_uint(s.lr);  // not sigma < 0, NaN, or above lr
+  if constexpr (kExactValues) {
+    if (!in_range) return false;
     e.G = exp_neg_rn(sigma, tab);
+    e.oG = s.o * e.G;
   } else {
-    const float g_fast = __builtin_amdgcn_exp2f(sigma * -1.44269504088896341f);
-    const float og_fast = s.o * g_fast;
-    if (og_fast < kAlphaMinLo) return false;
-    const bool near = og_fast < kAlphaMinHi || (og_fast > kAlphaMaxLo && og_fast < kAlphaMaxHi);
-    e.G = near ? exp_rn(-sigma, tab) : g_fast;
+    // Without branches but for the rare wave in which some lane lies near a threshold: there every lane takes the
+    // exact value through exp_rn (lanes not near keep the fast one; for the others exp_rn's result is unused, and
+    // its table index is masked, so any argument reads in bounds). A fast o G below kAlphaMinLo is a certain reject
+    // and gives alpha < 1/255 as it stands.
+    float g = __builtin_amdgcn_exp2f(sigma * -1.44269504088896341f);
+    float og = s.o * g;
+    // (bitwise operators: no short-circuit branches, the masks combine in scalar registers)
+    const bool near = in_range & (og >= kAlphaMinLo) & ((og < kAlphaMinHi) | ((og > kAlphaMaxLo) & (og < kAlphaMaxHi)));
+    if (__builtin_amdgcn_ballot_w64(near) != 0) {
+      const float g_exact = exp_rn(-sigma, tab);
+      g = near ? g_exact : g;
+      og = near ? s.o * g_exact : og;
+    }
+    e.G = g;
+    e.oG = og;
   }
-  e.oG = s.o * e.G;
   e.alpha = (e.oG < kAlphaMax) ? e.oG : kAlphaMax;
-  return !(e.alpha < kAlphaMin);
+  return in_range & !(e.alpha < kAlphaMin);
 }
 
 }  // namespace gsr
