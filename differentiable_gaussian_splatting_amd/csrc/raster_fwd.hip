@@ -75,6 +75,8 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
         s.x = q0.x, s.y = q0.y, s.ha = q0.z, s.b = q0.w;
         s.hc = q1.x, s.o = q1.y, s.r = q1.z, s.g = q1.w;
         s.bl = q2.x, s.lr = q2.y, s.hb = q2.z, s.idx = __float_as_uint(q2.w);
+        // o is read in this load, not in a fourth one inside the branches (which needs its own address register)
+        asm volatile("" ::"v"(s.o));
         ++walked;
         Eval e;
         if (evaluate<true>(s, cxe, cy, e, s_exp2)) {
