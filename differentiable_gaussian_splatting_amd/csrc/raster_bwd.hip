@@ -545,7 +545,7 @@ __device__ __forceinline__ void backward_splat_tile(GSR_BACKWARD_PARAMS) {
 }
 
 template <bool kSkip, bool kDet>
-__global__ __launch_bounds__(kTilePixels) __attribute__((amdgpu_waves_per_eu(5))) void k_backward_splat(GSR_BACKWARD_PARAMS) {
+__global__ __launch_bounds__(kTilePixels) void k_backward_splat(GSR_BACKWARD_PARAMS) {
   backward_splat_tile<kSkip, kDet>(GSR_BACKWARD_ARGS);
 }
 
