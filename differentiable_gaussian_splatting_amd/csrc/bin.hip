@@ -100,11 +100,14 @@ __device__ uint32_t ellipse_count(const float* __restrict__ sp, const Rect& r) {
   return cnt;
 }
 
+// With dkeys, the depth sort's keys and values: the depth bits, and the splat index i, or with count_shift < 32
+// i | count << count_shift (the presort scheme when both fit 32 bits), so that the sorted values carry the counts
+// in depth order and the scan reads them in place instead of gathering them.
 __global__ __launch_bounds__(kThreads) void k_prep(const float* __restrict__ splats, const float* __restrict__ depths,
                                                    uint32_t n, uint32_t tiles_x, uint32_t tiles_y, bool ellipse,
                                                    uint4* __restrict__ rects, uint32_t* __restrict__ counts,
                                                    uint32_t* __restrict__ dkeys, uint32_t* __restrict__ didx,
-                                                   uint64_t* __restrict__ part) {
+                                                   uint32_t count_shift, uint64_t* __restrict__ part) {
   __shared__ uint64_t smem[kThreads / kWave];
   const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
   uint64_t c = 0;
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const float* __restrict__ spl
     counts[i] = uint32_t(c);
     if (dkeys) {
       dkeys[i] = __float_as_uint(depth);
-      didx[i] = i;
+      didx[i] = count_shift < 32 ? i | uint32_t(c) << count_shift : i;
     }
   }
   uint64_t total;
@@ -136,10 +139,11 @@ __global__ __launch_bounds__(kThreads) void k_total(const uint64_t* __restrict__
 }
 
 // Two-launch exclusive scan of uint32 counts into uint64 offsets; offsets[n] = total. With `order`, position j
-// takes counts[order[j]] (order must be a permutation of 0..n-1; other entries count 0).
+// takes counts[order[j]] (order must be a permutation of 0..n-1; other entries count 0); without, counts[j] >> shift
+// (shift 0: plain counts; else the depth-sorted values of k_prep, whose count field starts at bit shift).
 __device__ __forceinline__ uint32_t count_at(const uint32_t* __restrict__ counts, const uint32_t* __restrict__ order,
-                                             uint32_t n, uint64_t j) {
-  if (!order) return counts[j];
+                                             uint32_t n, uint64_t j, uint32_t shift) {
+  if (!order) return counts[j] >> shift;
   const uint32_t i = order[j];
   return i < n ? counts[i] : 0u;
 }
@@ -167,7 +171,8 @@ __device__ __forceinline__ void scan_parts(uint64_t* __restrict__ part, uint32_t
 // published with atomic exchanges; the block that finishes last reads them back with atomics, turns part[0..nb)
 // into its exclusive scan and writes the total to part[nb] and offsets[n].
 __global__ __launch_bounds__(kThreads) void k_scan_reduce(const uint32_t* __restrict__ counts,
-                                                          const uint32_t* __restrict__ order, uint32_t n,
+                                                          const uint32_t* __restrict__ order, uint32_t shift,
+                                                          uint32_t n,
                                                           uint64_t* __restrict__ part,
                                                           uint32_t* __restrict__ ordered, uint32_t* done,
                                                           uint32_t* done_alias, uint64_t* __restrict__ offsets) {
@@ -179,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void k_scan_reduce(const uint32_t* __rest
 #pragma unroll
   for (uint32_t i = 0; i < kScanItems; ++i) {
     const uint64_t j = base + uint64_t(i) * kThreads + threadIdx.x;
-    c[i] = j < n ? count_at(counts, order, n, j) : 0u;
+    c[i] = j < n ? count_at(counts, order, n, j, shift) : 0u;
   }
 #pragma unroll
   for (uint32_t i = 0; i < kScanItems; ++i) {
@@ -199,7 +204,8 @@ __global__ __launch_bounds__(kThreads) void k_scan_reduce(const uint32_t* __rest
 }
 
 __global__ __launch_bounds__(kThreads) void k_scan_down(const uint32_t* __restrict__ counts,
-                                                        const uint32_t* __restrict__ order, uint32_t n,
+                                                        const uint32_t* __restrict__ order, uint32_t shift,
+                                                        uint32_t n,
                                                         const uint64_t* __restrict__ part,
                                                         uint64_t* __restrict__ offsets) {
   __shared__ uint64_t smem[kThreads / kWave];
@@ -208,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void k_scan_down(const uint32_t* __restri
   uint64_t sum = 0;
 #pragma unroll
   for (uint32_t i = 0; i < kScanItems; ++i) {
-    c[i] = (base + i < n) ? count_at(counts, order, n, base + i) : 0u;
+    c[i] = (base + i < n) ? count_at(counts, order, n, base + i, shift) : 0u;
     sum += c[i];
   }
   uint64_t run = part[blockIdx.x] + block_exclusive_scan<uint64_t, kThreads>(sum, nullptr, smem);
@@ -270,7 +276,8 @@ __device__ __forceinline__ uint32_t block_exclusive_max(uint32_t v, uint32_t car
 // (tile << idx_bits) | splat and no value array.
 template <typename K, bool kPacked = false>
 __global__ __launch_bounds__(kThreads) void k_emit(const uint4* __restrict__ rects, const float* __restrict__ depths,
-                                                   uint32_t n, const uint32_t* __restrict__ order, uint32_t tiles_x,
+                                                   uint32_t n, const uint32_t* __restrict__ order,
+                                                   uint32_t order_mask, uint32_t tiles_x,
                                                    const uint64_t* __restrict__ offsets, uint64_t num_pairs,
                                                    K* __restrict__ keys, uint32_t* __restrict__ vals,
                                                    uint32_t idx_bits) {
@@ -284,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void k_emit(const uint4* __restrict__ rec
   s_off[tid] = offsets[min(j, n)];
   if (tid == 0) s_off[kThreads] = offsets[min(blockIdx.x * kThreads + kThreads, n)];
   if (j < n) {
-    uint32_t i = order ? order[j] : j;
+    uint32_t i = order ? order[j] & order_mask : j;
     if (i >= n) i = 0;  // not reachable with a permutation in `order`; its count is 0 then (see count_at)
     const uint4 r = rects[i];
     s_tx0[tid] = r.x;
@@ -364,13 +371,14 @@ template <typename K, bool kPacked = false>
 __global__ __launch_bounds__(kThreads) void k_emit_ellipse(const float* __restrict__ splats,
                                                            const uint4* __restrict__ rects,
                                                            const float* __restrict__ depths, uint32_t n,
-                                                           const uint32_t* __restrict__ order, uint32_t tiles_x,
+                                                           const uint32_t* __restrict__ order, uint32_t order_mask,
+                                                           uint32_t tiles_x,
                                                            const uint64_t* __restrict__ offsets,
                                                            uint64_t num_pairs, K* __restrict__ keys,
                                                            uint32_t* __restrict__ vals, uint32_t idx_bits) {
   const uint32_t j = blockIdx.x * kThreads + threadIdx.x;
   if (j >= n) return;
-  const uint32_t i = order ? order[j] : j;
+  const uint32_t i = order ? order[j] & order_mask : j;
   if (i >= n) return;  // not reachable with a permutation in `order`
   const uint4 r = rects[i];
   const float* sp = splats + size_t(i) * 9;
@@ -570,6 +578,12 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   uint64_t* part = static_cast<uint64_t*>(a.scan_part.ptr);
   uint32_t* ok = static_cast<uint32_t*>(a.order.ptr);
   uint32_t* ov = static_cast<uint32_t*>(a.order_vals.ptr);
+  // the presort scheme carries each splat's count in its depth-sort value when index and count fit 32 bits
+  // (a count is at most num_tiles)
+  const uint32_t idx_bits = bits_of(n ? n - 1 : 0);
+  const bool pack_counts = presort && n && idx_bits + bits_of(num_tiles) <= 32;
+  const uint32_t count_shift = pack_counts ? idx_bits : 32u;
+  const uint32_t order_mask = pack_counts ? (idx_bits ? (1u << idx_bits) - 1u : 0u) : ~0u;
 
   // Rectangles, counts and the pair total first; the total goes to the host while the depth sort runs.
   timing_mark(ctx, GSR_STAGE_BIN, s, false);
@@ -577,7 +591,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     hipLaunchKernelGGL(k_prep, dim3(nb_prep), dim3(kThreads), 0, s, splats, depths, n, tiles_x, tiles_y, ellipse,
                        rects, counts,
                        presort ? ok : static_cast<uint32_t*>(nullptr), presort ? ov : static_cast<uint32_t*>(nullptr),
-                       part);
+                       count_shift, part);
     hipLaunchKernelGGL(k_total, dim3(1), dim3(kThreads), 0, s, part, nb_prep, offsets + n);
   } else {
     hipLaunchKernelGGL(k_total, dim3(1), dim3(kThreads), 0, s, part, 0u, offsets);
@@ -599,12 +613,21 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   }
   // offsets in emission order (depth order for the presort scheme); the scan rewrites offsets[n] with the same total
   if (n) {
-    // the presort scheme gathers its counts once, into the depth sort's (now free) value scratch
-    uint32_t* ordered = order ? static_cast<uint32_t*>(a.order_vals_alt.ptr) : nullptr;
-    hipLaunchKernelGGL(k_scan_reduce, dim3(nb_scan), dim3(kThreads), 0, s, counts, order, n, part, ordered,
-                       a.done, a.done, offsets);
-    hipLaunchKernelGGL(k_scan_down, dim3(nb_scan), dim3(kThreads), 0, s, order ? ordered : counts,
-                       static_cast<const uint32_t*>(nullptr), n, part, offsets);
+    if (pack_counts) {
+      // the sorted values carry the counts: both launches read them in place
+      hipLaunchKernelGGL(k_scan_reduce, dim3(nb_scan), dim3(kThreads), 0, s, static_cast<const uint32_t*>(ov),
+                         static_cast<const uint32_t*>(nullptr), count_shift, n, part, static_cast<uint32_t*>(nullptr),
+                         a.done, a.done, offsets);
+      hipLaunchKernelGGL(k_scan_down, dim3(nb_scan), dim3(kThreads), 0, s, static_cast<const uint32_t*>(ov),
+                         static_cast<const uint32_t*>(nullptr), count_shift, n, part, offsets);
+    } else {
+      // otherwise the presort scheme gathers its counts once, into the depth sort's (now free) value scratch
+      uint32_t* ordered = order ? static_cast<uint32_t*>(a.order_vals_alt.ptr) : nullptr;
+      hipLaunchKernelGGL(k_scan_reduce, dim3(nb_scan), dim3(kThreads), 0, s, counts, order, 0u, n, part, ordered,
+                         a.done, a.done, offsets);
+      hipLaunchKernelGGL(k_scan_down, dim3(nb_scan), dim3(kThreads), 0, s, order ? ordered : counts,
+                         static_cast<const uint32_t*>(nullptr), 0u, n, part, offsets);
+    }
   }
   if ((st = check_launch(ctx, "gsr_bin depth sort/scan"))) return st;
 
@@ -624,17 +647,16 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   uint64_t* final_k = nullptr;
   uint32_t* sorted_v = nullptr;
   // the splat index and the tile id share one 32-bit key when they fit (and there is a tile pass to unpack it)
-  const uint32_t idx_bits = bits_of(n ? n - 1 : 0);
   const bool packed = presort && n && P > 0 && tile_bits > 0 && idx_bits + tile_bits <= 32;
   if (packed) {
     uint32_t* kb[2] = {static_cast<uint32_t*>(a.keys[0].ptr), static_cast<uint32_t*>(a.keys[1].ptr)};
     if (ellipse)
       hipLaunchKernelGGL((k_emit_ellipse<uint32_t, true>), dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats,
-                         rects, depths, n, order, tiles_x, offsets, P, kb[0], static_cast<uint32_t*>(nullptr),
+                         rects, depths, n, order, order_mask, tiles_x, offsets, P, kb[0], static_cast<uint32_t*>(nullptr),
                          idx_bits);
     else
       hipLaunchKernelGGL((k_emit<uint32_t, true>), dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, rects, depths,
-                         n, order, tiles_x, offsets, P, kb[0], static_cast<uint32_t*>(nullptr), idx_bits);
+                         n, order, order_mask, tiles_x, offsets, P, kb[0], static_cast<uint32_t*>(nullptr), idx_bits);
     res = (sort_passes(tile_bits) & 1u) ? 1 : 0;  // the first pass writes buffer 1 either way
     if (ctx->bin_keys) {
       if ((st = grow(ctx, a.order_alt, std::max<size_t>(size_t(n) * 8, size_t(P) * 8)))) return st;
@@ -655,10 +677,10 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     {
       if (ellipse)
         hipLaunchKernelGGL(k_emit_ellipse<uint32_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats, rects,
-                           depths, n, order, tiles_x, offsets, P, kb[0], v0, 0u);
+                           depths, n, order, order_mask, tiles_x, offsets, P, kb[0], v0, 0u);
       else
         hipLaunchKernelGGL(k_emit<uint32_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, rects, depths, n, order,
-                           tiles_x, offsets, P, kb[0], v0, 0u);
+                           order_mask, tiles_x, offsets, P, kb[0], v0, 0u);
     }
     // The 64-bit keys go to the key buffer the sorted tile ids do not end in, written by the last sort pass (or by
     // the range kernel when there is no pass).
@@ -692,10 +714,10 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     {
       if (ellipse)
         hipLaunchKernelGGL(k_emit_ellipse<uint64_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats, rects,
-                           depths, n, order, tiles_x, offsets, P, kb[0], v0, 0u);
+                           depths, n, order, order_mask, tiles_x, offsets, P, kb[0], v0, 0u);
       else
         hipLaunchKernelGGL(k_emit<uint64_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, rects, depths, n, order,
-                           tiles_x, offsets, P, kb[0], v0, 0u);
+                           order_mask, tiles_x, offsets, P, kb[0], v0, 0u);
     }
     if (P > 0) {
       const uint32_t key_bits = 32 + tile_bits;

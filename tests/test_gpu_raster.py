@@ -224,6 +224,56 @@ def test_skips_change_no_result(ctx, name):
         assert np.array_equal(ga, gb)
 
 
+def test_cull_keeps_every_pixel_of_thin_tilted_splats(ctx):
+    """The block cull's separating axes (box and diagonals) against splats built to sit at its edges: needles up
+    to 300 times longer than wide (condition numbers up to about 1e5, where the cull gives up) at every angle,
+    opacities from 1/255 to 1, means scattered over and around a 96 x 80 image so that many ellipses pass close by
+    block corners. The forward and single-pixel backwards are bit-identical with and without the skips, and the
+    forward equals the oracle."""
+    from differentiable_gaussian_splatting_amd import gsr
+    import oracle
+    banner("cull thin tilted splats")
+    rng = np.random.default_rng(23)
+    W, H, n = 96, 80, 4000
+    s1 = np.exp(rng.uniform(np.log(0.2), np.log(2.0), n))
+    s2 = s1 * np.exp(rng.uniform(np.log(2.0), np.log(300.0), n))
+    th = rng.uniform(0.0, np.pi, n)
+    c, s = np.cos(th), np.sin(th)
+    sxx = c * c * s2 * s2 + s * s * s1 * s1
+    syy = s * s * s2 * s2 + c * c * s1 * s1
+    sxy = c * s * (s2 * s2 - s1 * s1)
+    det = sxx * syy - sxy * sxy
+    o = np.concatenate([rng.uniform(1.0 / 255.0, 1.0, n - 8), [1.0, 1.0, 1.0 / 255.0, 1.0 / 255.0, 0.5, 0.999, 0.0, 1e-3]])
+    sp = np.stack([rng.uniform(-40.0, W + 40.0, n), rng.uniform(-40.0, H + 40.0, n), syy / det, -sxy / det,
+                   sxx / det, rng.uniform(0, 1, n), rng.uniform(0, 1, n), rng.uniform(0, 1, n), o], 1).astype(np.float32)
+    depths = rng.uniform(0.1, 10.0, n).astype(np.float32)
+    spd = dev(sp)
+    bins = gsr.gsr_bin(ctx, spd, dev(depths), W, H)
+    upstream = []
+    for _ in range(3):
+        py, px = (int(v) for v in rng.integers(0, (H, W)))
+        v = np.zeros((H, W, 4), np.float32)
+        v[py, px, :3] = rng.normal(size=3)
+        upstream.append(v)
+    res = {}
+    try:
+        for on in (True, False):
+            set_skip(ctx, on)
+            out, ft, lc = run_forward(ctx, spd, bins, W, H)
+            grads = [host(gsr.gsr_render_backward(ctx, spd, bins, W, H, out, ft, lc, dev(v))) for v in upstream]
+            res[on] = (host(out), host(ft), host(lc, np.uint32), grads)
+    finally:
+        set_skip(ctx, True)
+    a, b = res[True], res[False]
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+    for ga, gb in zip(a[3], b[3]):
+        assert np.array_equal(ga, gb)
+    ob = oracle.bin(sp, depths, W, H)
+    ref = oracle.render_forward(sp, ob, W, H)
+    assert np.array_equal(a[2], ref[2]) and np.abs(a[0] - ref[0]).max() <= IMG_TOL
+    print(f"  composited pixels {int((a[2] > 0).sum())} of {W * H}; pairs {bins.num_pairs}")
+
+
 def test_backward_zeroes_and_fills_unaligned_gradient_buffers(ctx):
     """splats_grad starting 4 bytes past a 16-byte boundary (the zero fill takes its element-by-element path) gets
     the same bits as an aligned one, over buffers that held NaN before the call. One non-zero upstream pixel makes
