@@ -91,7 +91,9 @@ def test_bin_empty_and_all_culled(ctx, scheme):
 def test_bin_packed_and_unpacked_tile_sort(ctx, w, h, n):
     """The presort scheme packs (tile, splat) into one 32-bit key when bits(n - 1) + bits(tiles - 1) <= 32: a
     single tile (no tile pass: not packed), 2^20 splats on 4096 tiles (exactly 32 bits: packed), and 2^23 tiles
-    with 3000 splats (36 bits: the two-array form). All bit-exact against the oracle."""
+    with 3000 splats (36 bits: the two-array form). It also carries each splat's count in its depth-sort value when
+    bits(n - 1) + bits(tiles) <= 32: the first case does, the other two (33 and 36 bits) gather the counts through
+    the sorted indices instead. All bit-exact against the oracle."""
     banner(f"bin packing {w}x{h} n={n}")
     # round splats of s in 0.5-20 px over the image (drawn here: the scene generator's per-pixel upstream gradient
     # would not fit the largest image)
