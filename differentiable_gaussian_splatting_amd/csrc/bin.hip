@@ -246,14 +246,16 @@ __device__ __forceinline__ uint32_t block_exclusive_max(uint32_t v, uint32_t car
                                                         uint32_t* smem) {
   constexpr unsigned kWaves = kThreads / 64;
   const unsigned lane = threadIdx.x & 63u, w = threadIdx.x / 64u;
+  // inclusive running maximum over the wave with DPP moves (as wave_inclusive_sum; 0 is the identity), then the
+  // lane before's value (wave_shr 1; lane 0 gets 0)
   uint32_t x = v;
-#pragma unroll
-  for (unsigned off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off, 64);
-    if (lane >= off) x = max(x, y);
-  }
-  uint32_t ex = __shfl_up(x, 1, 64);
-  if (lane == 0) ex = 0;
+  x = max(x, dpp_or_zero<0x111, 0xF>(x));
+  x = max(x, dpp_or_zero<0x112, 0xF>(x));
+  x = max(x, dpp_or_zero<0x114, 0xF>(x));
+  x = max(x, dpp_or_zero<0x118, 0xF>(x));
+  x = max(x, dpp_or_zero<0x142, 0xA>(x));
+  x = max(x, dpp_or_zero<0x143, 0xC>(x));
+  const uint32_t ex = dpp_or_zero<0x138, 0xF>(x);
   if (lane == 63) smem[w] = x;
   __syncthreads();
   uint32_t before = carry, all = carry;

@@ -5,18 +5,37 @@
 
 namespace gsr {
 
+// v from the lane the DPP control selects, 0 where the control selects no lane or the row mask disables the lane.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), kCtrl, kRowMask, 0xF, true));
+}
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint64_t dpp_or_zero(uint64_t v) {
+  return (uint64_t(dpp_or_zero<kCtrl, kRowMask>(uint32_t(v >> 32))) << 32) | dpp_or_zero<kCtrl, kRowMask>(uint32_t(v));
+}
+
+// Inclusive sum over the wave's lanes 0..lane, with DPP moves (no LDS round trips): row_shr 1, 2, 4, 8 within each
+// 16-lane row, then row_bcast 15 (rows 1 and 3 add the last lane of the row before) and row_bcast 31 (rows 2 and 3
+// add lane 31). All 64 lanes must be active.
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_sum(T x) {
+  x += dpp_or_zero<0x111, 0xF>(x);
+  x += dpp_or_zero<0x112, 0xF>(x);
+  x += dpp_or_zero<0x114, 0xF>(x);
+  x += dpp_or_zero<0x118, 0xF>(x);
+  x += dpp_or_zero<0x142, 0xA>(x);
+  x += dpp_or_zero<0x143, 0xC>(x);
+  return x;
+}
+
 // Exclusive scan of one value per thread over a workgroup of kThreads (a multiple of 64) threads. `smem` holds
 // kThreads / 64 elements. Every thread of the workgroup must call it. If total is non-null it receives the sum.
 template <typename T, unsigned kThreads>
 __device__ __forceinline__ T block_exclusive_scan(T v, T* total, T* smem) {
   constexpr unsigned kWaves = kThreads / 64;
   const unsigned lane = threadIdx.x & 63u, w = threadIdx.x / 64u;
-  T x = v;
-#pragma unroll
-  for (unsigned off = 1; off < 64; off <<= 1) {
-    const T y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  const T x = wave_inclusive_sum(v);
   if (lane == 63) smem[w] = x;
   __syncthreads();
   T before = 0, all = 0;
