@@ -31,9 +31,12 @@ UNIT = "splat-pixel evals/s"
 TIMED_RANGE = "timed steps"  # ROCTx range around the timed steps
 MEASURED_RANGE = "measured steps"  # ROCTx range around the steps that carry HIP events
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
-# fp32 vector rate without packed dual-fp32 instructions: 256 CUs x 64 lanes x 2 flops (FMA) x 2.4 GHz
-ALU_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
-ALU_PUBLISHED_TFLOPS = 157.3  # the published fp32 vector figure, which counts packed dual-fp32 FMA
+ALU_PEAK_TFLOPS = 157.3  # MI355X's published fp32 vector peak (it counts packed dual-fp32 FMA)
+# fp32 vector rate without packed dual-fp32 instructions (which this build does not use): 256 CUs x 64 lanes x 2
+# flops (FMA) x 2.4 GHz, reported beside the published peak
+ALU_NONPACKED_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
+# VALU issue: a wave64 instruction occupies a 16-lane SIMD for 4 cycles; 1024 SIMDs at 2.4 GHz
+VALU_ISSUE_PER_S = 1024 * 2.4e9 / 4
 
 # Algorithmic operation counts per evaluation (each add, sub, mul, min, exp counts 1; comparisons and negations 0):
 #   sigma       dx, dy, (a dx) dx, (c dy) dy, (b dx) dy, two sums, x0.5                        = 11
@@ -52,6 +55,14 @@ BWD_OPS = {"sigma_skip": 11, "alpha_reject": 14, "contrib": 73}
 LOSS_OPS = 3 + 220 + 25 + 132 + 6
 
 
+def scene_label(spec) -> str:
+    """The generator's parameters of a workload, e.g. '70% s in 0.3-4 px, 30% s in 4-40 px, color_a =
+    sigmoid(N(-2, 1.5))'."""
+    tot = sum(c[0] for c in spec.size_classes)
+    sizes = ", ".join(f"{round(100 * c[0] / tot)}% s in {c[1]:g}-{c[2]:g} px" for c in spec.size_classes)
+    return f"{sizes}, color_a = sigmoid(N({spec.opacity_mu:g}, {spec.opacity_sd:g}))"
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -61,7 +72,9 @@ def parse():
     ap.add_argument("--bin-scheme", choices=["presort", "key64"], default="presort")
     ap.add_argument("--raster-skip", type=int, choices=[0, 1], default=1)
     ap.add_argument("--bin-rule", choices=["box", "ellipse"], default="box")
+    ap.add_argument("--repeats", type=int, default=3, help="timed repeats of K steps (median and spread reported)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bin-stress", action="store_true", help="skip the binning leg on the 1M-splat scene")
     ap.add_argument("--calib-copy", action="store_true")
     return ap.parse_args()
 
@@ -205,48 +218,61 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: exactly K steps, synchronized on both sides, with nothing else on the stream (HIP events
-    # between the kernels cost about 50 us of launch gaps per step, so they are taken in the steps after it)
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    # between the kernels cost about 50 us of launch gaps per step, so they are taken in the steps after it); the
+    # region is run `repeats` times and the median repeat is reported, with the spread
     rx = roctx()  # the timed region as a ROCTx range, so that a kernel trace can single out its dispatches
-    torch.cuda.synchronize()
-    if rx:
-        rx.roctxRangePushA(TIMED_RANGE.encode())
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        b = step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    if rx:
-        rx.roctxRangePop()
+    walls = []
+    for rep in range(args.repeats):
+        print(f"[bench] timing {args.steps} steps (repeat {rep + 1} of {args.repeats})", file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        if rx:
+            rx.roctxRangePushA(TIMED_RANGE.encode())
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            b = step()
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t0)
+        if rx:
+            rx.roctxRangePop()
+    wall = float(np.median(walls))
     ms_per_step = wall * 1e3 / args.steps
 
-    # K more steps with HIP events on the library's stream: torch's around each stage (its launches and small
-    # kernels included), the library's around each stage's main kernel (GSR_OPT_KERNEL_TIMING); the kernels' own
-    # durations are the ones the rooflines use
-    print(f"[bench] {args.steps} steps with per-stage and per-kernel events", file=sys.stderr, flush=True)
-    gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, args.steps)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    if rx:
-        rx.roctxRangePushA(MEASURED_RANGE.encode())
-    for k in range(args.steps):
-        b = step(events[k])
-    torch.cuda.synchronize()
-    if rx:
-        rx.roctxRangePop()
-    stage_ms = {nm: float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
-                for i, nm in enumerate(names)}
-    stage_ms_median = {nm: float(np.median([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
-                       for i, nm in enumerate(names)}
+    # K more steps per repeat with HIP events on the library's stream: torch's around each stage (its launches and
+    # small kernels included), the library's around each stage's main kernel (GSR_OPT_KERNEL_TIMING); the kernels'
+    # own durations are the ones the rooflines use. Per repeat the mean over its K steps; reported: the median of
+    # the repeats and their standard deviation.
     kernel_stage = {"bin": gsr.GSR_STAGE_BIN, "forward": gsr.GSR_STAGE_FORWARD, "backward": gsr.GSR_STAGE_BACKWARD,
                     "adam": gsr.GSR_STAGE_ADAM, "depth_sort": gsr.GSR_STAGE_DEPTH_SORT,
                     "tile_sort": gsr.GSR_STAGE_TILE_SORT}
-    kernel_ms = {}
-    for nm, stg in kernel_stage.items():
-        t = gsr.gsr_kernel_times(ctx, stg)
-        assert len(t) == args.steps, f"{nm}: {len(t)} launches recorded"
-        kernel_ms[nm] = float(np.mean(t))
-    gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, 0)
+    stage_reps = {nm: [] for nm in names}
+    kernel_reps = {nm: [] for nm in kernel_stage}
+    for rep in range(args.repeats):
+        print(f"[bench] {args.steps} steps with per-stage and per-kernel events (repeat {rep + 1})", file=sys.stderr,
+              flush=True)
+        gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, args.steps)
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        if rx:
+            rx.roctxRangePushA(MEASURED_RANGE.encode())
+        for k in range(args.steps):
+            b = step(events[k])
+        torch.cuda.synchronize()
+        if rx:
+            rx.roctxRangePop()
+        for i, nm in enumerate(names):
+            stage_reps[nm].append(float(np.mean([events[k][i].elapsed_time(events[k][i + 1])
+                                                 for k in range(args.steps)])))
+        for nm, stg in kernel_stage.items():
+            t = gsr.gsr_kernel_times(ctx, stg)
+            assert len(t) == args.steps, f"{nm}: {len(t)} launches recorded"
+            kernel_reps[nm].append(float(np.mean(t)))
+        gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, 0)
+    stage_ms = {nm: float(np.median(v)) for nm, v in stage_reps.items()}
+    kernel_ms = {nm: float(np.median(v)) for nm, v in kernel_reps.items()}
+    spread = {"ms_per_step": {"repeats": [w * 1e3 / args.steps for w in walls],
+                              "sigma": float(np.std([w * 1e3 / args.steps for w in walls]))},
+              "stage_ms": {nm: {"repeats": v, "sigma": float(np.std(v))} for nm, v in stage_reps.items()},
+              "kernel_ms": {nm: {"repeats": v, "sigma": float(np.std(v))} for nm, v in kernel_reps.items()}}
     P = b.num_pairs
     e_bwd_gpu = int(last_contrib.to(torch.int64).sum().item())
     det = bench_deterministic_backward(args, ctx, gsr, torch, np, stream, splats, b, W, H, out_rgba, final_T,
@@ -265,18 +291,19 @@ def main():
     result = {"metric": METRIC, "unit": UNIT, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
               "dtype": "f32", "data": "synthetic",
-              "config": {"workload": f"{args.workload}: {W}x{H} image, {N} splats "
-                                     "(70% s in 0.3-4 px, 30% s in 4-40 px, color_a = sigmoid(N(-2, 1.5))), "
+              "config": {"workload": f"{args.workload}: {W}x{H} image, {N} splats ({scene_label(sc.spec)}), "
                                      "bin + forward + backward + fused Adam over 59 fp32 params per splat",
                          "image": [W, H], "splats": N, "pairs": P, "adam_elements": adam_elems,
                          "bin_scheme": args.bin_scheme, "bin_rule": args.bin_rule,
                          "raster_skip": args.raster_skip}}
+    result["repeats"] = args.repeats
     result["stage_ms"] = stage_ms
-    result["stage_ms_median"] = stage_ms_median
     result["kernel_ms"] = kernel_ms  # the main kernel(s) of each stage alone (GSR_OPT_KERNEL_TIMING)
-    result["timing"] = ("value and ms_per_step: wall clock of the K timed steps, which carry no events; stage_ms "
-                        "and kernel_ms: HIP events in K further steps (torch's around each stage, the library's "
-                        "around each stage's main kernel on its stream)")
+    result["spread"] = spread
+    result["timing"] = ("value and ms_per_step: wall clock of K timed steps, which carry no events, the median of "
+                        f"{args.repeats} repeats; stage_ms and kernel_ms: HIP events in K further steps per repeat "
+                        "(torch's around each stage, the library's around each stage's main kernel on its stream), "
+                        "the median of the repeats' means; spread: each repeat and the standard deviation")
     result["fwd_bwd_ms"] = stage_ms["forward"] + stage_ms["backward"]
     det["ratio_to_default"] = det["ms"] / stage_ms["backward"]
     det["kernel_ratio_to_default"] = det["kernel_ms"] / kernel_ms["backward"]
@@ -300,11 +327,15 @@ def main():
                    BWD_OPS["alpha_reject"] * (bs["alpha_reject"] - bs["sigma_ge_skip"]) +
                    BWD_OPS["contrib"] * bs["contrib"])
         adam_bytes = 28 * adam_elems
+        eff = ("effective rate: the method's own operations per launch (the oracle's exact evaluation counts times "
+               "the per-evaluation operation model above) over the kernel's time; peak: the published fp32 vector "
+               "figure")
         roofs = {
             "forward": {"bound": "alu", "achieved": fwd_ops / (kernel_ms["forward"] * 1e-3) / 1e12,
-                        "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s", "work_per_launch": fwd_ops},
+                        "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s", "work_per_launch": fwd_ops, "achieved_kind": eff},
             "backward": {"bound": "alu", "achieved": bwd_ops / (kernel_ms["backward"] * 1e-3) / 1e12,
-                         "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s", "work_per_launch": bwd_ops},
+                         "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s", "work_per_launch": bwd_ops,
+                         "achieved_kind": eff},
             "adam": {"bound": "hbm", "achieved": adam_bytes / (kernel_ms["adam"] * 1e-3) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "work_per_launch": adam_bytes},
         }
@@ -321,10 +352,15 @@ def main():
                 r["traffic"] = profiling.traffic_for(profiling.sort_kernels(r["passes"]), traffic_md)
                 continue
             r["traffic"] = profiling.traffic_for(profiling.STAGE_KERNEL[k], traffic_md)
-            if r["bound"] == "alu":  # the share of VALU issue slots the kernel used (its counters, same record)
-                r["valu_issue_frac"] = profiling.valu_issue_for(profiling.STAGE_KERNEL[k], traffic_md)
+            if r["bound"] == "alu":
+                # the share of the chip's VALU issue slots the kernel used: its VALU wave instructions per launch
+                # (counter record) over this run's kernel time
+                insts = profiling.valu_insts_for(profiling.STAGE_KERNEL[k], traffic_md)
+                r["valu_insts_per_launch"] = insts
+                r["valu_issue_frac"] = (None if insts is None else
+                                        insts / (r["kernel_ms"] * 1e-3 * VALU_ISSUE_PER_S))
         for k in ("forward", "backward"):
-            roofs[k]["frac_of_published_157_3"] = roofs[k]["achieved"] / ALU_PUBLISHED_TFLOPS
+            roofs[k]["frac_of_nonpacked_78_6"] = roofs[k]["achieved"] / ALU_NONPACKED_TFLOPS
         dominant = max(("forward", "backward", "adam"), key=lambda k: kernel_ms[k])
         result["roofline"] = {"kernel": dominant, **roofs[dominant]}
         result["rooflines"] = roofs
@@ -349,6 +385,8 @@ def main():
                          "pages_splats": 409660, "this_fwd_bwd_adam_ms": stage_ms["forward"] + stage_ms["backward"]
                          + stage_ms["adam"], "this_backward_ms": stage_ms["backward"]}
     result["projection"] = bench_projection(args, ctx, gsr, scenes, sc, hp=hp, bc=bc)
+    if not args.no_bin_stress:
+        result["bin_stress"] = bench_bin_stress(args, ctx, gsr, scenes, torch, np)
     print(json.dumps(result), flush=True)
     ctx.close()
 
@@ -396,6 +434,66 @@ def sort_roofline(args, N, P, W, H, kernel_ms):
             "tile_sort_ms": kernel_ms["tile_sort"], "packed": packed, "passes": {"depth": 4, "tile": tile_passes},
             "pages_64bit_sort_bytes": pages_bytes,
             "pages_target_ms_at_70pct": pages_bytes / (0.7 * HBM_PEAK_GBS * 1e9) * 1e3}
+
+
+def bench_bin_stress(args, ctx, gsr, scenes, torch, np):
+    """The binning on its own on the 1M-splat stress scene (about 26M pairs under the box rule), under both
+    schemes, timed with the library's events over K calls per repeat (median of the repeats' means). Sort
+    rooflines on algorithmic bytes:
+      key64 (the pages' scheme): a stable LSD sort of the 64-bit (tile | depth) keys with their 32-bit values over
+        d = ceil((tile bits + 32) / 8) passes, P (8 + 24 d) bytes: one read of the keys for the digit histograms and
+        a read and a write of key and value per pass;
+      presort (the default): the depth sort of the n 32-bit depth keys with their indices (4 passes, 20 B per key
+        per pass) and the tile sort of the pairs by their tile id (per pass 12 B per pair on packed 32-bit words;
+        the last one adds the 4 B value, the 8 B 64-bit key and the 4 B depth gather)."""
+    sc = scenes.make_scene("bin1m")
+    W, H, N = sc.width, sc.height, sc.spec.n
+    sp, dp = torch.from_numpy(sc.splats).cuda(), torch.from_numpy(sc.depths).cuda()
+    tiles = ((W + 15) // 16) * ((H + 15) // 16)
+    tile_bits = int(tiles - 1).bit_length()
+    out = {"workload": f"bin1m: {W}x{H} image, {N} splats ({scene_label(sc.spec)}), box rule"}
+    for scheme, opt in (("presort", gsr.GSR_BIN_PRESORT), ("key64", gsr.GSR_BIN_KEY64)):
+        gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SCHEME, opt)
+        b = gsr.gsr_bin(ctx, sp, dp, W, H)
+        P = b.num_pairs
+        gsr.gsr_reserve(ctx, P, N)
+        for _ in range(3):
+            gsr.gsr_bin(ctx, sp, dp, W, H)
+        reps = {"bin": [], "depth_sort": [], "tile_sort": []}
+        for _ in range(args.repeats):
+            gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, args.steps)
+            for _ in range(args.steps):
+                gsr.gsr_bin(ctx, sp, dp, W, H)
+            torch.cuda.synchronize()
+            for nm, stg in (("bin", gsr.GSR_STAGE_BIN), ("depth_sort", gsr.GSR_STAGE_DEPTH_SORT),
+                            ("tile_sort", gsr.GSR_STAGE_TILE_SORT)):
+                t = gsr.gsr_kernel_times(ctx, stg)
+                reps[nm].append(float(np.mean(t)) if t else 0.0)
+            gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, 0)
+        ms = {nm: float(np.median(v)) for nm, v in reps.items()}
+        if scheme == "key64":
+            d = (tile_bits + 32 + 7) // 8
+            by = P * (8 + 24 * d)
+            sort_ms = ms["tile_sort"]
+            note = f"64-bit key sort, {d} passes of 8-bit digits: P (8 + 24 d) B"
+        else:
+            packed = int(N - 1).bit_length() + tile_bits <= 32
+            tp = (tile_bits + 5) // 6
+            by = 4 * 20 * N + ((12 * tp + 16) if packed else (20 * tp + 12)) * P
+            sort_ms = ms["depth_sort"] + ms["tile_sort"]
+            note = (f"depth sort 4 x 20 B per splat + tile sort {tp} passes of 6-bit digits "
+                    f"({'packed' if packed else 'unpacked'})")
+        ach = by / (sort_ms * 1e-3) / 1e9
+        out[scheme] = {"pairs": P, "bin_ms": ms["bin"], "depth_sort_ms": ms["depth_sort"],
+                       "tile_sort_ms": ms["tile_sort"], "sigma": {nm: float(np.std(v)) for nm, v in reps.items()},
+                       "sort_roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                         "frac": ach / HBM_PEAK_GBS, "work_per_launch": by, "kernel_ms": sort_ms,
+                                         "bytes": note}}
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SCHEME, gsr.GSR_BIN_PRESORT if args.bin_scheme == "presort"
+                       else gsr.GSR_BIN_KEY64)
+    k64 = out["key64"]["sort_roofline"]["work_per_launch"]
+    out["pages_target_ms_at_70pct"] = k64 / (0.7 * HBM_PEAK_GBS * 1e9) * 1e3
+    return out
 
 
 def bench_deterministic_backward(args, ctx, gsr, torch, np, stream, splats, b, W, H, out_rgba, final_T, last_contrib,

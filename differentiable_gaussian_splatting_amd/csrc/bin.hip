@@ -271,7 +271,9 @@ __device__ __forceinline__ uint32_t block_exclusive_max(uint32_t v, uint32_t car
 }
 
 // Emission. Workgroup b owns emission positions [256 b, 256 b + 256) and the contiguous output range of their
-// pairs, which it writes in chunks of 1024 pairs, four consecutive pairs per thread (coalesced stores). In each
+// pairs, which it writes in chunks of 1024 pairs, four consecutive pairs per thread (coalesced stores; the chunks
+// start at the range's first position rounded down to a multiple of four, so that each thread's four pairs are
+// one aligned 16-byte vector of 32-bit keys or values, and the positions before the range are masked). In each
 // chunk every splat marks the slot of its first pair with its position + 1, and a running maximum over the chunk
 // (seeded with the previous chunk's last owner) gives each pair its splat. Inside a splat the tiles go row by
 // row. 64-bit keys: (tile << 32) | depth bits; 32-bit keys: the tile id only, or with kPacked
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void k_emit(const uint4* __restrict__ rec
   const uint64_t my_start = s_off[tid];
   const bool has_pairs = s_off[tid + 1] > my_start;
   uint32_t carry = 0;
-  for (uint64_t c0 = begin; c0 < end; c0 += kChunk) {
+  for (uint64_t c0 = begin & ~uint64_t(kPer - 1); c0 < end; c0 += kChunk) {
 #pragma unroll
     for (uint32_t e = 0; e < kPer; ++e) s_mark[e * kThreads + tid] = 0;
     __syncthreads();
@@ -323,8 +325,9 @@ __global__ __launch_bounds__(kThreads) void k_emit(const uint4* __restrict__ rec
     }
     uint32_t chunk_max;
     const uint32_t before = block_exclusive_max<kThreads>(run, carry, &chunk_max, smem);
-    // the thread's kPer consecutive pairs; written as 16-byte vectors when all of them exist (p0 is a multiple of
-    // kPer, so the vectors are aligned), element by element at the ends of the range
+    // the thread's kPer consecutive pairs; written as vectors when all of them are in the range (p0 is a multiple
+    // of kPer, so the vectors are aligned: 16 bytes of 32-bit keys or values, 32 of 64-bit keys), element by
+    // element at the ends of the range
     const uint64_t p0 = c0 + kPer * tid;
     K kk[kPer];
     uint32_t vv[kPer];
@@ -333,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void k_emit(const uint4* __restrict__ rec
     for (uint32_t e = 0; e < kPer; ++e) {
       const uint64_t p = p0 + e;
       const uint32_t owner = max(before, m[e]);  // >= 1 for every pair below end
-      ok[e] = p < end && owner > 0;
+      ok[e] = p >= begin && p < end && owner > 0;
       const uint32_t q = owner > 0 ? owner - 1 : 0;
       const uint32_t k = uint32_t(p - s_off[q]);
       const uint32_t w = s_w[q];

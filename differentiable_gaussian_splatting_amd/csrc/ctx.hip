@@ -28,9 +28,31 @@ gsr_status enter(gsr_ctx* ctx) {
   return GSR_OK;
 }
 
+// Calls f on every buffer of the arena.
+template <typename F>
+static void for_each_buffer(Arena& a, F f) {
+  for (DevBuf* b : {&a.keys[0], &a.keys[1], &a.vals[0], &a.vals[1], &a.counts, &a.offsets, &a.order, &a.order_alt,
+                    &a.order_vals, &a.order_vals_alt, &a.scan_part, &a.hist, &a.digit_tot, &a.ranges, &a.rects,
+                    &a.tile_order_ext, &a.tile_cost, &a.loss_part, &a.loss_maps, &a.grad_fixed})
+    f(*b);
+}
+
+size_t arena_bytes(const Arena& a) {
+  size_t total = 0;
+  for_each_buffer(const_cast<Arena&>(a), [&](DevBuf& b) { total += b.bytes; });
+  return total;
+}
+
 gsr_status grow(gsr_ctx* ctx, DevBuf& b, size_t bytes) {
   if (bytes <= b.bytes) return GSR_OK;
   size_t want = std::max<size_t>({bytes, b.bytes + b.bytes / 2, size_t(1) << 16});
+  if (ctx->arena.limit) {
+    const size_t others = arena_bytes(ctx->arena) - b.bytes;
+    if (others + bytes > ctx->arena.limit)
+      return fail(ctx, GSR_ENOMEM, "device arena: growing a buffer to %zu bytes would pass the arena limit of %zu "
+                  "bytes (%zu held by the other buffers)", bytes, ctx->arena.limit, others);
+    want = std::min(want, ctx->arena.limit - others);
+  }
   void* p = nullptr;
   hipError_t e = hipMalloc(&p, want);
   if (e != hipSuccess) {
@@ -136,6 +158,7 @@ gsr_status gsr_create(gsr_ctx** out, int hip_device) {
   if (e == hipSuccess) e = hipMemset(a.done, 0, sizeof(uint32_t));
   if (e == hipSuccess) e = hipEventCreateWithFlags(&a.total_ready, hipEventDisableTiming);
   if (e != hipSuccess) {
+    if (a.total_ready) (void)hipEventDestroy(a.total_ready);
     if (a.done) (void)hipFree(a.done);
     (void)hipHostFree(a.host_total);
     delete ctx;
@@ -149,10 +172,7 @@ void gsr_destroy(gsr_ctx* ctx) {
   if (!ctx) return;
   (void)hipSetDevice(ctx->device);
   Arena& a = ctx->arena;
-  for (DevBuf* b : {&a.keys[0], &a.keys[1], &a.vals[0], &a.vals[1], &a.counts, &a.offsets, &a.order, &a.order_alt,
-                    &a.order_vals, &a.order_vals_alt, &a.scan_part, &a.hist, &a.digit_tot, &a.ranges, &a.rects,
-                    &a.tile_order_ext, &a.tile_cost, &a.loss_part, &a.loss_maps, &a.grad_fixed})
-    release(*b);
+  for_each_buffer(a, [](DevBuf& b) { release(b); });
   if (a.host_total) (void)hipHostFree(a.host_total);
   if (a.done) (void)hipFree(a.done);
   if (a.total_ready) (void)hipEventDestroy(a.total_ready);
@@ -191,6 +211,10 @@ gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value) {
       if (value != GSR_BACKWARD_PER_PIXEL && value != GSR_BACKWARD_PER_SPLAT)
         return fail(ctx, GSR_EINVAL, "gsr_set_option: unknown backward scheme %lld", (long long)value);
       ctx->backward_scheme = int32_t(value);
+      return GSR_OK;
+    case GSR_OPT_ARENA_LIMIT:
+      if (value < 0) return fail(ctx, GSR_EINVAL, "gsr_set_option: the arena limit must be >= 0");
+      ctx->arena.limit = size_t(value);
       return GSR_OK;
     case GSR_OPT_KERNEL_TIMING:
       if (value < 0 || value > 4096)

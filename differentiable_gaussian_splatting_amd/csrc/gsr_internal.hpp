@@ -45,6 +45,7 @@ struct Arena {
   DevBuf loss_part;   // double [2 tiles] per-tile sums of the SSIM map and |x - y| (the loss)
   DevBuf loss_maps;   // float [9][H][W] the SSIM map's three derivatives per channel, between the loss's passes
   DevBuf grad_fixed;  // the deterministic backward's sums: uint64 [n][9][2] fixed point, then uint32 [n] flags
+  size_t limit = 0;                // GSR_OPT_ARENA_LIMIT: most bytes the buffers above may hold together (0: none)
   uint64_t* host_total = nullptr;  // pinned host word for the one pair-count readback
   uint32_t* done = nullptr;        // last-block-done counter of the count scan (0 between launches)
   hipEvent_t total_ready = nullptr;  // recorded after the readback is queued
@@ -82,7 +83,11 @@ gsr_status hip_fail(gsr_ctx* ctx, hipError_t e, const char* what);
 // Makes ctx's device current for this thread.
 gsr_status enter(gsr_ctx* ctx);
 
-// Grows `b` to at least `bytes` (grow-only; factor 1.5 over the previous size, floor 64 KiB).
+// Bytes held by the arena's buffers.
+size_t arena_bytes(const Arena& a);
+
+// Grows `b` to at least `bytes` (grow-only; factor 1.5 over the previous size, floor 64 KiB, neither beyond the
+// arena limit). GSR_ENOMEM when the allocation fails or the arena would pass its limit; `b` then keeps its size.
 gsr_status grow(gsr_ctx* ctx, DevBuf& b, size_t bytes);
 
 // Checks for launch errors after queuing kernels.

@@ -426,11 +426,11 @@ extern "C" gsr_status gsr_project_forward(gsr_ctx* ctx, void* stream, const gsr_
   if (!ctx) return GSR_EINVAL;
   if (!cam) return fail(ctx, GSR_EINVAL, "gsr_project_forward: null camera");
   if (n == 0) return GSR_OK;
+  if (uint64_t(n) * 48 >= (uint64_t(1) << 32)) return fail(ctx, GSR_EOVERFLOW, "gsr_project_forward: n * 48 >= 2^32");
   if (!means || !log_scales || !quats || !raw_opacities || !sh || !splats || !depths)
     return fail(ctx, GSR_EINVAL, "gsr_project_forward: null pointer");
   if (!aligned16(quats) || !aligned16(sh))
     return fail(ctx, GSR_EINVAL, "gsr_project_forward: quats and sh must be 16-byte aligned");
-  if (uint64_t(n) * 48 >= (uint64_t(1) << 32)) return fail(ctx, GSR_EOVERFLOW, "gsr_project_forward: n * 48 >= 2^32");
   gsr_status st = enter(ctx);
   if (st) return st;
   timing_mark(ctx, GSR_STAGE_PROJECT_FORWARD, static_cast<hipStream_t>(stream), false);
@@ -449,13 +449,13 @@ extern "C" gsr_status gsr_project_backward(gsr_ctx* ctx, void* stream, const gsr
   if (!ctx) return GSR_EINVAL;
   if (!cam) return fail(ctx, GSR_EINVAL, "gsr_project_backward: null camera");
   if (n == 0) return GSR_OK;
+  if (uint64_t(n) * 48 >= (uint64_t(1) << 32))
+    return fail(ctx, GSR_EOVERFLOW, "gsr_project_backward: n * 48 >= 2^32");
   if (!means || !log_scales || !quats || !raw_opacities || !sh || !splats_grad || !means_grad || !log_scales_grad ||
       !quats_grad || !raw_opacities_grad || !sh_grad)
     return fail(ctx, GSR_EINVAL, "gsr_project_backward: null pointer");
   if (!aligned16(quats) || !aligned16(sh) || !aligned16(quats_grad) || !aligned16(sh_grad))
     return fail(ctx, GSR_EINVAL, "gsr_project_backward: quats, sh and their gradients must be 16-byte aligned");
-  if (uint64_t(n) * 48 >= (uint64_t(1) << 32))
-    return fail(ctx, GSR_EOVERFLOW, "gsr_project_backward: n * 48 >= 2^32");
   gsr_status st = enter(ctx);
   if (st) return st;
   timing_mark(ctx, GSR_STAGE_PROJECT_BACKWARD, static_cast<hipStream_t>(stream), false);

@@ -210,7 +210,7 @@ def pmc_md(base: str, cmd: str, workload: str, first: int | None = None) -> str:
             if base_kernel(k) in KERNEL_SOURCES:  # one record per instance (k_adam<false> and <true> differ)
                 inst = short_name(k).replace(", ", ",").replace("unsigned int", "uint32")
                 record[inst] = {"hbm_bytes": hbm, "fetch_kib": fetch, "write_kib": write, "valu_issue": issue,
-                                "sources": source_hash(inst)}
+                                "valu_insts": v.get("SQ_INSTS_VALU"), "sources": source_hash(inst)}
         tf = (64 * (f.get("SQ_INSTS_VALU_FLOPS_FP32", 0) + f.get("SQ_INSTS_VALU_FLOPS_FP64", 0)) / (f["_ns"] * 1e3)
               if f.get("_ns") else None)
         lines.append(f"| `{k[:60]}` | " + " | ".join(vals) + f" | {'' if issue is None else f'{issue:.3f}'} | "
@@ -253,6 +253,17 @@ def valu_issue_for(kernel, md_path: str):
         return None
     k = rec["kernels"][kernel]
     return k.get("valu_issue") if k.get("sources") == source_hash(kernel) else None
+
+
+def valu_insts_for(kernel, md_path: str):
+    """Recorded VALU wave instructions per launch (SQ_INSTS_VALU) of the kernel instance, or None when unrecorded or
+    its sources changed since: with the kernel's live duration it gives the share of the chip's VALU issue slots
+    the kernel used, SQ_INSTS_VALU x 4 cycles / (1024 SIMDs x duration x 2.4 GHz)."""
+    rec = read_traffic(md_path)
+    if not rec or kernel not in rec.get("kernels", {}):
+        return None
+    k = rec["kernels"][kernel]
+    return k.get("valu_insts") if k.get("sources") == source_hash(kernel) else None
 
 
 def main(argv=None):

@@ -97,6 +97,11 @@ gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats);
 #define GSR_OPT_KERNEL_TIMING 6 /* 0 (default): off; n in 1..4096: every entry point records a pair of HIP events   */
                               /*   on its stream around its main kernel(s), in a ring of the last n launches per  */
                               /*   stage (read with gsr_kernel_times); setting the option clears the rings        */
+#define GSR_OPT_ARENA_LIMIT 8  /* 0 (default): none; b > 0: the arena's buffers together never hold more than b   */
+                              /*   bytes - a call that would grow it further fails with GSR_ENOMEM before queuing */
+                              /*   anything that needs the growth, and the arena keeps its buffers and contents   */
+                              /*   (a device-memory budget; also how failure handling is tested from the host).   */
+                              /*   Lowering it frees nothing already held.                                       */
 gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value);
 
 /* Stages timed by GSR_OPT_KERNEL_TIMING, each the kernels between its pair of events. */

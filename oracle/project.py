@@ -94,8 +94,10 @@ def quat_to_rotmat(q: torch.Tensor) -> torch.Tensor:
     return r.reshape(-1, 3, 3)
 
 
-def _forward(cam: Camera, means, log_scales, quats, raw_op, sh):
-    """Torch fp64 forward; returns (splats [N, 9], depths [N])."""
+def _forward(cam: Camera, means, log_scales, quats, raw_op, sh, clamp_flip=None):
+    """Torch fp64 forward; returns (splats [N, 9], depths [N]). clamp_flip: optional bool [N, 3]; where set, the
+    colour channel takes the other side of its clamp decision (kept when the unclamped value is <= 0, clamped to 0
+    when it is > 0), the reading a floating-point evaluation may take when that value lies within its rounding of 0."""
     R = torch.as_tensor(np.asarray(cam.R, np.float64))
     tv = torch.as_tensor(np.asarray(cam.tv, np.float64))
     t = means @ R.T + tv
@@ -123,7 +125,10 @@ def _forward(cam: Camera, means, log_scales, quats, raw_op, sh):
     d = v / torch.linalg.norm(v, dim=1, keepdim=True)
     Y = sh_basis(d)  # [N, 16]
     raw_rgb = torch.einsum("nk,nkc->nc", Y, sh.reshape(-1, 16, 3)) + 0.5
-    rgb = torch.where(raw_rgb > 0, raw_rgb, torch.zeros_like(raw_rgb))
+    lit = raw_rgb > 0
+    if clamp_flip is not None:
+        lit = lit ^ torch.as_tensor(np.asarray(clamp_flip, bool).reshape(-1, 3))
+    rgb = torch.where(lit, raw_rgb, torch.zeros_like(raw_rgb))
     o = 1.0 / (1.0 + torch.exp(-raw_op))
     rec = torch.stack([mx, my, a, b, c, rgb[:, 0], rgb[:, 1], rgb[:, 2], o], 1)
     rec = torch.where(valid[:, None], rec, torch.zeros_like(rec))
@@ -152,11 +157,22 @@ def project_forward(cam: Camera, means, log_scales, quats, raw_opacities, sh):
     return rec.numpy(), depth.numpy()
 
 
-def project_backward(cam: Camera, means, log_scales, quats, raw_opacities, sh, splats_grad):
+def unclamped_colour(cam: Camera, means, sh) -> np.ndarray:
+    """sum_k sh[k] Y_k(d) + 0.5 per channel [N, 3] (float64): the colour before its clamp at 0."""
+    with torch.no_grad():
+        m = torch.as_tensor(np.asarray(means, np.float64).reshape(-1, 3))
+        v = m - torch.as_tensor(cam.centre())
+        d = v / torch.linalg.norm(v, dim=1, keepdim=True)
+        shc = torch.as_tensor(np.asarray(sh, np.float64).reshape(-1, 16, 3))
+        return (torch.einsum("nk,nkc->nc", sh_basis(d), shc) + 0.5).numpy()
+
+
+def project_backward(cam: Camera, means, log_scales, quats, raw_opacities, sh, splats_grad, clamp_flip=None):
     """Gradients (float64) of the five parameter groups given dL/d(record) [N, 9]: the derivative of
-    sum(splats_grad * record) through project_forward."""
+    sum(splats_grad * record) through project_forward. clamp_flip as in _forward: the derivative with those colour
+    channels' clamp decisions taken the other way."""
     ps = _params64(means, log_scales, quats, raw_opacities, sh, grad=True)
-    rec, _ = _forward(cam, *ps)
+    rec, _ = _forward(cam, *ps, clamp_flip=clamp_flip)
     g = torch.as_tensor(np.asarray(splats_grad, np.float64).reshape(-1, 9))
     grads = torch.autograd.grad((rec * g).sum(), ps, allow_unused=True)
     out = []

@@ -69,3 +69,15 @@ def grads_close(gpu: np.ndarray, ref: np.ndarray, atol=1e-4, rtol=1e-4):
     i = int(np.argmax(ratio)) if ratio.size else 0
     worst = float(ratio.reshape(-1)[i]) if ratio.size else 0.0
     return worst <= 1.0, worst, np.unravel_index(i, ratio.shape) if ratio.size else None
+
+
+# Bar of the loss gradient (gsr_loss_l1_ssim's v_out) against the fp64 oracle, element by element: 2e-5 of the
+# element plus 2e-5 of the largest element (the scale of the 121-term sums, for elements that cancel). The fp32
+# kernel's worst measured error is about 6e-6 on these terms; a CPU test checks that the bar fails the oracle's own
+# gradient under a wrong window size, window width, loss weight or SSIM constant.
+LOSS_GRAD_REL = 2e-5
+
+
+def loss_grad_bar(ref: np.ndarray) -> np.ndarray:
+    ref = np.asarray(ref, np.float64)
+    return LOSS_GRAD_REL * np.abs(ref[..., :3]) + LOSS_GRAD_REL * np.abs(ref).max()

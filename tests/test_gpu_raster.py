@@ -438,8 +438,6 @@ def set_scheme(ctx, per_splat: bool):
 def test_per_splat_backward_matches_oracle(ctx, name, skip):
     """The per-splat loop order (a lane per splat, the block's pixels swept diagonally) meets the oracle bar."""
     from differentiable_gaussian_splatting_amd import gsr
-    if name == "raster410k" and not skip:
-        pytest.skip("the cull-free sweep of the 410k scene adds nothing the 84k case does not cover")
     banner(f"per-splat backward {name} skip={skip}")
     sc = scene(name)
     sp = dev(sc.splats)

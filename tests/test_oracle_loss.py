@@ -105,3 +105,30 @@ def test_gradient_matches_central_differences():
         xm[i, j, c] -= h
         fd = (ol.l1_ssim(xp, y)[0] - ol.l1_ssim(xm, y)[0]) / (2 * h)
         assert math.isclose(fd, g[i, j, c], rel_tol=1e-6, abs_tol=1e-12), ((i, j, c), fd, g[i, j, c])
+
+
+def test_gpu_bar_fails_planted_mistakes():
+    """The GPU test's gradient bar (gpuhelp.loss_grad_bar) is tight enough to catch a wrong reading: the oracle's
+    gradient under a 13- or 9-tap window, a window width of 1.4, a loss weight of 0.19 or C2 10 % too large
+    differs from the correct one by more than the bar, on the 64 x 64 image of the GPU test."""
+    import sys, os
+    sys.path.insert(0, os.path.dirname(__file__))
+    from gpuhelp import loss_grad_bar
+    rng = np.random.default_rng(64 * 1000 + 64)
+    h = w = 64
+    x = np.zeros((h, w, 4), np.float32)
+    x[..., :3] = rng.uniform(0, 1, (h, w, 3))
+    x[..., 3] = rng.uniform(0, 1, (h, w))
+    y = rng.uniform(0, 1, (h, w, 3)).astype(np.float32)
+    ref, _ = ol.l1_ssim_backward(x, y)
+    bar = loss_grad_bar(ref)
+    for kw in (dict(k=13), dict(k=9), dict(sigma=1.4), dict(lam=0.19)):
+        g, _ = ol.l1_ssim_backward(x, y, **kw)
+        assert (np.abs(g[..., :3] - ref[..., :3]) / bar).max() > 5.0, kw
+    c2 = ol.C2
+    try:
+        ol.C2 = c2 * 1.1
+        g, _ = ol.l1_ssim_backward(x, y)
+    finally:
+        ol.C2 = c2
+    assert (np.abs(g[..., :3] - ref[..., :3]) / bar).max() > 5.0

@@ -197,6 +197,37 @@ def test_backward_closed_forms():
     assert np.allclose(grads[4].reshape(n, 16, 3)[:, 0, :], want, rtol=1e-13, atol=1e-15)
 
 
+def test_flipped_clamp_decisions():
+    """clamp_flip takes a channel's clamp decision the other way: a lit channel becomes 0 with no SH gradient, a
+    clamped one takes its unclamped value, and its DC gradient is then g_c / (2 sqrt(pi)); unflagged channels and
+    the other groups' gradients from the colour are unchanged. The unclamped colour equals the record where lit."""
+    rng = np.random.default_rng(16)
+    n = 12
+    cam = cam_identity()
+    means = np.column_stack([rng.uniform(-1, 1, n), rng.uniform(-1, 1, n), rng.uniform(2, 5, n)])
+    sh = rng.normal(0, 1.0, (n, 48))
+    args = one(means, rng.normal(-2, 0.3, (n, 3)), rng.normal(size=(n, 4)), rng.normal(size=n), sh)
+    g = rng.normal(size=(n, 9))
+    rec, _ = op.project_forward(cam, *args)
+    raw = op.unclamped_colour(cam, means, sh)
+    lit = raw > 0
+    assert lit.any() and (~lit).any()
+    assert np.allclose(rec[:, 5:8], np.where(lit, raw, 0.0), rtol=1e-13, atol=1e-15)
+    flip = np.zeros((n, 3), bool)
+    flip[::2, 0] = True
+    flip[1::3, 2] = True
+    base = op.project_backward(cam, *args, g)
+    fl = op.project_backward(cam, *args, g, clamp_flip=flip)
+    lit_f = lit ^ flip
+    dc = 1 / (2 * math.sqrt(math.pi))
+    assert np.allclose(fl[4].reshape(n, 16, 3)[:, 0, :], np.where(lit_f, g[:, 5:8] * dc, 0.0), rtol=1e-13, atol=1e-15)
+    same = ~flip.any(axis=1)
+    for a, b in zip(base, fl):
+        assert np.array_equal(a.reshape(n, -1)[same], b.reshape(n, -1)[same])
+    for k in (1, 2, 3):  # log_scales, quats, raw opacity: the colour does not reach them
+        assert np.array_equal(base[k], fl[k])
+
+
 def test_covariance_uses_the_derivative_of_the_mean_projection():
     """EWA: Sigma' = J Sigma_cam J^T + 0.3 I with J the derivative of the pixel mean with respect to the camera-space
     position. J is taken here by central differences of the oracle's own projected means, so the closed form below
