@@ -157,6 +157,7 @@ gsr_status gsr_create(gsr_ctx** out, int hip_device) {
   e = hipMalloc(reinterpret_cast<void**>(&a.done), sizeof(uint32_t));
   if (e == hipSuccess) e = hipMemset(a.done, 0, sizeof(uint32_t));
   if (e == hipSuccess) e = hipEventCreateWithFlags(&a.total_ready, hipEventDisableTiming);
+  if (e == hipSuccess && noalloc_setup(ctx) != GSR_OK) e = hipErrorInvalidSymbol;
   if (e != hipSuccess) {
     if (a.total_ready) (void)hipEventDestroy(a.total_ready);
     if (a.done) (void)hipFree(a.done);

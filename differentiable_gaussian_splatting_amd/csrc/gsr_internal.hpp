@@ -66,6 +66,9 @@ struct gsr_ctx {
   uint64_t cost_tiles = 0;  // tile count of the grid tile_cost describes (0: none yet)
   const uint32_t* order_ranges = nullptr;  // the ranges tile_order_ext was last ranked for (by a forward)
   uint64_t order_tiles = 0;
+  // gsr_render_forward_noalloc's scratch on this context's device: the device address of a file-scope array
+  // (looked up once, when the context is created)
+  uint32_t* noalloc_scratch = nullptr;
   // GSR_OPT_KERNEL_TIMING: events [stage][slot][begin, end], a ring of timing_cap launches per stage
   std::vector<hipEvent_t> timing_events;
   uint32_t timing_cap = 0;
@@ -95,6 +98,10 @@ gsr_status check_launch(gsr_ctx* ctx, const char* what);
 
 // With kernel timing on, records the begin (end = false) or end event of the stage's current launch on `s`.
 void timing_mark(gsr_ctx* ctx, int stage, hipStream_t s, bool end);
+
+// Looks up the device address of gsr_render_forward_noalloc's scratch array on the current device into
+// ctx->noalloc_scratch (raster_fwd.hip; called by gsr_create with ctx's device current).
+gsr_status noalloc_setup(gsr_ctx* ctx);
 
 // Raster launch order (bin.hip): writes into `order` the tiles 0..num_tiles-1 with the longest pair lists first
 // (64 length classes; any order inside a class), on stream s. One workgroup.

@@ -109,7 +109,23 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
   if (lane == 0) tile_cost[4 * size_t(tile) + w] = walked;
 }
 
+// Scratch of gsr_render_forward_noalloc, one copy per device (it lives as long as the library is loaded):
+// [0, kNoAllocMaxTiles) the tiles' launch order, [kNoAllocMaxTiles, 5 kNoAllocMaxTiles) the four per-wave walk
+// counts of each tile from the last no-alloc forward on the device, which rank the next one's launch order. Host code
+// uses the address noalloc_setup looks up, never the array's name (which is a host-side stand-in).
+constexpr uint32_t kNoAllocMaxTiles = 65536;
+__device__ __align__(256) uint32_t scratch[5 * kNoAllocMaxTiles];
+
 }  // namespace
+
+gsr_status noalloc_setup(gsr_ctx* ctx) {
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) return hip_fail(ctx, e != hipSuccess ? e : hipErrorInvalidSymbol, "noalloc scratch");
+  ctx->noalloc_scratch = static_cast<uint32_t*>(p);
+  return GSR_OK;
+}
+
 }  // namespace gsr
 
 using namespace gsr;
@@ -145,4 +161,39 @@ extern "C" gsr_status gsr_render_forward(gsr_ctx* ctx, void* stream, const float
   if ((st = check_launch(ctx, "gsr_render_forward"))) return st;
   ctx->cost_tiles = num_tiles;
   return GSR_OK;
+}
+
+extern "C" gsr_status gsr_render_forward_noalloc(gsr_ctx* ctx, void* stream, const float* splats, uint32_t n,
+                                                 const gsr_bins* bins, uint32_t width, uint32_t height,
+                                                 float* out_rgba, float* final_T, uint32_t* last_contrib) {
+  if (!ctx || !bins) return GSR_EINVAL;
+  if (width == 0 || height == 0) return fail(ctx, GSR_EINVAL, "gsr_render_forward_noalloc: empty image");
+  const uint32_t tiles_x = (width + kTile - 1) / kTile, tiles_y = (height + kTile - 1) / kTile;
+  const uint64_t num_tiles = uint64_t(tiles_x) * tiles_y;
+  if (num_tiles > kNoAllocMaxTiles)
+    return fail(ctx, GSR_EINVAL, "gsr_render_forward_noalloc: %llu tiles exceed the scratch's %u (use "
+                "gsr_render_forward)", (unsigned long long)num_tiles, kNoAllocMaxTiles);
+  if (bins->tiles_x != tiles_x || bins->tiles_y != tiles_y)
+    return fail(ctx, GSR_EINVAL, "gsr_render_forward_noalloc: bins are for %ux%u tiles, image needs %ux%u",
+                bins->tiles_x, bins->tiles_y, tiles_x, tiles_y);
+  if (!bins->ranges || (bins->num_pairs && !bins->vals) || (n && !splats) || !out_rgba || !final_T || !last_contrib)
+    return fail(ctx, GSR_EINVAL, "gsr_render_forward_noalloc: null pointer");
+  if (reinterpret_cast<uintptr_t>(out_rgba) % 16)
+    return fail(ctx, GSR_EINVAL, "gsr_render_forward_noalloc: out_rgba must be 16-byte aligned");
+  if (!ctx->noalloc_scratch) return fail(ctx, GSR_EHIP, "gsr_render_forward_noalloc: no scratch on this device");
+  gsr_status st = enter(ctx);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* order = ctx->noalloc_scratch;
+  uint32_t* cost = ctx->noalloc_scratch + kNoAllocMaxTiles;
+  // Rank by the walk counts the previous no-alloc forward on this device left (a valid permutation whatever they
+  // hold; the order changes no result), then render; this forward leaves its own counts for the next one.
+  launch_tile_order(s, bins->ranges, cost, uint32_t(num_tiles), bins->num_pairs, order);
+  auto kernel = ctx->raster_skip ? k_forward<true> : k_forward<false>;
+  timing_mark(ctx, GSR_STAGE_FORWARD, s, false);
+  hipLaunchKernelGGL(kernel, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, s, splats, n, bins->vals,
+                     bins->ranges, bins->num_pairs, tiles_x, width, height, reinterpret_cast<float4*>(out_rgba),
+                     final_T, last_contrib, static_cast<const uint32_t*>(order), uint32_t(num_tiles), cost);
+  timing_mark(ctx, GSR_STAGE_FORWARD, s, true);
+  return check_launch(ctx, "gsr_render_forward_noalloc");
 }

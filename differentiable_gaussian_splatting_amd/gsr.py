@@ -74,6 +74,7 @@ SIGNATURES = {
     "gsr_radix_sort": (_I32, [_P, _P, _P, _P, _U64, _U32, _P, _P]),
     "gsr_radix_pass_count": (_U32, [_U64, _U32]),
     "gsr_render_forward": (_I32, [_P, _P, _P, _U32, ctypes.POINTER(gsr_bins), _U32, _U32, _P, _P, _P]),
+    "gsr_render_forward_noalloc": (_I32, [_P, _P, _P, _U32, ctypes.POINTER(gsr_bins), _U32, _U32, _P, _P, _P]),
     "gsr_render_backward": (_I32, [_P, _P, _P, _U32, ctypes.POINTER(gsr_bins), _U32, _U32, _P, _P, _P, _P, _P]),
     "gsr_adam_step": (_I32, [_P, _P, ctypes.POINTER(gsr_adam_group), _U32, _F, _F, _F, _F, _F]),
     "gsr_kernel_times": (_I32, [_P, _I32, _P, _U32, _P]),
@@ -269,6 +270,23 @@ def gsr_render_forward(ctx: Context, splats: torch.Tensor, bins: Bins, width: in
     ctx.check(load().gsr_render_forward(ctx.handle, _stream(stream), _ptr(splats), n, ctypes.byref(bins.raw), width,
                                         height, _ptr(out_rgba), _ptr(final_T), _ptr(last_contrib)),
               "gsr_render_forward")
+    return out_rgba, final_T, last_contrib
+
+
+def gsr_render_forward_noalloc(ctx: Context, splats: torch.Tensor, bins: Bins, width: int, height: int,
+                               out_rgba: torch.Tensor, final_T: torch.Tensor, last_contrib: torch.Tensor,
+                               stream=None):
+    """gsr_render_forward into caller-given outputs, with no device allocation by the library (its scratch is a
+    fixed per-device array; at most 65536 tiles)."""
+    dev = ctx.device
+    n = splats.numel() // 9
+    _need(splats, "splats", (torch.float32,), n * 9, dev)
+    _need(out_rgba, "out_rgba", (torch.float32,), height * width * 4, dev)
+    _need(final_T, "final_T", (torch.float32,), height * width, dev)
+    _need(last_contrib, "last_contrib", (torch.int32,), height * width, dev)
+    ctx.check(load().gsr_render_forward_noalloc(ctx.handle, _stream(stream), _ptr(splats), n, ctypes.byref(bins.raw),
+                                                width, height, _ptr(out_rgba), _ptr(final_T), _ptr(last_contrib)),
+              "gsr_render_forward_noalloc")
     return out_rgba, final_T, last_contrib
 
 

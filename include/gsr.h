@@ -196,6 +196,18 @@ gsr_status gsr_render_forward(gsr_ctx* ctx, void* stream, const float* splats, u
                               uint32_t width, uint32_t height, float* out_rgba, float* final_T,
                               uint32_t* last_contrib);
 
+/* gsr_render_forward for callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, hosts that forbid allocation. The same results, bit for bit, and the same arguments and errors; it never
+ * calls hipMalloc or hipFree (gsr_render_forward may grow the context's arena on its first call on a grid).
+ * Its scratch - the tiles' launch order and the per-tile walk counts that rank the next call's order, 20 bytes per
+ * tile - is a fixed array of 1.25 MiB in device memory, one copy per device, held until the process ends; images of
+ * more than 65536 tiles (4096 x 4096 pixels) are refused with GSR_EINVAL. Every call on a device shares that
+ * device's array and leaves its walk counts there for the next call (any contents give a valid order; the order
+ * changes no result): calls that overlap on one device, on different streams or host threads, race. */
+gsr_status gsr_render_forward_noalloc(gsr_ctx* ctx, void* stream, const float* splats, uint32_t n,
+                                      const gsr_bins* bins, uint32_t width, uint32_t height, float* out_rgba,
+                                      float* final_T, uint32_t* last_contrib);
+
 /* Backward rasterization: dL/d(splat record) for the loss whose gradient with respect to out_rgba.rgb is v_out.rgb
  * (v_out.w is ignored). Each pixel replays its forward decisions up to last_contrib and, for each splat it
  * composited, with w = alpha T, mine = rgb w, after = C_final - acc - mine (acc = colour composited in front):
