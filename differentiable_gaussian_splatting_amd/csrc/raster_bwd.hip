@@ -197,14 +197,62 @@ __global__ __launch_bounds__(kTilePixels) void k_fixed_to_float(FixedSums acc, f
   splats, n, vals, ranges, num_pairs, tiles_x, width, height, out_rgba, last_contrib, v_out, splats_grad, fixed, \
       tile_order, num_tiles
 
+// The nine per-splat sums of a wave, as moments. With (u, t) = pixel centre - tile centre (exact: multiples of 0.5
+// in [-7.5, 7.5]) and per lane v = dL/do = dL/dalpha G (0 where the lane did not composite or alpha is clamped) and
+// w = alpha T (0 where it did not composite), the sums taken are
+//   S0..S5 = sum v (1, u, t, u^2, u t, t^2),   C0..C2 = sum w (g_r, g_g, g_b),
+// accumulated per staged splat in LDS as [S0..S5, C0..C2] over the tile's four waves. At the batch's end the splat's
+// mean and conic gradients follow from them with xl = x - tile centre x, yl = y - tile centre y (dx = u - xl,
+// dy = t - yl): sum v dx = S1 - xl S0, sum v dx^2 = S3 - xl (S1 + sum v dx), and likewise; these are the sums of
+// v dx, v dy, v dx^2, v dx dy, v dy^2 the gradient is made of, each with the rounding of a plain fp32 sum of terms
+// of the same size. The moments are a contraction over the wave's 64 pixels of two per-lane values against fixed
+// per-pixel features (a dense 9 x 64 by 64 x 2 product per splat), which the matrix cores take: each compositing
+// splat's v and w go to a per-wave LDS buffer of columns, and every kChunk splats one chain of 16
+// v_mfma_f32_16x16x4f32 contracts them. Waves that fall back to the lane butterfly (non-finite upstream gradients,
+// the deterministic option, the skip-free A/B form) reduce the same nine values.
+constexpr uint32_t kBatch = 96;       // splats staged per batch (a wave and a half stage them): with the column
+                                      // buffers the workgroup's LDS stays under 26.6 KB, six per compute unit
+constexpr uint32_t kChunk = 8;        // splats per MFMA contraction
+constexpr uint32_t kColStride = 68;   // floats per buffer column: 64 pixels + 4, so the 16 columns' reads of one
+                                      // 16-byte group fall on 16 distinct groups of banks
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// Moments and colour sums of a staged splat -> its nine gradient values in record order (x, y, a, b, c, r, g, b, o):
+// dL/dmean = o (a Sx + b Sy, b Sx + c Sy) = 2 o (ha Sx + hb Sy, hb Sx + hc Sy), dL/d(a, b, c) = -o (Sxx / 2, Sxy,
+// Syy / 2), dL/d rgb = C, dL/do = S0.
+__device__ __forceinline__ void moments_to_grads(float* acc, const StagedSplat& sp, float tcx, float tcy) {
+  const float S0 = acc[0], S1 = acc[1], S2 = acc[2], S3 = acc[3], S4 = acc[4], S5 = acc[5];
+  const float c0 = acc[6], c1 = acc[7], c2 = acc[8];
+  float g0 = 0.0f, g1 = 0.0f, g2 = 0.0f, g3 = 0.0f, g4 = 0.0f;
+  if (S0 != 0.0f || S1 != 0.0f || S2 != 0.0f || S3 != 0.0f || S4 != 0.0f || S5 != 0.0f) {
+    const float xl = sp.x - tcx, yl = sp.y - tcy;
+    const float Sx = S1 - xl * S0;
+    const float Sy = S2 - yl * S0;
+    const float Sxx = S3 - xl * (S1 + Sx);
+    const float Sxy = (S4 - xl * S2) - yl * Sx;
+    const float Syy = S5 - yl * (S2 + Sy);
+    const float o2 = sp.o + sp.o;
+    g0 = o2 * __fmaf_rn(sp.ha, Sx, sp.hb * Sy);
+    g1 = o2 * __fmaf_rn(sp.hb, Sx, sp.hc * Sy);
+    g2 = (-0.5f * sp.o) * Sxx;
+    g3 = -sp.o * Sxy;
+    g4 = (-0.5f * sp.o) * Syy;
+  }
+  acc[0] = g0, acc[1] = g1, acc[2] = g2, acc[3] = g3, acc[4] = g4;
+  acc[5] = c0, acc[6] = c1, acc[7] = c2, acc[8] = S0;
+}
+
 template <bool kSkip, bool kDet>
 __device__ __forceinline__ void backward_tile(GSR_BACKWARD_PARAMS) {
   constexpr uint32_t kWaves = kTilePixels / kWave;
-  __shared__ StagedSplat s_sp[kTilePixels];
+  constexpr uint32_t kStageWaves = (kBatch + kWave - 1) / kWave;  // waves whose lanes stage a splat
+  constexpr bool kMfmaForm = kSkip && !kDet;  // the matrix-core reduction (the default configuration)
+  __shared__ StagedSplat s_sp[kBatch];
   __shared__ double s_exp2[64];  // 2^(j/32) table of the exact exponential
   constexpr uint32_t kAcc = kDet ? 2 : 1;  // accumulators: one per pair of waves, or one for all four
-  __shared__ float s_acc[kAcc][kTilePixels][kGrads];
-  __shared__ uint64_t s_mask[kWaves][kWaves];  // [reading wave][staging wave]
+  __shared__ float s_acc[kAcc][kBatch][kGrads];
+  __shared__ uint64_t s_mask[kWaves][kStageWaves];  // [reading wave][staging wave]
+  __shared__ __align__(16) float s_cols[kMfmaForm ? kWaves : 1][kMfmaForm ? 2 * kChunk : 1][kColStride];
   __shared__ uint32_t s_max_last;
   const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int slot_any = transpose_index(lane);               // all lanes take part in the exchanges
@@ -218,6 +266,9 @@ __device__ __forceinline__ void backward_tile(GSR_BACKWARD_PARAMS) {
   const uint32_t start = min(ranges[2 * tile], num_pairs);
   const uint32_t end = max(start, min(ranges[2 * tile + 1], num_pairs));
   const float cx = float(px) + 0.5f, cy = float(py) + 0.5f;
+  const float tcx = float(tx0) + 8.0f, tcy = float(ty0) + 8.0f;  // the tile's centre, origin of the moments
+  const float mu = cx - tcx, mt = cy - tcy;                        // exact
+  const float muu = mu * mu, mut = mu * mt, mtt = mt * mt;         // exact
 
   uint32_t last = 0;
   float Cr = 0.0f, Cg = 0.0f, Cb = 0.0f, gr = 0.0f, gg = 0.0f, gb = 0.0f;
@@ -234,51 +285,123 @@ __device__ __forceinline__ void backward_tile(GSR_BACKWARD_PARAMS) {
     gb = g.z;
   }
   // A lane that does not composite a splat has wgt = 0, so its colour terms wgt g are exact zeros unless its
-  // upstream gradient g is not finite; waves holding such a pixel select the zeros explicitly.
+  // upstream gradient g is not finite; waves holding such a pixel select the zeros explicitly (lane butterfly).
   const bool g_finite = __builtin_isfinite(gr) && __builtin_isfinite(gg) && __builtin_isfinite(gb);
   const bool wave_g_finite = __builtin_amdgcn_readfirstlane(uint32_t(__ballot(!g_finite) == 0)) != 0;
   if (tid == 0) s_max_last = 0;
-#pragma unroll
-  for (uint32_t a = 0; a < kAcc; ++a)
-#pragma unroll
-    for (uint32_t q = 0; q < kGrads; ++q) s_acc[a][tid][q] = 0.0f;
+  for (uint32_t i = tid; i < kAcc * kBatch * kGrads; i += kTilePixels) (&s_acc[0][0][0])[i] = 0.0f;
   // the wave's bound: the largest last contributor among its lanes
   uint32_t wave_last = last;
   for (uint32_t off = 32; off > 0; off >>= 1) wave_last = max(wave_last, uint32_t(__shfl_xor(int(wave_last), off)));
   wave_last = __builtin_amdgcn_readfirstlane(wave_last);
+  // Matrix operand A of the contraction, one register per instruction i = 0..15 of a chain: lane l holds feature
+  // m = l mod 16 of the wave's pixel q = 4 i + l / 16 (1, u, t, u^2, u t, t^2, g_r, g_g, g_b, then zeros). Rows 6..8
+  // multiply the v columns and rows 0..5 the w columns into sums nobody reads.
+  float amat[16];
+  if constexpr (kMfmaForm) {
+    const uint32_t m = lane & 15u;
+#pragma unroll
+    for (uint32_t i = 0; i < 16; ++i) {
+      const uint32_t q = 4 * i + (lane >> 4);
+      const float qu = float(lane_px(w, q)) + 0.5f - 8.0f, qt = float(lane_py(w, q)) + 0.5f - 8.0f;
+      const float qg0 = __shfl(gr, int(q)), qg1 = __shfl(gg, int(q)), qg2 = __shfl(gb, int(q));
+      float f = 0.0f;
+      f = m == 0 ? 1.0f : f;
+      f = m == 1 ? qu : f;
+      f = m == 2 ? qt : f;
+      f = m == 3 ? qu * qu : f;
+      f = m == 4 ? qu * qt : f;
+      f = m == 5 ? qt * qt : f;
+      f = m == 6 ? qg0 : f;
+      f = m == 7 ? qg1 : f;
+      f = m == 8 ? qg2 : f;
+      amat[i] = f;
+    }
+  }
   __syncthreads();
   if (lane == 0) atomicMax(&s_max_last, wave_last);
   __syncthreads();
   const uint32_t stop = start + s_max_last;
 
   // The batch loop, instantiated twice: kGuard selects the colour terms' explicit zeros (waves with a non-finite
-  // upstream gradient). Waves of one workgroup may run different instantiations; both pass the same barriers.
+  // upstream gradient), reduced by the lane butterfly. Waves of one workgroup may run different instantiations;
+  // both pass the same barriers and fill the accumulator with the same nine values.
   auto batches = [&](auto guard) {
   constexpr bool kGuard = decltype(guard)::value;
+  constexpr bool kMfma = kMfmaForm && !kGuard;
   float T = 1.0f, ar = 0.0f, ag = 0.0f, ab = 0.0f;
-  for (uint32_t b0 = start; b0 < stop; b0 += kTilePixels) {
+  // this lane's pixel's place in a column: instruction i = q / 4 reads k-slot q mod 4 (lanes 16 (q mod 4) ...)
+  float* const col_base = &s_cols[kMfma ? w : 0][0][0];
+  float* const my_cell = col_base + (((lane & 3u) << 4) | (lane >> 2));
+  uint32_t used = 0;  // splats in the current chunk (wave-uniform)
+  int slot_j = 0;     // lane s holds the batch slot of the chunk's splat s
+  // Contracts the chunk's `count` splats and adds their sums to the accumulator. All 64 lanes, uniform flow.
+  auto contract = [&](uint32_t count) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    // B operands: column n = lane mod 16, k-slot lane / 16: floats 16 (lane / 16) + i of the column, i = 0..15
+    const floatx4* src = reinterpret_cast<const floatx4*>(col_base + (lane & 15u) * kColStride + ((lane >> 4) << 4));
+    const floatx4 b0 = src[0], b1 = src[1], b2 = src[2], b3 = src[3];
+    floatx4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(amat[0], b0[0], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(amat[1], b0[1], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(amat[2], b0[2], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(amat[3], b0[3], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(amat[4], b1[0], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(amat[5], b1[1], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(amat[6], b1[2], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(amat[7], b1[3], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(amat[8], b2[0], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(amat[9], b2[1], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(amat[10], b2[2], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(amat[11], b2[3], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(amat[12], b3[0], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(amat[13], b3[1], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(amat[14], b3[2], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(amat[15], b3[3], d, 0, 0, 0);
+    // lane l holds rows 4 (l / 16) + r of column l mod 16: column 2 s carries v (rows 0..5 useful), column 2 s + 1
+    // carries w (rows 6..8 useful) of the chunk's splat s
+    const uint32_t n = lane & 15u, sl = n >> 1, kind = n & 1u, row0 = (lane >> 4) << 2;
+    const int jb = __shfl(slot_j, int(sl));
+    if (sl < count) {
+      float* acc = s_acc[0][jb];
+#pragma unroll
+      for (uint32_t r = 0; r < 4; ++r) {
+        const uint32_t row = row0 + r;
+        if (kind == 0 ? row < 6u : (row >= 6u && row < 9u)) atomicAdd(acc + row, d[r]);
+      }
+    }
+    // the next chunk's stores go to the columns these reads came from (same wave: LDS keeps its order)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  };
+  for (uint32_t b0 = start; b0 < stop; b0 += kBatch) {
     const uint32_t k = b0 + tid;
     uint32_t reach = 0;
-    if (k < stop) {
+    if (tid < kBatch && k < stop) {
       const StagedSplat st = stage_splat(splats, vals[k], n);
       s_sp[tid] = st;
       reach = kSkip ? reach_mask(st, float(tx0) + 0.5f, float(ty0) + 0.5f) : 0xFu;
     }
+    if (w < kStageWaves) {
 #pragma unroll
-    for (uint32_t q = 0; q < kWaves; ++q) {
-      const uint64_t bits = __ballot((reach >> q) & 1u);
-      if (lane == 0) s_mask[q][w] = bits;
+      for (uint32_t q = 0; q < kWaves; ++q) {
+        const uint64_t bits = __ballot((reach >> q) & 1u);
+        if (lane == 0) s_mask[q][w] = bits;
+      }
     }
     lds_barrier();
     const uint32_t rel0 = b0 - start;
-    for (uint32_t sw = 0; sw < kWaves; ++sw) {
+    for (uint32_t sw = 0; sw < kStageWaves; ++sw) {
       uint64_t m = uniform64(s_mask[w][sw]);
       while (m) {
         const uint32_t j = sw * kWave + uint32_t(__builtin_ctzll(m));
         m &= m - 1;
         if (rel0 + j >= wave_last) {
           m = 0;
-          sw = kWaves;  // past every lane's last contributor: done with this batch and the tile
+          sw = kStageWaves;  // past every lane's last contributor: done with this batch and the tile
           break;
         }
         // the whole record in three 16-byte reads from one address register
@@ -290,21 +413,13 @@ __device__ __forceinline__ void backward_tile(GSR_BACKWARD_PARAMS) {
         s.bl = q2.x, s.lr = q2.y, s.hb = q2.z, s.idx = __float_as_uint(q2.w);
         Eval e;  // dx and dy are set in every lane; G, oG and alpha only where the evaluation passed
         const bool contrib = evaluate<false>(s, cx, cy, e, s_exp2) & (rel0 + j < last);
-        if (kSkip && __builtin_amdgcn_ballot_w64(contrib) == 0) continue;  // no lane composited this splat
         // Every lane forms the terms; in a lane that did not composite the splat, alpha = 0 and v = 0 make them
-        // +-0 and leave T and acc as they are (the splat is binned, so its values are finite).
-        float d[kGrads];
+        // +-0 and leave T and acc as they are (the splat is binned, so its values are finite). A compositing lane
+        // has alpha >= 1/255, so the skip tests alpha itself (one compare into the mask).
         const float alpha = contrib ? e.alpha : 0.0f;
+        if (kSkip && __builtin_amdgcn_ballot_w64(alpha != 0.0f) == 0) continue;  // no lane composited this splat
         const float one_m = 1.0f - alpha;
         const float wgt = alpha * T;
-        d[5] = wgt * gr;
-        d[6] = wgt * gg;
-        d[7] = wgt * gb;
-        if constexpr (kGuard) {
-          d[5] = contrib ? d[5] : 0.0f;
-          d[6] = contrib ? d[6] : 0.0f;
-          d[7] = contrib ? d[7] : 0.0f;
-        }
         const float mr = s.r * wgt, mg = s.g * wgt, mb = s.bl * wgt;
         // dL/dalpha = T (g . rgb) - (g . after) / (1 - alpha), after = C_final - acc - mine, per channel as
         // (C_final - acc) - mine: after is a difference of nearly equal values that 1 / (1 - alpha) amplifies, so
@@ -313,48 +428,59 @@ __device__ __forceinline__ void backward_tile(GSR_BACKWARD_PARAMS) {
         const float g_after = __fmaf_rn(gb, (Cb - ab) - mb, __fmaf_rn(gg, (Cg - ag) - mg, gr * ((Cr - ar) - mr)));
         const float dl_da = __fmaf_rn(T, g_rgb, -g_after * __builtin_amdgcn_rcpf(one_m));
         // alpha depends on o and sigma only below the clamp: the opacity and geometry terms get a 0 / 1 factor.
-        // v = dL/do = dL/dalpha G. With u = -dL/dsigma = o v, the mean gradient is u (a dx + b dy, b dx + c dy)
-        // and the conic's is -u (dx dx / 2, dx dy, dy dy / 2); o, a, b, c are the splat's, so the sums taken are
-        // those of v dx, v dy, v dx dx, v dx dy, v dy dy, and the splat's factors are applied once per splat when
-        // the tile's sums are flushed.
+        // v = dL/do = dL/dalpha G; the geometry sums are moments of v (see moments_to_grads)
         const float v = (contrib && e.oG < kAlphaMax) ? dl_da * e.G : 0.0f;
-        const float vx = v * e.dx, vy = v * e.dy;
-        d[0] = vx;
-        d[1] = vy;
-        d[2] = vx * e.dx;
-        d[3] = vx * e.dy;
-        d[4] = vy * e.dy;
-        d[8] = v;
         ar = ar + mr;
         ag = ag + mg;
         ab = ab + mb;
         T = T * one_m;
-        // Wave totals of the 9 terms; nine lanes add them to the LDS accumulator (distinct addresses).
-        const float x = transpose_reduce(d, lane);
-        if (my_slot >= 0) atomicAdd(&s_acc[kDet ? w >> 1 : 0][j][my_slot], x);
+        if constexpr (kMfma) {
+          // this lane's v and w into the chunk's columns 2 used and 2 used + 1
+          my_cell[(2 * used) * kColStride] = v;
+          my_cell[(2 * used + 1) * kColStride] = wgt;
+          asm volatile("v_writelane_b32 %0, %1, m0" : "+v"(slot_j) : "s"(j), "{m0}"(used));
+          if (++used == kChunk) {
+            contract(kChunk);
+            used = 0;
+          }
+        } else {
+          float d[kGrads];
+          d[0] = v;
+          d[1] = v * mu;
+          d[2] = v * mt;
+          d[3] = v * muu;
+          d[4] = v * mut;
+          d[5] = v * mtt;
+          d[6] = wgt * gr;
+          d[7] = wgt * gg;
+          d[8] = wgt * gb;
+          if constexpr (kGuard) {
+            d[6] = contrib ? d[6] : 0.0f;
+            d[7] = contrib ? d[7] : 0.0f;
+            d[8] = contrib ? d[8] : 0.0f;
+          }
+          // Wave totals of the 9 terms; nine lanes add them to the LDS accumulator (distinct addresses).
+          const float x = transpose_reduce(d, lane);
+          if (my_slot >= 0) atomicAdd(&s_acc[kDet ? w >> 1 : 0][j][my_slot], x);
+        }
+      }
+    }
+    if constexpr (kMfma) {
+      if (used) {
+        contract(used);
+        used = 0;
       }
     }
     lds_barrier();
-    // Per staged splat, its geometry sums S0..S4 (of v dx, v dy, v dx dx, v dx dy, v dy dy) become
-    // dL/dmean = o (a S0 + b S1, b S0 + c S1), formed as 2 o (ha S0 + hb S1, hb S0 + hc S1), and
-    // dL/d(a, b, c) = -o (S2 / 2, S3, S4 / 2). A splat no pixel composited keeps its zeros whatever its values.
-    const uint32_t staged = min(kTilePixels, stop - b0);
+    // Per staged splat, its moments become its nine gradient values (moments_to_grads).
+    const uint32_t staged = min(kBatch, stop - b0);
     if (tid < staged) {
       float* acc = s_acc[0][tid];
       if constexpr (kDet) {
 #pragma unroll
         for (uint32_t q = 0; q < kGrads; ++q) acc[q] += s_acc[1][tid][q];
       }
-      const float s0 = acc[0], s1 = acc[1], s2 = acc[2], s3 = acc[3], s4 = acc[4];
-      if (s0 != 0.0f || s1 != 0.0f || s2 != 0.0f || s3 != 0.0f || s4 != 0.0f) {
-        const StagedSplat& sp = s_sp[tid];
-        const float o2 = sp.o + sp.o;
-        acc[0] = o2 * __fmaf_rn(sp.ha, s0, sp.hb * s1);
-        acc[1] = o2 * __fmaf_rn(sp.hb, s0, sp.hc * s1);
-        acc[2] = (-0.5f * sp.o) * s2;
-        acc[3] = -sp.o * s3;
-        acc[4] = (-0.5f * sp.o) * s4;
-      }
+      moments_to_grads(acc, s_sp[tid], tcx, tcy);
     }
     lds_barrier();
     // Flush: the batch's accumulator is read in its [slot][value] order, so the 64 lanes of an atomic instruction
@@ -413,6 +539,7 @@ __device__ __forceinline__ void backward_splat_tile(GSR_BACKWARD_PARAMS) {
   const uint32_t tx0 = (tile % tiles_x) * kTile, ty0 = (tile / tiles_x) * kTile;
   const uint32_t start = min(ranges[2 * tile], num_pairs);
   const uint32_t end = max(start, min(ranges[2 * tile + 1], num_pairs));
+  const float tcx = float(tx0) + 8.0f, tcy = float(ty0) + 8.0f;  // the tile's centre, origin of the moments
   {
     // lane l sets up pixel l of the wave's block
     const uint32_t px = tx0 + lane_px(w, lane), py = ty0 + lane_py(w, lane);
@@ -498,16 +625,18 @@ __device__ __forceinline__ void backward_splat_tile(GSR_BACKWARD_PARAMS) {
           __fmaf_rn(pg.z, (pc.z - ab) - mb, __fmaf_rn(pg.y, (pc.y - ag) - mg, pg.x * ((pc.x - ar) - mr)));
       const float dl_da = __fmaf_rn(T, g_rgb, -g_after * __builtin_amdgcn_rcpf(one_m));
       const float v = (contrib && e.oG < kAlphaMax) ? dl_da * e.G : 0.0f;
-      const float vx = v * e.dx, vy = v * e.dy;
-      acc[0] += vx;
-      acc[1] += vy;
-      acc[2] += vx * e.dx;
-      acc[3] += vx * e.dy;
-      acc[4] += vy * e.dy;
-      acc[5] += d5;
-      acc[6] += d6;
-      acc[7] += d7;
-      acc[8] += v;
+      // the per-pixel kernel's moments (pixel centre relative to the tile centre, exact), so that a sum of one
+      // term gives that kernel's bits
+      const float mu = cx - tcx, mt = cy - tcy;
+      acc[0] += v;
+      acc[1] += v * mu;
+      acc[2] += v * mt;
+      acc[3] += v * (mu * mu);
+      acc[4] += v * (mu * mt);
+      acc[5] += v * (mt * mt);
+      acc[6] += d5;
+      acc[7] += d6;
+      acc[8] += d7;
       oT = T * one_m;
       oar = ar + mr;
       oag = ag + mg;
@@ -516,13 +645,7 @@ __device__ __forceinline__ void backward_splat_tile(GSR_BACKWARD_PARAMS) {
     }
     // the splat's factors, as at the per-pixel kernel's flush, then its nine totals
     if (mine && s.idx != 0xFFFFFFFFu) {
-      const float s0 = acc[0], s1 = acc[1], s2 = acc[2], s3 = acc[3], s4 = acc[4];
-      const float o2 = s.o + s.o;
-      acc[0] = o2 * __fmaf_rn(s.ha, s0, s.hb * s1);
-      acc[1] = o2 * __fmaf_rn(s.hb, s0, s.hc * s1);
-      acc[2] = (-0.5f * s.o) * s2;
-      acc[3] = -s.o * s3;
-      acc[4] = (-0.5f * s.o) * s4;
+      moments_to_grads(acc, s, tcx, tcy);
 #pragma unroll
       for (uint32_t q = 0; q < kGrads; ++q) {
         if (acc[q] == 0.0f) continue;
@@ -551,7 +674,7 @@ __global__ __launch_bounds__(kTilePixels) void k_backward_splat(GSR_BACKWARD_PAR
 
 // One block per 16x16 tile; the deterministic form under a name of its own, so that profiles keep the two apart.
 template <bool kSkip>
-__global__ __launch_bounds__(kTilePixels) __attribute__((amdgpu_waves_per_eu(7))) void k_backward(GSR_BACKWARD_PARAMS) {
+__global__ __launch_bounds__(kTilePixels) __attribute__((amdgpu_waves_per_eu(6))) void k_backward(GSR_BACKWARD_PARAMS) {
   backward_tile<kSkip, false>(GSR_BACKWARD_ARGS);
 }
 

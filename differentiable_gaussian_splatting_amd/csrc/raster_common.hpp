@@ -314,7 +314,13 @@ __device__ __forceinline__ bool evaluate(const StagedSplat& s, float cx, float c
     e.G = g;
     e.oG = og;
   }
-  e.alpha = (e.oG < kAlphaMax) ? e.oG : kAlphaMax;
+  if constexpr (kExactValues) {
+    e.alpha = (e.oG < kAlphaMax) ? e.oG : kAlphaMax;
+  } else {
+    // the same value as the select (o G is a product of finite values, never NaN), in one instruction: the
+    // compiler's min would first canonicalise its operand
+    asm("v_min_f32 %0, %1, %2" : "=v"(e.alpha) : "v"(e.oG), "v"(kAlphaMax));
+  }
   return in_range & !(e.alpha < kAlphaMin);
 }
 

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
   const float cx = float(px) + 0.5f, cy = float(py) + 0.5f;
 
   float T = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f;
-  uint32_t last = 0;
+  uint32_t last = 0, last_stop = 0;
   uint32_t walked = 0;  // splats this wave evaluated (wave-uniform): the tile's cost for the launch order
   // A lane whose pixel has stopped (or lies outside the image) moves its centre to +inf: sigma is then inf or NaN
   // for every later splat, which evaluate() rejects, so finished lanes need no test of their own.
@@ -62,6 +62,7 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
     }
     __syncthreads();
     if (__ballot(cxe != kFar) == 0) continue;  // this wave is finished; keep joining the barriers
+    const uint32_t pos0 = b0 - start + 1;
     for (uint32_t sw = 0; sw < kWaves; ++sw) {
       uint64_t m = uniform64(s_mask[w][sw]);
       while (m) {
@@ -80,18 +81,28 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
         ++walked;
         Eval e;
         if (evaluate<true>(s, cxe, cy, e, s_exp2)) {
-          // Without branches: a pixel that stops here (this splat is not composited) adds r 0 = +-0 to its
-          // colours, which leaves them as they are (a sum that starts at +0 is never -0, and binned colours are
-          // finite), and keeps T and last.
-          const float next_T = T * (1.0f - e.alpha);
-          const bool stop = next_T < kTStop;
-          const float wgt = stop ? 0.0f : e.alpha * T;
-          cr = cr + s.r * wgt;
-          cg = cg + s.g * wgt;
-          cb = cb + s.bl * wgt;
-          T = stop ? T : next_T;
-          last = stop ? last : b0 - start + j + 1;
-          cxe = stop ? kFar : cxe;
+          float alpha = e.alpha;
+          float next_T = T * (1.0f - alpha);
+          // A pixel that would fall below the stop threshold here does not composite this splat and stops. Rare
+          // (once per pixel), so behind a wave test: such a lane keeps its last contributor aside and takes
+          // alpha = 0, which makes the update below leave T and its colours as they are (r 0 = +-0 added to a sum
+          // that starts at +0 and never becomes -0; binned colours are finite), and its centre moves to +inf.
+          if (__builtin_amdgcn_ballot_w64(next_T < kTStop) != 0) {
+            const bool stop = next_T < kTStop;
+            last_stop = stop ? last : last_stop;
+            alpha = stop ? 0.0f : alpha;
+            next_T = stop ? T : next_T;
+            cxe = stop ? kFar : cxe;
+          }
+          // The colour sums use a fused multiply-add (one rounding per splat instead of two): the image stays
+          // within 2e-7 of the two-rounding sum, far inside its bar, and no decision depends on it (T and the
+          // stop test keep their plain fp32 operations).
+          const float wgt = alpha * T;
+          cr = __fmaf_rn(s.r, wgt, cr);
+          cg = __fmaf_rn(s.g, wgt, cg);
+          cb = __fmaf_rn(s.bl, wgt, cb);
+          T = next_T;
+          last = pos0 + j;
         }
         if (__ballot(cxe != kFar) == 0) {
           sw = kWaves;
@@ -100,6 +111,8 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
       }
     }
   }
+  // a stopped pixel's last contributor is the one kept aside (the update at its stopping splat overwrote it)
+  if (inside && cxe == kFar) last = last_stop;
   if (inside) {
     const size_t p = size_t(py) * width + px;
     out_rgba[p] = make_float4(cr, cg, cb, 1.0f - T);
