@@ -75,6 +75,7 @@ def parse():
     ap.add_argument("--repeats", type=int, default=3, help="timed repeats of K steps (median and spread reported)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bin-stress", action="store_true", help="skip the binning leg on the 1M-splat scene")
+    ap.add_argument("--no-views", action="store_true", help="skip the changing-views leg")
     ap.add_argument("--calib-copy", action="store_true")
     return ap.parse_args()
 
@@ -387,6 +388,8 @@ def main():
     result["projection"] = bench_projection(args, ctx, gsr, scenes, sc, hp=hp, bc=bc)
     if not args.no_bin_stress:
         result["bin_stress"] = bench_bin_stress(args, ctx, gsr, scenes, torch, np)
+    if not args.no_views:
+        result["changing_views"] = bench_changing_views(args, ctx, gsr, scenes, torch, np)
     print(json.dumps(result), flush=True)
     ctx.close()
 
@@ -494,6 +497,64 @@ def bench_bin_stress(args, ctx, gsr, scenes, torch, np):
     k64 = out["key64"]["sort_roofline"]["work_per_launch"]
     out["pages_target_ms_at_70pct"] = k64 / (0.7 * HBM_PEAK_GBS * 1e9) * 1e3
     return out
+
+
+def bench_changing_views(args, ctx, gsr, scenes, torch, np):
+    """The raster kernels when every step sees a new view, as in training: gauss410k projected by a camera that
+    turns 1 degree about its vertical axis per step (about 14 px, most of a tile, of image motion), then bin,
+    forward and backward. The default launch order ranks the tiles by the walk counts of the previous forward -
+    here a different view - so this leg times the forward and backward kernels (library events, K steps per
+    repeat, median of the repeats) under each order: cost (default), list length, tile index."""
+    g3 = scenes.make_gaussians("gauss410k")
+    W, H = g3.width, g3.height
+    ps = [torch.from_numpy(a).cuda() for a in (g3.means, g3.log_scales, g3.quats, g3.raw_opacities, g3.sh)]
+    v_out = torch.from_numpy(np.random.default_rng(31).normal(0.0, 0.01, (H, W, 4)).astype(np.float32)).cuda()
+    cams = []
+    for k in range(args.steps + 1):
+        a = np.deg2rad(1.0 * k)
+        Ry = np.array([[np.cos(a), 0.0, np.sin(a)], [0.0, 1.0, 0.0], [-np.sin(a), 0.0, np.cos(a)]])
+        R = Ry @ np.asarray(g3.camera["R"], np.float64)
+        cams.append(gsr.camera(R, g3.camera["tv"], g3.camera["fx"], g3.camera["fy"], g3.camera["cx"],
+                               g3.camera["cy"], g3.camera["near"]))
+    n = g3.spec.n
+    sp = torch.empty((n, 9), dtype=torch.float32, device="cuda")
+    dp = torch.empty(n, dtype=torch.float32, device="cuda")
+    out = torch.empty((H, W, 4), dtype=torch.float32, device="cuda")
+    ft = torch.empty((H, W), dtype=torch.float32, device="cuda")
+    lc = torch.empty((H, W), dtype=torch.int32, device="cuda")
+    grad = torch.empty((n, 9), dtype=torch.float32, device="cuda")
+    res = {"workload": f"gauss410k: {n} 3D Gaussians, {W}x{H}, camera turning 1 degree per step",
+           "pairs_first_last": None}
+    pairs = []
+    for name, order in (("cost", gsr.GSR_ORDER_COST), ("length", gsr.GSR_ORDER_LENGTH),
+                        ("index", gsr.GSR_ORDER_NONE)):
+        gsr.gsr_set_option(ctx, gsr.GSR_OPT_TILE_ORDER, order)
+        reps = {"forward": [], "backward": []}
+        for _ in range(args.repeats):
+            # a forward on the first view, so that the first timed step ranks by a previous view's counts
+            gsr.gsr_project_forward(ctx, cams[0], *ps, splats=sp, depths=dp)
+            b = gsr.gsr_bin(ctx, sp, dp, W, H)
+            gsr.gsr_render_forward(ctx, sp, b, W, H, out, ft, lc)
+            torch.cuda.synchronize()
+            gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, args.steps)
+            for k in range(1, args.steps + 1):
+                gsr.gsr_project_forward(ctx, cams[k], *ps, splats=sp, depths=dp)
+                b = gsr.gsr_bin(ctx, sp, dp, W, H)
+                gsr.gsr_render_forward(ctx, sp, b, W, H, out, ft, lc)
+                gsr.gsr_render_backward(ctx, sp, b, W, H, out, ft, lc, v_out, grad)
+                if name == "cost" and not pairs:
+                    pairs.append(b.num_pairs)
+            torch.cuda.synchronize()
+            pairs.append(b.num_pairs)
+            reps["forward"].append(float(np.mean(gsr.gsr_kernel_times(ctx, gsr.GSR_STAGE_FORWARD))))
+            reps["backward"].append(float(np.mean(gsr.gsr_kernel_times(ctx, gsr.GSR_STAGE_BACKWARD))))
+            gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, 0)
+        res[name] = {k: float(np.median(v)) for k, v in reps.items()}
+        res[name]["sigma"] = {k: float(np.std(v)) for k, v in reps.items()}
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_TILE_ORDER, gsr.GSR_ORDER_COST)
+    res["pairs_first_last"] = [pairs[0], pairs[-1]]
+    res["gain_of_cost_order_vs_length"] = {k: res["length"][k] / res["cost"][k] for k in ("forward", "backward")}
+    return res
 
 
 def bench_deterministic_backward(args, ctx, gsr, torch, np, stream, splats, b, W, H, out_rgba, final_T, last_contrib,

@@ -477,10 +477,15 @@ constexpr uint32_t kOrderThreads = 1024, kOrderClasses = 64;
 
 __global__ __launch_bounds__(kOrderThreads) void k_tile_order(const uint32_t* __restrict__ ranges,
                                                               const uint32_t* __restrict__ cost, uint32_t num_tiles,
-                                                              uint32_t num_pairs, uint32_t* __restrict__ order) {
+                                                              uint32_t num_pairs, uint32_t* __restrict__ order,
+                                                              bool identity) {
   __shared__ uint32_t s_count[kOrderClasses], s_base[kOrderClasses];
   __shared__ uint32_t s_max;
   const uint32_t tid = threadIdx.x;
+  if (identity) {
+    for (uint32_t t = tid; t < num_tiles; t += kOrderThreads) order[t] = t;
+    return;
+  }
   if (tid < kOrderClasses) s_count[tid] = 0;
   if (tid == 0) s_max = 0;
   __syncthreads();
@@ -525,9 +530,10 @@ uint32_t grid_for(uint64_t items, uint32_t per_block) { return uint32_t((items +
 namespace gsr {
 
 void launch_tile_order(hipStream_t s, const uint32_t* ranges, const uint32_t* cost, uint32_t num_tiles,
-                       uint32_t num_pairs, uint32_t* order) {
+                       uint32_t num_pairs, uint32_t* order, bool identity) {
   if (num_tiles)
-    hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(kOrderThreads), 0, s, ranges, cost, num_tiles, num_pairs, order);
+    hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(kOrderThreads), 0, s, ranges, cost, num_tiles, num_pairs, order,
+                       identity);
 }
 
 const uint32_t* raster_tile_order(gsr_ctx* ctx, hipStream_t s, const gsr_bins* bins, bool backward,
@@ -539,8 +545,10 @@ const uint32_t* raster_tile_order(gsr_ctx* ctx, hipStream_t s, const gsr_bins* b
     return static_cast<const uint32_t*>(a.tile_order_ext.ptr);
   if ((*st = grow(ctx, a.tile_order_ext, size_t(num_tiles) * 4))) return nullptr;
   uint32_t* order = static_cast<uint32_t*>(a.tile_order_ext.ptr);
-  const uint32_t* cost = ctx->cost_tiles == num_tiles ? static_cast<const uint32_t*>(a.tile_cost.ptr) : nullptr;
-  launch_tile_order(s, bins->ranges, cost, uint32_t(num_tiles), bins->num_pairs, order);
+  const uint32_t* cost = ctx->tile_order == GSR_ORDER_COST && ctx->cost_tiles == num_tiles
+                             ? static_cast<const uint32_t*>(a.tile_cost.ptr) : nullptr;
+  launch_tile_order(s, bins->ranges, cost, uint32_t(num_tiles), bins->num_pairs, order,
+                    ctx->tile_order == GSR_ORDER_NONE);
   ctx->order_ranges = backward ? nullptr : bins->ranges;
   ctx->order_tiles = num_tiles;
   return order;

@@ -213,6 +213,12 @@ gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value) {
         return fail(ctx, GSR_EINVAL, "gsr_set_option: unknown backward scheme %lld", (long long)value);
       ctx->backward_scheme = int32_t(value);
       return GSR_OK;
+    case GSR_OPT_TILE_ORDER:
+      if (value != GSR_ORDER_COST && value != GSR_ORDER_LENGTH && value != GSR_ORDER_NONE)
+        return fail(ctx, GSR_EINVAL, "gsr_set_option: unknown tile order %lld", (long long)value);
+      ctx->tile_order = int32_t(value);
+      ctx->order_ranges = nullptr;  // rank again at the next raster launch
+      return GSR_OK;
     case GSR_OPT_ARENA_LIMIT:
       if (value < 0) return fail(ctx, GSR_EINVAL, "gsr_set_option: the arena limit must be >= 0");
       ctx->arena.limit = size_t(value);

@@ -63,6 +63,7 @@ struct gsr_ctx {
   bool raster_skip = true;  // per-wave cull and the backward's all-lanes-rejected skip
   bool deterministic = false;  // backward sums independent of scheduling (fixed-point atomics)
   int32_t backward_scheme = GSR_BACKWARD_PER_PIXEL;
+  int32_t tile_order = GSR_ORDER_COST;  // how raster_tile_order ranks the tiles
   uint64_t cost_tiles = 0;  // tile count of the grid tile_cost describes (0: none yet)
   const uint32_t* order_ranges = nullptr;  // the ranges tile_order_ext was last ranked for (by a forward)
   uint64_t order_tiles = 0;
@@ -107,8 +108,9 @@ gsr_status noalloc_setup(gsr_ctx* ctx);
 // (64 length classes; any order inside a class), on stream s. One workgroup.
 // With `cost` ([4 tiles], per-wavefront walk lengths of an earlier forward on the same grid), tiles are ranked by
 // their summed cost instead of their list length.
+// With `identity`, order[t] = t (no ranking).
 void launch_tile_order(hipStream_t s, const uint32_t* ranges, const uint32_t* cost, uint32_t num_tiles,
-                       uint32_t num_pairs, uint32_t* order);
+                       uint32_t num_pairs, uint32_t* order, bool identity = false);
 // The launch order of the raster kernels for `bins`, computed now into the arena: by the last forward's measured
 // per-tile cost when it ran on the same tile grid, else by list length. Results never depend on the order; it only
 // lets the slowest tiles start first. Null on failure (the error is recorded on ctx).

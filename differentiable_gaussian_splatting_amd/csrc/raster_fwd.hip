@@ -201,7 +201,8 @@ extern "C" gsr_status gsr_render_forward_noalloc(gsr_ctx* ctx, void* stream, con
   uint32_t* cost = ctx->noalloc_scratch + kNoAllocMaxTiles;
   // Rank by the walk counts the previous no-alloc forward on this device left (a valid permutation whatever they
   // hold; the order changes no result), then render; this forward leaves its own counts for the next one.
-  launch_tile_order(s, bins->ranges, cost, uint32_t(num_tiles), bins->num_pairs, order);
+  launch_tile_order(s, bins->ranges, ctx->tile_order == GSR_ORDER_COST ? cost : nullptr, uint32_t(num_tiles),
+                    bins->num_pairs, order, ctx->tile_order == GSR_ORDER_NONE);
   auto kernel = ctx->raster_skip ? k_forward<true> : k_forward<false>;
   timing_mark(ctx, GSR_STAGE_FORWARD, s, false);
   hipLaunchKernelGGL(kernel, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, s, splats, n, bins->vals,

@@ -97,6 +97,12 @@ gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats);
 #define GSR_OPT_KERNEL_TIMING 6 /* 0 (default): off; n in 1..4096: every entry point records a pair of HIP events   */
                               /*   on its stream around its main kernel(s), in a ring of the last n launches per  */
                               /*   stage (read with gsr_kernel_times); setting the option clears the rings        */
+#define GSR_OPT_TILE_ORDER 9    /* the order in which the raster kernels start their tiles (results never depend on */
+#define GSR_ORDER_COST 0        /*   it): default: slowest first by the per-wavefront walk counts of the last       */
+                                /*   forward on the same tile grid (a stand-in for this view's costs; list length  */
+                                /*   before any forward);                                                          */
+#define GSR_ORDER_LENGTH 1      /*   longest tile list first;                                                      */
+#define GSR_ORDER_NONE 2        /*   tile index order                                                              */
 #define GSR_OPT_ARENA_LIMIT 8  /* 0 (default): none; b > 0: the arena's buffers together never hold more than b   */
                               /*   bytes - a call that would grow it further fails with GSR_ENOMEM before queuing */
                               /*   anything that needs the growth, and the arena keeps its buffers and contents   */

@@ -224,6 +224,31 @@ def test_skips_change_no_result(ctx, name):
         assert np.array_equal(ga, gb)
 
 
+def test_tile_launch_order_changes_no_result(ctx):
+    """The raster kernels start their tiles by the previous forward's walk counts, by list length or in index order
+    (GSR_OPT_TILE_ORDER): the forward is bit-identical under all three, and so is the deterministic backward."""
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("tile launch order raster84k")
+    sc = scene("raster84k")
+    sp = dev(sc.splats)
+    bins = gsr.gsr_bin(ctx, sp, dev(sc.depths), sc.width, sc.height)
+    res = []
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_DETERMINISTIC, 1)
+    try:
+        for order in (gsr.GSR_ORDER_COST, gsr.GSR_ORDER_LENGTH, gsr.GSR_ORDER_NONE):
+            gsr.gsr_set_option(ctx, gsr.GSR_OPT_TILE_ORDER, order)
+            out, ft, lc = run_forward(ctx, sp, bins, sc.width, sc.height)
+            res.append((host(out), host(ft), host(lc), host(run_backward(ctx, sc, bins, out, ft, lc))))
+    finally:
+        gsr.gsr_set_option(ctx, gsr.GSR_OPT_TILE_ORDER, gsr.GSR_ORDER_COST)
+        gsr.gsr_set_option(ctx, gsr.GSR_OPT_DETERMINISTIC, 0)
+    for r in res[1:]:
+        for a, b in zip(res[0], r):
+            assert a.tobytes() == b.tobytes()
+    lib = gsr.load()
+    assert lib.gsr_set_option(ctx.handle, gsr.GSR_OPT_TILE_ORDER, 3) == gsr.GSR_EINVAL
+
+
 def test_cull_keeps_every_pixel_of_thin_tilted_splats(ctx):
     """The block cull's separating axes (box and diagonals) against splats built to sit at its edges: needles up
     to 300 times longer than wide (condition numbers up to about 1e5, where the cull gives up) at every angle,
