@@ -76,6 +76,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bin-stress", action="store_true", help="skip the binning leg on the 1M-splat scene")
     ap.add_argument("--no-views", action="store_true", help="skip the changing-views leg")
+    ap.add_argument("--bin-stress-only", action="store_true",
+                    help="run only the binning leg on the 1M-splat scene (for its counter profile)")
     ap.add_argument("--calib-copy", action="store_true")
     return ap.parse_args()
 
@@ -166,6 +168,12 @@ def main():
     import torch
 
     from differentiable_gaussian_splatting_amd import gsr, scenes
+
+    if args.bin_stress_only:
+        ctx = gsr.Context(0)
+        print(json.dumps({"bin_stress": bench_bin_stress(args, ctx, gsr, scenes, torch, np)}), flush=True)
+        ctx.close()
+        return
 
     print(f"[bench] workload {args.workload}: generating inputs", file=sys.stderr, flush=True)
     sc = scenes.make_scene(args.workload)
@@ -360,6 +368,10 @@ def main():
                 r["valu_insts_per_launch"] = insts
                 r["valu_issue_frac"] = (None if insts is None else
                                         insts / (r["kernel_ms"] * 1e-3 * VALU_ISSUE_PER_S))
+                # SIMD cycles in fp32 MFMA (the backward's reduction), which do not overlap VALU issue on a SIMD
+                mcyc = profiling.mfma_busy_for(profiling.STAGE_KERNEL[k], traffic_md)
+                r["mfma_busy_frac"] = (None if mcyc is None else
+                                       mcyc / (r["kernel_ms"] * 1e-3 * 1024 * 2.4e9))
         for k in ("forward", "backward"):
             roofs[k]["frac_of_nonpacked_78_6"] = roofs[k]["achieved"] / ALU_NONPACKED_TFLOPS
         dominant = max(("forward", "backward", "adam"), key=lambda k: kernel_ms[k])
@@ -487,11 +499,20 @@ def bench_bin_stress(args, ctx, gsr, scenes, torch, np):
             note = (f"depth sort 4 x 20 B per splat + tile sort {tp} passes of 6-bit digits "
                     f"({'packed' if packed else 'unpacked'})")
         ach = by / (sort_ms * 1e-3) / 1e9
+        # HBM bytes per bin from the committed counter record of this leg (copy-calibrated), or null
+        from differentiable_gaussian_splatting_amd import profiling
+        md = os.path.join(ROOT, "profiles", "hbm_counters_bin1m.md")
+        if scheme == "key64":
+            d = (tile_bits + 32 + 7) // 8
+            kern = ("k_upsweep<uint64,16u,8u>", "k_scan_rows", "k_scatter<uint64,16u,8u,false,false>") * d
+        else:
+            kern = profiling.sort_kernels({"depth": 4, "tile": (tile_bits + 5) // 6})
+        traffic = profiling.traffic_for(kern, md)
         out[scheme] = {"pairs": P, "bin_ms": ms["bin"], "depth_sort_ms": ms["depth_sort"],
                        "tile_sort_ms": ms["tile_sort"], "sigma": {nm: float(np.std(v)) for nm, v in reps.items()},
                        "sort_roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                          "frac": ach / HBM_PEAK_GBS, "work_per_launch": by, "kernel_ms": sort_ms,
-                                         "bytes": note}}
+                                         "bytes": note, "traffic": traffic}}
     gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SCHEME, gsr.GSR_BIN_PRESORT if args.bin_scheme == "presort"
                        else gsr.GSR_BIN_KEY64)
     k64 = out["key64"]["sort_roofline"]["work_per_launch"]

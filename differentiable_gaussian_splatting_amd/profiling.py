@@ -89,24 +89,22 @@ def base_kernel(name: str) -> str:
     return short_name(name).split("<")[0]
 
 
-def _range_window(marker_csv: str, name: str):
-    """(start, end) timestamps of the ROCTx range `name` in a rocprofv3 marker trace, or None."""
+def _range_windows(marker_csv: str, name: str) -> list:
+    """(start, end) timestamps of every ROCTx range `name` in a rocprofv3 marker trace (bench.py opens one per
+    timed repeat)."""
     try:
         rows = list(csv.DictReader(open(marker_csv)))
     except OSError:
-        return None
-    for r in rows:
-        if name in r.values():
-            return int(r["Start_Timestamp"]), int(r["End_Timestamp"])
-    return None
+        return []
+    return [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows if name in r.values()]
 
 
-def timed_table(kernel_csv: str, window) -> list:
-    """Per-kernel calls and durations of the dispatches that ran inside `window`, longest total first."""
+def timed_table(kernel_csv: str, windows) -> list:
+    """Per-kernel calls and durations of the dispatches that ran inside any of `windows`, longest total first."""
     acc = collections.defaultdict(list)
     for r in csv.DictReader(open(kernel_csv)):
         t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
-        if t0 >= window[0] and t1 <= window[1]:
+        if any(t0 >= w0 and t1 <= w1 for w0, w1 in windows):
             acc[short_name(r["Kernel_Name"])].append(t1 - t0)
     total = sum(sum(v) for v in acc.values()) or 1
     out = ["| kernel | calls | avg µs | min µs | max µs | total ms | % |", "|---|---|---|---|---|---|---|"]
@@ -123,10 +121,11 @@ def trace_md(stats_csv: str, title: str, cmd: str, timed_range: str | None = Non
     out = [f"# {title}", "", "Command (run from the repository root):", "", "```", cmd, "```", ""]
     if timed_range:
         stem = stats_csv[:-len("kernel_stats.csv")]
-        window = _range_window(stem + "marker_api_trace.csv", timed_range)
-        if window:
-            out += [f"Dispatches inside the ROCTx range \"{timed_range}\" ({(window[1] - window[0]) / 1e6:.3f} ms):", ""]
-            out += timed_table(stem + "kernel_trace.csv", window) + ["", "Every dispatch of the run:", ""]
+        windows = _range_windows(stem + "marker_api_trace.csv", timed_range)
+        if windows:
+            span = sum(w1 - w0 for w0, w1 in windows) / 1e6
+            out += [f"Dispatches inside the {len(windows)} ROCTx ranges \"{timed_range}\" ({span:.3f} ms in all):", ""]
+            out += timed_table(stem + "kernel_trace.csv", windows) + ["", "Every dispatch of the run:", ""]
     out += ["| kernel | calls | avg µs | min µs | max µs | total ms | % |", "|---|---|---|---|---|---|---|"]
     for r in rows:
         out.append(f"| `{short_name(r['Name'])[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -181,17 +180,21 @@ def pmc_md(base: str, cmd: str, workload: str, first: int | None = None) -> str:
                   f"FETCH_SIZE KiB x 1024 x {scale.get('FETCH_SIZE', float('nan')):.4f}, "
                   f"WRITE_SIZE KiB x 1024 x {scale.get('WRITE_SIZE', float('nan')):.4f}.", ""]
     cols = [("valu", "_ns"), ("valu", "SQ_INSTS_VALU"), ("valu", "SQ_INSTS_SALU"), ("valu", "SQ_INSTS_LDS"),
+            ("valu", "SQ_INSTS_MFMA"), ("valu", "SQ_VALU_MFMA_BUSY_CYCLES"),
             ("flops", "SQ_INSTS_VALU_FLOPS_FP32"), ("flops", "SQ_INSTS_VALU_FLOPS_FP64"),
             ("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")]
     lines += [("Per dispatch (mean over each kernel's first %d dispatches: the step's warmup and timed launches "
                "come before\nthe other blocks of bench.py, which run some of the same kernels on other inputs). "
                % first if first else "Per dispatch (mean over the profiled dispatches). ") +
               "`_ns` is the dispatch duration in the valu pass;",
-              "VALU issue = SQ_INSTS_VALU x 4 cycles (a wave64 instruction on a 16-lane SIMD) / (1024 SIMDs x",
-              "duration x 2.4 GHz); the FLOPS counters count per wave instruction (an FMA counts 2), so counted",
-              "TFLOP/s = 64 lanes x (FLOPS_FP32 + FLOPS_FP64) / duration, an upper bound (inactive lanes count).", "",
-              "| kernel | " + " | ".join(c for _, c in cols) + " | VALU issue | counted TFLOP/s | HBM MB (scaled) |",
-              "|---|" + "---|" * (len(cols) + 3)]
+              "VALU issue = (SQ_INSTS_VALU - SQ_INSTS_MFMA) x 4 cycles (a wave64 instruction on a 16-lane SIMD) /",
+              "(1024 SIMDs x duration x 2.4 GHz), MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 x duration x 2.4 GHz)",
+              "(fp32 MFMA and VALU do not overlap on one SIMD, so their sum is the SIMDs' busy share); the FLOPS",
+              "counters count per wave instruction (an FMA counts 2), so counted TFLOP/s = 64 lanes x (FLOPS_FP32 +",
+              "FLOPS_FP64) / duration, an upper bound (inactive lanes count).", "",
+              "| kernel | " + " | ".join(c for _, c in cols) + " | VALU issue | MFMA busy | counted TFLOP/s | "
+              "HBM MB (scaled) |",
+              "|---|" + "---|" * (len(cols) + 4)]
     record = {}
     for k in kernels:
         vals = []
@@ -203,17 +206,23 @@ def pmc_md(base: str, cmd: str, workload: str, first: int | None = None) -> str:
         v = passes.get("valu", ({}, {}))[0].get(k, {})
         f = passes.get("flops", ({}, {}))[0].get(k, {})
         ns = v.get("_ns")
-        issue = v["SQ_INSTS_VALU"] * 4 / (1024 * ns * 2.4) if ns and "SQ_INSTS_VALU" in v else None
+        mfma = v.get("SQ_INSTS_MFMA", 0.0)
+        issue = (v["SQ_INSTS_VALU"] - mfma) * 4 / (1024 * ns * 2.4) if ns and "SQ_INSTS_VALU" in v else None
+        mbusy = v["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * ns * 2.4) if ns and "SQ_VALU_MFMA_BUSY_CYCLES" in v else None
         hbm = None
         if fetch is not None and write is not None and len(scale) == 2:
             hbm = fetch * 1024 * scale["FETCH_SIZE"] + write * 1024 * scale["WRITE_SIZE"]
             if base_kernel(k) in KERNEL_SOURCES:  # one record per instance (k_adam<false> and <true> differ)
-                inst = short_name(k).replace(", ", ",").replace("unsigned int", "uint32")
+                inst = (short_name(k).replace(", ", ",").replace("unsigned int", "uint32")
+                        .replace("unsigned long", "uint64"))
                 record[inst] = {"hbm_bytes": hbm, "fetch_kib": fetch, "write_kib": write, "valu_issue": issue,
-                                "valu_insts": v.get("SQ_INSTS_VALU"), "sources": source_hash(inst)}
+                                "valu_insts": None if "SQ_INSTS_VALU" not in v else v["SQ_INSTS_VALU"] - mfma,
+                                "mfma_insts": mfma, "mfma_busy_cycles": v.get("SQ_VALU_MFMA_BUSY_CYCLES"),
+                                "sources": source_hash(inst)}
         tf = (64 * (f.get("SQ_INSTS_VALU_FLOPS_FP32", 0) + f.get("SQ_INSTS_VALU_FLOPS_FP64", 0)) / (f["_ns"] * 1e3)
               if f.get("_ns") else None)
         lines.append(f"| `{k[:60]}` | " + " | ".join(vals) + f" | {'' if issue is None else f'{issue:.3f}'} | "
+                     f"{'' if mbusy is None else f'{mbusy:.3f}'} | "
                      f"{'' if tf is None else f'{tf:.2f}'} | {'' if hbm is None else f'{hbm / 1e6:.1f}'} |")
     lines += ["", TRAFFIC_BEGIN, json.dumps({"workload": workload, "scale": scale, "kernels": record}, indent=1),
               TRAFFIC_END, ""]
@@ -253,6 +262,16 @@ def valu_issue_for(kernel, md_path: str):
         return None
     k = rec["kernels"][kernel]
     return k.get("valu_issue") if k.get("sources") == source_hash(kernel) else None
+
+
+def mfma_busy_for(kernel, md_path: str):
+    """Recorded SIMD cycles per launch spent in MFMA instructions (SQ_VALU_MFMA_BUSY_CYCLES) of the kernel instance,
+    or None when unrecorded or its sources changed since."""
+    rec = read_traffic(md_path)
+    if not rec or kernel not in rec.get("kernels", {}):
+        return None
+    k = rec["kernels"][kernel]
+    return k.get("mfma_busy_cycles") if k.get("sources") == source_hash(kernel) else None
 
 
 def valu_insts_for(kernel, md_path: str):
