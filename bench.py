@@ -284,6 +284,7 @@ def main():
               "kernel_ms": {nm: {"repeats": v, "sigma": float(np.std(v))} for nm, v in kernel_reps.items()}}
     P = b.num_pairs
     e_bwd_gpu = int(last_contrib.to(torch.int64).sum().item())
+    sync_free = bench_sync_free(args, ctx, gsr, torch, np, step, b, walls)
     det = bench_deterministic_backward(args, ctx, gsr, torch, np, stream, splats, b, W, H, out_rgba, final_T,
                                        last_contrib, v_out, grad)
     per_splat = bench_per_splat_backward(args, ctx, gsr, torch, np, splats, b, W, H, out_rgba, final_T,
@@ -317,6 +318,7 @@ def main():
     det["ratio_to_default"] = det["ms"] / stage_ms["backward"]
     det["kernel_ratio_to_default"] = det["kernel_ms"] / kernel_ms["backward"]
     result["deterministic_backward"] = det
+    result["sync_free_bin"] = sync_free
     per_splat["kernel_ratio_to_default"] = per_splat["kernel_ms"] / kernel_ms["backward"]
     result["per_splat_backward"] = per_splat
     if cpu is not None:
@@ -576,6 +578,39 @@ def bench_changing_views(args, ctx, gsr, scenes, torch, np):
     res["pairs_first_last"] = [pairs[0], pairs[-1]]
     res["gain_of_cost_order_vs_length"] = {k: res["length"][k] / res["cost"][k] for k in ("forward", "backward")}
     return res
+
+
+def bench_sync_free(args, ctx, gsr, torch, np, step, bins_sync, walls_sync):
+    """The same steps with GSR_OPT_BIN_SYNC_FREE: gsr_bin queues its launches without waiting for the pair count
+    (buffers sized from the counts seen). Wall clock of K steps, `repeats` times, beside the waiting form's; checks
+    that no call overflowed and that the bins equal the waiting form's."""
+    print("[bench] sync-free binning", file=sys.stderr, flush=True)
+    ref_keys, ref_vals, ref_ranges = gsr.gsr_bins_copy(ctx, bins_sync)
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SYNC_FREE, 1)
+    try:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        walls = []
+        for _ in range(args.repeats):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                b = step()
+            torch.cuda.synchronize()
+            walls.append(time.perf_counter() - t0)
+        pairs, over = gsr.gsr_bin_pair_count(ctx)
+        keys, vals, ranges = gsr.gsr_bins_copy(ctx, b)
+        P = bins_sync.num_pairs
+        same = (not over and pairs == P and torch.equal(ranges, ref_ranges) and torch.equal(vals[:P], ref_vals)
+                and (keys is None or torch.equal(keys[:P], ref_keys)))
+    finally:
+        gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SYNC_FREE, 0)
+    ms = [w * 1e3 / args.steps for w in walls]
+    ms_sync = [w * 1e3 / args.steps for w in walls_sync]
+    return {"ms_per_step": float(np.median(ms)), "repeats": ms, "sigma": float(np.std(ms)),
+            "ms_per_step_waiting": float(np.median(ms_sync)), "capacity": int(b.num_pairs), "pairs": pairs,
+            "overflowed": over, "bins_equal_waiting_form": bool(same)}
 
 
 def bench_deterministic_backward(args, ctx, gsr, torch, np, stream, splats, b, W, H, out_rgba, final_T, last_contrib,

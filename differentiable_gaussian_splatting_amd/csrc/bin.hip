@@ -127,15 +127,20 @@ __global__ __launch_bounds__(kThreads) void k_prep(const float* __restrict__ spl
   if (threadIdx.x == 0) part[blockIdx.x] = total;
 }
 
-// *total = sum of part[0..nb), by one workgroup.
+// *total = sum of part[0..nb), by one workgroup, also stored to the pinned host word *host_total, which the host
+// reads once the launch has completed (one store instead of a copy launch). (A last-block-done sum inside k_prep
+// would save this launch but serialise its 1,600 workgroups on one counter: 26 us against 6 + 5.)
 __global__ __launch_bounds__(kThreads) void k_total(const uint64_t* __restrict__ part, uint32_t nb,
-                                                    uint64_t* __restrict__ total) {
+                                                    uint64_t* __restrict__ total, uint64_t* __restrict__ host_total) {
   __shared__ uint64_t smem[kThreads / kWave];
   uint64_t sum = 0;
   for (uint32_t j = threadIdx.x; j < nb; j += kThreads) sum += part[j];
   uint64_t all;
   block_exclusive_scan<uint64_t, kThreads>(sum, &all, smem);
-  if (threadIdx.x == 0) *total = all;
+  if (threadIdx.x == 0) {
+    *total = all;
+    *host_total = all;
+  }
 }
 
 // Two-launch exclusive scan of uint32 counts into uint64 offsets; offsets[n] = total. With `order`, position j
@@ -282,7 +287,8 @@ template <typename K, bool kPacked = false>
 __global__ __launch_bounds__(kThreads) void k_emit(const uint4* __restrict__ rects, const float* __restrict__ depths,
                                                    uint32_t n, const uint32_t* __restrict__ order,
                                                    uint32_t order_mask, uint32_t tiles_x,
-                                                   const uint64_t* __restrict__ offsets, uint64_t num_pairs,
+                                                   const uint64_t* __restrict__ offsets, uint64_t pairs_cap,
+                                                   const uint64_t* __restrict__ pairs_dev,
                                                    K* __restrict__ keys, uint32_t* __restrict__ vals,
                                                    uint32_t idx_bits) {
   constexpr uint32_t kPer = 4, kChunk = kPer * kThreads;  // kPer = 4: one 16-byte vector of values per thread
@@ -292,6 +298,7 @@ __global__ __launch_bounds__(kThreads) void k_emit(const uint4* __restrict__ rec
   __shared__ uint32_t smem[kThreads / kWave];
   const uint32_t tid = threadIdx.x;
   const uint32_t j = blockIdx.x * kThreads + tid;
+  const uint64_t num_pairs = count_within(pairs_dev, pairs_cap);  // 0: nothing fits, nothing is written
   s_off[tid] = offsets[min(j, n)];
   if (tid == 0) s_off[kThreads] = offsets[min(blockIdx.x * kThreads + kThreads, n)];
   if (j < n) {
@@ -379,7 +386,8 @@ __global__ __launch_bounds__(kThreads) void k_emit_ellipse(const float* __restri
                                                            const uint32_t* __restrict__ order, uint32_t order_mask,
                                                            uint32_t tiles_x,
                                                            const uint64_t* __restrict__ offsets,
-                                                           uint64_t num_pairs, K* __restrict__ keys,
+                                                           uint64_t pairs_cap, const uint64_t* __restrict__ pairs_dev,
+                                                           K* __restrict__ keys,
                                                            uint32_t* __restrict__ vals, uint32_t idx_bits) {
   const uint32_t j = blockIdx.x * kThreads + threadIdx.x;
   if (j >= n) return;
@@ -390,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void k_emit_ellipse(const float* __restri
   const float x = sp[0], y = sp[1], a = sp[2], b = sp[3], c = sp[4];
   const uint32_t dbits = __float_as_uint(depths[i]);
   uint64_t p = offsets[j];
-  const uint64_t p_end = min(offsets[j + 1], num_pairs);
+  const uint64_t p_end = min(offsets[j + 1], count_within(pairs_dev, pairs_cap));
   // rect = (tx0, ty0, w, h)
   for (uint32_t ty = r.y; ty < r.y + r.w && p < p_end; ++ty)
     for (uint32_t tx = r.x; tx < r.x + r.z && p < p_end; ++tx) {
@@ -416,10 +424,12 @@ constexpr uint32_t kRangeItems = 4;
 
 template <typename K>
 __global__ __launch_bounds__(kThreads) void k_ranges(const K* __restrict__ keys, const uint32_t* __restrict__ vals,
-                                                     uint32_t P, uint32_t num_tiles,
+                                                     uint64_t pairs_cap, const uint64_t* __restrict__ pairs_dev,
+                                                     uint32_t num_tiles,
                                                      const float* __restrict__ depths, uint32_t n,
                                                      uint64_t* __restrict__ keys_final,
                                                      uint32_t* __restrict__ ranges, uint32_t tile_shift) {
+  const uint64_t P = count_within(pairs_dev, pairs_cap);  // 0 when nothing fitted: every range is then empty
   const uint64_t i0 = (uint64_t(blockIdx.x) * kThreads + threadIdx.x) * kRangeItems;
   if (i0 > P) return;
   auto tile_of = [tile_shift](K k) -> int64_t {
@@ -573,6 +583,11 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   Arena& a = ctx->arena;
   const bool presort = ctx->bin_scheme == GSR_BIN_PRESORT;
   const bool ellipse = ctx->bin_rule == GSR_BIN_ELLIPSE;
+  // An earlier call's pair count that has arrived in the meantime raises the capacity hint (before this call's
+  // launch overwrites the pinned word).
+  if (ctx->pairs_pending && hipEventQuery(a.total_ready) == hipSuccess) note_pair_count(ctx);
+  // Without a wait only once there is a count or a reservation to size the pair buffers from.
+  const bool sync_free = ctx->bin_sync_free && n && (ctx->pair_hint > 0 || ctx->pair_reserved > 0);
 
   if ((st = grow(ctx, a.ranges, size_t(num_tiles) * 8))) return st;
   if ((st = grow(ctx, a.counts, size_t(n + 1) * 4)) || (st = grow(ctx, a.offsets, size_t(n + 1) * 8)) ||
@@ -598,21 +613,27 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   const uint32_t count_shift = pack_counts ? idx_bits : 32u;
   const uint32_t order_mask = pack_counts ? (idx_bits ? (1u << idx_bits) - 1u : 0u) : ~0u;
 
-  // Rectangles, counts and the pair total first; the total goes to the host while the depth sort runs.
+  // Rectangles, counts and the pair total first; the total goes to the host (a pinned word k_total writes) while
+  // the depth sort runs.
   timing_mark(ctx, GSR_STAGE_BIN, s, false);
+  hipError_t e = hipSuccess;
   if (n) {
     hipLaunchKernelGGL(k_prep, dim3(nb_prep), dim3(kThreads), 0, s, splats, depths, n, tiles_x, tiles_y, ellipse,
                        rects, counts,
                        presort ? ok : static_cast<uint32_t*>(nullptr), presort ? ov : static_cast<uint32_t*>(nullptr),
                        count_shift, part);
-    hipLaunchKernelGGL(k_total, dim3(1), dim3(kThreads), 0, s, part, nb_prep, offsets + n);
+    hipLaunchKernelGGL(k_total, dim3(1), dim3(kThreads), 0, s, static_cast<const uint64_t*>(part), nb_prep,
+                       offsets + n, a.host_total_dev);
+    if ((st = check_launch(ctx, "gsr_bin rectangles"))) return st;
+    e = hipEventRecord(a.total_ready, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "gsr_bin pair count readback");
+    ctx->pairs_pending = true;  // this call's count, on its way to the pinned word
+    ctx->last_cap = 0;
   } else {
-    hipLaunchKernelGGL(k_total, dim3(1), dim3(kThreads), 0, s, part, 0u, offsets);
+    ctx->pairs_pending = false;
+    ctx->last_pairs = 0;
+    ctx->last_cap = 0;
   }
-  if ((st = check_launch(ctx, "gsr_bin rectangles"))) return st;
-  hipError_t e = hipMemcpyAsync(a.host_total, offsets + n, sizeof(uint64_t), hipMemcpyDeviceToHost, s);
-  if (e == hipSuccess) e = hipEventRecord(a.total_ready, s);
-  if (e != hipSuccess) return hip_fail(ctx, e, "gsr_bin pair count readback");
 
   const uint32_t* order = nullptr;
   if (presort && n) {
@@ -644,10 +665,26 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   }
   if ((st = check_launch(ctx, "gsr_bin depth sort/scan"))) return st;
 
-  // The one wait of the call: the pair count sizes the arena and the launches below.
-  e = hipEventSynchronize(a.total_ready);
-  if (e != hipSuccess) return hip_fail(ctx, e, "gsr_bin pair count readback");
-  const uint64_t P = *a.host_total;
+  // The one wait of the call: the pair count sizes the arena and the launches below. Sync-free, the launches are
+  // sized for a capacity instead and read the count from device memory (offsets[n], the scan's total); when it
+  // exceeds the capacity they emit nothing and every tile's range is empty (gsr_bin_pair_count reports it).
+  uint64_t P = 0;  // the pair count, or the capacity the launches are sized for
+  const uint64_t* pairs_dev = nullptr;
+  if (sync_free) {
+    // the capacity rule of the C0 resident arena page (section 2 table, row "C0"): the largest of 2^16 pairs,
+    // 16 per splat and 1.5 times the count seen, here also of a reservation
+    P = std::min<uint64_t>(std::max<uint64_t>({ctx->pair_reserved, uint64_t(1) << 16, uint64_t(n) * 16,
+                                               ctx->pair_hint + ctx->pair_hint / 2}),
+                           (uint64_t(1) << 32) - 1);
+    pairs_dev = offsets + n;
+    ctx->last_cap = P;
+  } else if (n) {
+    e = hipEventSynchronize(a.total_ready);
+    if (e != hipSuccess) return hip_fail(ctx, e, "gsr_bin pair count readback");
+    note_pair_count(ctx);
+    P = ctx->last_pairs;
+    ctx->last_cap = P;
+  }
   if (P >= (uint64_t(1) << 32)) return fail(ctx, GSR_EOVERFLOW, "gsr_bin: %llu pairs exceed 2^32 - 1",
                                             (unsigned long long)P);
 
@@ -665,22 +702,24 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     uint32_t* kb[2] = {static_cast<uint32_t*>(a.keys[0].ptr), static_cast<uint32_t*>(a.keys[1].ptr)};
     if (ellipse)
       hipLaunchKernelGGL((k_emit_ellipse<uint32_t, true>), dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats,
-                         rects, depths, n, order, order_mask, tiles_x, offsets, P, kb[0], static_cast<uint32_t*>(nullptr),
-                         idx_bits);
+                         rects, depths, n, order, order_mask, tiles_x, offsets, P, pairs_dev, kb[0],
+                         static_cast<uint32_t*>(nullptr), idx_bits);
     else
       hipLaunchKernelGGL((k_emit<uint32_t, true>), dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, rects, depths,
-                         n, order, order_mask, tiles_x, offsets, P, kb[0], static_cast<uint32_t*>(nullptr), idx_bits);
+                         n, order, order_mask, tiles_x, offsets, P, pairs_dev, kb[0], static_cast<uint32_t*>(nullptr),
+                         idx_bits);
     res = (sort_passes(tile_bits) & 1u) ? 1 : 0;  // the first pass writes buffer 1 either way
     if (ctx->bin_keys) {
       if ((st = grow(ctx, a.order_alt, std::max<size_t>(size_t(n) * 8, size_t(P) * 8)))) return st;
       final_k = static_cast<uint64_t*>(a.order_alt.ptr);
     }
     timing_mark(ctx, GSR_STAGE_TILE_SORT, s, false);
-    st = radix_sort_tiles_packed(ctx, s, kb[0], P, idx_bits, tile_bits, kb[res], kb[1 - res], v0, final_k, depths, n);
+    st = radix_sort_tiles_packed(ctx, s, kb[0], P, idx_bits, tile_bits, kb[res], kb[1 - res], v0, final_k,
+                                 depths, n, pairs_dev);
     if (st) return st;
     timing_mark(ctx, GSR_STAGE_TILE_SORT, s, true);
     hipLaunchKernelGGL(k_ranges<uint32_t>, dim3(grid_for(P + 1, kThreads * kRangeItems)), dim3(kThreads), 0, s,
-                       kb[res], static_cast<const uint32_t*>(v0), uint32_t(P), uint32_t(num_tiles), depths, n,
+                       kb[res], static_cast<const uint32_t*>(v0), P, pairs_dev, uint32_t(num_tiles), depths, n,
                        static_cast<uint64_t*>(nullptr), ranges, idx_bits);
     sorted_v = v0;
   } else if (presort) {
@@ -690,10 +729,10 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     {
       if (ellipse)
         hipLaunchKernelGGL(k_emit_ellipse<uint32_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats, rects,
-                           depths, n, order, order_mask, tiles_x, offsets, P, kb[0], v0, 0u);
+                           depths, n, order, order_mask, tiles_x, offsets, P, pairs_dev, kb[0], v0, 0u);
       else
         hipLaunchKernelGGL(k_emit<uint32_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, rects, depths, n, order,
-                           order_mask, tiles_x, offsets, P, kb[0], v0, 0u);
+                           order_mask, tiles_x, offsets, P, pairs_dev, kb[0], v0, 0u);
     }
     // The 64-bit keys go to the key buffer the sorted tile ids do not end in, written by the last sort pass (or by
     // the range kernel when there is no pass).
@@ -707,10 +746,11 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
         // the last pass reads buffer 1 - res and writes buffer res; the 64-bit keys need a third place
         if ((st = grow(ctx, a.order_alt, std::max<size_t>(size_t(n) * 8, size_t(P) * 8)))) return st;
         final_k = static_cast<uint64_t*>(a.order_alt.ptr);
-        st = radix_sort_tiles_final(ctx, s, kb[0], v0, P, tile_bits, kb[res], vr, kb[1 - res], vt, final_k, depths, n);
+        st = radix_sort_tiles_final(ctx, s, kb[0], v0, P, tile_bits, kb[res], vr, kb[1 - res], vt, final_k, depths, n,
+                                    pairs_dev);
         keys_done = true;
       } else {
-        st = radix_sort_launch<uint32_t>(ctx, s, kb[0], v0, P, tile_bits, kb[res], vr, kb[1 - res], vt);
+        st = radix_sort_launch<uint32_t>(ctx, s, kb[0], v0, P, tile_bits, kb[res], vr, kb[1 - res], vt, pairs_dev);
       }
       if (st) return st;
       timing_mark(ctx, GSR_STAGE_TILE_SORT, s, true);
@@ -718,7 +758,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     uint64_t* ranges_final = nullptr;
     if (!keys_done) final_k = ranges_final = static_cast<uint64_t*>(a.keys[1 - res].ptr);
     hipLaunchKernelGGL(k_ranges<uint32_t>, dim3(grid_for(P + 1, kThreads * kRangeItems)), dim3(kThreads), 0, s,
-                       kb[res], static_cast<const uint32_t*>(a.vals[res].ptr), uint32_t(P), uint32_t(num_tiles),
+                       kb[res], static_cast<const uint32_t*>(a.vals[res].ptr), P, pairs_dev, uint32_t(num_tiles),
                        depths, n, ranges_final, ranges, 0u);
     sorted_v = static_cast<uint32_t*>(a.vals[res].ptr);
   } else {
@@ -727,10 +767,10 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     {
       if (ellipse)
         hipLaunchKernelGGL(k_emit_ellipse<uint64_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats, rects,
-                           depths, n, order, order_mask, tiles_x, offsets, P, kb[0], v0, 0u);
+                           depths, n, order, order_mask, tiles_x, offsets, P, pairs_dev, kb[0], v0, 0u);
       else
         hipLaunchKernelGGL(k_emit<uint64_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, rects, depths, n, order,
-                           order_mask, tiles_x, offsets, P, kb[0], v0, 0u);
+                           order_mask, tiles_x, offsets, P, pairs_dev, kb[0], v0, 0u);
     }
     if (P > 0) {
       const uint32_t key_bits = 32 + tile_bits;
@@ -738,13 +778,13 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
       timing_mark(ctx, GSR_STAGE_TILE_SORT, s, false);
       st = radix_sort_launch<uint64_t>(ctx, s, kb[0], v0, P, key_bits, kb[res],
                                        static_cast<uint32_t*>(a.vals[res].ptr), kb[1 - res],
-                                       static_cast<uint32_t*>(a.vals[1 - res].ptr));
+                                       static_cast<uint32_t*>(a.vals[1 - res].ptr), pairs_dev);
       if (st) return st;
       timing_mark(ctx, GSR_STAGE_TILE_SORT, s, true);
     }
     final_k = kb[res];
     hipLaunchKernelGGL(k_ranges<uint64_t>, dim3(grid_for(P + 1, kThreads * kRangeItems)), dim3(kThreads), 0, s,
-                       kb[res], static_cast<const uint32_t*>(a.vals[res].ptr), uint32_t(P), uint32_t(num_tiles),
+                       kb[res], static_cast<const uint32_t*>(a.vals[res].ptr), P, pairs_dev, uint32_t(num_tiles),
                        depths, n, static_cast<uint64_t*>(nullptr), ranges, 0u);
     sorted_v = static_cast<uint32_t*>(a.vals[res].ptr);
   }
@@ -758,5 +798,19 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   out->tiles_y = tiles_y;
   out->splat_pairs = n ? counts : nullptr;
   out->num_splats = n;
+  return GSR_OK;
+}
+
+extern "C" gsr_status gsr_bin_pair_count(gsr_ctx* ctx, uint64_t* num_pairs, int32_t* overflowed) {
+  if (!ctx || !num_pairs || !overflowed) return GSR_EINVAL;
+  gsr_status st = enter(ctx);
+  if (st) return st;
+  if (ctx->pairs_pending) {
+    const hipError_t e = hipEventSynchronize(ctx->arena.total_ready);
+    if (e != hipSuccess) return hip_fail(ctx, e, "gsr_bin_pair_count");
+    note_pair_count(ctx);
+  }
+  *num_pairs = ctx->last_pairs;
+  *overflowed = ctx->last_pairs > ctx->last_cap ? 1 : 0;
   return GSR_OK;
 }

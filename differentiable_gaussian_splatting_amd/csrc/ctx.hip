@@ -32,7 +32,8 @@ gsr_status enter(gsr_ctx* ctx) {
 template <typename F>
 static void for_each_buffer(Arena& a, F f) {
   for (DevBuf* b : {&a.keys[0], &a.keys[1], &a.vals[0], &a.vals[1], &a.counts, &a.offsets, &a.order, &a.order_alt,
-                    &a.order_vals, &a.order_vals_alt, &a.scan_part, &a.hist, &a.digit_tot, &a.ranges, &a.rects,
+                    &a.order_vals, &a.order_vals_alt, &a.scan_part, &a.hist, &a.digit_tot,
+                    &a.ranges, &a.rects,
                     &a.tile_order_ext, &a.tile_cost, &a.loss_part, &a.loss_maps, &a.grad_fixed})
     f(*b);
 }
@@ -126,6 +127,12 @@ static void release(DevBuf& b) {
   b.bytes = 0;
 }
 
+void note_pair_count(gsr_ctx* ctx) {
+  ctx->last_pairs = *static_cast<volatile uint64_t*>(ctx->arena.host_total);
+  ctx->pair_hint = std::max(ctx->pair_hint, ctx->last_pairs);
+  ctx->pairs_pending = false;
+}
+
 }  // namespace gsr
 
 using namespace gsr;
@@ -147,12 +154,20 @@ gsr_status gsr_create(gsr_ctx** out, int hip_device) {
     return GSR_EHIP;
   }
   Arena& a = ctx->arena;
-  e = hipHostMalloc(reinterpret_cast<void**>(&a.host_total), sizeof(uint64_t), hipHostMallocDefault);
+  // coherent: k_prep's store of the pair count is visible to the host once the launch has completed
+  e = hipHostMalloc(reinterpret_cast<void**>(&a.host_total), sizeof(uint64_t),
+                    hipHostMallocMapped | hipHostMallocCoherent);
   if (e != hipSuccess) {
     delete ctx;
     return GSR_ENOMEM;
   }
   *a.host_total = 0;
+  e = hipHostGetDevicePointer(reinterpret_cast<void**>(&a.host_total_dev), a.host_total, 0);
+  if (e != hipSuccess) {
+    (void)hipHostFree(a.host_total);
+    delete ctx;
+    return GSR_EHIP;
+  }
   // the count scan's last-block-done counter, zero between launches
   e = hipMalloc(reinterpret_cast<void**>(&a.done), sizeof(uint32_t));
   if (e == hipSuccess) e = hipMemset(a.done, 0, sizeof(uint32_t));
@@ -223,6 +238,10 @@ gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value) {
       if (value < 0) return fail(ctx, GSR_EINVAL, "gsr_set_option: the arena limit must be >= 0");
       ctx->arena.limit = size_t(value);
       return GSR_OK;
+    case GSR_OPT_BIN_SYNC_FREE:
+      if (value != 0 && value != 1) return fail(ctx, GSR_EINVAL, "gsr_set_option: bin sync-free must be 0 or 1");
+      ctx->bin_sync_free = value != 0;
+      return GSR_OK;
     case GSR_OPT_KERNEL_TIMING:
       if (value < 0 || value > 4096)
         return fail(ctx, GSR_EINVAL, "gsr_set_option: kernel timing ring must hold 0..4096 launches");
@@ -275,8 +294,10 @@ gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats) {
   };
   for (auto& p : plan)
     if ((st = grow(ctx, *p.b, p.bytes))) return st;
+  ctx->pair_reserved = std::max(ctx->pair_reserved, max_pairs);
   return GSR_OK;
 }
+
 
 gsr_status gsr_bins_copy(gsr_ctx* ctx, void* stream, const gsr_bins* bins, uint64_t* keys, uint32_t* vals,
                          uint32_t* ranges, uint32_t* splat_pairs) {

@@ -46,7 +46,8 @@ struct Arena {
   DevBuf loss_maps;   // float [9][H][W] the SSIM map's three derivatives per channel, between the loss's passes
   DevBuf grad_fixed;  // the deterministic backward's sums: uint64 [n][9][2] fixed point, then uint32 [n] flags
   size_t limit = 0;                // GSR_OPT_ARENA_LIMIT: most bytes the buffers above may hold together (0: none)
-  uint64_t* host_total = nullptr;  // pinned host word for the one pair-count readback
+  uint64_t* host_total = nullptr;  // pinned host word for the one pair-count readback (written by a kernel)
+  uint64_t* host_total_dev = nullptr;  // its device-side address
   uint32_t* done = nullptr;        // last-block-done counter of the count scan (0 between launches)
   hipEvent_t total_ready = nullptr;  // recorded after the readback is queued
 };
@@ -64,6 +65,13 @@ struct gsr_ctx {
   bool deterministic = false;  // backward sums independent of scheduling (fixed-point atomics)
   int32_t backward_scheme = GSR_BACKWARD_PER_PIXEL;
   int32_t tile_order = GSR_ORDER_COST;  // how raster_tile_order ranks the tiles
+  // GSR_OPT_BIN_SYNC_FREE, and the pair counts it sizes its buffers from
+  bool bin_sync_free = false;
+  bool pairs_pending = false;  // the last gsr_bin's count is still on its way to the pinned word
+  uint64_t pair_hint = 0;      // the largest pair count the host has read
+  uint64_t pair_reserved = 0;  // the largest gsr_reserve
+  uint64_t last_pairs = 0;     // the last count read
+  uint64_t last_cap = 0;       // pairs the last gsr_bin's launches were sized for (its count, when it waited)
   uint64_t cost_tiles = 0;  // tile count of the grid tile_cost describes (0: none yet)
   const uint32_t* order_ranges = nullptr;  // the ranges tile_order_ext was last ranked for (by a forward)
   uint64_t order_tiles = 0;
@@ -100,6 +108,10 @@ gsr_status check_launch(gsr_ctx* ctx, const char* what);
 // With kernel timing on, records the begin (end = false) or end event of the stage's current launch on `s`.
 void timing_mark(gsr_ctx* ctx, int stage, hipStream_t s, bool end);
 
+// Reads the pair count the last gsr_bin left in the pinned word (its launch must have completed) into
+// ctx->last_pairs and raises ctx->pair_hint to it.
+void note_pair_count(gsr_ctx* ctx);
+
 // Looks up the device address of gsr_render_forward_noalloc's scratch array on the current device into
 // ctx->noalloc_scratch (raster_fwd.hip; called by gsr_create with ctx's device current).
 gsr_status noalloc_setup(gsr_ctx* ctx);
@@ -122,24 +134,28 @@ const uint32_t* raster_tile_order(gsr_ctx* ctx, hipStream_t s, const gsr_bins* b
 // (sort_passes). The result lands in (keys_out, vals_out); (tmp_keys, tmp_vals) are scratch of n elements. The
 // first pass must not write over keys_in: keys_in may equal keys_out when the pass count is even and tmp_keys when
 // it is odd. Uses the arena's histogram buffers (grown as needed).
+// With n_dev (here and in the two tile sorts below), n is a capacity: the launches are sized for n keys and sort
+// the first *n_dev of them, a count earlier launches on the stream leave in device memory (none when it exceeds n).
 uint32_t sort_blocks(uint64_t n);
 uint32_t sort_passes(uint32_t key_bits);
 template <typename K>
 gsr_status radix_sort_launch(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint32_t* vals_in, uint64_t n,
-                             uint32_t key_bits, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals);
+                             uint32_t key_bits, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals,
+                             const uint64_t* n_dev = nullptr);
 
 // The same sort of 32-bit tile ids whose last pass also writes keys_final[g] = (key << 32) | bits(depths[val]) for
 // every output position g (values below n_depths; others get depth bits 0). Requires key_bits > 0.
 gsr_status radix_sort_tiles_final(gsr_ctx* ctx, hipStream_t s, const uint32_t* keys_in, const uint32_t* vals_in,
                                   uint64_t n, uint32_t key_bits, uint32_t* keys_out, uint32_t* vals_out,
                                   uint32_t* tmp_keys, uint32_t* tmp_vals, uint64_t* keys_final,
-                                  const float* depths, uint32_t n_depths);
+                                  const float* depths, uint32_t n_depths, const uint64_t* n_dev = nullptr);
 
 // The tile sort on packed keys (tile << idx_bits) | value (idx_bits + tile_bits <= 32): sorts stably by the tile
 // field, keys only; the last pass writes the sorted keys to keys_out, the values to vals_out and, when keys_final
 // is not null, keys_final[g] = (tile << 32) | bits(depths[value]). Same pass-parity rule as radix_sort_launch.
 gsr_status radix_sort_tiles_packed(gsr_ctx* ctx, hipStream_t s, const uint32_t* keys_in, uint64_t n,
                                    uint32_t idx_bits, uint32_t tile_bits, uint32_t* keys_out, uint32_t* tmp_keys,
-                                   uint32_t* vals_out, uint64_t* keys_final, const float* depths, uint32_t n_depths);
+                                   uint32_t* vals_out, uint64_t* keys_final, const float* depths,
+                                   uint32_t n_depths, const uint64_t* n_dev = nullptr);
 
 }  // namespace gsr

@@ -66,4 +66,12 @@ __device__ __forceinline__ bool count_done_after(uint64_t dep, uint32_t* done, u
   return last;
 }
 
+// The number of items a launch sized for `cap` items processes: cap itself, or with `dev` (a count that earlier
+// launches on the stream computed on the device) *dev when it is at most cap, else none.
+__device__ __forceinline__ uint64_t count_within(const uint64_t* dev, uint64_t cap) {
+  if (!dev) return cap;
+  const uint64_t v = *dev;
+  return v <= cap ? v : 0;
+}
+
 }  // namespace gsr

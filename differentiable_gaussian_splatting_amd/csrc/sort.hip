@@ -52,12 +52,18 @@ __device__ __forceinline__ uint64_t lanemask_lt(uint32_t lane) { return (uint64_
 // histogram of its own with LDS atomics (a wave's atomics on one address serialise, different waves never share
 // one), and the four are summed at the end.
 template <typename K, uint32_t kItems, uint32_t kBits>
-__global__ __launch_bounds__(kThreads) void k_upsweep(const K* __restrict__ keys, uint64_t n, uint32_t shift,
+__global__ __launch_bounds__(kThreads) void k_upsweep(const K* __restrict__ keys, uint64_t n_cap,
+                                                      const uint64_t* __restrict__ n_dev, uint32_t shift,
                                                       uint32_t nb, uint32_t* __restrict__ hist) {
   constexpr uint32_t kRadix = 1u << kBits, kWaves = kThreads / kWave;
   constexpr uint32_t kBlockKeys = kThreads * kItems, kWaveKeys = kWave * kItems;
   __shared__ uint32_t h[kWaves][kRadix];
   const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const uint64_t n = count_within(n_dev, n_cap);
+  if (uint64_t(blockIdx.x) * kBlockKeys >= n) {  // a block past the keys counts nothing (its column stays in the scan)
+    if (tid < kRadix) hist[uint64_t(tid) * nb + blockIdx.x] = 0;
+    return;
+  }
   for (uint32_t i = tid; i < kWaves * kRadix; i += kThreads) (&h[0][0])[i] = 0;
   const uint64_t base = uint64_t(blockIdx.x) * kBlockKeys + uint64_t(w) * kWaveKeys;
   // every load is issued before the first count (clamped indexes: no masked loads, no wait per key)
@@ -101,7 +107,8 @@ __global__ __launch_bounds__(kThreads) void k_scan_rows(uint32_t* __restrict__ h
 // the unpacked values to vals_out, other passes write keys only.
 template <typename K, uint32_t kItems, uint32_t kBits, bool kFinal, bool kPacked = false>
 __global__ __launch_bounds__(kThreads) void k_scatter(const K* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
-                                                      uint64_t n, uint32_t shift, uint32_t nb,
+                                                      uint64_t n_cap, const uint64_t* __restrict__ n_dev,
+                                                      uint32_t shift, uint32_t nb,
                                                       const uint32_t* __restrict__ hist,
                                                       const uint32_t* __restrict__ digit_tot, K* __restrict__ keys_out,
                                                       uint32_t* __restrict__ vals_out,
@@ -117,6 +124,8 @@ __global__ __launch_bounds__(kThreads) void k_scatter(const K* __restrict__ keys
   __shared__ uint32_t s_gbase[kRadix];         // global position of this block's first key of each digit
   __shared__ uint32_t smem[kWaves];
   const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const uint64_t n = count_within(n_dev, n_cap);
+  if (uint64_t(blockIdx.x) * kBlockKeys >= n) return;
 
   // all key and value loads are issued first (clamped indexes, no masked loads), so their latency overlaps the
   // block's scan of the digit bases below
@@ -213,8 +222,8 @@ struct FinalKeys {
 
 template <typename K, uint32_t kItems, uint32_t kBits>
 gsr_status run_passes(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint32_t* vals_in, uint64_t n,
-                      uint32_t passes, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals,
-                      FinalKeys fin) {
+                      const uint64_t* n_dev, uint32_t passes, K* keys_out, uint32_t* vals_out, K* tmp_keys,
+                      uint32_t* tmp_vals, FinalKeys fin) {
   constexpr uint32_t kRadix = 1u << kBits;
   const uint32_t nb = uint32_t((n + kThreads * kItems - 1) / (kThreads * kItems));
   gsr_status st = grow(ctx, ctx->arena.hist, size_t(nb) * kRadix * 4);
@@ -230,7 +239,8 @@ gsr_status run_passes(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint3
     uint32_t* dv = to_out ? vals_out : tmp_vals;
     if (p == 0 && dk == keys_in) return fail(ctx, GSR_EINVAL, "radix sort: first pass would overwrite its input");
     const uint32_t shift = fin.idx_bits + kBits * p;
-    hipLaunchKernelGGL((k_upsweep<K, kItems, kBits>), dim3(nb), dim3(kThreads), 0, s, src_k, n, shift, nb, hist);
+    hipLaunchKernelGGL((k_upsweep<K, kItems, kBits>), dim3(nb), dim3(kThreads), 0, s, src_k, n, n_dev, shift, nb,
+                       hist);
     hipLaunchKernelGGL(k_scan_rows, dim3(kRadix), dim3(kThreads), 0, s, hist, nb, tot);
     const bool last = p + 1 == passes;
     if constexpr (sizeof(K) == 4) {
@@ -238,11 +248,11 @@ gsr_status run_passes(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint3
         // keys only; the last pass unpacks the values (into vals_out, which the caller sized)
         if (last)
           hipLaunchKernelGGL((k_scatter<K, kItems, kBits, true, true>), dim3(nb), dim3(kThreads), 0, s, src_k,
-                             static_cast<const uint32_t*>(nullptr), n, shift, nb, hist, tot, dk, vals_out, fin.keys,
-                             fin.depths, fin.n, fin.idx_bits);
+                             static_cast<const uint32_t*>(nullptr), n, n_dev, shift, nb, hist, tot, dk, vals_out,
+                             fin.keys, fin.depths, fin.n, fin.idx_bits);
         else
           hipLaunchKernelGGL((k_scatter<K, kItems, kBits, false, true>), dim3(nb), dim3(kThreads), 0, s, src_k,
-                             static_cast<const uint32_t*>(nullptr), n, shift, nb, hist, tot, dk,
+                             static_cast<const uint32_t*>(nullptr), n, n_dev, shift, nb, hist, tot, dk,
                              static_cast<uint32_t*>(nullptr), static_cast<uint64_t*>(nullptr),
                              static_cast<const float*>(nullptr), 0u, fin.idx_bits);
         src_k = dk;
@@ -252,12 +262,12 @@ gsr_status run_passes(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint3
     bool final_pass = false;
     if constexpr (sizeof(K) == 4) final_pass = fin.keys && last;
     if (final_pass)
-      hipLaunchKernelGGL((k_scatter<K, kItems, kBits, true>), dim3(nb), dim3(kThreads), 0, s, src_k, src_v, n, shift,
-                         nb, hist, tot, dk, dv, fin.keys, fin.depths, fin.n, 0u);
+      hipLaunchKernelGGL((k_scatter<K, kItems, kBits, true>), dim3(nb), dim3(kThreads), 0, s, src_k, src_v, n, n_dev,
+                         shift, nb, hist, tot, dk, dv, fin.keys, fin.depths, fin.n, 0u);
     else
-      hipLaunchKernelGGL((k_scatter<K, kItems, kBits, false>), dim3(nb), dim3(kThreads), 0, s, src_k, src_v, n, shift,
-                         nb, hist, tot, dk, dv, static_cast<uint64_t*>(nullptr), static_cast<const float*>(nullptr),
-                         0u, 0u);
+      hipLaunchKernelGGL((k_scatter<K, kItems, kBits, false>), dim3(nb), dim3(kThreads), 0, s, src_k, src_v, n, n_dev,
+                         shift, nb, hist, tot, dk, dv, static_cast<uint64_t*>(nullptr),
+                         static_cast<const float*>(nullptr), 0u, 0u);
     src_k = dk;
     src_v = dv;
   }
@@ -283,54 +293,63 @@ uint32_t sort_passes(uint32_t key_bits) {
 // The first destination must differ from keys_in: with an even pass count keys_in may be keys_out, with an odd
 // one keys_in may be tmp.
 namespace {
+// With n_dev, n is a capacity and the launches sort *n_dev keys (none when *n_dev > n).
 template <typename K>
 gsr_status sort_any(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint32_t* vals_in, uint64_t n,
-                    uint32_t key_bits, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals,
-                    FinalKeys fin) {
+                    const uint64_t* n_dev, uint32_t key_bits, K* keys_out, uint32_t* vals_out, K* tmp_keys,
+                    uint32_t* tmp_vals, FinalKeys fin) {
   if (n == 0) return GSR_OK;
   const uint32_t passes = sort_passes(key_bits);
   if (key_bits <= kNarrowKeyBits) {
     if (n < kSmallSort)
-      return run_passes<K, 4, 6>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals, fin);
-    return run_passes<K, kLargeItems, 6>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals,
-                                         fin);
+      return run_passes<K, 4, 6>(ctx, s, keys_in, vals_in, n, n_dev, passes, keys_out, vals_out, tmp_keys, tmp_vals,
+                                 fin);
+    return run_passes<K, kLargeItems, 6>(ctx, s, keys_in, vals_in, n, n_dev, passes, keys_out, vals_out, tmp_keys,
+                                         tmp_vals, fin);
   }
   if (n < kSmallSort)
-    return run_passes<K, 4, 8>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals, fin);
-  return run_passes<K, kLargeItems, 8>(ctx, s, keys_in, vals_in, n, passes, keys_out, vals_out, tmp_keys, tmp_vals,
-                                       fin);
+    return run_passes<K, 4, 8>(ctx, s, keys_in, vals_in, n, n_dev, passes, keys_out, vals_out, tmp_keys, tmp_vals,
+                               fin);
+  return run_passes<K, kLargeItems, 8>(ctx, s, keys_in, vals_in, n, n_dev, passes, keys_out, vals_out, tmp_keys,
+                                       tmp_vals, fin);
 }
 }  // namespace
 
 template <typename K>
 gsr_status radix_sort_launch(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint32_t* vals_in, uint64_t n,
-                             uint32_t key_bits, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals) {
-  return sort_any<K>(ctx, s, keys_in, vals_in, n, key_bits, keys_out, vals_out, tmp_keys, tmp_vals, FinalKeys{});
+                             uint32_t key_bits, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals,
+                             const uint64_t* n_dev) {
+  return sort_any<K>(ctx, s, keys_in, vals_in, n, n_dev, key_bits, keys_out, vals_out, tmp_keys, tmp_vals,
+                     FinalKeys{});
 }
 
 gsr_status radix_sort_tiles_final(gsr_ctx* ctx, hipStream_t s, const uint32_t* keys_in, const uint32_t* vals_in,
                                   uint64_t n, uint32_t key_bits, uint32_t* keys_out, uint32_t* vals_out,
                                   uint32_t* tmp_keys, uint32_t* tmp_vals, uint64_t* keys_final,
-                                  const float* depths, uint32_t n_depths) {
+                                  const float* depths, uint32_t n_depths, const uint64_t* n_dev) {
   if (key_bits == 0) return fail(ctx, GSR_EINVAL, "radix sort: final keys need at least one pass");
-  return sort_any<uint32_t>(ctx, s, keys_in, vals_in, n, key_bits, keys_out, vals_out, tmp_keys, tmp_vals,
+  return sort_any<uint32_t>(ctx, s, keys_in, vals_in, n, n_dev, key_bits, keys_out, vals_out, tmp_keys, tmp_vals,
                             FinalKeys{keys_final, depths, n_depths});
 }
 
 gsr_status radix_sort_tiles_packed(gsr_ctx* ctx, hipStream_t s, const uint32_t* keys_in, uint64_t n,
                                    uint32_t idx_bits, uint32_t tile_bits, uint32_t* keys_out, uint32_t* tmp_keys,
-                                   uint32_t* vals_out, uint64_t* keys_final, const float* depths, uint32_t n_depths) {
+                                   uint32_t* vals_out, uint64_t* keys_final, const float* depths,
+                                   uint32_t n_depths, const uint64_t* n_dev) {
   if (tile_bits == 0 || idx_bits + tile_bits > 32)
     return fail(ctx, GSR_EINVAL, "radix sort: packed keys need 1..32 - idx_bits tile bits");
   if (!vals_out) return fail(ctx, GSR_EINVAL, "radix sort: packed keys need a value output");
   FinalKeys fin{keys_final, depths, n_depths, true, idx_bits};
-  return sort_any<uint32_t>(ctx, s, keys_in, nullptr, n, tile_bits, keys_out, vals_out, tmp_keys, nullptr, fin);
+  return sort_any<uint32_t>(ctx, s, keys_in, nullptr, n, n_dev, tile_bits, keys_out, vals_out, tmp_keys, nullptr,
+                            fin);
 }
 
 template gsr_status radix_sort_launch<uint32_t>(gsr_ctx*, hipStream_t, const uint32_t*, const uint32_t*, uint64_t,
-                                                uint32_t, uint32_t*, uint32_t*, uint32_t*, uint32_t*);
+                                                uint32_t, uint32_t*, uint32_t*, uint32_t*, uint32_t*,
+                                                const uint64_t*);
 template gsr_status radix_sort_launch<uint64_t>(gsr_ctx*, hipStream_t, const uint64_t*, const uint32_t*, uint64_t,
-                                                uint32_t, uint64_t*, uint32_t*, uint64_t*, uint32_t*);
+                                                uint32_t, uint64_t*, uint32_t*, uint64_t*, uint32_t*,
+                                                const uint64_t*);
 
 }  // namespace gsr
 

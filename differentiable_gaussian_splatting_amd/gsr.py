@@ -25,6 +25,7 @@ GSR_OPT_KERNEL_TIMING = 6
 GSR_OPT_BACKWARD_SCHEME, GSR_BACKWARD_PER_PIXEL, GSR_BACKWARD_PER_SPLAT = 7, 0, 1
 GSR_OPT_ARENA_LIMIT = 8
 GSR_OPT_TILE_ORDER, GSR_ORDER_COST, GSR_ORDER_LENGTH, GSR_ORDER_NONE = 9, 0, 1, 2
+GSR_OPT_BIN_SYNC_FREE = 10
 (GSR_STAGE_BIN, GSR_STAGE_FORWARD, GSR_STAGE_BACKWARD, GSR_STAGE_ADAM, GSR_STAGE_PROJECT_FORWARD,
  GSR_STAGE_PROJECT_BACKWARD, GSR_STAGE_LOSS, GSR_STAGE_DEPTH_SORT, GSR_STAGE_TILE_SORT) = range(9)
 GSR_ADAM_MAX_GROUPS = 8
@@ -71,6 +72,7 @@ SIGNATURES = {
     "gsr_reserve": (_I32, [_P, _U64, _U32]),
     "gsr_set_option": (_I32, [_P, _I32, _I64]),
     "gsr_bin": (_I32, [_P, _P, _P, _P, _U32, _U32, _U32, ctypes.POINTER(gsr_bins)]),
+    "gsr_bin_pair_count": (_I32, [_P, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_int32)]),
     "gsr_bins_copy": (_I32, [_P, _P, ctypes.POINTER(gsr_bins), _P, _P, _P, _P]),
     "gsr_radix_sort": (_I32, [_P, _P, _P, _P, _U64, _U32, _P, _P]),
     "gsr_radix_pass_count": (_U32, [_U64, _U32]),
@@ -206,6 +208,13 @@ def gsr_bin(ctx: Context, splats: torch.Tensor, depths: torch.Tensor, width: int
     ctx.check(load().gsr_bin(ctx.handle, _stream(stream), _ptr(splats), _ptr(depths), n, width, height,
                              ctypes.byref(raw)), "gsr_bin")
     return Bins(raw, (ctx,))
+
+
+def gsr_bin_pair_count(ctx: Context) -> tuple[int, bool]:
+    """(pairs, overflowed) of the context's last gsr_bin, waiting for the count if that call did not."""
+    pairs, over = ctypes.c_uint64(0), ctypes.c_int32(0)
+    ctx.check(load().gsr_bin_pair_count(ctx.handle, ctypes.byref(pairs), ctypes.byref(over)), "gsr_bin_pair_count")
+    return int(pairs.value), bool(over.value)
 
 
 def bins_from_tensors(keys: torch.Tensor | None, vals: torch.Tensor, ranges: torch.Tensor, width: int,

@@ -108,6 +108,14 @@ gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats);
                               /*   anything that needs the growth, and the arena keeps its buffers and contents   */
                               /*   (a device-memory budget; also how failure handling is tested from the host).   */
                               /*   Lowering it frees nothing already held.                                       */
+#define GSR_OPT_BIN_SYNC_FREE 10 /* 0 (default): gsr_bin waits once for the pair count and sizes its buffers to it;   */
+                                /*   1: gsr_bin queues everything without waiting, its buffers sized for a capacity  */
+                                /*   (the largest of 2^16, 16 n, 1.5 times the largest count seen and gsr_reserve's */
+                                /*   pairs [C0 resident arena + C1 pass skip page, section 2 table, row "C0"]); its */
+                                /*   kernels read the count from device memory. Identical results when the pairs    */
+                                /*   fit; when they do not, nothing is emitted, every tile's range is empty and     */
+                                /*   gsr_bin_pair_count reports the overflow (binning again then fits). A call with */
+                                /*   no count seen yet and no reservation still waits once.                         */
 gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value);
 
 /* Stages timed by GSR_OPT_KERNEL_TIMING, each the kernels between its pair of events. */
@@ -153,10 +161,20 @@ typedef struct gsr_bins {
  *   out     host struct filled with views into the arena (valid until the context's next gsr_bin), including
  *           splat_pairs: the number of pairs each splat emitted (0 for a culled or off-image splat).
  * Synchronisation: waits on `stream` once, to read the pair count before sizing the arena; the rest is queued.
+ *   With GSR_OPT_BIN_SYNC_FREE it does not wait: out->num_pairs is then the capacity the buffers were sized for
+ *   (the ranges hold the exact runs; keys and vals past the last pair are unspecified), and gsr_bin_pair_count
+ *   gives the count.
  * Errors: GSR_EINVAL (null pointers with n > 0, width or height 0, tiles_x * tiles_y >= 2^32),
  * GSR_EOVERFLOW (2^32 or more pairs), GSR_ENOMEM, GSR_EHIP. */
 gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, const float* depths, uint32_t n,
                    uint32_t width, uint32_t height, gsr_bins* out);
+
+/* The pair count of the context's last gsr_bin, waiting for it when that call did not (GSR_OPT_BIN_SYNC_FREE).
+ * *overflowed = 1 when those pairs exceeded the capacity that call was sized for (it then emitted nothing; the
+ * next gsr_bin sizes its buffers for at least this count), else 0. [C0 resident arena + C1 pass skip page,
+ * section 2 table, row "C0": overflow means growing the arena and emitting again]
+ * Errors: GSR_EINVAL (null pointers), GSR_EHIP. */
+gsr_status gsr_bin_pair_count(gsr_ctx* ctx, uint64_t* num_pairs, int32_t* overflowed);
 
 /* Copies the contents of `bins` into caller buffers (device pointers; any of them may be NULL to skip it):
  * keys [num_pairs] uint64, vals [num_pairs] uint32, ranges [2 * tiles] uint32, splat_pairs [num_splats] uint32.

@@ -1,0 +1,140 @@
+"""gsr_bin without its wait for the pair count (GSR_OPT_BIN_SYNC_FREE) against the oracle.
+
+Sync-free, the pair buffers are sized for a capacity (the larger of 2^16, 16 pairs per splat and 1.5 times the
+largest count seen, or a reservation) and the kernels read the count from device memory. When the pairs fit, the
+bins must equal the oracle's bit for bit; when they do not, nothing is emitted, every tile's range is empty,
+gsr_bin_pair_count reports the overflow, and the next call fits. [C0 resident arena + C1 pass skip page, section 2
+table, row "C0": capacity from the previous iteration's count, overflow grows the arena and emits again]
+"""
+import numpy as np
+import pytest
+
+from gpuhelp import banner, custom_scene, dev, host, oracle_bins, scene
+
+pytestmark = pytest.mark.gpu
+
+
+def new_ctx(scheme=0, rule=0):
+    from differentiable_gaussian_splatting_amd import gsr
+    c = gsr.Context(0)
+    gsr.gsr_set_option(c, gsr.GSR_OPT_BIN_SCHEME, scheme)
+    gsr.gsr_set_option(c, gsr.GSR_OPT_BIN_RULE, rule)
+    gsr.gsr_set_option(c, gsr.GSR_OPT_BIN_SYNC_FREE, 1)
+    return c
+
+
+def bin_and_compare(ctx, splats, depths, w, h, ref):
+    """Bins sync-free and checks the first count pairs and the ranges against ref; returns the bins."""
+    from differentiable_gaussian_splatting_amd import gsr
+    b = gsr.gsr_bin(ctx, dev(splats), dev(depths), w, h)
+    pairs, over = gsr.gsr_bin_pair_count(ctx)
+    assert (pairs, over) == (ref.num_pairs, False)
+    assert b.num_pairs >= pairs  # the capacity
+    keys, vals, ranges = gsr.gsr_bins_copy(ctx, b)
+    P = ref.num_pairs
+    if keys is not None:
+        assert np.array_equal(host(keys, np.uint64)[:P], ref.keys), "sorted keys differ"
+    assert np.array_equal(host(vals, np.uint32)[:P], ref.vals), "sorted values differ"
+    assert np.array_equal(host(ranges, np.uint32), ref.ranges), "tile ranges differ"
+    return b
+
+
+@pytest.mark.parametrize("scheme,rule", [(0, 0), (1, 0), (0, 1)])
+def test_sync_free_bins_equal_the_oracle(scheme, rule):
+    """First call on a fresh context: no count seen, so it waits once; the later calls size their buffers from the
+    counts seen (smaller scenes after a larger one, and the same scene again) and do not wait."""
+    import oracle
+    banner(f"bin sync-free scheme={scheme} rule={rule}")
+    ctx = new_ctx(scheme, rule)
+    try:
+        for name in ("raster84k", "tiny", "raster84k"):
+            sc = scene(name)
+            ref = oracle_bins(name) if rule == 0 else oracle.bin(sc.splats, sc.depths, sc.width, sc.height,
+                                                                  rule="ellipse")
+            bin_and_compare(ctx, sc.splats, sc.depths, sc.width, sc.height, ref)
+        # ragged image and a small scene on a capacity sized for a large one
+        sc = custom_scene(name="ragged", width=100, height=37, n=3000, seed=11, size_classes=((1.0, 0.3, 30.0),),
+                          margin=40.0)
+        ref = oracle.bin(sc.splats, sc.depths, 100, 37, rule="ellipse" if rule else "box")
+        bin_and_compare(ctx, sc.splats, sc.depths, 100, 37, ref)
+    finally:
+        ctx.close()
+
+
+def test_sync_free_unpacked_tile_sort():
+    """2^23 tiles with 3000 splats: the tile id and the splat rank do not fit one 32-bit key (the two-array form)."""
+    import oracle
+    banner("bin sync-free unpacked 65536x32768")
+    rng = np.random.default_rng(5)
+    n, w, h = 3000, 65536, 32768
+    s = np.exp(rng.uniform(np.log(0.5), np.log(20.0), n))
+    sp = np.zeros((n, 9), np.float32)
+    sp[:, 0], sp[:, 1] = rng.uniform(0, w, n), rng.uniform(0, h, n)
+    sp[:, 2] = sp[:, 4] = 1.0 / s ** 2
+    sp[:, 5:8] = rng.uniform(0, 1, (n, 3))
+    sp[:, 8] = rng.uniform(0.05, 1.0, n)
+    depths = rng.uniform(0.1, 10.0, n).astype(np.float32)
+    ref = oracle.bin(sp, depths, w, h)
+    ctx = new_ctx()
+    try:
+        bin_and_compare(ctx, sp, depths, w, h, ref)  # waits (no count seen)
+        bin_and_compare(ctx, sp, depths, w, h, ref)  # sync-free
+    finally:
+        ctx.close()
+
+
+def test_overflow_empties_the_ranges_and_the_next_call_fits():
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("bin sync-free overflow")
+    ctx = new_ctx()
+    try:
+        tiny = scene("tiny")
+        bin_and_compare(ctx, tiny.splats, tiny.depths, tiny.width, tiny.height, oracle_bins("tiny"))
+        # raster410k has 6.87 M pairs, more than 16 per splat (6.56 M) and far more than 1.5 times tiny's count
+        big = scene("raster410k")
+        ref = oracle_bins("raster410k")
+        assert ref.num_pairs > 16 * big.spec.n
+        sp, d = dev(big.splats), dev(big.depths)
+        b = gsr.gsr_bin(ctx, sp, d, big.width, big.height)
+        pairs, over = gsr.gsr_bin_pair_count(ctx)
+        assert pairs == ref.num_pairs and over
+        assert b.num_pairs < pairs
+        _, _, ranges = gsr.gsr_bins_copy(ctx, b)
+        r = host(ranges, np.uint32)
+        assert (r[:, 0] == r[:, 1]).all(), "an overflowed call must leave every range empty"
+        # the raster kernels see empty tiles: the background everywhere
+        out, ft, lc = gsr.gsr_render_forward(ctx, sp, b, big.width, big.height)
+        assert (host(out) == np.array([0, 0, 0, 0], np.float32)).all() and (host(ft) == 1).all()
+        assert (host(lc) == 0).all()
+        # the count seen sizes the next call
+        bin_and_compare(ctx, big.splats, big.depths, big.width, big.height, ref)
+    finally:
+        ctx.close()
+
+
+def test_reservation_sizes_the_first_call():
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("bin sync-free reserved")
+    ctx = new_ctx()
+    try:
+        sc = scene("raster84k")
+        ref = oracle_bins("raster84k")
+        gsr.gsr_reserve(ctx, ref.num_pairs, sc.spec.n)
+        b = bin_and_compare(ctx, sc.splats, sc.depths, sc.width, sc.height, ref)
+        assert b.num_pairs == max(ref.num_pairs, 1 << 16, 16 * sc.spec.n)  # sized without a wait
+    finally:
+        ctx.close()
+
+
+def test_sync_mode_reports_its_count():
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("bin count after a waiting call")
+    c = gsr.Context(0)
+    try:
+        sc = scene("tiny")
+        b = gsr.gsr_bin(c, dev(sc.splats), dev(sc.depths), sc.width, sc.height)
+        assert gsr.gsr_bin_pair_count(c) == (b.num_pairs, False) == (oracle_bins("tiny").num_pairs, False)
+        b = gsr.gsr_bin(c, dev(sc.splats[:0]), dev(sc.depths[:0]), sc.width, sc.height)
+        assert gsr.gsr_bin_pair_count(c) == (0, False)
+    finally:
+        c.close()
