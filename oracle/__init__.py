@@ -62,9 +62,11 @@ def _load():
     lib.oracle_render_forward_f32_mt.argtypes = [P, P, P, u32, u32, P, P, P, u32]
     lib.oracle_render_backward_f32_mt.argtypes = [P, u32, P, P, u32, u32, P, P, P, P, P, u32]
     lib.oracle_trace_pixel_f32.argtypes = [P, P, P, u32, u32, u32, u32, u32, P, P, P, P, P]
+    lib.oracle_trace_candidates_f32.argtypes = [P, P, P, u32, u32, u32, u32, u32, P, P, P, P]
     for name in ("oracle_bin_count", "oracle_tile_rect", "oracle_bin", "oracle_sort_pairs",
                  "oracle_render_forward_f32", "oracle_render_forward_f64", "oracle_render_backward_f32",
-                 "oracle_render_backward_f64", "oracle_adam_step", "oracle_trace_pixel_f32"):
+                 "oracle_render_backward_f64", "oracle_adam_step", "oracle_trace_pixel_f32",
+                 "oracle_trace_candidates_f32"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -276,3 +278,21 @@ def trace_pixel(splats, bins: Bins, width: int, height: int, px: int, py: int, m
     if j < 0:
         raise ValueError("pixel outside the image")
     return {"code": code[:j], "sigma": sig[:j], "alpha": al[:j], "T_before": tb[:j], "T_after": ta[:j]}
+
+
+def trace_candidates(splats, bins: Bins, width: int, height: int, px: int, py: int):
+    """One pixel's compositing candidates with the stop test left out (oracle_trace_candidates_f32): dict of
+    arrays pos (1-based list position), alpha, T_next (T (1 - alpha)) and rgb [m, 3] (the colour once composited).
+    The forward stops at the first candidate whose T_next is below 1e-4."""
+    lib = _load()
+    s = _c(splats, np.float32).reshape(-1, 9)
+    t = (py // 16) * bins.tiles_x + (px // 16)
+    n = int(bins.ranges[t, 1] - bins.ranges[t, 0])
+    pos = np.zeros(n, np.uint32)
+    al, tn = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    rgb = np.zeros((n, 3), np.float32)
+    j = lib.oracle_trace_candidates_f32(_ptr(s), _ptr(_c(bins.vals, np.uint32)), _ptr(_c(bins.ranges, np.uint32)),
+                                        width, height, px, py, n, _ptr(pos), _ptr(al), _ptr(tn), _ptr(rgb))
+    if j < 0:
+        raise ValueError("pixel outside the image")
+    return {"pos": pos[:j], "alpha": al[:j], "T_next": tn[:j], "rgb": rgb[:j]}

@@ -632,4 +632,41 @@ int oracle_trace_pixel_f32(const float* splats, const uint32_t* vals, const uint
   return int(j);
 }
 
+// One pixel's compositing candidates with the stop test left out, for judging stop decisions taken on a transmittance
+// that carries rounding error: every entry of the tile's list that passes the sigma and alpha tests, in list order,
+// composited as the forward composites (T' = T (1 - alpha), colour += rgb alpha T) whatever T' is. For candidate
+// j < max_len: pos[j] (its 1-based list position, the value last_contrib takes when it is the last one composited),
+// alpha[j], T_next[j] = T' and rgb[3 j .. 3 j + 2], the colour once it is composited. The forward stops at the first
+// candidate whose T_next is below 1e-4. Returns the number of candidates written.
+int oracle_trace_candidates_f32(const float* splats, const uint32_t* vals, const uint32_t* ranges, uint32_t width,
+                                uint32_t height, uint32_t px, uint32_t py, uint32_t max_len, uint32_t* pos,
+                                float* alpha, float* T_next, float* rgb) {
+  if (px >= width || py >= height) return -1;
+  using C = Consts<float>;
+  const uint32_t tiles_x = (width + kTile - 1) / kTile;
+  const uint32_t t = (py / kTile) * tiles_x + (px / kTile);
+  const float cx = float(px) + C::half, cy = float(py) + C::half;
+  float T = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f;
+  uint32_t j = 0;
+  for (uint32_t k = ranges[2 * t]; k < ranges[2 * t + 1] && j < max_len; ++k) {
+    const Splat<float> s = load_splat(splats, vals[k]);
+    const Eval<float> e = evaluate(s, cx, cy);
+    if (e.d != kComposite) continue;
+    const float next_T = T * (1.0f - e.alpha);
+    const float w = e.alpha * T;
+    cr = cr + s.r * w;
+    cg = cg + s.g * w;
+    cb = cb + s.bl * w;
+    T = next_T;
+    pos[j] = k - ranges[2 * t] + 1;
+    alpha[j] = e.alpha;
+    T_next[j] = next_T;
+    rgb[3 * j] = cr;
+    rgb[3 * j + 1] = cg;
+    rgb[3 * j + 2] = cb;
+    ++j;
+  }
+  return int(j);
+}
+
 }  // extern "C"

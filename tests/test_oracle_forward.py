@@ -207,3 +207,29 @@ def test_output_sizes_match_the_pages():
     g = load("layout_sizes.txt")
     assert ((g["image_width"] + 15) // 16) * ((g["image_height"] + 15) // 16) == g["tile_offsets"]
     assert 9 * 4 == g["splat2d_bytes"] and 16 + 4 + 4 == g["forward_output_bytes_per_pixel"]
+
+
+@pytest.mark.parametrize("which", ["tiny_scene", "dense_scene"])
+def test_candidate_trace_truncated_at_the_stop_is_the_forward(orc, request, which):
+    """The stop-free candidate trace, cut at its first T' < 1e-4, reproduces the forward bit for bit: last_contrib
+    is the position of the candidate before it, final T and the colour are that candidate's (or 1 and 0 with no
+    candidate), and every candidate before the cut has T' >= 1e-4."""
+    sc, b, out, ft, lc, st = request.getfixturevalue(which)
+    rng = np.random.default_rng(1)
+    W, H = sc.width, sc.height
+    pix = [(int(rng.integers(W)), int(rng.integers(H))) for _ in range(300)] + [(W - 1, H - 1), (0, 0)]
+    stopped = 0
+    for (px, py) in pix:
+        tr = orc.trace_candidates(sc.splats, b, W, H, px, py)
+        below = np.flatnonzero(tr["T_next"] < np.float32(1e-4))
+        cut = int(below[0]) if len(below) else len(tr["pos"])
+        stopped += len(below) > 0
+        assert np.all(np.diff(tr["T_next"]) <= 0) and np.all(np.diff(tr["pos"].astype(np.int64)) > 0)
+        if cut == 0:
+            assert lc[py, px] == 0 and ft[py, px] == 1 and np.all(out[py, px, :3] == 0)
+        else:
+            assert lc[py, px] == tr["pos"][cut - 1]
+            assert ft[py, px] == tr["T_next"][cut - 1]
+            assert np.array_equal(out[py, px, :3], tr["rgb"][cut - 1])
+    if which == "dense_scene":
+        assert stopped > 50  # the cut is exercised
