@@ -285,6 +285,7 @@ def main():
     P = b.num_pairs
     e_bwd_gpu = int(last_contrib.to(torch.int64).sum().item())
     sync_free = bench_sync_free(args, ctx, gsr, torch, np, step, b, walls)
+    fast_exp = bench_fast_exp_forward(args, ctx, gsr, torch, np, splats, b, W, H, out_rgba, final_T, last_contrib)
     det = bench_deterministic_backward(args, ctx, gsr, torch, np, stream, splats, b, W, H, out_rgba, final_T,
                                        last_contrib, v_out, grad)
     per_splat = bench_per_splat_backward(args, ctx, gsr, torch, np, splats, b, W, H, out_rgba, final_T,
@@ -319,6 +320,8 @@ def main():
     det["kernel_ratio_to_default"] = det["kernel_ms"] / kernel_ms["backward"]
     result["deterministic_backward"] = det
     result["sync_free_bin"] = sync_free
+    fast_exp["kernel_ratio_to_exact"] = fast_exp["kernel_ms"] / kernel_ms["forward"]
+    result["forward_fast_exp"] = fast_exp
     per_splat["kernel_ratio_to_default"] = per_splat["kernel_ms"] / kernel_ms["backward"]
     result["per_splat_backward"] = per_splat
     if cpu is not None:
@@ -374,7 +377,17 @@ def main():
                 mcyc = profiling.mfma_busy_for(profiling.STAGE_KERNEL[k], traffic_md)
                 r["mfma_busy_frac"] = (None if mcyc is None else
                                        mcyc / (r["kernel_ms"] * 1e-3 * 1024 * 2.4e9))
-        for k in ("forward", "backward"):
+        # the forward with the hardware exponential (GSR_OPT_FORWARD_EXP), the same operation count
+        kf = fast_exp["kernel_ms"]
+        roofs["forward_fast_exp"] = {"bound": "alu", "achieved": fwd_ops / (kf * 1e-3) / 1e12, "peak": ALU_PEAK_TFLOPS,
+                                     "unit": "TFLOP/s", "work_per_launch": fwd_ops, "achieved_kind": eff,
+                                     "kernel_ms": kf, "frac": fwd_ops / (kf * 1e-3) / 1e12 / ALU_PEAK_TFLOPS,
+                                     "traffic": profiling.traffic_for(profiling.STAGE_KERNEL["forward_fast_exp"],
+                                                                      traffic_md)}
+        insts = profiling.valu_insts_for(profiling.STAGE_KERNEL["forward_fast_exp"], traffic_md)
+        roofs["forward_fast_exp"]["valu_insts_per_launch"] = insts
+        roofs["forward_fast_exp"]["valu_issue_frac"] = None if insts is None else insts / (kf * 1e-3 * VALU_ISSUE_PER_S)
+        for k in ("forward", "backward", "forward_fast_exp"):
             roofs[k]["frac_of_nonpacked_78_6"] = roofs[k]["achieved"] / ALU_NONPACKED_TFLOPS
         dominant = max(("forward", "backward", "adam"), key=lambda k: kernel_ms[k])
         result["roofline"] = {"kernel": dominant, **roofs[dominant]}
@@ -578,6 +591,32 @@ def bench_changing_views(args, ctx, gsr, scenes, torch, np):
     res["pairs_first_last"] = [pairs[0], pairs[-1]]
     res["gain_of_cost_order_vs_length"] = {k: res["length"][k] / res["cost"][k] for k in ("forward", "backward")}
     return res
+
+
+def bench_fast_exp_forward(args, ctx, gsr, torch, np, splats, b, W, H, out_rgba, final_T, last_contrib):
+    """The forward with the hardware exponential (GSR_OPT_FORWARD_EXP = GSR_EXP_FAST) on the last step's bins:
+    its kernel's time from the library's events over K launches per repeat (the median of the repeats' means), and
+    how far its outputs are from the exact forward's: pixels whose last contributor differs, and the largest image
+    difference elsewhere."""
+    print("[bench] forward with the hardware exponential", file=sys.stderr, flush=True)
+    o2, t2, l2 = torch.empty_like(out_rgba), torch.empty_like(final_T), torch.empty_like(last_contrib)
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_FORWARD_EXP, gsr.GSR_EXP_FAST)
+    reps = []
+    try:
+        for _ in range(args.repeats):
+            gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, args.steps)
+            for _ in range(args.steps):
+                gsr.gsr_render_forward(ctx, splats, b, W, H, o2, t2, l2)
+            reps.append(float(np.mean(gsr.gsr_kernel_times(ctx, gsr.GSR_STAGE_FORWARD))))
+            gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, 0)
+    finally:
+        gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, 0)
+        gsr.gsr_set_option(ctx, gsr.GSR_OPT_FORWARD_EXP, gsr.GSR_EXP_EXACT)
+    same = l2 == last_contrib
+    d_img = float((o2 - out_rgba).abs().amax(dim=-1)[same].max().item()) if bool(same.any()) else 0.0
+    return {"kernel_ms": float(np.median(reps)), "repeats": reps, "sigma": float(np.std(reps)),
+            "pixels_stopping_apart_from_exact": int((~same).sum().item()),
+            "max_image_diff_elsewhere": d_img}
 
 
 def bench_sync_free(args, ctx, gsr, torch, np, step, bins_sync, walls_sync):

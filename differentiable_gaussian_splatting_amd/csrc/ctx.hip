@@ -238,6 +238,11 @@ gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value) {
       if (value < 0) return fail(ctx, GSR_EINVAL, "gsr_set_option: the arena limit must be >= 0");
       ctx->arena.limit = size_t(value);
       return GSR_OK;
+    case GSR_OPT_FORWARD_EXP:
+      if (value != GSR_EXP_EXACT && value != GSR_EXP_FAST)
+        return fail(ctx, GSR_EINVAL, "gsr_set_option: unknown forward exponential %lld", (long long)value);
+      ctx->forward_exp = int32_t(value);
+      return GSR_OK;
     case GSR_OPT_BIN_SYNC_FREE:
       if (value != 0 && value != 1) return fail(ctx, GSR_EINVAL, "gsr_set_option: bin sync-free must be 0 or 1");
       ctx->bin_sync_free = value != 0;

@@ -65,6 +65,7 @@ struct gsr_ctx {
   bool deterministic = false;  // backward sums independent of scheduling (fixed-point atomics)
   int32_t backward_scheme = GSR_BACKWARD_PER_PIXEL;
   int32_t tile_order = GSR_ORDER_COST;  // how raster_tile_order ranks the tiles
+  int32_t forward_exp = GSR_EXP_EXACT;  // the forward's exponential (GSR_OPT_FORWARD_EXP)
   // GSR_OPT_BIN_SYNC_FREE, and the pair counts it sizes its buffers from
   bool bin_sync_free = false;
   bool pairs_pending = false;  // the last gsr_bin's count is still on its way to the pinned word

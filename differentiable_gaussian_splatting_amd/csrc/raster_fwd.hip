@@ -15,7 +15,11 @@ namespace {
 
 // kCull: each wave walks only the staged splats that can reach alpha >= 1/255 in its 8x8 block (reach_mask); the
 // others are certain rejects for every lane of the wave, so skipping them changes no result.
-template <bool kCull>
+// kExact: exp(-sigma) correctly rounded (fp64 series), so T and every stop decision are those of a plain fp32
+// evaluation; otherwise the hardware exponential with the exact value only near the alpha thresholds (evaluate's
+// fast form, the backward's): reject and clamp decisions are still exact, T carries the fast value's error (below
+// 1e-6 relative per splat), so a pixel whose exact T' lies that close to 1e-4 may stop one splat apart.
+template <bool kCull, bool kExact>
 __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict__ splats, uint32_t n,
                                                          const uint32_t* __restrict__ vals,
                                                          const uint32_t* __restrict__ ranges, uint32_t num_pairs,
@@ -26,12 +30,15 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
                                                          uint32_t* __restrict__ tile_cost) {
   constexpr uint32_t kWaves = kTilePixels / kWave;
   __shared__ StagedSplat s_sp[kTilePixels];
-  __shared__ double s_exp2[2 * kExpTabN];  // 2^(-k/32) table of the exact exponential
+  __shared__ double s_exp2[kExact ? 2 * kExpTabN : 64];  // the exponential's table (exp_neg_rn's or exp_rn's)
   __shared__ uint64_t s_mask[kWaves][kWaves];  // [reading wave][staging wave]: slots that can reach the reader
   const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const uint32_t tile = tile_order[blockIdx.x];  // slowest expected first (a permutation of the tiles)
   if (tile >= num_tiles) return;                 // not reachable with a permutation; keeps reads in bounds
-  load_exp_neg_table(s_exp2);                    // the first batch barrier orders it
+  if constexpr (kExact)
+    load_exp_neg_table(s_exp2);  // the first batch barrier orders it
+  else
+    load_exp_table(s_exp2);
   const uint32_t tx0 = (tile % tiles_x) * kTile, ty0 = (tile / tiles_x) * kTile;
   const uint32_t px = tx0 + lane_px(w, lane), py = ty0 + lane_py(w, lane);
   const bool inside = px < width && py < height;
@@ -80,7 +87,7 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
         asm volatile("" ::"v"(s.o));
         ++walked;
         Eval e;
-        if (evaluate<true>(s, cxe, cy, e, s_exp2)) {
+        if (evaluate<kExact>(s, cxe, cy, e, s_exp2)) {
           float alpha = e.alpha;
           float next_T = T * (1.0f - alpha);
           // A pixel that would fall below the stop threshold here does not composite this splat and stops. Rare
@@ -129,6 +136,16 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
 constexpr uint32_t kNoAllocMaxTiles = 65536;
 __device__ __align__(256) uint32_t scratch[5 * kNoAllocMaxTiles];
 
+using ForwardKernel = void (*)(const float*, uint32_t, const uint32_t*, const uint32_t*, uint32_t, uint32_t, uint32_t,
+                               uint32_t, float4*, float*, uint32_t*, const uint32_t*, uint32_t, uint32_t*);
+
+// The forward kernel the context's options select (GSR_OPT_RASTER_SKIP, GSR_OPT_FORWARD_EXP).
+ForwardKernel forward_kernel(const gsr_ctx* ctx) {
+  const bool exact = ctx->forward_exp == GSR_EXP_EXACT;
+  if (ctx->raster_skip) return exact ? k_forward<true, true> : k_forward<true, false>;
+  return exact ? k_forward<false, true> : k_forward<false, false>;
+}
+
 }  // namespace
 
 gsr_status noalloc_setup(gsr_ctx* ctx) {
@@ -165,11 +182,11 @@ extern "C" gsr_status gsr_render_forward(gsr_ctx* ctx, void* stream, const float
   if (!order) return st;
   // the walk lengths of this forward rank the tiles of the next raster launch on this grid
   if ((st = grow(ctx, ctx->arena.tile_cost, size_t(num_tiles) * 16))) return st;
-  auto kernel = ctx->raster_skip ? k_forward<true> : k_forward<false>;
   timing_mark(ctx, GSR_STAGE_FORWARD, s, false);
-  hipLaunchKernelGGL(kernel, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, s, splats, n, bins->vals,
+  hipLaunchKernelGGL(forward_kernel(ctx), dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, s, splats, n, bins->vals,
                      bins->ranges, bins->num_pairs, tiles_x, width, height, reinterpret_cast<float4*>(out_rgba),
-                     final_T, last_contrib, order, uint32_t(num_tiles), static_cast<uint32_t*>(ctx->arena.tile_cost.ptr));
+                     final_T, last_contrib, order, uint32_t(num_tiles),
+                     static_cast<uint32_t*>(ctx->arena.tile_cost.ptr));
   timing_mark(ctx, GSR_STAGE_FORWARD, s, true);
   if ((st = check_launch(ctx, "gsr_render_forward"))) return st;
   ctx->cost_tiles = num_tiles;
@@ -203,9 +220,8 @@ extern "C" gsr_status gsr_render_forward_noalloc(gsr_ctx* ctx, void* stream, con
   // hold; the order changes no result), then render; this forward leaves its own counts for the next one.
   launch_tile_order(s, bins->ranges, ctx->tile_order == GSR_ORDER_COST ? cost : nullptr, uint32_t(num_tiles),
                     bins->num_pairs, order, ctx->tile_order == GSR_ORDER_NONE);
-  auto kernel = ctx->raster_skip ? k_forward<true> : k_forward<false>;
   timing_mark(ctx, GSR_STAGE_FORWARD, s, false);
-  hipLaunchKernelGGL(kernel, dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, s, splats, n, bins->vals,
+  hipLaunchKernelGGL(forward_kernel(ctx), dim3(uint32_t(num_tiles)), dim3(kTilePixels), 0, s, splats, n, bins->vals,
                      bins->ranges, bins->num_pairs, tiles_x, width, height, reinterpret_cast<float4*>(out_rgba),
                      final_T, last_contrib, static_cast<const uint32_t*>(order), uint32_t(num_tiles), cost);
   timing_mark(ctx, GSR_STAGE_FORWARD, s, true);

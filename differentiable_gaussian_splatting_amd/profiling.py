@@ -43,8 +43,9 @@ KERNEL_SOURCES = {
     "k_scatter": ["sort.hip", "scan_common.hpp", "gsr_internal.hpp"],
 }
 # bench.py stage -> the kernel instance its default configuration launches (template arguments as rocprofv3
-# prints them: the raster kernels with the skips on, the dense Adam)
-STAGE_KERNEL = {"forward": "k_forward<true>", "backward": "k_backward<true>",
+# prints them: the raster kernels with the skips on, the exact forward exponential, the dense Adam)
+STAGE_KERNEL = {"forward": "k_forward<true,true>", "forward_fast_exp": "k_forward<true,false>",
+                "backward": "k_backward<true>",
                 "backward_deterministic": "k_backward_det<true>", "backward_per_splat": "k_backward_splat<true,false>",
                 "adam": "k_adam<false>",
                 "adam_visible": "k_adam<true>", "project_forward": "k_project_forward",
