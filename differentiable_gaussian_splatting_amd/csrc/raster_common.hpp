@@ -284,7 +284,11 @@ constexpr float kBand = 1.0f / 262144.0f;
 constexpr float kAlphaMinLo = kAlphaMin * (1.0f - kBand), kAlphaMinHi = kAlphaMin * (1.0f + kBand);
 constexpr float kAlphaMaxLo = kAlphaMax * (1.0f - kBand), kAlphaMaxHi = kAlphaMax * (1.0f + kBand);
 
-template <bool kExactValues>
+// kClampBand = false (the forward's fast form): only the reject threshold gets the exact value. A fast o G on the
+// wrong side of 0.999 changes alpha by less than the fast value's own error (the clamp's choice is between o G and
+// 0.999, which then differ by less than that), and the forward's alpha only feeds T; the backward decides the clamp
+// exactly, since its gradient terms differ in kind on either side.
+template <bool kExactValues, bool kClampBand = true>
 __device__ __forceinline__ bool evaluate(const StagedSplat& s, float cx, float cy, Eval& e, const double* tab) {
   e.dx = cx - s.x;
   e.dy = cy - s.y;
@@ -305,7 +309,8 @@ __device__ __forceinline__ bool evaluate(const StagedSplat& s, float cx, float c
     float g = __builtin_amdgcn_exp2f(sigma * -1.44269504088896341f);
     float og = s.o * g;
     // (bitwise operators: no short-circuit branches, the masks combine in scalar registers)
-    const bool near = in_range & (og >= kAlphaMinLo) & ((og < kAlphaMinHi) | ((og > kAlphaMaxLo) & (og < kAlphaMaxHi)));
+    const bool near_max = kClampBand && ((og > kAlphaMaxLo) & (og < kAlphaMaxHi));
+    const bool near = in_range & (og >= kAlphaMinLo) & ((og < kAlphaMinHi) | near_max);
     if (__builtin_amdgcn_ballot_w64(near) != 0) {
       const float g_exact = exp_rn(-sigma, tab);
       g = near ? g_exact : g;

@@ -16,9 +16,9 @@ namespace {
 // kCull: each wave walks only the staged splats that can reach alpha >= 1/255 in its 8x8 block (reach_mask); the
 // others are certain rejects for every lane of the wave, so skipping them changes no result.
 // kExact: exp(-sigma) correctly rounded (fp64 series), so T and every stop decision are those of a plain fp32
-// evaluation; otherwise the hardware exponential with the exact value only near the alpha thresholds (evaluate's
-// fast form, the backward's): reject and clamp decisions are still exact, T carries the fast value's error (below
-// 1e-6 relative per splat), so a pixel whose exact T' lies that close to 1e-4 may stop one splat apart.
+// evaluation; otherwise the hardware exponential with the exact value only near the 1/255 threshold (evaluate's
+// fast form without the clamp band): reject decisions are still exact, alpha and T carry the fast value's error
+// (below 1e-6 relative per splat), so a pixel whose exact T' lies that close to 1e-4 may stop one splat apart.
 template <bool kCull, bool kExact>
 __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict__ splats, uint32_t n,
                                                          const uint32_t* __restrict__ vals,
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kTilePixels) void k_forward(const float* __restrict
         asm volatile("" ::"v"(s.o));
         ++walked;
         Eval e;
-        if (evaluate<kExact>(s, cxe, cy, e, s_exp2)) {
+        if (evaluate<kExact, kExact>(s, cxe, cy, e, s_exp2)) {
           float alpha = e.alpha;
           float next_T = T * (1.0f - alpha);
           // A pixel that would fall below the stop threshold here does not composite this splat and stops. Rare

@@ -120,9 +120,9 @@ gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats);
 #define GSR_EXP_EXACT 0         /*   (default) correctly rounded: T and every stop decision are those of a plain    */
                                 /*   fp32 evaluation of the definition;                                               */
 #define GSR_EXP_FAST 1          /*   the hardware exponential (relative error below 1e-6), the exact value only    */
-                                /*   within 2^-18 of the 1/255 and 0.999 thresholds: reject and clamp decisions stay */
-                                /*   exact, T carries the fast value's error, and a pixel whose exact T' falls that  */
-                                /*   close to 1e-4 may stop one splat apart. About 12 % faster.                      */
+                                /*   within 2^-18 of the 1/255 threshold: reject decisions stay exact, alpha and T  */
+                                /*   carry the fast value's error, and a pixel whose exact T' falls that close to    */
+                                /*   1e-4 may stop one splat apart. About 15 % faster.                               */
 gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value);
 
 /* Stages timed by GSR_OPT_KERNEL_TIMING, each the kernels between its pair of events. */

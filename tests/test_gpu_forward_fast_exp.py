@@ -1,8 +1,9 @@
 """The forward with the hardware exponential (GSR_OPT_FORWARD_EXP = GSR_EXP_FAST) against the oracle.
 
-In this mode exp(-sigma) is the hardware's (relative error below 1e-6) except within 2^-18 of the alpha thresholds,
-where the kernel takes the correctly rounded value: the reject and clamp decisions stay exact, so a pixel's
-compositing candidates are the oracle's, but the transmittance carries the fast values' error. The parity bar:
+In this mode exp(-sigma) is the hardware's (relative error below 1e-6) except within 2^-18 of the 1/255 threshold,
+where the kernel takes the correctly rounded value: the reject decisions stay exact, so a pixel's compositing
+candidates are the oracle's, but alpha (the 0.999 clamp included, which picks between o G and 0.999) and the
+transmittance carry the fast values' error. The parity bar:
   * pixels whose last_contrib equals the oracle's: image and final_T within 1e-5 absolute (as the exact mode);
   * any other pixel must have stopped on a decision that rounding can flip: from the oracle's stop-free candidate
     trace, every candidate the GPU composited has exact T' >= 1e-4 (1 - e), and the one it stopped at (if the list
@@ -39,9 +40,7 @@ def ctx():
 def stop_bound(alpha):
     """e_j for each candidate j of a trace (see the module docstring)."""
     a = alpha.astype(np.float64)
-    clamped = alpha == np.float32(0.999)  # the clamp value is exact
-    per = np.where(clamped, 0.0, a / (1.0 - a) * ALPHA_REL) + 3 * U
-    return np.cumsum(per)
+    return np.cumsum(a / (1.0 - a) * ALPHA_REL + 3 * U)
 
 
 def check_fast_forward(gpu, ref, splats, ob, w, h):
