@@ -323,8 +323,10 @@ __device__ __forceinline__ bool evaluate(const StagedSplat& s, float cx, float c
     e.alpha = (e.oG < kAlphaMax) ? e.oG : kAlphaMax;
   } else {
     // the same value as the select (o G is a product of finite values, never NaN), in one instruction: the
-    // compiler's min would first canonicalise its operand
-    asm("v_min_f32 %0, %1, %2" : "=v"(e.alpha) : "v"(e.oG), "v"(kAlphaMax));
+    // compiler's min would first canonicalise its operand; the constant is the instruction's literal (in a register
+    // operand it is materialised on every evaluation)
+    static_assert(__builtin_bit_cast(uint32_t, kAlphaMax) == 0x3f7fbe77u, "the literal below is 0.999f");
+    asm("v_min_f32 %0, 0x3f7fbe77, %1" : "=v"(e.alpha) : "v"(e.oG));
   }
   return in_range & !(e.alpha < kAlphaMin);
 }

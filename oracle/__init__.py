@@ -63,10 +63,11 @@ def _load():
     lib.oracle_render_backward_f32_mt.argtypes = [P, u32, P, P, u32, u32, P, P, P, P, P, u32]
     lib.oracle_trace_pixel_f32.argtypes = [P, P, P, u32, u32, u32, u32, u32, P, P, P, P, P]
     lib.oracle_trace_candidates_f32.argtypes = [P, P, P, u32, u32, u32, u32, u32, P, P, P, P]
+    lib.oracle_render_backward_exact.argtypes = [P, u32, P, P, u32, u32, P, P, P, P, u32]
     for name in ("oracle_bin_count", "oracle_tile_rect", "oracle_bin", "oracle_sort_pairs",
                  "oracle_render_forward_f32", "oracle_render_forward_f64", "oracle_render_backward_f32",
                  "oracle_render_backward_f64", "oracle_adam_step", "oracle_trace_pixel_f32",
-                 "oracle_trace_candidates_f32"):
+                 "oracle_trace_candidates_f32", "oracle_render_backward_exact"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -203,6 +204,24 @@ def render_backward(splats, bins: Bins, width: int, height: int, out_rgba, final
             stats.update({k: int(v) for k, v in zip(BWD_STAT_NAMES, st)})
     else:
         _check(lib.oracle_render_backward_f64(*args), "render_backward")
+    return grad
+
+
+def render_backward_exact(splats, bins: Bins, width: int, height: int, out_rgba, last_contrib, v_out,
+                          threads: int = 0):
+    """The backward's exact values on its given inputs (oracle_render_backward_exact): float64 [N, 9]. Decisions
+    (composite, clamp) as the fp32 backward takes them for entries before last_contrib; sigma, G, alpha, T and the
+    gradient terms in fp64, with C_final = out_rgba (the forward output the backward is given, taken in double).
+    `threads` 0: up to 16 host threads."""
+    lib = _load()
+    s = _c(splats, np.float32).reshape(-1, 9)
+    n = s.shape[0]
+    grad = np.zeros((n, 9), np.float64)
+    _check(lib.oracle_render_backward_exact(_ptr(s), n, _ptr(_c(bins.vals, np.uint32)),
+                                            _ptr(_c(bins.ranges, np.uint32)), width, height,
+                                            _ptr(_c(out_rgba, np.float64)), _ptr(_c(last_contrib, np.uint32)),
+                                            _ptr(_c(v_out, np.float32)), _ptr(grad),
+                                            threads or min(16, os.cpu_count() or 1)), "render_backward_exact")
     return grad
 
 

@@ -382,6 +382,65 @@ void render_backward(const R* splats, uint32_t n, const uint32_t* vals, const ui
     }
 }
 
+// The backward's exact values on its given inputs and the fp32 method's decisions: each pixel's decisions - which
+// entries before last_contrib composite, and which of them reach the 0.999 clamp - are taken by the fp32
+// evaluation above (the method's precision, the same decisions as the fp32 backward), and every value is then
+// formed in fp64 from the same records: sigma, G, alpha (0.999 exactly where the fp32 evaluation clamped, o G
+// elsewhere), the transmittance and the B1..B8 terms in the forward-order form, with C_final the forward output
+// the backward is given (out_rgba, in double). The result is what the backward computes from its inputs, free of
+// the fp32 rounding of its own values.
+void render_backward_exact(const float* splats, const uint32_t* vals, const uint32_t* ranges, uint32_t width,
+                           uint32_t row_begin, uint32_t row_end, const double* out_rgba,
+                           const uint32_t* last_contrib, const float* v_out, double* acc_grad) {
+  using Cf = Consts<float>;
+  using C = Consts<double>;
+  const uint32_t tiles_x = (width + kTile - 1) / kTile;
+  for (uint32_t py = row_begin; py < row_end; ++py)
+    for (uint32_t px = 0; px < width; ++px) {
+      const size_t p = size_t(py) * width + px;
+      const uint32_t t = (py / kTile) * tiles_x + (px / kTile);
+      const uint32_t start = ranges[2 * t];
+      const uint32_t last = last_contrib[p];
+      const float cxf = float(px) + Cf::half, cyf = float(py) + Cf::half;
+      const double cx = double(cxf), cy = double(cyf);
+      const double g[3] = {v_out[4 * p + 0], v_out[4 * p + 1], v_out[4 * p + 2]};
+      const double Cfin[3] = {out_rgba[4 * p + 0], out_rgba[4 * p + 1], out_rgba[4 * p + 2]};
+      double acc[3] = {0.0, 0.0, 0.0}, T = 1.0;
+      for (uint32_t k = start; k < start + last; ++k) {
+        const uint32_t idx = vals[k];
+        const Eval<float> ef = evaluate(load_splat(splats, idx), cxf, cyf);  // the decision, in fp32
+        if (ef.d != kComposite) continue;
+        const bool clamped = !(ef.oG < Cf::alpha_max);
+        const float* sp = splats + size_t(idx) * 9;
+        const Splat<double> sd{sp[0], sp[1], sp[2], sp[3], sp[4], sp[5], sp[6], sp[7], sp[8]};
+        const Eval<double> e = evaluate(sd, cx, cy);  // the values, in fp64
+        const double alpha = clamped ? C::alpha_max : e.oG;
+        const double rgb[3] = {sd.r, sd.g, sd.bl};
+        double* gr = acc_grad + size_t(idx) * 9;
+        const double w = alpha * T;  // B1
+        for (int ch = 0; ch < 3; ++ch) gr[5 + ch] += w * g[ch];
+        const double one_m = 1.0 - alpha;  // B2..B3
+        double my[3], dl_da = 0.0;
+        for (int ch = 0; ch < 3; ++ch) {
+          my[ch] = rgb[ch] * w;
+          const double after = Cfin[ch] - acc[ch] - my[ch];
+          dl_da += g[ch] * (rgb[ch] * T - after / one_m);
+        }
+        if (!clamped) {  // B4..B7
+          gr[8] += dl_da * e.G;
+          const double dl_ds = -(dl_da * e.oG);
+          gr[2] += dl_ds * (0.5 * e.dx * e.dx);
+          gr[3] += dl_ds * (e.dx * e.dy);
+          gr[4] += dl_ds * (0.5 * e.dy * e.dy);
+          gr[0] += dl_ds * -(sd.a * e.dx + sd.b * e.dy);
+          gr[1] += dl_ds * -(sd.b * e.dx + sd.c * e.dy);
+        }
+        for (int ch = 0; ch < 3; ++ch) acc[ch] += my[ch];  // B8
+        T *= one_m;
+      }
+    }
+}
+
 // Runs fn(thread, row_begin, row_end) over bands of 16 pixel rows dealt round-robin to `threads` threads.
 template <typename Fn>
 void run_bands(uint32_t height, uint32_t threads, Fn fn) {
@@ -532,6 +591,26 @@ int oracle_render_backward_f64(const double* splats, uint32_t n, const uint32_t*
   std::fill(splats_grad, splats_grad + size_t(n) * 9, 0.0);
   render_backward<double>(splats, n, vals, ranges, width, 0, height, out_rgba, final_T, last_contrib, v_out,
                           splats_grad, &st);
+  return 0;
+}
+
+// The backward's exact values on its given inputs and the fp32 method's decisions (render_backward_exact), over
+// `threads` host threads (bands of 16 pixel rows; per-thread sums in double added in thread order). out_rgba is the
+// forward output the backward is given, in double.
+int oracle_render_backward_exact(const float* splats, uint32_t n, const uint32_t* vals, const uint32_t* ranges,
+                                 uint32_t width, uint32_t height, const double* out_rgba,
+                                 const uint32_t* last_contrib, const float* v_out, double* splats_grad,
+                                 uint32_t threads) {
+  if (!ranges || !out_rgba || !last_contrib || !v_out || (n && !splats_grad) || width == 0 || height == 0 ||
+      threads == 0)
+    return -1;
+  std::vector<std::vector<double>> acc(threads, std::vector<double>(size_t(n) * 9, 0.0));
+  run_bands(height, threads, [&](uint32_t t, uint32_t y0, uint32_t y1) {
+    render_backward_exact(splats, vals, ranges, width, y0, y1, out_rgba, last_contrib, v_out, acc[t].data());
+  });
+  std::fill(splats_grad, splats_grad + size_t(n) * 9, 0.0);
+  for (uint32_t t = 0; t < threads; ++t)
+    for (size_t k = 0; k < size_t(n) * 9; ++k) splats_grad[k] += acc[t][k];
   return 0;
 }
 

@@ -13,13 +13,14 @@ transmittance carry the fast values' error. The parity bar:
     and u = 2^-24 for the rounding of 1 - alpha and of the product; its image and T must equal, within 1e-5, the
     oracle's colour and T composited up to the GPU's last contributor;
   * such pixels are rare: at most 1e-3 of the image.
-The backward takes the fast forward's outputs, and is compared with the oracle's backward on the same outputs.
+The backward does not depend on the forward's exponential; its parity is tested on the oracle forward's outputs
+(test_gpu_raster.py).
 [A.9 f16 forward page, implementation listing; W1 warp sparse skip + exp-skip page, summary]
 """
 import numpy as np
 import pytest
 
-from gpuhelp import banner, custom_scene, dev, grads_close, host, oracle_bins, oracle_forward, scene
+from gpuhelp import banner, custom_scene, dev, host, oracle_bins, oracle_forward, scene
 
 pytestmark = pytest.mark.gpu
 
@@ -139,20 +140,3 @@ def test_fast_forward_bar_rejects_a_wrong_stop(ctx):
     fake = tuple(dev(a) for a in (out, ft, lc))
     with pytest.raises(AssertionError):
         check_fast_forward(fake, ref, sc.splats, ob, sc.width, sc.height)
-
-
-@pytest.mark.parametrize("name", ["tiny", "raster84k", "raster410k"])
-def test_backward_after_fast_forward_matches_oracle(ctx, name):
-    import oracle
-    from differentiable_gaussian_splatting_amd import gsr
-    banner(f"backward after fast forward {name}")
-    sc = scene(name)
-    sp = dev(sc.splats)
-    bins = gsr.gsr_bin(ctx, sp, dev(sc.depths), sc.width, sc.height)
-    out, ft, lc = gsr.gsr_render_forward(ctx, sp, bins, sc.width, sc.height)
-    g = host(gsr.gsr_render_backward(ctx, sp, bins, sc.width, sc.height, out, ft, lc, dev(sc.v_out)))
-    ref = oracle.render_backward(sc.splats, oracle_bins(name), sc.width, sc.height, host(out), host(ft),
-                                 host(lc, np.uint32), sc.v_out)
-    ok, worst, at = grads_close(g, ref)
-    print(f"  worst |gpu-ref| / (1e-4 + 1e-4 |ref|) = {worst:.3g} at {at}")
-    assert ok, (worst, at, g[at], ref[at])

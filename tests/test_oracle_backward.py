@@ -180,3 +180,61 @@ def test_threaded_oracle_matches_single_threaded(orc):
         assert np.array_equal(o2, out) and np.array_equal(f2, ft) and np.array_equal(l2, lc)
         g2 = orc.render_backward_mt(sc.splats, b, 120, 88, out, ft, lc, sc.v_out, threads)
         assert np.allclose(g2, g, rtol=1e-6, atol=1e-9)
+
+
+# ------------------------------------------------------------------ exact values on the fp32 method's decisions
+@pytest.mark.parametrize("seed,vout_sd,smax", [(1, 0.01, 40.0), (2, 1.0, 8.0), (3, 1.0, 40.0)])
+def test_exact_backward_is_the_fp64_chain_where_decisions_agree(orc, seed, vout_sd, smax):
+    """render_backward_exact takes its decisions in fp32 and its values in fp64; on scenes where the fp32 and fp64
+    forwards take every decision alike (same fingerprint), given the fp64 forward's output it must equal the fp64
+    backward on it up to the order of double additions - the f64 path that the finite-difference pins above check."""
+    sc = scenes.make_scene(scenes.SceneSpec("ex", 96, 80, 2000, seed=seed,
+                                            size_classes=((0.7, 0.3, min(4.0, smax)), (0.3, min(4.0, smax), smax)),
+                                            opacity_mu=-0.5, opacity_sd=1.5, vout_sd=vout_sd, margin=8.0))
+    bins = orc.bin(sc.splats, sc.depths, 96, 80)
+    out32, ft32, lc32, st32 = orc.render_forward(sc.splats, bins, 96, 80, "f32")
+    sp64 = sc.splats.astype(np.float64)
+    out64, ft64, lc64, st64 = orc.render_forward(sp64, bins, 96, 80, "f64")
+    assert st32["fingerprint"] == st64["fingerprint"]
+    g64 = orc.render_backward(sp64, bins, 96, 80, out64, ft64, lc64, sc.v_out.astype(np.float64), "f64")
+    gx = orc.render_backward_exact(sc.splats, bins, 96, 80, out64, lc32, sc.v_out)
+    scale = np.abs(g64).max()
+    assert np.allclose(gx, g64, rtol=1e-9, atol=1e-12 * scale)
+    # and on the fp32 forward's output the fp32 oracle is within its own rounding of it (loose: the last case is
+    # where the fp32 form loses 2e-4)
+    g32 = orc.render_backward(sc.splats, bins, 96, 80, out32, ft32, lc32, sc.v_out)
+    gx32 = orc.render_backward_exact(sc.splats, bins, 96, 80, out32, lc32, sc.v_out)
+    assert np.allclose(g32, gx32, rtol=1e-3, atol=1e-3 * scale)
+
+
+def test_exact_backward_follows_the_fp32_decisions(orc):
+    """A pixel whose fp32 o G reaches the 0.999 clamp while the fp64 product stays below it: the fp32 evaluation
+    clamps (no opacity or geometry gradient from the pixel), fp64 would not; the exact-value backward follows fp32,
+    with alpha = 0.999 exactly."""
+    f = np.float32
+    a = f(0.25)
+    found = None
+    for k in range(1, 400):  # splat offsets dx = -k / 1000 px: sigma about 1.25e-7 k^2, each a different G
+        x = f(8.5 + k / 1000.0)
+        dx = f(8.5) - x
+        G32 = f(math.exp(-float(f(0.5) * (a * dx * dx))))
+        G64 = math.exp(-(0.5 * (float(a) * float(dx) * float(dx))))
+        o0 = f(float(f(0.999)) / G64)
+        for step in range(-8, 9):  # o within a few ulps of the clamp
+            o = o0
+            for _ in range(abs(step)):
+                o = np.nextafter(o, f(2) if step > 0 else f(0))
+            if o <= 1 and f(o * G32) >= f(0.999) and float(o) * G64 < float(f(0.999)):
+                found = o
+                break
+        if found is not None:
+            break
+    assert found is not None
+    sp = np.array([x, 8.5, a, 0.0, a, 1.0, 0.5, 0.25, found], np.float32)
+    g = np.zeros((16, 16, 4), np.float32)
+    g[8, 8, 0] = 1.0
+    lc = np.zeros((16, 16), np.uint32)
+    lc[8, 8] = 1
+    gx = orc.render_backward_exact(sp[None], single_bins(orc, 1), 16, 16, np.zeros((16, 16, 4)), lc, g)[0]
+    assert gx[8] == 0 and np.all(gx[:5] == 0)            # clamped: no opacity or geometry term
+    assert gx[5] == float(f(0.999))                       # alpha = 0.999 exactly, T = 1
