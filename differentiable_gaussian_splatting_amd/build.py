@@ -18,7 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgsr.so")
-SOURCES = ["ctx.hip", "bin.hip", "sort.hip", "raster_fwd.hip", "raster_bwd.hip", "adam.hip", "project.hip", "loss.hip"]
+SOURCES = ["ctx.hip", "bin.hip", "sort.hip", "raster_fwd.hip", "raster_bwd.hip", "adam.hip", "project.hip", "loss.hip",
+           "tile_depth.hip"]
 ARCH = os.environ.get("GSR_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -19,6 +19,7 @@ namespace gsr {
 namespace {
 
 constexpr uint32_t kThreads = 256;
+constexpr uint32_t kTileFirstAvg = 3072;  // the tile-first scheme's largest average list (its on-chip capacity: 3456)
 constexpr uint32_t kScanItems = 16;
 constexpr uint32_t kScanBlock = kThreads * kScanItems;
 
@@ -581,11 +582,16 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   ctx->order_ranges = nullptr;  // the ranges are rewritten: rank again before the next raster launch
   hipStream_t s = static_cast<hipStream_t>(stream);
   Arena& a = ctx->arena;
-  const bool presort = ctx->bin_scheme == GSR_BIN_PRESORT;
   const bool ellipse = ctx->bin_rule == GSR_BIN_ELLIPSE;
   // An earlier call's pair count that has arrived in the meantime raises the capacity hint (before this call's
   // launch overwrites the pinned word).
   if (ctx->pairs_pending && hipEventQuery(a.total_ready) == hipSuccess) note_pair_count(ctx);
+  // The tile-first scheme sorts each tile's list on chip; when the last count seen puts the average list beyond
+  // kTileFirstAvg pairs (most lists would exceed the on-chip capacity) the presort scheme takes the call instead.
+  // Both give the same bins bit for bit; the choice is only about speed.
+  const bool tile_first = ctx->bin_scheme == GSR_BIN_TILE_DEPTH &&
+                          ctx->last_pairs <= uint64_t(kTileFirstAvg) * num_tiles;
+  const bool presort = ctx->bin_scheme == GSR_BIN_PRESORT || (ctx->bin_scheme == GSR_BIN_TILE_DEPTH && !tile_first);
   // Without a wait only once there is a count or a reservation to size the pair buffers from.
   const bool sync_free = ctx->bin_sync_free && n && (ctx->pair_hint > 0 || ctx->pair_reserved > 0);
 
@@ -722,6 +728,72 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
                        kb[res], static_cast<const uint32_t*>(v0), P, pairs_dev, uint32_t(num_tiles), depths, n,
                        static_cast<uint64_t*>(nullptr), ranges, idx_bits);
     sorted_v = v0;
+  } else if (tile_first) {
+    // Pairs emitted splat by splat (index order), sorted stably by tile alone, then each tile's list by depth on
+    // chip (tile_depth.hip): splat and tile id packed in one word when they fit, else tile ids with a splat array.
+    uint32_t* kb[2] = {static_cast<uint32_t*>(a.keys[0].ptr), static_cast<uint32_t*>(a.keys[1].ptr)};
+    const bool tpacked = tile_bits > 0 && idx_bits + tile_bits <= 32;
+    if ((st = grow(ctx, a.order_vals_alt, std::max<size_t>(size_t(n) * 4, size_t(P) * 4)))) return st;
+    uint32_t* spare = static_cast<uint32_t*>(a.order_vals_alt.ptr);  // a pair-count array for long tiles
+    if (n) {
+      if (tpacked) {
+        if (ellipse)
+          hipLaunchKernelGGL((k_emit_ellipse<uint32_t, true>), dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s,
+                             splats, rects, depths, n, order, order_mask, tiles_x, offsets, P, pairs_dev, kb[0],
+                             static_cast<uint32_t*>(nullptr), idx_bits);
+        else
+          hipLaunchKernelGGL((k_emit<uint32_t, true>), dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, rects,
+                             depths, n, order, order_mask, tiles_x, offsets, P, pairs_dev, kb[0],
+                             static_cast<uint32_t*>(nullptr), idx_bits);
+      } else {
+        if (ellipse)
+          hipLaunchKernelGGL(k_emit_ellipse<uint32_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, splats,
+                             rects, depths, n, order, order_mask, tiles_x, offsets, P, pairs_dev, kb[0], v0, 0u);
+        else
+          hipLaunchKernelGGL(k_emit<uint32_t>, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, rects, depths, n,
+                             order, order_mask, tiles_x, offsets, P, pairs_dev, kb[0], v0, 0u);
+      }
+    }
+    // the tile-sorted list (list, and list_vals when unpacked), where the result goes, and four pair-count arrays
+    // free for lists longer than the on-chip capacity: the key buffers are 8 bytes per pair, so a list of 32-bit
+    // words leaves the second half of its buffer free
+    const uint32_t* list = kb[0];
+    const uint32_t* list_vals = tpacked ? nullptr : v0;
+    uint32_t* vals_out = tpacked ? v0 : static_cast<uint32_t*>(a.vals[1].ptr);
+    uint32_t* scratch[4] = {kb[1], kb[1] + P, kb[0] + P, tpacked ? static_cast<uint32_t*>(a.vals[1].ptr) : spare};
+    if (tile_bits > 0 && P > 0) {
+      res = (sort_passes(tile_bits) & 1u) ? 1 : 0;
+      timing_mark(ctx, GSR_STAGE_TILE_SORT, s, false);
+      if (tpacked) {
+        st = radix_sort_tiles_packed(ctx, s, kb[0], P, idx_bits, tile_bits, kb[res], kb[1 - res],
+                                     static_cast<uint32_t*>(nullptr), static_cast<uint64_t*>(nullptr),
+                                     static_cast<const float*>(nullptr), 0u, pairs_dev);
+      } else {
+        uint32_t* vr = static_cast<uint32_t*>(a.vals[res].ptr);
+        uint32_t* vt = static_cast<uint32_t*>(a.vals[1 - res].ptr);
+        st = radix_sort_launch<uint32_t>(ctx, s, kb[0], v0, P, tile_bits, kb[res], vr, kb[1 - res], vt, pairs_dev);
+        list_vals = vr;
+        vals_out = vt;
+      }
+      if (st) return st;
+      timing_mark(ctx, GSR_STAGE_TILE_SORT, s, true);
+      list = kb[res];
+      scratch[0] = kb[1 - res];
+      scratch[1] = kb[1 - res] + P;
+      scratch[2] = kb[res] + P;
+    }
+    hipLaunchKernelGGL(k_ranges<uint32_t>, dim3(grid_for(P + 1, kThreads * kRangeItems)), dim3(kThreads), 0, s,
+                       list, list_vals, P, pairs_dev, uint32_t(num_tiles), depths, n,
+                       static_cast<uint64_t*>(nullptr), ranges, tpacked ? idx_bits : 0u);
+    if (ctx->bin_keys) {
+      if ((st = grow(ctx, a.order_alt, std::max<size_t>(size_t(n) * 8, size_t(P) * 8)))) return st;
+      final_k = static_cast<uint64_t*>(a.order_alt.ptr);
+    }
+    timing_mark(ctx, GSR_STAGE_TILE_DEPTH, s, false);
+    launch_tile_depth(s, list, list_vals, tpacked ? idx_bits : 32u, ranges, P, pairs_dev, uint32_t(num_tiles),
+                      depths, n, vals_out, final_k, scratch[0], scratch[1], scratch[2], scratch[3]);
+    timing_mark(ctx, GSR_STAGE_TILE_DEPTH, s, true);
+    sorted_v = vals_out;
   } else if (presort) {
     // tile ids as 32-bit keys, sorted by their tile_bits low bits
     uint32_t* kb[2] = {static_cast<uint32_t*>(a.keys[0].ptr), static_cast<uint32_t*>(a.keys[1].ptr)};

@@ -202,7 +202,7 @@ gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value) {
   if (!ctx) return GSR_EINVAL;
   switch (option) {
     case GSR_OPT_BIN_SCHEME:
-      if (value != GSR_BIN_PRESORT && value != GSR_BIN_KEY64)
+      if (value != GSR_BIN_PRESORT && value != GSR_BIN_KEY64 && value != GSR_BIN_TILE_DEPTH)
         return fail(ctx, GSR_EINVAL, "gsr_set_option: unknown bin scheme %lld", (long long)value);
       ctx->bin_scheme = int32_t(value);
       return GSR_OK;

@@ -144,6 +144,18 @@ gsr_status radix_sort_launch(gsr_ctx* ctx, hipStream_t s, const K* keys_in, cons
                              uint32_t key_bits, K* keys_out, uint32_t* vals_out, K* tmp_keys, uint32_t* tmp_vals,
                              const uint64_t* n_dev = nullptr);
 
+// Per-tile depth order of the tile-first scheme (tile_depth.hip): one workgroup per tile sorts the tile's list
+// list[start..end) (ranges clamped to the pair count, *pairs_dev when not null) stably by the splats' depth bits. The
+// list holds packed words (tile << idx_bits) | splat when list_vals is null, else list_vals holds the splats; the
+// result is written to vals_out[start..end) and, when keys_out is not null, keys_out = (tile << 32) | depth bits.
+// Lists longer than tile_depth_capacity() are sorted through gk0, gk1, gp0, gp1 (pair-count arrays, each tile using
+// its own stretch).
+void launch_tile_depth(hipStream_t s, const uint32_t* list, const uint32_t* list_vals, uint32_t idx_bits,
+                       const uint32_t* ranges, uint64_t pairs_cap, const uint64_t* pairs_dev, uint32_t num_tiles,
+                       const float* depths, uint32_t n, uint32_t* vals_out, uint64_t* keys_out, uint32_t* gk0,
+                       uint32_t* gk1, uint32_t* gp0, uint32_t* gp1);
+uint32_t tile_depth_capacity();
+
 // The same sort of 32-bit tile ids whose last pass also writes keys_final[g] = (key << 32) | bits(depths[val]) for
 // every output position g (values below n_depths; others get depth bits 0). Requires key_bits > 0.
 gsr_status radix_sort_tiles_final(gsr_ctx* ctx, hipStream_t s, const uint32_t* keys_in, const uint32_t* vals_in,
@@ -153,7 +165,8 @@ gsr_status radix_sort_tiles_final(gsr_ctx* ctx, hipStream_t s, const uint32_t* k
 
 // The tile sort on packed keys (tile << idx_bits) | value (idx_bits + tile_bits <= 32): sorts stably by the tile
 // field, keys only; the last pass writes the sorted keys to keys_out, the values to vals_out and, when keys_final
-// is not null, keys_final[g] = (tile << 32) | bits(depths[value]). Same pass-parity rule as radix_sort_launch.
+// is not null, keys_final[g] = (tile << 32) | bits(depths[value]). With vals_out null the keys stay packed (the
+// last pass writes keys only). Same pass-parity rule as radix_sort_launch.
 gsr_status radix_sort_tiles_packed(gsr_ctx* ctx, hipStream_t s, const uint32_t* keys_in, uint64_t n,
                                    uint32_t idx_bits, uint32_t tile_bits, uint32_t* keys_out, uint32_t* tmp_keys,
                                    uint32_t* vals_out, uint64_t* keys_final, const float* depths,

@@ -74,4 +74,23 @@ __device__ __forceinline__ uint64_t count_within(const uint64_t* dev, uint64_t c
   return v <= cap ? v : 0;
 }
 
+// Lanes of this wave whose (valid) digit equals mine: one ballot per digit bit. Per bit, s is 0 or all ones (the
+// bit, sign-extended), and the lanes that agree with mine are ~(ballot ^ s), formed on each 32-bit half: a bit
+// extract, the ballot's compare, two XNORs and two ANDs.
+template <uint32_t kBits>
+__device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
+  const uint64_t v = __builtin_amdgcn_ballot_w64(valid);
+  uint32_t lo = uint32_t(v), hi = uint32_t(v >> 32);
+#pragma unroll
+  for (uint32_t bit = 0; bit < kBits; ++bit) {
+    const uint32_t s = uint32_t(-int32_t((d >> bit) & 1u));
+    const uint64_t b = __builtin_amdgcn_ballot_w64(s != 0u);
+    lo &= ~(uint32_t(b) ^ s);
+    hi &= ~(uint32_t(b >> 32) ^ s);
+  }
+  return (uint64_t(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(uint32_t lane) { return (uint64_t(1) << lane) - 1; }
+
 }  // namespace gsr

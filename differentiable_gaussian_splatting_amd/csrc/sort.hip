@@ -29,25 +29,6 @@ __device__ __forceinline__ uint32_t digit_of(K k, uint32_t shift) {
   return uint32_t(k >> shift) & ((1u << kBits) - 1u);
 }
 
-// Lanes of this wave whose (valid) digit equals mine: one ballot per digit bit. Per bit, s is 0 or all ones (the
-// bit, sign-extended), and the lanes that agree with mine are ~(ballot ^ s), formed on each 32-bit half: a bit
-// extract, the ballot's compare, two XNORs and two ANDs.
-template <uint32_t kBits>
-__device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
-  const uint64_t v = __builtin_amdgcn_ballot_w64(valid);
-  uint32_t lo = uint32_t(v), hi = uint32_t(v >> 32);
-#pragma unroll
-  for (uint32_t bit = 0; bit < kBits; ++bit) {
-    const uint32_t s = uint32_t(-int32_t((d >> bit) & 1u));
-    const uint64_t b = __builtin_amdgcn_ballot_w64(s != 0u);
-    lo &= ~(uint32_t(b) ^ s);
-    hi &= ~(uint32_t(b >> 32) ^ s);
-  }
-  return (uint64_t(hi) << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t lanemask_lt(uint32_t lane) { return (uint64_t(1) << lane) - 1; }
-
 // Digit counts of one block of keys. The order of the keys does not matter here, so each wave adds its keys to a
 // histogram of its own with LDS atomics (a wave's atomics on one address serialise, different waves never share
 // one), and the four are summed at the end.
@@ -245,8 +226,8 @@ gsr_status run_passes(gsr_ctx* ctx, hipStream_t s, const K* keys_in, const uint3
     const bool last = p + 1 == passes;
     if constexpr (sizeof(K) == 4) {
       if (fin.packed) {
-        // keys only; the last pass unpacks the values (into vals_out, which the caller sized)
-        if (last)
+        // keys only; the last pass unpacks the values (into vals_out, which the caller sized), if asked to
+        if (last && vals_out)
           hipLaunchKernelGGL((k_scatter<K, kItems, kBits, true, true>), dim3(nb), dim3(kThreads), 0, s, src_k,
                              static_cast<const uint32_t*>(nullptr), n, n_dev, shift, nb, hist, tot, dk, vals_out,
                              fin.keys, fin.depths, fin.n, fin.idx_bits);
@@ -338,7 +319,7 @@ gsr_status radix_sort_tiles_packed(gsr_ctx* ctx, hipStream_t s, const uint32_t* 
                                    uint32_t n_depths, const uint64_t* n_dev) {
   if (tile_bits == 0 || idx_bits + tile_bits > 32)
     return fail(ctx, GSR_EINVAL, "radix sort: packed keys need 1..32 - idx_bits tile bits");
-  if (!vals_out) return fail(ctx, GSR_EINVAL, "radix sort: packed keys need a value output");
+  if (!vals_out && keys_final) return fail(ctx, GSR_EINVAL, "radix sort: final keys need the value output");
   FinalKeys fin{keys_final, depths, n_depths, true, idx_bits};
   return sort_any<uint32_t>(ctx, s, keys_in, nullptr, n, n_dev, tile_bits, keys_out, vals_out, tmp_keys, nullptr,
                             fin);

@@ -1,0 +1,280 @@
+// Per-tile depth order for the tile-first binning scheme (GSR_BIN_TILE_DEPTH): the pairs have been emitted splat by
+// splat (ascending splat index) and sorted stably by tile id alone, so each tile's list holds its splats in index
+// order; one workgroup per tile then puts that list in (depth bits, splat index) order - the order of the 64-bit
+// keys (tile << 32) | depth bits sorted stably, ties in depth keeping splat order. [C0 resident arena + C1 pass skip
+// page, section 2 table, rows "C0" and "C1": the keys and their stable sort; the constant-digit pass skip is applied
+// per tile]
+//
+// Lists of at most kCap entries are sorted in LDS by buckets: the pair (depth bits, splat) is unique within a tile
+// (a splat covers a tile once), so the sort needs no stability. Each entry goes to one of nb buckets (nb = the
+// power of two >= the list length, 512 to 4096) by a monotone map of its depth bits, (bits - min) * nb / (max - min
+// + 1) in fp32 with truncation; a counting sort by bucket (LDS atomics give each entry a slot in its bucket in no
+// particular order) groups them, and each entry's rank in the tile is its bucket's start plus the number of entries
+// of its bucket with a smaller (depth bits, splat). On the pages' depth distributions a bucket holds about three
+// entries; a tile with a bucket of more than kBucketLimit (many equal depths) takes the radix sort instead.
+//
+// The radix sort is a least-significant-digit sort of the list's 32-bit depth keys in 8-bit digits, in LDS when the
+// list has at most kCap entries (keys and 16-bit positions in the tile's list, double-buffered), else in the same
+// steps through global scratch. Per pass: a digit histogram of the whole list (per-wave LDS counts), its exclusive
+// scan, and a stable scatter of chunks of 1024 keys in list order, each key ranked among the equal digits of its
+// wave by a 64-lane ballot match (as the device-wide sort's scatter) and placed after those of earlier waves and
+// chunks. A pass whose digit is the same for every key of the list is skipped. Being stable, it relies on the list's
+// index order for the ties.
+#include "gsr_internal.hpp"
+#include "scan_common.hpp"
+
+namespace gsr {
+namespace {
+
+constexpr uint32_t kThreads = 512, kWaves = kThreads / kWave;
+constexpr uint32_t kBits = 8, kRadix = 1u << kBits;
+constexpr uint32_t kItems = 4, kChunk = kThreads * kItems;  // keys ranked per step, four per thread
+constexpr uint32_t kCap = 3456;  // the longest list sorted in LDS (52 KB per workgroup: three per compute unit)
+static_assert(kThreads >= kRadix, "a thread per digit");
+static_assert(kCap <= 65536, "16-bit list positions");
+constexpr uint32_t kMinBuckets = kThreads, kMaxBuckets = 4096;  // kMaxBuckets: kCap rounded up to a power of two
+constexpr uint32_t kBucketLimit = 64;
+constexpr uint32_t kMaxItems = (kCap + kThreads - 1) / kThreads;  // list entries per thread
+constexpr uint32_t kScanPer = kMaxBuckets / kThreads;             // bucket counts per thread in the scan
+static_assert(kMaxBuckets >= kCap && kMinBuckets >= kThreads && kMaxBuckets % kThreads == 0, "bucket counts");
+
+struct SortShared {
+  uint32_t hist[kWaves][kRadix];  // per-wave digit counts, then per-wave prefixes within a chunk
+  uint32_t dstart[kRadix];        // first position of each digit in the pass's output
+  uint32_t run[kRadix];           // keys of each digit placed by the earlier chunks
+  uint32_t tot[kRadix];           // keys of each digit in the current chunk
+  uint32_t smem[kWaves];
+};
+
+union TileShared {
+  struct {
+    SortShared sh;
+    uint32_t key[2][kCap];
+    uint16_t pos[2][kCap];
+  } lsd;
+  struct {
+    uint32_t start[kMaxBuckets + 1];  // bucket counts, then their exclusive scan; start[nb] = m
+    uint64_t entry[kCap];             // the list grouped by bucket: (depth bits << 32) | splat
+    uint32_t wmin[kWaves], wmax[kWaves], wsum[kWaves];
+  } bkt;
+};
+
+__device__ __forceinline__ uint32_t bucket_of(uint32_t key, uint32_t lo, float scale, uint32_t nb) {
+  return min(nb - 1, uint32_t(float(key - lo) * scale));
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+#pragma unroll
+  for (int d = 1; d < int(kWave); d <<= 1) v = min(v, uint32_t(__shfl_xor(int(v), d)));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int d = 1; d < int(kWave); d <<= 1) v = max(v, uint32_t(__shfl_xor(int(v), d)));
+  return v;
+}
+
+// Sorts keys k0[0..m) with their positions p0[0..m) stably by the keys' 32 bits, through (k1, p1); returns which
+// buffer pair holds the result (0 or 1). The buffers are LDS (short lists) or global scratch (long ones). All threads
+// call it.
+template <typename PosT>
+__device__ __forceinline__ uint32_t sort_list(uint32_t* k0, uint32_t* k1, PosT* p0, PosT* p1, uint32_t m,
+                                              SortShared& sh) {
+  const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const bool owner = tid < kRadix;  // thread tid < kRadix owns digit tid
+  uint32_t src = 0;
+  for (uint32_t shift = 0; shift < 32; shift += kBits) {
+    uint32_t* const ks = src ? k1 : k0;
+    uint32_t* const kd = src ? k0 : k1;
+    PosT* const ps = src ? p1 : p0;
+    PosT* const pd = src ? p0 : p1;
+    for (uint32_t i = tid; i < kWaves * kRadix; i += kThreads) (&sh.hist[0][0])[i] = 0;
+    __syncthreads();
+    for (uint32_t e = tid; e < m; e += kThreads) atomicAdd(&sh.hist[w][(ks[e] >> shift) & (kRadix - 1)], 1u);
+    __syncthreads();
+    uint32_t tot = 0;
+    if (owner) {
+#pragma unroll
+      for (uint32_t q = 0; q < kWaves; ++q) tot += sh.hist[q][tid];
+    }
+    // one digit holding every key: this pass is the identity (uniform)
+    if (__syncthreads_or(owner && tot == m)) continue;
+    const uint32_t ds = block_exclusive_scan<uint32_t, kThreads>(tot, nullptr, sh.smem);
+    if (owner) {
+      sh.dstart[tid] = ds;
+      sh.run[tid] = 0;
+    }
+    for (uint32_t c0 = 0; c0 < m; c0 += kChunk) {
+      for (uint32_t i = lane; i < kRadix; i += kWave) sh.hist[w][i] = 0;
+      __syncthreads();
+      uint32_t kk[kItems], d[kItems], r[kItems];
+      PosT pp[kItems];
+      bool valid[kItems];
+#pragma unroll
+      for (uint32_t i = 0; i < kItems; ++i) {
+        const uint32_t idx = c0 + w * (kWave * kItems) + i * kWave + lane;
+        valid[i] = idx < m;
+        kk[i] = valid[i] ? ks[idx] : 0u;
+        pp[i] = valid[i] ? ps[idx] : PosT(0);
+        d[i] = (kk[i] >> shift) & (kRadix - 1);
+        const uint64_t peers = match_digit<kBits>(d[i], valid[i]);
+        r[i] = 0;
+        if (valid[i]) {
+          const uint64_t before = peers & lanemask_lt(lane);
+          const uint32_t old = sh.hist[w][d[i]];
+          r[i] = old + uint32_t(__popcll(before));
+          if (before == 0) sh.hist[w][d[i]] = old + uint32_t(__popcll(peers));
+        }
+      }
+      __syncthreads();
+      if (owner) {
+        uint32_t acc = 0;  // per-wave prefixes of digit tid and the chunk's total
+#pragma unroll
+        for (uint32_t q = 0; q < kWaves; ++q) {
+          const uint32_t c = sh.hist[q][tid];
+          sh.hist[q][tid] = acc;
+          acc += c;
+        }
+        sh.tot[tid] = acc;
+      }
+      __syncthreads();
+#pragma unroll
+      for (uint32_t i = 0; i < kItems; ++i)
+        if (valid[i]) {
+          const uint32_t dst = sh.dstart[d[i]] + sh.run[d[i]] + sh.hist[w][d[i]] + r[i];
+          kd[dst] = kk[i];
+          pd[dst] = pp[i];
+        }
+      __syncthreads();
+      if (owner) sh.run[tid] += sh.tot[tid];
+    }
+    __syncthreads();
+    src = 1 - src;
+  }
+  return src;
+}
+
+// One workgroup per tile. The tile's list is list[start..end) (ranges, clamped to the pair count): packed words
+// (tile << idx_bits) | splat when list_vals is null, else list_vals holds the splats. Writes vals_out[start + e] =
+// the e-th splat in (depth bits, index) order and, when keys_out is not null, keys_out[start + e] =
+// (tile << 32) | its depth bits. Lists longer than kCap use the scratch arrays gk0, gk1, gp0, gp1 (P entries each,
+// the tile's stretch [start, end) of them).
+__global__ __launch_bounds__(kThreads) void k_tile_depth(const uint32_t* __restrict__ list,
+                                                         const uint32_t* __restrict__ list_vals, uint32_t idx_bits,
+                                                         const uint32_t* __restrict__ ranges, uint64_t pairs_cap,
+                                                         const uint64_t* __restrict__ pairs_dev, uint32_t num_tiles,
+                                                         const float* __restrict__ depths, uint32_t n,
+                                                         uint32_t* __restrict__ vals_out, uint64_t* __restrict__ keys_out,
+                                                         uint32_t* gk0, uint32_t* gk1, uint32_t* gp0, uint32_t* gp1) {
+  __shared__ TileShared ts;
+  const uint32_t tile = blockIdx.x;
+  if (tile >= num_tiles) return;
+  const uint64_t P = count_within(pairs_dev, pairs_cap);
+  const uint32_t start = uint32_t(min<uint64_t>(ranges[2 * tile], P));
+  const uint32_t end = uint32_t(max<uint64_t>(start, min<uint64_t>(ranges[2 * tile + 1], P)));
+  const uint32_t m = end - start;
+  if (m == 0) return;
+  const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const uint32_t mask = idx_bits >= 32 ? ~0u : (1u << idx_bits) - 1u;
+  auto splat_at = [&](uint32_t e) -> uint32_t { return list_vals ? list_vals[start + e] : list[start + e] & mask; };
+  auto depth_bits = [&](uint32_t splat) -> uint32_t { return splat < n ? __float_as_uint(depths[splat]) : 0u; };
+  auto emit = [&](uint32_t e, uint32_t splat, uint32_t key) {
+    vals_out[start + e] = splat;
+    if (keys_out) keys_out[start + e] = (uint64_t(tile) << 32) | key;
+  };
+  if (m <= kCap) {
+    // buckets
+    uint32_t key[kMaxItems], spl[kMaxItems], slot[kMaxItems];
+    uint32_t kmin = ~0u, kmax = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < kMaxItems; ++i) {
+      const uint32_t e = tid + i * kThreads;
+      spl[i] = e < m ? splat_at(e) : 0u;
+      key[i] = e < m ? depth_bits(spl[i]) : 0u;
+      if (e < m) kmin = min(kmin, key[i]), kmax = max(kmax, key[i]);
+    }
+    const uint32_t nb = max(kMinBuckets, 1u << (32 - __clz(int(m - 1))));
+    for (uint32_t j = tid; j <= nb; j += kThreads) ts.bkt.start[j] = 0;
+    kmin = wave_min(kmin);
+    kmax = wave_max(kmax);
+    if (lane == 0) ts.bkt.wmin[w] = kmin, ts.bkt.wmax[w] = kmax;
+    __syncthreads();
+    uint32_t lo = ts.bkt.wmin[0], hi = ts.bkt.wmax[0];
+#pragma unroll
+    for (uint32_t q = 1; q < kWaves; ++q) lo = min(lo, ts.bkt.wmin[q]), hi = max(hi, ts.bkt.wmax[q]);
+    const float scale = float(nb) / (float(hi - lo) + 1.0f);
+#pragma unroll
+    for (uint32_t i = 0; i < kMaxItems; ++i)
+      if (tid + i * kThreads < m) slot[i] = atomicAdd(&ts.bkt.start[bucket_of(key[i], lo, scale, nb)], 1u);
+    __syncthreads();
+    // exclusive scan of the counts: thread tid takes nb / kThreads consecutive buckets
+    const uint32_t per = nb / kThreads;
+    uint32_t c[kScanPer], sum = 0, biggest = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < kScanPer; ++j) {
+      c[j] = j < per ? ts.bkt.start[tid * per + j] : 0u;
+      sum += c[j];
+      biggest = max(biggest, c[j]);
+    }
+    uint32_t run = block_exclusive_scan<uint32_t, kThreads>(sum, nullptr, ts.bkt.wsum);
+#pragma unroll
+    for (uint32_t j = 0; j < kScanPer; ++j)
+      if (j < per) {
+        ts.bkt.start[tid * per + j] = run;
+        run += c[j];
+      }
+    if (tid == 0) ts.bkt.start[nb] = m;
+    if (!__syncthreads_or(biggest > kBucketLimit)) {
+#pragma unroll
+      for (uint32_t i = 0; i < kMaxItems; ++i)
+        if (tid + i * kThreads < m)
+          ts.bkt.entry[ts.bkt.start[bucket_of(key[i], lo, scale, nb)] + slot[i]] = (uint64_t(key[i]) << 32) | spl[i];
+      __syncthreads();
+      for (uint32_t q = tid; q < m; q += kThreads) {
+        const uint64_t me = ts.bkt.entry[q];
+        const uint32_t k = uint32_t(me >> 32);
+        const uint32_t b = bucket_of(k, lo, scale, nb);
+        const uint32_t b0 = ts.bkt.start[b], b1 = ts.bkt.start[b + 1];
+        uint32_t r = b0;
+        for (uint32_t f = b0; f < b1; ++f) r += ts.bkt.entry[f] < me ? 1u : 0u;
+        emit(r, uint32_t(me), k);
+      }
+      return;
+    }
+    // a crowded bucket: the radix sort (the barrier above ends every read of the bucket layout)
+    for (uint32_t e = tid; e < m; e += kThreads) {
+      ts.lsd.key[0][e] = depth_bits(splat_at(e));
+      ts.lsd.pos[0][e] = uint16_t(e);
+    }
+    __syncthreads();
+    const uint32_t res = sort_list(ts.lsd.key[0], ts.lsd.key[1], ts.lsd.pos[0], ts.lsd.pos[1], m, ts.lsd.sh);
+    for (uint32_t e = tid; e < m; e += kThreads) emit(e, splat_at(ts.lsd.pos[res][e]), ts.lsd.key[res][e]);
+  } else {
+    uint32_t *k0 = gk0 + start, *k1 = gk1 + start, *p0 = gp0 + start, *p1 = gp1 + start;
+    for (uint32_t e = tid; e < m; e += kThreads) {
+      k0[e] = depth_bits(splat_at(e));
+      p0[e] = e;
+    }
+    __syncthreads();
+    const uint32_t res = sort_list(k0, k1, p0, p1, m, ts.lsd.sh);
+    const uint32_t* kr = res ? k1 : k0;
+    const uint32_t* pr = res ? p1 : p0;
+    for (uint32_t e = tid; e < m; e += kThreads) emit(e, splat_at(pr[e]), kr[e]);
+  }
+}
+
+}  // namespace
+
+void launch_tile_depth(hipStream_t s, const uint32_t* list, const uint32_t* list_vals, uint32_t idx_bits,
+                       const uint32_t* ranges, uint64_t pairs_cap, const uint64_t* pairs_dev, uint32_t num_tiles,
+                       const float* depths, uint32_t n, uint32_t* vals_out, uint64_t* keys_out, uint32_t* gk0,
+                       uint32_t* gk1, uint32_t* gp0, uint32_t* gp1) {
+  if (num_tiles)
+    hipLaunchKernelGGL(k_tile_depth, dim3(num_tiles), dim3(kThreads), 0, s, list, list_vals, idx_bits, ranges,
+                       pairs_cap, pairs_dev, num_tiles, depths, n, vals_out, keys_out, gk0, gk1, gp0, gp1);
+}
+
+uint32_t tile_depth_capacity() { return kCap; }
+
+}  // namespace gsr

@@ -6,7 +6,7 @@ from gpuhelp import banner, custom_scene, dev, host, oracle_bins, scene
 
 pytestmark = pytest.mark.gpu
 
-SCHEMES = {"presort": 0, "key64": 1}
+SCHEMES = {"presort": 0, "key64": 1, "tile_depth": 2}
 
 
 @pytest.fixture(scope="module")
@@ -220,3 +220,34 @@ def test_bin_ellipse_rule_ragged_images(ctx, w, h):
                               oracle.bin(sc.splats, sc.depths, w, h, rule="ellipse"))
     finally:
         set_rule(ctx, "box")
+
+
+@pytest.mark.parametrize("w,h,n,cluster", [(16, 16, 6000, 0.0), (64, 48, 30000, 0.0), (800, 800, 200000, 0.3)])
+def test_tile_depth_long_lists(ctx, w, h, n, cluster):
+    """Tile lists longer than the tile-first scheme's on-chip capacity (3456 pairs) are sorted through the arena
+    instead: one tile of 6000 pairs; twelve tiles of 5-11 thousand; and 16 tiles of up to 25 thousand (30% of the
+    splats in a 48-pixel square) among 2,484 short ones, both forms in one launch. Bit-exact against the oracle on a
+    fresh context (no count seen: the first call takes the tile-first path) and again with the count seen."""
+    import oracle
+    from differentiable_gaussian_splatting_amd import gsr
+    banner(f"bin tile_depth long lists {w}x{h} n={n} cluster={cluster}")
+    rng = np.random.default_rng(n)
+    s = np.exp(rng.uniform(np.log(0.5), np.log(8.0), n))
+    sp = np.zeros((n, 9), np.float32)
+    sp[:, 0], sp[:, 1] = rng.uniform(0, w, n), rng.uniform(0, h, n)
+    k = int(cluster * n)
+    sp[:k, 0], sp[:k, 1] = rng.uniform(376, 424, k), rng.uniform(376, 424, k)
+    sp[:, 2] = sp[:, 4] = 1.0 / s ** 2
+    sp[:, 5:8] = rng.uniform(0, 1, (n, 3))
+    sp[:, 8] = rng.uniform(0.05, 1.0, n)
+    depths = rng.uniform(0.1, 10.0, n).astype(np.float32)
+    depths[: n // 10] = depths[n // 10: 2 * (n // 10)]  # equal depths: ties keep splat order
+    ref = oracle.bin(sp, depths, w, h)
+    lens = ref.ranges[:, 1].astype(np.int64) - ref.ranges[:, 0]
+    assert lens.max() > 3456
+    c = gsr.Context(0)
+    try:
+        assert_bins_equal(c, sp, depths, w, h, "tile_depth", ref)
+        assert_bins_equal(c, sp, depths, w, h, "tile_depth", ref)
+    finally:
+        c.close()

@@ -39,7 +39,7 @@ def bin_and_compare(ctx, splats, depths, w, h, ref):
     return b
 
 
-@pytest.mark.parametrize("scheme,rule", [(0, 0), (1, 0), (0, 1)])
+@pytest.mark.parametrize("scheme,rule", [(0, 0), (1, 0), (0, 1), (2, 0), (2, 1)])
 def test_sync_free_bins_equal_the_oracle(scheme, rule):
     """First call on a fresh context: no count seen, so it waits once; the later calls size their buffers from the
     counts seen (smaller scenes after a larger one, and the same scene again) and do not wait."""
