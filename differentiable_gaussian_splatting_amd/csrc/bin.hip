@@ -416,6 +416,224 @@ __global__ __launch_bounds__(kThreads) void k_emit_ellipse(const float* __restri
     }
 }
 
+// Fused counting sort of the pairs by tile (the tile-first scheme under the box rule), in place of emitting keys and
+// radix-sorting them, and without the count scan. Block b of kFuseBlock consecutive splats (in index order) computes
+// their rectangles and counts, counts its pairs per tile in LDS and writes the counts as row b of a [blocks][tiles]
+// table (k_prep_rows); a column scan turns each row into the block's offset in each tile's list and gives each
+// tile's total (k_tile_cols), a scan of the totals gives the tiles' starts and the ranges (k_tile_starts); the same
+// blocks then enumerate their pairs again (from the rectangles and a block scan of the counts) and place each splat
+// at the next free slot of their stretch of the tile's list (an LDS counter per tile; k_tile_scatter). Within a
+// stretch the order is whatever the LDS atomics give: the per-tile sort that follows orders each list by (depth
+// bits, splat), which is unique, so the bins do not depend on it. The pairs are enumerated as in k_emit (chunks of
+// pairs, owner marks and a running maximum).
+constexpr uint32_t kFuseThreads = 1024;                  // a splat per thread
+constexpr uint32_t kFuseBlock = kFuseThreads;            // splats per block
+constexpr uint32_t kFuseMaxTiles = 8192;                 // the per-tile LDS counters (32 KB)
+constexpr uint32_t kColTiles = 64, kColThreads = 1024;   // the column scan: 64 tiles by 16 stretches of rows
+constexpr uint32_t kColParts = kColThreads / kColTiles;
+constexpr uint32_t kColBatch = 32;                       // rows loaded at once
+constexpr uint32_t kStartThreads = 1024, kStartPer = kFuseMaxTiles / kStartThreads;
+
+// Logical block of physical block i of nb. Workgroups are dealt to the eight dies in turn (die i mod 8); this hands
+// die x a contiguous run of logical blocks instead, so that each die writes one contiguous stretch of every tile's
+// list and its L2 merges the partial lines of that stretch before they go to memory.
+__device__ __forceinline__ uint32_t die_band(uint32_t i, uint32_t nb) {
+  const uint32_t x = i % 8u, j = i / 8u, per = nb / 8u, rem = nb % 8u;
+  return x * per + min(x, rem) + j;
+}
+
+// Enumerates the pairs of a block of kFuseBlock splats (thread tid holds splat tid of the block): s_off[0..kFuseBlock]
+// are the splats' block-local first pair positions (s_off[kFuseBlock] = the block's total, `end` the pairs to
+// enumerate, end <= that total), s_tx0 / s_ty0 / s_w their rectangles. Chunks of kPer pairs per thread, as k_emit.
+// Calls f(q, tile) for each pair, q the splat's index in the block. Every thread of the workgroup must call it.
+template <typename F>
+__device__ __forceinline__ void for_each_pair(const uint32_t* s_off, const uint32_t* s_tx0, const uint32_t* s_ty0,
+                                              const uint32_t* s_w, uint32_t end, uint32_t tiles_x, uint32_t* s_mark,
+                                              uint32_t* smem, F f) {
+  constexpr uint32_t kPer = 4, kChunk = kPer * kFuseThreads;
+  const uint32_t tid = threadIdx.x;
+  uint32_t carry = 0;
+  for (uint32_t c0 = 0; c0 < end; c0 += kChunk) {
+#pragma unroll
+    for (uint32_t e = 0; e < kPer; ++e) s_mark[e * kFuseThreads + tid] = 0;
+    __syncthreads();
+    {  // splats with pairs have distinct first positions
+      const uint32_t first = s_off[tid];
+      if (s_off[tid + 1] > first && first >= c0 && first < c0 + kChunk) s_mark[first - c0] = tid + 1;
+    }
+    __syncthreads();
+    uint32_t m[kPer];
+    uint32_t run = 0;
+#pragma unroll
+    for (uint32_t e = 0; e < kPer; ++e) {
+      run = max(run, s_mark[kPer * tid + e]);
+      m[e] = run;
+    }
+    uint32_t chunk_max;
+    const uint32_t before = block_exclusive_max<kFuseThreads>(run, carry, &chunk_max, smem);
+    const uint32_t p0 = c0 + kPer * tid;
+#pragma unroll
+    for (uint32_t e = 0; e < kPer; ++e) {
+      const uint32_t p = p0 + e;
+      const uint32_t owner = max(before, m[e]);  // >= 1 for every pair below end
+      if (p < end && owner > 0) {
+        const uint32_t q = owner - 1;
+        const uint32_t k = p - s_off[q];
+        const uint32_t w = s_w[q];
+        const uint32_t r = div_small(k, w);
+        f(q, (s_ty0[q] + r) * tiles_x + (s_tx0[q] + (k - r * w)));
+      }
+    }
+    carry = chunk_max;
+  }
+}
+
+// k_prep for the fused counting sort (box rule, num_tiles <= kFuseMaxTiles): blocks of kFuseBlock splats write
+// each splat's rectangle and count, the block's count total in part[block] (k_total sums them), and the block's
+// pairs per tile as row `block` of `rows`.
+__global__ __launch_bounds__(kFuseThreads) void k_prep_rows(const float* __restrict__ splats,
+                                                            const float* __restrict__ depths, uint32_t n,
+                                                            uint32_t tiles_x, uint32_t tiles_y,
+                                                            uint4* __restrict__ rects, uint32_t* __restrict__ counts,
+                                                            uint64_t* __restrict__ part, uint32_t num_tiles,
+                                                            uint32_t* __restrict__ rows) {
+  extern __shared__ uint32_t s_tile[];  // num_tiles counters
+  __shared__ uint32_t s_off[kFuseBlock + 1], s_tx0[kFuseBlock], s_ty0[kFuseBlock], s_w[kFuseBlock];
+  __shared__ uint32_t s_mark[4 * kFuseThreads];
+  __shared__ uint32_t smem[kFuseThreads / kWave];
+  const uint32_t tid = threadIdx.x, i = blockIdx.x * kFuseBlock + tid;
+  for (uint32_t t = tid; t < num_tiles; t += kFuseThreads) s_tile[t] = 0;
+  Rect r{0, 0, 0, 0};
+  if (i < n) {
+    r = tile_rect(splats + size_t(i) * 9, depths[i], tiles_x, tiles_y);
+    rects[i] = make_uint4(r.tx0, r.ty0, r.w, r.h);
+    counts[i] = r.w * r.h;
+  }
+  s_tx0[tid] = r.tx0;
+  s_ty0[tid] = r.ty0;
+  s_w[tid] = r.w ? r.w : 1u;
+  uint32_t total;
+  s_off[tid] = block_exclusive_scan<uint32_t, kFuseThreads>(r.w * r.h, &total, smem);
+  if (tid == 0) {
+    s_off[kFuseBlock] = total;
+    part[blockIdx.x] = total;
+  }
+  __syncthreads();
+  for_each_pair(s_off, s_tx0, s_ty0, s_w, total, tiles_x, s_mark, smem,
+                [&](uint32_t, uint32_t tile) { atomicAdd(&s_tile[tile], 1u); });
+  __syncthreads();
+  uint32_t* const row = rows + size_t(blockIdx.x) * num_tiles;
+  for (uint32_t t = tid; t < num_tiles; t += kFuseThreads) row[t] = s_tile[t];
+}
+
+// The scatter: the workgroup takes block blk (die-banded) of kFuseBlock splats, enumerates its pairs again from the
+// rectangles and counts, and puts each pair's splat at list[tile_start[tile] + rows[blk][tile] + its slot] (rows and
+// tile_start as k_tile_cols and k_tile_starts leave them). Nothing when the pairs exceed the capacity.
+__global__ __launch_bounds__(kFuseThreads) void k_tile_scatter(const uint4* __restrict__ rects,
+                                                               const uint32_t* __restrict__ counts, uint32_t n,
+                                                               uint32_t tiles_x, uint32_t num_tiles,
+                                                               uint64_t pairs_cap,
+                                                               const uint64_t* __restrict__ pairs_dev,
+                                                               const uint32_t* __restrict__ rows,
+                                                               const uint32_t* __restrict__ tile_start,
+                                                               uint32_t* __restrict__ list) {
+  extern __shared__ uint32_t s_tile[];  // num_tiles counters
+  __shared__ uint32_t s_off[kFuseBlock + 1], s_tx0[kFuseBlock], s_ty0[kFuseBlock], s_w[kFuseBlock];
+  __shared__ uint32_t s_mark[4 * kFuseThreads];
+  __shared__ uint32_t smem[kFuseThreads / kWave];
+  const uint32_t tid = threadIdx.x;
+  const uint32_t blk = die_band(blockIdx.x, gridDim.x);
+  const uint32_t j0 = blk * kFuseBlock, i = j0 + tid;
+  const uint32_t* const row = rows + size_t(blk) * num_tiles;
+  for (uint32_t t = tid; t < num_tiles; t += kFuseThreads) s_tile[t] = tile_start[t] + row[t];
+  uint32_t c = 0;
+  uint4 r = make_uint4(0, 0, 1, 0);
+  if (i < n) {
+    c = counts[i];
+    r = rects[i];
+  }
+  s_tx0[tid] = r.x;
+  s_ty0[tid] = r.y;
+  s_w[tid] = r.z ? r.z : 1u;
+  uint32_t total;
+  s_off[tid] = block_exclusive_scan<uint32_t, kFuseThreads>(c, &total, smem);
+  if (tid == 0) s_off[kFuseBlock] = total;
+  const uint32_t end = count_within(pairs_dev, pairs_cap) ? total : 0u;  // 0: nothing fits, nothing is written
+  __syncthreads();
+  for_each_pair(s_off, s_tx0, s_ty0, s_w, end, tiles_x, s_mark, smem,
+                [&](uint32_t q, uint32_t tile) { list[atomicAdd(&s_tile[tile], 1u)] = j0 + q; });
+}
+
+// Column scan of the [nblk][num_tiles] count table: each row becomes the block's exclusive offset within each
+// tile's pairs, and tile_total[tile] receives the column's sum. A workgroup takes kColTiles tiles; its kColParts
+// thread groups each sum a stretch of consecutive rows, then rewrite them starting from the sums of the stretches
+// before. The row loads of 64 consecutive tiles are 256-byte segments.
+__global__ __launch_bounds__(kColThreads) void k_tile_cols(uint32_t* __restrict__ rows, uint32_t nblk,
+                                                           uint32_t num_tiles, uint32_t* __restrict__ tile_total) {
+  __shared__ uint32_t s_sum[kColParts][kColTiles];
+  const uint32_t lt = threadIdx.x % kColTiles, part = threadIdx.x / kColTiles;
+  const uint32_t t = blockIdx.x * kColTiles + lt;
+  const uint32_t per = (nblk + kColParts - 1) / kColParts;
+  const uint32_t b0 = min(nblk, part * per), b1 = min(nblk, b0 + per);
+  const bool live = t < num_tiles;
+  uint32_t sum = 0;
+  for (uint32_t c = b0; c < b1; c += kColBatch) {
+    uint32_t v[kColBatch];
+#pragma unroll
+    for (uint32_t i = 0; i < kColBatch; ++i) v[i] = live && c + i < b1 ? rows[size_t(c + i) * num_tiles + t] : 0u;
+#pragma unroll
+    for (uint32_t i = 0; i < kColBatch; ++i) sum += v[i];
+  }
+  s_sum[part][lt] = sum;
+  __syncthreads();
+  uint32_t run = 0, total = 0;
+#pragma unroll
+  for (uint32_t q = 0; q < kColParts; ++q) {
+    const uint32_t x = s_sum[q][lt];
+    if (q < part) run += x;
+    total += x;
+  }
+  if (!live) return;
+  if (part == 0) tile_total[t] = total;
+  for (uint32_t c = b0; c < b1; c += kColBatch) {
+    uint32_t v[kColBatch];
+#pragma unroll
+    for (uint32_t i = 0; i < kColBatch; ++i) v[i] = c + i < b1 ? rows[size_t(c + i) * num_tiles + t] : 0u;
+#pragma unroll
+    for (uint32_t i = 0; i < kColBatch; ++i) {
+      if (c + i < b1) rows[size_t(c + i) * num_tiles + t] = run;
+      run += v[i];
+    }
+  }
+}
+
+// One workgroup: tile_start = the exclusive scan of tile_total (num_tiles <= kFuseMaxTiles, kStartPer consecutive
+// tiles per thread) and the ranges [start, start + total); every range empty when the pairs exceed the capacity.
+__global__ __launch_bounds__(kStartThreads) void k_tile_starts(const uint32_t* __restrict__ tile_total,
+                                                               uint32_t num_tiles, uint64_t pairs_cap,
+                                                               const uint64_t* __restrict__ pairs_dev,
+                                                               uint32_t* __restrict__ tile_start,
+                                                               uint32_t* __restrict__ ranges) {
+  __shared__ uint32_t smem[kStartThreads / kWave];
+  const uint32_t t0 = threadIdx.x * kStartPer;
+  const bool fits = count_within(pairs_dev, pairs_cap) > 0;
+  uint32_t v[kStartPer], sum = 0;
+#pragma unroll
+  for (uint32_t i = 0; i < kStartPer; ++i) {
+    v[i] = fits && t0 + i < num_tiles ? tile_total[t0 + i] : 0u;
+    sum += v[i];
+  }
+  uint32_t run = block_exclusive_scan<uint32_t, kStartThreads>(sum, nullptr, smem);
+#pragma unroll
+  for (uint32_t i = 0; i < kStartPer; ++i)
+    if (t0 + i < num_tiles) {
+      tile_start[t0 + i] = run;
+      ranges[2 * (t0 + i)] = run;
+      ranges[2 * (t0 + i) + 1] = run + v[i];
+      run += v[i];
+    }
+}
+
 // Per-tile ranges from the sorted keys: the boundary between pairs i-1 and i (i in [0, P]) opens the ranges of
 // the tiles after the previous pair's and closes those before the current pair's. Each thread takes kRangeItems
 // consecutive boundaries (16-byte loads of 32-bit keys). With keys_final (the presort scheme when no sort pass
@@ -592,6 +810,9 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   const bool tile_first = ctx->bin_scheme == GSR_BIN_TILE_DEPTH &&
                           ctx->last_pairs <= uint64_t(kTileFirstAvg) * num_tiles;
   const bool presort = ctx->bin_scheme == GSR_BIN_PRESORT || (ctx->bin_scheme == GSR_BIN_TILE_DEPTH && !tile_first);
+  // The counting sort by tile replaces emission and the tile sort under the box rule when the per-tile counters fit
+  // LDS.
+  const bool fused = tile_first && !ellipse && n && num_tiles <= kFuseMaxTiles;
   // Without a wait only once there is a count or a reservation to size the pair buffers from.
   const bool sync_free = ctx->bin_sync_free && n && (ctx->pair_hint > 0 || ctx->pair_reserved > 0);
 
@@ -623,13 +844,24 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   // the depth sort runs.
   timing_mark(ctx, GSR_STAGE_BIN, s, false);
   hipError_t e = hipSuccess;
-  if (n) {
+  const uint32_t nb_fuse = grid_for(n, kFuseBlock);
+  uint32_t* rows = nullptr;
+  if (fused) {
+    if ((st = grow(ctx, a.tile_rows, (size_t(nb_fuse) + 2) * num_tiles * 4))) return st;
+    rows = static_cast<uint32_t*>(a.tile_rows.ptr);
+    hipLaunchKernelGGL(k_prep_rows, dim3(nb_fuse), dim3(kFuseThreads), size_t(num_tiles) * 4, s, splats, depths, n,
+                       tiles_x, tiles_y, rects, counts, part, uint32_t(num_tiles), rows);
+    hipLaunchKernelGGL(k_total, dim3(1), dim3(kThreads), 0, s, static_cast<const uint64_t*>(part), nb_fuse,
+                       offsets + n, a.host_total_dev);
+  } else if (n) {
     hipLaunchKernelGGL(k_prep, dim3(nb_prep), dim3(kThreads), 0, s, splats, depths, n, tiles_x, tiles_y, ellipse,
                        rects, counts,
                        presort ? ok : static_cast<uint32_t*>(nullptr), presort ? ov : static_cast<uint32_t*>(nullptr),
                        count_shift, part);
     hipLaunchKernelGGL(k_total, dim3(1), dim3(kThreads), 0, s, static_cast<const uint64_t*>(part), nb_prep,
                        offsets + n, a.host_total_dev);
+  }
+  if (n) {
     if ((st = check_launch(ctx, "gsr_bin rectangles"))) return st;
     e = hipEventRecord(a.total_ready, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "gsr_bin pair count readback");
@@ -651,8 +883,9 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     timing_mark(ctx, GSR_STAGE_DEPTH_SORT, s, true);
     order = ov;
   }
-  // offsets in emission order (depth order for the presort scheme); the scan rewrites offsets[n] with the same total
-  if (n) {
+  // offsets in emission order (depth order for the presort scheme); the scan rewrites offsets[n] with the same total.
+  // The fused counting sort enumerates each block's pairs from a block scan of its counts instead.
+  if (n && !fused) {
     if (pack_counts) {
       // the sorted values carry the counts: both launches read them in place
       hipLaunchKernelGGL(k_scan_reduce, dim3(nb_scan), dim3(kThreads), 0, s, static_cast<const uint32_t*>(ov),
@@ -728,6 +961,33 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
                        kb[res], static_cast<const uint32_t*>(v0), P, pairs_dev, uint32_t(num_tiles), depths, n,
                        static_cast<uint64_t*>(nullptr), ranges, idx_bits);
     sorted_v = v0;
+  } else if (fused) {
+    // the counting sort by tile (rows counted by k_prep_rows), then each tile's list by (depth, splat) on chip
+    // (tile_depth.hip)
+    uint32_t* tile_total = rows + size_t(nb_fuse) * num_tiles;
+    uint32_t* tile_start = tile_total + num_tiles;
+    uint32_t* list = static_cast<uint32_t*>(a.vals[1].ptr);
+    timing_mark(ctx, GSR_STAGE_TILE_SORT, s, false);
+    hipLaunchKernelGGL(k_tile_cols, dim3(grid_for(num_tiles, kColTiles)), dim3(kColThreads), 0, s, rows, nb_fuse,
+                       uint32_t(num_tiles), tile_total);
+    hipLaunchKernelGGL(k_tile_starts, dim3(1), dim3(kStartThreads), 0, s, static_cast<const uint32_t*>(tile_total),
+                       uint32_t(num_tiles), P, pairs_dev, tile_start, ranges);
+    hipLaunchKernelGGL(k_tile_scatter, dim3(nb_fuse), dim3(kFuseThreads), size_t(num_tiles) * 4, s,
+                       static_cast<const uint4*>(rects), static_cast<const uint32_t*>(counts), n, tiles_x,
+                       uint32_t(num_tiles), P, pairs_dev, static_cast<const uint32_t*>(rows),
+                       static_cast<const uint32_t*>(tile_start), list);
+    timing_mark(ctx, GSR_STAGE_TILE_SORT, s, true);
+    if (ctx->bin_keys) {
+      if ((st = grow(ctx, a.order_alt, std::max<size_t>(size_t(n) * 8, size_t(P) * 8)))) return st;
+      final_k = static_cast<uint64_t*>(a.order_alt.ptr);
+    }
+    uint32_t* k0 = static_cast<uint32_t*>(a.keys[0].ptr);
+    uint32_t* k1 = static_cast<uint32_t*>(a.keys[1].ptr);
+    timing_mark(ctx, GSR_STAGE_TILE_DEPTH, s, false);
+    launch_tile_depth(s, static_cast<const uint32_t*>(nullptr), list, 32u, false, ranges, P, pairs_dev,
+                      uint32_t(num_tiles), depths, n, v0, final_k, k0, k0 + P, k1, k1 + P);
+    timing_mark(ctx, GSR_STAGE_TILE_DEPTH, s, true);
+    sorted_v = v0;
   } else if (tile_first) {
     // Pairs emitted splat by splat (index order), sorted stably by tile alone, then each tile's list by depth on
     // chip (tile_depth.hip): splat and tile id packed in one word when they fit, else tile ids with a splat array.
@@ -790,7 +1050,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
       final_k = static_cast<uint64_t*>(a.order_alt.ptr);
     }
     timing_mark(ctx, GSR_STAGE_TILE_DEPTH, s, false);
-    launch_tile_depth(s, list, list_vals, tpacked ? idx_bits : 32u, ranges, P, pairs_dev, uint32_t(num_tiles),
+    launch_tile_depth(s, list, list_vals, tpacked ? idx_bits : 32u, true, ranges, P, pairs_dev, uint32_t(num_tiles),
                       depths, n, vals_out, final_k, scratch[0], scratch[1], scratch[2], scratch[3]);
     timing_mark(ctx, GSR_STAGE_TILE_DEPTH, s, true);
     sorted_v = vals_out;

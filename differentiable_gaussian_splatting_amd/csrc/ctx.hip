@@ -34,7 +34,7 @@ static void for_each_buffer(Arena& a, F f) {
   for (DevBuf* b : {&a.keys[0], &a.keys[1], &a.vals[0], &a.vals[1], &a.counts, &a.offsets, &a.order, &a.order_alt,
                     &a.order_vals, &a.order_vals_alt, &a.scan_part, &a.hist, &a.digit_tot,
                     &a.ranges, &a.rects,
-                    &a.tile_order_ext, &a.tile_cost, &a.loss_part, &a.loss_maps, &a.grad_fixed})
+                    &a.tile_order_ext, &a.tile_cost, &a.tile_rows, &a.loss_part, &a.loss_maps, &a.grad_fixed})
     f(*b);
 }
 

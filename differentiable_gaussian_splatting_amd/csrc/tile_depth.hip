@@ -18,8 +18,9 @@
 // steps through global scratch. Per pass: a digit histogram of the whole list (per-wave LDS counts), its exclusive
 // scan, and a stable scatter of chunks of 1024 keys in list order, each key ranked among the equal digits of its
 // wave by a 64-lane ballot match (as the device-wide sort's scatter) and placed after those of earlier waves and
-// chunks. A pass whose digit is the same for every key of the list is skipped. Being stable, it relies on the list's
-// index order for the ties.
+// chunks. A pass whose digit is the same for every key of the list is skipped. Being stable, it needs the list in
+// splat order for the ties: a list in any other order (the fused counting sort by tile places each block's pairs in
+// no particular order within its stretch of the tile's list) is first sorted by splat index, the same way.
 #include "gsr_internal.hpp"
 #include "scan_common.hpp"
 
@@ -155,13 +156,42 @@ __device__ __forceinline__ uint32_t sort_list(uint32_t* k0, uint32_t* k1, PosT* 
   return src;
 }
 
+// The list's positions in (depth bits, splat) order with their depth bits, through the buffer pairs (k0, p0) and
+// (k1, p1); returns which pair holds them. Unless the list is in splat order, it is first sorted by splat index
+// (unique keys), and the depth sort then runs on that order.
+template <typename PosT, typename SplatAt, typename DepthBits>
+__device__ __forceinline__ uint32_t radix_order(uint32_t* k0, uint32_t* k1, PosT* p0, PosT* p1, uint32_t m,
+                                                bool ordered, SplatAt splat_at, DepthBits depth_bits,
+                                                SortShared& sh) {
+  const uint32_t tid = threadIdx.x;
+  uint32_t r = 0;
+  if (!ordered) {
+    for (uint32_t e = tid; e < m; e += kThreads) {
+      k0[e] = splat_at(e);
+      p0[e] = PosT(e);
+    }
+    __syncthreads();
+    r = sort_list(k0, k1, p0, p1, m, sh);
+  } else {
+    for (uint32_t e = tid; e < m; e += kThreads) p0[e] = PosT(e);
+  }
+  uint32_t* const ka = r ? k1 : k0;
+  uint32_t* const kb = r ? k0 : k1;
+  PosT* const pa = r ? p1 : p0;
+  PosT* const pb = r ? p0 : p1;
+  for (uint32_t e = tid; e < m; e += kThreads) ka[e] = depth_bits(splat_at(pa[e]));
+  __syncthreads();
+  return sort_list(ka, kb, pa, pb, m, sh) ? 1 - r : r;
+}
+
 // One workgroup per tile. The tile's list is list[start..end) (ranges, clamped to the pair count): packed words
-// (tile << idx_bits) | splat when list_vals is null, else list_vals holds the splats. Writes vals_out[start + e] =
-// the e-th splat in (depth bits, index) order and, when keys_out is not null, keys_out[start + e] =
-// (tile << 32) | its depth bits. Lists longer than kCap use the scratch arrays gk0, gk1, gp0, gp1 (P entries each,
-// the tile's stretch [start, end) of them).
+// (tile << idx_bits) | splat when list_vals is null, else list_vals holds the splats; `ordered` says the list is in
+// ascending splat order. Writes vals_out[start + e] = the e-th splat in (depth bits, index) order and, when keys_out
+// is not null, keys_out[start + e] = (tile << 32) | its depth bits. Lists longer than kCap use the scratch arrays
+// gk0, gk1, gp0, gp1 (P entries each, the tile's stretch [start, end) of them).
 __global__ __launch_bounds__(kThreads) void k_tile_depth(const uint32_t* __restrict__ list,
                                                          const uint32_t* __restrict__ list_vals, uint32_t idx_bits,
+                                                         bool ordered,
                                                          const uint32_t* __restrict__ ranges, uint64_t pairs_cap,
                                                          const uint64_t* __restrict__ pairs_dev, uint32_t num_tiles,
                                                          const float* __restrict__ depths, uint32_t n,
@@ -243,21 +273,14 @@ __global__ __launch_bounds__(kThreads) void k_tile_depth(const uint32_t* __restr
       return;
     }
     // a crowded bucket: the radix sort (the barrier above ends every read of the bucket layout)
-    for (uint32_t e = tid; e < m; e += kThreads) {
-      ts.lsd.key[0][e] = depth_bits(splat_at(e));
-      ts.lsd.pos[0][e] = uint16_t(e);
-    }
-    __syncthreads();
-    const uint32_t res = sort_list(ts.lsd.key[0], ts.lsd.key[1], ts.lsd.pos[0], ts.lsd.pos[1], m, ts.lsd.sh);
-    for (uint32_t e = tid; e < m; e += kThreads) emit(e, splat_at(ts.lsd.pos[res][e]), ts.lsd.key[res][e]);
+    const uint32_t res = radix_order(ts.lsd.key[0], ts.lsd.key[1], ts.lsd.pos[0], ts.lsd.pos[1], m, ordered, splat_at,
+                                     depth_bits, ts.lsd.sh);
+    const uint32_t* kr = res ? ts.lsd.key[1] : ts.lsd.key[0];
+    const uint16_t* pr = res ? ts.lsd.pos[1] : ts.lsd.pos[0];
+    for (uint32_t e = tid; e < m; e += kThreads) emit(e, splat_at(pr[e]), kr[e]);
   } else {
     uint32_t *k0 = gk0 + start, *k1 = gk1 + start, *p0 = gp0 + start, *p1 = gp1 + start;
-    for (uint32_t e = tid; e < m; e += kThreads) {
-      k0[e] = depth_bits(splat_at(e));
-      p0[e] = e;
-    }
-    __syncthreads();
-    const uint32_t res = sort_list(k0, k1, p0, p1, m, ts.lsd.sh);
+    const uint32_t res = radix_order(k0, k1, p0, p1, m, ordered, splat_at, depth_bits, ts.lsd.sh);
     const uint32_t* kr = res ? k1 : k0;
     const uint32_t* pr = res ? p1 : p0;
     for (uint32_t e = tid; e < m; e += kThreads) emit(e, splat_at(pr[e]), kr[e]);
@@ -267,12 +290,12 @@ __global__ __launch_bounds__(kThreads) void k_tile_depth(const uint32_t* __restr
 }  // namespace
 
 void launch_tile_depth(hipStream_t s, const uint32_t* list, const uint32_t* list_vals, uint32_t idx_bits,
-                       const uint32_t* ranges, uint64_t pairs_cap, const uint64_t* pairs_dev, uint32_t num_tiles,
-                       const float* depths, uint32_t n, uint32_t* vals_out, uint64_t* keys_out, uint32_t* gk0,
-                       uint32_t* gk1, uint32_t* gp0, uint32_t* gp1) {
+                       bool ordered, const uint32_t* ranges, uint64_t pairs_cap, const uint64_t* pairs_dev,
+                       uint32_t num_tiles, const float* depths, uint32_t n, uint32_t* vals_out, uint64_t* keys_out,
+                       uint32_t* gk0, uint32_t* gk1, uint32_t* gp0, uint32_t* gp1) {
   if (num_tiles)
-    hipLaunchKernelGGL(k_tile_depth, dim3(num_tiles), dim3(kThreads), 0, s, list, list_vals, idx_bits, ranges,
-                       pairs_cap, pairs_dev, num_tiles, depths, n, vals_out, keys_out, gk0, gk1, gp0, gp1);
+    hipLaunchKernelGGL(k_tile_depth, dim3(num_tiles), dim3(kThreads), 0, s, list, list_vals, idx_bits, ordered,
+                       ranges, pairs_cap, pairs_dev, num_tiles, depths, n, vals_out, keys_out, gk0, gk1, gp0, gp1);
 }
 
 uint32_t tile_depth_capacity() { return kCap; }
