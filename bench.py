@@ -69,7 +69,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="iter410k")
-    ap.add_argument("--bin-scheme", choices=["presort", "key64"], default="presort")
+    ap.add_argument("--bin-scheme", choices=["tile_depth", "presort", "key64"], default="tile_depth")
     ap.add_argument("--raster-skip", type=int, choices=[0, 1], default=1)
     ap.add_argument("--bin-rule", choices=["box", "ellipse"], default="box")
     ap.add_argument("--repeats", type=int, default=3, help="timed repeats of K steps (median and spread reported)")
@@ -183,8 +183,7 @@ def main():
     adam_host = scenes.make_adam_groups(N, seed=sc.spec.seed)
 
     ctx = gsr.Context(0)
-    gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SCHEME, gsr.GSR_BIN_PRESORT if args.bin_scheme == "presort"
-                       else gsr.GSR_BIN_KEY64)
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SCHEME, scheme_opt(gsr, args.bin_scheme))
     gsr.gsr_set_option(ctx, gsr.GSR_OPT_RASTER_SKIP, args.raster_skip)
     gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_RULE, gsr.GSR_BIN_ELLIPSE if args.bin_rule == "ellipse" else gsr.GSR_BIN_BOX)
     splats = torch.from_numpy(sc.splats).cuda()
@@ -252,7 +251,10 @@ def main():
     # the repeats and their standard deviation.
     kernel_stage = {"bin": gsr.GSR_STAGE_BIN, "forward": gsr.GSR_STAGE_FORWARD, "backward": gsr.GSR_STAGE_BACKWARD,
                     "adam": gsr.GSR_STAGE_ADAM, "depth_sort": gsr.GSR_STAGE_DEPTH_SORT,
-                    "tile_sort": gsr.GSR_STAGE_TILE_SORT}
+                    "tile_sort": gsr.GSR_STAGE_TILE_SORT, "tile_scan": gsr.GSR_STAGE_TILE_SCAN,
+                    "tile_depth": gsr.GSR_STAGE_TILE_DEPTH}
+    # the binning's inner stages a scheme does not run record nothing (0 ms)
+    optional = {"depth_sort", "tile_scan", "tile_depth"}
     stage_reps = {nm: [] for nm in names}
     kernel_reps = {nm: [] for nm in kernel_stage}
     for rep in range(args.repeats):
@@ -273,8 +275,8 @@ def main():
                                                  for k in range(args.steps)])))
         for nm, stg in kernel_stage.items():
             t = gsr.gsr_kernel_times(ctx, stg)
-            assert len(t) == args.steps, f"{nm}: {len(t)} launches recorded"
-            kernel_reps[nm].append(float(np.mean(t)))
+            assert len(t) == args.steps or (nm in optional and not t), f"{nm}: {len(t)} launches recorded"
+            kernel_reps[nm].append(float(np.mean(t)) if t else 0.0)
         gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, 0)
     stage_ms = {nm: float(np.median(v)) for nm, v in stage_reps.items()}
     kernel_ms = {nm: float(np.median(v)) for nm, v in kernel_reps.items()}
@@ -363,7 +365,11 @@ def main():
         for k, r in roofs.items():
             r["frac"] = r["achieved"] / r["peak"]
             if k == "sort":
-                r["traffic"] = profiling.traffic_for(profiling.sort_kernels(r["passes"]), traffic_md)
+                if r["scheme"] == "tile_depth":
+                    kern = profiling.TILE_FIRST_SORT_KERNELS if r["tile_scan_ms"] > 0 else None
+                else:
+                    kern = profiling.sort_kernels(r["passes"])
+                r["traffic"] = profiling.traffic_for(kern, traffic_md) if kern else None
                 continue
             r["traffic"] = profiling.traffic_for(profiling.STAGE_KERNEL[k], traffic_md)
             if r["bound"] == "alu":
@@ -441,10 +447,15 @@ def bench_per_splat_backward(args, ctx, gsr, torch, np, splats, b, W, H, out_rgb
     return {"kernel_ms": kms, "max_diff_to_default_in_units_of_1e-4_abs_plus_rel": dev}
 
 
+def scheme_opt(gsr, name):
+    return {"tile_depth": gsr.GSR_BIN_TILE_DEPTH, "presort": gsr.GSR_BIN_PRESORT, "key64": gsr.GSR_BIN_KEY64}[name]
+
+
 def sort_roofline(args, N, P, W, H, kernel_ms):
-    """The binning's two radix sorts (presort scheme) against HBM: algorithmic bytes of this scheme per launch over
-    their kernels' own time. Depth sort: 4 passes of 8-bit digits over the n 32-bit depth keys with their indices,
-    each pass reading the keys for the histogram (4 B) and reading and writing key and index (16 B). Tile sort: 2
+    """The binning's sorts against HBM: algorithmic bytes of the scheme per launch over their kernels' own time.
+    Tile-first (the default): see the branch below. Presort: the two radix sorts. Depth sort: 4 passes of 8-bit
+    digits over the n 32-bit depth keys with their indices, each pass reading the keys for the histogram (4 B) and
+    reading and writing key and index (16 B). Tile sort: 2
     passes of 6-bit digits over the pairs; packed (tile and splat in one 32-bit word when they fit) a pass reads
     the words twice and writes them once (12 B), and the last one also writes the splat index (4 B), the 64-bit key
     (8 B) and gathers the depth (4 B); unpacked each pass moves tile id and index (20 B) and the last one adds the
@@ -455,20 +466,45 @@ def sort_roofline(args, N, P, W, H, kernel_ms):
     tile_bits = bits(tiles - 1)
     tile_passes = (tile_bits + 5) // 6
     packed = N > 0 and tile_bits > 0 and bits(N - 1) + tile_bits <= 32
+    pages_bytes = P * (8 + 24 * 6)
+    pages = {"pages_64bit_sort_bytes": pages_bytes,
+             "pages_target_ms_at_70pct": pages_bytes / (0.7 * HBM_PEAK_GBS * 1e9) * 1e3}
+    if args.bin_scheme == "tile_depth" and kernel_ms["tile_depth"] > 0:
+        # tile-first: the pairs in tile order, then each tile's list by (depth, splat). The per-tile order reads each
+        # pair's splat and gathers its depth (8 B), writes the value and the 64-bit key (12 B). Under the box rule
+        # (the counting sort, tile_scan > 0) the scatter reads each splat's rectangle and count (20 B), its block's
+        # row of the count table and the tile starts (8 B per tile and block of 1024 splats), and writes each pair's
+        # splat (4 B); the column scan reads the table twice and writes it once (12 B per entry), the tile starts
+        # read the totals and write starts and ranges (16 B per tile). Otherwise the tile ids' radix sort on packed
+        # words, 12 B per pair and pass.
+        fused = kernel_ms["tile_scan"] > 0
+        nblk = (N + 1023) // 1024
+        if fused:
+            by = 24 * P + 20 * N + 20 * nblk * tiles + 16 * tiles
+            ms = kernel_ms["tile_scan"] + kernel_ms["tile_sort"] + kernel_ms["tile_depth"]
+            note = "count table scan + tile starts + scatter + per-tile order"
+        else:
+            by = (12 * tile_passes + 20) * P
+            ms = kernel_ms["tile_sort"] + kernel_ms["tile_depth"]
+            note = f"radix sort of the tile ids ({tile_passes} passes, packed words) + per-tile order"
+        return {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "work_per_launch": by, "kernel_ms": ms, "scheme": "tile_depth", "bytes": note,
+                "tile_scan_ms": kernel_ms["tile_scan"], "tile_sort_ms": kernel_ms["tile_sort"],
+                "tile_depth_ms": kernel_ms["tile_depth"], **pages}
     per_pair = (12 * tile_passes + 16) if packed else (20 * tile_passes + 12)
     by = 4 * 20 * N + per_pair * P
     ms = kernel_ms["depth_sort"] + kernel_ms["tile_sort"]
-    pages_bytes = P * (8 + 24 * 6)
     return {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "work_per_launch": by, "kernel_ms": ms, "depth_sort_ms": kernel_ms["depth_sort"],
+            "work_per_launch": by, "kernel_ms": ms, "scheme": "presort", "depth_sort_ms": kernel_ms["depth_sort"],
             "tile_sort_ms": kernel_ms["tile_sort"], "packed": packed, "passes": {"depth": 4, "tile": tile_passes},
-            "pages_64bit_sort_bytes": pages_bytes,
-            "pages_target_ms_at_70pct": pages_bytes / (0.7 * HBM_PEAK_GBS * 1e9) * 1e3}
+            **pages}
 
 
 def bench_bin_stress(args, ctx, gsr, scenes, torch, np):
-    """The binning on its own on the 1M-splat stress scene (about 26M pairs under the box rule), under both
-    schemes, timed with the library's events over K calls per repeat (median of the repeats' means). Sort
+    """The binning on its own on the 1M-splat stress scene (about 26M pairs under the box rule), under the presort
+    and 64-bit key schemes (the tile-first default averages more than 3072 pairs per tile here, so after its first
+    call it runs the presort scheme), timed with the library's events over K calls per repeat (median of the
+    repeats' means). Sort
     rooflines on algorithmic bytes:
       key64 (the pages' scheme): a stable LSD sort of the 64-bit (tile | depth) keys with their 32-bit values over
         d = ceil((tile bits + 32) / 8) passes, P (8 + 24 d) bytes: one read of the keys for the digit histograms and
@@ -528,8 +564,7 @@ def bench_bin_stress(args, ctx, gsr, scenes, torch, np):
                        "sort_roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                          "frac": ach / HBM_PEAK_GBS, "work_per_launch": by, "kernel_ms": sort_ms,
                                          "bytes": note, "traffic": traffic}}
-    gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SCHEME, gsr.GSR_BIN_PRESORT if args.bin_scheme == "presort"
-                       else gsr.GSR_BIN_KEY64)
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SCHEME, scheme_opt(gsr, args.bin_scheme))
     k64 = out["key64"]["sort_roofline"]["work_per_launch"]
     out["pages_target_ms_at_70pct"] = k64 / (0.7 * HBM_PEAK_GBS * 1e9) * 1e3
     return out

@@ -844,15 +844,38 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   // the depth sort runs.
   timing_mark(ctx, GSR_STAGE_BIN, s, false);
   hipError_t e = hipSuccess;
+  // Sync-free, the launches are sized for a capacity: the capacity rule of the C0 resident arena page (section 2
+  // table, row "C0"), the largest of 2^16 pairs, 16 per splat and 1.5 times the count seen, here also of a
+  // reservation.
+  const uint64_t capacity =
+      sync_free ? std::min<uint64_t>(std::max<uint64_t>({ctx->pair_reserved, uint64_t(1) << 16, uint64_t(n) * 16,
+                                                         ctx->pair_hint + ctx->pair_hint / 2}),
+                                     (uint64_t(1) << 32) - 1)
+                : 0;
   const uint32_t nb_fuse = grid_for(n, kFuseBlock);
   uint32_t* rows = nullptr;
+  uint32_t* tile_start = nullptr;
   if (fused) {
+    // the counting sort's count table, its column scan and the tile starts (with the ranges) need no pair count:
+    // they are queued before the wait for it
     if ((st = grow(ctx, a.tile_rows, (size_t(nb_fuse) + 2) * num_tiles * 4))) return st;
     rows = static_cast<uint32_t*>(a.tile_rows.ptr);
+    uint32_t* tile_total = rows + size_t(nb_fuse) * num_tiles;
+    tile_start = tile_total + num_tiles;
     hipLaunchKernelGGL(k_prep_rows, dim3(nb_fuse), dim3(kFuseThreads), size_t(num_tiles) * 4, s, splats, depths, n,
                        tiles_x, tiles_y, rects, counts, part, uint32_t(num_tiles), rows);
     hipLaunchKernelGGL(k_total, dim3(1), dim3(kThreads), 0, s, static_cast<const uint64_t*>(part), nb_fuse,
                        offsets + n, a.host_total_dev);
+    e = hipEventRecord(a.total_ready, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "gsr_bin pair count readback");
+    timing_mark(ctx, GSR_STAGE_TILE_SCAN, s, false);
+    hipLaunchKernelGGL(k_tile_cols, dim3(grid_for(num_tiles, kColTiles)), dim3(kColThreads), 0, s, rows, nb_fuse,
+                       uint32_t(num_tiles), tile_total);
+    hipLaunchKernelGGL(k_tile_starts, dim3(1), dim3(kStartThreads), 0, s, static_cast<const uint32_t*>(tile_total),
+                       uint32_t(num_tiles), sync_free ? capacity : ~uint64_t(0),
+                       sync_free ? static_cast<const uint64_t*>(offsets + n) : static_cast<const uint64_t*>(nullptr),
+                       tile_start, static_cast<uint32_t*>(a.ranges.ptr));
+    timing_mark(ctx, GSR_STAGE_TILE_SCAN, s, true);
   } else if (n) {
     hipLaunchKernelGGL(k_prep, dim3(nb_prep), dim3(kThreads), 0, s, splats, depths, n, tiles_x, tiles_y, ellipse,
                        rects, counts,
@@ -863,7 +886,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   }
   if (n) {
     if ((st = check_launch(ctx, "gsr_bin rectangles"))) return st;
-    e = hipEventRecord(a.total_ready, s);
+    if (!fused) e = hipEventRecord(a.total_ready, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "gsr_bin pair count readback");
     ctx->pairs_pending = true;  // this call's count, on its way to the pinned word
     ctx->last_cap = 0;
@@ -910,11 +933,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   uint64_t P = 0;  // the pair count, or the capacity the launches are sized for
   const uint64_t* pairs_dev = nullptr;
   if (sync_free) {
-    // the capacity rule of the C0 resident arena page (section 2 table, row "C0"): the largest of 2^16 pairs,
-    // 16 per splat and 1.5 times the count seen, here also of a reservation
-    P = std::min<uint64_t>(std::max<uint64_t>({ctx->pair_reserved, uint64_t(1) << 16, uint64_t(n) * 16,
-                                               ctx->pair_hint + ctx->pair_hint / 2}),
-                           (uint64_t(1) << 32) - 1);
+    P = capacity;
     pairs_dev = offsets + n;
     ctx->last_cap = P;
   } else if (n) {
@@ -962,16 +981,10 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
                        static_cast<uint64_t*>(nullptr), ranges, idx_bits);
     sorted_v = v0;
   } else if (fused) {
-    // the counting sort by tile (rows counted by k_prep_rows), then each tile's list by (depth, splat) on chip
-    // (tile_depth.hip)
-    uint32_t* tile_total = rows + size_t(nb_fuse) * num_tiles;
-    uint32_t* tile_start = tile_total + num_tiles;
+    // the counting sort's scatter (the count table and the starts are queued above), then each tile's list by
+    // (depth, splat) on chip (tile_depth.hip)
     uint32_t* list = static_cast<uint32_t*>(a.vals[1].ptr);
     timing_mark(ctx, GSR_STAGE_TILE_SORT, s, false);
-    hipLaunchKernelGGL(k_tile_cols, dim3(grid_for(num_tiles, kColTiles)), dim3(kColThreads), 0, s, rows, nb_fuse,
-                       uint32_t(num_tiles), tile_total);
-    hipLaunchKernelGGL(k_tile_starts, dim3(1), dim3(kStartThreads), 0, s, static_cast<const uint32_t*>(tile_total),
-                       uint32_t(num_tiles), P, pairs_dev, tile_start, ranges);
     hipLaunchKernelGGL(k_tile_scatter, dim3(nb_fuse), dim3(kFuseThreads), size_t(num_tiles) * 4, s,
                        static_cast<const uint4*>(rects), static_cast<const uint32_t*>(counts), n, tiles_x,
                        uint32_t(num_tiles), P, pairs_dev, static_cast<const uint32_t*>(rows),

@@ -59,7 +59,7 @@ struct gsr_ctx {
   int device = 0;
   std::string error;
   gsr::Arena arena;
-  int32_t bin_scheme = GSR_BIN_PRESORT;
+  int32_t bin_scheme = GSR_BIN_TILE_DEPTH;
   int32_t bin_rule = GSR_BIN_BOX;
   bool bin_keys = true;
   bool raster_skip = true;  // per-wave cull and the backward's all-lanes-rejected skip

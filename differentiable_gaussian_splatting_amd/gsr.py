@@ -29,7 +29,8 @@ GSR_OPT_BIN_SYNC_FREE = 10
 GSR_BIN_TILE_DEPTH = 2
 GSR_OPT_FORWARD_EXP, GSR_EXP_EXACT, GSR_EXP_FAST = 11, 0, 1
 (GSR_STAGE_BIN, GSR_STAGE_FORWARD, GSR_STAGE_BACKWARD, GSR_STAGE_ADAM, GSR_STAGE_PROJECT_FORWARD,
- GSR_STAGE_PROJECT_BACKWARD, GSR_STAGE_LOSS, GSR_STAGE_DEPTH_SORT, GSR_STAGE_TILE_SORT, GSR_STAGE_TILE_DEPTH) = range(10)
+ GSR_STAGE_PROJECT_BACKWARD, GSR_STAGE_LOSS, GSR_STAGE_DEPTH_SORT, GSR_STAGE_TILE_SORT, GSR_STAGE_TILE_DEPTH,
+ GSR_STAGE_TILE_SCAN) = range(11)
 GSR_ADAM_MAX_GROUPS = 8
 _STATUS = {GSR_EINVAL: "GSR_EINVAL", GSR_ENOMEM: "GSR_ENOMEM", GSR_EHIP: "GSR_EHIP", GSR_EOVERFLOW: "GSR_EOVERFLOW"}
 

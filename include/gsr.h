@@ -62,13 +62,15 @@ gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats);
 
 /* Context options (gsr_set_option). */
 #define GSR_OPT_BIN_SCHEME 1 /* how gsr_bin orders the pairs; all schemes give bit-identical results:            */
-#define GSR_BIN_PRESORT 0    /*   default: radix-sort splats by depth, emit pairs in that order, then a stable     */
-                             /*   radix sort of the pairs by tile id only                                         */
+#define GSR_BIN_PRESORT 0    /*   radix-sort splats by depth, emit pairs in that order, then a stable radix sort  */
+                             /*   of the pairs by tile id only                                                    */
 #define GSR_BIN_KEY64 1      /*   emit pairs splat by splat and radix-sort the full 64-bit keys                   */
-#define GSR_BIN_TILE_DEPTH 2 /*   emit pairs splat by splat, radix-sort them by tile id only, then sort each tile's */
-                             /*   list by (depth, splat) in one workgroup (on chip up to 3456 pairs, through the  */
-                             /*   arena beyond); when the last pair count seen averages more than 3072 pairs per  */
-                             /*   tile, a call runs the presort scheme instead                                    */
+#define GSR_BIN_TILE_DEPTH 2 /*   default: put the pairs in tile order first (under the box rule with at most     */
+                             /*   8192 tiles a counting sort by tile fused with their enumeration, else emission  */
+                             /*   in splat order and a radix sort by tile id), then order each tile's list by     */
+                             /*   (depth, splat) in one workgroup (on chip up to 3456 pairs, through the arena    */
+                             /*   beyond); when the last pair count seen averages more than 3072 pairs per tile,  */
+                             /*   a call runs the presort scheme instead                                          */
 #define GSR_OPT_BIN_KEYS 2   /* 1 (default): gsr_bin materialises the sorted 64-bit keys; 0: keys = NULL          */
 #define GSR_OPT_RASTER_SKIP 3 /* 1 (default): the raster kernels skip work that provably changes nothing - splats   */
                               /*   that cannot reach alpha >= 1/255 in a wavefront's 8x8 block, and, in the        */
@@ -142,7 +144,9 @@ gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value);
 #define GSR_STAGE_TILE_SORT 8        /* inside gsr_bin: the radix sort of the pairs (by tile, or by the 64-bit   */
                                      /*   key with GSR_BIN_KEY64)                                                */
 #define GSR_STAGE_TILE_DEPTH 9       /* inside gsr_bin: the per-tile depth order (tile-first scheme)            */
-#define GSR_NUM_STAGES 10
+#define GSR_STAGE_TILE_SCAN 10       /* inside gsr_bin: the column scan and tile starts of the tile-first scheme's */
+                                     /*   counting sort (its scatter is GSR_STAGE_TILE_SORT)                      */
+#define GSR_NUM_STAGES 11
 
 /* GPU durations in milliseconds of the recorded launches of `stage`, oldest first: the last min(recorded, ring
  * size, max) of them. Waits for the newest one to finish. *count = the number written.

@@ -122,10 +122,13 @@ def test_bin_arena_growth_and_reuse(ctx):
         fresh.close()
 
 
-def test_bin_is_deterministic(ctx):
-    banner("bin determinism raster84k")
+@pytest.mark.parametrize("scheme", ["presort", "tile_depth"])
+def test_bin_is_deterministic(ctx, scheme):
+    """The tile-first scheme's counting sort places each block's pairs in LDS-atomic order; the per-tile order by
+    (depth, splat) must still make every output identical from call to call."""
+    banner(f"bin determinism raster84k scheme={scheme}")
     sc = scene("raster84k")
-    runs = [gpu_bin(ctx, sc.splats, sc.depths, 800, 800, "presort")[1:] for _ in range(3)]
+    runs = [gpu_bin(ctx, sc.splats, sc.depths, 800, 800, scheme)[1:] for _ in range(3)]
     for r in runs[1:]:
         assert all(np.array_equal(a, b) for a, b in zip(r, runs[0]))
 

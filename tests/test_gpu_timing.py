@@ -20,6 +20,7 @@ def test_kernel_times_record_each_stage_in_a_ring(ctx):
     banner("kernel timing rings")
     sc = scene("raster84k")
     sp, dp, vo = dev(sc.splats), dev(sc.depths), dev(sc.v_out)
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SCHEME, gsr.GSR_BIN_PRESORT)
     gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, 3)
     for _ in range(5):
         b = gsr.gsr_bin(ctx, sp, dp, sc.width, sc.height)
@@ -45,6 +46,25 @@ def test_kernel_times_record_each_stage_in_a_ring(ctx):
         gsr.gsr_kernel_times(ctx, gsr.GSR_STAGE_FORWARD)
 
 
+def test_kernel_times_of_the_tile_first_binning(ctx):
+    """The tile-first scheme (the default) records its counting sort's scans, its scatter and the per-tile order;
+    no depth sort runs."""
+    from differentiable_gaussian_splatting_amd import gsr
+    banner("kernel timing tile-first")
+    sc = scene("raster84k")
+    sp, dp = dev(sc.splats), dev(sc.depths)
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, 3)
+    for _ in range(4):
+        gsr.gsr_bin(ctx, sp, dp, sc.width, sc.height)
+    inner = 0.0
+    for stage in (gsr.GSR_STAGE_TILE_SCAN, gsr.GSR_STAGE_TILE_SORT, gsr.GSR_STAGE_TILE_DEPTH):
+        t = gsr.gsr_kernel_times(ctx, stage)
+        assert len(t) == 3 and all(0 < x < 1000 for x in t), (stage, t)
+        inner += sum(t)
+    assert gsr.gsr_kernel_times(ctx, gsr.GSR_STAGE_DEPTH_SORT) == []
+    assert inner < sum(gsr.gsr_kernel_times(ctx, gsr.GSR_STAGE_BIN))
+
+
 def test_kernel_timing_rejects_bad_arguments(ctx):
     from differentiable_gaussian_splatting_amd import gsr
     banner("kernel timing argument errors")
@@ -53,6 +73,6 @@ def test_kernel_timing_rejects_bad_arguments(ctx):
     with pytest.raises(gsr.GsrError):
         gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, -1)
     gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, 2)
-    for bad in (-1, gsr.GSR_STAGE_TILE_SORT + 1):
+    for bad in (-1, gsr.GSR_STAGE_TILE_SCAN + 1):
         with pytest.raises(gsr.GsrError):
             gsr.gsr_kernel_times(ctx, bad)
