@@ -948,6 +948,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
 
   for (int q = 0; q < 2; ++q)
     if ((st = grow(ctx, a.keys[q], size_t(P) * 8)) || (st = grow(ctx, a.vals[q], size_t(P) * 4))) return st;
+  if (tile_first && (st = grow(ctx, a.tile_scratch, size_t(P) * 8))) return st;
   uint32_t* v0 = static_cast<uint32_t*>(a.vals[0].ptr);
   uint32_t* ranges = static_cast<uint32_t*>(a.ranges.ptr);
   const uint32_t tile_bits = bits_of(num_tiles - 1);
@@ -998,7 +999,8 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     uint32_t* k1 = static_cast<uint32_t*>(a.keys[1].ptr);
     timing_mark(ctx, GSR_STAGE_TILE_DEPTH, s, false);
     launch_tile_depth(s, static_cast<const uint32_t*>(nullptr), list, 32u, false, ranges, P, pairs_dev,
-                      uint32_t(num_tiles), depths, n, v0, final_k, k0, k0 + P, k1, k1 + P);
+                      uint32_t(num_tiles), depths, n, v0, final_k, static_cast<uint64_t*>(a.tile_scratch.ptr), k0,
+                      k0 + P, k1, k1 + P);
     timing_mark(ctx, GSR_STAGE_TILE_DEPTH, s, true);
     sorted_v = v0;
   } else if (tile_first) {
@@ -1064,7 +1066,8 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     }
     timing_mark(ctx, GSR_STAGE_TILE_DEPTH, s, false);
     launch_tile_depth(s, list, list_vals, tpacked ? idx_bits : 32u, true, ranges, P, pairs_dev, uint32_t(num_tiles),
-                      depths, n, vals_out, final_k, scratch[0], scratch[1], scratch[2], scratch[3]);
+                      depths, n, vals_out, final_k, static_cast<uint64_t*>(a.tile_scratch.ptr), scratch[0],
+                      scratch[1], scratch[2], scratch[3]);
     timing_mark(ctx, GSR_STAGE_TILE_DEPTH, s, true);
     sorted_v = vals_out;
   } else if (presort) {

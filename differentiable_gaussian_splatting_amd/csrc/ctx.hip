@@ -34,7 +34,7 @@ static void for_each_buffer(Arena& a, F f) {
   for (DevBuf* b : {&a.keys[0], &a.keys[1], &a.vals[0], &a.vals[1], &a.counts, &a.offsets, &a.order, &a.order_alt,
                     &a.order_vals, &a.order_vals_alt, &a.scan_part, &a.hist, &a.digit_tot,
                     &a.ranges, &a.rects,
-                    &a.tile_order_ext, &a.tile_cost, &a.tile_rows, &a.loss_part, &a.loss_maps, &a.grad_fixed})
+                    &a.tile_order_ext, &a.tile_cost, &a.tile_rows, &a.tile_scratch, &a.loss_part, &a.loss_maps, &a.grad_fixed})
     f(*b);
 }
 
@@ -292,7 +292,9 @@ gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats) {
       {&a.counts, size_t(ns) * 4},         {&a.offsets, size_t(ns + 1) * 8},
       {&a.order, size_t(ns) * 8},
       {&a.order_alt, size_t(std::max<uint64_t>(ns, max_pairs)) * 8},  // also the presort scheme's 64-bit keys
-      {&a.order_vals, size_t(ns) * 4},     {&a.order_vals_alt, size_t(ns) * 4},
+      {&a.order_vals, size_t(ns) * 4},
+      {&a.order_vals_alt, size_t(std::max<uint64_t>(ns, max_pairs)) * 4},  // also the tile-first scheme's scratch
+      {&a.tile_scratch, size_t(max_pairs) * 8},
       {&a.scan_part, size_t(std::max<uint64_t>(nb, ns / 256 + 1) + 1) * 8},
       {&a.hist, size_t(nb) * 256 * 4},     {&a.digit_tot, 256 * 4},
       {&a.rects, size_t(ns) * 16},

@@ -40,6 +40,7 @@ struct Arena {
   DevBuf digit_tot;   // uint32 [256] per-digit totals of the current pass
   DevBuf ranges;      // uint32 [2 * tiles]
   DevBuf rects;       // uint32x4 [splat capacity] tile rectangle (tx0, ty0, w, h) of each splat, natural order
+  DevBuf tile_scratch;  // uint64 [pair capacity] the tile-first per-tile order's entries for lists longer than LDS
   DevBuf tile_rows;   // uint32 [splat blocks + 2][tiles] tile-first counting sort: block offsets, tile totals, starts
   DevBuf tile_order_ext;  // uint32 [tiles] raster launch order: the slowest expected tiles first
   DevBuf tile_cost;   // uint32 [4 tiles] splats each wavefront of the last forward walked (launch-order hint)
@@ -150,11 +151,12 @@ gsr_status radix_sort_launch(gsr_ctx* ctx, hipStream_t s, const K* keys_in, cons
 // list holds packed words (tile << idx_bits) | splat when list_vals is null, else list_vals holds the splats;
 // `ordered` says it is in ascending splat order (otherwise any order). The result is written to vals_out[start..end)
 // and, when keys_out is not null, keys_out = (tile << 32) | depth bits. Lists longer than tile_depth_capacity() are
-// sorted through gk0, gk1, gp0, gp1 (pair-count arrays, each tile using its own stretch).
+// sorted through gent (a 64-bit pair-count array) and gk0, gk1, gp0, gp1 (32-bit pair-count arrays), each tile using
+// its own stretch; gent shares no memory with the other five.
 void launch_tile_depth(hipStream_t s, const uint32_t* list, const uint32_t* list_vals, uint32_t idx_bits,
                        bool ordered, const uint32_t* ranges, uint64_t pairs_cap, const uint64_t* pairs_dev,
                        uint32_t num_tiles, const float* depths, uint32_t n, uint32_t* vals_out, uint64_t* keys_out,
-                       uint32_t* gk0, uint32_t* gk1, uint32_t* gp0, uint32_t* gp1);
+                       uint64_t* gent, uint32_t* gk0, uint32_t* gk1, uint32_t* gp0, uint32_t* gp1);
 uint32_t tile_depth_capacity();
 
 // The same sort of 32-bit tile ids whose last pass also writes keys_final[g] = (key << 32) | bits(depths[val]) for

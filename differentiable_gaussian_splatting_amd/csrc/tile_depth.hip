@@ -58,6 +58,11 @@ union TileShared {
     uint64_t entry[kCap];             // the list grouped by bucket: (depth bits << 32) | splat
     uint32_t wmin[kWaves], wmax[kWaves], wsum[kWaves];
   } bkt;
+  struct {                            // lists longer than kCap: the entries go through the arena
+    uint32_t start[kMaxBuckets + 1];
+    uint32_t run[kMaxBuckets];        // next free slot of each bucket
+    uint32_t wmin[kWaves], wmax[kWaves], wsum[kWaves];
+  } big;
 };
 
 __device__ __forceinline__ uint32_t bucket_of(uint32_t key, uint32_t lo, float scale, uint32_t nb) {
@@ -184,11 +189,35 @@ __device__ __forceinline__ uint32_t radix_order(uint32_t* k0, uint32_t* k1, PosT
   return sort_list(ka, kb, pa, pb, m, sh) ? 1 - r : r;
 }
 
+// Exclusive scan of the bucket counts start[0..nb) in place (nb a multiple of kThreads, at most kMaxBuckets;
+// start[nb] = m); returns the largest count. All threads call it; it ends with a barrier.
+__device__ __forceinline__ uint32_t scan_buckets(uint32_t* start, uint32_t nb, uint32_t m, uint32_t* wsum) {
+  const uint32_t tid = threadIdx.x, per = nb / kThreads;
+  uint32_t c[kScanPer], sum = 0, biggest = 0;
+#pragma unroll
+  for (uint32_t j = 0; j < kScanPer; ++j) {
+    c[j] = j < per ? start[tid * per + j] : 0u;
+    sum += c[j];
+    biggest = max(biggest, c[j]);
+  }
+  uint32_t run = block_exclusive_scan<uint32_t, kThreads>(sum, nullptr, wsum);
+#pragma unroll
+  for (uint32_t j = 0; j < kScanPer; ++j)
+    if (j < per) {
+      start[tid * per + j] = run;
+      run += c[j];
+    }
+  if (tid == 0) start[nb] = m;
+  __syncthreads();
+  return biggest;
+}
+
 // One workgroup per tile. The tile's list is list[start..end) (ranges, clamped to the pair count): packed words
 // (tile << idx_bits) | splat when list_vals is null, else list_vals holds the splats; `ordered` says the list is in
 // ascending splat order. Writes vals_out[start + e] = the e-th splat in (depth bits, index) order and, when keys_out
-// is not null, keys_out[start + e] = (tile << 32) | its depth bits. Lists longer than kCap use the scratch arrays
-// gk0, gk1, gp0, gp1 (P entries each, the tile's stretch [start, end) of them).
+// is not null, keys_out[start + e] = (tile << 32) | its depth bits. Lists longer than kCap use the arena: the bucket
+// path stages each entry's depth bits in gp0 and groups the entries (64-bit) in gent; the radix path the arrays gk0,
+// gk1, gp0, gp1 (P entries each, every tile using its own stretch [start, end)). gent overlaps none of the four.
 __global__ __launch_bounds__(kThreads) void k_tile_depth(const uint32_t* __restrict__ list,
                                                          const uint32_t* __restrict__ list_vals, uint32_t idx_bits,
                                                          bool ordered,
@@ -196,7 +225,8 @@ __global__ __launch_bounds__(kThreads) void k_tile_depth(const uint32_t* __restr
                                                          const uint64_t* __restrict__ pairs_dev, uint32_t num_tiles,
                                                          const float* __restrict__ depths, uint32_t n,
                                                          uint32_t* __restrict__ vals_out, uint64_t* __restrict__ keys_out,
-                                                         uint32_t* gk0, uint32_t* gk1, uint32_t* gp0, uint32_t* gp1) {
+                                                         uint64_t* gent, uint32_t* gk0, uint32_t* gk1, uint32_t* gp0,
+                                                         uint32_t* gp1) {
   __shared__ TileShared ts;
   const uint32_t tile = blockIdx.x;
   if (tile >= num_tiles) return;
@@ -239,22 +269,7 @@ __global__ __launch_bounds__(kThreads) void k_tile_depth(const uint32_t* __restr
       if (tid + i * kThreads < m) slot[i] = atomicAdd(&ts.bkt.start[bucket_of(key[i], lo, scale, nb)], 1u);
     __syncthreads();
     // exclusive scan of the counts: thread tid takes nb / kThreads consecutive buckets
-    const uint32_t per = nb / kThreads;
-    uint32_t c[kScanPer], sum = 0, biggest = 0;
-#pragma unroll
-    for (uint32_t j = 0; j < kScanPer; ++j) {
-      c[j] = j < per ? ts.bkt.start[tid * per + j] : 0u;
-      sum += c[j];
-      biggest = max(biggest, c[j]);
-    }
-    uint32_t run = block_exclusive_scan<uint32_t, kThreads>(sum, nullptr, ts.bkt.wsum);
-#pragma unroll
-    for (uint32_t j = 0; j < kScanPer; ++j)
-      if (j < per) {
-        ts.bkt.start[tid * per + j] = run;
-        run += c[j];
-      }
-    if (tid == 0) ts.bkt.start[nb] = m;
+    const uint32_t biggest = scan_buckets(ts.bkt.start, nb, m, ts.bkt.wsum);
     if (!__syncthreads_or(biggest > kBucketLimit)) {
 #pragma unroll
       for (uint32_t i = 0; i < kMaxItems; ++i)
@@ -279,6 +294,51 @@ __global__ __launch_bounds__(kThreads) void k_tile_depth(const uint32_t* __restr
     const uint16_t* pr = res ? ts.lsd.pos[1] : ts.lsd.pos[0];
     for (uint32_t e = tid; e < m; e += kThreads) emit(e, splat_at(pr[e]), kr[e]);
   } else {
+    // buckets as above with kMaxBuckets of them; the depth bits staged in list order (one gather), the grouped
+    // entries in the arena
+    uint32_t* const staged = gp0 + start;
+    uint32_t kmin = ~0u, kmax = 0;
+    for (uint32_t e = tid; e < m; e += kThreads) {
+      const uint32_t k = depth_bits(splat_at(e));
+      staged[e] = k;
+      kmin = min(kmin, k);
+      kmax = max(kmax, k);
+    }
+    const uint32_t nb = kMaxBuckets;
+    for (uint32_t j = tid; j <= nb; j += kThreads) ts.big.start[j] = 0;
+    kmin = wave_min(kmin);
+    kmax = wave_max(kmax);
+    if (lane == 0) ts.big.wmin[w] = kmin, ts.big.wmax[w] = kmax;
+    __syncthreads();
+    uint32_t lo = ts.big.wmin[0], hi = ts.big.wmax[0];
+#pragma unroll
+    for (uint32_t q = 1; q < kWaves; ++q) lo = min(lo, ts.big.wmin[q]), hi = max(hi, ts.big.wmax[q]);
+    const float scale = float(nb) / (float(hi - lo) + 1.0f);
+    for (uint32_t e = tid; e < m; e += kThreads) atomicAdd(&ts.big.start[bucket_of(staged[e], lo, scale, nb)], 1u);
+    __syncthreads();
+    const uint32_t biggest = scan_buckets(ts.big.start, nb, m, ts.big.wsum);
+    // a bucket may hold a few times the mean of m / nb entries before the radix sort is cheaper
+    const uint32_t limit = max(kBucketLimit, 8 * ((m + nb - 1) / nb));
+    if (!__syncthreads_or(biggest > limit)) {
+      uint64_t* const ent = gent + start;
+      for (uint32_t j = tid; j < nb; j += kThreads) ts.big.run[j] = ts.big.start[j];
+      __syncthreads();
+      for (uint32_t e = tid; e < m; e += kThreads) {
+        const uint32_t k = staged[e];
+        ent[atomicAdd(&ts.big.run[bucket_of(k, lo, scale, nb)], 1u)] = (uint64_t(k) << 32) | splat_at(e);
+      }
+      __syncthreads();
+      for (uint32_t q = tid; q < m; q += kThreads) {
+        const uint64_t me = ent[q];
+        const uint32_t k = uint32_t(me >> 32);
+        const uint32_t b = bucket_of(k, lo, scale, nb);
+        const uint32_t b0 = ts.big.start[b], b1 = ts.big.start[b + 1];
+        uint32_t r = b0;
+        for (uint32_t f = b0; f < b1; ++f) r += ent[f] < me ? 1u : 0u;
+        emit(r, uint32_t(me), k);
+      }
+      return;
+    }
     uint32_t *k0 = gk0 + start, *k1 = gk1 + start, *p0 = gp0 + start, *p1 = gp1 + start;
     const uint32_t res = radix_order(k0, k1, p0, p1, m, ordered, splat_at, depth_bits, ts.lsd.sh);
     const uint32_t* kr = res ? k1 : k0;
@@ -292,10 +352,11 @@ __global__ __launch_bounds__(kThreads) void k_tile_depth(const uint32_t* __restr
 void launch_tile_depth(hipStream_t s, const uint32_t* list, const uint32_t* list_vals, uint32_t idx_bits,
                        bool ordered, const uint32_t* ranges, uint64_t pairs_cap, const uint64_t* pairs_dev,
                        uint32_t num_tiles, const float* depths, uint32_t n, uint32_t* vals_out, uint64_t* keys_out,
-                       uint32_t* gk0, uint32_t* gk1, uint32_t* gp0, uint32_t* gp1) {
+                       uint64_t* gent, uint32_t* gk0, uint32_t* gk1, uint32_t* gp0, uint32_t* gp1) {
   if (num_tiles)
     hipLaunchKernelGGL(k_tile_depth, dim3(num_tiles), dim3(kThreads), 0, s, list, list_vals, idx_bits, ordered,
-                       ranges, pairs_cap, pairs_dev, num_tiles, depths, n, vals_out, keys_out, gk0, gk1, gp0, gp1);
+                       ranges, pairs_cap, pairs_dev, num_tiles, depths, n, vals_out, keys_out, gent, gk0, gk1, gp0,
+                       gp1);
 }
 
 uint32_t tile_depth_capacity() { return kCap; }

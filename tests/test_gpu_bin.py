@@ -225,15 +225,17 @@ def test_bin_ellipse_rule_ragged_images(ctx, w, h):
         set_rule(ctx, "box")
 
 
-@pytest.mark.parametrize("w,h,n,cluster", [(16, 16, 6000, 0.0), (64, 48, 30000, 0.0), (800, 800, 200000, 0.3)])
-def test_tile_depth_long_lists(ctx, w, h, n, cluster):
-    """Tile lists longer than the tile-first scheme's on-chip capacity (3456 pairs) are sorted through the arena
-    instead: one tile of 6000 pairs; twelve tiles of 5-11 thousand; and 16 tiles of up to 25 thousand (30% of the
-    splats in a 48-pixel square) among 2,484 short ones, both forms in one launch. Bit-exact against the oracle on a
-    fresh context (no count seen: the first call takes the tile-first path) and again with the count seen."""
+@pytest.mark.parametrize("w,h,n,cluster,levels", [(16, 16, 6000, 0.0, 0), (64, 48, 30000, 0.0, 0),
+                                                   (800, 800, 200000, 0.3, 0), (16, 16, 6000, 0.0, 3)])
+def test_tile_depth_long_lists(ctx, w, h, n, cluster, levels):
+    """Tile lists longer than the tile-first scheme's on-chip capacity (3456 pairs) are ordered through the arena
+    instead: one tile of 6000 pairs; twelve tiles of 5-11 thousand; 16 tiles of up to 25 thousand (30% of the
+    splats in a 48-pixel square) among 2,484 short ones, both forms in one launch; and one tile of 6000 pairs at
+    three depths (crowded buckets: the radix sort through the arena). Bit-exact against the oracle on a fresh
+    context (no count seen: the first call takes the tile-first path) and again with the count seen."""
     import oracle
     from differentiable_gaussian_splatting_amd import gsr
-    banner(f"bin tile_depth long lists {w}x{h} n={n} cluster={cluster}")
+    banner(f"bin tile_depth long lists {w}x{h} n={n} cluster={cluster} levels={levels}")
     rng = np.random.default_rng(n)
     s = np.exp(rng.uniform(np.log(0.5), np.log(8.0), n))
     sp = np.zeros((n, 9), np.float32)
@@ -245,6 +247,8 @@ def test_tile_depth_long_lists(ctx, w, h, n, cluster):
     sp[:, 8] = rng.uniform(0.05, 1.0, n)
     depths = rng.uniform(0.1, 10.0, n).astype(np.float32)
     depths[: n // 10] = depths[n // 10: 2 * (n // 10)]  # equal depths: ties keep splat order
+    if levels:
+        depths = rng.choice(np.array([0.5, 2.0, 7.5], np.float32)[:levels], n)
     ref = oracle.bin(sp, depths, w, h)
     lens = ref.ranges[:, 1].astype(np.int64) - ref.ranges[:, 0]
     assert lens.max() > 3456
