@@ -53,7 +53,8 @@ constexpr double kExp2Tab[64] = {
     0x1.f50765b6e4540p+0, 0x1.9d3e12dd8a18bp-54,  // j = 31
 };
 
-// e^x rounded to fp32, for |x| below 80, with `tab` holding kExp2Tab (an LDS copy on the device). Reduction
+// e^x rounded to fp32, for |x| below 80, with `tab` holding kExp2Tab (an LDS copy on the device). The method is
+// P. T. P. Tang's table-driven exponential (ACM Transactions on Mathematical Software 15(2), 1989): reduction
 // x = k ln2/32 + r with |r| <= ln2/64 (ln2/32 split into a 32-bit head, exact in k * head for |k| < 2^21, and a
 // tail), e^r - 1 by its Taylor series to degree 6 (truncation below 4e-18), then
 // 2^(k/32) e^r = 2^floor(k/32) (hi + (hi (e^r - 1) + lo)) with one rounding to double and one to fp32. The double

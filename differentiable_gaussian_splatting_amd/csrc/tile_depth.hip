@@ -212,24 +212,19 @@ __device__ __forceinline__ uint32_t scan_buckets(uint32_t* start, uint32_t nb, u
   return biggest;
 }
 
-// One workgroup per tile. The tile's list is list[start..end) (ranges, clamped to the pair count): packed words
+// One tile, by one workgroup. The tile's list is list[start..end) (ranges, clamped to the pair count): packed words
 // (tile << idx_bits) | splat when list_vals is null, else list_vals holds the splats; `ordered` says the list is in
 // ascending splat order. Writes vals_out[start + e] = the e-th splat in (depth bits, index) order and, when keys_out
 // is not null, keys_out[start + e] = (tile << 32) | its depth bits. Lists longer than kCap use the arena: the bucket
 // path stages each entry's depth bits in gp0 and groups the entries (64-bit) in gent; the radix path the arrays gk0,
 // gk1, gp0, gp1 (P entries each, every tile using its own stretch [start, end)). gent overlaps none of the four.
-__global__ __launch_bounds__(kThreads) void k_tile_depth(const uint32_t* __restrict__ list,
-                                                         const uint32_t* __restrict__ list_vals, uint32_t idx_bits,
-                                                         bool ordered,
-                                                         const uint32_t* __restrict__ ranges, uint64_t pairs_cap,
-                                                         const uint64_t* __restrict__ pairs_dev, uint32_t num_tiles,
-                                                         const float* __restrict__ depths, uint32_t n,
-                                                         uint32_t* __restrict__ vals_out, uint64_t* __restrict__ keys_out,
-                                                         uint64_t* gent, uint32_t* gk0, uint32_t* gk1, uint32_t* gp0,
-                                                         uint32_t* gp1) {
-  __shared__ TileShared ts;
-  const uint32_t tile = blockIdx.x;
-  if (tile >= num_tiles) return;
+#define GSR_TILE_DEPTH_PARAMS                                                                                     \
+  const uint32_t *__restrict__ list, const uint32_t *__restrict__ list_vals, uint32_t idx_bits, bool ordered,       \
+      const uint32_t *__restrict__ ranges, uint64_t pairs_cap, const uint64_t *__restrict__ pairs_dev,             \
+      uint32_t num_tiles, const float *__restrict__ depths, uint32_t n, uint32_t *__restrict__ vals_out,           \
+      uint64_t *__restrict__ keys_out, uint64_t *gent, uint32_t *gk0, uint32_t *gk1, uint32_t *gp0, uint32_t *gp1
+
+__device__ __forceinline__ void order_tile(uint32_t tile, TileShared& ts, GSR_TILE_DEPTH_PARAMS) {
   const uint64_t P = count_within(pairs_dev, pairs_cap);
   const uint32_t start = uint32_t(min<uint64_t>(ranges[2 * tile], P));
   const uint32_t end = uint32_t(max<uint64_t>(start, min<uint64_t>(ranges[2 * tile + 1], P)));
@@ -347,16 +342,42 @@ __global__ __launch_bounds__(kThreads) void k_tile_depth(const uint32_t* __restr
   }
 }
 
+// A workgroup per tile; past kMaxGrid tiles (a workgroup per tile of a 2^23-tile image would be 2^32 work-items,
+// more than a launch takes) kLoop: workgroup b orders tiles b, b + gridDim.x, ...
+constexpr uint32_t kMaxGrid = 1u << 20;
+
+template <bool kLoop>
+__global__ __launch_bounds__(kThreads) void k_tile_depth(GSR_TILE_DEPTH_PARAMS) {
+  __shared__ TileShared ts;
+  if constexpr (!kLoop) {
+    if (blockIdx.x < num_tiles)
+      order_tile(blockIdx.x, ts, list, list_vals, idx_bits, ordered, ranges, pairs_cap, pairs_dev, num_tiles, depths,
+                 n, vals_out, keys_out, gent, gk0, gk1, gp0, gp1);
+  } else {
+    for (uint32_t tile = blockIdx.x; tile < num_tiles; tile += gridDim.x) {
+      order_tile(tile, ts, list, list_vals, idx_bits, ordered, ranges, pairs_cap, pairs_dev, num_tiles, depths, n,
+                 vals_out, keys_out, gent, gk0, gk1, gp0, gp1);
+      __syncthreads();  // the next tile reuses the LDS
+    }
+  }
+}
+
 }  // namespace
 
 void launch_tile_depth(hipStream_t s, const uint32_t* list, const uint32_t* list_vals, uint32_t idx_bits,
                        bool ordered, const uint32_t* ranges, uint64_t pairs_cap, const uint64_t* pairs_dev,
                        uint32_t num_tiles, const float* depths, uint32_t n, uint32_t* vals_out, uint64_t* keys_out,
                        uint64_t* gent, uint32_t* gk0, uint32_t* gk1, uint32_t* gp0, uint32_t* gp1) {
-  if (num_tiles)
-    hipLaunchKernelGGL(k_tile_depth, dim3(num_tiles), dim3(kThreads), 0, s, list, list_vals, idx_bits, ordered,
+  if (num_tiles <= kMaxGrid) {
+    if (num_tiles)
+      hipLaunchKernelGGL(k_tile_depth<false>, dim3(num_tiles), dim3(kThreads), 0, s, list, list_vals, idx_bits,
+                         ordered, ranges, pairs_cap, pairs_dev, num_tiles, depths, n, vals_out, keys_out, gent, gk0,
+                         gk1, gp0, gp1);
+  } else {
+    hipLaunchKernelGGL(k_tile_depth<true>, dim3(kMaxGrid), dim3(kThreads), 0, s, list, list_vals, idx_bits, ordered,
                        ranges, pairs_cap, pairs_dev, num_tiles, depths, n, vals_out, keys_out, gent, gk0, gk1, gp0,
                        gp1);
+  }
 }
 
 uint32_t tile_depth_capacity() { return kCap; }

@@ -70,7 +70,7 @@ def sort_kernels(passes: dict) -> tuple:
 
 # the tile-first scheme's sort under the box rule: the count table's column scan, the tile starts, the scatter and
 # the per-tile order, one launch each
-TILE_FIRST_SORT_KERNELS = ("k_tile_cols", "k_tile_starts", "k_tile_scatter", "k_tile_depth")
+TILE_FIRST_SORT_KERNELS = ("k_tile_cols", "k_tile_starts", "k_tile_scatter", "k_tile_depth<false>")
 
 CALIB_BYTES = 256 * 1024 * 1024  # read and written by each copy of bench.py --calib-copy
 TRAFFIC_BEGIN, TRAFFIC_END = "<!-- traffic-json", "traffic-json -->"

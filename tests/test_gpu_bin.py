@@ -87,14 +87,17 @@ def test_bin_empty_and_all_culled(ctx, scheme):
     assert b.num_pairs == 0
 
 
+@pytest.mark.parametrize("scheme", ["presort", "tile_depth"])
 @pytest.mark.parametrize("w,h,n", [(16, 16, 700), (1024, 1024, 1 << 20), (65536, 32768, 3000)])
-def test_bin_packed_and_unpacked_tile_sort(ctx, w, h, n):
+def test_bin_packed_and_unpacked_tile_sort(ctx, w, h, n, scheme):
     """The presort scheme packs (tile, splat) into one 32-bit key when bits(n - 1) + bits(tiles - 1) <= 32: a
     single tile (no tile pass: not packed), 2^20 splats on 4096 tiles (exactly 32 bits: packed), and 2^23 tiles
     with 3000 splats (36 bits: the two-array form). It also carries each splat's count in its depth-sort value when
     bits(n - 1) + bits(tiles) <= 32: the first case does, the other two (33 and 36 bits) gather the counts through
-    the sorted indices instead. All bit-exact against the oracle."""
-    banner(f"bin packing {w}x{h} n={n}")
+    the sorted indices instead. The tile-first scheme takes its counting sort in the first two cases and, past 8192
+    tiles, emission and the radix sort of the tile ids (the two-array form at 36 bits). All bit-exact against the
+    oracle."""
+    banner(f"bin packing {w}x{h} n={n} scheme={scheme}")
     # round splats of s in 0.5-20 px over the image (drawn here: the scene generator's per-pixel upstream gradient
     # would not fit the largest image)
     rng = np.random.default_rng(n + w)
@@ -105,7 +108,7 @@ def test_bin_packed_and_unpacked_tile_sort(ctx, w, h, n):
     sp[:, 5:8] = rng.uniform(0, 1, (n, 3))
     sp[:, 8] = rng.uniform(0.05, 1.0, n)
     depths = rng.uniform(0.1, 10.0, n).astype(np.float32)
-    assert_bins_equal(ctx, sp, depths, w, h, "presort")
+    assert_bins_equal(ctx, sp, depths, w, h, scheme)
 
 
 def test_bin_arena_growth_and_reuse(ctx):

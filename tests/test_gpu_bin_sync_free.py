@@ -83,10 +83,11 @@ def test_sync_free_unpacked_tile_sort():
         ctx.close()
 
 
-def test_overflow_empties_the_ranges_and_the_next_call_fits():
+@pytest.mark.parametrize("scheme", [0, 2])
+def test_overflow_empties_the_ranges_and_the_next_call_fits(scheme):
     from differentiable_gaussian_splatting_amd import gsr
-    banner("bin sync-free overflow")
-    ctx = new_ctx()
+    banner(f"bin sync-free overflow scheme={scheme}")
+    ctx = new_ctx(scheme)
     try:
         tiny = scene("tiny")
         bin_and_compare(ctx, tiny.splats, tiny.depths, tiny.width, tiny.height, oracle_bins("tiny"))
