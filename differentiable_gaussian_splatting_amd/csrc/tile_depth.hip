@@ -234,9 +234,12 @@ __device__ __forceinline__ void order_tile(uint32_t tile, TileShared& ts, GSR_TI
   const uint32_t mask = idx_bits >= 32 ? ~0u : (1u << idx_bits) - 1u;
   auto splat_at = [&](uint32_t e) -> uint32_t { return list_vals ? list_vals[start + e] : list[start + e] & mask; };
   auto depth_bits = [&](uint32_t splat) -> uint32_t { return splat < n ? __float_as_uint(depths[splat]) : 0u; };
+  // the results are written once and not read again here: non-temporal stores (4.5 us of 60 at 410k). The scatter
+  // that fills the lists needs the opposite: its scattered 4-byte stores rely on merging in L2 (with non-temporal
+  // stores it took 0.28 ms instead of 0.05).
   auto emit = [&](uint32_t e, uint32_t splat, uint32_t key) {
-    vals_out[start + e] = splat;
-    if (keys_out) keys_out[start + e] = (uint64_t(tile) << 32) | key;
+    __builtin_nontemporal_store(splat, &vals_out[start + e]);
+    if (keys_out) __builtin_nontemporal_store((uint64_t(tile) << 32) | key, &keys_out[start + e]);
   };
   if (m <= kCap) {
     // buckets
