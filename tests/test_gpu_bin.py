@@ -261,3 +261,39 @@ def test_tile_depth_long_lists(ctx, w, h, n, cluster, levels):
         assert_bins_equal(c, sp, depths, w, h, "tile_depth", ref)
     finally:
         c.close()
+
+
+@pytest.mark.parametrize("w,h", [(2048, 1024), (2064, 1024)])
+def test_tile_first_fused_tile_limit(ctx, w, h):
+    """The tile-first scheme's counting sort keeps a counter per tile in LDS, up to 8192 tiles: 2048 x 1024 (8192
+    tiles) takes it, 2064 x 1024 (8256) emission and the radix sort of the tile ids. Both bit-exact."""
+    banner(f"bin tile-first fused limit {w}x{h}")
+    sc = custom_scene(name="limit", width=w, height=h, n=20000, seed=w + h, size_classes=((1.0, 0.3, 30.0),),
+                      margin=40.0)
+    assert_bins_equal(ctx, sc.splats, sc.depths, w, h, "tile_depth")
+
+
+@pytest.mark.parametrize("m", [1, 2, 3456, 3457])
+def test_tile_depth_list_length_edges(ctx, m):
+    """One tile holding exactly m pairs: a single entry, two, the on-chip capacity (3456) and one more (the arena
+    path). Splats of 0.3-1 px inside the tile's inner 8 x 8 pixels, so each covers that tile only; a third of them
+    share depths, so ties are ordered by splat index."""
+    banner(f"bin tile-depth list length m={m}")
+    rng = np.random.default_rng(m)
+    s = rng.uniform(0.3, 1.0, m)
+    sp = np.zeros((m, 9), np.float32)
+    sp[:, 0], sp[:, 1] = rng.uniform(4.5, 11.5, m), rng.uniform(4.5, 11.5, m)
+    sp[:, 2] = sp[:, 4] = 1.0 / s ** 2
+    sp[:, 5:8] = rng.uniform(0, 1, (m, 3))
+    sp[:, 8] = rng.uniform(0.05, 1.0, m)
+    depths = rng.uniform(0.1, 10.0, m).astype(np.float32)
+    depths[: m // 3] = depths[m - m // 3:]
+    import oracle
+    ref = oracle.bin(sp, depths, 16, 16)
+    assert ref.num_pairs == m
+    from differentiable_gaussian_splatting_amd import gsr
+    c = gsr.Context(0)  # a fresh context: the tile-first path on the first call
+    try:
+        assert_bins_equal(c, sp, depths, 16, 16, "tile_depth", ref)
+    finally:
+        c.close()
