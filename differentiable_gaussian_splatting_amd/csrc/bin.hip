@@ -1130,7 +1130,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
       if (st) return st;
       timing_mark(ctx, GSR_STAGE_TILE_SORT, s, true);
     }
-    final_k = kb[res];
+    final_k = ctx->bin_keys ? kb[res] : nullptr;  // the sort's own keys, returned only when asked for
     hipLaunchKernelGGL(k_ranges<uint64_t>, dim3(grid_for(P + 1, kThreads * kRangeItems)), dim3(kThreads), 0, s,
                        kb[res], static_cast<const uint32_t*>(a.vals[res].ptr), P, pairs_dev, uint32_t(num_tiles),
                        depths, n, static_cast<uint64_t*>(nullptr), ranges, 0u);

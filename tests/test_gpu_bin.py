@@ -136,17 +136,19 @@ def test_bin_is_deterministic(ctx, scheme):
         assert all(np.array_equal(a, b) for a, b in zip(r, runs[0]))
 
 
-def test_bin_without_keys(ctx):
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+@pytest.mark.parametrize("name", ["tiny", "raster84k"])
+def test_bin_without_keys(ctx, name, scheme):
     from differentiable_gaussian_splatting_amd import gsr
-    banner("bin keys off")
-    sc = scene("tiny")
-    gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SCHEME, 0)
+    banner(f"bin keys off {name} scheme={scheme}")
+    sc = scene(name)
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SCHEME, SCHEMES[scheme])
     gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_KEYS, 0)
     try:
-        b = gsr.gsr_bin(ctx, dev(sc.splats), dev(sc.depths), 64, 64)
+        b = gsr.gsr_bin(ctx, dev(sc.splats), dev(sc.depths), sc.width, sc.height)
         assert b.raw.keys is None
         _, v, r = gsr.gsr_bins_copy(ctx, b)
-        ref = oracle_bins("tiny")
+        ref = oracle_bins(name)
         assert np.array_equal(host(v, np.uint32), ref.vals) and np.array_equal(host(r, np.uint32), ref.ranges)
     finally:
         gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_KEYS, 1)
