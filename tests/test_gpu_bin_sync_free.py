@@ -39,7 +39,7 @@ def bin_and_compare(ctx, splats, depths, w, h, ref):
     return b
 
 
-@pytest.mark.parametrize("scheme,rule", [(0, 0), (1, 0), (0, 1), (2, 0), (2, 1)])
+@pytest.mark.parametrize("scheme,rule", [(0, 0), (1, 0), (2, 0), (0, 1), (1, 1), (2, 1)])
 def test_sync_free_bins_equal_the_oracle(scheme, rule):
     """First call on a fresh context: no count seen, so it waits once; the later calls size their buffers from the
     counts seen (smaller scenes after a larger one, and the same scene again) and do not wait."""
@@ -139,3 +139,20 @@ def test_sync_mode_reports_its_count():
         assert gsr.gsr_bin_pair_count(c) == (0, False)
     finally:
         c.close()
+
+
+@pytest.mark.parametrize("scheme", [0, 1, 2])
+def test_sync_free_without_keys(scheme):
+    """Sync-free with GSR_OPT_BIN_KEYS = 0: no keys, and the values and ranges still the oracle's."""
+    from differentiable_gaussian_splatting_amd import gsr
+    banner(f"bin sync-free keys off scheme={scheme}")
+    ctx = new_ctx(scheme)
+    gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_KEYS, 0)
+    try:
+        sc = scene("raster84k")
+        ref = oracle_bins("raster84k")
+        for _ in range(2):  # the first call waits (no count seen), the second does not
+            b = bin_and_compare(ctx, sc.splats, sc.depths, sc.width, sc.height, ref)
+            assert b.raw.keys is None
+    finally:
+        ctx.close()
