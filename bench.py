@@ -383,6 +383,11 @@ def main():
                 mcyc = profiling.mfma_busy_for(profiling.STAGE_KERNEL[k], traffic_md)
                 r["mfma_busy_frac"] = (None if mcyc is None else
                                        mcyc / (r["kernel_ms"] * 1e-3 * 1024 * 2.4e9))
+                # the hardware's own vector flop count over the same time: inactive lanes count (an upper bound on
+                # the vector work) and matrix-core flops do not (the backward's moment sums run there)
+                cf = profiling.counted_flops_for(profiling.STAGE_KERNEL[k], traffic_md)
+                r["counted_tflops_upper"] = None if cf is None else cf / (r["kernel_ms"] * 1e-3) / 1e12
+                r["counted_frac_upper"] = None if cf is None else r["counted_tflops_upper"] / ALU_PEAK_TFLOPS
         # the forward with the hardware exponential (GSR_OPT_FORWARD_EXP), the same operation count
         kf = fast_exp["kernel_ms"]
         roofs["forward_fast_exp"] = {"bound": "alu", "achieved": fwd_ops / (kf * 1e-3) / 1e12, "peak": ALU_PEAK_TFLOPS,

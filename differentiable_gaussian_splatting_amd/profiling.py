@@ -225,10 +225,12 @@ def pmc_md(base: str, cmd: str, workload: str, first: int | None = None) -> str:
             if base_kernel(k) in KERNEL_SOURCES:  # one record per instance (k_adam<false> and <true> differ)
                 inst = (short_name(k).replace(", ", ",").replace("unsigned int", "uint32")
                         .replace("unsigned long", "uint64"))
+                counted = (64 * (f.get("SQ_INSTS_VALU_FLOPS_FP32", 0) + f.get("SQ_INSTS_VALU_FLOPS_FP64", 0))
+                           if "SQ_INSTS_VALU_FLOPS_FP32" in f else None)
                 record[inst] = {"hbm_bytes": hbm, "fetch_kib": fetch, "write_kib": write, "valu_issue": issue,
                                 "valu_insts": None if "SQ_INSTS_VALU" not in v else v["SQ_INSTS_VALU"] - mfma,
                                 "mfma_insts": mfma, "mfma_busy_cycles": v.get("SQ_VALU_MFMA_BUSY_CYCLES"),
-                                "sources": source_hash(inst)}
+                                "counted_flops": counted, "sources": source_hash(inst)}
         tf = (64 * (f.get("SQ_INSTS_VALU_FLOPS_FP32", 0) + f.get("SQ_INSTS_VALU_FLOPS_FP64", 0)) / (f["_ns"] * 1e3)
               if f.get("_ns") else None)
         lines.append(f"| `{k[:60]}` | " + " | ".join(vals) + f" | {'' if issue is None else f'{issue:.3f}'} | "
@@ -293,6 +295,17 @@ def valu_insts_for(kernel, md_path: str):
         return None
     k = rec["kernels"][kernel]
     return k.get("valu_insts") if k.get("sources") == source_hash(kernel) else None
+
+
+def counted_flops_for(kernel, md_path: str):
+    """Recorded vector flops per launch of the kernel instance from the FLOPS counters, 64 lanes x
+    (SQ_INSTS_VALU_FLOPS_FP32 + SQ_INSTS_VALU_FLOPS_FP64): an upper bound on the vector work, since inactive lanes
+    count; MFMA flops are not in these counters. None when unrecorded or its sources changed since."""
+    rec = read_traffic(md_path)
+    if not rec or kernel not in rec.get("kernels", {}):
+        return None
+    k = rec["kernels"][kernel]
+    return k.get("counted_flops") if k.get("sources") == source_hash(kernel) else None
 
 
 def main(argv=None):

@@ -231,12 +231,14 @@ def test_bin_ellipse_rule_ragged_images(ctx, w, h):
 
 
 @pytest.mark.parametrize("w,h,n,cluster,levels", [(16, 16, 6000, 0.0, 0), (64, 48, 30000, 0.0, 0),
-                                                   (800, 800, 200000, 0.3, 0), (16, 16, 6000, 0.0, 3)])
+                                                   (800, 800, 200000, 0.3, 0), (16, 16, 6000, 0.0, 3),
+                                                   (16, 16, 70000, 0.0, 0), (16, 16, 70000, 0.0, 3)])
 def test_tile_depth_long_lists(ctx, w, h, n, cluster, levels):
     """Tile lists longer than the tile-first scheme's on-chip capacity (3456 pairs) are ordered through the arena
     instead: one tile of 6000 pairs; twelve tiles of 5-11 thousand; 16 tiles of up to 25 thousand (30% of the
-    splats in a 48-pixel square) among 2,484 short ones, both forms in one launch; and one tile of 6000 pairs at
-    three depths (crowded buckets: the radix sort through the arena). Bit-exact against the oracle on a fresh
+    splats in a 48-pixel square) among 2,484 short ones, both forms in one launch; one tile of 6000 pairs at three
+    depths (crowded buckets: the radix sort through the arena); and one tile of 70,000 pairs (positions past 16
+    bits), by buckets and at three depths by the radix sort. Bit-exact against the oracle on a fresh
     context (no count seen: the first call takes the tile-first path) and again with the count seen."""
     import oracle
     from differentiable_gaussian_splatting_amd import gsr

@@ -145,6 +145,55 @@ def test_backward_ragged_images(ctx, w, h):
     assert ok, (worst, at)
 
 
+@pytest.fixture(scope="module")
+def deep_pile():
+    """48 x 40 pixels under 12,000 large faint splats: every tile's list holds 11,700-12,000 pairs (past what one
+    workgroup sorts on chip, so the tile-first binning takes its long-list path), most alphas sit near 1/255, and
+    some pixels composite nearly the whole list while others stop part way."""
+    import oracle
+    w, h = 48, 40
+    sc = custom_scene(name="pile", width=w, height=h, n=12000, seed=91, size_classes=((1.0, 8.0, 30.0),),
+                      opacity_mu=-6.0, opacity_sd=1.0, vout_sd=1.0, margin=0.0)
+    ob = oracle.bin(sc.splats, sc.depths, w, h)
+    fwd = oracle.render_forward(sc.splats, ob, w, h)
+    ref = oracle.render_backward(sc.splats, ob, w, h, *fwd[:3], sc.v_out)
+    return sc, ob, fwd, ref
+
+
+@pytest.mark.parametrize("form", ["default", "deterministic", "per_splat"])
+def test_deep_pile_matches_oracle(deep_pile, form):
+    """Bins, image and gradients of the deep pile against the oracle. A fresh context has seen no pair count, so
+    its first call takes the tile-first binning (lists past the on-chip capacity); the next call has seen 12,000
+    pairs per tile and takes the presort scheme. Both bins bit-exact, then the raster under each backward form."""
+    from differentiable_gaussian_splatting_amd import gsr
+    sc, ob, fwd, ref = deep_pile
+    w, h = sc.width, sc.height
+    banner(f"deep pile 48x40 n=12000 backward={form}")
+    lengths = ob.ranges[:, 1] - ob.ranges[:, 0]
+    ft_ref = fwd[1]
+    assert lengths.min() > 11000 and (ft_ref < 2e-4).any() and (ft_ref > 1e-3).any()
+    c = gsr.Context(0)
+    try:
+        sp = dev(sc.splats)
+        for _ in range(2):
+            bins = gsr.gsr_bin(c, sp, dev(sc.depths), w, h)
+            keys, vals, ranges = gsr.gsr_bins_copy(c, bins)
+            assert np.array_equal(host(keys, np.uint64), ob.keys)
+            assert np.array_equal(host(vals, np.uint32), ob.vals)
+            assert np.array_equal(host(ranges, np.uint32), ob.ranges)
+        out, ft, lc = run_forward(c, sp, bins, w, h)
+        compare_forward((out, ft, lc), fwd)
+        set_det(c, form == "deterministic")
+        gsr.gsr_set_option(c, gsr.GSR_OPT_BACKWARD_SCHEME,
+                           gsr.GSR_BACKWARD_PER_SPLAT if form == "per_splat" else gsr.GSR_BACKWARD_PER_PIXEL)
+        g = host(run_backward(c, sc, bins, out, ft, lc))
+    finally:
+        c.close()
+    ok, worst, at = grads_close(g, ref)
+    print(f"  worst |gpu-ref| / (1e-4 + 1e-4 |ref|) = {worst:.3g} at {at}")
+    assert ok, (worst, at, g[at], ref[at])
+
+
 def set_det(ctx, on: bool):
     from differentiable_gaussian_splatting_amd import gsr
     gsr.gsr_set_option(ctx, gsr.GSR_OPT_DETERMINISTIC, 1 if on else 0)
