@@ -95,6 +95,33 @@ def calib_copy():
     print(json.dumps({"calib_copy_bytes_read": 4 * n, "calib_copy_bytes_written": 4 * n, "copies": 10}))
 
 
+def device_stream_gbs(torch) -> dict:
+    """Bytes moved per second (read + written) by two of torch's streaming kernels on 512 MiB vectors, each the
+    median of ten event-timed launches: a copy (one read, one write) and an addition (two reads, one write). They
+    show the HBM rate plain streaming kernels reach on this GPU, beside the published 8 TB/s."""
+    import numpy as np
+    n = 128 * 1024 * 1024
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.ones_like(a)
+    c = torch.empty_like(a)
+
+    def rate(f, nbytes):
+        f()
+        ts = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return nbytes / (float(np.median(ts)) * 1e-3) / 1e9
+
+    out = {"copy": rate(lambda: c.copy_(a), 8 * n), "add": rate(lambda: torch.add(a, b, out=c), 12 * n)}
+    del a, b, c
+    return out
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -423,6 +450,10 @@ def main():
     result["context"] = {"pages_m4max_ms_per_iter_fwd_bwd_adam": 15.354, "pages_m4max_backward_ms_per_call": 4.65,
                          "pages_splats": 409660, "this_fwd_bwd_adam_ms": stage_ms["forward"] + stage_ms["backward"]
                          + stage_ms["adam"], "this_backward_ms": stage_ms["backward"]}
+    stream = device_stream_gbs(torch)
+    result["context"]["torch_stream_gbs"] = stream
+    if result.get("rooflines"):
+        result["context"]["adam_frac_of_torch_add"] = result["rooflines"]["adam"]["achieved"] / stream["add"]
     result["projection"] = bench_projection(args, ctx, gsr, scenes, sc, hp=hp, bc=bc)
     if not args.no_bin_stress:
         result["bin_stress"] = bench_bin_stress(args, ctx, gsr, scenes, torch, np)

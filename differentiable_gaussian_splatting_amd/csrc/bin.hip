@@ -701,48 +701,85 @@ __global__ __launch_bounds__(kThreads) void k_ranges(const K* __restrict__ keys,
 }
 
 // Longest lists first, so that the raster kernels start the slowest tiles at once and the short ones fill the
-// workgroup slots that free up (the tile loads differ several-fold, and the grid exceeds the resident slots).
-constexpr uint32_t kOrderThreads = 1024, kOrderClasses = 64;
+// workgroup slots that free up (the tile loads differ several-fold, and the grid exceeds the resident slots). A
+// counting sort of the tiles into 64 classes of list length (or of the previous forward's walk counts): most tiles
+// fall into a few classes, so each wave first groups its lanes by class (a ballot per class bit) and one lane per
+// class does the LDS addition for all of them. Each thread keeps the lengths of its first kOrderItems tiles in
+// registers; further tiles are read again in each pass.
+constexpr uint32_t kOrderThreads = 1024, kOrderClasses = 64, kOrderItems = 4;
+static_assert(kOrderClasses == kWave, "one class per lane in the scan");
 
 __global__ __launch_bounds__(kOrderThreads) void k_tile_order(const uint32_t* __restrict__ ranges,
                                                               const uint32_t* __restrict__ cost, uint32_t num_tiles,
                                                               uint32_t num_pairs, uint32_t* __restrict__ order,
                                                               bool identity) {
   __shared__ uint32_t s_count[kOrderClasses], s_base[kOrderClasses];
-  __shared__ uint32_t s_max;
-  const uint32_t tid = threadIdx.x;
+  __shared__ uint32_t s_max[kOrderThreads / kWave];
+  const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   if (identity) {
     for (uint32_t t = tid; t < num_tiles; t += kOrderThreads) order[t] = t;
     return;
   }
-  if (tid < kOrderClasses) s_count[tid] = 0;
-  if (tid == 0) s_max = 0;
-  __syncthreads();
-  auto len_of = [&](uint32_t t) {
-    if (cost) return cost[4 * t] + cost[4 * t + 1] + cost[4 * t + 2] + cost[4 * t + 3];
+  auto len_of = [&](uint32_t t) -> uint32_t {
+    if (cost) {
+      const uint4 c = reinterpret_cast<const uint4*>(cost)[t];
+      return c.x + c.y + c.z + c.w;
+    }
     const uint32_t start = min(ranges[2 * t], num_pairs);
     const uint32_t end = max(start, min(ranges[2 * t + 1], num_pairs));
     return end - start;
   };
+  if (tid < kOrderClasses) s_count[tid] = 0;
+  uint32_t len[kOrderItems];
   uint32_t lmax = 0;
-  for (uint32_t t = tid; t < num_tiles; t += kOrderThreads) lmax = max(lmax, len_of(t));
-  atomicMax(&s_max, lmax);
+#pragma unroll
+  for (uint32_t i = 0; i < kOrderItems; ++i) {
+    const uint32_t t = tid + i * kOrderThreads;
+    len[i] = t < num_tiles ? len_of(t) : 0u;
+    lmax = max(lmax, len[i]);
+  }
+  for (uint32_t t = tid + kOrderItems * kOrderThreads; t < num_tiles; t += kOrderThreads) lmax = max(lmax, len_of(t));
+  for (uint32_t d = 1; d < kWave; d <<= 1) lmax = max(lmax, uint32_t(__shfl_xor(int(lmax), int(d))));
+  if (lane == 0) s_max[w] = lmax;
   __syncthreads();
-  const uint64_t span = uint64_t(s_max) + 1;
-  auto class_of = [&](uint32_t t) {  // 0 = longest
-    return kOrderClasses - 1 - uint32_t(uint64_t(len_of(t)) * kOrderClasses / span);
+  uint32_t m = 0;
+#pragma unroll
+  for (uint32_t q = 0; q < kOrderThreads / kWave; ++q) m = max(m, s_max[q]);
+  const uint64_t span = uint64_t(m) + 1;
+  auto class_of = [&](uint32_t l) {  // 0 = longest
+    return kOrderClasses - 1 - uint32_t(uint64_t(l) * kOrderClasses / span);
   };
-  for (uint32_t t = tid; t < num_tiles; t += kOrderThreads) atomicAdd(&s_count[class_of(t)], 1u);
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t run = 0;
-    for (uint32_t c = 0; c < kOrderClasses; ++c) {
-      s_base[c] = run;
-      run += s_count[c];
+  // f(t, valid, class) for every tile, in chunks of kOrderThreads that every thread of the workgroup takes part in
+  auto for_each_tile = [&](auto f) {
+#pragma unroll
+    for (uint32_t i = 0; i < kOrderItems; ++i) {
+      if (i * kOrderThreads >= num_tiles) return;
+      const uint32_t t = tid + i * kOrderThreads;
+      f(t, t < num_tiles, class_of(len[i]));
     }
+    for (uint32_t t0 = kOrderItems * kOrderThreads; t0 < num_tiles; t0 += kOrderThreads) {
+      const uint32_t t = t0 + tid;
+      f(t, t < num_tiles, class_of(t < num_tiles ? len_of(t) : 0u));
+    }
+  };
+  for_each_tile([&](uint32_t, bool valid, uint32_t c) {
+    const uint64_t peers = match_digit<6>(c, valid);
+    if (valid && (peers & lanemask_lt(lane)) == 0) atomicAdd(&s_count[c], uint32_t(__popcll(peers)));
+  });
+  __syncthreads();
+  if (w == 0) {
+    const uint32_t x = s_count[lane];
+    s_base[lane] = wave_inclusive_sum(x) - x;
   }
   __syncthreads();
-  for (uint32_t t = tid; t < num_tiles; t += kOrderThreads) order[atomicAdd(&s_base[class_of(t)], 1u)] = t;
+  for_each_tile([&](uint32_t t, bool valid, uint32_t c) {
+    const uint64_t peers = match_digit<6>(c, valid);
+    const int leader = valid ? int(__ffsll(static_cast<unsigned long long>(peers))) - 1 : 0;
+    uint32_t base = 0;
+    if (valid && int(lane) == leader) base = atomicAdd(&s_base[c], uint32_t(__popcll(peers)));
+    base = uint32_t(__shfl(int(base), leader));
+    if (valid) order[base + uint32_t(__popcll(peers & lanemask_lt(lane)))] = t;
+  });
 }
 
 uint32_t bits_of(uint64_t v) {
