@@ -1,8 +1,9 @@
 """Benchmark of the splat rasterizer hot path on one MI355X.
 
-A step is one pass of the whole path over the 800x800, 410k-splat workload: bin (emit, radix sort, tile ranges),
-render_forward, render_backward, then the fused Adam step over 59 float32 parameters per splat (5 groups). Inputs
-are seeded synthetic data resident in device memory before the timed region; the arena is pre-grown.
+A step is one pass of the whole path over the 800x800, 410k-splat workload: bin (the (tile, depth) order of the
+pairs and the tile ranges), render_forward, render_backward, then the fused Adam step over 59 float32 parameters per
+splat (5 groups). Inputs are seeded synthetic data resident in device memory before the timed region; the arena is
+pre-grown. Defaults: W = 10 warmup steps, then 3 repeats of K = 50 timed steps (the median repeat is reported).
 
 Prints one JSON line: the metric is splat-pixel evaluations per second over whole steps, where the evaluations of a
 step are E_fwd (list entries the forward examines, up to and including each pixel's stopping splat) plus E_bwd
@@ -66,8 +67,8 @@ def scene_label(spec) -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="iter410k")
     ap.add_argument("--bin-scheme", choices=["tile_depth", "presort", "key64"], default="tile_depth")
     ap.add_argument("--raster-skip", type=int, choices=[0, 1], default=1)
@@ -610,14 +611,16 @@ def bench_changing_views(args, ctx, gsr, scenes, torch, np):
     """The raster kernels when every step sees a new view, as in training: gauss410k projected by a camera that
     turns 1 degree about its vertical axis per step (about 14 px, most of a tile, of image motion), then bin,
     forward and backward. The default launch order ranks the tiles by the walk counts of the previous forward -
-    here a different view - so this leg times the forward and backward kernels (library events, K steps per
-    repeat, median of the repeats) under each order: cost (default), list length, tile index."""
+    here a different view - so this leg times the forward and backward kernels (library events, min(K, 20) steps
+    per repeat, so that the camera turns at most 20 degrees; median of the repeats) under each order: cost
+    (default), list length, tile index."""
+    nv = min(args.steps, 20)
     g3 = scenes.make_gaussians("gauss410k")
     W, H = g3.width, g3.height
     ps = [torch.from_numpy(a).cuda() for a in (g3.means, g3.log_scales, g3.quats, g3.raw_opacities, g3.sh)]
     v_out = torch.from_numpy(np.random.default_rng(31).normal(0.0, 0.01, (H, W, 4)).astype(np.float32)).cuda()
     cams = []
-    for k in range(args.steps + 1):
+    for k in range(nv + 1):
         a = np.deg2rad(1.0 * k)
         Ry = np.array([[np.cos(a), 0.0, np.sin(a)], [0.0, 1.0, 0.0], [-np.sin(a), 0.0, np.cos(a)]])
         R = Ry @ np.asarray(g3.camera["R"], np.float64)
@@ -643,8 +646,8 @@ def bench_changing_views(args, ctx, gsr, scenes, torch, np):
             b = gsr.gsr_bin(ctx, sp, dp, W, H)
             gsr.gsr_render_forward(ctx, sp, b, W, H, out, ft, lc)
             torch.cuda.synchronize()
-            gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, args.steps)
-            for k in range(1, args.steps + 1):
+            gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, nv)
+            for k in range(1, nv + 1):
                 gsr.gsr_project_forward(ctx, cams[k], *ps, splats=sp, depths=dp)
                 b = gsr.gsr_bin(ctx, sp, dp, W, H)
                 gsr.gsr_render_forward(ctx, sp, b, W, H, out, ft, lc)
