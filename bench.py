@@ -166,7 +166,17 @@ def run_oracle(sc, adam_groups, hp, bc, bin_rule="box"):
     oracle.render_backward_mt(sc.splats, ob, sc.width, sc.height, out, ft, lc, sc.v_out, threads)
     tm["backward"] = time.perf_counter() - t0
     return {"times": t, "times_mt": tm, "threads": threads, "fwd_stats": fst, "bwd_stats": bst,
-            "num_pairs": ob.num_pairs, "out": out, "lc": lc, "ranges": ob.ranges}
+            "num_pairs": ob.num_pairs, "out": out, "lc": lc, "ranges": ob.ranges,
+            "super_pairs": super_pairs(ob.keys, ob.vals, sc.width)}
+
+
+def super_pairs(keys, vals, width):
+    """(splat, super-tile) pairs of the bins: the distinct 2 x 2-tile squares among each splat's tiles."""
+    import numpy as np
+    tx_n = (width + 15) // 16
+    tiles = (keys >> np.uint64(32)).astype(np.int64)
+    sup = (tiles // tx_n // 2) * ((tx_n + 1) // 2) + (tiles % tx_n) // 2
+    return int(np.unique(vals.astype(np.int64) * (1 << 32) + sup).size)
 
 
 def roctx():
@@ -385,7 +395,7 @@ def main():
         }
         for k, r in roofs.items():
             r["kernel_ms"] = kernel_ms[k]
-        roofs["sort"] = sort_roofline(args, N, P, W, H, kernel_ms)
+        roofs["sort"] = sort_roofline(args, N, P, W, H, kernel_ms, cpu["super_pairs"])
         # HBM bytes per launch from the committed counter summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated);
         # null when the kernel's sources changed since the counters were taken
         from differentiable_gaussian_splatting_amd import profiling
@@ -488,7 +498,7 @@ def scheme_opt(gsr, name):
     return {"tile_depth": gsr.GSR_BIN_TILE_DEPTH, "presort": gsr.GSR_BIN_PRESORT, "key64": gsr.GSR_BIN_KEY64}[name]
 
 
-def sort_roofline(args, N, P, W, H, kernel_ms):
+def sort_roofline(args, N, P, W, H, kernel_ms, Ps=None):
     """The binning's sorts against HBM: algorithmic bytes of the scheme per launch over their kernels' own time.
     Tile-first (the default): see the branch below. Presort: the two radix sorts. Depth sort: 4 passes of 8-bit
     digits over the n 32-bit depth keys with their indices, each pass reading the keys for the histogram (4 B) and
@@ -507,22 +517,26 @@ def sort_roofline(args, N, P, W, H, kernel_ms):
     pages = {"pages_64bit_sort_bytes": pages_bytes,
              "pages_target_ms_at_70pct": pages_bytes / (0.7 * HBM_PEAK_GBS * 1e9) * 1e3}
     if args.bin_scheme == "tile_depth" and kernel_ms["tile_depth"] > 0:
-        # tile-first: the pairs in tile order, then each tile's list by (depth, splat). The per-tile order reads each
-        # pair's splat and gathers its depth (8 B), writes the value and the 64-bit key (12 B). Under the box rule
-        # (the counting sort, tile_scan > 0) the scatter reads each splat's rectangle and count (20 B), its block's
-        # row of the count table and the tile starts (8 B per tile and block of 1024 splats), and writes each pair's
-        # splat (4 B); the column scan reads the table twice and writes it once (12 B per entry), the tile starts
-        # read the totals and write starts and ranges (16 B per tile). Otherwise the tile ids' radix sort on packed
-        # words, 12 B per pair and pass.
+        # tile-first. Under the box rule (the two-level counting sort, tile_scan > 0): the column scan reads the
+        # [blocks of 1024 splats][tiles + super-tiles] count table twice and writes it once (12 B per entry), the
+        # starts read the totals and write the starts (8 B per list) and the tiles' ranges (8 B per tile); the
+        # scatter reads each splat's rectangle and depth (20 B), its block's row of the super-tile part of the table
+        # and the super-tile starts (8 B per super-tile and block), and writes each (splat, super-tile) pair's 8 B
+        # entry; the per-super-tile order reads those entries (8 B) and writes each (splat, tile) pair's value and
+        # 64-bit key (12 B). Otherwise the tile ids' radix sort on packed words (12 B per pair and pass) and the
+        # per-tile order (it reads each pair's splat and gathers its depth, 8 B, and writes 12 B).
         fused = kernel_ms["tile_scan"] > 0
         nblk = (N + 1023) // 1024
+        sups = ((W + 31) // 32) * ((H + 31) // 32)
         if fused:
-            by = 24 * P + 20 * N + 20 * nblk * tiles + 16 * tiles
+            by = (12 * P + 16 * Ps + 20 * N + 12 * nblk * (tiles + sups) + 8 * nblk * sups + 8 * (tiles + sups)
+                  + 8 * tiles)
             ms = kernel_ms["tile_scan"] + kernel_ms["tile_sort"] + kernel_ms["tile_depth"]
-            note = "count table scan + tile starts + scatter + per-tile order"
+            note = ("count table scan + list starts + scatter to super-tiles + per-super-tile order "
+                    f"({Ps} super-tile pairs)")
         else:
             by = (12 * tile_passes + 20) * P
-            ms = kernel_ms["tile_sort"] + kernel_ms["tile_depth"]
+            ms = kernel_ms["tile_sort"] + kernel_ms["tile_depth"] + kernel_ms["tile_scan"]
             note = f"radix sort of the tile ids ({tile_passes} passes, packed words) + per-tile order"
         return {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "work_per_launch": by, "kernel_ms": ms, "scheme": "tile_depth", "bytes": note,

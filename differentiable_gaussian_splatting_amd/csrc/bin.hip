@@ -417,18 +417,22 @@ __global__ __launch_bounds__(kThreads) void k_emit_ellipse(const float* __restri
 }
 
 // Fused counting sort of the pairs by tile (the tile-first scheme under the box rule), in place of emitting keys and
-// radix-sorting them, and without the count scan. Block b of kFuseBlock consecutive splats (in index order) computes
-// their rectangles and counts, counts its pairs per tile in LDS and writes the counts as row b of a [blocks][tiles]
-// table (k_prep_rows); a column scan turns each row into the block's offset in each tile's list and gives each
-// tile's total (k_tile_cols), a scan of the totals gives the tiles' starts and the ranges (k_tile_starts); the same
-// blocks then enumerate their pairs again (from the rectangles and a block scan of the counts) and place each splat
-// at the next free slot of their stretch of the tile's list (an LDS counter per tile; k_tile_scatter). Within a
-// stretch the order is whatever the LDS atomics give: the per-tile sort that follows orders each list by (depth
-// bits, splat), which is unique, so the bins do not depend on it. The pairs are enumerated as in k_emit (chunks of
-// pairs, owner marks and a running maximum).
+// radix-sorting them, and without the count scan; in two levels, tiles and super-tiles (squares of 2 x 2 tiles).
+// Block b of kFuseBlock consecutive splats (in index order) computes their rectangles and counts, and counts its
+// splats per tile and per super-tile with two difference arrays in LDS (four additions per splat and level: +1 at
+// the rectangle's first corner, -1 past its right and bottom edges, +1 past both; prefix sums along x and then y
+// turn them into the counts), written as row b of a [blocks][tiles + super-tiles] table (k_prep_rows). A column scan
+// turns each row into the block's offset in each list and gives each list's total (k_tile_cols); scans of the
+// totals give the tiles' starts with the ranges, and the super-tiles' starts (k_tile_starts). The same blocks then
+// enumerate their (splat, super-tile) pairs - a third of the (splat, tile) pairs at 410k splats - and place each
+// splat at the next free slot of their stretch of the super-tile's list (an LDS counter per super-tile;
+// k_tile_scatter). Within a stretch the order is whatever the LDS atomics give: the per-super-tile order that
+// follows (tile_depth.hip) sorts each list by (depth bits, splat), which is unique, and writes the four tiles'
+// lists from it, so the bins do not depend on it. The pairs are enumerated as in k_emit (chunks of pairs, owner
+// marks and a running maximum).
 constexpr uint32_t kFuseThreads = 1024;                  // a splat per thread
 constexpr uint32_t kFuseBlock = kFuseThreads;            // splats per block
-constexpr uint32_t kFuseMaxTiles = 8192;                 // the per-tile LDS counters (32 KB)
+constexpr uint32_t kFuseMaxTiles = 8192;                 // tiles (+ at most half as many super-tiles) counted in LDS
 constexpr uint32_t kColTiles = 64, kColThreads = 1024;   // the column scan: 64 tiles by 16 stretches of rows
 constexpr uint32_t kColParts = kColThreads / kColTiles;
 constexpr uint32_t kColBatch = 32;                       // rows loaded at once
@@ -445,11 +449,12 @@ __device__ __forceinline__ uint32_t die_band(uint32_t i, uint32_t nb) {
 // Enumerates the pairs of a block of kFuseBlock splats (thread tid holds splat tid of the block): s_off[0..kFuseBlock]
 // are the splats' block-local first pair positions (s_off[kFuseBlock] = the block's total, `end` the pairs to
 // enumerate, end <= that total), s_tx0 / s_ty0 / s_w their rectangles. Chunks of kPer pairs per thread, as k_emit.
-// Calls f(q, tile) for each pair, q the splat's index in the block. Every thread of the workgroup must call it.
+// Calls f(q, row, col) for each pair, q the splat's index in the block and (col, row) the pair's cell of the grid.
+// Every thread of the workgroup must call it.
 template <typename F>
 __device__ __forceinline__ void for_each_pair(const uint32_t* s_off, const uint32_t* s_tx0, const uint32_t* s_ty0,
-                                              const uint32_t* s_w, uint32_t end, uint32_t tiles_x, uint32_t* s_mark,
-                                              uint32_t* smem, F f) {
+                                              const uint32_t* s_w, uint32_t end, uint32_t* s_mark, uint32_t* smem,
+                                              F f) {
   constexpr uint32_t kPer = 4, kChunk = kPer * kFuseThreads;
   const uint32_t tid = threadIdx.x;
   uint32_t carry = 0;
@@ -481,91 +486,149 @@ __device__ __forceinline__ void for_each_pair(const uint32_t* s_off, const uint3
         const uint32_t k = p - s_off[q];
         const uint32_t w = s_w[q];
         const uint32_t r = div_small(k, w);
-        f(q, (s_ty0[q] + r) * tiles_x + (s_tx0[q] + (k - r * w)));
+        f(q, s_ty0[q] + r, s_tx0[q] + (k - r * w));
       }
     }
     carry = chunk_max;
   }
 }
 
+// Super-tiles of a grid of tiles_x x tiles_y tiles: ceil(tiles_x / 2) x ceil(tiles_y / 2), super-tile (sx, sy)
+// holding tiles (2 sx + dx, 2 sy + dy), dx, dy in {0, 1}.
+__host__ __device__ __forceinline__ uint32_t super_dim(uint32_t tiles) { return (tiles + 1) / 2; }
+
+// Adds the rectangle [x0, x1) x [y0, y1) to the difference array d[ny][nx] in LDS (wrapping 32-bit sums): after
+// inclusive prefix sums along x and then along y each of its cells holds one more. Corners past the last column or
+// row are left out (nothing after them is summed).
+__device__ __forceinline__ void diff_add(uint32_t* d, uint32_t nx, uint32_t ny, uint32_t x0, uint32_t y0,
+                                         uint32_t x1, uint32_t y1) {
+  atomicAdd(&d[y0 * nx + x0], 1u);
+  if (x1 < nx) atomicAdd(&d[y0 * nx + x1], ~0u);
+  if (y1 < ny) {
+    atomicAdd(&d[y1 * nx + x0], ~0u);
+    if (x1 < nx) atomicAdd(&d[y1 * nx + x1], 1u);
+  }
+}
+
+// Inclusive prefix sums, in place in LDS, of `lines` sequences of `len` values: sequence k starts at a[k * step]
+// and its values lie `stride` apart. The workgroup's waves take the sequences in turn, 64 values per step.
+__device__ __forceinline__ void lds_scan_lines(uint32_t* a, uint32_t lines, uint32_t len, uint32_t step,
+                                               uint32_t stride) {
+  const uint32_t lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave, waves = blockDim.x / kWave;
+  for (uint32_t k = w; k < lines; k += waves) {
+    uint32_t* const line = a + k * step;
+    uint32_t carry = 0;
+    for (uint32_t c0 = 0; c0 < len; c0 += kWave) {
+      const uint32_t i = c0 + lane;
+      const uint32_t x = wave_inclusive_sum(i < len ? line[i * stride] : 0u) + carry;
+      if (i < len) line[i * stride] = x;
+      carry = uint32_t(__builtin_amdgcn_readlane(int(x), int(kWave - 1)));
+    }
+  }
+}
+
 // k_prep for the fused counting sort (box rule, num_tiles <= kFuseMaxTiles): blocks of kFuseBlock splats write
 // each splat's rectangle and count, the block's count total in part[block] (k_total sums them), and the block's
-// pairs per tile as row `block` of `rows`.
+// splats per tile and per super-tile as row `block` of `rows` ([blocks][tiles + super-tiles]).
 __global__ __launch_bounds__(kFuseThreads) void k_prep_rows(const float* __restrict__ splats,
                                                             const float* __restrict__ depths, uint32_t n,
                                                             uint32_t tiles_x, uint32_t tiles_y,
                                                             uint4* __restrict__ rects, uint32_t* __restrict__ counts,
-                                                            uint64_t* __restrict__ part, uint32_t num_tiles,
+                                                            uint64_t* __restrict__ part,
                                                             uint32_t* __restrict__ rows) {
-  extern __shared__ uint32_t s_tile[];  // num_tiles counters
-  __shared__ uint32_t s_off[kFuseBlock + 1], s_tx0[kFuseBlock], s_ty0[kFuseBlock], s_w[kFuseBlock];
-  __shared__ uint32_t s_mark[4 * kFuseThreads];
+  extern __shared__ uint32_t s_cnt[];  // [tiles_y][tiles_x], then [sup_y][sup_x]: difference arrays, then counts
   __shared__ uint32_t smem[kFuseThreads / kWave];
+  const uint32_t sup_x = super_dim(tiles_x), sup_y = super_dim(tiles_y);
+  const uint32_t num_tiles = tiles_x * tiles_y, width = num_tiles + sup_x * sup_y;
+  uint32_t* const s_sup = s_cnt + num_tiles;
   const uint32_t tid = threadIdx.x, i = blockIdx.x * kFuseBlock + tid;
-  for (uint32_t t = tid; t < num_tiles; t += kFuseThreads) s_tile[t] = 0;
+  for (uint32_t t = tid; t < width; t += kFuseThreads) s_cnt[t] = 0;
   Rect r{0, 0, 0, 0};
   if (i < n) {
     r = tile_rect(splats + size_t(i) * 9, depths[i], tiles_x, tiles_y);
     rects[i] = make_uint4(r.tx0, r.ty0, r.w, r.h);
     counts[i] = r.w * r.h;
   }
-  s_tx0[tid] = r.tx0;
-  s_ty0[tid] = r.ty0;
-  s_w[tid] = r.w ? r.w : 1u;
-  uint32_t total;
-  s_off[tid] = block_exclusive_scan<uint32_t, kFuseThreads>(r.w * r.h, &total, smem);
-  if (tid == 0) {
-    s_off[kFuseBlock] = total;
-    part[blockIdx.x] = total;
+  uint32_t total;  // the scan's barriers also order the zeroing before the additions
+  block_exclusive_scan<uint32_t, kFuseThreads>(r.w * r.h, &total, smem);
+  if (tid == 0) part[blockIdx.x] = total;
+  if (r.w) {
+    diff_add(s_cnt, tiles_x, tiles_y, r.tx0, r.ty0, r.tx0 + r.w, r.ty0 + r.h);
+    diff_add(s_sup, sup_x, sup_y, r.tx0 / 2, r.ty0 / 2, (r.tx0 + r.w - 1) / 2 + 1, (r.ty0 + r.h - 1) / 2 + 1);
   }
   __syncthreads();
-  for_each_pair(s_off, s_tx0, s_ty0, s_w, total, tiles_x, s_mark, smem,
-                [&](uint32_t, uint32_t tile) { atomicAdd(&s_tile[tile], 1u); });
+  lds_scan_lines(s_cnt, tiles_y, tiles_x, tiles_x, 1);  // along x
+  lds_scan_lines(s_sup, sup_y, sup_x, sup_x, 1);
   __syncthreads();
-  uint32_t* const row = rows + size_t(blockIdx.x) * num_tiles;
-  for (uint32_t t = tid; t < num_tiles; t += kFuseThreads) row[t] = s_tile[t];
+  lds_scan_lines(s_cnt, tiles_x, tiles_y, 1, tiles_x);  // along y
+  lds_scan_lines(s_sup, sup_x, sup_y, 1, sup_x);
+  __syncthreads();
+  uint32_t* const row = rows + size_t(blockIdx.x) * width;
+  for (uint32_t t = tid; t < width; t += kFuseThreads) row[t] = s_cnt[t];
 }
 
-// The scatter: the workgroup takes block blk (die-banded) of kFuseBlock splats, enumerates its pairs again from the
-// rectangles and counts, and puts each pair's splat at list[tile_start[tile] + rows[blk][tile] + its slot] (rows and
-// tile_start as k_tile_cols and k_tile_starts leave them). Nothing when the pairs exceed the capacity.
+// The scatter: the workgroup takes block blk (die-banded) of kFuseBlock splats, enumerates its (splat, super-tile)
+// pairs from the rectangles, and puts at list[sup_start[s] + rows[blk][num_tiles + s] + its slot] the pair's entry
+// (depth bits << 32) | (cover << 28) | splat, cover the four bits (2 dy + dx) of the super-tile's tiles the splat's
+// rectangle covers (rows and the starts as k_tile_cols and k_tile_starts leave them; n < 2^28). Nothing when the
+// pairs exceed the capacity.
+constexpr uint32_t kCoverShift = 28;
 __global__ __launch_bounds__(kFuseThreads) void k_tile_scatter(const uint4* __restrict__ rects,
-                                                               const uint32_t* __restrict__ counts, uint32_t n,
-                                                               uint32_t tiles_x, uint32_t num_tiles,
-                                                               uint64_t pairs_cap,
+                                                               const float* __restrict__ depths, uint32_t n,
+                                                               uint32_t tiles_x, uint32_t tiles_y, uint64_t pairs_cap,
                                                                const uint64_t* __restrict__ pairs_dev,
                                                                const uint32_t* __restrict__ rows,
-                                                               const uint32_t* __restrict__ tile_start,
-                                                               uint32_t* __restrict__ list) {
-  extern __shared__ uint32_t s_tile[];  // num_tiles counters
+                                                               const uint32_t* __restrict__ sup_start,
+                                                               uint64_t* __restrict__ list) {
+  extern __shared__ uint32_t s_tile[];  // a counter per super-tile
   __shared__ uint32_t s_off[kFuseBlock + 1], s_tx0[kFuseBlock], s_ty0[kFuseBlock], s_w[kFuseBlock];
+  __shared__ uint32_t s_rx[kFuseBlock], s_ry[kFuseBlock], s_dbits[kFuseBlock];  // tile rectangle (x0 | w << 16, ..)
   __shared__ uint32_t s_mark[4 * kFuseThreads];
   __shared__ uint32_t smem[kFuseThreads / kWave];
   const uint32_t tid = threadIdx.x;
+  const uint32_t sup_x = super_dim(tiles_x), num_tiles = tiles_x * tiles_y, num_sup = sup_x * super_dim(tiles_y);
   const uint32_t blk = die_band(blockIdx.x, gridDim.x);
   const uint32_t j0 = blk * kFuseBlock, i = j0 + tid;
-  const uint32_t* const row = rows + size_t(blk) * num_tiles;
-  for (uint32_t t = tid; t < num_tiles; t += kFuseThreads) s_tile[t] = tile_start[t] + row[t];
+  const uint32_t* const row = rows + size_t(blk) * (num_tiles + num_sup) + num_tiles;
+  for (uint32_t t = tid; t < num_sup; t += kFuseThreads) s_tile[t] = sup_start[t] + row[t];
   uint32_t c = 0;
-  uint4 r = make_uint4(0, 0, 1, 0);
+  uint32_t sx0 = 0, sy0 = 0, sw = 1;
+  uint4 r = make_uint4(0, 0, 0, 0);
   if (i < n) {
-    c = counts[i];
     r = rects[i];
+    if (r.z) {
+      sx0 = r.x / 2, sy0 = r.y / 2;
+      sw = (r.x + r.z - 1) / 2 - sx0 + 1;
+      c = sw * ((r.y + r.w - 1) / 2 - sy0 + 1);
+    }
   }
-  s_tx0[tid] = r.x;
-  s_ty0[tid] = r.y;
-  s_w[tid] = r.z ? r.z : 1u;
+  s_tx0[tid] = sx0;
+  s_ty0[tid] = sy0;
+  s_w[tid] = sw;
+  s_rx[tid] = r.x | (r.z << 16);  // tiles_x, tiles_y <= kFuseMaxTiles: 16 bits each
+  s_ry[tid] = r.y | (r.w << 16);
+  s_dbits[tid] = c ? __float_as_uint(depths[i]) : 0u;
   uint32_t total;
   s_off[tid] = block_exclusive_scan<uint32_t, kFuseThreads>(c, &total, smem);
   if (tid == 0) s_off[kFuseBlock] = total;
-  const uint32_t end = count_within(pairs_dev, pairs_cap) ? total : 0u;  // 0: nothing fits, nothing is written
+  const uint64_t cap = count_within(pairs_dev, pairs_cap);
+  const uint32_t end = cap ? total : 0u;  // 0: nothing fits, nothing is written
   __syncthreads();
-  for_each_pair(s_off, s_tx0, s_ty0, s_w, end, tiles_x, s_mark, smem,
-                [&](uint32_t q, uint32_t tile) { list[atomicAdd(&s_tile[tile], 1u)] = j0 + q; });
+  for_each_pair(s_off, s_tx0, s_ty0, s_w, end, s_mark, smem, [&](uint32_t q, uint32_t sy, uint32_t sx) {
+    const uint32_t rx = s_rx[q], ry = s_ry[q];
+    uint32_t cover = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < 4; ++j)
+      if (2 * sx + (j & 1u) - (rx & 0xFFFFu) < (rx >> 16) && 2 * sy + (j >> 1) - (ry & 0xFFFFu) < (ry >> 16))
+        cover |= 1u << j;
+    const uint32_t slot = atomicAdd(&s_tile[sy * sup_x + sx], 1u);
+    if (slot < cap)  // always, when the counts agree; keeps a stray write in bounds
+      list[slot] = (uint64_t(s_dbits[q]) << 32) | (cover << kCoverShift) | (j0 + q);
+  });
 }
 
-// Column scan of the [nblk][num_tiles] count table: each row becomes the block's exclusive offset within each
-// tile's pairs, and tile_total[tile] receives the column's sum. A workgroup takes kColTiles tiles; its kColParts
+// Column scan of the [nblk][num_tiles] count table (num_tiles: the row width, here tiles and super-tiles): each row
+// becomes the block's exclusive offset within each list, and tile_total[column] receives the column's sum. A workgroup takes kColTiles tiles; its kColParts
 // thread groups each sum a stretch of consecutive rows, then rewrite them starting from the sums of the stretches
 // before. The row loads of 64 consecutive tiles are 256-byte segments.
 __global__ __launch_bounds__(kColThreads) void k_tile_cols(uint32_t* __restrict__ rows, uint32_t nblk,
@@ -607,31 +670,37 @@ __global__ __launch_bounds__(kColThreads) void k_tile_cols(uint32_t* __restrict_
   }
 }
 
-// One workgroup: tile_start = the exclusive scan of tile_total (num_tiles <= kFuseMaxTiles, kStartPer consecutive
-// tiles per thread) and the ranges [start, start + total); every range empty when the pairs exceed the capacity.
-__global__ __launch_bounds__(kStartThreads) void k_tile_starts(const uint32_t* __restrict__ tile_total,
-                                                               uint32_t num_tiles, uint64_t pairs_cap,
+// One workgroup: start[0..num_tiles) = the exclusive scan of total[0..num_tiles) with the ranges [start, start +
+// total), and start[num_tiles..+num_sup) = the exclusive scan of the super-tiles' totals (each at most kFuseMaxTiles
+// entries, kStartPer consecutive ones per thread); every range empty when the pairs exceed the capacity.
+__global__ __launch_bounds__(kStartThreads) void k_tile_starts(const uint32_t* __restrict__ total, uint32_t num_tiles,
+                                                               uint32_t num_sup, uint64_t pairs_cap,
                                                                const uint64_t* __restrict__ pairs_dev,
-                                                               uint32_t* __restrict__ tile_start,
+                                                               uint32_t* __restrict__ start,
                                                                uint32_t* __restrict__ ranges) {
   __shared__ uint32_t smem[kStartThreads / kWave];
-  const uint32_t t0 = threadIdx.x * kStartPer;
   const bool fits = count_within(pairs_dev, pairs_cap) > 0;
-  uint32_t v[kStartPer], sum = 0;
+  for (uint32_t level = 0; level < 2; ++level) {
+    const uint32_t off = level ? num_tiles : 0u, count = level ? num_sup : num_tiles;
+    const uint32_t t0 = threadIdx.x * kStartPer;
+    uint32_t v[kStartPer], sum = 0;
 #pragma unroll
-  for (uint32_t i = 0; i < kStartPer; ++i) {
-    v[i] = fits && t0 + i < num_tiles ? tile_total[t0 + i] : 0u;
-    sum += v[i];
-  }
-  uint32_t run = block_exclusive_scan<uint32_t, kStartThreads>(sum, nullptr, smem);
-#pragma unroll
-  for (uint32_t i = 0; i < kStartPer; ++i)
-    if (t0 + i < num_tiles) {
-      tile_start[t0 + i] = run;
-      ranges[2 * (t0 + i)] = run;
-      ranges[2 * (t0 + i) + 1] = run + v[i];
-      run += v[i];
+    for (uint32_t i = 0; i < kStartPer; ++i) {
+      v[i] = fits && t0 + i < count ? total[off + t0 + i] : 0u;
+      sum += v[i];
     }
+    uint32_t run = block_exclusive_scan<uint32_t, kStartThreads>(sum, nullptr, smem);
+#pragma unroll
+    for (uint32_t i = 0; i < kStartPer; ++i)
+      if (t0 + i < count) {
+        start[off + t0 + i] = run;
+        if (!level) {
+          ranges[2 * (t0 + i)] = run;
+          ranges[2 * (t0 + i) + 1] = run + v[i];
+        }
+        run += v[i];
+      }
+  }
 }
 
 // Per-tile ranges from the sorted keys: the boundary between pairs i-1 and i (i in [0, P]) opens the ranges of
@@ -849,7 +918,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   const bool presort = ctx->bin_scheme == GSR_BIN_PRESORT || (ctx->bin_scheme == GSR_BIN_TILE_DEPTH && !tile_first);
   // The counting sort by tile replaces emission and the tile sort under the box rule when the per-tile counters fit
   // LDS.
-  const bool fused = tile_first && !ellipse && n && num_tiles <= kFuseMaxTiles;
+  const bool fused = tile_first && !ellipse && n && n < (1u << kCoverShift) && num_tiles <= kFuseMaxTiles;
   // Without a wait only once there is a count or a reservation to size the pair buffers from.
   const bool sync_free = ctx->bin_sync_free && n && (ctx->pair_hint > 0 || ctx->pair_reserved > 0);
 
@@ -890,28 +959,32 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
                                      (uint64_t(1) << 32) - 1)
                 : 0;
   const uint32_t nb_fuse = grid_for(n, kFuseBlock);
+  // the fused counting sort's lists: the tiles, then the super-tiles (2 x 2 tiles)
+  const uint32_t num_sup = super_dim(tiles_x) * super_dim(tiles_y);
+  const uint32_t lists = uint32_t(num_tiles) + num_sup;
   uint32_t* rows = nullptr;
-  uint32_t* tile_start = nullptr;
+  uint32_t* list_total = nullptr;
+  uint32_t* list_start = nullptr;
   if (fused) {
-    // the counting sort's count table, its column scan and the tile starts (with the ranges) need no pair count:
-    // they are queued before the wait for it
-    if ((st = grow(ctx, a.tile_rows, (size_t(nb_fuse) + 2) * num_tiles * 4))) return st;
+    // the counting sort's count table, its column scan and the list starts (with the tile ranges) need no pair
+    // count: they are queued before the wait for it
+    if ((st = grow(ctx, a.tile_rows, (size_t(nb_fuse) + 2) * lists * 4))) return st;
     rows = static_cast<uint32_t*>(a.tile_rows.ptr);
-    uint32_t* tile_total = rows + size_t(nb_fuse) * num_tiles;
-    tile_start = tile_total + num_tiles;
-    hipLaunchKernelGGL(k_prep_rows, dim3(nb_fuse), dim3(kFuseThreads), size_t(num_tiles) * 4, s, splats, depths, n,
-                       tiles_x, tiles_y, rects, counts, part, uint32_t(num_tiles), rows);
+    list_total = rows + size_t(nb_fuse) * lists;
+    list_start = list_total + lists;
+    hipLaunchKernelGGL(k_prep_rows, dim3(nb_fuse), dim3(kFuseThreads), size_t(lists) * 4, s, splats, depths, n,
+                       tiles_x, tiles_y, rects, counts, part, rows);
     hipLaunchKernelGGL(k_total, dim3(1), dim3(kThreads), 0, s, static_cast<const uint64_t*>(part), nb_fuse,
                        offsets + n, a.host_total_dev);
     e = hipEventRecord(a.total_ready, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "gsr_bin pair count readback");
     timing_mark(ctx, GSR_STAGE_TILE_SCAN, s, false);
-    hipLaunchKernelGGL(k_tile_cols, dim3(grid_for(num_tiles, kColTiles)), dim3(kColThreads), 0, s, rows, nb_fuse,
-                       uint32_t(num_tiles), tile_total);
-    hipLaunchKernelGGL(k_tile_starts, dim3(1), dim3(kStartThreads), 0, s, static_cast<const uint32_t*>(tile_total),
-                       uint32_t(num_tiles), sync_free ? capacity : ~uint64_t(0),
+    hipLaunchKernelGGL(k_tile_cols, dim3(grid_for(lists, kColTiles)), dim3(kColThreads), 0, s, rows, nb_fuse, lists,
+                       list_total);
+    hipLaunchKernelGGL(k_tile_starts, dim3(1), dim3(kStartThreads), 0, s, static_cast<const uint32_t*>(list_total),
+                       uint32_t(num_tiles), num_sup, sync_free ? capacity : ~uint64_t(0),
                        sync_free ? static_cast<const uint64_t*>(offsets + n) : static_cast<const uint64_t*>(nullptr),
-                       tile_start, static_cast<uint32_t*>(a.ranges.ptr));
+                       list_start, static_cast<uint32_t*>(a.ranges.ptr));
     timing_mark(ctx, GSR_STAGE_TILE_SCAN, s, true);
   } else if (n) {
     hipLaunchKernelGGL(k_prep, dim3(nb_prep), dim3(kThreads), 0, s, splats, depths, n, tiles_x, tiles_y, ellipse,
@@ -985,7 +1058,7 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
 
   for (int q = 0; q < 2; ++q)
     if ((st = grow(ctx, a.keys[q], size_t(P) * 8)) || (st = grow(ctx, a.vals[q], size_t(P) * 4))) return st;
-  if (tile_first && (st = grow(ctx, a.tile_scratch, size_t(P) * 8))) return st;
+  if (tile_first && !fused && (st = grow(ctx, a.tile_scratch, size_t(P) * 8))) return st;
   uint32_t* v0 = static_cast<uint32_t*>(a.vals[0].ptr);
   uint32_t* ranges = static_cast<uint32_t*>(a.ranges.ptr);
   const uint32_t tile_bits = bits_of(num_tiles - 1);
@@ -1019,14 +1092,17 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
                        static_cast<uint64_t*>(nullptr), ranges, idx_bits);
     sorted_v = v0;
   } else if (fused) {
-    // the counting sort's scatter (the count table and the starts are queued above), then each tile's list by
-    // (depth, splat) on chip (tile_depth.hip)
-    uint32_t* list = static_cast<uint32_t*>(a.vals[1].ptr);
+    // the counting sort's scatter into the super-tiles' lists (the count table and the starts are queued above; a
+    // super-tile's list is no longer than its tiles' lists together, so P entries hold them), then each super-tile
+    // sorts its list by (depth, splat) on chip and writes its tiles' lists (tile_depth.hip); the lists' 64-bit
+    // entries go in the scratch the other tile-first path uses for long lists
+    if ((st = grow(ctx, a.tile_scratch, size_t(P) * 8))) return st;
+    uint64_t* list = static_cast<uint64_t*>(a.tile_scratch.ptr);
     timing_mark(ctx, GSR_STAGE_TILE_SORT, s, false);
-    hipLaunchKernelGGL(k_tile_scatter, dim3(nb_fuse), dim3(kFuseThreads), size_t(num_tiles) * 4, s,
-                       static_cast<const uint4*>(rects), static_cast<const uint32_t*>(counts), n, tiles_x,
-                       uint32_t(num_tiles), P, pairs_dev, static_cast<const uint32_t*>(rows),
-                       static_cast<const uint32_t*>(tile_start), list);
+    hipLaunchKernelGGL(k_tile_scatter, dim3(nb_fuse), dim3(kFuseThreads), size_t(num_sup) * 4, s,
+                       static_cast<const uint4*>(rects), depths, n, tiles_x, tiles_y, P, pairs_dev,
+                       static_cast<const uint32_t*>(rows), static_cast<const uint32_t*>(list_start + num_tiles),
+                       list);
     timing_mark(ctx, GSR_STAGE_TILE_SORT, s, true);
     if (ctx->bin_keys) {
       if ((st = grow(ctx, a.order_alt, std::max<size_t>(size_t(n) * 8, size_t(P) * 8)))) return st;
@@ -1035,9 +1111,8 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
     uint32_t* k0 = static_cast<uint32_t*>(a.keys[0].ptr);
     uint32_t* k1 = static_cast<uint32_t*>(a.keys[1].ptr);
     timing_mark(ctx, GSR_STAGE_TILE_DEPTH, s, false);
-    launch_tile_depth(s, static_cast<const uint32_t*>(nullptr), list, 32u, false, ranges, P, pairs_dev,
-                      uint32_t(num_tiles), depths, n, v0, final_k, static_cast<uint64_t*>(a.tile_scratch.ptr), k0,
-                      k0 + P, k1, k1 + P);
+    launch_super_order(s, list, list_start + num_tiles, list_total + num_tiles, num_sup, tiles_x, tiles_y, ranges, P,
+                       pairs_dev, depths, n, v0, final_k, k0, k0 + P, k1, k1 + P);
     timing_mark(ctx, GSR_STAGE_TILE_DEPTH, s, true);
     sorted_v = v0;
   } else if (tile_first) {

@@ -159,6 +159,19 @@ void launch_tile_depth(hipStream_t s, const uint32_t* list, const uint32_t* list
                        uint64_t* gent, uint32_t* gk0, uint32_t* gk1, uint32_t* gp0, uint32_t* gp1);
 uint32_t tile_depth_capacity();
 
+// Per-super-tile order of the fused counting sort (tile_depth.hip): one workgroup per super-tile (2 x 2 tiles,
+// row-major over a grid of ceil(tiles_x / 2) columns) sorts its list list[sup_start .. + sup_total) (clamped to the
+// pair count) of entries (depth bits << 32) | (cover << 28) | splat, in any order, by (depth bits, splat) and writes
+// each of its tiles' lists from the tile's start (ranges) on: vals_out = the splats, keys_out (if not null) =
+// (tile << 32) | depth bits. Cover bit 2 dy + dx says the splat belongs to tile (dx, dy) of the super-tile. Lists
+// longer than LDS holds, or with many equal depths, are sorted through gk0, gk1, gp0, gp1 (32-bit pair-count
+// arrays, each super-tile using its own stretch).
+void launch_super_order(hipStream_t s, const uint64_t* list, const uint32_t* sup_start, const uint32_t* sup_total,
+                        uint32_t num_sup, uint32_t tiles_x, uint32_t tiles_y, const uint32_t* ranges,
+                        uint64_t pairs_cap, const uint64_t* pairs_dev, const float* depths, uint32_t n,
+                        uint32_t* vals_out, uint64_t* keys_out, uint32_t* gk0, uint32_t* gk1, uint32_t* gp0,
+                        uint32_t* gp1);
+
 // The same sort of 32-bit tile ids whose last pass also writes keys_final[g] = (key << 32) | bits(depths[val]) for
 // every output position g (values below n_depths; others get depth bits 0). Requires key_bits > 0.
 gsr_status radix_sort_tiles_final(gsr_ctx* ctx, hipStream_t s, const uint32_t* keys_in, const uint32_t* vals_in,

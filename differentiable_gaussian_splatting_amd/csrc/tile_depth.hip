@@ -365,6 +365,171 @@ __global__ __launch_bounds__(kThreads) void k_tile_depth(GSR_TILE_DEPTH_PARAMS) 
   }
 }
 
+// ---------------------------------------------------------------------------------------------------------------
+// Per-super-tile order (the fused counting sort's second level). A super-tile is a square of 2 x 2 tiles; its list
+// holds an entry (depth bits << 32) | (cover << 28) | splat for every splat whose tile rectangle meets it, in no
+// particular order, cover being the four bits (2 dy + dx) of the tiles the rectangle covers. One workgroup sorts
+// the list by (depth bits, splat) once - buckets in LDS as above, or the radix sort through the arena for lists
+// longer than kSupCap or with a crowded bucket - and then writes each of its tiles' lists by a stable filter of that
+// order: an entry goes to tile j when its cover bit j is set. The cover bits follow the rule by which the tiles'
+// totals (and so the ranges) were counted, so each tile's list comes out whole and in (depth bits, splat) order.
+constexpr uint32_t kSupCap = 4608;      // the longest super-tile list sorted in LDS (46 KB per workgroup)
+constexpr uint32_t kSupBuckets = 2048;  // the most buckets of a list sorted in LDS
+constexpr uint32_t kSupItems = (kSupCap + kThreads - 1) / kThreads;
+constexpr uint32_t kCover = 28;         // the cover bits' place in an entry's low word
+constexpr uint64_t kSortBits = ~(uint64_t(0xFu) << kCover);  // an entry's (depth bits, splat)
+static_assert(kSupBuckets % kThreads == 0 && kSupBuckets <= kMaxBuckets, "super-tile bucket counts");
+
+struct SuperShared {
+  union {
+    SortShared sh;  // the radix sort's counts
+    struct {
+      uint32_t start[kSupBuckets + 1];  // bucket counts, then their exclusive scan; start[nb] = m
+      uint64_t entry[kSupCap];          // the entries grouped by bucket, then in sorted order
+      uint32_t wmin[kWaves], wmax[kWaves], wsum[kWaves];
+    } bkt;
+  } u;
+  uint32_t wtot[2][kWaves][4];  // the filter's per-wave counts per tile, double-buffered
+};
+
+#define GSR_SUPER_ORDER_PARAMS                                                                                    \
+  const uint64_t *__restrict__ list, const uint32_t *__restrict__ sup_start, const uint32_t *__restrict__ sup_total, \
+      uint32_t tiles_x, uint32_t tiles_y, const uint32_t *__restrict__ ranges, uint64_t pairs_cap,                 \
+      const uint64_t *__restrict__ pairs_dev, const float *__restrict__ depths, uint32_t n,                         \
+      uint32_t *__restrict__ vals_out, uint64_t *__restrict__ keys_out, uint32_t *gk0, uint32_t *gk1, uint32_t *gp0, \
+      uint32_t *gp1
+
+// Three workgroups per compute unit (LDS 46 KB each): six waves per SIMD, 80 registers.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) void k_super_order(
+    GSR_SUPER_ORDER_PARAMS) {
+  __shared__ SuperShared ts;
+  const uint64_t P = count_within(pairs_dev, pairs_cap);  // 0 when the pairs did not fit: nothing is written
+  const uint32_t sup = blockIdx.x, sup_x = (tiles_x + 1) / 2;
+  const uint32_t st = uint32_t(min<uint64_t>(sup_start[sup], P));
+  const uint32_t m = uint32_t(min<uint64_t>(sup_total[sup], P - st));
+  if (m == 0) return;
+  const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const uint32_t bx = (sup % sup_x) * 2, by = (sup / sup_x) * 2;
+  uint32_t tile[4], base[4];  // the four tiles and their lists' starts (uniform: held in scalar registers)
+#pragma unroll
+  for (uint32_t j = 0; j < 4; ++j) {
+    const uint32_t tx = bx + (j & 1u), ty = by + (j >> 1);
+    tile[j] = tx < tiles_x && ty < tiles_y ? ty * tiles_x + tx : 0u;
+    base[j] = __builtin_amdgcn_readfirstlane(tx < tiles_x && ty < tiles_y ? ranges[2 * tile[j]] : 0u);
+  }
+  const uint64_t* const lst = list + st;
+  auto splat_at = [&](uint32_t e) -> uint32_t { return uint32_t(lst[e]) & ((1u << kCover) - 1u); };
+  auto depth_bits = [&](uint32_t splat) -> uint32_t { return splat < n ? __float_as_uint(depths[splat]) : 0u; };
+
+  bool in_lds = false;
+  if (m <= kSupCap) {
+    uint64_t x[kSupItems];
+    uint32_t slot[kSupItems];
+    uint32_t kmin = ~0u, kmax = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < kSupItems; ++i) {  // every load in flight at once (positions past m read entry 0)
+      const uint32_t e = tid + i * kThreads;
+      x[i] = lst[e < m ? e : 0u];
+    }
+#pragma unroll
+    for (uint32_t i = 0; i < kSupItems; ++i)
+      if (tid + i * kThreads < m) kmin = min(kmin, uint32_t(x[i] >> 32)), kmax = max(kmax, uint32_t(x[i] >> 32));
+    const uint32_t half = (m + 1) / 2;
+    const uint32_t nb = min(kSupBuckets, max(kMinBuckets, half > 1 ? 1u << (32 - __clz(int(half - 1))) : 1u));
+    for (uint32_t j = tid; j <= nb; j += kThreads) ts.u.bkt.start[j] = 0;
+    kmin = wave_min(kmin);
+    kmax = wave_max(kmax);
+    if (lane == 0) ts.u.bkt.wmin[w] = kmin, ts.u.bkt.wmax[w] = kmax;
+    __syncthreads();
+    uint32_t lo = ts.u.bkt.wmin[0], hi = ts.u.bkt.wmax[0];
+#pragma unroll
+    for (uint32_t q = 1; q < kWaves; ++q) lo = min(lo, ts.u.bkt.wmin[q]), hi = max(hi, ts.u.bkt.wmax[q]);
+    const float scale = float(nb) / (float(hi - lo) + 1.0f);
+#pragma unroll
+    for (uint32_t i = 0; i < kSupItems; ++i)
+      if (tid + i * kThreads < m) slot[i] = atomicAdd(&ts.u.bkt.start[bucket_of(uint32_t(x[i] >> 32), lo, scale, nb)], 1u);
+    __syncthreads();
+    const uint32_t biggest = scan_buckets(ts.u.bkt.start, nb, m, ts.u.bkt.wsum);
+    in_lds = !__syncthreads_or(biggest > kBucketLimit);
+    if (in_lds) {
+#pragma unroll
+      for (uint32_t i = 0; i < kSupItems; ++i)
+        if (tid + i * kThreads < m)
+          ts.u.bkt.entry[ts.u.bkt.start[bucket_of(uint32_t(x[i] >> 32), lo, scale, nb)] + slot[i]] = x[i];
+      __syncthreads();
+      // each entry's rank among the (depth bits, splat) of its bucket, then the entries moved to their ranks (the
+      // barrier between ends every read)
+#pragma unroll
+      for (uint32_t i = 0; i < kSupItems; ++i) {
+        const uint32_t q = tid + i * kThreads;
+        slot[i] = ~0u;
+        if (q < m) {
+          x[i] = ts.u.bkt.entry[q];
+          const uint64_t me = x[i] & kSortBits;
+          const uint32_t b = bucket_of(uint32_t(me >> 32), lo, scale, nb);
+          const uint32_t b0 = ts.u.bkt.start[b], b1 = ts.u.bkt.start[b + 1];
+          uint32_t r = b0;
+          for (uint32_t f = b0; f < b1; ++f) r += (ts.u.bkt.entry[f] & kSortBits) < me ? 1u : 0u;
+          slot[i] = r;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (uint32_t i = 0; i < kSupItems; ++i)
+        if (slot[i] != ~0u) ts.u.bkt.entry[slot[i]] = x[i];
+      __syncthreads();
+    }
+  }
+  // otherwise the radix sort through the arena (a barrier above ends every read of the bucket layout)
+  const uint32_t* kr = nullptr;
+  const uint32_t* pr = nullptr;
+  if (!in_lds) {
+    uint32_t *k0 = gk0 + st, *k1 = gk1 + st, *p0 = gp0 + st, *p1 = gp1 + st;
+    const uint32_t res = radix_order(k0, k1, p0, p1, m, false, splat_at, depth_bits, ts.u.sh);
+    kr = res ? k1 : k0;
+    pr = res ? p1 : p0;
+  }
+  // The stable filter: the e-th entry of the sorted list goes to the tiles its cover bits name. Steps of kThreads
+  // consecutive entries, one per thread: per tile, a ballot gives each entry its place among its wave's entries of
+  // that tile, the per-wave totals (double-buffered in LDS, one barrier per step) its wave's place, so the entries of
+  // a tile leave each wave as one contiguous run of stores.
+  uint32_t carry[4] = {0u, 0u, 0u, 0u};
+  for (uint32_t c0 = 0, step = 0; c0 < m; c0 += kThreads, step ^= 1u) {
+    const uint32_t e = c0 + tid;
+    uint64_t x = 0;
+    if (e < m) x = in_lds ? ts.u.bkt.entry[e] : (uint64_t(kr[e]) << 32) | uint32_t(lst[pr[e]]);
+    const uint32_t spl = uint32_t(x) & ((1u << kCover) - 1u), key = uint32_t(x >> 32), mk = uint32_t(x) >> kCover;
+    uint32_t below[4];
+#pragma unroll
+    for (uint32_t j = 0; j < 4; ++j) {
+      const uint64_t bal = __builtin_amdgcn_ballot_w64((mk >> j) & 1u);
+      below[j] = uint32_t(__popcll(bal & lanemask_lt(lane)));
+      if (lane == 0) ts.wtot[step][w][j] = uint32_t(__popcll(bal));
+    }
+    __syncthreads();
+#pragma unroll
+    for (uint32_t j = 0; j < 4; ++j) {
+      uint32_t before = 0, all = 0;
+#pragma unroll
+      for (uint32_t q = 0; q < kWaves; ++q) {
+        const uint32_t c = ts.wtot[step][q][j];
+        before += q < w ? c : 0u;
+        all += c;
+      }
+      if ((mk >> j) & 1u) {
+        const uint64_t o = uint64_t(base[j]) + carry[j] + before + below[j];
+        // plain stores: a wave's run shares cache lines with the neighbouring waves' runs, which L2 merges
+        // (non-temporal stores of these partial lines measured 43 against 35 us at 410k splats)
+        if (o < P) {  // always, when the tiles' totals and the cover bits agree; keeps a stray write in bounds
+          vals_out[o] = spl;
+          if (keys_out) keys_out[o] = (uint64_t(tile[j]) << 32) | key;
+        }
+      }
+      carry[j] = __builtin_amdgcn_readfirstlane(carry[j] + all);
+    }
+  }
+}
+
 }  // namespace
 
 void launch_tile_depth(hipStream_t s, const uint32_t* list, const uint32_t* list_vals, uint32_t idx_bits,
@@ -384,5 +549,15 @@ void launch_tile_depth(hipStream_t s, const uint32_t* list, const uint32_t* list
 }
 
 uint32_t tile_depth_capacity() { return kCap; }
+
+void launch_super_order(hipStream_t s, const uint64_t* list, const uint32_t* sup_start, const uint32_t* sup_total,
+                        uint32_t num_sup, uint32_t tiles_x, uint32_t tiles_y, const uint32_t* ranges,
+                        uint64_t pairs_cap, const uint64_t* pairs_dev, const float* depths, uint32_t n,
+                        uint32_t* vals_out, uint64_t* keys_out, uint32_t* gk0, uint32_t* gk1, uint32_t* gp0,
+                        uint32_t* gp1) {
+  if (num_sup)
+    hipLaunchKernelGGL(k_super_order, dim3(num_sup), dim3(kThreads), 0, s, list, sup_start, sup_total, tiles_x,
+                       tiles_y, ranges, pairs_cap, pairs_dev, depths, n, vals_out, keys_out, gk0, gk1, gp0, gp1);
+}
 
 }  // namespace gsr

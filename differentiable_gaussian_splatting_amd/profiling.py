@@ -46,6 +46,7 @@ KERNEL_SOURCES = {
     "k_tile_starts": ["bin.hip", "scan_common.hpp", "gsr_internal.hpp"],
     "k_tile_scatter": ["bin.hip", "scan_common.hpp", "gsr_internal.hpp"],
     "k_tile_depth": ["tile_depth.hip", "scan_common.hpp", "gsr_internal.hpp"],
+    "k_super_order": ["tile_depth.hip", "scan_common.hpp", "gsr_internal.hpp"],
 }
 # bench.py stage -> the kernel instance its default configuration launches (template arguments as rocprofv3
 # prints them: the raster kernels with the skips on, the exact forward exponential, the dense Adam)
@@ -70,7 +71,7 @@ def sort_kernels(passes: dict) -> tuple:
 
 # the tile-first scheme's sort under the box rule: the count table's column scan, the tile starts, the scatter and
 # the per-tile order, one launch each
-TILE_FIRST_SORT_KERNELS = ("k_tile_cols", "k_tile_starts", "k_tile_scatter", "k_tile_depth<false>")
+TILE_FIRST_SORT_KERNELS = ("k_tile_cols", "k_tile_starts", "k_tile_scatter", "k_super_order")
 
 CALIB_BYTES = 256 * 1024 * 1024  # read and written by each copy of bench.py --calib-copy
 TRAFFIC_BEGIN, TRAFFIC_END = "<!-- traffic-json", "traffic-json -->"

@@ -65,12 +65,14 @@ gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats);
 #define GSR_BIN_PRESORT 0    /*   radix-sort splats by depth, emit pairs in that order, then a stable radix sort  */
                              /*   of the pairs by tile id only                                                    */
 #define GSR_BIN_KEY64 1      /*   emit pairs splat by splat and radix-sort the full 64-bit keys                   */
-#define GSR_BIN_TILE_DEPTH 2 /*   default: put the pairs in tile order first (under the box rule with at most     */
-                             /*   8192 tiles a counting sort by tile fused with their enumeration, else emission  */
-                             /*   in splat order and a radix sort by tile id), then order each tile's list by     */
-                             /*   (depth, splat) in one workgroup (on chip up to 3456 pairs, through the arena    */
-                             /*   beyond); when the last pair count seen averages more than 3072 pairs per tile,  */
-                             /*   a call runs the presort scheme instead                                          */
+#define GSR_BIN_TILE_DEPTH 2 /*   default: tile order first, then each list by (depth, splat) in one workgroup.   */
+                             /*   Under the box rule with at most 8192 tiles and fewer than 2^28 splats, a        */
+                             /*   counting sort into the lists of 2x2-tile super-tiles, each of which is sorted   */
+                             /*   once (on chip up to 4608 entries) and filtered into its four tiles' lists;      */
+                             /*   otherwise emission in splat order, a radix sort by tile id and a sort of each   */
+                             /*   tile's list (on chip up to 3456 pairs); longer lists go through the arena. When */
+                             /*   the last pair count seen averages more than 3072 pairs per tile, a call runs    */
+                             /*   the presort scheme instead                                                      */
 #define GSR_OPT_BIN_KEYS 2   /* 1 (default): gsr_bin materialises the sorted 64-bit keys; 0: keys = NULL          */
 #define GSR_OPT_RASTER_SKIP 3 /* 1 (default): the raster kernels skip work that provably changes nothing - splats   */
                               /*   that cannot reach alpha >= 1/255 in a wavefront's 8x8 block, and, in the        */
@@ -142,10 +144,11 @@ gsr_status gsr_set_option(gsr_ctx* ctx, int32_t option, int64_t value);
 #define GSR_STAGE_LOSS 6             /* both passes of the L1 + SSIM loss                                        */
 #define GSR_STAGE_DEPTH_SORT 7       /* inside gsr_bin: the radix sort of the splats by depth (presort scheme)   */
 #define GSR_STAGE_TILE_SORT 8        /* inside gsr_bin: the radix sort of the pairs (by tile, or by the 64-bit   */
-                                     /*   key with GSR_BIN_KEY64)                                                */
-#define GSR_STAGE_TILE_DEPTH 9       /* inside gsr_bin: the per-tile depth order (tile-first scheme)            */
-#define GSR_STAGE_TILE_SCAN 10       /* inside gsr_bin: the column scan and tile starts of the tile-first scheme's */
-                                     /*   counting sort (its scatter is GSR_STAGE_TILE_SORT)                      */
+                                     /*   key with GSR_BIN_KEY64), or the counting sort's scatter to super-tiles */
+#define GSR_STAGE_TILE_DEPTH 9       /* inside gsr_bin: the per-tile (or per-super-tile) depth order of the      */
+                                     /*   tile-first scheme                                                      */
+#define GSR_STAGE_TILE_SCAN 10       /* inside gsr_bin: the column scan and list starts of the tile-first        */
+                                     /*   scheme's counting sort (its scatter is GSR_STAGE_TILE_SORT)            */
 #define GSR_NUM_STAGES 11
 
 /* GPU durations in milliseconds of the recorded launches of `stage`, oldest first: the last min(recorded, ring

@@ -277,12 +277,15 @@ def test_tile_first_fused_tile_limit(ctx, w, h):
     assert_bins_equal(ctx, sc.splats, sc.depths, w, h, "tile_depth")
 
 
-@pytest.mark.parametrize("m", [1, 2, 3456, 3457])
-def test_tile_depth_list_length_edges(ctx, m):
-    """One tile holding exactly m pairs: a single entry, two, the on-chip capacity (3456) and one more (the arena
-    path). Splats of 0.3-1 px inside the tile's inner 8 x 8 pixels, so each covers that tile only; a third of them
-    share depths, so ties are ordered by splat index."""
-    banner(f"bin tile-depth list length m={m}")
+@pytest.mark.parametrize("rule,m", [("box", 1), ("box", 2), ("box", 4608), ("box", 4609), ("ellipse", 1),
+                                    ("ellipse", 2), ("ellipse", 3456), ("ellipse", 3457)])
+def test_tile_depth_list_length_edges(ctx, rule, m):
+    """One tile holding exactly m pairs: a single entry, two, the on-chip capacity and one more (the arena path).
+    Under the box rule the counting sort's super-tile (here the one tile, its three other tiles off the grid) orders
+    up to 4608 entries on chip; under the ellipse rule each tile's list is ordered on its own, up to 3456 on chip.
+    Splats of 0.3-1 px inside the tile's inner 8 x 8 pixels, so each covers that tile only; a third of them share
+    depths, so ties are ordered by splat index."""
+    banner(f"bin tile-depth list length rule={rule} m={m}")
     rng = np.random.default_rng(m)
     s = rng.uniform(0.3, 1.0, m)
     sp = np.zeros((m, 9), np.float32)
@@ -293,11 +296,12 @@ def test_tile_depth_list_length_edges(ctx, m):
     depths = rng.uniform(0.1, 10.0, m).astype(np.float32)
     depths[: m // 3] = depths[m - m // 3:]
     import oracle
-    ref = oracle.bin(sp, depths, 16, 16)
+    ref = oracle.bin(sp, depths, 16, 16, rule=rule)
     assert ref.num_pairs == m
     from differentiable_gaussian_splatting_amd import gsr
     c = gsr.Context(0)  # a fresh context: the tile-first path on the first call
     try:
+        set_rule(c, rule)
         assert_bins_equal(c, sp, depths, 16, 16, "tile_depth", ref)
     finally:
         c.close()
