@@ -369,7 +369,8 @@ __global__ __launch_bounds__(kThreads) void k_tile_depth(GSR_TILE_DEPTH_PARAMS) 
 // Per-super-tile order (the fused counting sort's second level). A super-tile is a square of 2 x 2 tiles; its list
 // holds an entry (depth bits << 32) | (cover << 28) | splat for every splat whose tile rectangle meets it, in no
 // particular order, cover being the four bits (2 dy + dx) of the tiles the rectangle covers. One workgroup sorts
-// the list by (depth bits, splat) once - buckets in LDS as above, or the radix sort through the arena for lists
+// the list by (depth bits, splat) once - buckets in LDS as above (linear in the depth value rather than in its
+// bits), or the radix sort through the arena for lists
 // longer than kSupCap or with a crowded bucket - and then writes each of its tiles' lists by a stable filter of that
 // order: an entry goes to tile j when its cover bit j is set. The cover bits follow the rule by which the tiles'
 // totals (and so the ranges) were counted, so each tile's list comes out whole and in (depth bits, splat) order.
@@ -444,7 +445,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) v
     uint32_t lo = ts.u.bkt.wmin[0], hi = ts.u.bkt.wmax[0];
 #pragma unroll
     for (uint32_t q = 1; q < kWaves; ++q) lo = min(lo, ts.u.bkt.wmin[q]), hi = max(hi, ts.u.bkt.wmax[q]);
-    const float scale = float(nb) / (float(hi - lo) + 1.0f);
+    // buckets linear in the depth value between the list's extremes (monotone: fp32 subtraction, scaling by a
+    // positive factor and truncation all preserve order), which spreads the workloads' uniform depths evenly; the
+    // per-tile order's map, linear in the bits, crowds the top of a wide range (33 against 35 us at 410k splats)
+    const float lov = __uint_as_float(lo);
+    const float scale = float(nb) / fmaxf(__uint_as_float(hi) - lov, 1e-30f);
+    auto bucket_of = [&](uint32_t key, uint32_t, float, uint32_t) {
+      return min(nb - 1, uint32_t((__uint_as_float(key) - lov) * scale));
+    };
 #pragma unroll
     for (uint32_t i = 0; i < kSupItems; ++i)
       if (tid + i * kThreads < m) slot[i] = atomicAdd(&ts.u.bkt.start[bucket_of(uint32_t(x[i] >> 32), lo, scale, nb)], 1u);
