@@ -1,9 +1,10 @@
-// Per-tile depth order for the tile-first binning scheme (GSR_BIN_TILE_DEPTH): the pairs have been emitted splat by
-// splat (ascending splat index) and sorted stably by tile id alone, so each tile's list holds its splats in index
-// order; one workgroup per tile then puts that list in (depth bits, splat index) order - the order of the 64-bit
-// keys (tile << 32) | depth bits sorted stably, ties in depth keeping splat order. [C0 resident arena + C1 pass skip
-// page, section 2 table, rows "C0" and "C1": the keys and their stable sort; the constant-digit pass skip is applied
-// per tile]
+// Depth order within tiles for the tile-first binning scheme (GSR_BIN_TILE_DEPTH): the order of the 64-bit keys
+// (tile << 32) | depth bits sorted stably, ties in depth keeping splat order. [C0 resident arena + C1 pass skip page,
+// section 2 table, rows "C0" and "C1": the keys and their stable sort; the constant-digit pass skip is applied per
+// list] Two forms. The per-tile order: the pairs have been put in tile order (emitted splat by splat and sorted
+// stably by tile id, or by a counting sort), and one workgroup per tile puts the tile's list in (depth bits, splat
+// index) order. The per-super-tile order (below): the counting sort filled the lists of squares of 2 x 2 tiles,
+// and one workgroup per square sorts its list once and filters it into its four tiles' lists.
 //
 // Lists of at most kCap entries are sorted in LDS by buckets: the pair (depth bits, splat) is unique within a tile
 // (a splat covers a tile once), so the sort needs no stability. Each entry goes to one of nb buckets (nb = the
