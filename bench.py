@@ -552,15 +552,15 @@ def sort_roofline(args, N, P, W, H, kernel_ms, Ps=None):
 
 
 def bench_bin_stress(args, ctx, gsr, scenes, torch, np):
-    """The binning on its own on the 1M-splat stress scene (about 26M pairs under the box rule), under the presort
-    and 64-bit key schemes (the tile-first default averages more than 3072 pairs per tile here, so after its first
-    call it runs the presort scheme), timed with the library's events over K calls per repeat (median of the
-    repeats' means). Sort
-    rooflines on algorithmic bytes:
+    """The binning on its own on the 1M-splat stress scene (about 26M pairs under the box rule), under the tile-first
+    default and the presort and 64-bit key schemes, timed with the library's events over K calls per repeat (median
+    of the repeats' means). Sort rooflines on algorithmic bytes:
+      tile_depth (the default): as sort_roofline's two-level form (the super-tile lists, about 15,000 entries each
+        here, are ordered in chunks on chip);
       key64 (the pages' scheme): a stable LSD sort of the 64-bit (tile | depth) keys with their 32-bit values over
         d = ceil((tile bits + 32) / 8) passes, P (8 + 24 d) bytes: one read of the keys for the digit histograms and
         a read and a write of key and value per pass;
-      presort (the default): the depth sort of the n 32-bit depth keys with their indices (4 passes, 20 B per key
+      presort: the depth sort of the n 32-bit depth keys with their indices (4 passes, 20 B per key
         per pass) and the tile sort of the pairs by their tile id (per pass 12 B per pair on packed 32-bit words;
         the last one adds the 4 B value, the 8 B 64-bit key and the 4 B depth gather)."""
     sc = scenes.make_scene("bin1m")
@@ -569,26 +569,33 @@ def bench_bin_stress(args, ctx, gsr, scenes, torch, np):
     tiles = ((W + 15) // 16) * ((H + 15) // 16)
     tile_bits = int(tiles - 1).bit_length()
     out = {"workload": f"bin1m: {W}x{H} image, {N} splats ({scene_label(sc.spec)}), box rule"}
-    for scheme, opt in (("presort", gsr.GSR_BIN_PRESORT), ("key64", gsr.GSR_BIN_KEY64)):
+    for scheme, opt in (("tile_depth", gsr.GSR_BIN_TILE_DEPTH), ("presort", gsr.GSR_BIN_PRESORT),
+                        ("key64", gsr.GSR_BIN_KEY64)):
         gsr.gsr_set_option(ctx, gsr.GSR_OPT_BIN_SCHEME, opt)
         b = gsr.gsr_bin(ctx, sp, dp, W, H)
         P = b.num_pairs
         gsr.gsr_reserve(ctx, P, N)
         for _ in range(3):
             gsr.gsr_bin(ctx, sp, dp, W, H)
-        reps = {"bin": [], "depth_sort": [], "tile_sort": []}
+        reps = {"bin": [], "depth_sort": [], "tile_sort": [], "tile_scan": [], "tile_depth": []}
         for _ in range(args.repeats):
             gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, args.steps)
             for _ in range(args.steps):
-                gsr.gsr_bin(ctx, sp, dp, W, H)
+                b = gsr.gsr_bin(ctx, sp, dp, W, H)
             torch.cuda.synchronize()
             for nm, stg in (("bin", gsr.GSR_STAGE_BIN), ("depth_sort", gsr.GSR_STAGE_DEPTH_SORT),
-                            ("tile_sort", gsr.GSR_STAGE_TILE_SORT)):
+                            ("tile_sort", gsr.GSR_STAGE_TILE_SORT), ("tile_scan", gsr.GSR_STAGE_TILE_SCAN),
+                            ("tile_depth", gsr.GSR_STAGE_TILE_DEPTH)):
                 t = gsr.gsr_kernel_times(ctx, stg)
                 reps[nm].append(float(np.mean(t)) if t else 0.0)
             gsr.gsr_set_option(ctx, gsr.GSR_OPT_KERNEL_TIMING, 0)
         ms = {nm: float(np.median(v)) for nm, v in reps.items()}
-        if scheme == "key64":
+        if scheme == "tile_depth":
+            keys, vals, _ = gsr.gsr_bins_copy(ctx, b)
+            Ps = super_pairs(keys.cpu().numpy().view(np.uint64), vals.cpu().numpy().view(np.uint32), W)
+            roof = sort_roofline(argparse.Namespace(bin_scheme="tile_depth"), N, P, W, H, ms, Ps)
+            by, sort_ms, note = roof["work_per_launch"], roof["kernel_ms"], roof["bytes"]
+        elif scheme == "key64":
             d = (tile_bits + 32 + 7) // 8
             by = P * (8 + 24 * d)
             sort_ms = ms["tile_sort"]
@@ -604,14 +611,17 @@ def bench_bin_stress(args, ctx, gsr, scenes, torch, np):
         # HBM bytes per bin from the committed counter record of this leg (copy-calibrated), or null
         from differentiable_gaussian_splatting_amd import profiling
         md = os.path.join(ROOT, "profiles", "hbm_counters_bin1m.md")
-        if scheme == "key64":
+        if scheme == "tile_depth":
+            kern = profiling.TILE_FIRST_SORT_KERNELS
+        elif scheme == "key64":
             d = (tile_bits + 32 + 7) // 8
             kern = ("k_upsweep<uint64,16u,8u>", "k_scan_rows", "k_scatter<uint64,16u,8u,false,false>") * d
         else:
             kern = profiling.sort_kernels({"depth": 4, "tile": (tile_bits + 5) // 6})
         traffic = profiling.traffic_for(kern, md)
         out[scheme] = {"pairs": P, "bin_ms": ms["bin"], "depth_sort_ms": ms["depth_sort"],
-                       "tile_sort_ms": ms["tile_sort"], "sigma": {nm: float(np.std(v)) for nm, v in reps.items()},
+                       "tile_sort_ms": ms["tile_sort"], "tile_scan_ms": ms["tile_scan"],
+                       "tile_depth_ms": ms["tile_depth"], "sigma": {nm: float(np.std(v)) for nm, v in reps.items()},
                        "sort_roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                          "frac": ach / HBM_PEAK_GBS, "work_per_launch": by, "kernel_ms": sort_ms,
                                          "bytes": note, "traffic": traffic}}

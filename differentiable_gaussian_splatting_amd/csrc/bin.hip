@@ -910,15 +910,16 @@ extern "C" gsr_status gsr_bin(gsr_ctx* ctx, void* stream, const float* splats, c
   // An earlier call's pair count that has arrived in the meantime raises the capacity hint (before this call's
   // launch overwrites the pinned word).
   if (ctx->pairs_pending && hipEventQuery(a.total_ready) == hipSuccess) note_pair_count(ctx);
-  // The tile-first scheme sorts each tile's list on chip; when the last count seen puts the average list beyond
-  // kTileFirstAvg pairs (most lists would exceed the on-chip capacity) the presort scheme takes the call instead.
-  // Both give the same bins bit for bit; the choice is only about speed.
+  // The tile-first scheme's two-level counting sort (box rule, the per-tile and per-super-tile counters fit LDS,
+  // splat indices below the cover bits) orders long lists in chunks on chip. Its other form sorts each tile's list
+  // on chip and longer ones through the arena; there, when the last count seen puts the average list beyond
+  // kTileFirstAvg pairs, the presort scheme takes the call instead. All give the same bins bit for bit; the choice
+  // is only about speed.
+  const bool fusable = !ellipse && n && n < (1u << kCoverShift) && num_tiles <= kFuseMaxTiles;
   const bool tile_first = ctx->bin_scheme == GSR_BIN_TILE_DEPTH &&
-                          ctx->last_pairs <= uint64_t(kTileFirstAvg) * num_tiles;
+                          (fusable || ctx->last_pairs <= uint64_t(kTileFirstAvg) * num_tiles);
   const bool presort = ctx->bin_scheme == GSR_BIN_PRESORT || (ctx->bin_scheme == GSR_BIN_TILE_DEPTH && !tile_first);
-  // The counting sort by tile replaces emission and the tile sort under the box rule when the per-tile counters fit
-  // LDS.
-  const bool fused = tile_first && !ellipse && n && n < (1u << kCoverShift) && num_tiles <= kFuseMaxTiles;
+  const bool fused = tile_first && fusable;
   // Without a wait only once there is a count or a reservation to size the pair buffers from.
   const bool sync_free = ctx->bin_sync_free && n && (ctx->pair_hint > 0 || ctx->pair_reserved > 0);
 

@@ -164,9 +164,10 @@ uint32_t tile_depth_capacity();
 // pair count) of entries (depth bits << 32) | (cover << 28) | splat, in any order, by (depth bits, splat) and writes
 // each of its tiles' lists from the tile's start (ranges) on: vals_out = the splats, keys_out (if not null) =
 // (tile << 32) | depth bits. Cover bit 2 dy + dx says the splat belongs to tile (dx, dy) of the super-tile. Lists
-// longer than LDS holds, or with many equal depths, are sorted through gk0, gk1, gp0, gp1 (32-bit pair-count
-// arrays, each super-tile using its own stretch).
-void launch_super_order(hipStream_t s, const uint64_t* list, const uint32_t* sup_start, const uint32_t* sup_total,
+// longer than LDS holds are partitioned through gk0, gk1 and ordered in chunks; lists or chunks with many equal
+// depths are sorted through gk0, gk1, gp0, gp1 (32-bit pair-count arrays, each super-tile using its own stretch)
+// and the list's own stretch, which the call overwrites.
+void launch_super_order(hipStream_t s, uint64_t* list, const uint32_t* sup_start, const uint32_t* sup_total,
                         uint32_t num_sup, uint32_t tiles_x, uint32_t tiles_y, const uint32_t* ranges,
                         uint64_t pairs_cap, const uint64_t* pairs_dev, const float* depths, uint32_t n,
                         uint32_t* vals_out, uint64_t* keys_out, uint32_t* gk0, uint32_t* gk1, uint32_t* gp0,

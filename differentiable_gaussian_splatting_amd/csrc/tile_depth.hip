@@ -379,6 +379,7 @@ constexpr uint32_t kSupCap = 4608;      // the longest super-tile list sorted in
 constexpr uint32_t kSupBuckets = 2048;  // the most buckets of a list sorted in LDS
 constexpr uint32_t kSupItems = (kSupCap + kThreads - 1) / kThreads;
 constexpr uint32_t kCover = 28;         // the cover bits' place in an entry's low word
+constexpr uint32_t kCoarse = 256;       // a long list's chunking buckets
 constexpr uint64_t kSortBits = ~(uint64_t(0xFu) << kCover);  // an entry's (depth bits, splat)
 static_assert(kSupBuckets % kThreads == 0 && kSupBuckets <= kMaxBuckets, "super-tile bucket counts");
 
@@ -392,16 +393,20 @@ struct SuperShared {
     } bkt;
   } u;
   uint32_t wtot[2][kWaves][4];  // the filter's per-wave counts per tile, double-buffered
+  uint32_t cstart[kCoarse + 1];  // a long list's coarse buckets: counts, then starts
+  uint32_t crun[kCoarse];        // their next free slots
+  uint32_t chunk[kCoarse + 1];   // the first bucket of each chunk
+  uint32_t nchunk;
 };
 
 #define GSR_SUPER_ORDER_PARAMS                                                                                    \
-  const uint64_t *__restrict__ list, const uint32_t *__restrict__ sup_start, const uint32_t *__restrict__ sup_total, \
+  uint64_t *__restrict__ list, const uint32_t *__restrict__ sup_start, const uint32_t *__restrict__ sup_total,       \
       uint32_t tiles_x, uint32_t tiles_y, const uint32_t *__restrict__ ranges, uint64_t pairs_cap,                 \
       const uint64_t *__restrict__ pairs_dev, const float *__restrict__ depths, uint32_t n,                         \
       uint32_t *__restrict__ vals_out, uint64_t *__restrict__ keys_out, uint32_t *gk0, uint32_t *gk1, uint32_t *gp0, \
       uint32_t *gp1
 
-// Three workgroups per compute unit (LDS 46 KB each): six waves per SIMD, 80 registers.
+// Three workgroups per compute unit (LDS 49 KB each): six waves per SIMD, 80 registers.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) void k_super_order(
     GSR_SUPER_ORDER_PARAMS) {
   __shared__ SuperShared ts;
@@ -423,120 +428,201 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) v
   auto splat_at = [&](uint32_t e) -> uint32_t { return uint32_t(lst[e]) & ((1u << kCover) - 1u); };
   auto depth_bits = [&](uint32_t splat) -> uint32_t { return splat < n ? __float_as_uint(depths[splat]) : 0u; };
 
-  bool in_lds = false;
-  if (m <= kSupCap) {
-    uint64_t x[kSupItems];
-    uint32_t slot[kSupItems];
+  // The extremes of kSupItems entries per thread (x[i] valid for tid + i kThreads < mc), over the workgroup.
+  auto extremes = [&](const uint64_t* x, uint32_t mc, uint32_t& lo, uint32_t& hi) {
     uint32_t kmin = ~0u, kmax = 0;
 #pragma unroll
-    for (uint32_t i = 0; i < kSupItems; ++i) {  // every load in flight at once (positions past m read entry 0)
-      const uint32_t e = tid + i * kThreads;
-      x[i] = lst[e < m ? e : 0u];
-    }
-#pragma unroll
     for (uint32_t i = 0; i < kSupItems; ++i)
-      if (tid + i * kThreads < m) kmin = min(kmin, uint32_t(x[i] >> 32)), kmax = max(kmax, uint32_t(x[i] >> 32));
-    const uint32_t half = (m + 1) / 2;
-    const uint32_t nb = min(kSupBuckets, max(kMinBuckets, half > 1 ? 1u << (32 - __clz(int(half - 1))) : 1u));
-    for (uint32_t j = tid; j <= nb; j += kThreads) ts.u.bkt.start[j] = 0;
+      if (tid + i * kThreads < mc) kmin = min(kmin, uint32_t(x[i] >> 32)), kmax = max(kmax, uint32_t(x[i] >> 32));
     kmin = wave_min(kmin);
     kmax = wave_max(kmax);
     if (lane == 0) ts.u.bkt.wmin[w] = kmin, ts.u.bkt.wmax[w] = kmax;
     __syncthreads();
+    lo = ts.u.bkt.wmin[0], hi = ts.u.bkt.wmax[0];
+#pragma unroll
+    for (uint32_t q = 1; q < kWaves; ++q) lo = min(lo, ts.u.bkt.wmin[q]), hi = max(hi, ts.u.bkt.wmax[q]);
+  };
+
+  // Sorts mc <= kSupCap entries load(e) into ts.u.bkt.entry[0..mc) by (depth bits, splat). Buckets linear in the
+  // depth value between the entries' extremes (monotone: fp32 subtraction, scaling by a positive factor and
+  // truncation all preserve order), which spreads the workloads' uniform depths evenly (the per-tile order's map,
+  // linear in the bits, crowds the top of a wide range: 35 against 33 us at 410k splats); each entry's rank among
+  // the (depth bits, splat) of its bucket, then the entries moved to their ranks. Returns false, having sorted
+  // nothing, when a bucket holds more than kBucketLimit entries (many equal depths), unless `force`.
+  auto sort_in_lds = [&](uint32_t mc, auto load, bool force) -> bool {
+    uint64_t x[kSupItems];
+    uint32_t slot[kSupItems];
+#pragma unroll
+    for (uint32_t i = 0; i < kSupItems; ++i) {  // every load in flight at once (positions past mc read entry 0)
+      const uint32_t e = tid + i * kThreads;
+      x[i] = load(e < mc ? e : 0u);
+    }
+    const uint32_t half = (mc + 1) / 2;
+    const uint32_t nb = min(kSupBuckets, max(kMinBuckets, half > 1 ? 1u << (32 - __clz(int(half - 1))) : 1u));
+    for (uint32_t j = tid; j <= nb; j += kThreads) ts.u.bkt.start[j] = 0;
+    uint32_t lo, hi;
+    extremes(x, mc, lo, hi);
+    const float lov = __uint_as_float(lo);
+    const float scale = float(nb) / fmaxf(__uint_as_float(hi) - lov, 1e-30f);
+    auto bucket = [&](uint32_t key) { return min(nb - 1, uint32_t((__uint_as_float(key) - lov) * scale)); };
+#pragma unroll
+    for (uint32_t i = 0; i < kSupItems; ++i)
+      if (tid + i * kThreads < mc) slot[i] = atomicAdd(&ts.u.bkt.start[bucket(uint32_t(x[i] >> 32))], 1u);
+    __syncthreads();
+    const uint32_t biggest = scan_buckets(ts.u.bkt.start, nb, mc, ts.u.bkt.wsum);
+    const bool crowded = __syncthreads_or(biggest > kBucketLimit);
+    if (crowded && !force) return false;
+#pragma unroll
+    for (uint32_t i = 0; i < kSupItems; ++i)
+      if (tid + i * kThreads < mc) ts.u.bkt.entry[ts.u.bkt.start[bucket(uint32_t(x[i] >> 32))] + slot[i]] = x[i];
+    __syncthreads();
+#pragma unroll
+    for (uint32_t i = 0; i < kSupItems; ++i) {
+      const uint32_t q = tid + i * kThreads;
+      slot[i] = ~0u;
+      if (q < mc) {
+        x[i] = ts.u.bkt.entry[q];
+        const uint64_t me = x[i] & kSortBits;
+        const uint32_t b = bucket(uint32_t(me >> 32));
+        const uint32_t b0 = ts.u.bkt.start[b], b1 = ts.u.bkt.start[b + 1];
+        uint32_t r = b0;
+        for (uint32_t f = b0; f < b1; ++f) r += (ts.u.bkt.entry[f] & kSortBits) < me ? 1u : 0u;
+        slot[i] = r;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (uint32_t i = 0; i < kSupItems; ++i)
+      if (slot[i] != ~0u) ts.u.bkt.entry[slot[i]] = x[i];
+    __syncthreads();
+    return true;
+  };
+
+  // The stable filter: the e-th of mc sorted entries entry_at(e) goes to the tiles its cover bits name, after the
+  // `carry` entries of each tile that earlier calls wrote. Steps of kThreads consecutive entries, one per thread:
+  // per tile, a ballot gives each entry its place among its wave's entries of that tile, the per-wave totals
+  // (double-buffered in LDS, one barrier per step) its wave's place, so the entries of a tile leave each wave as one
+  // contiguous run of stores.
+  uint32_t carry[4] = {0u, 0u, 0u, 0u};
+  auto filter = [&](uint32_t mc, auto entry_at) {
+    for (uint32_t c0 = 0, step = 0; c0 < mc; c0 += kThreads, step ^= 1u) {
+      const uint32_t e = c0 + tid;
+      const uint64_t x = e < mc ? entry_at(e) : 0;
+      const uint32_t spl = uint32_t(x) & ((1u << kCover) - 1u), key = uint32_t(x >> 32), mk = uint32_t(x) >> kCover;
+      uint32_t below[4];
+#pragma unroll
+      for (uint32_t j = 0; j < 4; ++j) {
+        const uint64_t bal = __builtin_amdgcn_ballot_w64((mk >> j) & 1u);
+        below[j] = uint32_t(__popcll(bal & lanemask_lt(lane)));
+        if (lane == 0) ts.wtot[step][w][j] = uint32_t(__popcll(bal));
+      }
+      __syncthreads();
+#pragma unroll
+      for (uint32_t j = 0; j < 4; ++j) {
+        uint32_t before = 0, all = 0;
+#pragma unroll
+        for (uint32_t q = 0; q < kWaves; ++q) {
+          const uint32_t c = ts.wtot[step][q][j];
+          before += q < w ? c : 0u;
+          all += c;
+        }
+        // plain stores: a wave's run shares cache lines with the neighbouring waves' runs, which L2 merges
+        // (non-temporal stores of these partial lines measured 43 against 35 us at 410k splats)
+        if ((mk >> j) & 1u) {
+          const uint64_t o = uint64_t(base[j]) + carry[j] + before + below[j];
+          if (o < P) {  // always, when the tiles' totals and the cover bits agree; keeps a stray write in bounds
+            vals_out[o] = spl;
+            if (keys_out) keys_out[o] = (uint64_t(tile[j]) << 32) | key;
+          }
+        }
+        carry[j] = __builtin_amdgcn_readfirstlane(carry[j] + all);
+      }
+    }
+  };
+
+  if (m <= kSupCap) {
+    if (sort_in_lds(m, [&](uint32_t e) { return lst[e]; }, false)) {
+      filter(m, [&](uint32_t e) { return ts.u.bkt.entry[e]; });
+      return;
+    }
+  } else {
+    // A longer list in chunks that LDS holds: kCoarse buckets linear in the depth value between the list's
+    // extremes (equal depths share one) count the entries and partition them into the arena (low words in gk0,
+    // high words in gk1, at the list's stretch); runs of consecutive buckets of at most kSupCap entries are then
+    // sorted and filtered one after the other (the filter carries each tile's count from chunk to chunk). A bucket
+    // of more than kSupCap entries sends the list to the radix sort instead (decided before anything is written); a
+    // chunk with a crowded bucket is sorted by the radix sort on its own.
+    uint32_t kmin = ~0u, kmax = 0;
+    for (uint32_t e = tid; e < m; e += kThreads) {
+      const uint32_t k = uint32_t(lst[e] >> 32);
+      kmin = min(kmin, k), kmax = max(kmax, k);
+    }
+    kmin = wave_min(kmin);
+    kmax = wave_max(kmax);
+    if (lane == 0) ts.u.bkt.wmin[w] = kmin, ts.u.bkt.wmax[w] = kmax;
+    for (uint32_t c = tid; c <= kCoarse; c += kThreads) ts.cstart[c] = 0;
+    __syncthreads();
     uint32_t lo = ts.u.bkt.wmin[0], hi = ts.u.bkt.wmax[0];
 #pragma unroll
     for (uint32_t q = 1; q < kWaves; ++q) lo = min(lo, ts.u.bkt.wmin[q]), hi = max(hi, ts.u.bkt.wmax[q]);
-    // buckets linear in the depth value between the list's extremes (monotone: fp32 subtraction, scaling by a
-    // positive factor and truncation all preserve order), which spreads the workloads' uniform depths evenly; the
-    // per-tile order's map, linear in the bits, crowds the top of a wide range (33 against 35 us at 410k splats)
     const float lov = __uint_as_float(lo);
-    const float scale = float(nb) / fmaxf(__uint_as_float(hi) - lov, 1e-30f);
-    auto bucket_of = [&](uint32_t key, uint32_t, float, uint32_t) {
-      return min(nb - 1, uint32_t((__uint_as_float(key) - lov) * scale));
-    };
-#pragma unroll
-    for (uint32_t i = 0; i < kSupItems; ++i)
-      if (tid + i * kThreads < m) slot[i] = atomicAdd(&ts.u.bkt.start[bucket_of(uint32_t(x[i] >> 32), lo, scale, nb)], 1u);
+    const float cscale = float(kCoarse) / fmaxf(__uint_as_float(hi) - lov, 1e-30f);
+    auto coarse = [&](uint32_t key) { return min(kCoarse - 1, uint32_t((__uint_as_float(key) - lov) * cscale)); };
+    for (uint32_t e = tid; e < m; e += kThreads) atomicAdd(&ts.cstart[coarse(uint32_t(lst[e] >> 32))], 1u);
     __syncthreads();
-    const uint32_t biggest = scan_buckets(ts.u.bkt.start, nb, m, ts.u.bkt.wsum);
-    in_lds = !__syncthreads_or(biggest > kBucketLimit);
-    if (in_lds) {
-#pragma unroll
-      for (uint32_t i = 0; i < kSupItems; ++i)
-        if (tid + i * kThreads < m)
-          ts.u.bkt.entry[ts.u.bkt.start[bucket_of(uint32_t(x[i] >> 32), lo, scale, nb)] + slot[i]] = x[i];
+    const uint32_t cnt = tid < kCoarse ? ts.cstart[tid] : 0u;
+    if (!__syncthreads_or(cnt > kSupCap)) {
+      const uint32_t first = block_exclusive_scan<uint32_t, kThreads>(cnt, nullptr, ts.u.bkt.wsum);
+      if (tid < kCoarse) ts.cstart[tid] = first, ts.crun[tid] = first;
+      if (tid == 0) ts.cstart[kCoarse] = m;
       __syncthreads();
-      // each entry's rank among the (depth bits, splat) of its bucket, then the entries moved to their ranks (the
-      // barrier between ends every read)
-#pragma unroll
-      for (uint32_t i = 0; i < kSupItems; ++i) {
-        const uint32_t q = tid + i * kThreads;
-        slot[i] = ~0u;
-        if (q < m) {
-          x[i] = ts.u.bkt.entry[q];
-          const uint64_t me = x[i] & kSortBits;
-          const uint32_t b = bucket_of(uint32_t(me >> 32), lo, scale, nb);
-          const uint32_t b0 = ts.u.bkt.start[b], b1 = ts.u.bkt.start[b + 1];
-          uint32_t r = b0;
-          for (uint32_t f = b0; f < b1; ++f) r += (ts.u.bkt.entry[f] & kSortBits) < me ? 1u : 0u;
-          slot[i] = r;
+      if (tid == 0) {  // chunk boundaries: runs of consecutive buckets of at most kSupCap entries
+        uint32_t nch = 0, acc = 0;
+        ts.chunk[0] = 0;
+        for (uint32_t c = 0; c < kCoarse; ++c) {
+          const uint32_t k = ts.cstart[c + 1] - ts.cstart[c];
+          if (acc + k > kSupCap) ts.chunk[++nch] = c, acc = 0;
+          acc += k;
         }
+        ts.chunk[++nch] = kCoarse;
+        ts.nchunk = nch;
       }
-      __syncthreads();
-#pragma unroll
-      for (uint32_t i = 0; i < kSupItems; ++i)
-        if (slot[i] != ~0u) ts.u.bkt.entry[slot[i]] = x[i];
-      __syncthreads();
-    }
-  }
-  // otherwise the radix sort through the arena (a barrier above ends every read of the bucket layout)
-  const uint32_t* kr = nullptr;
-  const uint32_t* pr = nullptr;
-  if (!in_lds) {
-    uint32_t *k0 = gk0 + st, *k1 = gk1 + st, *p0 = gp0 + st, *p1 = gp1 + st;
-    const uint32_t res = radix_order(k0, k1, p0, p1, m, false, splat_at, depth_bits, ts.u.sh);
-    kr = res ? k1 : k0;
-    pr = res ? p1 : p0;
-  }
-  // The stable filter: the e-th entry of the sorted list goes to the tiles its cover bits name. Steps of kThreads
-  // consecutive entries, one per thread: per tile, a ballot gives each entry its place among its wave's entries of
-  // that tile, the per-wave totals (double-buffered in LDS, one barrier per step) its wave's place, so the entries of
-  // a tile leave each wave as one contiguous run of stores.
-  uint32_t carry[4] = {0u, 0u, 0u, 0u};
-  for (uint32_t c0 = 0, step = 0; c0 < m; c0 += kThreads, step ^= 1u) {
-    const uint32_t e = c0 + tid;
-    uint64_t x = 0;
-    if (e < m) x = in_lds ? ts.u.bkt.entry[e] : (uint64_t(kr[e]) << 32) | uint32_t(lst[pr[e]]);
-    const uint32_t spl = uint32_t(x) & ((1u << kCover) - 1u), key = uint32_t(x >> 32), mk = uint32_t(x) >> kCover;
-    uint32_t below[4];
-#pragma unroll
-    for (uint32_t j = 0; j < 4; ++j) {
-      const uint64_t bal = __builtin_amdgcn_ballot_w64((mk >> j) & 1u);
-      below[j] = uint32_t(__popcll(bal & lanemask_lt(lane)));
-      if (lane == 0) ts.wtot[step][w][j] = uint32_t(__popcll(bal));
-    }
-    __syncthreads();
-#pragma unroll
-    for (uint32_t j = 0; j < 4; ++j) {
-      uint32_t before = 0, all = 0;
-#pragma unroll
-      for (uint32_t q = 0; q < kWaves; ++q) {
-        const uint32_t c = ts.wtot[step][q][j];
-        before += q < w ? c : 0u;
-        all += c;
+      for (uint32_t e = tid; e < m; e += kThreads) {
+        const uint64_t x = lst[e];
+        const uint32_t q = atomicAdd(&ts.crun[coarse(uint32_t(x >> 32))], 1u);
+        gk0[st + q] = uint32_t(x);
+        gk1[st + q] = uint32_t(x >> 32);
       }
-      if ((mk >> j) & 1u) {
-        const uint64_t o = uint64_t(base[j]) + carry[j] + before + below[j];
-        // plain stores: a wave's run shares cache lines with the neighbouring waves' runs, which L2 merges
-        // (non-temporal stores of these partial lines measured 43 against 35 us at 410k splats)
-        if (o < P) {  // always, when the tiles' totals and the cover bits agree; keeps a stray write in bounds
-          vals_out[o] = spl;
-          if (keys_out) keys_out[o] = (uint64_t(tile[j]) << 32) | key;
+      __syncthreads();  // the partition's global writes are seen by the whole workgroup after the barrier
+      const uint32_t nch = ts.nchunk;
+      for (uint32_t k = 0; k < nch; ++k) {
+        const uint32_t e0 = ts.cstart[ts.chunk[k]], mc = ts.cstart[ts.chunk[k + 1]] - e0;
+        const uint32_t* const lw = gk0 + st + e0;
+        const uint32_t* const hw = gk1 + st + e0;
+        if (sort_in_lds(mc, [&](uint32_t e) { return (uint64_t(hw[e]) << 32) | lw[e]; }, false)) {
+          filter(mc, [&](uint32_t e) { return ts.u.bkt.entry[e]; });
+        } else {
+          // a crowded chunk (many equal or nearly equal depths): the radix sort through the arena, keys in gp0 and
+          // gp1 and positions in the list's own stretch, free once partitioned (its 64-bit words as 2m 32-bit ones)
+          uint32_t* const free32 = reinterpret_cast<uint32_t*>(list + st);
+          uint32_t *k0 = gp0 + st + e0, *k1 = gp1 + st + e0, *p0 = free32 + e0, *p1 = free32 + m + e0;
+          auto chunk_splat = [&](uint32_t e) -> uint32_t { return lw[e] & ((1u << kCover) - 1u); };
+          const uint32_t res = radix_order(k0, k1, p0, p1, mc, false, chunk_splat, depth_bits, ts.u.sh);
+          const uint32_t* const kr = res ? k1 : k0;
+          const uint32_t* const pr = res ? p1 : p0;
+          filter(mc, [&](uint32_t e) { return (uint64_t(kr[e]) << 32) | lw[pr[e]]; });
         }
+        __syncthreads();  // the next chunk reuses the LDS
       }
-      carry[j] = __builtin_amdgcn_readfirstlane(carry[j] + all);
+      return;
     }
   }
+  // otherwise the radix sort through the arena (a barrier above ends every read of the LDS)
+  uint32_t *k0 = gk0 + st, *k1 = gk1 + st, *p0 = gp0 + st, *p1 = gp1 + st;
+  const uint32_t res = radix_order(k0, k1, p0, p1, m, false, splat_at, depth_bits, ts.u.sh);
+  const uint32_t* kr = res ? k1 : k0;
+  const uint32_t* pr = res ? p1 : p0;
+  filter(m, [&](uint32_t e) { return (uint64_t(kr[e]) << 32) | uint32_t(lst[pr[e]]); });
 }
 
 }  // namespace
@@ -559,7 +645,7 @@ void launch_tile_depth(hipStream_t s, const uint32_t* list, const uint32_t* list
 
 uint32_t tile_depth_capacity() { return kCap; }
 
-void launch_super_order(hipStream_t s, const uint64_t* list, const uint32_t* sup_start, const uint32_t* sup_total,
+void launch_super_order(hipStream_t s, uint64_t* list, const uint32_t* sup_start, const uint32_t* sup_total,
                         uint32_t num_sup, uint32_t tiles_x, uint32_t tiles_y, const uint32_t* ranges,
                         uint64_t pairs_cap, const uint64_t* pairs_dev, const float* depths, uint32_t n,
                         uint32_t* vals_out, uint64_t* keys_out, uint32_t* gk0, uint32_t* gk1, uint32_t* gp0,

@@ -230,19 +230,22 @@ def test_bin_ellipse_rule_ragged_images(ctx, w, h):
         set_rule(ctx, "box")
 
 
+@pytest.mark.parametrize("rule", ["box", "ellipse"])
 @pytest.mark.parametrize("w,h,n,cluster,levels", [(16, 16, 6000, 0.0, 0), (64, 48, 30000, 0.0, 0),
                                                    (800, 800, 200000, 0.3, 0), (16, 16, 6000, 0.0, 3),
                                                    (16, 16, 70000, 0.0, 0), (16, 16, 70000, 0.0, 3)])
-def test_tile_depth_long_lists(ctx, w, h, n, cluster, levels):
-    """Tile lists longer than the tile-first scheme's on-chip capacity (3456 pairs) are ordered through the arena
-    instead: one tile of 6000 pairs; twelve tiles of 5-11 thousand; 16 tiles of up to 25 thousand (30% of the
-    splats in a 48-pixel square) among 2,484 short ones, both forms in one launch; one tile of 6000 pairs at three
-    depths (crowded buckets: the radix sort through the arena); and one tile of 70,000 pairs (positions past 16
-    bits), by buckets and at three depths by the radix sort. Bit-exact against the oracle on a fresh
-    context (no count seen: the first call takes the tile-first path) and again with the count seen."""
+def test_tile_depth_long_lists(ctx, w, h, n, cluster, levels, rule):
+    """Lists longer than the tile-first scheme's on-chip capacities: one tile of 6000 pairs; twelve tiles of 5-11
+    thousand; 16 tiles of up to 25 thousand (30% of the splats in a 48-pixel square) among 2,484 short ones, both
+    forms in one launch; one tile of 6000 pairs at three depths (crowded buckets); and one tile of 70,000 pairs
+    (positions past 16 bits), at spread depths and at three. Under the box rule the lists are the super-tiles' (the
+    same splats), ordered in chunks of at most 4608 on chip, or by the radix sort through the arena when one chunk
+    would be longer (70,000 at three depths); under the ellipse rule each tile's list is ordered on its own, past
+    3456 pairs by buckets through the arena, or by the radix sort when a bucket is crowded. Bit-exact against the
+    oracle on a fresh context and again with the count seen."""
     import oracle
     from differentiable_gaussian_splatting_amd import gsr
-    banner(f"bin tile_depth long lists {w}x{h} n={n} cluster={cluster} levels={levels}")
+    banner(f"bin tile_depth long lists {w}x{h} n={n} cluster={cluster} levels={levels} rule={rule}")
     rng = np.random.default_rng(n)
     s = np.exp(rng.uniform(np.log(0.5), np.log(8.0), n))
     sp = np.zeros((n, 9), np.float32)
@@ -256,11 +259,12 @@ def test_tile_depth_long_lists(ctx, w, h, n, cluster, levels):
     depths[: n // 10] = depths[n // 10: 2 * (n // 10)]  # equal depths: ties keep splat order
     if levels:
         depths = rng.choice(np.array([0.5, 2.0, 7.5], np.float32)[:levels], n)
-    ref = oracle.bin(sp, depths, w, h)
+    ref = oracle.bin(sp, depths, w, h, rule=rule)
     lens = ref.ranges[:, 1].astype(np.int64) - ref.ranges[:, 0]
-    assert lens.max() > 3456
+    assert lens.max() > 4608
     c = gsr.Context(0)
     try:
+        set_rule(c, rule)
         assert_bins_equal(c, sp, depths, w, h, "tile_depth", ref)
         assert_bins_equal(c, sp, depths, w, h, "tile_depth", ref)
     finally:

@@ -162,9 +162,9 @@ def deep_pile():
 
 @pytest.mark.parametrize("form", ["default", "deterministic", "per_splat"])
 def test_deep_pile_matches_oracle(deep_pile, form):
-    """Bins, image and gradients of the deep pile against the oracle. A fresh context has seen no pair count, so
-    its first call takes the tile-first binning (lists past the on-chip capacity); the next call has seen 12,000
-    pairs per tile and takes the presort scheme. Both bins bit-exact, then the raster under each backward form."""
+    """Bins, image and gradients of the deep pile against the oracle: the tile-first binning (its super-tiles'
+    lists of 12,000 entries ordered in chunks on chip) and the presort scheme both bit-exact, then the raster under
+    each backward form on the tile-first bins."""
     from differentiable_gaussian_splatting_amd import gsr
     sc, ob, fwd, ref = deep_pile
     w, h = sc.width, sc.height
@@ -175,7 +175,8 @@ def test_deep_pile_matches_oracle(deep_pile, form):
     c = gsr.Context(0)
     try:
         sp = dev(sc.splats)
-        for _ in range(2):
+        for scheme in (gsr.GSR_BIN_PRESORT, gsr.GSR_BIN_TILE_DEPTH):
+            gsr.gsr_set_option(c, gsr.GSR_OPT_BIN_SCHEME, scheme)
             bins = gsr.gsr_bin(c, sp, dev(sc.depths), w, h)
             keys, vals, ranges = gsr.gsr_bins_copy(c, bins)
             assert np.array_equal(host(keys, np.uint64), ob.keys)
