@@ -380,6 +380,7 @@ constexpr uint32_t kSupBuckets = 2048;  // the most buckets of a list sorted in 
 constexpr uint32_t kSupItems = (kSupCap + kThreads - 1) / kThreads;
 constexpr uint32_t kCover = 28;         // the cover bits' place in an entry's low word
 constexpr uint32_t kCoarse = 256;       // a long list's chunking buckets
+constexpr uint32_t kPass = 8;           // a long list's entries per thread per load batch
 constexpr uint64_t kSortBits = ~(uint64_t(0xFu) << kCover);  // an entry's (depth bits, splat)
 static_assert(kSupBuckets % kThreads == 0 && kSupBuckets <= kMaxBuckets, "super-tile bucket counts");
 
@@ -552,11 +553,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) v
     // sorted and filtered one after the other (the filter carries each tile's count from chunk to chunk). A bucket
     // of more than kSupCap entries sends the list to the radix sort instead (decided before anything is written); a
     // chunk with a crowded bucket is sorted by the radix sort on its own.
+    // f(e, entry) for every entry, kPass loads per thread in flight at once
+    auto each_entry = [&](auto f) {
+      for (uint32_t e0 = 0; e0 < m; e0 += kPass * kThreads) {
+        uint64_t x[kPass];
+#pragma unroll
+        for (uint32_t i = 0; i < kPass; ++i) {
+          const uint32_t e = e0 + i * kThreads + tid;
+          x[i] = lst[e < m ? e : 0u];
+        }
+#pragma unroll
+        for (uint32_t i = 0; i < kPass; ++i)
+          if (e0 + i * kThreads + tid < m) f(e0 + i * kThreads + tid, x[i]);
+      }
+    };
     uint32_t kmin = ~0u, kmax = 0;
-    for (uint32_t e = tid; e < m; e += kThreads) {
-      const uint32_t k = uint32_t(lst[e] >> 32);
+    each_entry([&](uint32_t, uint64_t x) {
+      const uint32_t k = uint32_t(x >> 32);
       kmin = min(kmin, k), kmax = max(kmax, k);
-    }
+    });
     kmin = wave_min(kmin);
     kmax = wave_max(kmax);
     if (lane == 0) ts.u.bkt.wmin[w] = kmin, ts.u.bkt.wmax[w] = kmax;
@@ -568,7 +583,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) v
     const float lov = __uint_as_float(lo);
     const float cscale = float(kCoarse) / fmaxf(__uint_as_float(hi) - lov, 1e-30f);
     auto coarse = [&](uint32_t key) { return min(kCoarse - 1, uint32_t((__uint_as_float(key) - lov) * cscale)); };
-    for (uint32_t e = tid; e < m; e += kThreads) atomicAdd(&ts.cstart[coarse(uint32_t(lst[e] >> 32))], 1u);
+    each_entry([&](uint32_t, uint64_t x) { atomicAdd(&ts.cstart[coarse(uint32_t(x >> 32))], 1u); });
     __syncthreads();
     const uint32_t cnt = tid < kCoarse ? ts.cstart[tid] : 0u;
     if (!__syncthreads_or(cnt > kSupCap)) {
@@ -587,12 +602,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) v
         ts.chunk[++nch] = kCoarse;
         ts.nchunk = nch;
       }
-      for (uint32_t e = tid; e < m; e += kThreads) {
-        const uint64_t x = lst[e];
+      each_entry([&](uint32_t, uint64_t x) {
         const uint32_t q = atomicAdd(&ts.crun[coarse(uint32_t(x >> 32))], 1u);
         gk0[st + q] = uint32_t(x);
         gk1[st + q] = uint32_t(x >> 32);
-      }
+      });
       __syncthreads();  // the partition's global writes are seen by the whole workgroup after the barrier
       const uint32_t nch = ts.nchunk;
       for (uint32_t k = 0; k < nch; ++k) {
