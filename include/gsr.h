@@ -68,11 +68,11 @@ gsr_status gsr_reserve(gsr_ctx* ctx, uint64_t max_pairs, uint32_t max_splats);
 #define GSR_BIN_TILE_DEPTH 2 /*   default: tile order first, then each list by (depth, splat) in one workgroup.   */
                              /*   Under the box rule with at most 8192 tiles and fewer than 2^28 splats, a        */
                              /*   counting sort into the lists of 2x2-tile super-tiles, each of which is sorted   */
-                             /*   once (on chip up to 4608 entries) and filtered into its four tiles' lists;      */
-                             /*   otherwise emission in splat order, a radix sort by tile id and a sort of each   */
-                             /*   tile's list (on chip up to 3456 pairs); longer lists go through the arena. When */
-                             /*   the last pair count seen averages more than 3072 pairs per tile, a call runs    */
-                             /*   the presort scheme instead                                                      */
+                             /*   once on chip (longer lists than 4608 entries in chunks of consecutive depths)   */
+                             /*   and filtered into its four tiles' lists; otherwise emission in splat order, a   */
+                             /*   radix sort by tile id and a sort of each tile's list (on chip up to 3456        */
+                             /*   pairs, longer lists through the arena), and when the last pair count seen       */
+                             /*   averages more than 3072 pairs per tile, a call runs the presort scheme instead  */
 #define GSR_OPT_BIN_KEYS 2   /* 1 (default): gsr_bin materialises the sorted 64-bit keys; 0: keys = NULL          */
 #define GSR_OPT_RASTER_SKIP 3 /* 1 (default): the raster kernels skip work that provably changes nothing - splats   */
                               /*   that cannot reach alpha >= 1/255 in a wavefront's 8x8 block, and, in the        */
