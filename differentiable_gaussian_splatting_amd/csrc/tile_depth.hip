@@ -611,6 +611,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) v
       const uint32_t nch = ts.nchunk;
       for (uint32_t k = 0; k < nch; ++k) {
         const uint32_t e0 = ts.cstart[ts.chunk[k]], mc = ts.cstart[ts.chunk[k + 1]] - e0;
+        if (mc == 0) continue;  // not reached: every chunk holds an entry (uniform)
         const uint32_t* const lw = gk0 + st + e0;
         const uint32_t* const hw = gk1 + st + e0;
         if (sort_in_lds(mc, [&](uint32_t e) { return (uint64_t(hw[e]) << 32) | lw[e]; }, false)) {
