@@ -141,6 +141,21 @@ def test_sync_mode_reports_its_count():
         c.close()
 
 
+@pytest.mark.parametrize("scheme", [0, 2])
+def test_sync_free_bin1m(scheme):
+    """The 1M-splat stress scene sync-free: 26 M pairs, whose super-tile lists (about 15,000 entries) the tile-first
+    scheme orders in chunks; the second call sizes its buffers from the first's count and does not wait."""
+    banner(f"bin sync-free bin1m scheme={scheme}")
+    ctx = new_ctx(scheme)
+    try:
+        sc = scene("bin1m")
+        ref = oracle_bins("bin1m")
+        for _ in range(2):
+            bin_and_compare(ctx, sc.splats, sc.depths, sc.width, sc.height, ref)
+    finally:
+        ctx.close()
+
+
 @pytest.mark.parametrize("scheme", [0, 1, 2])
 def test_sync_free_without_keys(scheme):
     """Sync-free with GSR_OPT_BIN_KEYS = 0: no keys, and the values and ranges still the oracle's."""
