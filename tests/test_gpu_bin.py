@@ -230,6 +230,31 @@ def test_bin_ellipse_rule_ragged_images(ctx, w, h):
         set_rule(ctx, "box")
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_tile_first_random_scenes(ctx, seed):
+    """Seeded random scenes for the tile-first scheme's two-level counting sort: image sizes from 1 to 400 pixels a
+    side (odd tile counts leave super-tiles partly off the grid), 1 to 20,000 splats of 0.2-60 px, means spread past
+    the image, and in half of them depths quantised to a few levels (ties and crowded buckets). A fresh context per
+    scene (its first call has no pair count to go by). Bit-exact against the oracle."""
+    import oracle
+    from differentiable_gaussian_splatting_amd import gsr
+    rng = np.random.default_rng(1000 + seed)
+    w, h = int(rng.integers(1, 401)), int(rng.integers(1, 401))
+    n = int(rng.choice([1, 2, 50, 500, 5000, 20000]))
+    levels = int(rng.choice([0, 0, 2, 7])) if seed % 2 else 0
+    sc = custom_scene(name="rand", width=w, height=h, n=n, seed=2000 + seed,
+                      size_classes=((0.6, 0.2, 6.0), (0.4, 6.0, 60.0)), margin=float(rng.uniform(0, 80)),
+                      depth_levels=levels)
+    banner(f"bin tile-first random seed={seed} {w}x{h} n={n} levels={levels}")
+    ref = oracle.bin(sc.splats, sc.depths, w, h)
+    c = gsr.Context(0)
+    try:
+        assert_bins_equal(c, sc.splats, sc.depths, w, h, "tile_depth", ref)
+        assert_bins_equal(c, sc.splats, sc.depths, w, h, "tile_depth", ref)
+    finally:
+        c.close()
+
+
 @pytest.mark.parametrize("rule", ["box", "ellipse"])
 @pytest.mark.parametrize("w,h,n,cluster,levels", [(16, 16, 6000, 0.0, 0), (64, 48, 30000, 0.0, 0),
                                                    (800, 800, 200000, 0.3, 0), (16, 16, 6000, 0.0, 3),
