@@ -195,6 +195,41 @@ def test_deep_pile_matches_oracle(deep_pile, form):
     assert ok, (worst, at, g[at], ref[at])
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_raster_random_scenes(ctx, seed):
+    """Seeded random scenes through bin, forward and backward: image sizes from 1 to 200 pixels a side, 1 to 5,000
+    splats with opacities from faint to opaque, means spread past the image, and in half of them quantised depths.
+    Bins bit-exact, image and final T within 1e-5 and last_contrib exact on every scene. Seeds 0-7 hold splats of
+    0.2-10 px and also check the gradients against the bar. Seeds 8-11 hold splats up to 40 px and check the forward
+    only: on such splats over small images the fp32 method's own rounding (the oracle's, in the pages' order of
+    operations) lies 2-5 bars from the exact fp64 gradients, so no fp32 implementation can be held to the bar there;
+    on the 10-px scenes the oracle lies within 0.2 bar of the exact values."""
+    import oracle
+    from differentiable_gaussian_splatting_amd import gsr
+    rng = np.random.default_rng(3000 + seed)
+    w, h = int(rng.integers(1, 201)), int(rng.integers(1, 201))
+    n = (1, 20, 300, 2000, 5000, 300, 2000, 5000, 5000, 2000, 300, 5000)[seed]
+    large = seed >= 8
+    sizes = ((0.7, 0.2, 5.0), (0.3, 5.0, 40.0)) if large else ((0.7, 0.2, 3.0), (0.3, 3.0, 10.0))
+    sc = custom_scene(name="rand", width=w, height=h, n=n, seed=4000 + seed, size_classes=sizes,
+                      opacity_mu=float(rng.uniform(-3.0, 2.0)), opacity_sd=1.5, vout_sd=0.1,
+                      margin=float(rng.uniform(0, 40)), depth_levels=int(rng.choice([3, 9])) if seed % 2 else 0)
+    banner(f"raster random seed={seed} {w}x{h} n={n}")
+    ob = oracle.bin(sc.splats, sc.depths, w, h)
+    fwd = oracle.render_forward(sc.splats, ob, w, h)
+    sp = dev(sc.splats)
+    bins = gsr.gsr_bin(ctx, sp, dev(sc.depths), w, h)
+    _, vals, ranges = gsr.gsr_bins_copy(ctx, bins)
+    assert np.array_equal(host(vals, np.uint32), ob.vals) and np.array_equal(host(ranges, np.uint32), ob.ranges)
+    out, ft, lc = run_forward(ctx, sp, bins, w, h)
+    compare_forward((out, ft, lc), fwd)
+    if large:
+        return
+    ref = oracle.render_backward(sc.splats, ob, w, h, *fwd[:3], sc.v_out)
+    ok, worst, at = grads_close(host(run_backward(ctx, sc, bins, out, ft, lc)), ref)
+    assert ok, (worst, at)
+
+
 def set_det(ctx, on: bool):
     from differentiable_gaussian_splatting_amd import gsr
     gsr.gsr_set_option(ctx, gsr.GSR_OPT_DETERMINISTIC, 1 if on else 0)
