@@ -233,15 +233,16 @@ def bins_from_tensors(keys: torch.Tensor | None, vals: torch.Tensor, ranges: tor
 
 
 def gsr_bins_copy(ctx: Context, bins: Bins, stream=None):
-    """Copies a bins view into new tensors: keys int64 [P] (None if the bins carry none), vals int32 [P],
-    ranges int32 [T, 2]."""
+    """Copies a bins view into new tensors: keys int64 [P] (None if the bins carry none; empty when P = 0, where the
+    library may leave the pointers NULL), vals int32 [P], ranges int32 [T, 2]."""
     P, T = bins.num_pairs, bins.tiles_x * bins.tiles_y
     dev = ctx.device
-    keys = torch.empty(P, dtype=torch.int64, device=dev) if bins.raw.keys else None
+    keys = torch.empty(P, dtype=torch.int64, device=dev) if (bins.raw.keys or P == 0) else None
     vals = torch.empty(P, dtype=torch.int32, device=dev)
     ranges = torch.empty((T, 2), dtype=torch.int32, device=dev)
-    ctx.check(load().gsr_bins_copy(ctx.handle, _stream(stream), ctypes.byref(bins.raw), _ptr(keys), _ptr(vals),
-                                   _ptr(ranges), None), "gsr_bins_copy")
+    ctx.check(load().gsr_bins_copy(ctx.handle, _stream(stream), ctypes.byref(bins.raw),
+                                   _ptr(keys) if P else None, _ptr(vals) if P else None, _ptr(ranges), None),
+              "gsr_bins_copy")
     return keys, vals, ranges
 
 

@@ -159,8 +159,9 @@ gsr_status gsr_kernel_times(gsr_ctx* ctx, int32_t stage, float* ms, uint32_t max
 /* Views into the context's arena, valid until the next gsr_bin or gsr_reserve on the same context. A caller may
  * also fill one with its own device buffers of the same layout (for example bins computed elsewhere). */
 typedef struct gsr_bins {
-  const uint64_t* keys;   /* [num_pairs] (tile id << 32) | float bits of the splat's depth, ascending            */
-  const uint32_t* vals;   /* [num_pairs] splat index of each key                                                */
+  const uint64_t* keys;   /* [num_pairs] (tile id << 32) | float bits of the splat's depth, ascending; NULL     */
+                          /*   with GSR_OPT_BIN_KEYS = 0, and it may be NULL when num_pairs is 0               */
+  const uint32_t* vals;   /* [num_pairs] splat index of each key (may be NULL when num_pairs is 0)             */
   const uint32_t* ranges; /* [2 * tiles_x * tiles_y] (start, end) of each tile's run in keys / vals            */
   uint32_t num_pairs;
   uint32_t tiles_x;
@@ -197,7 +198,8 @@ gsr_status gsr_bin_pair_count(gsr_ctx* ctx, uint64_t* num_pairs, int32_t* overfl
 
 /* Copies the contents of `bins` into caller buffers (device pointers; any of them may be NULL to skip it):
  * keys [num_pairs] uint64, vals [num_pairs] uint32, ranges [2 * tiles] uint32, splat_pairs [num_splats] uint32.
- * Queued on stream. GSR_EINVAL when keys or splat_pairs is asked for and the bins carry none. */
+ * Queued on stream. GSR_EINVAL when keys (with num_pairs > 0) or splat_pairs (with num_splats > 0) is asked for
+ * and the bins carry none. */
 gsr_status gsr_bins_copy(gsr_ctx* ctx, void* stream, const gsr_bins* bins, uint64_t* keys, uint32_t* vals,
                          uint32_t* ranges, uint32_t* splat_pairs);
 

@@ -235,7 +235,8 @@ def test_tile_first_random_scenes(ctx, seed):
     """Seeded random scenes for the tile-first scheme's two-level counting sort: image sizes from 1 to 400 pixels a
     side (odd tile counts leave super-tiles partly off the grid), 1 to 20,000 splats of 0.2-60 px, means spread past
     the image, and in half of them depths quantised to a few levels (ties and crowded buckets). A fresh context per
-    scene (its first call has no pair count to go by). Bit-exact against the oracle."""
+    scene (its first call has no pair count to go by). Bit-exact against the oracle; then the same scene under the
+    other schemes, and under the ellipse rule with every scheme."""
     import oracle
     from differentiable_gaussian_splatting_amd import gsr
     rng = np.random.default_rng(1000 + seed)
@@ -251,6 +252,14 @@ def test_tile_first_random_scenes(ctx, seed):
     try:
         assert_bins_equal(c, sc.splats, sc.depths, w, h, "tile_depth", ref)
         assert_bins_equal(c, sc.splats, sc.depths, w, h, "tile_depth", ref)
+        # the same scene under the other schemes, and under the ellipse rule (per-tile lists) with every scheme
+        for scheme in SCHEMES:
+            if scheme != "tile_depth":
+                assert_bins_equal(c, sc.splats, sc.depths, w, h, scheme, ref)
+        ref_e = oracle.bin(sc.splats, sc.depths, w, h, rule="ellipse")
+        set_rule(c, "ellipse")
+        for scheme in SCHEMES:
+            assert_bins_equal(c, sc.splats, sc.depths, w, h, scheme, ref_e)
     finally:
         c.close()
 

@@ -200,7 +200,8 @@ def test_raster_random_scenes(ctx, seed):
     """Seeded random scenes through bin, forward and backward: image sizes from 1 to 200 pixels a side, 1 to 5,000
     splats with opacities from faint to opaque, means spread past the image, and in half of them quantised depths.
     Bins bit-exact, image and final T within 1e-5 and last_contrib exact on every scene. Seeds 0-7 hold splats of
-    0.2-10 px and also check the gradients against the bar. Seeds 8-11 hold splats up to 40 px and check the forward
+    0.2-10 px and also check the gradients against the bar, under the default, the deterministic and the per-splat
+    backward. Seeds 8-11 hold splats up to 40 px and check the forward
     only: on such splats over small images the fp32 method's own rounding (the oracle's, in the pages' order of
     operations) lies 2-5 bars from the exact fp64 gradients, so no fp32 implementation can be held to the bar there;
     on the 10-px scenes the oracle lies within 0.2 bar of the exact values."""
@@ -228,6 +229,17 @@ def test_raster_random_scenes(ctx, seed):
     ref = oracle.render_backward(sc.splats, ob, w, h, *fwd[:3], sc.v_out)
     ok, worst, at = grads_close(host(run_backward(ctx, sc, bins, out, ft, lc)), ref)
     assert ok, (worst, at)
+    # the deterministic and the per-splat backward on the same bins
+    for det, per_splat in ((True, False), (False, True)):
+        c = gsr.Context(0)
+        try:
+            set_det(c, det)
+            if per_splat:
+                gsr.gsr_set_option(c, gsr.GSR_OPT_BACKWARD_SCHEME, gsr.GSR_BACKWARD_PER_SPLAT)
+            ok, worst, at = grads_close(host(run_backward(c, sc, bins, out, ft, lc)), ref)
+            assert ok, (det, per_splat, worst, at)
+        finally:
+            c.close()
 
 
 def set_det(ctx, on: bool):
