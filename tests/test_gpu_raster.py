@@ -201,10 +201,13 @@ def test_raster_random_scenes(ctx, seed):
     splats with opacities from faint to opaque, means spread past the image, and in half of them quantised depths.
     Bins bit-exact, image and final T within 1e-5 and last_contrib exact on every scene. Seeds 0-7 hold splats of
     0.2-10 px and also check the gradients against the bar, under the default, the deterministic and the per-splat
-    backward. Seeds 8-11 hold splats up to 40 px and check the forward
-    only: on such splats over small images the fp32 method's own rounding (the oracle's, in the pages' order of
-    operations) lies 2-5 bars from the exact fp64 gradients, so no fp32 implementation can be held to the bar there;
-    on the 10-px scenes the oracle lies within 0.2 bar of the exact values."""
+    backward. Seeds 8-11 hold splats up to 40 px: on such splats over small images the fp32 method's own rounding
+    (the oracle's, in the pages' order of operations) lies 2-5 bars from the exact fp64 gradients, so no fp32
+    implementation can be held to the bar against the fp32 oracle there (on the 10-px scenes the oracle lies within
+    0.2 bar of the exact values). Their gradients, under all three backward forms, are held instead to the fp32
+    method's own envelope around the exact values (the oracle's exact-value backward on the same decisions): the
+    largest distance in bars may be at most three times the fp32 oracle's own largest distance plus one bar, which
+    a dropped term, a wrong sign or a misplaced value exceeds by orders of magnitude."""
     import oracle
     from differentiable_gaussian_splatting_amd import gsr
     rng = np.random.default_rng(3000 + seed)
@@ -224,11 +227,21 @@ def test_raster_random_scenes(ctx, seed):
     assert np.array_equal(host(vals, np.uint32), ob.vals) and np.array_equal(host(ranges, np.uint32), ob.ranges)
     out, ft, lc = run_forward(ctx, sp, bins, w, h)
     compare_forward((out, ft, lc), fwd)
-    if large:
-        return
     ref = oracle.render_backward(sc.splats, ob, w, h, *fwd[:3], sc.v_out)
-    ok, worst, at = grads_close(host(run_backward(ctx, sc, bins, out, ft, lc)), ref)
-    assert ok, (worst, at)
+    if large:
+        exact = oracle.render_backward_exact(sc.splats, ob, w, h, fwd[0], fwd[2], sc.v_out)
+        bar = 1e-4 + 1e-4 * np.abs(exact)
+        env = float((np.abs(ref - exact) / bar).max()) if exact.size else 0.0
+
+        def check(g, what):
+            d = float((np.abs(g.astype(np.float64) - exact) / bar).max()) if exact.size else 0.0
+            print(f"  {what}: {d:.2f} bars from the exact values (fp32 oracle {env:.2f})", flush=True)
+            assert d <= 3.0 * env + 1.0, (what, d, env)
+    else:
+        def check(g, what):
+            ok, worst, at = grads_close(g, ref)
+            assert ok, (what, worst, at)
+    check(host(run_backward(ctx, sc, bins, out, ft, lc)), "default")
     # the deterministic and the per-splat backward on the same bins
     for det, per_splat in ((True, False), (False, True)):
         c = gsr.Context(0)
@@ -236,8 +249,7 @@ def test_raster_random_scenes(ctx, seed):
             set_det(c, det)
             if per_splat:
                 gsr.gsr_set_option(c, gsr.GSR_OPT_BACKWARD_SCHEME, gsr.GSR_BACKWARD_PER_SPLAT)
-            ok, worst, at = grads_close(host(run_backward(c, sc, bins, out, ft, lc)), ref)
-            assert ok, (det, per_splat, worst, at)
+            check(host(run_backward(c, sc, bins, out, ft, lc)), f"deterministic={det} per_splat={per_splat}")
         finally:
             c.close()
 
